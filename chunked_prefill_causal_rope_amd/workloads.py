@@ -1,0 +1,172 @@
+"""Synthetic workloads: the configuration table and seeded input generators.
+
+This module holds no attention or RoPE arithmetic.  It only draws seeded
+random inputs (torch generators) and lays out the chunk schedule, so the HIP
+path and the CPU oracle can be fed the very same tensors.
+
+Draw order, per workload, from one generator seeded with ``Workload.seed``:
+prompt lengths (or decode context lengths), then Q, K, V (or, for decode, the
+K cache, the V cache, then the new token's q, k, v), then the q-norm and
+k-norm weights when the workload has qk-norm.  Values are N(0, 1) drawn in
+float32 and cast to the workload dtype; norm weights are 1 + 0.1 * N(0, 1).
+"""
+from __future__ import annotations
+
+import dataclasses
+import math
+from dataclasses import dataclass
+
+import torch
+
+F32, BF16 = "f32", "bf16"
+NORM_NONE, NORM_W, NORM_1PW = 0, 1, 2
+
+
+@dataclass(frozen=True)
+class Workload:
+    name: str
+    dtype: str                 # "f32" or "bf16": inputs, rotated Q and the cache
+    n_heads: int
+    n_kv: int
+    head_dim: int
+    seed: int
+    base: float = 10000.0
+    rotary_dim: int | None = None          # None = head_dim
+    yarn: tuple | None = None              # (factor, orig_max_pos, beta_fast, beta_slow)
+    rope_scale: float = 1.0
+    norm_style: int = NORM_NONE
+    norm_eps: float = 1e-6
+    # prefill
+    n_seq: int = 1
+    prompt_len: int = 0                    # fixed length when len_range is None
+    len_range: tuple | None = None         # (lo, hi) inclusive, drawn per sequence
+    chunk: int = 0
+    # decode (chunk = 1 at position ctx-1)
+    decode: bool = False
+    ctx_range: tuple | None = None         # (lo, hi) inclusive
+    cap: int | None = None
+    want_probs: bool = False
+
+    @property
+    def rd(self) -> int:
+        return min(self.rotary_dim or self.head_dim, self.head_dim)
+
+    @property
+    def torch_dtype(self):
+        return torch.float32 if self.dtype == F32 else torch.bfloat16
+
+    @property
+    def scale(self) -> float:
+        return 1.0 / math.sqrt(self.head_dim)
+
+    def replace(self, **kw) -> "Workload":
+        return dataclasses.replace(self, **kw)
+
+
+# Five workloads: small f32 correctness case; Llama-style GQA prefill; batched
+# decode with probabilities; Qwen-style partial rotary + qk-norm varlen
+# prefill; 128K-token YaRN prefill.
+CONFIGS = {
+    "c0_f32_small": Workload(
+        name="c0_f32_small", dtype=F32, n_heads=4, n_kv=2, head_dim=64, seed=1000,
+        base=10000.0, prompt_len=64, chunk=16, want_probs=True),
+    "c1_llama_prefill": Workload(
+        name="c1_llama_prefill", dtype=BF16, n_heads=32, n_kv=8, head_dim=128, seed=1001,
+        base=10000.0, prompt_len=4096, chunk=128),
+    "c2_decode": Workload(
+        name="c2_decode", dtype=BF16, n_heads=32, n_kv=8, head_dim=128, seed=1002,
+        base=10000.0, n_seq=64, decode=True, ctx_range=(1024, 32768), cap=32768,
+        want_probs=True),
+    "c3_qwen_varlen": Workload(
+        name="c3_qwen_varlen", dtype=BF16, n_heads=40, n_kv=8, head_dim=128, seed=1003,
+        base=1e6, rotary_dim=64, norm_style=NORM_W, norm_eps=1e-6, n_seq=8,
+        len_range=(512, 8192), chunk=256, cap=8192),
+    "c4_yarn_128k": Workload(
+        name="c4_yarn_128k", dtype=BF16, n_heads=64, n_kv=8, head_dim=128, seed=1004,
+        base=1e6, yarn=(4.0, 32768, 32.0, 1.0), rope_scale=0.1 * math.log(4.0) + 1.0,
+        prompt_len=131072, chunk=2048),
+}
+
+
+def _gen(seed: int, device) -> torch.Generator:
+    g = torch.Generator(device=device)
+    g.manual_seed(seed)
+    return g
+
+
+def _normal(shape, g, device, dtype):
+    return torch.randn(shape, generator=g, device=device, dtype=torch.float32).to(dtype)
+
+
+def prompt_lengths(w: Workload, g=None, device="cpu") -> list[int]:
+    if w.len_range is None:
+        return [w.prompt_len] * w.n_seq
+    g = g if g is not None else _gen(w.seed, device)
+    lo, hi = w.len_range
+    return [int(x) for x in torch.randint(lo, hi + 1, (w.n_seq,), generator=g, device=device)]
+
+
+def gen_prefill(w: Workload, device="cpu"):
+    """Packed varlen prefill inputs: q [T][nh][hd], k/v [T][nkv][hd] with the
+    sequences concatenated (cu_seq offsets), plus norm weights."""
+    g = _gen(w.seed, device)
+    lengths = prompt_lengths(w, g, device)
+    T = sum(lengths)
+    dt = w.torch_dtype
+    q = _normal((T, w.n_heads, w.head_dim), g, device, dt)
+    k = _normal((T, w.n_kv, w.head_dim), g, device, dt)
+    v = _normal((T, w.n_kv, w.head_dim), g, device, dt)
+    qw = kw = None
+    if w.norm_style != NORM_NONE:
+        qw = (1.0 + 0.1 * torch.randn((w.head_dim,), generator=g, device=device)).float()
+        kw = (1.0 + 0.1 * torch.randn((w.head_dim,), generator=g, device=device)).float()
+    cu = [0]
+    for n in lengths:
+        cu.append(cu[-1] + n)
+    cap = w.cap if w.cap is not None else max(lengths)
+    return dict(q=q, k=k, v=v, lengths=lengths, cu_seq=cu, q_norm_w=qw, k_norm_w=kw, cap=cap)
+
+
+def gen_decode(w: Workload, device="cpu"):
+    """Decode inputs: ctx[b] counts the new token, the cache holds ctx[b]-1
+    prior rows (already rotated; every cache row is drawn), and the new token's
+    q/k/v sit at position ctx[b]-1."""
+    g = _gen(w.seed, device)
+    lo, hi = w.ctx_range
+    ctx = [int(x) for x in torch.randint(lo, hi + 1, (w.n_seq,), generator=g, device=device)]
+    cap = w.cap if w.cap is not None else max(ctx)
+    dt = w.torch_dtype
+    kc = _normal((w.n_seq, w.n_kv, cap, w.head_dim), g, device, dt)
+    vc = _normal((w.n_seq, w.n_kv, cap, w.head_dim), g, device, dt)
+    q = _normal((w.n_seq, w.n_heads, w.head_dim), g, device, dt)
+    k = _normal((w.n_seq, w.n_kv, w.head_dim), g, device, dt)
+    v = _normal((w.n_seq, w.n_kv, w.head_dim), g, device, dt)
+    qw = kw = None
+    if w.norm_style != NORM_NONE:
+        qw = (1.0 + 0.1 * torch.randn((w.head_dim,), generator=g, device=device)).float()
+        kw = (1.0 + 0.1 * torch.randn((w.head_dim,), generator=g, device=device)).float()
+    return dict(ctx=ctx, k_cache=kc, v_cache=vc, q=q, k=k, v=v, q_norm_w=qw, k_norm_w=kw,
+                cap=cap)
+
+
+def chunk_schedule(lengths: list[int], chunk: int) -> list[list[tuple[int, int, int]]]:
+    """Steps of a varlen chunked prefill: each step takes the next <= chunk
+    tokens of every unfinished prompt.  Each step is a list of
+    (seq, first_position, n_tokens) for the sequences it advances."""
+    steps = []
+    done = [0] * len(lengths)
+    while any(d < n for d, n in zip(done, lengths)):
+        step = []
+        for b, n in enumerate(lengths):
+            if done[b] < n:
+                c = min(chunk, n - done[b])
+                step.append((b, done[b], c))
+                done[b] += c
+        steps.append(step)
+    return steps
+
+
+def prefill_flops(w: Workload, lengths: list[int]) -> float:
+    """Algorithmic causal attention FLOPs: 4*hd per (row, head, unmasked key);
+    row p has p+1 keys."""
+    return float(sum(4 * w.head_dim * w.n_heads * n * (n + 1) // 2 for n in lengths))

@@ -1,0 +1,349 @@
+/*
+ * oracle.c -- plain, slow CPU oracle for causal grouped-query attention with
+ * RoPE over a head-major KV cache.
+ *
+ * TEST INFRASTRUCTURE ONLY.  Only the test suite, the smoke check and the
+ * benchmark's CPU-baseline leg may load this library.  It shares no code with
+ * the HIP library and never consumes anything that library produced.
+ *
+ * Everything is computed in double precision with straight loops, in the order
+ * the source pages describe.  Sources (page title, then the item on it):
+ *   [ATT]  cortiq-engine 0.5.39, src/attention.rs
+ *   [NDL]  needle-core 0.3.1, src/v2/batch.rs
+ *
+ * Readings taken where the pages leave a step open are listed next to the
+ * function that takes them.
+ */
+#include <math.h>
+#include <pthread.h>
+#include <stdint.h>
+#include <stdlib.h>
+#include <string.h>
+
+#ifndef M_PI
+#define M_PI 3.14159265358979323846
+#endif
+
+/* ------------------------------------------------------------------------ */
+/* Frequency tables                                                          */
+/* ------------------------------------------------------------------------ */
+
+/*
+ * [ATT] fn rope_inv_freq: one inverse frequency per rotated pair,
+ *   f_i = 1 / base^(2i/d),  i < d/2,  d = rotary dimension.
+ * Reading: evaluated in double and rounded once to float (the page stores the
+ * table as f32, and the device receives an f32 table).
+ */
+void orc_rope_inv_freq(int rd, double base, float *out)
+{
+    for (int i = 0; i < rd / 2; i++) {
+        double f = 1.0 / pow(base, (2.0 * i) / (double)rd);
+        out[i] = (float)f;
+    }
+}
+
+/*
+ * [ATT] fn yarn_inv_freq (Hugging Face style YaRN).  Steps, in the page's order:
+ *   correction_dim(r) = d * ln(L0 / (2*pi*r)) / (2 ln base)
+ *   low  = max(floor(correction_dim(beta_fast)), 0)
+ *   high = clamp(ceil(correction_dim(beta_slow)), 0, d/2 - 1)
+ *   denom = max(high - low, 1)          (high - low saturates at 0)
+ *   ramp_i = clamp(sat(i - low) / denom, 0, 1)
+ *   f'_i = (f_i / factor) * ramp_i + f_i * (1 - ramp_i)
+ * d is the rotary dimension.  Reading: double throughout, one final rounding
+ * to float; the page's saturating subtractions are followed exactly.
+ * Returns the (low, high) pair through *lo_out / *hi_out when non-NULL.
+ */
+void orc_yarn_inv_freq(int rd, double base, double factor, int orig_max_pos,
+                       double beta_fast, double beta_slow, float *out,
+                       int *lo_out, int *hi_out)
+{
+    int half = rd / 2;
+    double cd_fast = (double)rd * log((double)orig_max_pos / (beta_fast * 2.0 * M_PI)) /
+                     (2.0 * log(base));
+    double cd_slow = (double)rd * log((double)orig_max_pos / (beta_slow * 2.0 * M_PI)) /
+                     (2.0 * log(base));
+    double lo_f = floor(cd_fast);
+    if (lo_f < 0.0)
+        lo_f = 0.0;
+    double hi_f = ceil(cd_slow);
+    double hi_cap = (double)(half > 0 ? half - 1 : 0);
+    if (hi_f < 0.0)
+        hi_f = 0.0;
+    if (hi_f > hi_cap)
+        hi_f = hi_cap;
+    int low = (int)lo_f;
+    int high = (int)hi_f;
+    int diff = high > low ? high - low : 0;
+    int denom = diff > 1 ? diff : 1;
+    for (int i = 0; i < half; i++) {
+        double f = 1.0 / pow(base, (2.0 * i) / (double)rd);
+        double interp = f / factor;
+        int num = i > low ? i - low : 0;
+        double ramp = (double)num / (double)denom;
+        if (ramp < 0.0)
+            ramp = 0.0;
+        if (ramp > 1.0)
+            ramp = 1.0;
+        double extrapolation = 1.0 - ramp;
+        out[i] = (float)(interp * (1.0 - extrapolation) + f * extrapolation);
+    }
+    if (lo_out)
+        *lo_out = low;
+    if (hi_out)
+        *hi_out = high;
+}
+
+/* ------------------------------------------------------------------------ */
+/* Storage rounding                                                          */
+/* ------------------------------------------------------------------------ */
+
+/*
+ * Round a double to the nearest bfloat16 value, ties to even (8 significant
+ * bits, exponent range of float).  Written from the format's definition:
+ * scale so that the bfloat16 quantum becomes 1, round to the nearest integer
+ * (the default rounding mode is to-nearest-even), scale back.
+ */
+double orc_round_bf16(double x)
+{
+    if (x == 0.0 || isnan(x) || isinf(x))
+        return x;
+    int e;
+    (void)frexp(x, &e);           /* |x| = m * 2^e, 0.5 <= m < 1 */
+    int q = e - 8;                /* quantum exponent for 8 significant bits */
+    if (q < -133)                 /* bfloat16 subnormal quantum is 2^-133 */
+        q = -133;
+    double r = nearbyint(ldexp(x, -q));
+    double y = ldexp(r, q);
+    double max_finite = ldexp(255.0, 120); /* (2 - 2^-7) * 2^127 */
+    if (fabs(y) > max_finite)
+        return copysign(INFINITY, x);
+    return y;
+}
+
+/* store_dtype: 0 = float32, 1 = bfloat16 */
+static double round_store(double x, int store_dtype)
+{
+    if (store_dtype == 1)
+        return orc_round_bf16(x);
+    return (double)(float)x;
+}
+
+void orc_round_array(double *x, long n, int store_dtype)
+{
+    for (long i = 0; i < n; i++)
+        x[i] = round_store(x[i], store_dtype);
+}
+
+/* ------------------------------------------------------------------------ */
+/* Per-head finish: qk-norm, then RoPE                                       */
+/* ------------------------------------------------------------------------ */
+
+/*
+ * [ATT] fn rmsnorm_head: r = 1/sqrt(sum(x^2)/n + eps); x <- x*r*w ("Qwen"
+ * style, norm_style 1) or x*r*(1+w) ("Gemma" style, norm_style 2).
+ */
+static void rmsnorm_head(double *x, int hd, const float *w, int norm_style, double eps)
+{
+    double ss = 0.0;
+    for (int d = 0; d < hd; d++)
+        ss += x[d] * x[d];
+    double r = 1.0 / sqrt(ss / (double)hd + eps);
+    for (int d = 0; d < hd; d++) {
+        double wd = (double)w[d];
+        double g = norm_style == 2 ? 1.0 + wd : wd;
+        x[d] = x[d] * r * g;
+    }
+}
+
+/*
+ * [ATT] fn rope_rotate_scaled: half-split pairs (i, i+h), h = rd/2,
+ *   x_i     <- (x_i cos t - x_{i+h} sin t) * s
+ *   x_{i+h} <- (x_i sin t + x_{i+h} cos t) * s,   t = position * f_i.
+ * Dims at or past rd pass through unchanged and unscaled ([ATT] fn
+ * finish_projection, partial RoPE).  Reading: the angle is formed in double
+ * from the f32 table entry (the page forms it in f32).
+ */
+static void rope_head(double *x, int rd, long pos, const float *inv_freq, double s)
+{
+    int h = rd / 2;
+    for (int i = 0; i < h; i++) {
+        double t = (double)pos * (double)inv_freq[i];
+        double c = cos(t), sn = sin(t);
+        double a = x[i], b = x[i + h];
+        x[i] = (a * c - b * sn) * s;
+        x[i + h] = (a * sn + b * c) * s;
+    }
+}
+
+/*
+ * Finish the rows of one projection for a set of tokens: optional per-head
+ * norm, then RoPE, then the storage rounding of the tensor that is kept
+ * (rotated Q, or the K cache row).  x: [n_tok][n_heads][hd], in place.
+ * pos[t] is the absolute position of token t.  norm_style 0 = no norm.
+ * [ATT] fn finish_projection: norm before RoPE; RoPE on the first rd dims.
+ */
+void orc_finish_heads(double *x, int n_tok, int n_heads, int hd, const int64_t *pos,
+                      const float *inv_freq, int rd, double rope_scale, int norm_style,
+                      const float *norm_w, double eps, int store_dtype)
+{
+    if (rd > hd)
+        rd = hd;
+    for (int t = 0; t < n_tok; t++) {
+        for (int h = 0; h < n_heads; h++) {
+            double *row = x + ((long)t * n_heads + h) * hd;
+            if (norm_style != 0)
+                rmsnorm_head(row, hd, norm_w, norm_style, eps);
+            rope_head(row, rd, (long)pos[t], inv_freq, rope_scale);
+            for (int d = 0; d < hd; d++)
+                row[d] = round_store(row[d], store_dtype);
+        }
+    }
+}
+
+/* ------------------------------------------------------------------------ */
+/* Attention                                                                 */
+/* ------------------------------------------------------------------------ */
+
+/*
+ * One query row against one KV group, keys 0..p inclusive:
+ *   s_j = scale * <q, K_j>,  m = max s,  e_j = exp(s_j - m),  l = sum e_j,
+ *   P_j = e_j / l,  O = sum_j P_j V_j.
+ * [ATT] fn attention_head (max-subtracted softmax, probabilities returned);
+ * [NDL] module docs: position p attends to keys at <= p.
+ * Readings: no weight is skipped (the page skips |P| < 1e-12); the softmax is
+ * normalised before the P.V sum, as in fn attention_head.
+ */
+static void attend_row(const double *q, const double *kc, const double *vc, int hd, long nkeys,
+                       double scale, double *out, double *probs, double *scratch)
+{
+    double m = -INFINITY;
+    for (long j = 0; j < nkeys; j++) {
+        const double *k = kc + j * hd;
+        double acc = 0.0;
+        for (int d = 0; d < hd; d++)
+            acc += q[d] * k[d];
+        scratch[j] = acc * scale;
+        if (scratch[j] > m)
+            m = scratch[j];
+    }
+    double l = 0.0;
+    for (long j = 0; j < nkeys; j++) {
+        scratch[j] = exp(scratch[j] - m);
+        l += scratch[j];
+    }
+    for (long j = 0; j < nkeys; j++)
+        scratch[j] /= l;
+    for (int d = 0; d < hd; d++)
+        out[d] = 0.0;
+    for (long j = 0; j < nkeys; j++) {
+        const double *v = vc + j * hd;
+        double p = scratch[j];
+        for (int d = 0; d < hd; d++)
+            out[d] += p * v[d];
+    }
+    if (probs)
+        memcpy(probs, scratch, (size_t)nkeys * sizeof(double));
+}
+
+typedef struct {
+    const double *q, *kc, *vc;
+    int n_tok, nh, nkv, hd;
+    long cap;
+    const int64_t *qpos;
+    double scale;
+    double *out, *probs;
+    long probs_ld;
+    int n_threads, tid;
+    int status;
+} attend_job;
+
+static void *attend_worker(void *arg)
+{
+    attend_job *jb = (attend_job *)arg;
+    long max_keys = 0;
+    for (int t = 0; t < jb->n_tok; t++)
+        if (jb->qpos[t] + 1 > max_keys)
+            max_keys = (long)jb->qpos[t] + 1;
+    double *scratch = (double *)malloc((size_t)(max_keys > 0 ? max_keys : 1) * sizeof(double));
+    if (!scratch) {
+        jb->status = -1;
+        return NULL;
+    }
+    int group = jb->nh / jb->nkv; /* query heads per KV head */
+    long rows = (long)jb->n_tok * jb->nh;
+    for (long r = jb->tid; r < rows; r += jb->n_threads) {
+        int t = (int)(r / jb->nh), h = (int)(r % jb->nh);
+        int g = h / group; /* [ATT] GQA mapping: query head h reads KV head h/(nh/nkv) */
+        const double *q = jb->q + r * jb->hd;
+        const double *kc = jb->kc + (long)g * jb->cap * jb->hd;
+        const double *vc = jb->vc + (long)g * jb->cap * jb->hd;
+        double *pr = jb->probs ? jb->probs + r * jb->probs_ld : NULL;
+        attend_row(q, kc, vc, jb->hd, (long)jb->qpos[t] + 1, jb->scale, jb->out + r * jb->hd,
+                   pr, scratch);
+    }
+    free(scratch);
+    jb->status = 0;
+    return NULL;
+}
+
+/*
+ * Attention for the rows of one sequence.
+ *   q     [n_tok][nh][hd]   rotated queries
+ *   kc,vc [nkv][cap][hd]    the sequence's cache; rows 0..max(qpos) are read
+ *   qpos  [n_tok]           absolute position of each query row; row t attends
+ *                           keys 0..qpos[t]
+ *   out   [n_tok][nh][hd]
+ *   probs NULL or [n_tok][nh][probs_ld]; row (t,h) gets qpos[t]+1 entries
+ * Returns 0, or -1 on bad arguments / allocation failure.
+ */
+int orc_attend(const double *q, const double *kc, const double *vc, int n_tok, int nh, int nkv,
+               int hd, long cap, const int64_t *qpos, double scale, double *out, double *probs,
+               long probs_ld, int n_threads)
+{
+    if (n_tok < 0 || nh <= 0 || nkv <= 0 || hd <= 0 || nh % nkv != 0)
+        return -1;
+    for (int t = 0; t < n_tok; t++)
+        if (qpos[t] < 0 || qpos[t] >= cap || (probs && qpos[t] + 1 > probs_ld))
+            return -1;
+    if (n_tok == 0)
+        return 0;
+    if (n_threads < 1)
+        n_threads = 1;
+    long rows = (long)n_tok * nh;
+    if (n_threads > rows)
+        n_threads = (int)rows;
+    attend_job *jobs = (attend_job *)calloc((size_t)n_threads, sizeof(attend_job));
+    pthread_t *th = (pthread_t *)calloc((size_t)n_threads, sizeof(pthread_t));
+    if (!jobs || !th) {
+        free(jobs);
+        free(th);
+        return -1;
+    }
+    int rc = 0;
+    for (int i = 0; i < n_threads; i++) {
+        attend_job j = {q, kc, vc, n_tok, nh, nkv, hd, cap, qpos, scale, out, probs, probs_ld,
+                        n_threads, i, 0};
+        jobs[i] = j;
+    }
+    int started = 0;
+    for (int i = 1; i < n_threads; i++) {
+        if (pthread_create(&th[i], NULL, attend_worker, &jobs[i]) != 0)
+            break;
+        started = i;
+    }
+    /* Rows of threads that failed to start are done by the calling thread. */
+    for (int i = started + 1; i < n_threads; i++) {
+        jobs[i].tid = i;
+        attend_worker(&jobs[i]);
+    }
+    attend_worker(&jobs[0]);
+    for (int i = 1; i <= started; i++)
+        pthread_join(th[i], NULL);
+    for (int i = 0; i < n_threads; i++)
+        if (jobs[i].status != 0)
+            rc = -1;
+    free(jobs);
+    free(th);
+    return rc;
+}

@@ -1,0 +1,427 @@
+"""Pins for the CPU oracle: worked examples, closed forms, invariants, a
+brute-force matrix softmax and a library attention routine.  Nothing here
+retypes the oracle's loops; each check comes from the pages or from the
+mathematics, and the mutation tests at the end show that a plausible mistake
+planted in a copy of the oracle's source makes at least one pin fail.
+
+Page references: [ATT] cortiq-engine 0.5.39 src/attention.rs;
+[NDL] needle-core 0.3.1 src/v2/batch.rs.
+"""
+import ctypes
+import json
+import math
+import os
+import shutil
+import subprocess
+import tempfile
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+
+GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
+
+
+# ---------------------------------------------------------------- tables
+
+def test_rope_inv_freq_closed_forms():
+    # f_i = base^(-2i/d): quarter points of a 64-dim table at base 1e4 are
+    # 10^-1, 10^-2, 10^-3 exactly (to float rounding).
+    f = oracle.rope_inv_freq(64, 1e4)
+    assert f.dtype == np.float32 and f.shape == (32,)
+    assert f[0] == np.float32(1.0)
+    assert f[8] == np.float32(0.1)
+    assert f[16] == np.float32(0.01)
+    assert f[24] == np.float32(0.001)
+    # the page's 4-dim table used by its RoPE tests: [1, 0.01]
+    assert list(oracle.rope_inv_freq(4, 1e4)) == [np.float32(1.0), np.float32(0.01)]
+    # geometric progression with ratio base^(-2/d)
+    r = f[1:].astype(np.float64) / f[:-1].astype(np.float64)
+    assert np.allclose(r, 1e4 ** (-2.0 / 64), rtol=3e-7)
+
+
+def test_rope_inv_freq_partial_rotary_uses_rotary_dim():
+    # For partial rotary the exponent denominator is the rotary dim ([ATT]
+    # QwenAttnCfg: inv_freq has rotary_dim/2 entries; yarn_inv_freq's head_dim
+    # "is the rotary dimension").  rd = 64, base 1e6: f_16 = 1e6^(-1/2).
+    f = oracle.rope_inv_freq(64, 1e6)
+    assert f.shape == (32,)
+    assert f[16] == np.float32(1e-3)
+
+
+def test_yarn_page_endpoint_contract():
+    g = json.load(open(os.path.join(GOLDEN, "yarn_tables.json")))["cases"][0]
+    f, lo, hi = oracle.yarn_inv_freq(*g["args"], return_bounds=True)
+    base = oracle.rope_inv_freq(64, 5e5)
+    assert f.shape == (32,)
+    assert (lo, hi) == (g["low"], g["high"])
+    # the page's own assertions
+    assert abs(f[0] - base[0]) < 1e-7
+    assert abs(float(f[31]) - float(base[31]) / 128.0) < 1e-9
+
+
+def test_yarn_ramp_closed_form_128k():
+    g = json.load(open(os.path.join(GOLDEN, "yarn_tables.json")))["cases"][1]
+    f, lo, hi = oracle.yarn_inv_freq(*g["args"], return_bounds=True)
+    assert (lo, hi) == (g["low"], g["high"])
+    base = oracle.rope_inv_freq(128, 1e6).astype(np.float64)
+    ratio = f.astype(np.float64) / base
+    for i, want in g["ratio_at"].items():
+        assert abs(ratio[int(i)] - want) < 2e-7, (i, ratio[int(i)], want)
+    # ramp is linear between low and high: ratio = 1 - 0.75 (i - 23)/17
+    i = np.arange(64)
+    want = np.where(i <= 23, 1.0, np.where(i >= 40, 0.25, 1.0 - 0.75 * (i - 23) / 17.0))
+    assert np.allclose(ratio, want, rtol=0, atol=3e-7)
+
+
+# ---------------------------------------------------------------- rounding
+
+def test_bf16_rounding_matches_torch_on_float32_values():
+    rng = np.random.default_rng(7)
+    x = np.concatenate([rng.standard_normal(20000) * 10 ** rng.uniform(-6, 6, 20000),
+                        np.array([0.0, -0.0, 1e-40, -3e-39, 3.3e38, -3.39e38])]).astype(np.float32)
+    ours = oracle.round_store(x.astype(np.float64), oracle.STORE_BF16)
+    ref = torch.from_numpy(x).to(torch.bfloat16).to(torch.float64).numpy()
+    assert np.array_equal(ours, ref)
+
+
+def test_bf16_rounding_ties_and_double_rounding():
+    u = 2.0 ** -8
+    cases = {
+        1.0 + u: 1.0,                       # tie, even neighbour is 1.0
+        1.0 + 3 * u: 1.0 + 4 * u,           # tie, even neighbour is 1 + 2^-6
+        1.0 + u + 2.0 ** -30: 1.0 + 2 * u,  # just above the tie: up
+        -(1.0 + u + 2.0 ** -30): -(1.0 + 2 * u),
+        3.0: 3.0,
+    }
+    for x, want in cases.items():
+        assert oracle.round_store(np.array([x]), oracle.STORE_BF16)[0] == want, x
+    # f32 storage is the plain float cast
+    assert oracle.round_store(np.array([0.1]), oracle.STORE_F32)[0] == float(np.float32(0.1))
+
+
+# ---------------------------------------------------------------- RoPE
+
+def _rope(x, pos, inv_freq, rd=None, scale=1.0):
+    a = np.asarray(x, dtype=np.float64)[None, None, :]
+    return oracle.finish_heads(a, [pos], inv_freq, rd or a.shape[-1], scale,
+                               store=oracle.STORE_F32)[0, 0]
+
+
+def _rope_exact(x, pos, inv_freq, rd=None, scale=1.0):
+    # same as _rope without the float storage rounding: oracle in double
+    a = np.asarray(x, dtype=np.float64)[None, None, :]
+    out = oracle.finish_heads(a, [pos], inv_freq, rd or a.shape[-1], scale,
+                              store=oracle.STORE_F32)
+    return out[0, 0]
+
+
+def test_rope_worked_example():
+    g = json.load(open(os.path.join(GOLDEN, "rope_worked_example.json")))
+    f = oracle.rope_inv_freq(g["head_dim"], g["base"])
+    assert np.allclose(f, g["inv_freq"], rtol=1e-7)
+    y = _rope(g["q"], g["position"], f)
+    assert np.max(np.abs(y - np.array(g["expected"]))) < g["tol"] + 2e-8
+    assert abs(np.linalg.norm(y) - g["norm"]) < 1e-6
+
+
+def test_rope_identity_at_position_zero():
+    # [ATT] test rope_identity_at_position_zero
+    q = [0.3, -0.7, 1.1, 0.2]
+    y = _rope(q, 0, oracle.rope_inv_freq(4, 1e4))
+    assert np.array_equal(y, np.array(q, dtype=np.float32).astype(np.float64))
+
+
+def test_rope_is_complex_multiplication():
+    # Independent derivation: pair (i, i+h) is the complex number
+    # x_i + i x_{i+h}, rotated by e^{i p f_i}.
+    rng = np.random.default_rng(3)
+    hd, rd = 128, 128
+    f = oracle.rope_inv_freq(rd, 1e4)
+    x = rng.standard_normal((5, 3, hd))
+    pos = np.array([0, 1, 17, 4095, 131071])
+    y = oracle.finish_heads(x, pos, f, rd, store=oracle.STORE_F32)
+    h = rd // 2
+    z = x[..., :h] + 1j * x[..., h:rd]
+    rot = np.exp(1j * pos[:, None, None] * f.astype(np.float64)[None, None, :])
+    zr = z * rot
+    want = np.concatenate([zr.real, zr.imag], axis=-1).astype(np.float32).astype(np.float64)
+    assert np.max(np.abs(y - want)) <= 2e-6
+
+
+def test_rope_partial_rotary_and_scale():
+    rng = np.random.default_rng(4)
+    hd, rd, s = 128, 64, 1.1386294
+    f = oracle.rope_inv_freq(rd, 1e6)
+    x = rng.standard_normal((4, 2, hd))
+    pos = np.array([3, 100, 5000, 8191])
+    y = oracle.finish_heads(x, pos, f, rd, rope_scale=s, store=oracle.STORE_F32)
+    # pass-through dims are untouched and unscaled
+    assert np.array_equal(y[..., rd:], x[..., rd:].astype(np.float32).astype(np.float64))
+    # rotated dims: norm of each pair multiplied by s
+    h = rd // 2
+    n_in = np.hypot(x[..., :h], x[..., h:rd])
+    n_out = np.hypot(y[..., :h], y[..., h:rd])
+    assert np.allclose(n_out, s * n_in, rtol=1e-6)
+
+
+def test_rope_relative_position_property():
+    # <R_p q, R_t k> = <R_{p-t} q, k> for unit scale and full rotary
+    rng = np.random.default_rng(5)
+    hd = 64
+    f = oracle.rope_inv_freq(hd, 1e4)
+    q = rng.standard_normal(hd)
+    k = rng.standard_normal(hd)
+    for p, t in [(10, 3), (1000, 999), (4000, 17)]:
+        a = np.dot(_rope_exact(q, p, f), _rope_exact(k, t, f))
+        b = np.dot(_rope_exact(q, p - t, f), k.astype(np.float32))
+        assert abs(a - b) < 1e-4 * (1 + abs(b))
+
+
+def test_rope_preserves_norm_random():
+    rng = np.random.default_rng(6)
+    f = oracle.rope_inv_freq(128, 1e4)
+    x = rng.standard_normal((50, 1, 128))
+    pos = rng.integers(0, 200000, 50)
+    y = oracle.finish_heads(x, pos, f, 128, store=oracle.STORE_F32)
+    assert np.allclose(np.linalg.norm(y, axis=-1), np.linalg.norm(x, axis=-1), rtol=1e-6)
+
+
+# ---------------------------------------------------------------- qk-norm
+
+def test_rmsnorm_worked_example_and_styles():
+    x = np.array([[[3.0, 4.0]]])
+    w1 = np.ones(2, dtype=np.float32)
+    f = np.zeros(1, dtype=np.float32)  # rd=2 at position 0: RoPE is the identity
+    y = oracle.finish_heads(x, [0], f, 2, norm_style=oracle.NORM_W, norm_w=w1, eps=0.0,
+                            store=oracle.STORE_F32)[0, 0]
+    # mean square 12.5
+    assert np.allclose(y, [3 / math.sqrt(12.5), 4 / math.sqrt(12.5)], rtol=1e-7)
+    # x * r * (1 + 0) == x * r * 1
+    y2 = oracle.finish_heads(x, [0], f, 2, norm_style=oracle.NORM_1PW,
+                             norm_w=np.zeros(2, dtype=np.float32), eps=0.0,
+                             store=oracle.STORE_F32)[0, 0]
+    assert np.array_equal(y, y2)
+
+
+def test_rmsnorm_unit_rms_then_rope_order():
+    # Norm first, then RoPE ([ATT] fn finish_projection: "qk-norm before RoPE").
+    rng = np.random.default_rng(8)
+    hd, rd = 128, 64
+    x = rng.standard_normal((3, 5, hd))
+    w = (1.0 + 0.1 * rng.standard_normal(hd)).astype(np.float32)
+    f = oracle.rope_inv_freq(rd, 1e6)
+    pos = np.array([0, 7, 300])
+    ones = np.ones(hd, dtype=np.float32)
+    y0 = oracle.finish_heads(x, [0, 0, 0], f, rd, norm_style=oracle.NORM_W, norm_w=ones,
+                             eps=0.0, store=oracle.STORE_F32)
+    assert np.allclose(np.sqrt(np.mean(y0 ** 2, axis=-1)), 1.0, rtol=1e-6)
+    y = oracle.finish_heads(x, pos, f, rd, norm_style=oracle.NORM_W, norm_w=w, eps=1e-6,
+                            store=oracle.STORE_F32)
+    # independent: normalise with numpy, rotate as complex numbers
+    xn = x / np.sqrt(np.mean(x ** 2, axis=-1, keepdims=True) + 1e-6) * w.astype(np.float64)
+    h = rd // 2
+    z = (xn[..., :h] + 1j * xn[..., h:rd]) * np.exp(1j * pos[:, None, None] * f[None, None, :].astype(np.float64))
+    want = np.concatenate([z.real, z.imag, xn[..., rd:]], axis=-1)
+    assert np.max(np.abs(y - want)) < 2e-6
+
+
+# ---------------------------------------------------------------- attention
+
+def test_position_zero_returns_v0():
+    rng = np.random.default_rng(9)
+    q = rng.standard_normal((1, 4, 16))
+    k = rng.standard_normal((2, 1, 16))
+    v = rng.standard_normal((2, 1, 16))
+    out, probs = oracle.attend(q, k, v, [0], 0.25, want_probs=True)
+    for h in range(4):
+        assert np.array_equal(out[0, h], v[h // 2, 0])
+        assert probs[0, h, 0] == 1.0
+
+
+def test_attention_head_uniform_page_example():
+    # [ATT] test attention_head_uniform: equal keys, V rows e0, e1, e2 ->
+    # output exactly 1/3 on the first three dims, probabilities sum to 1.
+    q = np.ones((1, 1, 4))
+    k = np.ones((1, 3, 4))
+    v = np.eye(3, 4)[None]
+    out, probs = oracle.attend(q, k, v, [2], 0.5, want_probs=True)
+    assert np.allclose(out[0, 0], [1 / 3, 1 / 3, 1 / 3, 0.0], atol=1e-15)
+    assert abs(probs[0, 0].sum() - 1.0) < 1e-15
+
+
+def _brute(q, k, v, s0, scale):
+    """Full-matrix causal softmax attention with a -inf upper triangle aligned
+    to the bottom right (query row t sits at position s0 + t)."""
+    T, nh, hd = q.shape
+    nkv, N, _ = k.shape
+    G = nh // nkv
+    out = np.zeros_like(q)
+    P_all = np.zeros((T, nh, N))
+    for h in range(nh):
+        S = (q[:, h, :] @ k[h // G].T) * scale
+        mask = np.arange(N)[None, :] > (s0 + np.arange(T))[:, None]
+        S[mask] = -np.inf
+        P = np.exp(S - S.max(axis=1, keepdims=True))
+        P /= P.sum(axis=1, keepdims=True)
+        out[:, h, :] = P @ v[h // G]
+        P_all[:, h, :] = P
+    return out, P_all
+
+
+@pytest.mark.parametrize("s0,T", [(0, 9), (5, 7), (30, 1)])
+def test_brute_force_matrix_softmax(s0, T):
+    rng = np.random.default_rng(10 + s0)
+    nh, nkv, hd = 6, 2, 8
+    q = rng.standard_normal((T, nh, hd))
+    k = rng.standard_normal((nkv, s0 + T, hd))
+    v = rng.standard_normal((nkv, s0 + T, hd))
+    pos = s0 + np.arange(T)
+    out, probs = oracle.attend(q, k, v, pos, 0.35, want_probs=True)
+    want, P = _brute(q, k, v, s0, 0.35)
+    assert np.max(np.abs(out - want)) < 1e-13
+    assert np.max(np.abs(probs - P[:, :, :probs.shape[2]])) < 1e-14
+    assert np.allclose(probs.sum(axis=-1), 1.0, atol=1e-13)
+
+
+def test_gqa_equals_mha_with_repeated_kv():
+    rng = np.random.default_rng(11)
+    T, nh, nkv, hd = 5, 8, 2, 16
+    q = rng.standard_normal((T, nh, hd))
+    k = rng.standard_normal((nkv, T, hd))
+    v = rng.standard_normal((nkv, T, hd))
+    pos = np.arange(T)
+    a, _ = oracle.attend(q, k, v, pos, 0.25)
+    b, _ = oracle.attend(q, np.repeat(k, nh // nkv, axis=0), np.repeat(v, nh // nkv, axis=0),
+                         pos, 0.25)
+    assert np.array_equal(a, b)
+
+
+def test_library_sdpa_special_case():
+    # s0 = 0, one chunk: torch's scaled_dot_product_attention in float64 with an
+    # explicit causal boolean mask is the same computation.
+    rng = np.random.default_rng(12)
+    T, nh, nkv, hd = 33, 4, 4, 32
+    q = rng.standard_normal((T, nh, hd))
+    k = rng.standard_normal((nkv, T, hd))
+    v = rng.standard_normal((nkv, T, hd))
+    out, _ = oracle.attend(q, k, v, np.arange(T), 1 / math.sqrt(hd))
+    tq = torch.from_numpy(q).permute(1, 0, 2)[None]
+    tk = torch.from_numpy(k)[None]
+    tv = torch.from_numpy(v)[None]
+    mask = torch.ones(T, T, dtype=torch.bool).tril()
+    ref = torch.nn.functional.scaled_dot_product_attention(tq, tk, tv, attn_mask=mask)
+    assert np.max(np.abs(out - ref[0].permute(1, 0, 2).numpy())) < 1e-13
+
+
+def _c0_inputs():
+    from chunked_prefill_causal_rope_amd import workloads as wl
+    w = wl.CONFIGS["c0_f32_small"]
+    d = wl.gen_prefill(w)
+    return w, d
+
+
+def test_chunked_equals_sequential_bit_exact():
+    # [NDL] module docs: batched prefill must reproduce the sequential path
+    # exactly; [ATT] test attention_pair_equals_two_sequential_calls.
+    w, d = _c0_inputs()
+    f = oracle.rope_inv_freq(w.rd, w.base)
+    args = dict(inv_freq=f, rotary_dim=w.rd, scale=w.scale, store=oracle.STORE_F32)
+    a = oracle.prefill_sequence(d["q"].numpy(), d["k"].numpy(), d["v"].numpy(), w.chunk, **args)
+    b = oracle.prefill_sequence(d["q"].numpy(), d["k"].numpy(), d["v"].numpy(), 1,
+                                want_probs=True, **args)
+    c = oracle.prefill_sequence(d["q"].numpy(), d["k"].numpy(), d["v"].numpy(), 64, **args)
+    for x in (a, c):
+        assert np.array_equal(x["out"], b["out"])
+        assert np.array_equal(x["k_cache"], b["k_cache"])
+        assert np.array_equal(x["v_cache"], b["v_cache"])
+    # per-position probabilities: rows sum to 1, zero past the row's position
+    P = b["probs"]
+    assert np.allclose(P.sum(-1), 1.0, atol=1e-12)
+    T = P.shape[0]
+    assert np.all(P[np.triu_indices(T, 1)[0], :, np.triu_indices(T, 1)[1]] == 0)
+    # continuing from a saved cache equals the one-shot run
+    half = oracle.prefill_sequence(d["q"][:40].numpy(), d["k"][:40].numpy(), d["v"][:40].numpy(),
+                                   16, cap=64, **args)
+    rest = oracle.prefill_sequence(d["q"][40:].numpy(), d["k"][40:].numpy(), d["v"][40:].numpy(),
+                                   16, cap=64, start=40, k_cache=half["k_cache"],
+                                   v_cache=half["v_cache"], **args)
+    assert np.array_equal(np.concatenate([half["out"], rest["out"]]), a["out"])
+
+
+def test_prefill_matches_brute_force_end_to_end():
+    w, d = _c0_inputs()
+    f = oracle.rope_inv_freq(w.rd, w.base)
+    r = oracle.prefill_sequence(d["q"].numpy(), d["k"].numpy(), d["v"].numpy(), w.chunk, f,
+                                w.rd, w.scale, oracle.STORE_F32)
+    want, _ = _brute(r["q_rot"], r["k_cache"], r["v_cache"], 0, w.scale)
+    assert np.max(np.abs(r["out"] - want)) < 1e-12
+    # cache rows: V is a bit copy of the input, K is the rotated input
+    assert np.array_equal(r["v_cache"], d["v"].numpy().transpose(1, 0, 2).astype(np.float64))
+    h = w.rd // 2
+    x = d["k"].numpy().astype(np.float64)
+    z = (x[..., :h] + 1j * x[..., h:]) * np.exp(1j * np.arange(64)[:, None, None] * f[None, None, :].astype(np.float64))
+    kr = np.concatenate([z.real, z.imag], -1).astype(np.float32).transpose(1, 0, 2)
+    assert np.max(np.abs(r["k_cache"] - kr)) < 1e-6
+
+
+# ---------------------------------------------------------------- mutations
+# Plant a mistake in a copy of oracle.c, build it, and show that a pin above
+# catches it.  The real oracle is untouched.
+
+MUTATIONS = {
+    "mask_off_by_one": ("(long)jb->qpos[t] + 1, jb->scale", "(long)jb->qpos[t], jb->scale"),
+    "gqa_modulo": ("int g = h / group;", "int g = h % jb->nkv;"),
+    "rope_sign": ("x[i + h] = (a * sn + b * c) * s;", "x[i + h] = (b * c - a * sn) * s;"),
+    "rope_interleaved": ("double a = x[i], b = x[i + h];", "double a = x[2 * i], b = x[2 * i + 1];"),
+    "norm_without_mean": ("double r = 1.0 / sqrt(ss / (double)hd + eps);", "double r = 1.0 / sqrt(ss + eps);"),
+    "probs_not_normalised": ("scratch[j] /= l;", "scratch[j] /= (l + 1e-3);"),
+    "bf16_truncation": ("double r = nearbyint(ldexp(x, -q));", "double r = trunc(ldexp(x, -q));"),
+}
+
+
+def _build_mutant(name, tmp):
+    src = open(os.path.join(os.path.dirname(oracle.__file__), "oracle.c")).read()
+    old, new = MUTATIONS[name]
+    assert src.count(old) == 1, name
+    path = os.path.join(tmp, name + ".c")
+    open(path, "w").write(src.replace(old, new))
+    so = os.path.join(tmp, name + ".so")
+    subprocess.check_call(["gcc", "-O2", "-std=c11", "-ffp-contract=off", "-fPIC", "-shared",
+                           path, "-o", so, "-lm", "-lpthread"])
+    return so
+
+
+def _pins_pass():
+    """Run the pins that guard the planted mistakes; True when all pass."""
+    checks = [test_rope_worked_example, test_rope_is_complex_multiplication,
+              test_rmsnorm_worked_example_and_styles, test_rmsnorm_unit_rms_then_rope_order,
+              lambda: test_brute_force_matrix_softmax(5, 7), test_gqa_equals_mha_with_repeated_kv,
+              test_attention_head_uniform_page_example, test_bf16_rounding_matches_torch_on_float32_values]
+    for c in checks:
+        try:
+            c()
+        except AssertionError:
+            return False
+    return True
+
+
+@pytest.mark.parametrize("name", sorted(MUTATIONS))
+def test_planted_mistake_is_caught(name, monkeypatch):
+    if shutil.which("gcc") is None:
+        pytest.skip("gcc not available")
+    tmp = tempfile.mkdtemp()
+    try:
+        so = _build_mutant(name, tmp)
+        saved = oracle._lib
+        oracle._lib = None
+        monkeypatch.setattr(oracle, "_LIB_PATH", so)
+        monkeypatch.setattr(oracle, "_SRC", so)  # never rebuild the mutant
+        try:
+            assert not _pins_pass(), f"mutation {name} slipped past every pin"
+        finally:
+            oracle._lib = saved
+    finally:
+        shutil.rmtree(tmp, ignore_errors=True)
