@@ -1,0 +1,295 @@
+"""Benchmark of the chunked-prefill attention hot path on one MI355X.
+
+A step is one pass of the whole path over one batch of synthetic input:
+  prefill workloads -- every chunk of the prompt(s): finish Q (RoPE), append
+                       K/V (RoPE) to the cache, causal attention of the chunk;
+  decode workload   -- finish q, append k/v at ctx-1, attention over the
+                       context with probabilities.
+Inputs are resident in HBM before timing starts.  The timed steps replay a
+HIP graph of one step (the chunk loop is launch-bound at small chunks); the
+graph was checked against eager execution by the test suite.
+
+Prints ONE JSON line.  `value` is the whole-step throughput (algorithmic
+FLOP/s for prefill, K/V bytes read per second for decode); `roofline` is the
+attention call measured per launch with HIP events on its stream;
+`cpu_baseline` is the CPU oracle timed on a bounded sample of the same
+workload on this host.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import math
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+METRIC = "prefill attn TFLOP/s (% MFMA peak); decode KV-read GB/s (% HBM peak)"
+PEAK_MFMA_BF16_TFLOPS = 2500.0     # MI355X dense bf16 matrix peak
+PEAK_VALU_F32_TFLOPS = 157.3
+PEAK_HBM_GBS = 8000.0              # MI355X HBM3E
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=10)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--workload", default="c1_llama_prefill")
+    ap.add_argument("--no-decode", action="store_true", help="skip the secondary decode line")
+    ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
+    ap.add_argument("--cpu-seconds", type=float, default=12.0)
+    ap.add_argument("--eager", action="store_true", help="time eager launches, not a graph")
+    return ap.parse_args()
+
+
+def step_flops(w, run, i):
+    """Algorithmic causal FLOPs of one chunk call: 4*hd per (row, head, key)."""
+    b = run.steps[i]["batch"]
+    tot = 0
+    for s, n in zip(b.starts, b.lens):
+        # rows at positions s..s+n-1 see p+1 keys each
+        tot += n * s + n * (n + 1) // 2
+    return 4.0 * w.head_dim * w.n_heads * tot
+
+
+def time_launches(torch, calls, stream):
+    """Per-launch durations (ms) of `calls`, each bracketed by HIP events on
+    `stream`; the GPU is first held by a spin so every launch is queued
+    back to back and no host gap lands inside a bracket."""
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+           for _ in calls]
+    with torch.cuda.stream(stream):
+        if hasattr(torch.cuda, "_sleep"):
+            torch.cuda._sleep(20_000_000)
+        for (e0, e1), fn in zip(evs, calls):
+            e0.record(stream)
+            fn()
+            e1.record(stream)
+    torch.cuda.synchronize()
+    return [e0.elapsed_time(e1) for e0, e1 in evs]
+
+
+def graph_of(torch, fn, stream):
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.stream(stream):
+        fn()
+        torch.cuda.synchronize()
+        with torch.cuda.graph(g, stream=stream):
+            fn()
+    torch.cuda.synchronize()
+    return g
+
+
+def time_steps(torch, step_fn, steps, warmup, eager, stream):
+    if eager:
+        run = step_fn
+    else:
+        g = graph_of(torch, step_fn, stream)
+        run = g.replay
+    with torch.cuda.stream(stream):
+        for _ in range(warmup):
+            run()
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        for _ in range(steps):
+            run()
+        torch.cuda.synchronize()
+        t1 = time.perf_counter()
+    return (t1 - t0) / steps
+
+
+# ------------------------------------------------------------------ CPU baseline
+
+def cpu_baseline_prefill(w, d, budget_s):
+    """The oracle, as it stands, on the last chunks of the first prompt (the
+    costliest rows), walking backwards until about budget_s seconds of CPU
+    work; reports its algorithmic FLOP rate in TFLOP/s."""
+    import numpy as np
+
+    import oracle
+    f = (oracle.yarn_inv_freq(w.rd, w.base, *w.yarn) if w.yarn is not None
+         else oracle.rope_inv_freq(w.rd, w.base))
+    store = oracle.STORE_BF16 if w.dtype == "bf16" else oracle.STORE_F32
+    n = d["lengths"][0]
+    threads = oracle.default_threads()
+    norm = dict(norm_style=w.norm_style, eps=w.norm_eps)
+    t_start = time.perf_counter()
+    flops = 0.0
+    rows = 0
+    chunks = 0
+    c_end = n
+    kc = vc = None
+    while c_end > 0 and time.perf_counter() - t_start < budget_s:
+        c0 = max(0, c_end - w.chunk)
+        if kc is None:
+            kn = dict(norm, norm_w=d["k_norm_w"].numpy()) if w.norm_style else {}
+            k = oracle.finish_heads(d["k"][:c_end].float().numpy(), np.arange(c_end), f, w.rd,
+                                    w.rope_scale, store=store, **kn)
+            kc = np.ascontiguousarray(k.transpose(1, 0, 2))
+            vc = np.ascontiguousarray(d["v"][:c_end].float().numpy().astype(np.float64)
+                                      .transpose(1, 0, 2))
+        qn = dict(norm, norm_w=d["q_norm_w"].numpy()) if w.norm_style else {}
+        pos = np.arange(c0, c_end)
+        q = oracle.finish_heads(d["q"][c0:c_end].float().numpy(), pos, f, w.rd, w.rope_scale,
+                                store=store, **qn)
+        oracle.attend(q, kc, vc, pos, w.scale, n_threads=threads)
+        flops += 4.0 * w.head_dim * w.n_heads * float(np.sum(pos + 1))
+        rows += c_end - c0
+        chunks += 1
+        c_end = c0
+    dt = time.perf_counter() - t_start
+    return {"value": flops / dt / 1e12, "unit": "TFLOP/s", "cores": threads, "kind": "oracle",
+            "sample": f"last {chunks} chunk(s) ({rows} positions x {w.n_heads} heads) of prompt 0, "
+                      f"f64 oracle incl. K/Q RoPE, {dt:.1f} s"}
+
+
+def cpu_baseline_decode(w, d, budget_s):
+    import numpy as np
+
+    import oracle
+    f = oracle.rope_inv_freq(w.rd, w.base)
+    threads = oracle.default_threads()
+    t_start = time.perf_counter()
+    nbytes = 0.0
+    seqs = 0
+    for b, c in enumerate(d["ctx"]):
+        if time.perf_counter() - t_start >= budget_s:
+            break
+        pos = np.array([c - 1])
+        kc = d["k_cache"][b, :, :c].float().cpu().numpy().astype(np.float64)
+        vc = d["v_cache"][b, :, :c].float().cpu().numpy().astype(np.float64)
+        kc[:, c - 1] = oracle.finish_heads(d["k"][b:b + 1].float().cpu().numpy(), pos, f, w.rd,
+                                           store=oracle.STORE_BF16)[0]
+        vc[:, c - 1] = d["v"][b].float().cpu().numpy()
+        q = oracle.finish_heads(d["q"][b:b + 1].float().cpu().numpy(), pos, f, w.rd,
+                                store=oracle.STORE_BF16)
+        oracle.attend(q, kc, vc, pos, w.scale, want_probs=True, n_threads=threads)
+        nbytes += 2.0 * c * w.n_kv * w.head_dim * 2
+        seqs += 1
+    dt = time.perf_counter() - t_start
+    return {"value": nbytes / dt / 1e9, "unit": "GB/s", "cores": threads, "kind": "oracle",
+            "sample": f"{seqs} of {len(d['ctx'])} sequences (all heads, with probabilities), "
+                      f"f64 oracle, {dt:.1f} s"}
+
+
+# ------------------------------------------------------------------ workloads
+
+def bench_prefill(torch, w, args, stream):
+    from chunked_prefill_causal_rope_amd import runner, workloads as wl
+    dev = "cuda"
+    d = wl.gen_prefill(w, device=dev)
+    run = runner.ChunkedPrefill(w, d, device=dev)
+    n_steps = len(run.steps)
+    total_flops = wl.prefill_flops(w, d["lengths"])
+    sec = time_steps(torch, run.run_all, args.steps, args.warmup, args.eager, stream)
+    value = total_flops / sec / 1e12
+    # dominant kernel: the attention call, per launch, with the cache filled
+    per_launch = []
+    for _ in range(2):
+        per_launch = time_launches(torch, [lambda i=i: run.attend_step(i) for i in range(n_steps)],
+                                   stream)
+    flops = [step_flops(w, run, i) for i in range(n_steps)]
+    avg_ms = sum(per_launch) / n_steps
+    achieved = sum(flops) / (sum(per_launch) * 1e-3) / 1e12
+    splits = []
+    from chunked_prefill_causal_rope_amd import api
+    for s in run.steps:
+        wsb = api.prefill_workspace_bytes(s["batch"], w.n_heads, w.n_kv, w.head_dim)
+        per = s["batch"].n_tok * w.n_heads * (w.head_dim + 4) * 4
+        splits.append(max(1, wsb // per) if wsb else 1)
+    roof = {"bound": "mfma", "achieved": round(achieved, 2), "peak": PEAK_MFMA_BF16_TFLOPS,
+            "unit": "TFLOP/s", "frac": round(achieved / PEAK_MFMA_BF16_TFLOPS, 4),
+            "traffic": None,
+            "kernel": "attn_prefill_chunk (prefill_bf16_kernel"
+                      + (" + prefill_combine_kernel" if max(splits) > 1 else "") + ")",
+            "launches": n_steps, "avg_launch_ms": round(avg_ms, 4),
+            "flop_per_launch": round(sum(flops) / n_steps), "max_key_splits": int(max(splits))}
+    cfg = {"workload": w.name, "n_heads": w.n_heads, "n_kv": w.n_kv, "head_dim": w.head_dim,
+           "n_seq": w.n_seq, "tokens": sum(d["lengths"]), "chunk": w.chunk,
+           "chunks": n_steps, "rotary_dim": w.rd, "yarn": w.yarn is not None,
+           "qk_norm": bool(w.norm_style), "graph": not args.eager}
+    out = {"metric": METRIC, "value": round(value, 3), "unit": "TFLOP/s", "n_gpus": 1,
+           "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(sec * 1e3, 4),
+           "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+           "dtype": "bf16" if w.dtype == "bf16" else "f32", "data": "synthetic", "config": cfg,
+           "roofline": roof}
+    return out, d
+
+
+def decode_bytes(w, ctx):
+    kv = 2.0 * sum(ctx) * w.n_kv * w.head_dim * 2
+    probs = 4.0 * sum(ctx) * w.n_heads if w.want_probs else 0.0
+    small = len(ctx) * w.n_heads * w.head_dim * (2 + 4)
+    return kv, kv + probs + small
+
+
+def bench_decode(torch, w, args, stream):
+    from chunked_prefill_causal_rope_amd import runner, workloads as wl
+    d = wl.gen_decode(w, device="cuda")
+    step = runner.DecodeStep(w, d, device="cuda")
+    sec = time_steps(torch, step.run, args.steps, args.warmup, args.eager, stream)
+    kv, alg = decode_bytes(w, d["ctx"])
+    per_launch = []
+    for _ in range(2):
+        per_launch = time_launches(torch, [step.attend] * max(3, args.steps), stream)
+    avg_ms = sum(per_launch) / len(per_launch)
+    achieved = alg / (avg_ms * 1e-3) / 1e9
+    roof = {"bound": "hbm", "achieved": round(achieved, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
+            "frac": round(achieved / PEAK_HBM_GBS, 4), "traffic": None,
+            "kernel": "attn_decode (decode_split_kernel + decode_combine_kernel)",
+            "avg_launch_ms": round(avg_ms, 4), "bytes_per_launch": alg,
+            "kv_read_gbs": round(kv / (avg_ms * 1e-3) / 1e9, 1)}
+    out = {"metric": "decode KV-read GB/s", "value": round(kv / sec / 1e9, 1), "unit": "GB/s",
+           "ms_per_step": round(sec * 1e3, 4), "workload": w.name,
+           "config": {"n_seq": w.n_seq, "n_heads": w.n_heads, "n_kv": w.n_kv,
+                      "head_dim": w.head_dim, "ctx_total": sum(d["ctx"]),
+                      "probs": w.want_probs},
+           "roofline": roof}
+    return out, d
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU only; --gpus {args.gpus} is not supported "
+              "(the path shards by KV head or by sequence with no exchange; see DESIGN.md)",
+              file=sys.stderr)
+        sys.exit(2)
+    import torch
+
+    from chunked_prefill_causal_rope_amd import workloads as wl
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        sys.exit(2)
+    torch.cuda.set_device(0)
+    stream = torch.cuda.Stream()
+    w = wl.CONFIGS[args.workload]
+    if w.decode:
+        res, d = bench_decode(torch, w, args, stream)
+        res = {"metric": METRIC, "value": res["value"], "unit": "GB/s", "n_gpus": 1,
+               "steps": args.steps, "warmup": args.warmup, "ms_per_step": res["ms_per_step"],
+               "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "bf16",
+               "data": "synthetic", "config": dict(res["config"], workload=w.name),
+               "roofline": res["roofline"]}
+        if not args.no_cpu:
+            res["cpu_baseline"] = cpu_baseline_decode(w, d, args.cpu_seconds)
+    else:
+        res, d = bench_prefill(torch, w, args, stream)
+        if not args.no_cpu:
+            dc = {k: (v.cpu() if hasattr(v, "cpu") else v) for k, v in d.items()}
+            res["cpu_baseline"] = cpu_baseline_prefill(w, dc, args.cpu_seconds)
+        del d
+        if not args.no_decode:
+            torch.cuda.empty_cache()
+            dec, _ = bench_decode(torch, wl.CONFIGS["c2_decode"], args, stream)
+            res["decode"] = dec
+    print(json.dumps(res), flush=True)
+
+
+if __name__ == "__main__":
+    main()

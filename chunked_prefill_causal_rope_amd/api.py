@@ -1,0 +1,213 @@
+"""Thin ctypes binding of libattn.so (the C ABI in include/attn.h).
+
+Argument marshalling only: tensors are checked for device, dtype, shape and
+contiguity, then their device pointers and the current torch stream are handed
+to the library.  Every step of the path runs in the library's HIP kernels; if
+the library is missing this module raises, it never computes anything itself.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+import torch
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(HERE, "libattn.so")
+
+F32, BF16 = 0, 1
+NORM_NONE, NORM_W, NORM_1PW = 0, 1, 2
+_STATUS = {0: "ok", -1: "invalid argument", -2: "exceeds cache capacity",
+           -3: "unsupported configuration", -4: "device launch failed"}
+
+_lib = None
+
+EXPORTS = ("attn_rope_inv_freq", "attn_yarn_inv_freq", "attn_rope_apply", "attn_kv_append",
+           "attn_prefill_chunk", "attn_prefill_workspace_bytes", "attn_decode",
+           "attn_decode_workspace_bytes", "attn_status_string", "attn_version")
+
+
+class AttnError(RuntimeError):
+    def __init__(self, fn: str, status: int):
+        super().__init__(f"{fn}: {_STATUS.get(status, 'unknown status')} ({status})")
+        self.status = status
+
+
+def lib() -> ctypes.CDLL:
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(LIB_PATH):
+        raise RuntimeError(f"{LIB_PATH} is not built: run __graft_entry__.build() first "
+                           "(there is no fallback implementation)")
+    L = ctypes.CDLL(LIB_PATH)
+    i, d, f, vp, sz = ctypes.c_int, ctypes.c_double, ctypes.c_float, ctypes.c_void_p, ctypes.c_size_t
+    fp = ctypes.POINTER(ctypes.c_float)
+    L.attn_rope_inv_freq.argtypes = [i, d, fp]
+    L.attn_yarn_inv_freq.argtypes = [i, d, d, i, d, d, fp]
+    L.attn_rope_apply.argtypes = [vp, vp, i, i, i, i, i, vp, vp, i, vp, i, f, i, vp, d, vp]
+    L.attn_kv_append.argtypes = [vp, vp, i, i, i, i, i, vp, vp, i, vp, vp, i, i, vp, i, f, i, vp,
+                                 d, vp]
+    L.attn_prefill_chunk.argtypes = [vp, vp, vp, i, i, i, i, i, i, i, vp, vp, i, i, f, vp, vp, sz,
+                                     vp]
+    L.attn_prefill_workspace_bytes.argtypes = [i, i, i, i, i, i, i]
+    L.attn_prefill_workspace_bytes.restype = sz
+    L.attn_decode.argtypes = [vp, vp, vp, i, i, i, i, i, i, vp, i, f, vp, vp, i, vp, sz, vp]
+    L.attn_decode_workspace_bytes.argtypes = [i, i, i, i, i]
+    L.attn_decode_workspace_bytes.restype = sz
+    L.attn_status_string.argtypes = [i]
+    L.attn_status_string.restype = ctypes.c_char_p
+    L.attn_version.restype = ctypes.c_char_p
+    for name in ("attn_rope_inv_freq", "attn_yarn_inv_freq", "attn_rope_apply", "attn_kv_append",
+                 "attn_prefill_chunk", "attn_decode"):
+        getattr(L, name).restype = i
+    _lib = L
+    return L
+
+
+def _check(fn: str, st: int):
+    if st != 0:
+        raise AttnError(fn, st)
+
+
+def _dtype_code(t: torch.Tensor) -> int:
+    if t.dtype == torch.float32:
+        return F32
+    if t.dtype == torch.bfloat16:
+        return BF16
+    raise TypeError(f"unsupported dtype {t.dtype}")
+
+
+def _dev(t: torch.Tensor | None, name: str, dtype=None):
+    if t is None:
+        return None
+    if not t.is_cuda:
+        raise ValueError(f"{name} must be a device tensor")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    if dtype is not None and t.dtype != dtype:
+        raise TypeError(f"{name} must be {dtype}, got {t.dtype}")
+    return t.data_ptr()
+
+
+def _stream():
+    return ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
+
+
+# ---------------------------------------------------------------- tables
+
+def rope_inv_freq(rotary_dim: int, base: float) -> torch.Tensor:
+    out = torch.zeros(rotary_dim // 2, dtype=torch.float32)
+    _check("attn_rope_inv_freq", lib().attn_rope_inv_freq(
+        rotary_dim, base, ctypes.cast(out.data_ptr(), ctypes.POINTER(ctypes.c_float))))
+    return out
+
+
+def yarn_inv_freq(rotary_dim: int, base: float, factor: float, orig_max_pos: int,
+                  beta_fast: float, beta_slow: float) -> torch.Tensor:
+    out = torch.zeros(rotary_dim // 2, dtype=torch.float32)
+    _check("attn_yarn_inv_freq", lib().attn_yarn_inv_freq(
+        rotary_dim, base, factor, orig_max_pos, beta_fast, beta_slow,
+        ctypes.cast(out.data_ptr(), ctypes.POINTER(ctypes.c_float))))
+    return out
+
+
+# ---------------------------------------------------------------- batch descriptor
+
+class Batch:
+    """Varlen descriptor: sequences b = 0..n_seq-1 contribute lens[b] packed
+    rows starting at absolute position starts[b]."""
+
+    def __init__(self, starts: list[int], lens: list[int], device="cuda"):
+        assert len(starts) == len(lens)
+        self.starts = [int(s) for s in starts]
+        self.lens = [int(n) for n in lens]
+        cu = [0]
+        for n in self.lens:
+            cu.append(cu[-1] + n)
+        self.cu_list = cu
+        self.n_seq = len(lens)
+        self.n_tok = cu[-1]
+        self.max_chunk = max(self.lens) if self.lens else 0
+        self.max_end = max((s + n for s, n in zip(self.starts, self.lens)), default=0)
+        self.cu_seq = torch.tensor(cu, dtype=torch.int32, device=device)
+        self.start = torch.tensor(self.starts or [0], dtype=torch.int32, device=device)
+
+
+# ---------------------------------------------------------------- entry points
+
+def rope_apply(x: torch.Tensor, y: torch.Tensor, batch: Batch, inv_freq: torch.Tensor,
+               rotary_dim: int, rope_scale: float = 1.0, norm: int = NORM_NONE,
+               norm_w: torch.Tensor | None = None, eps: float = 1e-6):
+    n_tok, n_heads, hd = x.shape
+    assert y.shape == x.shape and y.dtype == x.dtype and n_tok >= batch.n_tok
+    st = lib().attn_rope_apply(
+        _dev(x, "x"), _dev(y, "y"), _dtype_code(x), n_tok, n_heads, hd, batch.n_seq,
+        _dev(batch.cu_seq, "cu_seq", torch.int32), _dev(batch.start, "start", torch.int32),
+        batch.max_chunk, _dev(inv_freq, "inv_freq", torch.float32) if rotary_dim else None,
+        rotary_dim, rope_scale, norm, _dev(norm_w, "norm_w", torch.float32), eps, _stream())
+    _check("attn_rope_apply", st)
+
+
+def kv_append(k_cache: torch.Tensor, v_cache: torch.Tensor, k_new: torch.Tensor,
+              v_new: torch.Tensor, batch: Batch, inv_freq: torch.Tensor, rotary_dim: int,
+              rope_scale: float = 1.0, norm: int = NORM_NONE,
+              norm_w: torch.Tensor | None = None, eps: float = 1e-6):
+    n_seq_c, n_kv, cap, hd = k_cache.shape
+    assert v_cache.shape == k_cache.shape and n_seq_c >= batch.n_seq
+    n_tok = k_new.shape[0]
+    assert k_new.shape == (n_tok, n_kv, hd) and v_new.shape == k_new.shape
+    assert k_new.dtype == k_cache.dtype == v_cache.dtype == v_new.dtype
+    st = lib().attn_kv_append(
+        _dev(k_cache, "k_cache"), _dev(v_cache, "v_cache"), _dtype_code(k_cache), batch.n_seq,
+        n_kv, hd, cap, _dev(k_new, "k_new"), _dev(v_new, "v_new"), n_tok,
+        _dev(batch.cu_seq, "cu_seq", torch.int32), _dev(batch.start, "start", torch.int32),
+        batch.max_chunk, batch.max_end,
+        _dev(inv_freq, "inv_freq", torch.float32) if rotary_dim else None, rotary_dim,
+        rope_scale, norm, _dev(norm_w, "norm_w", torch.float32), eps, _stream())
+    _check("attn_kv_append", st)
+
+
+def prefill_workspace_bytes(batch: Batch, n_heads: int, n_kv: int, head_dim: int) -> int:
+    return int(lib().attn_prefill_workspace_bytes(batch.n_seq, n_heads, n_kv, head_dim,
+                                                  batch.n_tok, batch.max_chunk, batch.max_end))
+
+
+def prefill_chunk(q: torch.Tensor, k_cache: torch.Tensor, v_cache: torch.Tensor, batch: Batch,
+                  scale: float, out: torch.Tensor, workspace: torch.Tensor | None = None):
+    n_tok, nh, hd = q.shape
+    n_seq_c, n_kv, cap, hd2 = k_cache.shape
+    assert hd2 == hd and out.shape == (n_tok, nh, hd) and out.dtype == torch.float32
+    assert n_seq_c >= batch.n_seq and n_tok >= batch.n_tok
+    ws = _dev(workspace, "workspace") if workspace is not None else None
+    wsb = workspace.numel() * workspace.element_size() if workspace is not None else 0
+    st = lib().attn_prefill_chunk(
+        _dev(q, "q"), _dev(k_cache, "k_cache"), _dev(v_cache, "v_cache"), _dtype_code(q),
+        batch.n_seq, nh, n_kv, hd, cap, n_tok, _dev(batch.cu_seq, "cu_seq", torch.int32),
+        _dev(batch.start, "start", torch.int32), batch.max_chunk, batch.max_end, scale,
+        _dev(out, "out"), ws, wsb, _stream())
+    _check("attn_prefill_chunk", st)
+
+
+def decode_workspace_bytes(n_seq: int, n_heads: int, n_kv: int, head_dim: int, max_ctx: int) -> int:
+    return int(lib().attn_decode_workspace_bytes(n_seq, n_heads, n_kv, head_dim, max_ctx))
+
+
+def decode(q: torch.Tensor, k_cache: torch.Tensor, v_cache: torch.Tensor, ctx: torch.Tensor,
+           max_ctx: int, scale: float, out: torch.Tensor, probs: torch.Tensor | None = None,
+           workspace: torch.Tensor | None = None):
+    n_seq, nh, hd = q.shape
+    n_seq_c, n_kv, cap, hd2 = k_cache.shape
+    assert hd2 == hd and n_seq_c >= n_seq and out.shape == (n_seq, nh, hd)
+    assert ctx.shape == (n_seq,) and ctx.dtype == torch.int32
+    ld = 0
+    if probs is not None:
+        assert probs.dim() == 3 and probs.shape[:2] == (n_seq, nh) and probs.dtype == torch.float32
+        ld = probs.shape[2]
+    ws = _dev(workspace, "workspace") if workspace is not None else None
+    wsb = workspace.numel() * workspace.element_size() if workspace is not None else 0
+    st = lib().attn_decode(
+        _dev(q, "q"), _dev(k_cache, "k_cache"), _dev(v_cache, "v_cache"), _dtype_code(q), n_seq,
+        nh, n_kv, hd, cap, _dev(ctx, "ctx"), max_ctx, scale, _dev(out, "out"),
+        _dev(probs, "probs"), ld, ws, wsb, _stream())
+    _check("attn_decode", st)

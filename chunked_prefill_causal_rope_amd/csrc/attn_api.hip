@@ -1,0 +1,305 @@
+// C ABI of the library: argument validation, launch geometry, status codes.
+// Declared in include/attn.h, which documents every entry point.
+#include <math.h>
+#include <stddef.h>
+#include <stdint.h>
+
+#include <hip/hip_runtime.h>
+
+#include "../../include/attn.h"
+#include "launch.h"
+
+namespace {
+
+constexpr int kDecodePartPad = 4;
+constexpr int kDecodeSplit = 1024;      // keys per decode part
+
+bool dtype_ok(int dtype) { return dtype == ATTN_F32 || dtype == ATTN_BF16; }
+bool hd_ok(int hd) { return hd == 64 || hd == 128; }
+
+int status_of(hipError_t e) { return e == hipSuccess ? ATTN_OK : ATTN_EDEVICE; }
+
+int check_rope(int dtype, int n_tok, int n_heads, int head_dim, int n_seq, const int32_t* cu_seq,
+               const int32_t* start, int max_chunk, const float* inv_freq, int rotary_dim,
+               int norm, const float* norm_w) {
+    if (!dtype_ok(dtype) || !hd_ok(head_dim)) return ATTN_EUNSUPPORTED;
+    if (n_tok < 0 || n_seq < 0 || max_chunk < 0 || n_heads <= 0) return ATTN_EINVAL;
+    if (rotary_dim < 0 || (rotary_dim & 1)) return ATTN_EINVAL;
+    if (rotary_dim > 0 && !inv_freq) return ATTN_EINVAL;
+    if (norm < ATTN_NORM_NONE || norm > ATTN_NORM_1PW) return ATTN_EINVAL;
+    if (norm != ATTN_NORM_NONE && !norm_w) return ATTN_EINVAL;
+    if (n_seq > 0 && (!cu_seq || !start)) return ATTN_EINVAL;
+    if (n_seq > 65535) return ATTN_EINVAL;   // grid y
+    return ATTN_OK;
+}
+
+int decode_splits_full(int max_ctx) { return (max_ctx + kDecodeSplit - 1) / kDecodeSplit; }
+
+size_t decode_part_bytes(int n_seq, int n_heads, int head_dim, int splits) {
+    return (size_t)n_seq * n_heads * splits * (head_dim + kDecodePartPad) * sizeof(float);
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* attn_version(void) { return "0.1.0"; }
+
+const char* attn_status_string(int status) {
+    switch (status) {
+        case ATTN_OK: return "ok";
+        case ATTN_EINVAL: return "invalid argument";
+        case ATTN_ECAPACITY: return "exceeds cache capacity";
+        case ATTN_EUNSUPPORTED: return "unsupported configuration";
+        case ATTN_EDEVICE: return "device launch failed";
+        default: return "unknown status";
+    }
+}
+
+int attn_rope_inv_freq(int rotary_dim, double base, float* inv_freq) {
+    if (rotary_dim <= 0 || (rotary_dim & 1) || !(base > 0.0) || !inv_freq) return ATTN_EINVAL;
+    for (int i = 0; i < rotary_dim / 2; ++i)
+        inv_freq[i] = (float)(1.0 / pow(base, (double)(2 * i) / (double)rotary_dim));
+    return ATTN_OK;
+}
+
+int attn_yarn_inv_freq(int rotary_dim, double base, double factor, int orig_max_pos,
+                       double beta_fast, double beta_slow, float* inv_freq) {
+    if (rotary_dim <= 0 || (rotary_dim & 1) || !(base > 1.0) || !(factor > 0.0) ||
+        orig_max_pos <= 0 || !(beta_fast > 0.0) || !(beta_slow > 0.0) || !inv_freq)
+        return ATTN_EINVAL;
+    const int half = rotary_dim / 2;
+    const double two_pi = 6.283185307179586476925286766559;
+    auto corr_dim = [&](double rotations) {
+        return (double)rotary_dim * log((double)orig_max_pos / (rotations * two_pi)) /
+               (2.0 * log(base));
+    };
+    const double lo_d = fmax(floor(corr_dim(beta_fast)), 0.0);
+    const double hi_d = fmin(fmax(ceil(corr_dim(beta_slow)), 0.0), (double)(half - 1));
+    const long lo = (long)lo_d;
+    const long hi = (long)hi_d;
+    const long span = hi > lo ? hi - lo : 0;
+    const double denom = (double)(span > 1 ? span : 1);
+    for (int i = 0; i < half; ++i) {
+        const double f = 1.0 / pow(base, (double)(2 * i) / (double)rotary_dim);
+        const double ramp = fmin(fmax((double)(i > lo ? i - lo : 0) / denom, 0.0), 1.0);
+        // ramp 0 keeps the original frequency, ramp 1 divides it by factor
+        inv_freq[i] = (float)((f / factor) * ramp + f * (1.0 - ramp));
+    }
+    return ATTN_OK;
+}
+
+int attn_rope_apply(const void* x, void* y, int dtype, int n_tok, int n_heads, int head_dim,
+                    int n_seq, const int32_t* cu_seq, const int32_t* start, int max_chunk,
+                    const float* inv_freq, int rotary_dim, float rope_scale, int norm,
+                    const float* norm_w, double eps, void* stream) {
+    int st = check_rope(dtype, n_tok, n_heads, head_dim, n_seq, cu_seq, start, max_chunk, inv_freq,
+                        rotary_dim, norm, norm_w);
+    if (st != ATTN_OK) return st;
+    if (n_seq == 0 || n_tok == 0 || max_chunk == 0) return ATTN_OK;
+    if (!x || !y) return ATTN_EINVAL;
+    attn::RopeArgs a{};
+    a.x = x;
+    a.y = y;
+    a.cu_seq = cu_seq;
+    a.start = start;
+    a.inv_freq = inv_freq;
+    a.norm_w = norm_w;
+    a.eps = eps;
+    a.rope_scale = rope_scale;
+    a.n_tok = n_tok;
+    a.n_heads = n_heads;
+    a.head_dim = head_dim;
+    a.cap = 0;
+    a.n_seq = n_seq;
+    a.max_chunk = max_chunk;
+    a.rotary_dim = rotary_dim < head_dim ? rotary_dim : head_dim;
+    a.norm = norm;
+    return status_of(attn::launch_rope_rows(a, dtype, false, (hipStream_t)stream));
+}
+
+int attn_kv_append(void* k_cache, void* v_cache, int dtype, int n_seq, int n_kv, int head_dim,
+                   int cap, const void* k_new, const void* v_new, int n_tok,
+                   const int32_t* cu_seq, const int32_t* start, int max_chunk, int max_end,
+                   const float* inv_freq, int rotary_dim, float rope_scale, int norm,
+                   const float* norm_w, double eps, void* stream) {
+    int st = check_rope(dtype, n_tok, n_kv, head_dim, n_seq, cu_seq, start, max_chunk, inv_freq,
+                        rotary_dim, norm, norm_w);
+    if (st != ATTN_OK) return st;
+    if (cap <= 0 || max_end < 0) return ATTN_EINVAL;
+    if (max_end > cap) return ATTN_ECAPACITY;
+    if (n_seq == 0 || n_tok == 0 || max_chunk == 0) return ATTN_OK;
+    if (!k_cache || !v_cache || !k_new || !v_new) return ATTN_EINVAL;
+    attn::RopeArgs a{};
+    a.x = k_new;
+    a.y = k_cache;
+    a.v_src = v_new;
+    a.v_dst = v_cache;
+    a.cu_seq = cu_seq;
+    a.start = start;
+    a.inv_freq = inv_freq;
+    a.norm_w = norm_w;
+    a.eps = eps;
+    a.rope_scale = rope_scale;
+    a.n_tok = n_tok;
+    a.n_heads = n_kv;
+    a.head_dim = head_dim;
+    a.cap = cap;
+    a.n_seq = n_seq;
+    a.max_chunk = max_chunk;
+    a.rotary_dim = rotary_dim < head_dim ? rotary_dim : head_dim;
+    a.norm = norm;
+    return status_of(attn::launch_rope_rows(a, dtype, true, (hipStream_t)stream));
+}
+
+size_t attn_prefill_workspace_bytes(int n_seq, int n_heads, int n_kv, int head_dim, int n_tok,
+                                    int max_chunk, int max_end) {
+    if (n_seq <= 0 || n_heads <= 0 || n_kv <= 0 || n_heads % n_kv || n_tok <= 0 || max_chunk <= 0 ||
+        max_end <= 0 || !hd_ok(head_dim))
+        return 0;
+    return attn::plan_prefill(n_seq, n_heads, n_kv, head_dim, n_tok, max_chunk, max_end,
+                              (size_t)-1).ws_bytes;
+}
+
+int attn_prefill_chunk(const void* q, const void* k_cache, const void* v_cache, int dtype,
+                       int n_seq, int n_heads, int n_kv, int head_dim, int cap, int n_tok,
+                       const int32_t* cu_seq, const int32_t* start, int max_chunk, int max_end,
+                       float scale, float* out, void* workspace, size_t workspace_bytes,
+                       void* stream) {
+    if (!dtype_ok(dtype) || !hd_ok(head_dim)) return ATTN_EUNSUPPORTED;
+    if (n_seq < 0 || n_tok < 0 || max_chunk < 0 || max_end < 0 || n_heads <= 0 || n_kv <= 0 ||
+        cap <= 0 || n_heads % n_kv != 0 || !isfinite(scale))
+        return ATTN_EINVAL;
+    if (max_end > cap) return ATTN_ECAPACITY;
+    if (n_seq == 0 || n_tok == 0 || max_chunk == 0) return ATTN_OK;
+    if (!q || !k_cache || !v_cache || !out || !cu_seq || !start) return ATTN_EINVAL;
+    if (n_seq > 65535) return ATTN_EINVAL;
+    hipStream_t s = (hipStream_t)stream;
+    const int group = n_heads / n_kv;
+    if (dtype == ATTN_F32) {
+        attn::AttendF32Args a{};
+        a.q = (const float*)q;
+        a.k_cache = (const float*)k_cache;
+        a.v_cache = (const float*)v_cache;
+        a.out = out;
+        a.cu_seq = cu_seq;
+        a.start = start;
+        a.scale = scale;
+        a.decode = 0;
+        a.n_seq = n_seq;
+        a.n_heads = n_heads;
+        a.n_kv = n_kv;
+        a.group = group;
+        a.head_dim = head_dim;
+        a.cap = cap;
+        a.n_tok = n_tok;
+        a.max_chunk = max_chunk;
+        return status_of(attn::launch_attend_f32(a, s));
+    }
+    attn::PrefillArgs a{};
+    a.q = q;
+    a.k_cache = k_cache;
+    a.v_cache = v_cache;
+    a.out = out;
+    a.cu_seq = cu_seq;
+    a.start = start;
+    a.scale = scale;
+    a.n_seq = n_seq;
+    a.n_heads = n_heads;
+    a.n_kv = n_kv;
+    a.group = group;
+    a.head_dim = head_dim;
+    a.cap = cap;
+    a.n_tok = n_tok;
+    a.max_chunk = max_chunk;
+    a.max_end = max_end;
+    const attn::PrefillPlan plan = attn::plan_prefill(n_seq, n_heads, n_kv, head_dim, n_tok,
+                                                      max_chunk, max_end,
+                                                      workspace ? workspace_bytes : 0);
+    a.rows_per_tile = plan.rows_per_tile;
+    a.n_qtiles = plan.n_qtiles;
+    a.n_splits = plan.n_splits;
+    a.part = plan.n_splits > 1 ? (float*)workspace : nullptr;
+    const int splits = plan.n_splits;
+    const long blocks = (long)n_seq * a.n_qtiles * a.n_splits * n_kv;
+    if (blocks > 0x7fffffffL) return ATTN_EINVAL;
+    hipError_t e = attn::launch_prefill_bf16(a, s);
+    if (e == hipSuccess && splits > 1) e = attn::launch_prefill_combine(a, s);
+    return status_of(e);
+}
+
+size_t attn_decode_workspace_bytes(int n_seq, int n_heads, int n_kv, int head_dim, int max_ctx) {
+    if (n_seq <= 0 || n_heads <= 0 || n_kv <= 0 || n_heads % n_kv || max_ctx <= 0 ||
+        !hd_ok(head_dim))
+        return 0;
+    return decode_part_bytes(n_seq, n_heads, head_dim, decode_splits_full(max_ctx));
+}
+
+int attn_decode(const void* q, const void* k_cache, const void* v_cache, int dtype, int n_seq,
+                int n_heads, int n_kv, int head_dim, int cap, const int32_t* ctx, int max_ctx,
+                float scale, float* out, float* probs, int probs_ld, void* workspace,
+                size_t workspace_bytes, void* stream) {
+    if (!dtype_ok(dtype) || !hd_ok(head_dim)) return ATTN_EUNSUPPORTED;
+    if (n_seq < 0 || max_ctx < 0 || n_heads <= 0 || n_kv <= 0 || cap <= 0 ||
+        n_heads % n_kv != 0 || !isfinite(scale))
+        return ATTN_EINVAL;
+    if (max_ctx > cap) return ATTN_ECAPACITY;
+    if (n_seq == 0 || max_ctx == 0) return ATTN_OK;
+    if (!q || !k_cache || !v_cache || !out || !ctx) return ATTN_EINVAL;
+    if (probs && probs_ld < max_ctx) return ATTN_EINVAL;
+    hipStream_t s = (hipStream_t)stream;
+    const int group = n_heads / n_kv;
+    if (dtype == ATTN_F32) {
+        attn::AttendF32Args a{};
+        a.q = (const float*)q;
+        a.k_cache = (const float*)k_cache;
+        a.v_cache = (const float*)v_cache;
+        a.out = out;
+        a.probs = probs;
+        a.ctx = ctx;
+        a.scale = scale;
+        a.decode = 1;
+        a.n_seq = n_seq;
+        a.n_heads = n_heads;
+        a.n_kv = n_kv;
+        a.group = group;
+        a.head_dim = head_dim;
+        a.cap = cap;
+        a.n_tok = n_seq;
+        a.max_ctx = max_ctx;
+        a.probs_ld = probs_ld;
+        return status_of(attn::launch_attend_f32(a, s));
+    }
+    if (group > attn::decode_group_limit()) return ATTN_EUNSUPPORTED;
+    const size_t per = decode_part_bytes(n_seq, n_heads, head_dim, 1);
+    if (!workspace || workspace_bytes < per) return ATTN_EINVAL;
+    int splits = decode_splits_full(max_ctx);
+    const size_t fit = workspace_bytes / per;
+    if ((size_t)splits > fit) splits = (int)fit;
+    int split_len = (max_ctx + splits - 1) / splits;
+    split_len = (split_len + 63) / 64 * 64;
+    splits = (max_ctx + split_len - 1) / split_len;
+    attn::DecodeArgs a{};
+    a.q = q;
+    a.k_cache = k_cache;
+    a.v_cache = v_cache;
+    a.out = out;
+    a.probs = probs;
+    a.part = (float*)workspace;
+    a.ctx = ctx;
+    a.scale = scale;
+    a.n_seq = n_seq;
+    a.n_heads = n_heads;
+    a.n_kv = n_kv;
+    a.group = group;
+    a.head_dim = head_dim;
+    a.cap = cap;
+    a.max_ctx = max_ctx;
+    a.probs_ld = probs ? probs_ld : 0;
+    a.split_len = split_len;
+    a.n_splits = splits;
+    if ((long)n_seq * splits * n_kv > 0x7fffffffL) return ATTN_EINVAL;
+    return status_of(attn::launch_decode_bf16(a, s));
+}
+
+}  // extern "C"

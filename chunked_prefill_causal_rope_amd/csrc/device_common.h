@@ -1,0 +1,78 @@
+// Device-side helpers shared by the gfx950 kernels: vector types for the
+// matrix-core builtins, bfloat16 bit conversions, wave reductions.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace attn {
+
+typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+typedef float f32x16_t __attribute__((ext_vector_type(16)));
+typedef float f32x4_t __attribute__((ext_vector_type(4)));
+
+constexpr float kLog2e = 1.4426950408889634f;
+
+__device__ __forceinline__ float bf16_lo(uint32_t u) { return __uint_as_float(u << 16); }
+__device__ __forceinline__ float bf16_hi(uint32_t u) { return __uint_as_float(u & 0xffff0000u); }
+__device__ __forceinline__ float bf16_to_f32(uint16_t b) {
+    return __uint_as_float(((uint32_t)b) << 16);
+}
+
+// Pack two floats into two bfloat16 (round to nearest even), low half = a.
+__device__ __forceinline__ uint32_t pack_bf16x2(float a, float b) {
+    bf16x2_t v;
+    v.x = (__bf16)a;
+    v.y = (__bf16)b;
+    return __builtin_bit_cast(uint32_t, v);
+}
+
+// Round a double to bfloat16, ties to even, in one rounding.  The double is
+// first narrowed to float with round-to-odd (truncate, then set the last bit
+// when inexact); float keeps more than bfloat16's 8 significant bits plus two,
+// so the second, ties-to-even narrowing then rounds exactly as a direct one.
+__device__ __forceinline__ uint16_t f64_to_bf16_bits(double x) {
+    float f = (float)x;                       // ties to even
+    double back = (double)f;
+    uint32_t u = __float_as_uint(f);
+    if (back != x && !__builtin_isnan(x)) {
+        if (__builtin_fabs(back) > __builtin_fabs(x)) u -= 1;   // step toward zero
+        u |= 1u;                                                  // sticky bit
+    }
+    if ((u & 0x7fffffffu) > 0x7f800000u) return (uint16_t)((u >> 16) | 0x40u);  // quiet NaN
+    u += 0x7fffu + ((u >> 16) & 1u);
+    return (uint16_t)(u >> 16);
+}
+
+template <typename T> struct Elem;
+template <> struct Elem<float> {
+    __device__ static double load(const float* p) { return (double)*p; }
+    __device__ static void store(float* p, double x) { *p = (float)x; }
+};
+template <> struct Elem<uint16_t> {
+    __device__ static double load(const uint16_t* p) { return (double)bf16_to_f32(*p); }
+    __device__ static void store(uint16_t* p, double x) { *p = f64_to_bf16_bits(x); }
+};
+
+// Each shuffle is evaluated exactly once, by every lane: a cross-lane read
+// (ds_bpermute) placed under a divergent branch would read from lanes that are
+// switched off.
+template <typename T>
+__device__ __forceinline__ T wave_max(T v) {
+#pragma unroll
+    for (int o = 32; o > 0; o >>= 1) {
+        const T other = __shfl_xor(v, o);
+        v = v > other ? v : other;
+    }
+    return v;
+}
+
+template <typename T>
+__device__ __forceinline__ T wave_sum(T v) {
+#pragma unroll
+    for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o);
+    return v;
+}
+
+}  // namespace attn

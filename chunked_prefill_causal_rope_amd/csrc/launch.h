@@ -1,0 +1,83 @@
+// Internal launch interface between the C-ABI layer and the kernels.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace attn {
+
+// Per-head finish (norm + RoPE + rounding) of Q rows, or of K rows into the
+// cache with the V rows copied alongside.
+struct RopeArgs {
+    const void* x;         // rows [n_tok][n_heads][head_dim]
+    void* y;               // Q: [n_tok][n_heads][head_dim]; KV: K cache
+    const void* v_src;     // KV only: V rows [n_tok][n_heads][head_dim]
+    void* v_dst;           // KV only: V cache
+    const int32_t* cu_seq;
+    const int32_t* start;
+    const float* inv_freq;
+    const float* norm_w;
+    double eps;
+    float rope_scale;
+    int n_tok, n_heads, head_dim, cap, n_seq, max_chunk, rotary_dim, norm;
+};
+hipError_t launch_rope_rows(const RopeArgs& a, int dtype, bool kv, hipStream_t stream);
+
+// Causal attention of packed chunk rows over the head-major cache.
+struct PrefillArgs {
+    const void* q;
+    const void* k_cache;
+    const void* v_cache;
+    float* out;
+    float* part;           // split partials [n_tok*n_heads][n_splits][head_dim+4] or null
+    const int32_t* cu_seq;
+    const int32_t* start;
+    float scale;
+    int n_seq, n_heads, n_kv, group, head_dim, cap, n_tok, max_chunk, max_end;
+    int rows_per_tile, n_qtiles, n_splits;
+};
+// Launch plan of the bf16 prefill, from host scalars only: query rows per
+// workgroup (128 or 256), row tiles, key-range parts, workspace they need.
+struct PrefillPlan {
+    int rows_per_tile, n_qtiles, n_splits;
+    size_t ws_bytes;
+};
+PrefillPlan plan_prefill(int n_seq, int n_heads, int n_kv, int head_dim, int n_tok, int max_chunk,
+                         int max_end, size_t ws_available);
+hipError_t launch_prefill_bf16(const PrefillArgs& a, hipStream_t stream);
+hipError_t launch_prefill_combine(const PrefillArgs& a, hipStream_t stream);
+
+// float32 path (prefill rows and decode rows) -- vector ALU, one wave per row.
+struct AttendF32Args {
+    const float* q;
+    const float* k_cache;
+    const float* v_cache;
+    float* out;
+    float* probs;          // decode only, may be null
+    const int32_t* cu_seq; // prefill mode
+    const int32_t* start;  // prefill mode
+    const int32_t* ctx;    // decode mode
+    float scale;
+    int decode;
+    int n_seq, n_heads, n_kv, group, head_dim, cap, n_tok, max_chunk, max_ctx, probs_ld;
+};
+hipError_t launch_attend_f32(const AttendF32Args& a, hipStream_t stream);
+
+// bf16 decode: split the key range of each (sequence, KV head), then merge.
+struct DecodeArgs {
+    const void* q;
+    const void* k_cache;
+    const void* v_cache;
+    float* out;
+    float* probs;
+    float* part;           // [n_seq*n_heads][n_splits][head_dim+4]
+    const int32_t* ctx;
+    float scale;
+    int n_seq, n_heads, n_kv, group, head_dim, cap, max_ctx, probs_ld;
+    int split_len, n_splits;
+};
+int decode_group_limit();
+hipError_t launch_decode_bf16(const DecodeArgs& a, hipStream_t stream);
+
+}  // namespace attn

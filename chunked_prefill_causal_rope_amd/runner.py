@@ -1,0 +1,154 @@
+"""Host-side drivers for the chunk loop and for a decode step.
+
+Each prefill step issues, through the C ABI and on the current stream:
+  attn_rope_apply  (finish the step's query rows into a rotated buffer),
+  attn_kv_append   (finish the step's key rows into the cache, copy values),
+  attn_prefill_chunk (causal attention of the step's rows over the cache).
+That is the order of needle-core 0.3.1 src/v2/batch.rs (prefill_batch walks
+the prompt in chunks; a chunk's K/V are written before any of its positions
+attends) and of cortiq-engine 0.5.39 src/attention.rs fn qwen_attention_batch.
+Varlen batches take, per step, the next <= chunk tokens of every unfinished
+prompt; a finished prompt stays in the batch with zero tokens so that batch
+index b is always cache slot b.
+
+All inputs are staged per step before any work is timed; the drivers only
+launch library calls.
+"""
+from __future__ import annotations
+
+import torch
+
+from . import api
+from .workloads import Workload, chunk_schedule
+
+
+def tables(w: Workload, device="cuda") -> torch.Tensor:
+    """Inverse-frequency table of the workload, computed by the library on the
+    host and copied to the device once."""
+    if w.yarn is not None:
+        f = api.yarn_inv_freq(w.rd, w.base, *w.yarn)
+    else:
+        f = api.rope_inv_freq(w.rd, w.base)
+    return f.to(device)
+
+
+class ChunkedPrefill:
+    def __init__(self, w: Workload, data: dict, device="cuda", chunk: int | None = None,
+                 cap: int | None = None, k_cache=None, v_cache=None, start_offset: int = 0):
+        self.w = w
+        self.device = device
+        lengths = data["lengths"]
+        cu = data["cu_seq"]
+        self.lengths = lengths
+        self.cu_seq = cu
+        self.chunk = chunk or w.chunk
+        n_seq = len(lengths)
+        self.cap = cap or data.get("cap") or (start_offset + max(lengths))
+        hd, nkv, nh = w.head_dim, w.n_kv, w.n_heads
+        dt = w.torch_dtype
+        if k_cache is None:
+            k_cache = torch.zeros((n_seq, nkv, self.cap, hd), dtype=dt, device=device)
+            v_cache = torch.zeros((n_seq, nkv, self.cap, hd), dtype=dt, device=device)
+        self.k_cache, self.v_cache = k_cache, v_cache
+        self.inv_freq = tables(w, device)
+        self.q_norm_w = data["q_norm_w"].to(device) if data.get("q_norm_w") is not None else None
+        self.k_norm_w = data["k_norm_w"].to(device) if data.get("k_norm_w") is not None else None
+        q, k, v = data["q"], data["k"], data["v"]
+        self.steps = []
+        for step in chunk_schedule(lengths, self.chunk):
+            per_seq = {b: (p, c) for b, p, c in step}
+            starts, lens, rows = [], [], []
+            for b in range(n_seq):
+                p, c = per_seq.get(b, (lengths[b], 0))
+                starts.append(start_offset + p)
+                lens.append(c)
+                rows.extend(range(cu[b] + p, cu[b] + p + c))
+            batch = api.Batch(starts, lens, device=device)
+            r0, r1 = rows[0], rows[-1] + 1
+            if rows == list(range(r0, r1)):
+                sl = slice(r0, r1)
+                qs, ks, vs = q[sl], k[sl], v[sl]
+            else:
+                idx = torch.tensor(rows, dtype=torch.long, device=q.device)
+                qs, ks, vs = q[idx], k[idx], v[idx]
+            qs, ks, vs = (x.to(device).contiguous() for x in (qs, ks, vs))
+            n_tok = len(rows)
+            self.steps.append(dict(
+                batch=batch, rows=rows, q=qs, k=ks, v=vs,
+                q_rot=torch.empty_like(qs),
+                out=torch.empty((n_tok, nh, hd), dtype=torch.float32, device=device)))
+        ws = max(api.prefill_workspace_bytes(s["batch"], nh, nkv, hd) for s in self.steps)
+        self.workspace = torch.empty(max(ws, 16) // 4 + 1, dtype=torch.float32, device=device)
+
+    def run_step(self, i: int, attend: bool = True):
+        w, s = self.w, self.steps[i]
+        api.rope_apply(s["q"], s["q_rot"], s["batch"], self.inv_freq, w.rd, w.rope_scale,
+                       w.norm_style, self.q_norm_w, w.norm_eps)
+        api.kv_append(self.k_cache, self.v_cache, s["k"], s["v"], s["batch"], self.inv_freq, w.rd,
+                      w.rope_scale, w.norm_style, self.k_norm_w, w.norm_eps)
+        if attend:
+            self.attend_step(i)
+
+    def attend_step(self, i: int):
+        s = self.steps[i]
+        api.prefill_chunk(s["q_rot"], self.k_cache, self.v_cache, s["batch"], self.w.scale,
+                          s["out"], self.workspace)
+
+    def run_all(self):
+        for i in range(len(self.steps)):
+            self.run_step(i)
+
+    def gather(self, key: str) -> torch.Tensor:
+        """Per-token results of every step, back in the packed input order."""
+        first = self.steps[0][key]
+        total = self.cu_seq[-1]
+        res = torch.empty((total,) + tuple(first.shape[1:]), dtype=first.dtype, device=first.device)
+        for s in self.steps:
+            idx = torch.tensor(s["rows"], dtype=torch.long, device=first.device)
+            res[idx] = s[key]
+        return res
+
+
+class DecodeStep:
+    """One decode step for a batch of sequences: finish the new query, append
+    the new key/value at position ctx-1, attend keys 0..ctx-1 (with the
+    probabilities when the workload asks for them)."""
+
+    def __init__(self, w: Workload, data: dict, device="cuda"):
+        self.w = w
+        ctx = data["ctx"]
+        self.ctx_list = ctx
+        self.max_ctx = max(ctx)
+        n_seq = len(ctx)
+        self.k_cache = data["k_cache"].to(device)
+        self.v_cache = data["v_cache"].to(device)
+        self.cap = self.k_cache.shape[2]
+        self.q = data["q"].to(device).contiguous()
+        self.k = data["k"].to(device).contiguous()
+        self.v = data["v"].to(device).contiguous()
+        self.q_rot = torch.empty_like(self.q)
+        self.inv_freq = tables(w, device)
+        self.q_norm_w = data["q_norm_w"].to(device) if data.get("q_norm_w") is not None else None
+        self.k_norm_w = data["k_norm_w"].to(device) if data.get("k_norm_w") is not None else None
+        self.batch = api.Batch([c - 1 for c in ctx], [1] * n_seq, device=device)
+        self.ctx = torch.tensor(ctx, dtype=torch.int32, device=device)
+        self.out = torch.empty((n_seq, w.n_heads, w.head_dim), dtype=torch.float32, device=device)
+        self.probs = (torch.empty((n_seq, w.n_heads, self.max_ctx), dtype=torch.float32,
+                                  device=device) if w.want_probs else None)
+        wsb = api.decode_workspace_bytes(n_seq, w.n_heads, w.n_kv, w.head_dim, self.max_ctx)
+        self.workspace = torch.empty(max(wsb, 16) // 4 + 1, dtype=torch.float32, device=device)
+
+    def finish_and_append(self):
+        w = self.w
+        api.rope_apply(self.q, self.q_rot, self.batch, self.inv_freq, w.rd, w.rope_scale,
+                       w.norm_style, self.q_norm_w, w.norm_eps)
+        api.kv_append(self.k_cache, self.v_cache, self.k, self.v, self.batch, self.inv_freq, w.rd,
+                      w.rope_scale, w.norm_style, self.k_norm_w, w.norm_eps)
+
+    def attend(self):
+        api.decode(self.q_rot, self.k_cache, self.v_cache, self.ctx, self.max_ctx, self.w.scale,
+                   self.out, self.probs, self.workspace)
+
+    def run(self):
+        self.finish_and_append()
+        self.attend()

@@ -1,0 +1,219 @@
+/*
+ * attn.h -- C ABI of the MI355X (gfx950) library for causal grouped-query
+ * attention with RoPE over a head-major KV cache.
+ *
+ * Sources (page title, then the item on it):
+ *   [ATT] cortiq-engine 0.5.39, src/attention.rs
+ *   [NDL] needle-core 0.3.1, src/v2/batch.rs
+ *
+ * Conventions shared by every entry point
+ * ---------------------------------------
+ * - Pointers marked "device" are HIP device pointers; "host" pointers are
+ *   ordinary host memory.  The caller owns every buffer; the library allocates
+ *   nothing, keeps no global mutable state and enqueues work only on `stream`
+ *   (a hipStream_t passed as void*; NULL is the default stream).  Calls return
+ *   as soon as the work is enqueued.
+ * - dtype: ATTN_F32 or ATTN_BF16.  It is the element type of the raw and
+ *   rotated Q, of the new K/V rows and of the K/V cache.  Attention outputs
+ *   and probabilities are always float32.
+ * - Varlen batch descriptor (prefill, RoPE, append): n_seq sequences whose
+ *   tokens are packed back to back in token-major tensors of n_tok rows.
+ *   cu_seq [n_seq+1] (device, int32) gives each sequence's first packed row;
+ *   start [n_seq] (device, int32) gives the absolute position of that row
+ *   ([ATT] fn qwen_attention_batch: the configured position is the chunk's
+ *   FIRST absolute position).  Token i of sequence b is packed row
+ *   cu_seq[b]+i at position start[b]+i.  max_chunk (host) bounds every
+ *   sequence's token count; max_end (host) bounds every start[b]+len_b.  The
+ *   host checks sizes from these host scalars; the device arrays are trusted
+ *   to agree with them, and kernels skip any row outside [0, n_tok) or any
+ *   position outside [0, cap) so a disagreeing array can never write out of
+ *   bounds.
+ * - Layouts (row-major, innermost last):
+ *     Q, output            [n_tok][n_heads][head_dim]
+ *     new K, new V         [n_tok][n_kv][head_dim]
+ *     K cache, V cache     [n_seq][n_kv][cap][head_dim]  (head-major: each
+ *                          KV head's rows are one contiguous [cap][head_dim]
+ *                          slice, [ATT] fn multi_head_attention notes)
+ *   Query head h reads KV head h / (n_heads / n_kv) ([ATT] fn
+ *   multi_head_attention, fn attend_all_heads).
+ * - Errors: every call returns an attn_status; nothing else crosses the ABI.
+ *   Empty work (n_seq == 0, n_tok == 0 or max_chunk == 0) returns ATTN_OK and
+ *   launches nothing.  There is no fallback path: a configuration without a
+ *   kernel returns ATTN_EUNSUPPORTED.
+ */
+#ifndef ATTN_H
+#define ATTN_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum { ATTN_F32 = 0, ATTN_BF16 = 1 } attn_dtype;
+
+typedef enum {
+    ATTN_OK = 0,
+    ATTN_EINVAL = -1,      /* bad argument: null pointer, non-positive size,
+                              n_heads % n_kv != 0, odd rotary_dim, ... */
+    ATTN_ECAPACITY = -2,   /* max_end (or max_ctx) exceeds the cache capacity */
+    ATTN_EUNSUPPORTED = -3,/* head_dim not 64/128, unknown dtype, or a GQA
+                              group wider than the kernel supports */
+    ATTN_EDEVICE = -4      /* a HIP launch failed (hipGetLastError) */
+} attn_status;
+
+typedef enum {
+    ATTN_NORM_NONE = 0,
+    ATTN_NORM_W = 1,       /* x * r * w        ("Qwen" style)  */
+    ATTN_NORM_1PW = 2      /* x * r * (1 + w)  ("Gemma" style) */
+} attn_norm;
+
+/*
+ * RoPE inverse-frequency table.  [ATT] fn rope_inv_freq:
+ *   inv_freq[i] = 1 / base^(2i / rotary_dim),  i < rotary_dim / 2,
+ * evaluated in double and rounded once to float.
+ * inv_freq: host, float[rotary_dim/2], written.
+ * Errors: EINVAL if rotary_dim is not positive and even, base <= 0, or
+ * inv_freq is NULL.
+ */
+int attn_rope_inv_freq(int rotary_dim, double base, float *inv_freq);
+
+/*
+ * YaRN inverse-frequency table.  [ATT] fn yarn_inv_freq ("Hugging Face
+ * compatible"; rotary_dim is the rotary dimension, not the head width):
+ *   cd(r)  = rotary_dim * ln(orig_max_pos / (2 pi r)) / (2 ln base)
+ *   low    = max(floor(cd(beta_fast)), 0)
+ *   high   = clamp(ceil(cd(beta_slow)), 0, rotary_dim/2 - 1)
+ *   ramp_i = clamp(max(i - low, 0) / max(high - low, 1), 0, 1)
+ *   inv_freq[i] = (f_i / factor) * ramp_i + f_i * (1 - ramp_i),
+ * with f_i the plain RoPE frequency; double arithmetic, one rounding to float.
+ * inv_freq: host, float[rotary_dim/2], written.
+ * Errors: EINVAL if rotary_dim is not positive and even, base <= 1,
+ * factor <= 0, orig_max_pos <= 0, beta_fast/beta_slow <= 0, or a NULL table.
+ */
+int attn_yarn_inv_freq(int rotary_dim, double base, double factor, int orig_max_pos,
+                       double beta_fast, double beta_slow, float *inv_freq);
+
+/*
+ * Finish the query rows: optional per-head RMS norm, then RoPE, then rounding
+ * to dtype.  [ATT] fn finish_projection (qk-norm before RoPE, partial RoPE on
+ * the first rotary_dim dims), fn rmsnorm_head, fn rope_rotate_scaled:
+ *   r = 1 / sqrt(mean(x^2) + eps);  x <- x*r*w  or  x*r*(1+w)
+ *   x_i     <- (x_i cos t - x_{i+h} sin t) * rope_scale
+ *   x_{i+h} <- (x_i sin t + x_{i+h} cos t) * rope_scale,
+ *   h = rotary_dim / 2, t = position * inv_freq[i];
+ * dims at or past rotary_dim are normed but neither rotated nor scaled.  The
+ * norm, angle and rotation are computed in double; each stored element is
+ * rounded once to dtype (ties to even).
+ *   x        device [n_tok][n_heads][head_dim], read
+ *   y        device [n_tok][n_heads][head_dim], written (y == x is allowed)
+ *   inv_freq device float[rotary_dim/2]; rotary_dim 0 disables RoPE;
+ *            rotary_dim > head_dim is clamped to head_dim ([ATT] uses
+ *            rotary_dim.min(head_dim))
+ *   norm_w   device float[head_dim], shared by all heads; NULL iff norm is
+ *            ATTN_NORM_NONE
+ * Errors: EINVAL (sizes, odd rotary_dim, NULL pointers, bad norm),
+ * EUNSUPPORTED (dtype, head_dim), EDEVICE.
+ */
+int attn_rope_apply(const void *x, void *y, int dtype, int n_tok, int n_heads, int head_dim,
+                    int n_seq, const int32_t *cu_seq, const int32_t *start, int max_chunk,
+                    const float *inv_freq, int rotary_dim, float rope_scale, int norm,
+                    const float *norm_w, double eps, void *stream);
+
+/*
+ * Append a chunk's keys and values to the head-major cache: each K row gets
+ * the same finish as attn_rope_apply (norm, RoPE, rounding) and is written to
+ * k_cache[b][g][start[b]+i][:]; each V row is copied bit for bit to
+ * v_cache[b][g][start[b]+i][:].  Every row of the chunk is written by this
+ * call, i.e. before any of the chunk's positions attends ([NDL] module docs,
+ * "What has to stay sequential"; [ATT] fn qwen_attention_batch appends every
+ * position of the chunk before the batched attend).  Rows outside
+ * [start[b], start[b]+len_b) are not touched.
+ *   k_cache, v_cache device [n_seq][n_kv][cap][head_dim], updated
+ *   k_new, v_new     device [n_tok][n_kv][head_dim], read
+ *   norm_w           the k-norm weight, device float[head_dim] or NULL
+ * Errors: ECAPACITY if max_end > cap; otherwise as attn_rope_apply.
+ */
+int attn_kv_append(void *k_cache, void *v_cache, int dtype, int n_seq, int n_kv, int head_dim,
+                   int cap, const void *k_new, const void *v_new, int n_tok,
+                   const int32_t *cu_seq, const int32_t *start, int max_chunk, int max_end,
+                   const float *inv_freq, int rotary_dim, float rope_scale, int norm,
+                   const float *norm_w, double eps, void *stream);
+
+/*
+ * Causal attention for the rows of a chunk whose keys and values are already
+ * in the cache (call attn_kv_append first).  For row i of sequence b at
+ * position p = start[b]+i and query head h, with g = h / (n_heads/n_kv):
+ *   s_j = scale * <q, K[b][g][j]>,  j = 0..p   (keys <= p only)
+ *   out = sum_j softmax(s)_j V[b][g][j],  max-subtracted softmax
+ * [ATT] fn attention_head, the batched causal fallback of fn
+ * qwen_attention_batch (limit s0+bi+1), gpu::chunk_attend's signature;
+ * [NDL] module docs (position p attends keys <= p).
+ * bf16: products on bf16 matrix cores with float32 accumulation, softmax in
+ * float32, probabilities rounded to bf16 for the P.V product; f32: float32
+ * vector arithmetic.
+ *   q        device [n_tok][n_heads][head_dim] (rotated), read
+ *   out      device float[n_tok][n_heads][head_dim], written
+ *   scale    the score scale, normally 1/sqrt(head_dim)
+ *   workspace device scratch of workspace_bytes (may be NULL/0); with less
+ *            than attn_prefill_workspace_bytes() the key range is split into
+ *            fewer parts (never an error).  Contents need no initialisation
+ *            and are clobbered.  Calls that share a workspace must be ordered
+ *            on one stream.
+ * Errors: ECAPACITY if max_end > cap; EINVAL, EUNSUPPORTED, EDEVICE.
+ */
+int attn_prefill_chunk(const void *q, const void *k_cache, const void *v_cache, int dtype,
+                       int n_seq, int n_heads, int n_kv, int head_dim, int cap, int n_tok,
+                       const int32_t *cu_seq, const int32_t *start, int max_chunk, int max_end,
+                       float scale, float *out, void *workspace, size_t workspace_bytes,
+                       void *stream);
+
+/*
+ * Workspace that lets attn_prefill_chunk split the key range as far as it
+ * chooses for these sizes (bytes; 0 when it would not split).
+ */
+size_t attn_prefill_workspace_bytes(int n_seq, int n_heads, int n_kv, int head_dim, int n_tok,
+                                    int max_chunk, int max_end);
+
+/*
+ * Decode: one query per sequence (chunk = 1) at position ctx[b]-1, whose K/V
+ * row is already in the cache (append it first with attn_kv_append,
+ * start[b] = ctx[b]-1).  Row (b, h) attends keys 0..ctx[b]-1 of KV head
+ * h/(n_heads/n_kv), as attn_prefill_chunk; optionally it also returns the
+ * attention probabilities ([ATT] fn attention_head returns (out, probs); the
+ * probabilities feed importance accounting).  The key range of each sequence
+ * is split across workgroups and the parts are merged with a log-sum-exp
+ * combine.
+ *   q      device [n_seq][n_heads][head_dim] (rotated), read
+ *   ctx    device int32[n_seq], 1 <= ctx[b] <= max_ctx (values above max_ctx
+ *          are clamped to it; a row with ctx[b] < 1 gets zeros)
+ *   out    device float[n_seq][n_heads][head_dim], written
+ *   probs  NULL, or device float[n_seq][n_heads][probs_ld]; row (b, h) gets
+ *          ctx[b] entries summing to 1, entries past ctx[b] are not written
+ *   workspace device scratch, clobbered, no initialisation needed.  bf16
+ *          needs at least n_seq*n_heads*(head_dim+2)*4 bytes (one part per
+ *          row, EINVAL below that); attn_decode_workspace_bytes() gives the
+ *          size for the full split, and a smaller one means fewer, longer
+ *          parts.  f32 needs none.
+ * Errors: ECAPACITY if max_ctx > cap; EINVAL (probs_ld < max_ctx, ...),
+ * EUNSUPPORTED (bf16 with more than 16 query heads per KV head), EDEVICE.
+ */
+int attn_decode(const void *q, const void *k_cache, const void *v_cache, int dtype, int n_seq,
+                int n_heads, int n_kv, int head_dim, int cap, const int32_t *ctx, int max_ctx,
+                float scale, float *out, float *probs, int probs_ld, void *workspace,
+                size_t workspace_bytes, void *stream);
+
+size_t attn_decode_workspace_bytes(int n_seq, int n_heads, int n_kv, int head_dim, int max_ctx);
+
+/* Static, human-readable name of a status code. */
+const char *attn_status_string(int status);
+
+/* Library version, "major.minor.patch". */
+const char *attn_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* ATTN_H */

@@ -1,0 +1,109 @@
+"""Helpers for the GPU parity tests: oracle references for runner outputs and
+the tolerance checks.  Imports the oracle (test infrastructure) and the
+product package side by side; no value flows from the GPU into the oracle."""
+from __future__ import annotations
+
+import sys
+
+import numpy as np
+import torch
+
+import oracle
+from chunked_prefill_causal_rope_amd import workloads as wl
+
+# bf16: per output row (position, head), max_d |dO| <= 2e-2 * RMS_d(O_ref).
+BF16_ROW_TOL = 2e-2
+# f32: max abs error
+F32_ABS_TOL = 1e-4
+
+
+def say(*a):
+    print(*a, flush=True)
+    sys.stdout.flush()
+
+
+def store_of(w: wl.Workload) -> int:
+    return oracle.STORE_F32 if w.dtype == wl.F32 else oracle.STORE_BF16
+
+
+def oracle_table(w: wl.Workload) -> np.ndarray:
+    if w.yarn is not None:
+        return oracle.yarn_inv_freq(w.rd, w.base, *w.yarn)
+    return oracle.rope_inv_freq(w.rd, w.base)
+
+
+def np64(t: torch.Tensor) -> np.ndarray:
+    return t.detach().float().cpu().numpy().astype(np.float64)
+
+
+def norm_kwargs(w, d, which):
+    if w.norm_style == wl.NORM_NONE:
+        return dict(norm_style=oracle.NORM_NONE)
+    return dict(norm_style=w.norm_style, norm_w=d[which].cpu().numpy(), eps=w.norm_eps)
+
+
+def oracle_prefill_packed(w, d, chunk, want_probs=False):
+    """Oracle chunked prefill of every sequence of a packed batch; returns
+    out [T][nh][hd] in packed order plus per-sequence caches."""
+    f = oracle_table(w)
+    outs, caches, qrots, probs = [], [], [], []
+    cu = d["cu_seq"]
+    for b, n in enumerate(d["lengths"]):
+        sl = slice(cu[b], cu[b] + n)
+        qn = norm_kwargs(w, d, "q_norm_w")
+        kn = norm_kwargs(w, d, "k_norm_w")
+        r = oracle.prefill_sequence(
+            np64(d["q"][sl]), np64(d["k"][sl]), np64(d["v"][sl]), chunk, f, w.rd, w.scale,
+            store_of(w), rope_scale=w.rope_scale,
+            norm_style=qn.get("norm_style", 0), q_norm_w=qn.get("norm_w"),
+            k_norm_w=kn.get("norm_w"), eps=w.norm_eps, want_probs=want_probs)
+        outs.append(r["out"])
+        caches.append((r["k_cache"], r["v_cache"]))
+        qrots.append(r["q_rot"])
+        probs.append(r["probs"])
+    return dict(out=np.concatenate(outs), caches=caches, q_rot=np.concatenate(qrots), probs=probs)
+
+
+def oracle_rows(w, d, b, positions, heads=None):
+    """Oracle output of selected rows of sequence b (prompt starting at
+    position 0): finish the prefix's keys, finish the selected queries, attend.
+    Returns [len(positions)][nh][hd] (all heads)."""
+    f = oracle_table(w)
+    positions = np.asarray(sorted(positions), dtype=np.int64)
+    pmax = int(positions.max())
+    t0 = d["cu_seq"][b]
+    kn = norm_kwargs(w, d, "k_norm_w")
+    qn = norm_kwargs(w, d, "q_norm_w")
+    k_raw = np64(d["k"][t0:t0 + pmax + 1])
+    v_raw = np64(d["v"][t0:t0 + pmax + 1])
+    kc = oracle.finish_heads(k_raw, np.arange(pmax + 1), f, w.rd, w.rope_scale,
+                             store=store_of(w), **kn)
+    idx = torch.as_tensor(t0 + positions, device=d["q"].device)
+    q_raw = np64(d["q"][idx])
+    q = oracle.finish_heads(q_raw, positions, f, w.rd, w.rope_scale, store=store_of(w), **qn)
+    out, _ = oracle.attend(q, kc.transpose(1, 0, 2).copy(), v_raw.transpose(1, 0, 2).copy(),
+                           positions, w.scale)
+    return positions, out
+
+
+def check_bf16_rows(got: np.ndarray, ref: np.ndarray, label=""):
+    """Per-row criterion; returns (worst row err/rms, tensor-level max/rms, rel rmse)."""
+    got = got.reshape(-1, got.shape[-1])
+    ref = ref.reshape(-1, ref.shape[-1])
+    assert np.all(np.isfinite(got)), f"{label}: non-finite output"
+    rms = np.sqrt(np.mean(ref ** 2, axis=-1))
+    err = np.max(np.abs(got - ref), axis=-1)
+    worst = float(np.max(err / rms))
+    tensor = float(np.max(err) / np.sqrt(np.mean(ref ** 2)))
+    rrmse = float(np.sqrt(np.mean((got - ref) ** 2)) / np.sqrt(np.mean(ref ** 2)))
+    say(f"  {label}: worst row err/rms {worst:.3e}  tensor max/rms {tensor:.3e}  rel rmse {rrmse:.3e}")
+    assert worst <= BF16_ROW_TOL, f"{label}: worst row err/rms {worst}"
+    return worst, tensor, rrmse
+
+
+def check_f32(got: np.ndarray, ref: np.ndarray, label=""):
+    assert np.all(np.isfinite(got)), f"{label}: non-finite output"
+    e = float(np.max(np.abs(got - ref)))
+    say(f"  {label}: max abs err {e:.3e}")
+    assert e <= F32_ABS_TOL, f"{label}: max abs err {e}"
+    return e

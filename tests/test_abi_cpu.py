@@ -1,0 +1,177 @@
+"""CPU checks of the C ABI: the library loads, exports every function that
+include/attn.h declares, its host-side frequency tables agree with the oracle,
+and argument validation returns the documented status before any launch."""
+import ctypes
+import os
+import re
+
+import numpy as np
+import pytest
+
+import oracle
+from chunked_prefill_causal_rope_amd import api
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "attn.h")
+
+OK, EINVAL, ECAP, EUNSUP = 0, -1, -2, -3
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(attn_[a-z0-9_]+)\s*\(", text)))
+
+
+def test_library_exports_every_declared_symbol():
+    L = api.lib()
+    names = declared_functions()
+    assert len(names) >= 10
+    for n in names:
+        assert hasattr(L, n), f"{n} declared in attn.h but not exported"
+    assert set(api.EXPORTS) <= set(names)
+    assert L.attn_version().decode().count(".") == 2
+
+
+def test_status_strings():
+    L = api.lib()
+    for code in (OK, EINVAL, ECAP, EUNSUP, -4):
+        assert L.attn_status_string(code).decode() != "unknown status"
+    assert L.attn_status_string(123).decode() == "unknown status"
+
+
+@pytest.mark.parametrize("rd,base", [(4, 1e4), (64, 1e4), (128, 1e4), (64, 1e6), (128, 5e5), (32, 500.0)])
+def test_rope_table_matches_oracle(rd, base):
+    got = api.rope_inv_freq(rd, base).numpy()
+    ref = oracle.rope_inv_freq(rd, base)
+    ulps = np.abs(got.view(np.int32).astype(np.int64) - ref.view(np.int32).astype(np.int64))
+    assert ulps.max() <= 1, ulps.max()
+
+
+@pytest.mark.parametrize("args", [
+    (64, 5e5, 128.0, 8192, 32.0, 1.0),
+    (128, 1e6, 4.0, 32768, 32.0, 1.0),
+    (64, 1e4, 8.0, 4096, 32.0, 1.0),
+    (128, 1e4, 2.0, 2048, 16.0, 2.0),
+])
+def test_yarn_table_matches_oracle(args):
+    got = api.yarn_inv_freq(*args).numpy()
+    ref = oracle.yarn_inv_freq(*args)
+    ulps = np.abs(got.view(np.int32).astype(np.int64) - ref.view(np.int32).astype(np.int64))
+    assert ulps.max() <= 1, ulps.max()
+
+
+def test_table_argument_errors():
+    L = api.lib()
+    buf = (ctypes.c_float * 64)()
+    assert L.attn_rope_inv_freq(7, 1e4, buf) == EINVAL
+    assert L.attn_rope_inv_freq(0, 1e4, buf) == EINVAL
+    assert L.attn_rope_inv_freq(64, -1.0, buf) == EINVAL
+    assert L.attn_rope_inv_freq(64, 1e4, None) == EINVAL
+    assert L.attn_yarn_inv_freq(64, 1e4, 0.0, 4096, 32.0, 1.0, buf) == EINVAL
+    assert L.attn_yarn_inv_freq(64, 1e4, 4.0, 0, 32.0, 1.0, buf) == EINVAL
+
+
+# A fake device address: the validation paths below return before any HIP
+# call, so it is never dereferenced.
+P = ctypes.c_void_p(4096)
+
+
+def prefill(**kw):
+    a = dict(q=P, k=P, v=P, dtype=1, n_seq=1, nh=8, nkv=2, hd=128, cap=256, n_tok=16, cu=P, st=P,
+             max_chunk=16, max_end=64, scale=0.088, out=P, ws=None, wsb=0, stream=None)
+    a.update(kw)
+    return api.lib().attn_prefill_chunk(a["q"], a["k"], a["v"], a["dtype"], a["n_seq"], a["nh"],
+                                        a["nkv"], a["hd"], a["cap"], a["n_tok"], a["cu"], a["st"],
+                                        a["max_chunk"], a["max_end"], a["scale"], a["out"],
+                                        a["ws"], a["wsb"], a["stream"])
+
+
+def test_prefill_validation():
+    assert prefill(hd=96) == EUNSUP
+    assert prefill(dtype=5) == EUNSUP
+    assert prefill(nh=6, nkv=4) == EINVAL
+    assert prefill(nkv=0) == EINVAL
+    assert prefill(max_end=257) == ECAP
+    assert prefill(scale=float("nan")) == EINVAL
+    assert prefill(q=None) == EINVAL
+    assert prefill(cu=None) == EINVAL
+    # empty work: OK and nothing launched
+    assert prefill(n_tok=0) == OK
+    assert prefill(n_seq=0) == OK
+    assert prefill(max_chunk=0) == OK
+
+
+def append(**kw):
+    a = dict(kc=P, vc=P, dtype=1, n_seq=1, nkv=2, hd=128, cap=256, kn=P, vn=P, n_tok=16, cu=P,
+             st=P, max_chunk=16, max_end=64, f=P, rd=128, rs=1.0, norm=0, w=None, eps=1e-6)
+    a.update(kw)
+    return api.lib().attn_kv_append(a["kc"], a["vc"], a["dtype"], a["n_seq"], a["nkv"], a["hd"],
+                                    a["cap"], a["kn"], a["vn"], a["n_tok"], a["cu"], a["st"],
+                                    a["max_chunk"], a["max_end"], a["f"], a["rd"], a["rs"],
+                                    a["norm"], a["w"], a["eps"], None)
+
+
+def test_append_validation():
+    assert append(max_end=300) == ECAP
+    assert append(rd=63) == EINVAL
+    assert append(f=None) == EINVAL
+    assert append(norm=1, w=None) == EINVAL
+    assert append(norm=3, w=P) == EINVAL
+    assert append(hd=80) == EUNSUP
+    assert append(cap=0) == EINVAL
+    assert append(n_tok=0) == OK
+    assert append(rd=0, f=None, n_seq=0) == OK
+
+
+def rope(**kw):
+    a = dict(x=P, y=P, dtype=0, n_tok=4, nh=4, hd=64, n_seq=1, cu=P, st=P, max_chunk=4, f=P,
+             rd=64, rs=1.0, norm=0, w=None, eps=1e-6)
+    a.update(kw)
+    return api.lib().attn_rope_apply(a["x"], a["y"], a["dtype"], a["n_tok"], a["nh"], a["hd"],
+                                     a["n_seq"], a["cu"], a["st"], a["max_chunk"], a["f"], a["rd"],
+                                     a["rs"], a["norm"], a["w"], a["eps"], None)
+
+
+def test_rope_validation():
+    assert rope(hd=48) == EUNSUP
+    assert rope(nh=0) == EINVAL
+    assert rope(rd=3) == EINVAL
+    assert rope(n_tok=-1) == EINVAL
+    assert rope(x=None) == EINVAL
+    assert rope(norm=2, w=None) == EINVAL
+    assert rope(n_seq=0) == OK
+    assert rope(max_chunk=0) == OK
+
+
+def decode(**kw):
+    a = dict(q=P, k=P, v=P, dtype=1, n_seq=4, nh=32, nkv=8, hd=128, cap=4096, ctx=P, max_ctx=4096,
+             scale=0.088, out=P, probs=None, ld=0, ws=P, wsb=1 << 30)
+    a.update(kw)
+    return api.lib().attn_decode(a["q"], a["k"], a["v"], a["dtype"], a["n_seq"], a["nh"],
+                                 a["nkv"], a["hd"], a["cap"], a["ctx"], a["max_ctx"], a["scale"],
+                                 a["out"], a["probs"], a["ld"], a["ws"], a["wsb"], None)
+
+
+def test_decode_validation():
+    assert decode(max_ctx=4097) == ECAP
+    assert decode(probs=P, ld=100) == EINVAL
+    assert decode(nh=34) == EINVAL
+    assert decode(nh=64, nkv=2) == EUNSUP        # 32 query heads per KV head
+    assert decode(ws=None, wsb=0) == EINVAL      # bf16 needs a workspace
+    assert decode(wsb=16) == EINVAL
+    assert decode(hd=256) == EUNSUP
+    assert decode(n_seq=0) == OK
+    assert decode(max_ctx=0) == OK
+
+
+def test_workspace_sizes():
+    L = api.lib()
+    # decode: one part per 1024 keys
+    assert L.attn_decode_workspace_bytes(64, 32, 8, 128, 32768) == 64 * 32 * 32 * 132 * 4
+    assert L.attn_decode_workspace_bytes(0, 32, 8, 128, 32768) == 0
+    # prefill: a large grid needs no split
+    assert L.attn_prefill_workspace_bytes(1, 64, 8, 128, 2048, 2048, 4096) == 0
+    # a small chunk over a long context splits the key range
+    n = L.attn_prefill_workspace_bytes(1, 32, 8, 128, 128, 128, 4096)
+    assert n > 0 and n % (128 * 32 * 132 * 4) == 0

@@ -1,0 +1,313 @@
+"""GPU parity: every library entry point against the CPU oracle on the same
+seeded inputs.  Bars: bit-exact cache layout (V rows, untouched rows), K and
+rotated Q equal to the oracle's correctly rounded values, f32 outputs within
+1e-4 absolute, bf16 outputs within 2e-2 of each output row's RMS."""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from chunked_prefill_causal_rope_amd import api, runner, workloads as wl
+from parity_util import (check_bf16_rows, check_f32, np64, oracle_prefill_packed, oracle_table,
+                         say, store_of)
+
+pytestmark = pytest.mark.gpu
+
+DEV = "cuda:0"
+
+
+@pytest.fixture(autouse=True)
+def _gpu():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    torch.cuda.set_device(0)
+    yield
+    torch.cuda.synchronize()
+
+
+def _bits(t: torch.Tensor) -> np.ndarray:
+    t = t.detach().cpu().contiguous()
+    if t.dtype == torch.bfloat16:
+        return t.view(torch.int16).numpy()
+    return t.view(torch.int32).numpy()
+
+
+def _to_dtype_bits(x: np.ndarray, dtype) -> np.ndarray:
+    return _bits(torch.from_numpy(x).to(dtype))
+
+
+# ------------------------------------------------------------------ RoPE
+
+@pytest.mark.parametrize("dtype", [wl.F32, wl.BF16])
+@pytest.mark.parametrize("hd,rd,norm,scale", [
+    (128, 128, wl.NORM_NONE, 1.0),
+    (128, 64, wl.NORM_W, 1.0),
+    (64, 64, wl.NORM_1PW, 1.1386294),
+    (128, 32, wl.NORM_NONE, 1.1386294),
+])
+def test_rope_apply_matches_oracle(dtype, hd, rd, norm, scale):
+    # rope_scale crosses the ABI as a float (the page's f32 field): the oracle
+    # gets that same float value
+    scale = float(np.float32(scale))
+    say(f"rope_apply dtype={dtype} hd={hd} rd={rd} norm={norm} scale={scale}")
+    w = wl.Workload(name="rope", dtype=dtype, n_heads=6, n_kv=2, head_dim=hd, seed=11,
+                    rotary_dim=rd, norm_style=norm, rope_scale=scale, base=1e4,
+                    n_seq=3, len_range=(1, 40), chunk=40)
+    d = wl.gen_prefill(w)
+    starts = [0, 17, 131000]
+    batch = api.Batch(starts, d["lengths"], device=DEV)
+    x = d["q"].to(DEV)
+    y = torch.full_like(x, float("nan"))
+    f = runner.tables(w, DEV)
+    qw = d["q_norm_w"].to(DEV) if norm else None
+    api.rope_apply(x, y, batch, f, rd, scale, norm, qw, w.norm_eps)
+    torch.cuda.synchronize()
+    pos = np.concatenate([np.arange(s, s + n) for s, n in zip(starts, d["lengths"])])
+    kw = dict(norm_style=norm, norm_w=d["q_norm_w"].numpy() if norm else None, eps=w.norm_eps)
+    ref = oracle.finish_heads(np64(d["q"]), pos, oracle_table(w), rd, scale, store=store_of(w), **kw)
+    diff = _bits(y) != _to_dtype_bits(ref, w.torch_dtype)
+    say(f"  mismatching elements: {int(diff.sum())} of {diff.size}")
+    # double arithmetic on both sides: the stored values agree bit for bit
+    # except where the exact value sits within ~1e-16 of a rounding boundary
+    assert diff.sum() <= max(1, diff.size // 100000)
+    # in place gives the same bits
+    x2 = x.clone()
+    api.rope_apply(x2, x2, batch, f, rd, scale, norm, qw, w.norm_eps)
+    torch.cuda.synchronize()
+    assert np.array_equal(_bits(x2), _bits(y))
+
+
+# ------------------------------------------------------------------ append
+
+@pytest.mark.parametrize("dtype", [wl.F32, wl.BF16])
+def test_kv_append_layout_and_sentinels(dtype):
+    say(f"kv_append layout dtype={dtype}")
+    w = wl.Workload(name="app", dtype=dtype, n_heads=8, n_kv=4, head_dim=128, seed=12,
+                    rotary_dim=128, base=1e4, n_seq=3, len_range=(5, 70), chunk=70,
+                    norm_style=wl.NORM_W)
+    d = wl.gen_prefill(w)
+    cap = 300
+    starts = [0, 100, cap - d["lengths"][2]]
+    batch = api.Batch(starts, d["lengths"], device=DEV)
+    kc = torch.full((3, w.n_kv, cap, w.head_dim), float("nan"), dtype=w.torch_dtype, device=DEV)
+    vc = torch.full_like(kc, float("nan"))
+    before_k, before_v = _bits(kc), _bits(vc)
+    f = runner.tables(w, DEV)
+    api.kv_append(kc, vc, d["k"].to(DEV), d["v"].to(DEV), batch, f, w.rd, 1.0, w.norm_style,
+                  d["k_norm_w"].to(DEV), w.norm_eps)
+    torch.cuda.synchronize()
+    gk, gv = _bits(kc), _bits(vc)
+    written = np.zeros(kc.shape[:3], dtype=bool)
+    cu = d["cu_seq"]
+    mism = 0
+    for b, (s, n) in enumerate(zip(starts, d["lengths"])):
+        written[b, :, s:s + n] = True
+        rows = slice(cu[b], cu[b] + n)
+        pos = np.arange(s, s + n)
+        ref = oracle.finish_heads(np64(d["k"][rows]), pos, oracle_table(w), w.rd, 1.0,
+                                  norm_style=w.norm_style, norm_w=d["k_norm_w"].numpy(),
+                                  eps=w.norm_eps, store=store_of(w))
+        want_k = _to_dtype_bits(ref.transpose(1, 0, 2).copy(), w.torch_dtype)
+        mism += int((gk[b, :, s:s + n] != want_k).sum())
+        want_v = _bits(d["v"][rows].transpose(0, 1).contiguous())
+        assert np.array_equal(gv[b, :, s:s + n], want_v), "V rows must be a bit copy"
+    say(f"  K mismatching elements: {mism}")
+    assert mism <= 1
+    # every row outside the appended ranges keeps its sentinel bits
+    assert np.array_equal(gk[~written], before_k[~written])
+    assert np.array_equal(gv[~written], before_v[~written])
+
+
+# ------------------------------------------------------------------ f32 path
+
+def test_c0_f32_prefill_and_sequential_probs():
+    w = wl.CONFIGS["c0_f32_small"]
+    say(f"c0 f32 prefill {w}")
+    d = wl.gen_prefill(w)
+    ref_seq = oracle_prefill_packed(w, d, 1, want_probs=True)
+    for chunk in (16, 1, 64, 7):
+        run = runner.ChunkedPrefill(w, d, device=DEV, chunk=chunk)
+        run.run_all()
+        torch.cuda.synchronize()
+        check_f32(np64(run.gather("out")), ref_seq["out"], f"chunk {chunk}")
+    # per-position probabilities: 64 decode calls, one per position
+    f = runner.tables(w, DEV)
+    kc = torch.zeros((1, w.n_kv, 64, w.head_dim), dtype=torch.float32, device=DEV)
+    vc = torch.zeros_like(kc)
+    q = d["q"].to(DEV)
+    k = d["k"].to(DEV)
+    v = d["v"].to(DEV)
+    ws = torch.empty(1 << 16, dtype=torch.float32, device=DEV)
+    P_ref = ref_seq["probs"][0]
+    worst_p = 0.0
+    for p in range(64):
+        batch = api.Batch([p], [1], device=DEV)
+        qr = torch.empty_like(q[p:p + 1])
+        api.rope_apply(q[p:p + 1].contiguous(), qr, batch, f, w.rd)
+        api.kv_append(kc, vc, k[p:p + 1].contiguous(), v[p:p + 1].contiguous(), batch, f, w.rd)
+        out = torch.empty((1, w.n_heads, w.head_dim), dtype=torch.float32, device=DEV)
+        probs = torch.full((1, w.n_heads, 64), float("nan"), device=DEV)
+        ctx = torch.tensor([p + 1], dtype=torch.int32, device=DEV)
+        api.decode(qr, kc, vc, ctx, p + 1, w.scale, out, probs, ws)
+        torch.cuda.synchronize()
+        check_f32(np64(out)[0], ref_seq["out"][p], f"decode pos {p}") if p % 16 == 0 else None
+        assert float(np.max(np.abs(np64(out)[0] - ref_seq["out"][p]))) <= 1e-4
+        pg = np64(probs)[0]
+        assert np.all(np.isnan(pg[:, p + 1:])), "entries past ctx must stay untouched"
+        dp = np.max(np.abs(pg[:, :p + 1] - P_ref[p, :, :p + 1]))
+        worst_p = max(worst_p, float(dp))
+        assert np.allclose(pg[:, :p + 1].sum(-1), 1.0, atol=1e-5)
+    say(f"  probs max abs err {worst_p:.3e}")
+    assert worst_p <= 1e-4
+
+
+# ------------------------------------------------------------------ bf16 prefill
+
+CASES = [
+    # name, nh, nkv, hd, T, chunk
+    ("gqa4_hd128", 8, 2, 128, 300, 128),
+    ("gqa4_hd128_small_chunks", 8, 2, 128, 200, 16),
+    ("mha_hd64", 3, 3, 64, 190, 64),
+    ("gqa5_hd128", 10, 2, 128, 261, 96),
+    ("gqa8_hd64", 16, 2, 64, 130, 130),
+    ("gqa1_long_split", 2, 2, 128, 2100, 37),
+]
+
+
+@pytest.mark.parametrize("name,nh,nkv,hd,T,chunk", CASES)
+def test_bf16_prefill_matches_oracle(name, nh, nkv, hd, T, chunk):
+    say(f"bf16 prefill {name}: nh={nh} nkv={nkv} hd={hd} T={T} chunk={chunk}")
+    w = wl.Workload(name=name, dtype=wl.BF16, n_heads=nh, n_kv=nkv, head_dim=hd, seed=21,
+                    prompt_len=T, chunk=chunk)
+    d = wl.gen_prefill(w)
+    run = runner.ChunkedPrefill(w, d, device=DEV)
+    run.run_all()
+    torch.cuda.synchronize()
+    ref = oracle_prefill_packed(w, d, chunk)
+    check_bf16_rows(np64(run.gather("out")), ref["out"], name)
+    # the rotated queries and the cache equal the oracle's rounded values
+    assert np.array_equal(_bits(run.gather("q_rot")), _to_dtype_bits(ref["q_rot"], torch.bfloat16))
+    kc_ref, vc_ref = ref["caches"][0]
+    assert np.array_equal(_bits(run.k_cache[0]), _to_dtype_bits(kc_ref, torch.bfloat16))
+    assert np.array_equal(_bits(run.v_cache[0]), _to_dtype_bits(vc_ref, torch.bfloat16))
+
+
+def test_bf16_varlen_qknorm_partial_rotary():
+    w = wl.Workload(name="varlen", dtype=wl.BF16, n_heads=10, n_kv=2, head_dim=128, seed=23,
+                    base=1e6, rotary_dim=64, norm_style=wl.NORM_W, n_seq=4, len_range=(40, 700),
+                    chunk=256, cap=700)
+    say(f"bf16 varlen {w}")
+    d = wl.gen_prefill(w)
+    run = runner.ChunkedPrefill(w, d, device=DEV)
+    run.run_all()
+    torch.cuda.synchronize()
+    ref = oracle_prefill_packed(w, d, 256)
+    check_bf16_rows(np64(run.gather("out")), ref["out"], "varlen")
+
+
+def test_bf16_chunked_equals_sequential():
+    w = wl.Workload(name="seq", dtype=wl.BF16, n_heads=8, n_kv=2, head_dim=128, seed=24,
+                    prompt_len=160, chunk=64)
+    d = wl.gen_prefill(w)
+    outs = {}
+    for chunk in (1, 2, 64, 160):
+        run = runner.ChunkedPrefill(w, d, device=DEV, chunk=chunk)
+        run.run_all()
+        torch.cuda.synchronize()
+        outs[chunk] = np64(run.gather("out"))
+        caches = (_bits(run.k_cache), _bits(run.v_cache))
+        if chunk == 1:
+            ref_caches = caches
+        else:
+            # the cache does not depend on the chunking, bit for bit
+            assert np.array_equal(caches[0], ref_caches[0])
+            assert np.array_equal(caches[1], ref_caches[1])
+    ref = oracle_prefill_packed(w, d, 1)["out"]
+    for chunk, o in outs.items():
+        check_bf16_rows(o, ref, f"chunk {chunk}")
+
+
+def test_empty_and_single_token():
+    w = wl.Workload(name="one", dtype=wl.BF16, n_heads=4, n_kv=1, head_dim=64, seed=25,
+                    prompt_len=1, chunk=1)
+    d = wl.gen_prefill(w)
+    run = runner.ChunkedPrefill(w, d, device=DEV)
+    run.run_all()
+    torch.cuda.synchronize()
+    # position 0 attends only itself: the output is V0 exactly
+    v0 = np64(d["v"][0])
+    got = np64(run.gather("out"))[0]
+    for h in range(4):
+        assert np.array_equal(got[h], v0[0])
+    # an empty batch is a no-op
+    out = torch.full((1, 4, 64), 7.0, device=DEV)
+    empty = api.Batch([0], [0], device=DEV)
+    api.prefill_chunk(run.steps[0]["q_rot"], run.k_cache, run.v_cache, empty, w.scale, out)
+    torch.cuda.synchronize()
+    assert torch.all(out == 7.0)
+
+
+# ------------------------------------------------------------------ bf16 decode
+
+@pytest.mark.parametrize("nh,nkv,hd", [(16, 4, 128), (16, 2, 64), (8, 8, 128), (40, 8, 128)])
+def test_bf16_decode_matches_oracle(nh, nkv, hd):
+    ctx = [1, 63, 64, 65, 1025, 3000]
+    w = wl.Workload(name="dec", dtype=wl.BF16, n_heads=nh, n_kv=nkv, head_dim=hd, seed=31,
+                    n_seq=len(ctx), decode=True, ctx_range=(1, 3000), cap=3072, want_probs=True)
+    say(f"bf16 decode nh={nh} nkv={nkv} hd={hd} ctx={ctx}")
+    d = wl.gen_decode(w)
+    d["ctx"] = ctx
+    step = runner.DecodeStep(w, d, device=DEV)
+    step.probs.fill_(float("nan"))
+    step.run()
+    torch.cuda.synchronize()
+    f = oracle_table(w)
+    got_o = np64(step.out)
+    got_p = np64(step.probs)
+    for b, c in enumerate(ctx):
+        pos = np.array([c - 1])
+        kc = np64(d["k_cache"][b])[:, :c].copy()
+        vc = np64(d["v_cache"][b])[:, :c].copy()
+        kc[:, c - 1] = oracle.finish_heads(np64(d["k"][b:b + 1]), pos, f, w.rd,
+                                           store=oracle.STORE_BF16)[0]
+        vc[:, c - 1] = np64(d["v"][b])
+        q = oracle.finish_heads(np64(d["q"][b:b + 1]), pos, f, w.rd, store=oracle.STORE_BF16)
+        o, P = oracle.attend(q, kc, vc, pos, w.scale, want_probs=True)
+        check_bf16_rows(got_o[b], o[0], f"seq {b} ctx {c}")
+        pg = got_p[b, :, :c]
+        assert np.all(np.isnan(got_p[b, :, c:])), "entries past ctx must stay untouched"
+        assert np.allclose(pg.sum(-1), 1.0, atol=1e-5)
+        dp = np.max(np.abs(pg - P[0]), axis=-1) / np.sqrt(np.mean(P[0] ** 2, axis=-1))
+        assert dp.max() <= 2e-2, dp.max()
+    # the new token's K/V rows were appended at ctx-1
+    for b, c in enumerate(ctx):
+        assert np.array_equal(_bits(step.v_cache[b, :, c - 1]), _bits(d["v"][b]))
+
+
+# ------------------------------------------------------------------ graphs
+
+def test_graph_replay_matches_eager():
+    w = wl.Workload(name="graph", dtype=wl.BF16, n_heads=8, n_kv=2, head_dim=128, seed=41,
+                    prompt_len=512, chunk=128)
+    d = wl.gen_prefill(w)
+    run = runner.ChunkedPrefill(w, d, device=DEV)
+    run.run_all()
+    torch.cuda.synchronize()
+    eager = run.gather("out").clone()
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.stream(s):
+        run.run_all()  # warm-up on the capture stream
+        torch.cuda.synchronize()
+        with torch.cuda.graph(g, stream=s):
+            run.run_all()
+    torch.cuda.current_stream().wait_stream(s)
+    for rep in range(4):
+        for st in run.steps:
+            st["out"].fill_(float("nan"))
+        junk = torch.randn(1 << 20, device=DEV).sum()  # eager work between replays
+        g.replay()
+        torch.cuda.synchronize()
+        assert torch.isfinite(junk)
+        assert torch.equal(run.gather("out"), eager), f"replay {rep} differs from eager"
