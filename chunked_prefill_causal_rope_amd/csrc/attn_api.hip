@@ -29,7 +29,7 @@ int check_rope(int dtype, int n_tok, int n_heads, int head_dim, int n_seq, const
     if (norm < ATTN_NORM_NONE || norm > ATTN_NORM_1PW) return ATTN_EINVAL;
     if (norm != ATTN_NORM_NONE && !norm_w) return ATTN_EINVAL;
     if (n_seq > 0 && (!cu_seq || !start)) return ATTN_EINVAL;
-    if (n_seq > 65535) return ATTN_EINVAL;   // grid y
+    if (n_seq > 65535) return ATTN_EINVAL;   // grid z
     return ATTN_OK;
 }
 

@@ -265,8 +265,23 @@ __global__ __launch_bounds__(256) void decode_combine_kernel(DecodeArgs a) {
         orow[d] = acc * inv;
     }
     if (a.probs) {
+        // P_j = 2^(x_j - m) / l over the row's ctx entries; 16-byte accesses
+        // between a scalar head (up to the first aligned element) and tail
         float* prow = a.probs + (size_t)row * a.probs_ld;
-        for (int j = tid; j < ctx; j += 256) prow[j] = __builtin_amdgcn_exp2f(prow[j] - m) * inv;
+        const int head = min((int)((4 - (((uintptr_t)prow >> 2) & 3)) & 3), ctx);
+        for (int j = tid; j < head; j += 256) prow[j] = __builtin_amdgcn_exp2f(prow[j] - m) * inv;
+        float4* p4 = reinterpret_cast<float4*>(prow + head);
+        const int n4 = (ctx - head) >> 2;
+        for (int j = tid; j < n4; j += 256) {
+            float4 v = p4[j];
+            v.x = __builtin_amdgcn_exp2f(v.x - m) * inv;
+            v.y = __builtin_amdgcn_exp2f(v.y - m) * inv;
+            v.z = __builtin_amdgcn_exp2f(v.z - m) * inv;
+            v.w = __builtin_amdgcn_exp2f(v.w - m) * inv;
+            p4[j] = v;
+        }
+        for (int j = head + 4 * n4 + tid; j < ctx; j += 256)
+            prow[j] = __builtin_amdgcn_exp2f(prow[j] - m) * inv;
     }
 }
 

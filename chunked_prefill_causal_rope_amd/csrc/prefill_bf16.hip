@@ -51,19 +51,34 @@ constexpr float kRescaleSlack = 8.f;
 
 template <int HD>
 struct PrefillSmem {
-    static constexpr int KS = HD + 8;   // K row stride in bf16 (16 B pad)
-    static constexpr int VS = kTK + 4;  // V^T row stride in bf16: 34 dwords,
-                                        // 32 rows land on distinct bank pairs
+    // K rows padded by 16 B: the 32 rows of an A-operand read start on
+    // distinct 4-bank groups.  V rows padded by 64 B: the 8 rows of a
+    // transposing read (4 keys per 16-lane group, two groups per half-wave)
+    // start 16 banks apart.
+    static constexpr int KS = HD + 8;
+    static constexpr int VS = HD + 32;
     uint16_t k[2][kTK * KS];
-    uint16_t vt[2][HD * VS];
+    uint16_t v[2][kTK * VS];
 };
 
 __device__ __forceinline__ f32x16_t mfma32(bf16x8_t a, bf16x8_t b, f32x16_t c) {
     return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
 }
 
+typedef short s16x4_t __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) s16x4_t lds_s16x4_t;
+
+// LDS transposing read: within each 16-lane group, lane j receives element j
+// (then j+16, j+32, j+48) of the 64 16-bit values the group's lanes point at,
+// 4 per lane in lane order.  Pointing lane a at V[k0 + a/4][d0 + 4(a%4)]
+// therefore hands lane j the column V[k0 .. k0+3][d0 + j].
+__device__ __forceinline__ uint2 lds_read_tr16(const uint16_t* p) {
+    const s16x4_t v = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4_t*)(p));
+    return __builtin_bit_cast(uint2, v);
+}
+
 // Sum of the two bfloat16 halves of each packed word, exactly (products by 1).
-__device__ __forceinline__ float sum_bf16_pairs(const uint32_t* pk, int n) {
+__device__ __forceinline__ float sum_bf16_pairs(const uint32_t* pk) {
     const bf16x2_t one = __builtin_bit_cast(bf16x2_t, 0x3f803f80u);
     float s0 = 0.f, s1 = 0.f;
 #pragma unroll
@@ -74,18 +89,15 @@ __device__ __forceinline__ float sum_bf16_pairs(const uint32_t* pk, int n) {
     return s0 + s1;
 }
 
-// QB: 32-row blocks of query rows per wave (1 or 2).  Each wave holds QB rows
-// per lane; a K or V^T fragment read from LDS feeds QB matrix products.
-template <int HD, int QB>
-__global__ __launch_bounds__(kThreads, QB == 1 ? 2 : 1) void prefill_bf16_kernel(PrefillArgs a) {
+template <int HD>
+__global__ __launch_bounds__(kThreads, 2) void prefill_bf16_kernel(PrefillArgs a) {
     using Sm = PrefillSmem<HD>;
     constexpr int KS = Sm::KS;
     constexpr int VS = Sm::VS;
     constexpr int CH = HD / 8;                    // 16-byte chunks per cache row
-    constexpr int KCH = kTK * CH / kThreads;      // K chunks per thread
-    constexpr int VITEMS = (kTK / 4) * CH;        // (4-key, 8-dim) blocks of V
+    constexpr int NCH = kTK * CH / kThreads;      // K (and V) chunks per thread
     constexpr int NDB = HD / 32;                  // 32-dim blocks of O
-    constexpr int TILE_ROWS = kWaves * 32 * QB;   // query rows per workgroup
+    constexpr int TILE_ROWS = kWaves * 32;        // query rows per workgroup
     __shared__ Sm sm;
 
     const int tid = threadIdx.x;
@@ -118,33 +130,27 @@ __global__ __launch_bounds__(kThreads, QB == 1 ? 2 : 1) void prefill_bf16_kernel
     const int tb = s * per;
     const int te = min(tb + per, n_tiles);
 
-    // this wave's rows: blocks of 32, row = r_tile0 + wave*32*QB + qb*32 + rl
-    const int rw0 = r_tile0 + wave * 32 * QB;
+    // this lane's query row (position-major within the group) and its wave's
+    const int r = r_tile0 + wave * 32 + rl;
+    const int i = r / G;
+    const int t = t0 + i;
+    const int h = g * G + (r - i * G);
+    const bool row_ok = r < rows_b && t >= 0 && t < a.n_tok;
+    const int pos = row_ok ? p0 + i : -1;
+    const int rw0 = r_tile0 + wave * 32;
     const bool wave_ok = rw0 < rows_b;
     const int pw_lo = p0 + rw0 / G;
-    const int pw_hi = p0 + min(rw0 + 32 * QB - 1, rows_b - 1) / G;
-    int pos[QB], tq[QB], hq[QB];
-    bool ok[QB];
-#pragma unroll
-    for (int qb = 0; qb < QB; ++qb) {
-        const int r = rw0 + qb * 32 + rl;
-        const int i = r / G;
-        tq[qb] = t0 + i;
-        hq[qb] = g * G + (r - i * G);
-        ok[qb] = r < rows_b && tq[qb] >= 0 && tq[qb] < a.n_tok;
-        pos[qb] = ok[qb] ? p0 + i : -1;
-    }
+    const int pw_hi = p0 + min(rw0 + 31, rows_b - 1) / G;
 
-    bf16x8_t qf[QB][HD / 16];
-#pragma unroll
-    for (int qb = 0; qb < QB; ++qb) {
+    bf16x8_t qf[HD / 16];
+    {
         const uint16_t* qrow =
-            reinterpret_cast<const uint16_t*>(a.q) + ((size_t)tq[qb] * a.n_heads + hq[qb]) * HD;
+            reinterpret_cast<const uint16_t*>(a.q) + ((size_t)t * a.n_heads + h) * HD;
 #pragma unroll
         for (int k = 0; k < HD / 16; ++k) {
             uint4 u = make_uint4(0, 0, 0, 0);
-            if (ok[qb]) u = *reinterpret_cast<const uint4*>(qrow + 16 * k + 8 * hf);
-            qf[qb][k] = __builtin_bit_cast(bf16x8_t, u);
+            if (row_ok) u = *reinterpret_cast<const uint4*>(qrow + 16 * k + 8 * hf);
+            qf[k] = __builtin_bit_cast(bf16x8_t, u);
         }
     }
 
@@ -152,75 +158,43 @@ __global__ __launch_bounds__(kThreads, QB == 1 ? 2 : 1) void prefill_bf16_kernel
     const uint16_t* kc = reinterpret_cast<const uint16_t*>(a.k_cache) + kvbase;
     const uint16_t* vc = reinterpret_cast<const uint16_t*>(a.v_cache) + kvbase;
 
-    // V^T staging: thread -> (4-key group kq, 8-dim chunk ch), kq fastest so a
-    // wave's transposed 8-byte stores spread over the LDS banks
-    const int v_kq = tid % (kTK / 4);
-    const int v_ch = tid / (kTK / 4);
-    uint4 kreg[KCH];
-    uint32_t vreg[4][4];
+    // staging: thread -> NCH (row, 16-byte chunk) pairs of each of K and V;
+    // rows past the last key are zero-filled and never read from memory
+    uint4 kreg[NCH], vreg[NCH];
     auto load_tile = [&](int j) {
         const int k0 = j * kTK;
 #pragma unroll
-        for (int c = 0; c < KCH; ++c) {
+        for (int c = 0; c < NCH; ++c) {
             const int idx = c * kThreads + tid;
             const int key = k0 + idx / CH;
-            const int ch = idx % CH;
-            kreg[c] = key < n_keys ? *reinterpret_cast<const uint4*>(kc + (size_t)key * HD + ch * 8)
-                                   : make_uint4(0, 0, 0, 0);
-        }
-        if (tid < VITEMS) {
-#pragma unroll
-            for (int jj = 0; jj < 4; ++jj) {
-                const int key = k0 + 4 * v_kq + jj;
-                uint4 u = key < n_keys
-                              ? *reinterpret_cast<const uint4*>(vc + (size_t)key * HD + v_ch * 8)
-                              : make_uint4(0, 0, 0, 0);
-                vreg[jj][0] = u.x;
-                vreg[jj][1] = u.y;
-                vreg[jj][2] = u.z;
-                vreg[jj][3] = u.w;
-            }
+            const size_t off = (size_t)key * HD + (idx % CH) * 8;
+            const bool in = key < n_keys;
+            kreg[c] = in ? *reinterpret_cast<const uint4*>(kc + off) : make_uint4(0, 0, 0, 0);
+            vreg[c] = in ? *reinterpret_cast<const uint4*>(vc + off) : make_uint4(0, 0, 0, 0);
         }
     };
     auto store_tile = [&](int buf) {
 #pragma unroll
-        for (int c = 0; c < KCH; ++c) {
+        for (int c = 0; c < NCH; ++c) {
             const int idx = c * kThreads + tid;
             const int kr = idx / CH;
             const int ch = idx % CH;
             *reinterpret_cast<uint4*>(&sm.k[buf][kr * KS + ch * 8]) = kreg[c];
-        }
-        if (tid < VITEMS) {
-#pragma unroll
-            for (int e = 0; e < 8; ++e) {
-                const int w = e >> 1;
-                uint32_t lo, hi;
-                if ((e & 1) == 0) {
-                    lo = (vreg[0][w] & 0xffffu) | (vreg[1][w] << 16);
-                    hi = (vreg[2][w] & 0xffffu) | (vreg[3][w] << 16);
-                } else {
-                    lo = (vreg[0][w] >> 16) | (vreg[1][w] & 0xffff0000u);
-                    hi = (vreg[2][w] >> 16) | (vreg[3][w] & 0xffff0000u);
-                }
-                *reinterpret_cast<uint2*>(&sm.vt[buf][(v_ch * 8 + e) * VS + 4 * v_kq]) =
-                    make_uint2(lo, hi);
-            }
+            *reinterpret_cast<uint4*>(&sm.v[buf][kr * VS + ch * 8]) = vreg[c];
         }
     };
 
-    f32x16_t O[QB][NDB];
+    // transposing-read address of this lane inside a V tile, relative to the
+    // 16-key block: group lane a = lane % 16 points at key a/4, dims 4(a%4)
+    const int tr_off = ((lane & 15) >> 2) * VS + 4 * (lane & 3) + 16 * ((lane >> 4) & 1);
+
+    f32x16_t O[NDB];
 #pragma unroll
-    for (int qb = 0; qb < QB; ++qb)
+    for (int db = 0; db < NDB; ++db)
 #pragma unroll
-        for (int db = 0; db < NDB; ++db)
-#pragma unroll
-            for (int q = 0; q < 16; ++q) O[qb][db][q] = 0.f;
-    float m_run[QB], l_run[QB];
-#pragma unroll
-    for (int qb = 0; qb < QB; ++qb) {
-        m_run[qb] = -INFINITY;
-        l_run[qb] = 0.f;
-    }
+        for (int q = 0; q < 16; ++q) O[db][q] = 0.f;
+    float m_run = -INFINITY;
+    float l_run = 0.f;
     const float sl = a.scale * kLog2e;
 
     if (tb < te) {
@@ -232,16 +206,14 @@ __global__ __launch_bounds__(kThreads, QB == 1 ? 2 : 1) void prefill_bf16_kernel
             if (j + 1 < te) load_tile(j + 1);
             const int k0 = j * kTK;
             if (wave_ok && k0 <= pw_hi) {
-                // ---- S^T = K Q^T: 64 keys x the lane's QB rows
+                // ---- S^T = K Q^T for 64 keys x this lane's row
                 const uint16_t* kl = sm.k[buf];
-                f32x16_t S[QB][2];
+                f32x16_t S0, S1;
 #pragma unroll
-                for (int qb = 0; qb < QB; ++qb)
-#pragma unroll
-                    for (int q = 0; q < 16; ++q) {
-                        S[qb][0][q] = 0.f;
-                        S[qb][1][q] = 0.f;
-                    }
+                for (int q = 0; q < 16; ++q) {
+                    S0[q] = 0.f;
+                    S1[q] = 0.f;
+                }
 #pragma unroll
                 for (int kk = 0; kk < HD / 16; ++kk) {
                     const bf16x8_t a0 = __builtin_bit_cast(
@@ -249,80 +221,68 @@ __global__ __launch_bounds__(kThreads, QB == 1 ? 2 : 1) void prefill_bf16_kernel
                     const bf16x8_t a1 = __builtin_bit_cast(
                         bf16x8_t,
                         *reinterpret_cast<const uint4*>(kl + (32 + rl) * KS + kk * 16 + hf * 8));
+                    S0 = mfma32(a0, qf[kk], S0);
+                    S1 = mfma32(a1, qf[kk], S1);
+                }
+                // ---- causal mask on tiles that cross the diagonal: element q
+                // of S0 is key k0 + 8(q/4) + 4hf + q%4, of S1 that plus 32
+                if (k0 + kTK - 1 > pw_lo) {
+                    const int lim = pos - k0 - 4 * hf;
 #pragma unroll
-                    for (int qb = 0; qb < QB; ++qb) {
-                        S[qb][0] = mfma32(a0, qf[qb][kk], S[qb][0]);
-                        S[qb][1] = mfma32(a1, qf[qb][kk], S[qb][1]);
+                    for (int q = 0; q < 16; ++q) {
+                        const int off = 8 * (q >> 2) + (q & 3);
+                        if (off > lim) S0[q] = -INFINITY;
+                        if (off + 32 > lim) S1[q] = -INFINITY;
                     }
                 }
-                // ---- causal mask (diagonal tiles only), online softmax
-                const bool need_mask = k0 + kTK - 1 > pw_lo;
-                uint32_t pk[QB][16];
+                // ---- online softmax
+                float mx = fmaxf(S0[0], S1[0]);
 #pragma unroll
-                for (int qb = 0; qb < QB; ++qb) {
-                    if (need_mask) {
+                for (int q = 1; q < 16; ++q) mx = fmaxf(mx, fmaxf(S0[q], S1[q]));
+                mx = fmaxf(mx, __shfl_xor(mx, 32));
+                const float mt = mx * sl;                 // log2 units; -inf stays
+                const bool grow = mt > m_run + kRescaleSlack;
+                const float m_new = grow ? mt : m_run;
+                const float m_use = m_new == -INFINITY ? 0.f : m_new;
+                if (__any(grow)) {
+                    const float alpha = grow ? __builtin_amdgcn_exp2f(m_run - m_use) : 1.f;
+                    l_run *= alpha;
 #pragma unroll
-                        for (int q = 0; q < 16; ++q) {
-                            const int key = k0 + 8 * (q >> 2) + 4 * hf + (q & 3);
-                            if (key > pos[qb]) S[qb][0][q] = -INFINITY;
-                            if (key + 32 > pos[qb]) S[qb][1][q] = -INFINITY;
-                        }
-                    }
-                    float mx = S[qb][0][0];
+                    for (int db = 0; db < NDB; ++db)
 #pragma unroll
-                    for (int q = 1; q < 16; ++q) mx = fmaxf(mx, S[qb][0][q]);
-#pragma unroll
-                    for (int q = 0; q < 16; ++q) mx = fmaxf(mx, S[qb][1][q]);
-                    mx = fmaxf(mx, __shfl_xor(mx, 32));
-                    const float mt = mx * sl;             // log2 units; -inf stays
-                    const bool grow = mt > m_run[qb] + kRescaleSlack;
-                    const float m_new = grow ? mt : m_run[qb];
-                    const float m_use = m_new == -INFINITY ? 0.f : m_new;
-                    if (__any(grow)) {
-                        const float alpha = grow ? __builtin_amdgcn_exp2f(m_run[qb] - m_use) : 1.f;
-                        l_run[qb] *= alpha;
-#pragma unroll
-                        for (int db = 0; db < NDB; ++db)
-#pragma unroll
-                            for (int q = 0; q < 16; ++q) O[qb][db][q] *= alpha;
-                    }
-                    m_run[qb] = m_new;
-                    const float nm = -m_use;
-#pragma unroll
-                    for (int q = 0; q < 8; ++q) {
-                        pk[qb][q] = pack_bf16x2(
-                            __builtin_amdgcn_exp2f(__builtin_fmaf(S[qb][0][2 * q], sl, nm)),
-                            __builtin_amdgcn_exp2f(__builtin_fmaf(S[qb][0][2 * q + 1], sl, nm)));
-                        pk[qb][8 + q] = pack_bf16x2(
-                            __builtin_amdgcn_exp2f(__builtin_fmaf(S[qb][1][2 * q], sl, nm)),
-                            __builtin_amdgcn_exp2f(__builtin_fmaf(S[qb][1][2 * q + 1], sl, nm)));
-                    }
-                    // the row sum is taken from the rounded probabilities that
-                    // feed the P.V product
-                    l_run[qb] += sum_bf16_pairs(pk[qb], 16);
+                        for (int q = 0; q < 16; ++q) O[db][q] *= alpha;
                 }
-                // ---- O^T += V^T P^T
-                const uint16_t* vl = sm.vt[buf];
+                m_run = m_new;
+                const float nm = -m_use;
+                uint32_t pk[16];
+#pragma unroll
+                for (int q = 0; q < 8; ++q) {
+                    pk[q] = pack_bf16x2(__builtin_amdgcn_exp2f(__builtin_fmaf(S0[2 * q], sl, nm)),
+                                        __builtin_amdgcn_exp2f(__builtin_fmaf(S0[2 * q + 1], sl, nm)));
+                    pk[8 + q] =
+                        pack_bf16x2(__builtin_amdgcn_exp2f(__builtin_fmaf(S1[2 * q], sl, nm)),
+                                    __builtin_amdgcn_exp2f(__builtin_fmaf(S1[2 * q + 1], sl, nm)));
+                }
+                // the row sum is taken from the rounded probabilities that
+                // feed the P.V product
+                l_run += sum_bf16_pairs(pk);
+                // ---- O^T += V^T P^T; the A operand comes transposed from LDS
+                const uint16_t* vl = sm.v[buf] + tr_off + 4 * hf * VS;
 #pragma unroll
                 for (int kb = 0; kb < 2; ++kb) {
 #pragma unroll
                     for (int tt = 0; tt < 2; ++tt) {
                         const int pq = kb * 8 + tt * 4;
-                        bf16x8_t pb[QB];
-#pragma unroll
-                        for (int qb = 0; qb < QB; ++qb)
-                            pb[qb] = __builtin_bit_cast(
-                                bf16x8_t, make_uint4(pk[qb][pq], pk[qb][pq + 1], pk[qb][pq + 2],
-                                                     pk[qb][pq + 3]));
+                        const bf16x8_t pb = __builtin_bit_cast(
+                            bf16x8_t, make_uint4(pk[pq], pk[pq + 1], pk[pq + 2], pk[pq + 3]));
+                        const uint16_t* vrow = vl + (kb * 32 + tt * 16) * VS;
 #pragma unroll
                         for (int db = 0; db < NDB; ++db) {
-                            const uint16_t* vp = vl + (db * 32 + rl) * VS + kb * 32 + tt * 16 + hf * 4;
-                            const uint2 lo = *reinterpret_cast<const uint2*>(vp);
-                            const uint2 hi = *reinterpret_cast<const uint2*>(vp + 8);
+                            const uint2 lo = lds_read_tr16(vrow + db * 32);
+                            const uint2 hi = lds_read_tr16(vrow + 8 * VS + db * 32);
                             const bf16x8_t av =
                                 __builtin_bit_cast(bf16x8_t, make_uint4(lo.x, lo.y, hi.x, hi.y));
-#pragma unroll
-                            for (int qb = 0; qb < QB; ++qb) O[qb][db] = mfma32(av, pb[qb], O[qb][db]);
+                            O[db] = mfma32(av, pb, O[db]);
                         }
                     }
                 }
@@ -332,34 +292,30 @@ __global__ __launch_bounds__(kThreads, QB == 1 ? 2 : 1) void prefill_bf16_kernel
         }
     }
 
+    const float l_tot = l_run + __shfl_xor(l_run, 32);
+    if (!row_ok) return;
+    if (a.n_splits == 1) {
+        const float inv = 1.f / l_tot;
+        float* orow = a.out + ((size_t)t * a.n_heads + h) * HD;
 #pragma unroll
-    for (int qb = 0; qb < QB; ++qb) {
-        const float l_tot = l_run[qb] + __shfl_xor(l_run[qb], 32);
-        if (!ok[qb]) continue;
-        if (a.n_splits == 1) {
-            const float inv = 1.f / l_tot;
-            float* orow = a.out + ((size_t)tq[qb] * a.n_heads + hq[qb]) * HD;
+        for (int db = 0; db < NDB; ++db)
 #pragma unroll
-            for (int db = 0; db < NDB; ++db)
+            for (int q4 = 0; q4 < 4; ++q4) {
+                float4 v = make_float4(O[db][4 * q4] * inv, O[db][4 * q4 + 1] * inv,
+                                       O[db][4 * q4 + 2] * inv, O[db][4 * q4 + 3] * inv);
+                *reinterpret_cast<float4*>(orow + db * 32 + 8 * q4 + 4 * hf) = v;
+            }
+    } else {
+        float* pr = a.part + (((size_t)t * a.n_heads + h) * a.n_splits + s) * (HD + kPartPad);
+        if (hf == 0) *reinterpret_cast<float2*>(pr) = make_float2(m_run, l_tot);
 #pragma unroll
-                for (int q4 = 0; q4 < 4; ++q4) {
-                    float4 v = make_float4(O[qb][db][4 * q4] * inv, O[qb][db][4 * q4 + 1] * inv,
-                                           O[qb][db][4 * q4 + 2] * inv, O[qb][db][4 * q4 + 3] * inv);
-                    *reinterpret_cast<float4*>(orow + db * 32 + 8 * q4 + 4 * hf) = v;
-                }
-        } else {
-            float* pr = a.part +
-                        (((size_t)tq[qb] * a.n_heads + hq[qb]) * a.n_splits + s) * (HD + kPartPad);
-            if (hf == 0) *reinterpret_cast<float2*>(pr) = make_float2(m_run[qb], l_tot);
+        for (int db = 0; db < NDB; ++db)
 #pragma unroll
-            for (int db = 0; db < NDB; ++db)
-#pragma unroll
-                for (int q4 = 0; q4 < 4; ++q4) {
-                    float4 v = make_float4(O[qb][db][4 * q4], O[qb][db][4 * q4 + 1],
-                                           O[qb][db][4 * q4 + 2], O[qb][db][4 * q4 + 3]);
-                    *reinterpret_cast<float4*>(pr + kPartPad + db * 32 + 8 * q4 + 4 * hf) = v;
-                }
-        }
+            for (int q4 = 0; q4 < 4; ++q4) {
+                float4 v = make_float4(O[db][4 * q4], O[db][4 * q4 + 1], O[db][4 * q4 + 2],
+                                       O[db][4 * q4 + 3]);
+                *reinterpret_cast<float4*>(pr + kPartPad + db * 32 + 8 * q4 + 4 * hf) = v;
+            }
     }
 }
 
@@ -394,12 +350,17 @@ __global__ __launch_bounds__(256) void prefill_combine_kernel(PrefillArgs a) {
 }
 
 
-// Variant and split choice.  Large chunks (enough 256-row tiles to give every
-// CU a workgroup) take 64 rows per wave; otherwise 128-row tiles, with the key
-// range split so that about two workgroups per CU are in flight, each part
-// keeping at least kMinTilesPerSplit key tiles.
-constexpr int kTargetBlocks = 512;
-constexpr int kMinTilesPerSplit = 4;
+// Split choice: 128-row tiles; when they are too few to keep about two
+// workgroups per CU busy, the key range is split, each part keeping at least
+// kMinTilesPerSplit key tiles.
+#ifndef ATTN_PREFILL_TARGET_BLOCKS
+#define ATTN_PREFILL_TARGET_BLOCKS 512
+#endif
+#ifndef ATTN_PREFILL_MIN_TILES_PER_SPLIT
+#define ATTN_PREFILL_MIN_TILES_PER_SPLIT 4
+#endif
+constexpr int kTargetBlocks = ATTN_PREFILL_TARGET_BLOCKS;
+constexpr int kMinTilesPerSplit = ATTN_PREFILL_MIN_TILES_PER_SPLIT;
 constexpr int kMaxSplits = 32;
 
 PrefillPlan plan_prefill(int n_seq, int n_heads, int n_kv, int head_dim, int n_tok, int max_chunk,
@@ -407,12 +368,6 @@ PrefillPlan plan_prefill(int n_seq, int n_heads, int n_kv, int head_dim, int n_t
     PrefillPlan p{kWaves * 32, 1, 1, 0};
     const long group = n_heads / n_kv;
     const long rows = (long)max_chunk * group;
-    const long big_tiles = (rows + kWaves * 64 - 1) / (kWaves * 64);
-    if ((long)n_seq * big_tiles * n_kv >= 384) {
-        p.rows_per_tile = kWaves * 64;
-        p.n_qtiles = (int)big_tiles;
-        return p;
-    }
     p.n_qtiles = (int)((rows + kWaves * 32 - 1) / (kWaves * 32));
     const long base = (long)n_seq * p.n_qtiles * n_kv;
     const long tiles = ((long)max_end + kTK - 1) / kTK;
@@ -437,13 +392,8 @@ hipError_t launch_prefill_bf16(const PrefillArgs& a, hipStream_t stream) {
     const long blocks = (long)a.n_seq * a.n_qtiles * a.n_splits * a.n_kv;
     if (blocks <= 0) return hipSuccess;
     const dim3 grid((unsigned)blocks), block(kThreads);
-    if (a.rows_per_tile == kWaves * 64) {
-        if (a.head_dim == 128) prefill_bf16_kernel<128, 2><<<grid, block, 0, stream>>>(a);
-        else prefill_bf16_kernel<64, 2><<<grid, block, 0, stream>>>(a);
-    } else {
-        if (a.head_dim == 128) prefill_bf16_kernel<128, 1><<<grid, block, 0, stream>>>(a);
-        else prefill_bf16_kernel<64, 1><<<grid, block, 0, stream>>>(a);
-    }
+    if (a.head_dim == 128) prefill_bf16_kernel<128><<<grid, block, 0, stream>>>(a);
+    else prefill_bf16_kernel<64><<<grid, block, 0, stream>>>(a);
     return hipGetLastError();
 }
 
