@@ -63,7 +63,7 @@ def _load():
     lib.orc_round_array.restype = None
     lib.orc_finish_heads.argtypes = [_dp, ctypes.c_int, ctypes.c_int, ctypes.c_int, _ip, _fp,
                                      ctypes.c_int, ctypes.c_double, ctypes.c_int, _fp,
-                                     ctypes.c_double, ctypes.c_int]
+                                     ctypes.c_double, ctypes.c_int, ctypes.c_int]
     lib.orc_finish_heads.restype = None
     lib.orc_attend.argtypes = [_dp, _dp, _dp, ctypes.c_int, ctypes.c_int, ctypes.c_int,
                                ctypes.c_int, ctypes.c_long, _ip, ctypes.c_double, _dp, _dp,
@@ -119,7 +119,7 @@ def round_store(x, store: int) -> np.ndarray:
 
 def finish_heads(x, pos, inv_freq, rotary_dim: int, rope_scale: float = 1.0,
                  norm_style: int = NORM_NONE, norm_w=None, eps: float = 1e-6,
-                 store: int = STORE_F32) -> np.ndarray:
+                 store: int = STORE_F32, n_threads: int | None = None) -> np.ndarray:
     """Optional per-head RMS norm, then RoPE, then storage rounding.
     x: [n_tok][n_heads][hd]; pos: [n_tok] absolute positions.  Returns a new
     array.  [ATT] fn finish_projection."""
@@ -137,7 +137,8 @@ def finish_heads(x, pos, inv_freq, rotary_dim: int, rope_scale: float = 1.0,
     else:
         wp = None
     _load().orc_finish_heads(a.ctypes.data_as(_dp), n_tok, n_heads, hd, p.ctypes.data_as(_ip),
-                             f.ctypes.data_as(_fp), rd, rope_scale, norm_style, wp, eps, store)
+                             f.ctypes.data_as(_fp), rd, rope_scale, norm_style, wp, eps, store,
+                             n_threads or default_threads())
     return a
 
 

@@ -182,23 +182,62 @@ static void rope_head(double *x, int rd, long pos, const float *inv_freq, double
  * (rotated Q, or the K cache row).  x: [n_tok][n_heads][hd], in place.
  * pos[t] is the absolute position of token t.  norm_style 0 = no norm.
  * [ATT] fn finish_projection: norm before RoPE; RoPE on the first rd dims.
+ * Tokens are independent; they are shared out over n_threads threads.
  */
+typedef struct {
+    double *x;
+    int n_tok, n_heads, hd, rd, norm_style, store_dtype, n_threads, tid;
+    const int64_t *pos;
+    const float *inv_freq, *norm_w;
+    double rope_scale, eps;
+} finish_job;
+
+static void *finish_worker(void *arg)
+{
+    finish_job *jb = (finish_job *)arg;
+    for (int t = jb->tid; t < jb->n_tok; t += jb->n_threads) {
+        for (int h = 0; h < jb->n_heads; h++) {
+            double *row = jb->x + ((long)t * jb->n_heads + h) * jb->hd;
+            if (jb->norm_style != 0)
+                rmsnorm_head(row, jb->hd, jb->norm_w, jb->norm_style, jb->eps);
+            rope_head(row, jb->rd, (long)jb->pos[t], jb->inv_freq, jb->rope_scale);
+            for (int d = 0; d < jb->hd; d++)
+                row[d] = round_store(row[d], jb->store_dtype);
+        }
+    }
+    return NULL;
+}
+
 void orc_finish_heads(double *x, int n_tok, int n_heads, int hd, const int64_t *pos,
                       const float *inv_freq, int rd, double rope_scale, int norm_style,
-                      const float *norm_w, double eps, int store_dtype)
+                      const float *norm_w, double eps, int store_dtype, int n_threads)
 {
     if (rd > hd)
         rd = hd;
-    for (int t = 0; t < n_tok; t++) {
-        for (int h = 0; h < n_heads; h++) {
-            double *row = x + ((long)t * n_heads + h) * hd;
-            if (norm_style != 0)
-                rmsnorm_head(row, hd, norm_w, norm_style, eps);
-            rope_head(row, rd, (long)pos[t], inv_freq, rope_scale);
-            for (int d = 0; d < hd; d++)
-                row[d] = round_store(row[d], store_dtype);
-        }
+    if (n_threads < 1)
+        n_threads = 1;
+    if (n_threads > n_tok)
+        n_threads = n_tok > 0 ? n_tok : 1;
+    finish_job jobs[64];
+    pthread_t th[64];
+    if (n_threads > 64)
+        n_threads = 64;
+    for (int i = 0; i < n_threads; i++) {
+        finish_job j = {x, n_tok, n_heads, hd, rd, norm_style, store_dtype, n_threads, i,
+                        pos, inv_freq, norm_w, rope_scale, eps};
+        jobs[i] = j;
     }
+    int started = 0;
+    for (int i = 1; i < n_threads; i++) {
+        if (pthread_create(&th[i], NULL, finish_worker, &jobs[i]) != 0)
+            break;
+        started = i;
+    }
+    for (int i = started + 1; i < n_threads; i++)
+        finish_worker(&jobs[i]);
+    finish_worker(&jobs[0]);
+    for (int i = 1; i <= started; i++)
+        pthread_join(th[i], NULL);
 }
 
 /* ------------------------------------------------------------------------ */

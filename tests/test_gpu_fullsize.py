@@ -1,0 +1,138 @@
+"""Parity at the full workload sizes, in the launch configuration bench.py
+times (the same chunk driver and chunk sizes), on sampled outputs the oracle
+computes one row at a time: position 0, rows on both sides of chunk
+boundaries, the final row and seeded random rows, every query head of each.
+The K/V cache is also checked in full where that is cheap."""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from chunked_prefill_causal_rope_amd import runner, workloads as wl
+from parity_util import check_bf16_rows, np64, oracle_rows, oracle_table, say
+
+pytestmark = pytest.mark.gpu
+DEV = "cuda:0"
+
+
+@pytest.fixture(autouse=True)
+def _gpu():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    torch.cuda.set_device(0)
+    yield
+    torch.cuda.synchronize()
+    torch.cuda.empty_cache()
+
+
+def sample_positions(n, chunk, seed, extra=12):
+    rng = np.random.default_rng(seed)
+    pos = {0, 1, n - 1, n - 2}
+    for c in (chunk, 2 * chunk, (n // chunk // 2) * chunk, (n // chunk - 1) * chunk):
+        if 0 < c < n:
+            pos.update({c - 1, c})
+    pos.update(int(x) for x in rng.integers(0, n, extra))
+    return sorted(p for p in pos if 0 <= p < n)
+
+
+def _bits(t):
+    return t.detach().cpu().contiguous().view(torch.int16).numpy()
+
+
+def run_prefill(name):
+    w = wl.CONFIGS[name]
+    say(f"full-size prefill {name}: {w}")
+    d = wl.gen_prefill(w, device=DEV)
+    run = runner.ChunkedPrefill(w, d, device=DEV)
+    run.run_all()
+    torch.cuda.synchronize()
+    return w, d, run
+
+
+def check_sequence(w, d, run, b, seed, label, check_cache=True):
+    n = d["lengths"][b]
+    positions = sample_positions(n, w.chunk, seed)
+    pos, ref = oracle_rows(w, d, b, positions)
+    got_all = run.gather("out")
+    idx = torch.as_tensor(d["cu_seq"][b] + pos, device=got_all.device)
+    got = np64(got_all[idx])
+    assert np.all(np.isfinite(np64(got_all[d["cu_seq"][b]:d["cu_seq"][b] + n])))
+    check_bf16_rows(got, ref, f"{label} seq {b} ({len(pos)} positions x {w.n_heads} heads)")
+    if check_cache:
+        # every cache row of the sequence equals the oracle's rounded K and the input V
+        f = oracle_table(w)
+        t0 = d["cu_seq"][b]
+        kn = {} if w.norm_style == wl.NORM_NONE else dict(
+            norm_style=w.norm_style, norm_w=d["k_norm_w"].cpu().numpy(), eps=w.norm_eps)
+        kref = oracle.finish_heads(np64(d["k"][t0:t0 + n]), np.arange(n), f, w.rd, w.rope_scale,
+                                   store=oracle.STORE_BF16, **kn)
+        want = torch.from_numpy(kref.transpose(1, 0, 2).copy()).to(torch.bfloat16)
+        mism = int((_bits(run.k_cache[b, :, :n]) != want.view(torch.int16).numpy()).sum())
+        say(f"  K cache mismatching elements: {mism} of {want.numel()}")
+        assert mism <= max(1, want.numel() // 1_000_000)
+        assert np.array_equal(_bits(run.v_cache[b, :, :n]),
+                              _bits(d["v"][t0:t0 + n].transpose(0, 1)))
+
+
+def test_c1_llama_prefill_full():
+    w, d, run = run_prefill("c1_llama_prefill")
+    check_sequence(w, d, run, 0, 101, "c1")
+
+
+def test_c3_qwen_varlen_full():
+    w, d, run = run_prefill("c3_qwen_varlen")
+    say(f"  prompt lengths {d['lengths']}")
+    for b in range(w.n_seq):
+        check_sequence(w, d, run, b, 300 + b, "c3", check_cache=(b % 3 == 0))
+
+
+def test_c4_yarn_128k_full():
+    w, d, run = run_prefill("c4_yarn_128k")
+    check_sequence(w, d, run, 0, 404, "c4", check_cache=False)
+    # cache spot check: rows at chunk boundaries and the last row
+    f = oracle_table(w)
+    rows = np.array([0, 2047, 2048, 65535, 65536, 131071])
+    kref = oracle.finish_heads(np64(d["k"][torch.as_tensor(rows, device=DEV)]), rows, f, w.rd,
+                               w.rope_scale, store=oracle.STORE_BF16)
+    got = run.k_cache[0][:, torch.as_tensor(rows, device=DEV)].transpose(0, 1)
+    want = torch.from_numpy(kref).to(torch.bfloat16)
+    assert np.array_equal(_bits(got), want.view(torch.int16).numpy())
+
+
+def test_c2_decode_full():
+    w = wl.CONFIGS["c2_decode"]
+    say(f"full-size decode: {w}")
+    d = wl.gen_decode(w, device=DEV)
+    step = runner.DecodeStep(w, d, device=DEV)
+    step.probs.fill_(float("nan"))
+    step.run()
+    torch.cuda.synchronize()
+    ctx = d["ctx"]
+    order = np.argsort(ctx)
+    picks = sorted({int(order[0]), int(order[1]), int(order[-1]), int(order[-2]),
+                    int(order[len(ctx) // 2]), 7})
+    say(f"  checking sequences {picks} with ctx {[ctx[b] for b in picks]}")
+    f = oracle_table(w)
+    out = np64(step.out)
+    for b in picks:
+        c = ctx[b]
+        pos = np.array([c - 1])
+        kc = np64(d["k_cache"][b, :, :c])
+        vc = np64(d["v_cache"][b, :, :c])
+        kc[:, c - 1] = oracle.finish_heads(np64(d["k"][b:b + 1]), pos, f, w.rd,
+                                           store=oracle.STORE_BF16)[0]
+        vc[:, c - 1] = np64(d["v"][b])
+        q = oracle.finish_heads(np64(d["q"][b:b + 1]), pos, f, w.rd, store=oracle.STORE_BF16)
+        o, P = oracle.attend(q, kc, vc, pos, w.scale, want_probs=True)
+        check_bf16_rows(out[b], o[0], f"c2 seq {b} ctx {c}")
+        pg = np64(step.probs[b])
+        assert np.all(np.isnan(pg[:, c:])), "entries past ctx must stay untouched"
+        pg = pg[:, :c]
+        assert np.allclose(pg.sum(-1), 1.0, atol=1e-5)
+        rel = np.max(np.abs(pg - P[0]), axis=-1) / np.sqrt(np.mean(P[0] ** 2, axis=-1))
+        say(f"    probs worst row err/rms {rel.max():.3e}")
+        assert rel.max() <= 2e-2
+    # all outputs finite, every appended row in place
+    assert np.all(np.isfinite(out))
+    for b, c in enumerate(ctx):
+        assert torch.equal(step.v_cache[b, :, c - 1], d["v"][b].to(DEV))
