@@ -44,7 +44,35 @@ def parse():
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
     ap.add_argument("--eager", action="store_true", help="time eager launches, not a graph")
+    ap.add_argument("--copy-calibration", type=int, default=0, metavar="BYTES",
+                    help="only run a plain device-to-device copy of BYTES (counter calibration)")
     return ap.parse_args()
+
+
+def kernel_source_hash():
+    """Hash of the HIP sources; recorded counter traffic is only reported while
+    the kernels it was taken on are unchanged."""
+    import glob
+    import hashlib
+    h = hashlib.sha256()
+    for f in sorted(glob.glob(os.path.join(ROOT, "chunked_prefill_causal_rope_amd", "csrc", "*"))):
+        h.update(os.path.basename(f).encode())
+        h.update(open(f, "rb").read())
+    return h.hexdigest()[:16]
+
+
+def recorded_traffic(workload):
+    """HBM bytes per launch of the attention call from the committed counter
+    record (FETCH_SIZE + WRITE_SIZE, scaled by a plain copy), or None when there
+    is no record for this workload or the kernels changed since."""
+    path = os.path.join(ROOT, "profiles", "traffic.json")
+    if not os.path.exists(path):
+        return None
+    rec = json.load(open(path))
+    if rec.get("kernel_source_hash") != kernel_source_hash():
+        return None
+    w = rec.get("workloads", {}).get(workload)
+    return None if w is None else w.get("bytes_per_launch")
 
 
 def step_flops(w, run, i):
@@ -204,7 +232,7 @@ def bench_prefill(torch, w, args, stream):
         splits.append(max(1, wsb // per) if wsb else 1)
     roof = {"bound": "mfma", "achieved": round(achieved, 2), "peak": PEAK_MFMA_BF16_TFLOPS,
             "unit": "TFLOP/s", "frac": round(achieved / PEAK_MFMA_BF16_TFLOPS, 4),
-            "traffic": None,
+            "traffic": recorded_traffic(w.name),
             "kernel": "attn_prefill_chunk (prefill_bf16_kernel"
                       + (" + prefill_combine_kernel" if max(splits) > 1 else "") + ")",
             "launches": n_steps, "avg_launch_ms": round(avg_ms, 4),
@@ -240,7 +268,7 @@ def bench_decode(torch, w, args, stream):
     avg_ms = sum(per_launch) / len(per_launch)
     achieved = alg / (avg_ms * 1e-3) / 1e9
     roof = {"bound": "hbm", "achieved": round(achieved, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
-            "frac": round(achieved / PEAK_HBM_GBS, 4), "traffic": None,
+            "frac": round(achieved / PEAK_HBM_GBS, 4), "traffic": recorded_traffic(w.name),
             "kernel": "attn_decode (decode_split_kernel + decode_combine_kernel)",
             "avg_launch_ms": round(avg_ms, 4), "bytes_per_launch": alg,
             "kv_read_gbs": round(kv / (avg_ms * 1e-3) / 1e9, 1)}
@@ -267,6 +295,15 @@ def main():
         print("bench.py needs a GPU", file=sys.stderr)
         sys.exit(2)
     torch.cuda.set_device(0)
+    if args.copy_calibration:
+        n = args.copy_calibration // 4
+        x = torch.ones(n, dtype=torch.float32, device="cuda")
+        y = torch.empty_like(x)
+        torch.cuda.synchronize()
+        y.copy_(x)
+        torch.cuda.synchronize()
+        print(json.dumps({"copy_bytes": 4 * n, "kernel_source_hash": kernel_source_hash()}))
+        return
     stream = torch.cuda.Stream()
     w = wl.CONFIGS[args.workload]
     if w.decode:
