@@ -34,14 +34,14 @@
 //    range is split and the parts are merged by a log-sum-exp combine.
 //  * blockIdx -> (group, split, row tile, sequence) with the group fastest,
 //    so with 8 KV groups every XCD streams one group's K/V from its own L2.
+#include <type_traits>
+
 #include "device_common.h"
 #include "launch.h"
 
 namespace attn {
 
 constexpr int kTK = 64;                 // keys per tile
-constexpr int kWaves = 4;
-constexpr int kThreads = kWaves * 64;
 constexpr int kPartPad = 4;             // (m, l, pad, pad) before O in a partial
 // A row's running maximum (log2 units) is only moved, and O rescaled, when a
 // new score exceeds it by more than this; until then probabilities are
@@ -72,9 +72,9 @@ typedef __attribute__((address_space(3))) s16x4_t lds_s16x4_t;
 // (then j+16, j+32, j+48) of the 64 16-bit values the group's lanes point at,
 // 4 per lane in lane order.  Pointing lane a at V[k0 + a/4][d0 + 4(a%4)]
 // therefore hands lane j the column V[k0 .. k0+3][d0 + j].
-__device__ __forceinline__ uint2 lds_read_tr16(const uint16_t* p) {
+__device__ __forceinline__ u32x2_t lds_read_tr16(const uint16_t* p) {
     const s16x4_t v = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4_t*)(p));
-    return __builtin_bit_cast(uint2, v);
+    return __builtin_bit_cast(u32x2_t, v);
 }
 
 // Sum of the two bfloat16 halves of each packed word, exactly (products by 1).
@@ -89,15 +89,32 @@ __device__ __forceinline__ float sum_bf16_pairs(const uint32_t* pk) {
     return s0 + s1;
 }
 
-template <int HD>
-__global__ __launch_bounds__(kThreads, 2) void prefill_bf16_kernel(PrefillArgs a) {
+// Scheduling hints for the interleaved sections: each matrix product is
+// followed by a few vector-ALU instructions of the independent softmax stream.
+#define ATTN_INTERLEAVE(n, mfma, valu)                               \
+    do {                                                             \
+        _Pragma("unroll") for (int _i = 0; _i < (n); ++_i) {         \
+            __builtin_amdgcn_sched_group_barrier(0x008, (mfma), 0);  \
+            __builtin_amdgcn_sched_group_barrier(0x002, (valu), 0);  \
+        }                                                            \
+    } while (0)
+
+// NW waves of 32 query rows each share every K/V tile.  With 8 waves each
+// thread stages half a tile's worth of K and V, which leaves room for two
+// staging sets: the global loads of a tile are then issued two tiles before
+// they are stored to LDS (PD = 2) instead of one.
+template <int HD, int NW>
+__global__ __launch_bounds__(NW * 64, 8 / NW) void prefill_bf16_kernel(PrefillArgs a) {
     using Sm = PrefillSmem<HD>;
+    constexpr int kThreads = NW * 64;
+    constexpr int PD = NW == 8 ? 2 : 1;           // staging sets = prefetch depth
     constexpr int KS = Sm::KS;
     constexpr int VS = Sm::VS;
     constexpr int CH = HD / 8;                    // 16-byte chunks per cache row
     constexpr int NCH = kTK * CH / kThreads;      // K (and V) chunks per thread
     constexpr int NDB = HD / 32;                  // 32-dim blocks of O
-    constexpr int TILE_ROWS = kWaves * 32;        // query rows per workgroup
+    constexpr int NKK = HD / 16;                  // K-steps of a score product
+    constexpr int TILE_ROWS = NW * 32;            // query rows per workgroup
     __shared__ Sm sm;
 
     const int tid = threadIdx.x;
@@ -138,18 +155,16 @@ __global__ __launch_bounds__(kThreads, 2) void prefill_bf16_kernel(PrefillArgs a
     const bool row_ok = r < rows_b && t >= 0 && t < a.n_tok;
     const int pos = row_ok ? p0 + i : -1;
     const int rw0 = r_tile0 + wave * 32;
-    const bool wave_ok = rw0 < rows_b;
     const int pw_lo = p0 + rw0 / G;
-    const int pw_hi = p0 + min(rw0 + 31, rows_b - 1) / G;
 
-    bf16x8_t qf[HD / 16];
+    bf16x8_t qf[NKK];
     {
         const uint16_t* qrow =
             reinterpret_cast<const uint16_t*>(a.q) + ((size_t)t * a.n_heads + h) * HD;
 #pragma unroll
-        for (int k = 0; k < HD / 16; ++k) {
-            uint4 u = make_uint4(0, 0, 0, 0);
-            if (row_ok) u = *reinterpret_cast<const uint4*>(qrow + 16 * k + 8 * hf);
+        for (int k = 0; k < NKK; ++k) {
+            u32x4_t u = {0u, 0u, 0u, 0u};
+            if (row_ok) u = ld16(qrow + 16 * k + 8 * hf);
             qf[k] = __builtin_bit_cast(bf16x8_t, u);
         }
     }
@@ -158,35 +173,57 @@ __global__ __launch_bounds__(kThreads, 2) void prefill_bf16_kernel(PrefillArgs a
     const uint16_t* kc = reinterpret_cast<const uint16_t*>(a.k_cache) + kvbase;
     const uint16_t* vc = reinterpret_cast<const uint16_t*>(a.v_cache) + kvbase;
 
-    // staging: thread -> NCH (row, 16-byte chunk) pairs of each of K and V;
-    // rows past the last key are zero-filled and never read from memory
-    uint4 kreg[NCH], vreg[NCH];
-    auto load_tile = [&](int j) {
-        const int k0 = j * kTK;
-#pragma unroll
-        for (int c = 0; c < NCH; ++c) {
-            const int idx = c * kThreads + tid;
-            const int key = k0 + idx / CH;
-            const size_t off = (size_t)key * HD + (idx % CH) * 8;
-            const bool in = key < n_keys;
-            kreg[c] = in ? *reinterpret_cast<const uint4*>(kc + off) : make_uint4(0, 0, 0, 0);
-            vreg[c] = in ? *reinterpret_cast<const uint4*>(vc + off) : make_uint4(0, 0, 0, 0);
-        }
+    // staging: thread -> NCH (row, 16-byte chunk) pairs of a tile.  Rows past
+    // the last key re-read the last key's row (always in bounds): their scores
+    // are masked to -inf and their probabilities are exactly 0, so the copy
+    // never contributes.
+    u32x4_t kreg[PD][NCH], vreg[PD][NCH];
+    auto row_off = [&](int j, int c) __attribute__((always_inline)) {
+        const int idx = c * kThreads + tid;
+        return (size_t)min(j * kTK + idx / CH, n_keys - 1) * HD + (idx % CH) * 8;
     };
-    auto store_tile = [&](int buf) {
+    auto lds_off = [&](int c, int stride) __attribute__((always_inline)) {
+        const int idx = c * kThreads + tid;
+        return (idx / CH) * stride + (idx % CH) * 8;
+    };
+    auto load_k = [&](int j, auto set) __attribute__((always_inline)) {
 #pragma unroll
-        for (int c = 0; c < NCH; ++c) {
-            const int idx = c * kThreads + tid;
-            const int kr = idx / CH;
-            const int ch = idx % CH;
-            *reinterpret_cast<uint4*>(&sm.k[buf][kr * KS + ch * 8]) = kreg[c];
-            *reinterpret_cast<uint4*>(&sm.v[buf][kr * VS + ch * 8]) = vreg[c];
+        for (int c = 0; c < NCH; ++c) kreg[set.value][c] = ld16(kc + row_off(j, c));
+    };
+    auto load_v = [&](int j, auto set) __attribute__((always_inline)) {
+#pragma unroll
+        for (int c = 0; c < NCH; ++c) vreg[set.value][c] = ld16(vc + row_off(j, c));
+    };
+    auto store_k = [&](int buf, auto set) __attribute__((always_inline)) {
+#pragma unroll
+        for (int c = 0; c < NCH; ++c) st16(&sm.k[buf][lds_off(c, KS)], kreg[set.value][c]);
+    };
+    auto store_v = [&](int buf, auto set) __attribute__((always_inline)) {
+#pragma unroll
+        for (int c = 0; c < NCH; ++c) st16(&sm.v[buf][lds_off(c, VS)], vreg[set.value][c]);
+    };
+    constexpr std::integral_constant<int, 0> set0{};
+    constexpr std::integral_constant<int, PD - 1> set1{};
+    auto scores = [&](const uint16_t* kl, f32x16_t& S0, f32x16_t& S1) __attribute__((always_inline)) {
+#pragma unroll
+        for (int q = 0; q < 16; ++q) {
+            S0[q] = 0.f;
+            S1[q] = 0.f;
+        }
+#pragma unroll
+        for (int kk = 0; kk < NKK; ++kk) {
+            const bf16x8_t a0 = __builtin_bit_cast(bf16x8_t, ld16(kl + rl * KS + kk * 16 + hf * 8));
+            const bf16x8_t a1 =
+                __builtin_bit_cast(bf16x8_t, ld16(kl + (32 + rl) * KS + kk * 16 + hf * 8));
+            S0 = mfma32(a0, qf[kk], S0);
+            S1 = mfma32(a1, qf[kk], S1);
         }
     };
 
-    // transposing-read address of this lane inside a V tile, relative to the
-    // 16-key block: group lane a = lane % 16 points at key a/4, dims 4(a%4)
-    const int tr_off = ((lane & 15) >> 2) * VS + 4 * (lane & 3) + 16 * ((lane >> 4) & 1);
+    // transposing-read address of this lane inside a V tile: group lane
+    // a = lane % 16 points at key a/4, dims 4(a%4); the wave half picks keys
+    // +4, the 16-lane group picks dims +16
+    const int tr_off = (4 * hf + ((lane & 15) >> 2)) * VS + 4 * (lane & 3) + 16 * ((lane >> 4) & 1);
 
     f32x16_t O[NDB];
 #pragma unroll
@@ -198,97 +235,155 @@ __global__ __launch_bounds__(kThreads, 2) void prefill_bf16_kernel(PrefillArgs a
     const float sl = a.scale * kLog2e;
 
     if (tb < te) {
-        load_tile(tb);
-        store_tile(0);
+        // K and V are double-buffered one tile apart: during tile j the
+        // workgroup holds K[j+1] (scores of the next tile) and V[j].
+        load_k(tb, set0);
+        load_v(tb, set0);
+        store_k(0, set0);
+        store_v(0, set0);
+        if (tb + 1 < te) {
+            load_k(tb + 1, set0);
+            store_k(1, set0);
+        }
         __syncthreads();
-        for (int j = tb; j < te; ++j) {
-            const int buf = (j - tb) & 1;
-            if (j + 1 < te) load_tile(j + 1);
+        f32x16_t S0, S1;
+        scores(sm.k[0], S0, S1);
+        // Loads are unconditional (tile index clamped into range): past the
+        // last tile they refill LDS slots that are never read again.  With two
+        // staging sets, the loads stored at the end of tile j (K[j+2], V[j+1])
+        // were issued one tile earlier.
+        if (PD == 2) {
+            load_k(min(tb + 2, te - 1), set0);
+            load_v(min(tb + 1, te - 1), set0);
+        }
+
+        auto tile = [&](int j, auto cur, auto nxt) __attribute__((always_inline)) {
+            const int rr = (j - tb) & 1;
+            load_k(min(j + 1 + PD, te - 1), nxt);
+            load_v(min(j + PD, te - 1), nxt);
             const int k0 = j * kTK;
-            if (wave_ok && k0 <= pw_hi) {
-                // ---- S^T = K Q^T for 64 keys x this lane's row
-                const uint16_t* kl = sm.k[buf];
-                f32x16_t S0, S1;
+
+            // ---- causal mask of the current tile (tiles crossing the diagonal)
+            if (k0 + kTK - 1 > pw_lo) {
+                const int lim = pos - k0 - 4 * hf;
 #pragma unroll
                 for (int q = 0; q < 16; ++q) {
-                    S0[q] = 0.f;
-                    S1[q] = 0.f;
-                }
-#pragma unroll
-                for (int kk = 0; kk < HD / 16; ++kk) {
-                    const bf16x8_t a0 = __builtin_bit_cast(
-                        bf16x8_t, *reinterpret_cast<const uint4*>(kl + rl * KS + kk * 16 + hf * 8));
-                    const bf16x8_t a1 = __builtin_bit_cast(
-                        bf16x8_t,
-                        *reinterpret_cast<const uint4*>(kl + (32 + rl) * KS + kk * 16 + hf * 8));
-                    S0 = mfma32(a0, qf[kk], S0);
-                    S1 = mfma32(a1, qf[kk], S1);
-                }
-                // ---- causal mask on tiles that cross the diagonal: element q
-                // of S0 is key k0 + 8(q/4) + 4hf + q%4, of S1 that plus 32
-                if (k0 + kTK - 1 > pw_lo) {
-                    const int lim = pos - k0 - 4 * hf;
-#pragma unroll
-                    for (int q = 0; q < 16; ++q) {
-                        const int off = 8 * (q >> 2) + (q & 3);
-                        if (off > lim) S0[q] = -INFINITY;
-                        if (off + 32 > lim) S1[q] = -INFINITY;
-                    }
-                }
-                // ---- online softmax
-                float mx = fmaxf(S0[0], S1[0]);
-#pragma unroll
-                for (int q = 1; q < 16; ++q) mx = fmaxf(mx, fmaxf(S0[q], S1[q]));
-                mx = fmaxf(mx, __shfl_xor(mx, 32));
-                const float mt = mx * sl;                 // log2 units; -inf stays
-                const bool grow = mt > m_run + kRescaleSlack;
-                const float m_new = grow ? mt : m_run;
-                const float m_use = m_new == -INFINITY ? 0.f : m_new;
-                if (__any(grow)) {
-                    const float alpha = grow ? __builtin_amdgcn_exp2f(m_run - m_use) : 1.f;
-                    l_run *= alpha;
-#pragma unroll
-                    for (int db = 0; db < NDB; ++db)
-#pragma unroll
-                        for (int q = 0; q < 16; ++q) O[db][q] *= alpha;
-                }
-                m_run = m_new;
-                const float nm = -m_use;
-                uint32_t pk[16];
-#pragma unroll
-                for (int q = 0; q < 8; ++q) {
-                    pk[q] = pack_bf16x2(__builtin_amdgcn_exp2f(__builtin_fmaf(S0[2 * q], sl, nm)),
-                                        __builtin_amdgcn_exp2f(__builtin_fmaf(S0[2 * q + 1], sl, nm)));
-                    pk[8 + q] =
-                        pack_bf16x2(__builtin_amdgcn_exp2f(__builtin_fmaf(S1[2 * q], sl, nm)),
-                                    __builtin_amdgcn_exp2f(__builtin_fmaf(S1[2 * q + 1], sl, nm)));
-                }
-                // the row sum is taken from the rounded probabilities that
-                // feed the P.V product
-                l_run += sum_bf16_pairs(pk);
-                // ---- O^T += V^T P^T; the A operand comes transposed from LDS
-                const uint16_t* vl = sm.v[buf] + tr_off + 4 * hf * VS;
-#pragma unroll
-                for (int kb = 0; kb < 2; ++kb) {
-#pragma unroll
-                    for (int tt = 0; tt < 2; ++tt) {
-                        const int pq = kb * 8 + tt * 4;
-                        const bf16x8_t pb = __builtin_bit_cast(
-                            bf16x8_t, make_uint4(pk[pq], pk[pq + 1], pk[pq + 2], pk[pq + 3]));
-                        const uint16_t* vrow = vl + (kb * 32 + tt * 16) * VS;
-#pragma unroll
-                        for (int db = 0; db < NDB; ++db) {
-                            const uint2 lo = lds_read_tr16(vrow + db * 32);
-                            const uint2 hi = lds_read_tr16(vrow + 8 * VS + db * 32);
-                            const bf16x8_t av =
-                                __builtin_bit_cast(bf16x8_t, make_uint4(lo.x, lo.y, hi.x, hi.y));
-                            O[db] = mfma32(av, pb, O[db]);
-                        }
-                    }
+                    const int off = 8 * (q >> 2) + (q & 3);
+                    if (off > lim) S0[q] = -INFINITY;
+                    if (off + 32 > lim) S1[q] = -INFINITY;
                 }
             }
-            if (j + 1 < te) store_tile(buf ^ 1);
+
+            // ---- row max of this tile and the (rare) rescale of O
+            float mx = fmaxf(S0[0], S1[0]);
+#pragma unroll
+            for (int q = 1; q < 16; ++q) mx = fmaxf(mx, fmaxf(S0[q], S1[q]));
+            mx = fmaxf(mx, __shfl_xor(mx, 32));
+            const float mt = mx * sl;                     // log2 units; -inf stays
+            const bool grow = mt > m_run + kRescaleSlack;
+            const float m_new = grow ? mt : m_run;
+            const float m_use = m_new == -INFINITY ? 0.f : m_new;
+            if (__any(grow)) {
+                const float alpha = grow ? __builtin_amdgcn_exp2f(m_run - m_use) : 1.f;
+                l_run *= alpha;
+#pragma unroll
+                for (int db = 0; db < NDB; ++db)
+#pragma unroll
+                    for (int q = 0; q < 16; ++q) O[db][q] *= alpha;
+            }
+            m_run = m_new;
+            const float nm = -m_use;
+            uint32_t pk[16];
+
+            // ---- next tile's scores on the matrix cores while the vector ALU
+            // computes this tile's probabilities for keys 0..31; K fragments
+            // are read one step ahead
+            f32x16_t N0, N1;
+            {
+                const uint16_t* kl = sm.k[rr ^ 1];
+#pragma unroll
+                for (int q = 0; q < 16; ++q) {
+                    N0[q] = 0.f;
+                    N1[q] = 0.f;
+                }
+                u32x4_t a0 = ld16(kl + rl * KS + hf * 8);
+                u32x4_t a1 = ld16(kl + (32 + rl) * KS + hf * 8);
+#pragma unroll
+                for (int kk = 0; kk < NKK; ++kk) {
+                    u32x4_t b0 = a0, b1 = a1;
+                    if (kk + 1 < NKK) {
+                        b0 = ld16(kl + rl * KS + (kk + 1) * 16 + hf * 8);
+                        b1 = ld16(kl + (32 + rl) * KS + (kk + 1) * 16 + hf * 8);
+                    }
+                    N0 = mfma32(__builtin_bit_cast(bf16x8_t, a0), qf[kk], N0);
+                    N1 = mfma32(__builtin_bit_cast(bf16x8_t, a1), qf[kk], N1);
+                    // keys 0..31 (8 packed pairs) spread over the NKK steps
+#pragma unroll
+                    for (int q = kk * 8 / NKK; q < (kk + 1) * 8 / NKK; ++q)
+                        pk[q] = pack_bf16x2(
+                            __builtin_amdgcn_exp2f(__builtin_fmaf(S0[2 * q], sl, nm)),
+                            __builtin_amdgcn_exp2f(__builtin_fmaf(S0[2 * q + 1], sl, nm)));
+                    a0 = b0;
+                    a1 = b1;
+                }
+                ATTN_INTERLEAVE(NKK, 2, 6);
+            }
+
+            // ---- O^T += V^T P^T: keys 0..31 while the probabilities of keys
+            // 32..63 are computed, then keys 32..63; V^T fragments are read
+            // one step ahead
+            {
+                const uint16_t* vl = sm.v[rr] + tr_off;
+                auto vfrag = [&](int kb, int tt, int db) __attribute__((always_inline)) {
+                    const uint16_t* vrow = vl + (kb * 32 + tt * 16) * VS + db * 32;
+                    const u32x2_t lo = lds_read_tr16(vrow);
+                    const u32x2_t hi = lds_read_tr16(vrow + 8 * VS);
+                    const u32x4_t vv = {lo.x, lo.y, hi.x, hi.y};
+                    return vv;
+                };
+                u32x4_t va = vfrag(0, 0, 0);
+#pragma unroll
+                for (int st = 0; st < 4 * NDB; ++st) {          // st = (kb, tt, db)
+                    const int kb = st / (2 * NDB), tt = (st / NDB) % 2, db = st % NDB;
+                    u32x4_t vn = va;
+                    if (st + 1 < 4 * NDB) {
+                        const int st1 = st + 1;
+                        vn = vfrag(st1 / (2 * NDB), (st1 / NDB) % 2, st1 % NDB);
+                    }
+                    const int pq = kb * 8 + tt * 4;
+                    const u32x4_t pv = {pk[pq], pk[pq + 1], pk[pq + 2], pk[pq + 3]};
+                    O[db] = mfma32(__builtin_bit_cast(bf16x8_t, va), __builtin_bit_cast(bf16x8_t, pv), O[db]);
+                    // keys 32..63 (8 packed pairs) spread over the 2*NDB steps
+                    // of keys 0..31, so they are ready before they are used
+                    if (st < 2 * NDB) {
+#pragma unroll
+                        for (int q = st * 8 / (2 * NDB); q < (st + 1) * 8 / (2 * NDB); ++q)
+                            pk[8 + q] = pack_bf16x2(
+                                __builtin_amdgcn_exp2f(__builtin_fmaf(S1[2 * q], sl, nm)),
+                                __builtin_amdgcn_exp2f(__builtin_fmaf(S1[2 * q + 1], sl, nm)));
+                    }
+                    va = vn;
+                }
+                ATTN_INTERLEAVE(2 * NDB, 1, 5);
+            }
+            // the row sum is taken from the rounded probabilities that feed
+            // the P.V product
+            l_run += sum_bf16_pairs(pk);
+
+            store_k(rr, cur);
+            store_v(rr ^ 1, cur);
             __syncthreads();
+            S0 = N0;
+            S1 = N1;
+        };
+        for (int j = tb; j < te; ++j) {
+            if (PD == 2) {
+                tile(j, set0, set1);
+                if (++j >= te) break;
+                tile(j, set1, set0);
+            } else {
+                tile(j, set0, set0);
+            }
         }
     }
 
@@ -359,16 +454,23 @@ __global__ __launch_bounds__(256) void prefill_combine_kernel(PrefillArgs a) {
 #ifndef ATTN_PREFILL_MIN_TILES_PER_SPLIT
 #define ATTN_PREFILL_MIN_TILES_PER_SPLIT 4
 #endif
+#ifndef ATTN_PREFILL_BIG_TILE_BLOCKS
+#define ATTN_PREFILL_BIG_TILE_BLOCKS 256
+#endif
 constexpr int kTargetBlocks = ATTN_PREFILL_TARGET_BLOCKS;
 constexpr int kMinTilesPerSplit = ATTN_PREFILL_MIN_TILES_PER_SPLIT;
+constexpr int kBigTileBlocks = ATTN_PREFILL_BIG_TILE_BLOCKS;
 constexpr int kMaxSplits = 32;
 
 PrefillPlan plan_prefill(int n_seq, int n_heads, int n_kv, int head_dim, int n_tok, int max_chunk,
                          int max_end, size_t ws_available) {
-    PrefillPlan p{kWaves * 32, 1, 1, 0};
     const long group = n_heads / n_kv;
     const long rows = (long)max_chunk * group;
-    p.n_qtiles = (int)((rows + kWaves * 32 - 1) / (kWaves * 32));
+    // 256-row workgroups (8 waves, deeper prefetch) when they alone give every
+    // CU a workgroup; otherwise 128-row workgroups, split along the keys
+    const long big = (long)n_seq * ((rows + 255) / 256) * n_kv;
+    if (big >= kBigTileBlocks) return PrefillPlan{256, (int)((rows + 255) / 256), 1, 0};
+    PrefillPlan p{128, (int)((rows + 127) / 128), 1, 0};
     const long base = (long)n_seq * p.n_qtiles * n_kv;
     const long tiles = ((long)max_end + kTK - 1) / kTK;
     long sp = base > 0 ? (kTargetBlocks + base - 1) / base : 1;
@@ -391,9 +493,14 @@ PrefillPlan plan_prefill(int n_seq, int n_heads, int n_kv, int head_dim, int n_t
 hipError_t launch_prefill_bf16(const PrefillArgs& a, hipStream_t stream) {
     const long blocks = (long)a.n_seq * a.n_qtiles * a.n_splits * a.n_kv;
     if (blocks <= 0) return hipSuccess;
-    const dim3 grid((unsigned)blocks), block(kThreads);
-    if (a.head_dim == 128) prefill_bf16_kernel<128><<<grid, block, 0, stream>>>(a);
-    else prefill_bf16_kernel<64><<<grid, block, 0, stream>>>(a);
+    const dim3 grid((unsigned)blocks);
+    if (a.rows_per_tile == 256) {
+        if (a.head_dim == 128) prefill_bf16_kernel<128, 8><<<grid, dim3(512), 0, stream>>>(a);
+        else prefill_bf16_kernel<64, 8><<<grid, dim3(512), 0, stream>>>(a);
+    } else {
+        if (a.head_dim == 128) prefill_bf16_kernel<128, 4><<<grid, dim3(256), 0, stream>>>(a);
+        else prefill_bf16_kernel<64, 4><<<grid, dim3(256), 0, stream>>>(a);
+    }
     return hipGetLastError();
 }
 

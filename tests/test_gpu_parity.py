@@ -205,6 +205,21 @@ def test_bf16_varlen_qknorm_partial_rotary():
     check_bf16_rows(np64(run.gather("out")), ref["out"], "varlen")
 
 
+def test_bf16_varlen_many_sequences_wide_tiles():
+    # 32 prompts x 8 KV groups give enough 256-row tiles for the 8-wave,
+    # deeper-prefetch variant; ragged lengths cover empty and partial tiles
+    w = wl.Workload(name="wide", dtype=wl.BF16, n_heads=32, n_kv=8, head_dim=128, seed=26,
+                    n_seq=32, len_range=(1, 200), chunk=64, cap=200)
+    say(f"bf16 varlen 32 sequences {w}")
+    d = wl.gen_prefill(w)
+    run = runner.ChunkedPrefill(w, d, device=DEV)
+    assert any(api.prefill_workspace_bytes(s["batch"], 32, 8, 128) == 0 for s in run.steps)
+    run.run_all()
+    torch.cuda.synchronize()
+    ref = oracle_prefill_packed(w, d, 64)
+    check_bf16_rows(np64(run.gather("out")), ref["out"], "wide")
+
+
 def test_bf16_chunked_equals_sequential():
     w = wl.Workload(name="seq", dtype=wl.BF16, n_heads=8, n_kv=2, head_dim=128, seed=24,
                     prompt_len=160, chunk=64)
