@@ -12,7 +12,10 @@
 namespace {
 
 constexpr int kDecodePartPad = 4;
-constexpr int kDecodeSplit = 1024;      // keys per decode part
+#ifndef ATTN_DECODE_SPLIT
+#define ATTN_DECODE_SPLIT 1024
+#endif
+constexpr int kDecodeSplit = ATTN_DECODE_SPLIT;   // keys per decode part
 
 bool dtype_ok(int dtype) { return dtype == ATTN_F32 || dtype == ATTN_BF16; }
 bool hd_ok(int hd) { return hd == 64 || hd == 128; }
@@ -33,7 +36,17 @@ int check_rope(int dtype, int n_tok, int n_heads, int head_dim, int n_seq, const
     return ATTN_OK;
 }
 
-int decode_splits_full(int max_ctx) { return (max_ctx + kDecodeSplit - 1) / kDecodeSplit; }
+// Parts of kDecodeSplit keys, shorter when the group is wide (the kernel
+// keeps a part's raw scores on chip; the limit holds with or without
+// probabilities so the workspace size never depends on them).
+int decode_split_len(int group) {
+    const int lim = attn::decode_part_limit(group, true);
+    return kDecodeSplit < lim ? kDecodeSplit : lim;
+}
+int decode_splits_full(int max_ctx, int group) {
+    const int len = decode_split_len(group);
+    return (max_ctx + len - 1) / len;
+}
 
 size_t decode_part_bytes(int n_seq, int n_heads, int head_dim, int splits) {
     return (size_t)n_seq * n_heads * splits * (head_dim + kDecodePartPad) * sizeof(float);
@@ -232,7 +245,7 @@ size_t attn_decode_workspace_bytes(int n_seq, int n_heads, int n_kv, int head_di
     if (n_seq <= 0 || n_heads <= 0 || n_kv <= 0 || n_heads % n_kv || max_ctx <= 0 ||
         !hd_ok(head_dim))
         return 0;
-    return decode_part_bytes(n_seq, n_heads, head_dim, decode_splits_full(max_ctx));
+    return decode_part_bytes(n_seq, n_heads, head_dim, decode_splits_full(max_ctx, n_heads / n_kv));
 }
 
 int attn_decode(const void* q, const void* k_cache, const void* v_cache, int dtype, int n_seq,
@@ -273,7 +286,7 @@ int attn_decode(const void* q, const void* k_cache, const void* v_cache, int dty
     if (group > attn::decode_group_limit()) return ATTN_EUNSUPPORTED;
     const size_t per = decode_part_bytes(n_seq, n_heads, head_dim, 1);
     if (!workspace || workspace_bytes < per) return ATTN_EINVAL;
-    int splits = decode_splits_full(max_ctx);
+    int splits = decode_splits_full(max_ctx, group);
     const size_t fit = workspace_bytes / per;
     if ((size_t)splits > fit) splits = (int)fit;
     int split_len = (max_ctx + splits - 1) / splits;

@@ -10,14 +10,21 @@
 // Design (gfx950):
 //  * The context of each (sequence, KV group) is split into parts of
 //    split_len keys, one single-wave workgroup per part, so a batch of long
-//    sequences gives thousands of independent streams to cover HBM latency.
-//  * Scores for 64 keys come from four v_mfma_f32_16x16x32_bf16: A = the
-//    group's queries (rows = heads, padded to 16), B = K rows straight from
-//    global memory (each lane loads 16 contiguous bytes of one key row).
+//    sequences gives thousands of independent streams.
+//  * The wave walks its part 32 keys at a time with the next step's K and V
+//    loads (16 KB, nontemporal: every byte is used once) in flight while the
+//    current step is computed, so HBM always has work queued.
+//  * Scores for 16 keys come from v_mfma_f32_16x16x32_bf16 with A = the
+//    group's queries and B = K rows straight from global memory.  Query head
+//    h sits in A row 4*(h/HPL) + h%HPL, so in the result the 16-lane group j
+//    holds heads j*HPL.. and lane j*16+c holds key c: softmax reductions are
+//    four DPP steps inside a 16-lane row.
 //  * P.V runs on the vector ALU in float32: each lane owns 8 dims of V for
-//    every (512/head_dim)-th key, so one wave instruction loads 1 KB of
-//    consecutive rows; the
-//    probabilities and the per-head rescale factors go through LDS.
+//    every (512/head_dim)-th key, so one wave load covers 1 KB of
+//    consecutive rows; the probabilities reach those lanes through LDS.
+//  * The running maximum only moves (and O is rescaled) when a score exceeds
+//    it by more than 2^8; until then probabilities are referenced to the old
+//    maximum, which leaves the softmax unchanged.
 //  * Each part leaves (m, l, O) in the workspace and, when asked, its raw
 //    log2-domain scores in the probabilities buffer; the combine kernel merges
 //    the parts with log-sum-exp and turns the scores into probabilities.
@@ -26,24 +33,76 @@
 
 namespace attn {
 
-constexpr int kDecKB = 64;      // keys per iteration
+constexpr int kDecKB = 32;      // keys per step
 constexpr int kPartPadD = 4;    // (m, l, pad, pad) before O in a partial
 constexpr int kDecMaxGroup = 16;
+constexpr float kDecSlack = 8.f;
+// LDS floats per wave that hold a part's raw scores (16 KB)
+constexpr int kDecPartFloats = 4096;
 
 int decode_group_limit() { return kDecMaxGroup; }
+
+// Heads handled per KV group by the kernel instance (4, 8 or 16); with
+// probabilities a part holds at most kDecPartFloats / that many keys.
+static int decode_heads_padded(int group) { return group <= 4 ? 4 : group <= 8 ? 8 : 16; }
+int decode_part_limit(int group, bool probs) {
+    return probs ? kDecPartFloats / decode_heads_padded(group) : 1 << 30;
+}
 
 __device__ __forceinline__ f32x4_t mfma16(bf16x8_t a, bf16x8_t b, f32x4_t c) {
     return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
 }
 
-template <int HD, int GQ>
+// DPP reductions over the 16 lanes of a row: pair, quad, half-row mirror,
+// row mirror.  Every lane of the row ends with the result.
+__device__ __forceinline__ float dpp_f(float x, int ctrl_sel) {
+    const int v = __float_as_int(x);
+    int r;
+    switch (ctrl_sel) {
+        case 0: r = __builtin_amdgcn_update_dpp(v, v, 0xB1, 0xF, 0xF, false); break;   // quad_perm 1,0,3,2
+        case 1: r = __builtin_amdgcn_update_dpp(v, v, 0x4E, 0xF, 0xF, false); break;   // quad_perm 2,3,0,1
+        case 2: r = __builtin_amdgcn_update_dpp(v, v, 0x141, 0xF, 0xF, false); break;  // row_half_mirror
+        default: r = __builtin_amdgcn_update_dpp(v, v, 0x140, 0xF, 0xF, false); break; // row_mirror
+    }
+    return __int_as_float(r);
+}
+__device__ __forceinline__ float row16_max(float x) {
+#pragma unroll
+    for (int c = 0; c < 4; ++c) x = fmaxf(x, dpp_f(x, c));
+    return x;
+}
+__device__ __forceinline__ float row16_sum(float x) {
+#pragma unroll
+    for (int c = 0; c < 4; ++c) x += dpp_f(x, c);
+    return x;
+}
+
+// A 16-byte vector that only needs 4-byte alignment (probability rows start
+// wherever probs_ld puts them; global accesses need no wider alignment).
+typedef float f32x4_a4_t __attribute__((ext_vector_type(4), aligned(4)));
+
+__device__ __forceinline__ u32x4_t ld16_nt(const uint16_t* p) {
+    return __builtin_nontemporal_load(reinterpret_cast<const u32x4_t*>(p));
+}
+
+// The workgroup is one wave, whose LDS accesses execute in program order, so
+// exchanging values between lanes through LDS only needs the compiler to
+// keep the accesses in order (a fence would also wait for the global loads
+// in flight, which are the next step's prefetch).
+__device__ __forceinline__ void lds_order() { asm volatile("" ::: "memory"); }
+
+template <int HD, int HPL, bool PROBS>
 __global__ __launch_bounds__(64) void decode_split_kernel(DecodeArgs a) {
+    constexpr int GQ = 4 * HPL;                 // query heads per group handled
     constexpr int NK = HD / 32;                 // K-steps per 16x16x32 product
-    constexpr int LPR = HD / 8;                 // lanes per V row (8 dims each)
-    constexpr int KPI = 64 / LPR;               // V rows per wave instruction
-    constexpr int VROWS = kDecKB / KPI;         // V rows per lane per iteration
-    __shared__ float pbuf[kDecKB * 16];
-    __shared__ float abuf[16];
+    constexpr int CPR = HD / 8;                 // 16-byte chunks per cache row
+    constexpr int RPI = 64 / CPR;               // V rows per wave load
+    constexpr int NV = kDecKB / RPI;            // V loads per lane per step
+    __shared__ __attribute__((aligned(16))) float pbuf[kDecKB * GQ];   // P[key][head]
+    __shared__ __attribute__((aligned(16))) float abuf[GQ];
+    // the part's raw scores, [head][key], written out once the part is done
+    __shared__ __attribute__((aligned(16))) float sbuf[PROBS ? kDecPartFloats : 4];
+    constexpr int PK = kDecPartFloats / GQ;     // longest part with probabilities
 
     const int lane = threadIdx.x;
     int id = blockIdx.x;
@@ -58,30 +117,33 @@ __global__ __launch_bounds__(64) void decode_split_kernel(DecodeArgs a) {
     if (k_lo >= k_hi) return;
     const int G = a.group;
 
-    const int qh = lane & 15;    // score layout: key column / query-row index
-    const int quad = lane >> 4;  // score layout: heads 4*quad .. 4*quad+3
-    const int c = lane % LPR;    // P.V layout: dims 8c .. 8c+7
-    const int kr = lane / LPR;   // P.V layout: keys kr, kr+KPI, ...
+    const int col = lane & 15;   // score layout: key within a 16-key block
+    const int grp = lane >> 4;   // score layout: heads grp*HPL .. grp*HPL+HPL-1
+    const int vc_ = lane % CPR;  // P.V layout: dims 8*vc_ .. 8*vc_+7
+    const int vr = lane / CPR;   // P.V layout: keys vr, vr+RPI, ...
 
     bf16x8_t qa[NK];
     {
+        // A row `col` holds head (col/4)*HPL + col%4 when col%4 < HPL
+        const int hq = (col >> 2) * HPL + (col & 3);
+        const bool ok = (col & 3) < HPL && hq < G;
         const uint16_t* qb =
-            reinterpret_cast<const uint16_t*>(a.q) + ((size_t)b * a.n_heads + g * G) * HD;
+            reinterpret_cast<const uint16_t*>(a.q) + ((size_t)b * a.n_heads + g * G + (ok ? hq : 0)) * HD;
 #pragma unroll
         for (int k = 0; k < NK; ++k) {
-            uint4 u = make_uint4(0, 0, 0, 0);
-            if (qh < G) u = *reinterpret_cast<const uint4*>(qb + (size_t)qh * HD + 32 * k + 8 * quad);
+            u32x4_t u = {0u, 0u, 0u, 0u};
+            if (ok) u = ld16(qb + 32 * k + 8 * grp);
             qa[k] = __builtin_bit_cast(bf16x8_t, u);
         }
     }
     const size_t base = ((size_t)b * a.n_kv + g) * (size_t)a.cap * HD;
     const uint16_t* kc = reinterpret_cast<const uint16_t*>(a.k_cache) + base;
-    const uint16_t* vc = reinterpret_cast<const uint16_t*>(a.v_cache) + base;
-    float* prow = a.probs ? a.probs + ((size_t)b * a.n_heads + g * G) * a.probs_ld : nullptr;
+    const uint16_t* vcache = reinterpret_cast<const uint16_t*>(a.v_cache) + base;
+    float* prow = PROBS ? a.probs + ((size_t)b * a.n_heads + g * G) * a.probs_ld : nullptr;
 
-    float m_run[4], l_run[4];
+    float m_run[HPL], l_run[HPL];
 #pragma unroll
-    for (int r = 0; r < 4; ++r) {
+    for (int r = 0; r < HPL; ++r) {
         m_run[r] = -INFINITY;
         l_run[r] = 0.f;
     }
@@ -91,101 +153,116 @@ __global__ __launch_bounds__(64) void decode_split_kernel(DecodeArgs a) {
 #pragma unroll
         for (int e = 0; e < 8; ++e) o[hh][e] = 0.f;
     const float sl = a.scale * kLog2e;
+    const int last = k_hi - 1;
 
-    for (int k0 = k_lo; k0 < k_hi; k0 += kDecKB) {
-        uint4 kf[4][NK];
+    // Rows past the part's end re-read its last row (in bounds); their
+    // scores are masked to -inf so their probabilities are exactly 0.
+    u32x4_t kf[2][2][NK], vf[2][NV];
+    auto load = [&](int k0, int buf) __attribute__((always_inline)) {
 #pragma unroll
-        for (int blk = 0; blk < 4; ++blk) {
-            const int key = k0 + 16 * blk + qh;
+        for (int blk = 0; blk < 2; ++blk) {
+            const int key = min(k0 + 16 * blk + col, last);
 #pragma unroll
-            for (int k = 0; k < NK; ++k)
-                kf[blk][k] = key < k_hi
-                                 ? *reinterpret_cast<const uint4*>(kc + (size_t)key * HD + 32 * k + 8 * quad)
-                                 : make_uint4(0, 0, 0, 0);
+            for (int k = 0; k < NK; ++k) kf[buf][blk][k] = ld16_nt(kc + (size_t)key * HD + 32 * k + 8 * grp);
         }
-        uint4 vf[VROWS];
 #pragma unroll
-        for (int ii = 0; ii < VROWS; ++ii) {
-            const int key = k0 + kr + KPI * ii;
-            vf[ii] = key < k_hi ? *reinterpret_cast<const uint4*>(vc + (size_t)key * HD + 8 * c)
-                                : make_uint4(0, 0, 0, 0);
+        for (int i = 0; i < NV; ++i) {
+            const int key = min(k0 + RPI * i + vr, last);
+            vf[buf][i] = ld16_nt(vcache + (size_t)key * HD + 8 * vc_);
         }
-        // scores: S[blk][r] = head 4*quad + r, key k0 + 16*blk + qh
-        float x[4][4];
+    };
+
+    // Raw scores wait in LDS and are written once per PK keys (normally once
+    // per part): a global write among the K/V reads stalls the read stream
+    // far more than its size suggests (HBM read/write turnaround).
+    // flush: keys [base, base+n) of the buffer to the probabilities rows.
+    auto flush = [&](int base, int n) __attribute__((always_inline)) {
+        lds_order();
+        for (int t = lane; t < G * (PK / 4); t += 64) {
+            const int hh = t / (PK / 4), kq = 4 * (t % (PK / 4));
+            if (kq < n) {
+                const f32x4_t v = *reinterpret_cast<const f32x4_t*>(&sbuf[hh * PK + kq]);
+                float* dst = prow + (size_t)hh * a.probs_ld + base + kq;
+                if (kq + 3 < n) {
+                    *reinterpret_cast<f32x4_a4_t*>(dst) = v;
+                } else {
 #pragma unroll
-        for (int blk = 0; blk < 4; ++blk) {
-            f32x4_t S = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-            for (int k = 0; k < NK; ++k) S = mfma16(qa[k], __builtin_bit_cast(bf16x8_t, kf[blk][k]), S);
-            const bool ok = k0 + 16 * blk + qh < k_hi;
-#pragma unroll
-            for (int r = 0; r < 4; ++r) x[blk][r] = ok ? S[r] * sl : -INFINITY;
-        }
-        if (prow) {
-#pragma unroll
-            for (int blk = 0; blk < 4; ++blk) {
-                const int key = k0 + 16 * blk + qh;
-#pragma unroll
-                for (int r = 0; r < 4; ++r) {
-                    const int hh = 4 * quad + r;
-                    if (hh < G && key < k_hi) prow[(size_t)hh * a.probs_ld + key] = x[blk][r];
+                    for (int e = 0; e < 3; ++e)
+                        if (kq + e < n) dst[e] = v[e];
                 }
             }
         }
-        float alpha[4];
-#pragma unroll
-        for (int r = 0; r < 4; ++r) {
-            float mt = fmaxf(fmaxf(x[0][r], x[1][r]), fmaxf(x[2][r], x[3][r]));
-#pragma unroll
-            for (int off = 1; off < 16; off <<= 1) mt = fmaxf(mt, __shfl_xor(mt, off));
-            const float m_new = fmaxf(m_run[r], mt);   // finite: key k0 is in range
-            alpha[r] = __builtin_amdgcn_exp2f(m_run[r] - m_new);
-            float ps = 0.f;
-#pragma unroll
-            for (int blk = 0; blk < 4; ++blk) {
-                x[blk][r] = __builtin_amdgcn_exp2f(x[blk][r] - m_new);
-                ps += x[blk][r];
-            }
-            l_run[r] = l_run[r] * alpha[r] + ps;
-            m_run[r] = m_new;
-        }
-#pragma unroll
-        for (int blk = 0; blk < 4; ++blk)
-            *reinterpret_cast<float4*>(&pbuf[(16 * blk + qh) * 16 + 4 * quad]) =
-                make_float4(x[blk][0], x[blk][1], x[blk][2], x[blk][3]);
-        if (qh == 0)
-            *reinterpret_cast<float4*>(&abuf[4 * quad]) =
-                make_float4(alpha[0], alpha[1], alpha[2], alpha[3]);
-        __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
-        __builtin_amdgcn_wave_barrier();
-        __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+        lds_order();
+    };
 
+    auto step = [&](int k0, int buf) __attribute__((always_inline)) {
+        float x[2][HPL];
 #pragma unroll
-        for (int hq = 0; hq < GQ / 4; ++hq) {
-            const float4 al = *reinterpret_cast<const float4*>(&abuf[4 * hq]);
+        for (int blk = 0; blk < 2; ++blk) {
+            f32x4_t S = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-            for (int e = 0; e < 8; ++e) {
-                o[4 * hq + 0][e] *= al.x;
-                o[4 * hq + 1][e] *= al.y;
-                o[4 * hq + 2][e] *= al.z;
-                o[4 * hq + 3][e] *= al.w;
-            }
+            for (int k = 0; k < NK; ++k) S = mfma16(qa[k], __builtin_bit_cast(bf16x8_t, kf[buf][blk][k]), S);
+            const bool ok = k0 + 16 * blk + col < k_hi;
+#pragma unroll
+            for (int r = 0; r < HPL; ++r) x[blk][r] = ok ? S[r] * sl : -INFINITY;
         }
+        bool grow_any = false;
+        float mt[HPL];
 #pragma unroll
-        for (int ii = 0; ii < VROWS; ++ii) {
-            const int kl = kr + KPI * ii;
-            float v[8];
-            v[0] = bf16_lo(vf[ii].x);
-            v[1] = bf16_hi(vf[ii].x);
-            v[2] = bf16_lo(vf[ii].y);
-            v[3] = bf16_hi(vf[ii].y);
-            v[4] = bf16_lo(vf[ii].z);
-            v[5] = bf16_hi(vf[ii].z);
-            v[6] = bf16_lo(vf[ii].w);
-            v[7] = bf16_hi(vf[ii].w);
+        for (int r = 0; r < HPL; ++r) {
+            mt[r] = row16_max(fmaxf(x[0][r], x[1][r]));   // finite: key k0 is in range
+            grow_any |= mt[r] > m_run[r] + kDecSlack;
+        }
+        if (__any(grow_any)) {
+            float al[HPL];
+#pragma unroll
+            for (int r = 0; r < HPL; ++r) {
+                const bool grow = mt[r] > m_run[r] + kDecSlack;
+                al[r] = grow ? __builtin_amdgcn_exp2f(m_run[r] - mt[r]) : 1.f;
+                m_run[r] = grow ? mt[r] : m_run[r];
+                l_run[r] *= al[r];
+            }
+            if (col == 0) {
+#pragma unroll
+                for (int r = 0; r < HPL; ++r) abuf[grp * HPL + r] = al[r];
+            }
+            lds_order();
 #pragma unroll
             for (int hq = 0; hq < GQ / 4; ++hq) {
-                const float4 p = *reinterpret_cast<const float4*>(&pbuf[kl * 16 + 4 * hq]);
+                const float4 f = *reinterpret_cast<const float4*>(&abuf[4 * hq]);
+#pragma unroll
+                for (int e = 0; e < 8; ++e) {
+                    o[4 * hq + 0][e] *= f.x;
+                    o[4 * hq + 1][e] *= f.y;
+                    o[4 * hq + 2][e] *= f.z;
+                    o[4 * hq + 3][e] *= f.w;
+                }
+            }
+        }
+#pragma unroll
+        for (int blk = 0; blk < 2; ++blk)
+#pragma unroll
+            for (int r = 0; r < HPL; ++r) {
+                const float p = __builtin_amdgcn_exp2f(x[blk][r] - m_run[r]);
+                l_run[r] += p;
+                pbuf[(16 * blk + col) * GQ + grp * HPL + r] = p;
+            }
+        lds_order();
+#pragma unroll
+        for (int i = 0; i < NV; ++i) {
+            const int kl = RPI * i + vr;
+            float v[8];
+            v[0] = bf16_lo(vf[buf][i].x);
+            v[1] = bf16_hi(vf[buf][i].x);
+            v[2] = bf16_lo(vf[buf][i].y);
+            v[3] = bf16_hi(vf[buf][i].y);
+            v[4] = bf16_lo(vf[buf][i].z);
+            v[5] = bf16_hi(vf[buf][i].z);
+            v[6] = bf16_lo(vf[buf][i].w);
+            v[7] = bf16_hi(vf[buf][i].w);
+#pragma unroll
+            for (int hq = 0; hq < GQ / 4; ++hq) {
+                const float4 p = *reinterpret_cast<const float4*>(&pbuf[kl * GQ + 4 * hq]);
 #pragma unroll
                 for (int e = 0; e < 8; ++e) {
                     o[4 * hq + 0][e] += p.x * v[e];
@@ -195,39 +272,64 @@ __global__ __launch_bounds__(64) void decode_split_kernel(DecodeArgs a) {
                 }
             }
         }
-        // pbuf/abuf are rewritten by the next iteration
-        __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
-        __builtin_amdgcn_wave_barrier();
-        __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+        // pbuf/abuf are rewritten by the next step
+        lds_order();
+        if (PROBS) {
+            const int kb = (k0 - k_lo) % PK;      // PK is a multiple of 64
+#pragma unroll
+            for (int blk = 0; blk < 2; ++blk)
+#pragma unroll
+                for (int r = 0; r < HPL; ++r) sbuf[(grp * HPL + r) * PK + kb + 16 * blk + col] = x[blk][r];
+            // a part longer than the buffer writes it out each time it fills
+            if (kb + kDecKB == PK && k0 + kDecKB < k_hi) flush(k0 + kDecKB - PK, PK);
+        }
+    };
+
+    // two register sets: the loads of step i+1 are issued before step i
+    // runs.  They are unconditional (a prefetch past the part's end re-reads
+    // its last row) so the compiler's wait counts stay exact.
+    // Steps go in pairs; an odd count ends with a step whose keys are all
+    // past the part (scores -inf, probabilities 0, nothing stored).
+    load(k_lo, 0);
+    for (int k0 = k_lo; k0 < k_hi; k0 += 2 * kDecKB) {
+        load(k0 + kDecKB, 1);
+        step(k0, 0);
+        load(k0 + 2 * kDecKB, 0);
+        step(k0 + kDecKB, 1);
     }
 
-    // l: sum the 16 key-lanes of each head quad; O: sum the key residues
+    // the rest of the part's raw scores
+    if (PROBS) {
+        const int last_base = k_lo + (k_hi - 1 - k_lo) / PK * PK;
+        flush(last_base, k_hi - last_base);
+    }
+
+    // l: sum over the 16 key lanes of each head row; O: sum over the lanes
+    // that hold the same dims
 #pragma unroll
-    for (int r = 0; r < 4; ++r)
-#pragma unroll
-        for (int off = 1; off < 16; off <<= 1) l_run[r] += __shfl_xor(l_run[r], off);
+    for (int r = 0; r < HPL; ++r) l_run[r] = row16_sum(l_run[r]);
 #pragma unroll
     for (int hh = 0; hh < GQ; ++hh)
 #pragma unroll
         for (int e = 0; e < 8; ++e)
 #pragma unroll
-            for (int off = LPR; off < 64; off <<= 1) o[hh][e] += __shfl_xor(o[hh][e], off);
+            for (int off = CPR; off < 64; off <<= 1) o[hh][e] += __shfl_xor(o[hh][e], off);
 
     constexpr int PS = HD + kPartPadD;
     float* part = a.part + (((size_t)b * a.n_heads + g * G) * a.n_splits + s) * PS;
     const size_t head_stride = (size_t)a.n_splits * PS;
-    if (qh == 0) {
+    if (col == 0) {
 #pragma unroll
-        for (int r = 0; r < 4; ++r) {
-            const int hh = 4 * quad + r;
+        for (int r = 0; r < HPL; ++r) {
+            const int hh = grp * HPL + r;
             if (hh < G) *reinterpret_cast<float2*>(part + hh * head_stride) = make_float2(m_run[r], l_run[r]);
         }
     }
-    if (kr == 0) {
+    if (vr == 0) {
 #pragma unroll
         for (int hh = 0; hh < GQ; ++hh) {
             if (hh < G) {
-                float* dst = part + hh * head_stride + kPartPadD + 8 * c;
+                float* dst = part + hh * head_stride + kPartPadD + 8 * vc_;
                 *reinterpret_cast<float4*>(dst) = make_float4(o[hh][0], o[hh][1], o[hh][2], o[hh][3]);
                 *reinterpret_cast<float4*>(dst + 4) = make_float4(o[hh][4], o[hh][5], o[hh][6], o[hh][7]);
             }
@@ -238,8 +340,22 @@ __global__ __launch_bounds__(64) void decode_split_kernel(DecodeArgs a) {
 // One workgroup per (sequence, head): merge the parts that cover
 // [0, ctx) and, when asked, rewrite the raw scores as probabilities
 // P_j = 2^(x_j - m) / l.
+__device__ __forceinline__ float block_reduce(float v, float* sh, bool is_max) {
+    v = is_max ? wave_max(v) : wave_sum(v);
+    const int w = threadIdx.x >> 6;
+    __syncthreads();                    // sh may still be read from a previous reduction
+    if ((threadIdx.x & 63) == 0) sh[w] = v;
+    __syncthreads();
+    float r = sh[0];
+#pragma unroll
+    for (int i = 1; i < 4; ++i) r = is_max ? fmaxf(r, sh[i]) : r + sh[i];
+    return r;
+}
+
 template <int HD>
 __global__ __launch_bounds__(256) void decode_combine_kernel(DecodeArgs a) {
+    __shared__ float red[4];
+    __shared__ float osum[256];
     const int row = blockIdx.x;
     const int b = row / a.n_heads;
     const int tid = threadIdx.x;
@@ -253,47 +369,90 @@ __global__ __launch_bounds__(256) void decode_combine_kernel(DecodeArgs a) {
     constexpr int PS = HD + kPartPadD;
     const int n_parts = min((ctx + a.split_len - 1) / a.split_len, a.n_splits);
     const float* pr = a.part + (size_t)row * a.n_splits * PS;
-    float m = -INFINITY;
-    for (int s = 0; s < n_parts; ++s) m = fmaxf(m, pr[(size_t)s * PS]);
-    float l = 0.f;
-    for (int s = 0; s < n_parts; ++s) l += pr[(size_t)s * PS + 1] * __builtin_amdgcn_exp2f(pr[(size_t)s * PS] - m);
+    float mm = -INFINITY;
+    for (int s = tid; s < n_parts; s += 256) mm = fmaxf(mm, pr[(size_t)s * PS]);
+    const float m = block_reduce(mm, red, true);
+    float ll = 0.f;
+    for (int s = tid; s < n_parts; s += 256)
+        ll += pr[(size_t)s * PS + 1] * __builtin_amdgcn_exp2f(pr[(size_t)s * PS] - m);
+    const float l = block_reduce(ll, red, false);
     const float inv = 1.f / l;
-    for (int d = tid; d < HD; d += 256) {
+    // O: thread -> (dim, phase); phases take every (256/HD)-th part
+    {
+        constexpr int PH = 256 / HD;
+        const int d = tid % HD, ph = tid / HD;
         float acc = 0.f;
-        for (int s = 0; s < n_parts; ++s)
-            acc += pr[(size_t)s * PS + kPartPadD + d] * __builtin_amdgcn_exp2f(pr[(size_t)s * PS] - m);
-        orow[d] = acc * inv;
+        int s = ph;
+        for (; s + 3 * PH < n_parts; s += 4 * PH) {
+            float w[4], x[4];
+#pragma unroll
+            for (int u = 0; u < 4; ++u) {
+                const float* p = pr + (size_t)(s + u * PH) * PS;
+                w[u] = p[0];
+                x[u] = p[kPartPadD + d];
+            }
+#pragma unroll
+            for (int u = 0; u < 4; ++u) acc += x[u] * __builtin_amdgcn_exp2f(w[u] - m);
+        }
+        for (; s < n_parts; s += PH) acc += pr[(size_t)s * PS + kPartPadD + d] * __builtin_amdgcn_exp2f(pr[(size_t)s * PS] - m);
+        osum[tid] = acc;
+        __syncthreads();
+        if (tid < HD) {
+            float t = 0.f;
+#pragma unroll
+            for (int q = 0; q < PH; ++q) t += osum[q * HD + tid];
+            orow[tid] = t * inv;
+        }
     }
     if (a.probs) {
         // P_j = 2^(x_j - m) / l over the row's ctx entries; 16-byte accesses
-        // between a scalar head (up to the first aligned element) and tail
+        // (four in flight per thread) between a scalar head, up to the first
+        // aligned element, and a scalar tail
         float* prow = a.probs + (size_t)row * a.probs_ld;
         const int head = min((int)((4 - (((uintptr_t)prow >> 2) & 3)) & 3), ctx);
         for (int j = tid; j < head; j += 256) prow[j] = __builtin_amdgcn_exp2f(prow[j] - m) * inv;
-        float4* p4 = reinterpret_cast<float4*>(prow + head);
+        f32x4_t* p4 = reinterpret_cast<f32x4_t*>(prow + head);
         const int n4 = (ctx - head) >> 2;
-        for (int j = tid; j < n4; j += 256) {
-            float4 v = p4[j];
-            v.x = __builtin_amdgcn_exp2f(v.x - m) * inv;
-            v.y = __builtin_amdgcn_exp2f(v.y - m) * inv;
-            v.z = __builtin_amdgcn_exp2f(v.z - m) * inv;
-            v.w = __builtin_amdgcn_exp2f(v.w - m) * inv;
-            p4[j] = v;
+        int j = tid;
+        for (; j + 3 * 256 < n4; j += 4 * 256) {
+            f32x4_t v[4];
+#pragma unroll
+            for (int u = 0; u < 4; ++u) v[u] = __builtin_nontemporal_load(p4 + j + u * 256);
+#pragma unroll
+            for (int u = 0; u < 4; ++u) {
+#pragma unroll
+                for (int e = 0; e < 4; ++e) v[u][e] = __builtin_amdgcn_exp2f(v[u][e] - m) * inv;
+                __builtin_nontemporal_store(v[u], p4 + j + u * 256);
+            }
         }
-        for (int j = head + 4 * n4 + tid; j < ctx; j += 256)
-            prow[j] = __builtin_amdgcn_exp2f(prow[j] - m) * inv;
+        for (; j < n4; j += 256) {
+            f32x4_t v = __builtin_nontemporal_load(p4 + j);
+#pragma unroll
+            for (int e = 0; e < 4; ++e) v[e] = __builtin_amdgcn_exp2f(v[e] - m) * inv;
+            __builtin_nontemporal_store(v, p4 + j);
+        }
+        for (int t = head + 4 * n4 + tid; t < ctx; t += 256)
+            prow[t] = __builtin_amdgcn_exp2f(prow[t] - m) * inv;
     }
+}
+
+template <int HD, bool PROBS>
+static void launch_split(const DecodeArgs& a, hipStream_t stream) {
+    const dim3 grid((unsigned)((long)a.n_seq * a.n_splits * a.n_kv));
+    if (a.group <= 4)
+        decode_split_kernel<HD, 1, PROBS><<<grid, dim3(64), 0, stream>>>(a);
+    else if (a.group <= 8)
+        decode_split_kernel<HD, 2, PROBS><<<grid, dim3(64), 0, stream>>>(a);
+    else
+        decode_split_kernel<HD, 4, PROBS><<<grid, dim3(64), 0, stream>>>(a);
 }
 
 template <int HD>
 static void launch_decode_hd(const DecodeArgs& a, hipStream_t stream) {
-    const long blocks = (long)a.n_seq * a.n_splits * a.n_kv;
-    if (a.group <= 4)
-        decode_split_kernel<HD, 4><<<dim3((unsigned)blocks), dim3(64), 0, stream>>>(a);
-    else if (a.group <= 8)
-        decode_split_kernel<HD, 8><<<dim3((unsigned)blocks), dim3(64), 0, stream>>>(a);
+    if (a.probs)
+        launch_split<HD, true>(a, stream);
     else
-        decode_split_kernel<HD, 16><<<dim3((unsigned)blocks), dim3(64), 0, stream>>>(a);
+        launch_split<HD, false>(a, stream);
     decode_combine_kernel<HD><<<dim3((unsigned)(a.n_seq * a.n_heads)), dim3(256), 0, stream>>>(a);
 }
 

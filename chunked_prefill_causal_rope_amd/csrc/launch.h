@@ -78,6 +78,8 @@ struct DecodeArgs {
     int split_len, n_splits;
 };
 int decode_group_limit();
+// Longest key range one decode part may cover (a multiple of 64).
+int decode_part_limit(int group, bool probs);
 hipError_t launch_decode_bf16(const DecodeArgs& a, hipStream_t stream);
 
 }  // namespace attn

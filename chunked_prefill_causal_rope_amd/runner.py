@@ -114,7 +114,7 @@ class DecodeStep:
     the new key/value at position ctx-1, attend keys 0..ctx-1 (with the
     probabilities when the workload asks for them)."""
 
-    def __init__(self, w: Workload, data: dict, device="cuda"):
+    def __init__(self, w: Workload, data: dict, device="cuda", probs_ld_multiple: int = 32):
         self.w = w
         ctx = data["ctx"]
         self.ctx_list = ctx
@@ -133,7 +133,11 @@ class DecodeStep:
         self.batch = api.Batch([c - 1 for c in ctx], [1] * n_seq, device=device)
         self.ctx = torch.tensor(ctx, dtype=torch.int32, device=device)
         self.out = torch.empty((n_seq, w.n_heads, w.head_dim), dtype=torch.float32, device=device)
-        self.probs = (torch.empty((n_seq, w.n_heads, self.max_ctx), dtype=torch.float32,
+        # probability rows padded to a multiple of 32 floats by default, so
+        # every row starts on a 128-byte line (any probs_ld >= max_ctx works)
+        m = max(1, int(probs_ld_multiple))
+        probs_ld = (self.max_ctx + m - 1) // m * m
+        self.probs = (torch.empty((n_seq, w.n_heads, probs_ld), dtype=torch.float32,
                                   device=device) if w.want_probs else None)
         wsb = api.decode_workspace_bytes(n_seq, w.n_heads, w.n_kv, w.head_dim, self.max_ctx)
         self.workspace = torch.empty(max(wsb, 16) // 4 + 1, dtype=torch.float32, device=device)

@@ -264,15 +264,16 @@ def test_empty_and_single_token():
 
 # ------------------------------------------------------------------ bf16 decode
 
-@pytest.mark.parametrize("nh,nkv,hd", [(16, 4, 128), (16, 2, 64), (8, 8, 128), (40, 8, 128)])
-def test_bf16_decode_matches_oracle(nh, nkv, hd):
+@pytest.mark.parametrize("nh,nkv,hd,ld_mult", [(16, 4, 128, 32), (16, 2, 64, 1), (8, 8, 128, 1),
+                                                (40, 8, 128, 32), (32, 8, 128, 1)])
+def test_bf16_decode_matches_oracle(nh, nkv, hd, ld_mult):
     ctx = [1, 63, 64, 65, 1025, 3000]
     w = wl.Workload(name="dec", dtype=wl.BF16, n_heads=nh, n_kv=nkv, head_dim=hd, seed=31,
                     n_seq=len(ctx), decode=True, ctx_range=(1, 3000), cap=3072, want_probs=True)
     say(f"bf16 decode nh={nh} nkv={nkv} hd={hd} ctx={ctx}")
     d = wl.gen_decode(w)
     d["ctx"] = ctx
-    step = runner.DecodeStep(w, d, device=DEV)
+    step = runner.DecodeStep(w, d, device=DEV, probs_ld_multiple=ld_mult)
     step.probs.fill_(float("nan"))
     step.run()
     torch.cuda.synchronize()
@@ -297,6 +298,44 @@ def test_bf16_decode_matches_oracle(nh, nkv, hd):
     # the new token's K/V rows were appended at ctx-1
     for b, c in enumerate(ctx):
         assert np.array_equal(_bits(step.v_cache[b, :, c - 1]), _bits(d["v"][b]))
+
+
+@pytest.mark.parametrize("nh,nkv,parts_per_row", [(32, 2, 1), (16, 2, 2)])
+def test_bf16_decode_small_workspace(nh, nkv, parts_per_row):
+    """A workspace for fewer parts makes each part longer than the on-chip
+    raw-score buffer of a wide group (16 or 8 heads), so the split kernel
+    writes the scores out several times per part."""
+    ctx = [3000, 700, 1, 2049]
+    hd = 128
+    w = wl.Workload(name="dec-ws", dtype=wl.BF16, n_heads=nh, n_kv=nkv, head_dim=hd, seed=37,
+                    n_seq=len(ctx), decode=True, ctx_range=(1, 3000), cap=3072, want_probs=True)
+    say(f"bf16 decode small workspace nh={nh} nkv={nkv} parts/row={parts_per_row} ctx={ctx}")
+    d = wl.gen_decode(w)
+    d["ctx"] = ctx
+    step = runner.DecodeStep(w, d, device=DEV, probs_ld_multiple=1)
+    step.workspace = torch.empty(len(ctx) * nh * (hd + 4) * parts_per_row, dtype=torch.float32,
+                                 device=DEV)
+    step.probs.fill_(float("nan"))
+    step.run()
+    torch.cuda.synchronize()
+    f = oracle_table(w)
+    got_o = np64(step.out)
+    got_p = np64(step.probs)
+    for b, c in enumerate(ctx):
+        pos = np.array([c - 1])
+        kc = np64(d["k_cache"][b])[:, :c].copy()
+        vc = np64(d["v_cache"][b])[:, :c].copy()
+        kc[:, c - 1] = oracle.finish_heads(np64(d["k"][b:b + 1]), pos, f, w.rd,
+                                           store=oracle.STORE_BF16)[0]
+        vc[:, c - 1] = np64(d["v"][b])
+        q = oracle.finish_heads(np64(d["q"][b:b + 1]), pos, f, w.rd, store=oracle.STORE_BF16)
+        o, P = oracle.attend(q, kc, vc, pos, w.scale, want_probs=True)
+        check_bf16_rows(got_o[b], o[0], f"seq {b} ctx {c}")
+        assert np.all(np.isnan(got_p[b, :, c:])), "entries past ctx must stay untouched"
+        pg = got_p[b, :, :c]
+        assert np.allclose(pg.sum(-1), 1.0, atol=1e-5)
+        dp = np.max(np.abs(pg - P[0]), axis=-1) / np.sqrt(np.mean(P[0] ** 2, axis=-1))
+        assert dp.max() <= 2e-2, dp.max()
 
 
 # ------------------------------------------------------------------ graphs
