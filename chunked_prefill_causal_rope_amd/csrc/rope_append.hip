@@ -9,11 +9,11 @@
 // the first rd dims), fn qwen_attention_batch (every row of the chunk is
 // appended before the chunk attends).
 //
-// One workgroup per (token, group of 4 heads), one wave per head: the token's
-// cos/sin table (rd/2 entries, double) is built in LDS by the workgroup and
-// shared by its heads.  The arithmetic is double precision, so the stored
-// value is the correctly rounded image of the exact finish (up to the last
-// bits of the double sine and cosine).
+// General path: one workgroup per (token, group of 4 heads), one wave per
+// head: the token's cos/sin table (rd/2 entries, double) is built in LDS by
+// the workgroup and shared by its heads.  On both paths the arithmetic is
+// double precision, so the stored value is the correctly rounded image of
+// the exact finish (up to the last bits of the double sine and cosine).
 #include "device_common.h"
 #include "launch.h"
 
@@ -112,15 +112,186 @@ __global__ __launch_bounds__(kRopeThreads) void rope_rows_kernel(RopeArgs a) {
     }
 }
 
-hipError_t launch_rope_rows(const RopeArgs& a, int dtype, bool kv, hipStream_t stream) {
-    dim3 grid(a.max_chunk, (a.n_heads + kRopeWaves - 1) / kRopeWaves, a.n_seq);
-    dim3 block(kRopeThreads);
-    if (dtype == 0) {
-        if (kv) rope_rows_kernel<float, true><<<grid, block, 0, stream>>>(a);
-        else rope_rows_kernel<float, false><<<grid, block, 0, stream>>>(a);
+// Fast path, for rotary_dim a multiple of 8: one workgroup per token and all
+// of its heads, so the token's cos/sin table (double) is built once.  A head
+// row is handled by HD/8 consecutive lanes, each owning 8 of its dims: a
+// "pair" lane owns dims 4c..4c+3 and their RoPE partners 4c+rd/2.., a "pass"
+// lane 8 dims past the rotary part.  Every lane issues its loads before the
+// table is built, the norm's sum of squares is a reduction over the lanes of
+// one row, and stores are 8 or 16 bytes wide.
+template <typename T> struct Raw;
+template <> struct Raw<uint16_t> {
+    // 8 bf16 = 16 bytes
+    u32x4_t w = {0u, 0u, 0u, 0u};
+    __device__ void load4x2(const uint16_t* p0, const uint16_t* p1) {
+        const u32x2_t a = *reinterpret_cast<const u32x2_t*>(p0);
+        const u32x2_t b = *reinterpret_cast<const u32x2_t*>(p1);
+        w = u32x4_t{a.x, a.y, b.x, b.y};
+    }
+    __device__ void load8(const uint16_t* p) { w = ld16(p); }
+    __device__ double get(int e) const {
+        const uint32_t u = w[e >> 1];
+        return (double)((e & 1) ? bf16_hi(u) : bf16_lo(u));
+    }
+};
+template <> struct Raw<float> {
+    f32x4_t lo = {0.f, 0.f, 0.f, 0.f}, hi = {0.f, 0.f, 0.f, 0.f};
+    __device__ void load4x2(const float* p0, const float* p1) {
+        lo = *reinterpret_cast<const f32x4_t*>(p0);
+        hi = *reinterpret_cast<const f32x4_t*>(p1);
+    }
+    __device__ void load8(const float* p) {
+        lo = *reinterpret_cast<const f32x4_t*>(p);
+        hi = *reinterpret_cast<const f32x4_t*>(p + 4);
+    }
+    __device__ double get(int e) const { return (double)(e < 4 ? lo[e] : hi[e - 4]); }
+};
+
+__device__ __forceinline__ void store_vals(uint16_t* p, const double* v, int n) {
+    // n = 4 (8 bytes) or 8 (16 bytes), each value rounded once to bf16
+    uint32_t u[4];
+#pragma unroll
+    for (int j = 0; j < 4; ++j)
+        u[j] = j < n / 2 ? (uint32_t)f64_to_bf16_bits(v[2 * j]) | ((uint32_t)f64_to_bf16_bits(v[2 * j + 1]) << 16) : 0u;
+    if (n == 8) st16(p, u32x4_t{u[0], u[1], u[2], u[3]});
+    else *reinterpret_cast<u32x2_t*>(p) = u32x2_t{u[0], u[1]};
+}
+__device__ __forceinline__ void store_vals(float* p, const double* v, int n) {
+    *reinterpret_cast<f32x4_t*>(p) = f32x4_t{(float)v[0], (float)v[1], (float)v[2], (float)v[3]};
+    if (n == 8) *reinterpret_cast<f32x4_t*>(p + 4) = f32x4_t{(float)v[4], (float)v[5], (float)v[6], (float)v[7]};
+}
+
+template <int W>
+__device__ __forceinline__ double group_sum(double v) {
+#pragma unroll
+    for (int o = W / 2; o > 0; o >>= 1) v += __shfl_xor(v, o);
+    return v;
+}
+
+constexpr int kTokThreads = 256;
+constexpr int kTokPasses = 4;       // head passes whose loads are issued up front
+
+template <typename T, bool KV, int HD>
+__global__ __launch_bounds__(kTokThreads) void rope_token_kernel(RopeArgs a) {
+    constexpr int TPH = HD / 8;                // lanes per head row
+    constexpr int HPP = kTokThreads / TPH;     // head rows per pass
+    __shared__ double cs_cos[HD / 2];
+    __shared__ double cs_sin[HD / 2];
+
+    const int b = blockIdx.z;
+    const int i = blockIdx.x;
+    const int seq0 = a.cu_seq[b];
+    const int len = a.cu_seq[b + 1] - seq0;
+    if (i >= len) return;
+    const int t = seq0 + i;
+    const int pos = a.start[b] + i;
+    if (t < 0 || t >= a.n_tok || pos < 0) return;
+    if (KV && pos >= a.cap) return;
+
+    const int rd = a.rotary_dim;
+    const int half = rd / 2;
+    const int np = rd / 8;                     // pair lanes per row
+    const int tid = threadIdx.x;
+    const int c = tid % TPH;
+    const bool pair = c < np;
+    // first dim of this lane's 8 (pair: 4 + 4 at d0 and d0 + half)
+    const int d0 = pair ? 4 * c : rd + 8 * (c - np);
+    const T* src = reinterpret_cast<const T*>(a.x) + (size_t)t * a.n_heads * HD;
+    const double rs = (double)a.rope_scale;
+
+    for (int h0 = 0; h0 < a.n_heads; h0 += kTokPasses * HPP) {
+        Raw<T> raw[kTokPasses];
+#pragma unroll
+        for (int ps = 0; ps < kTokPasses; ++ps) {
+            const int h = h0 + ps * HPP + tid / TPH;
+            if (h < a.n_heads) {
+                const T* row = src + (size_t)h * HD;
+                if (pair) raw[ps].load4x2(row + d0, row + d0 + half);
+                else raw[ps].load8(row + d0);
+            }
+        }
+        if (h0 == 0) {
+            for (int k = tid; k < half; k += kTokThreads) {
+                // position * f_k is exact in double (integer times a float)
+                const double th = (double)pos * (double)a.inv_freq[k];
+                double sn, cn;
+                sincos(th, &sn, &cn);
+                cs_cos[k] = cn;
+                cs_sin[k] = sn;
+            }
+            __syncthreads();
+        }
+#pragma unroll
+        for (int ps = 0; ps < kTokPasses; ++ps) {
+            const int h = h0 + ps * HPP + tid / TPH;
+            // rows of one head are whole groups of TPH lanes, so a row is
+            // either entirely valid or entirely past n_heads
+            double v[8];
+#pragma unroll
+            for (int e = 0; e < 8; ++e) v[e] = raw[ps].get(e);
+            if (a.norm != 0) {
+                double ss = 0.0;
+#pragma unroll
+                for (int e = 0; e < 8; ++e) ss += v[e] * v[e];
+                ss = group_sum<TPH>(ss);
+                const double r = 1.0 / sqrt(ss / (double)HD + a.eps);
+                if (h < a.n_heads) {
+#pragma unroll
+                    for (int e = 0; e < 8; ++e) {
+                        const int d = pair ? d0 + (e & 3) + (e >> 2) * half : d0 + e;
+                        const double w = (double)a.norm_w[d];
+                        v[e] = v[e] * r * (a.norm == 2 ? 1.0 + w : w);
+                    }
+                }
+            }
+            if (h >= a.n_heads) continue;
+            T* dst;
+            if (KV) dst = reinterpret_cast<T*>(a.y) + (((size_t)b * a.n_heads + h) * a.cap + pos) * HD;
+            else dst = reinterpret_cast<T*>(a.y) + ((size_t)t * a.n_heads + h) * HD;
+            if (pair) {
+                double y[8];
+#pragma unroll
+                for (int e = 0; e < 4; ++e) {
+                    const double cn = cs_cos[d0 + e], sn = cs_sin[d0 + e];
+                    y[e] = (v[e] * cn - v[e + 4] * sn) * rs;
+                    y[e + 4] = (v[e] * sn + v[e + 4] * cn) * rs;
+                }
+                store_vals(dst + d0, y, 4);
+                store_vals(dst + d0 + half, y + 4, 4);
+            } else {
+                store_vals(dst + d0, v, 8);
+            }
+            if (KV) {
+                // the matching V row, copied unchanged
+                const T* vs = reinterpret_cast<const T*>(a.v_src) + ((size_t)t * a.n_heads + h) * HD;
+                T* vd = reinterpret_cast<T*>(a.v_dst) + (((size_t)b * a.n_heads + h) * a.cap + pos) * HD;
+                constexpr int PER = 16 / sizeof(T);          // elements per 16 bytes
+                for (int e = c * PER; e < HD; e += TPH * PER) st16(vd + e, ld16(vs + e));
+            }
+        }
+    }
+}
+
+template <typename T, bool KV>
+static void launch_rope_typed(const RopeArgs& a, hipStream_t stream) {
+    const bool fast = a.rotary_dim % 8 == 0 && (a.head_dim == 64 || a.head_dim == 128);
+    if (fast) {
+        const dim3 grid(a.max_chunk, 1, a.n_seq);
+        if (a.head_dim == 128) rope_token_kernel<T, KV, 128><<<grid, dim3(kTokThreads), 0, stream>>>(a);
+        else rope_token_kernel<T, KV, 64><<<grid, dim3(kTokThreads), 0, stream>>>(a);
     } else {
-        if (kv) rope_rows_kernel<uint16_t, true><<<grid, block, 0, stream>>>(a);
-        else rope_rows_kernel<uint16_t, false><<<grid, block, 0, stream>>>(a);
+        const dim3 grid(a.max_chunk, (a.n_heads + kRopeWaves - 1) / kRopeWaves, a.n_seq);
+        rope_rows_kernel<T, KV><<<grid, dim3(kRopeThreads), 0, stream>>>(a);
+    }
+}
+
+hipError_t launch_rope_rows(const RopeArgs& a, int dtype, bool kv, hipStream_t stream) {
+    if (dtype == 0) {
+        if (kv) launch_rope_typed<float, true>(a, stream);
+        else launch_rope_typed<float, false>(a, stream);
+    } else {
+        if (kv) launch_rope_typed<uint16_t, true>(a, stream);
+        else launch_rope_typed<uint16_t, false>(a, stream);
     }
     return hipGetLastError();
 }
