@@ -38,17 +38,42 @@ __device__ __forceinline__ uint32_t pack_bf16x2(float a, float b) {
 // first narrowed to float with round-to-odd (truncate, then set the last bit
 // when inexact); float keeps more than bfloat16's 8 significant bits plus two,
 // so the second, ties-to-even narrowing then rounds exactly as a direct one.
+// Written with selects only (no divergent branches).
 __device__ __forceinline__ uint16_t f64_to_bf16_bits(double x) {
-    float f = (float)x;                       // ties to even
-    double back = (double)f;
-    uint32_t u = __float_as_uint(f);
-    if (back != x && !__builtin_isnan(x)) {
-        if (__builtin_fabs(back) > __builtin_fabs(x)) u -= 1;   // step toward zero
-        u |= 1u;                                                  // sticky bit
-    }
-    if ((u & 0x7fffffffu) > 0x7f800000u) return (uint16_t)((u >> 16) | 0x40u);  // quiet NaN
-    u += 0x7fffu + ((u >> 16) & 1u);
-    return (uint16_t)(u >> 16);
+    const float f = (float)x;                 // ties to even
+    const double back = (double)f;
+    const uint32_t uf = __float_as_uint(f);
+    const bool inexact = back != x;           // also true for NaN
+    const bool above = __builtin_fabs(back) > __builtin_fabs(x);
+    uint32_t u = (inexact && above) ? uf - 1u : uf;   // step toward zero
+    u = inexact ? (u | 1u) : u;                        // sticky bit
+    const uint32_t rounded = (u + 0x7fffu + ((u >> 16) & 1u)) >> 16;
+    const uint32_t qnan = (uf >> 16) | 0x40u;
+    return (uint16_t)(__builtin_isnan(x) ? qnan : rounded);
+}
+
+// Out of line so the compiler keeps it off the common path below.
+__device__ __attribute__((noinline)) uint16_t f64_to_bf16_bits_rare(double x) { return f64_to_bf16_bits(x); }
+
+// The same rounding done on the double's bit pattern, for results in
+// bfloat16's normal range (|x| in [2^-126, 2^128), after rounding up to
+// infinity): round to nearest even on the 45 dropped mantissa bits, then
+// rebias the exponent.  Anything else (tiny, infinite, NaN) takes the
+// float path above.  Integer instructions only, on the common path.
+__device__ __forceinline__ uint16_t f64_to_bf16_bits_fast(double x) {
+    const uint64_t u = __builtin_bit_cast(uint64_t, x);
+    const uint32_t lo = (uint32_t)u, hi = (uint32_t)(u >> 32);
+    const uint32_t e = (hi >> 20) & 0x7ffu;
+    // dropped bits: hi[12:0] and lo; half = hi bit 12, kept lsb = hi bit 13
+    const bool half = (hi & 0x1000u) != 0;
+    const bool rest = ((hi & 0xfffu) | lo) != 0;
+    const bool lsb = (hi & 0x2000u) != 0;
+    const uint32_t rhi = (hi & ~0x1fffu) + ((half && (rest || lsb)) ? 0x2000u : 0u);
+    const uint32_t sign = (hi >> 16) & 0x8000u;
+    const uint32_t em = (rhi >> 13) & 0x3ffffu;          // exponent (11) : mantissa (7)
+    uint32_t b = em > (1150u << 7 | 0x7fu) ? 0x7f80u : em - (896u << 7);
+    if (__builtin_expect(e < 897u || e == 0x7ffu, 0)) return f64_to_bf16_bits_rare(x);
+    return (uint16_t)(sign | b);
 }
 
 template <typename T> struct Elem;

@@ -152,7 +152,9 @@ __device__ __forceinline__ void store_vals(uint16_t* p, const double* v, int n) 
     uint32_t u[4];
 #pragma unroll
     for (int j = 0; j < 4; ++j)
-        u[j] = j < n / 2 ? (uint32_t)f64_to_bf16_bits(v[2 * j]) | ((uint32_t)f64_to_bf16_bits(v[2 * j + 1]) << 16) : 0u;
+        u[j] = j < n / 2 ? (uint32_t)f64_to_bf16_bits_fast(v[2 * j]) |
+                               ((uint32_t)f64_to_bf16_bits_fast(v[2 * j + 1]) << 16)
+                         : 0u;
     if (n == 8) st16(p, u32x4_t{u[0], u[1], u[2], u[3]});
     else *reinterpret_cast<u32x2_t*>(p) = u32x2_t{u[0], u[1]};
 }
@@ -161,10 +163,24 @@ __device__ __forceinline__ void store_vals(float* p, const double* v, int n) {
     if (n == 8) *reinterpret_cast<f32x4_t*>(p + 4) = f32x4_t{(float)v[4], (float)v[5], (float)v[6], (float)v[7]};
 }
 
+// Sum over aligned groups of W (8 or 16) consecutive lanes, every lane of a
+// group ending with its total: DPP pair, quad, half-row-mirror and row-mirror
+// exchanges of the two 32-bit halves (no LDS round trips).
+template <int CTRL>
+__device__ __forceinline__ double dpp_f64(double v) {
+    const int2 u = __builtin_bit_cast(int2, v);
+    int2 r;
+    r.x = __builtin_amdgcn_update_dpp(u.x, u.x, CTRL, 0xF, 0xF, false);
+    r.y = __builtin_amdgcn_update_dpp(u.y, u.y, CTRL, 0xF, 0xF, false);
+    return __builtin_bit_cast(double, r);
+}
 template <int W>
 __device__ __forceinline__ double group_sum(double v) {
-#pragma unroll
-    for (int o = W / 2; o > 0; o >>= 1) v += __shfl_xor(v, o);
+    static_assert(W == 8 || W == 16, "row groups of 8 or 16 lanes");
+    v += dpp_f64<0xB1>(v);    // quad_perm 1,0,3,2
+    v += dpp_f64<0x4E>(v);    // quad_perm 2,3,0,1
+    v += dpp_f64<0x141>(v);   // row_half_mirror
+    if (W == 16) v += dpp_f64<0x140>(v);   // row_mirror
     return v;
 }
 
@@ -198,6 +214,18 @@ __global__ __launch_bounds__(kTokThreads) void rope_token_kernel(RopeArgs a) {
     const int d0 = pair ? 4 * c : rd + 8 * (c - np);
     const T* src = reinterpret_cast<const T*>(a.x) + (size_t)t * a.n_heads * HD;
     const double rs = (double)a.rope_scale;
+    const bool scaled = a.rope_scale != 1.f;
+    // this lane's 8 norm weights (the same dims for every head), as the
+    // factor w or 1 + w
+    double wn[8];
+    if (a.norm != 0) {
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+            const int d = pair ? d0 + (e & 3) + (e >> 2) * half : d0 + e;
+            const double w = (double)a.norm_w[d];
+            wn[e] = a.norm == 2 ? 1.0 + w : w;
+        }
+    }
 
     for (int h0 = 0; h0 < a.n_heads; h0 += kTokPasses * HPP) {
         Raw<T> raw[kTokPasses];
@@ -235,14 +263,8 @@ __global__ __launch_bounds__(kTokThreads) void rope_token_kernel(RopeArgs a) {
                 for (int e = 0; e < 8; ++e) ss += v[e] * v[e];
                 ss = group_sum<TPH>(ss);
                 const double r = 1.0 / sqrt(ss / (double)HD + a.eps);
-                if (h < a.n_heads) {
 #pragma unroll
-                    for (int e = 0; e < 8; ++e) {
-                        const int d = pair ? d0 + (e & 3) + (e >> 2) * half : d0 + e;
-                        const double w = (double)a.norm_w[d];
-                        v[e] = v[e] * r * (a.norm == 2 ? 1.0 + w : w);
-                    }
-                }
+                for (int e = 0; e < 8; ++e) v[e] = v[e] * r * wn[e];
             }
             if (h >= a.n_heads) continue;
             T* dst;
@@ -253,8 +275,12 @@ __global__ __launch_bounds__(kTokThreads) void rope_token_kernel(RopeArgs a) {
 #pragma unroll
                 for (int e = 0; e < 4; ++e) {
                     const double cn = cs_cos[d0 + e], sn = cs_sin[d0 + e];
-                    y[e] = (v[e] * cn - v[e + 4] * sn) * rs;
-                    y[e + 4] = (v[e] * sn + v[e + 4] * cn) * rs;
+                    y[e] = v[e] * cn - v[e + 4] * sn;
+                    y[e + 4] = v[e] * sn + v[e + 4] * cn;
+                }
+                if (scaled) {
+#pragma unroll
+                    for (int e = 0; e < 8; ++e) y[e] *= rs;
                 }
                 store_vals(dst + d0, y, 4);
                 store_vals(dst + d0 + half, y + 4, 4);
