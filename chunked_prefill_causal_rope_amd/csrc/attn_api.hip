@@ -231,13 +231,15 @@ int attn_prefill_chunk(const void* q, const void* k_cache, const void* v_cache, 
                                                       workspace ? workspace_bytes : 0);
     a.rows_per_tile = plan.rows_per_tile;
     a.n_qtiles = plan.n_qtiles;
-    a.n_splits = plan.n_splits;
-    a.part = plan.n_splits > 1 ? (float*)workspace : nullptr;
-    const int splits = plan.n_splits;
-    const long blocks = (long)n_seq * a.n_qtiles * a.n_splits * n_kv;
+    a.split = plan.split;
+    a.grid = plan.grid;
+    a.slots = plan.slots;
+    a.table = plan.split ? (int*)workspace : nullptr;
+    a.part = plan.split ? (float*)((char*)workspace + plan.table_bytes) : nullptr;
+    const long blocks = (long)n_seq * a.n_qtiles * n_kv;
     if (blocks > 0x7fffffffL) return ATTN_EINVAL;
     hipError_t e = attn::launch_prefill_bf16(a, s);
-    if (e == hipSuccess && splits > 1) e = attn::launch_prefill_combine(a, s);
+    if (e == hipSuccess && plan.split) e = attn::launch_prefill_combine(a, s);
     return status_of(e);
 }
 

@@ -49,7 +49,9 @@ __device__ __forceinline__ uint16_t f64_to_bf16_bits(double x) {
     u = inexact ? (u | 1u) : u;                        // sticky bit
     const uint32_t rounded = (u + 0x7fffu + ((u >> 16) & 1u)) >> 16;
     const uint32_t qnan = (uf >> 16) | 0x40u;
-    return (uint16_t)(__builtin_isnan(x) ? qnan : rounded);
+    const uint64_t ux = __builtin_bit_cast(uint64_t, x);
+    const bool nan = (ux & 0x7fffffffffffffffull) > 0x7ff0000000000000ull;
+    return (uint16_t)(nan ? qnan : rounded);
 }
 
 // Out of line so the compiler keeps it off the common path below.

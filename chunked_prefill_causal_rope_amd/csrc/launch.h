@@ -30,18 +30,21 @@ struct PrefillArgs {
     const void* k_cache;
     const void* v_cache;
     float* out;
-    float* part;           // split partials [n_tok*n_heads][n_splits][head_dim+4] or null
+    float* part;           // split calls: partials [item][rows_per_tile][head_dim+4]
+    int* table;            // split calls: per (sequence, row tile) first item, part count
     const int32_t* cu_seq;
     const int32_t* start;
     float scale;
     int n_seq, n_heads, n_kv, group, head_dim, cap, n_tok, max_chunk, max_end;
-    int rows_per_tile, n_qtiles, n_splits;
+    // rows per workgroup, row tiles per sequence, split call (persistent
+    // grid with device-chosen key-range parts, merged by the combine kernel)
+    int rows_per_tile, n_qtiles, split, grid, slots;
 };
 // Launch plan of the bf16 prefill, from host scalars only: query rows per
-// workgroup (128 or 256), row tiles, key-range parts, workspace they need.
+// workgroup (128 or 256), row tiles, whether to split, grid, workspace.
 struct PrefillPlan {
-    int rows_per_tile, n_qtiles, n_splits;
-    size_t ws_bytes;
+    int rows_per_tile, n_qtiles, split, grid, slots;
+    size_t ws_bytes, table_bytes;
 };
 PrefillPlan plan_prefill(int n_seq, int n_heads, int n_kv, int head_dim, int n_tok, int max_chunk,
                          int max_end, size_t ws_available);

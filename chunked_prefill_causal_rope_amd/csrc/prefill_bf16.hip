@@ -99,6 +99,91 @@ __device__ __forceinline__ float sum_bf16_pairs(const uint32_t* pk) {
         }                                                            \
     } while (0)
 
+// ---------------------------------------------------------------- schedule
+// A work item is (sequence b, row tile qt, KV group g, part) and covers one
+// part of the row tile's key tiles; workgroup i takes item i.  Without
+// splitting there is one part per row tile.  With splitting (few row tiles)
+// every workgroup derives the same schedule from cu_seq/start: a row tile of
+// n key tiles gets ceil(n / T) parts of equal length, T being the smallest
+// length (at least kMinTilesPerSplit) that keeps the item count within one
+// workgroup per CU slot, so the longest sequence is spread over the CUs
+// instead of deciding the call's duration alone.  The grid has room for the
+// largest item count the schedule can produce; the workgroups past the
+// actual count exit.
+#ifndef ATTN_PREFILL_MIN_TILES_PER_SPLIT
+#define ATTN_PREFILL_MIN_TILES_PER_SPLIT 4
+#endif
+constexpr int kMinTilesPerSplit = ATTN_PREFILL_MIN_TILES_PER_SPLIT;
+
+// key tiles of row tile qt of sequence b (0 if the row tile is empty)
+__device__ __forceinline__ int group_tiles(const PrefillArgs& a, int b, int qt) {
+    const int t0 = a.cu_seq[b];
+    const int len = min(a.cu_seq[b + 1] - t0, a.max_chunk);
+    const int p0 = a.start[b];
+    const int rows_b = len * a.group;
+    const int r0 = qt * a.rows_per_tile;
+    if (len <= 0 || p0 < 0 || r0 >= rows_b) return 0;
+    const int r_last = min(r0 + a.rows_per_tile, rows_b) - 1;
+    const int n_keys = min(p0 + r_last / a.group + 1, a.cap);
+    return (n_keys + kTK - 1) / kTK;
+}
+
+struct PrefillItem {
+    int b, qt, g, part, nsp;
+};
+
+// Schedule of a split call, computed by every wave alike: lane l holds row
+// tile group l = (b, qt) (at most 64 groups).  The part length T minimises
+// the estimated duration ceil(items / slots) * (T + 2) (2 tiles for an
+// item's start-up) over T = ceil(longest / k); then item -> group by a
+// prefix sum over the groups' item counts.  Lane 0 of workgroup 0 also
+// writes, per group, its first item and part count for the combine kernel.
+__device__ PrefillItem split_schedule(const PrefillArgs& a, int item) {
+    const int lane = threadIdx.x & 63;
+    const int n_groups = a.n_seq * a.n_qtiles;
+    const int gt = lane < n_groups ? group_tiles(a, lane / a.n_qtiles, lane % a.n_qtiles) : 0;
+    const int gmax = max(wave_max(gt), 1);
+    const long slots = a.slots;
+    int best_T = gmax;
+    long best_cost = -1;
+    int prev_T = 0;
+    constexpr int kCand[12] = {1, 2, 3, 4, 6, 8, 12, 16, 24, 32, 48, 64};
+    for (int ci = 0; ci < 12; ++ci) {
+        const int k = kCand[ci];
+        const int T = (gmax + k - 1) / k;
+        if (T < kMinTilesPerSplit && k > 1) break;
+        if (T == prev_T) continue;
+        prev_T = T;
+        const int n = wave_sum(gt > 0 ? (gt + T - 1) / T : 0) * a.n_kv;
+        if (n > a.grid) continue;             // one workgroup per item
+        const long cost = (long)((n + slots - 1) / slots) * (T + 2);
+        if (best_cost < 0 || cost < best_cost) {
+            best_cost = cost;
+            best_T = T;
+        }
+    }
+    const int T = best_T;
+    const int nsp = gt > 0 ? (gt + T - 1) / T : 0;
+    const int cnt = nsp * a.n_kv;
+    // exclusive prefix sum of the groups' item counts
+    int incl = cnt;
+#pragma unroll
+    for (int o = 1; o < 64; o <<= 1) {
+        const int v = __shfl_up(incl, o);
+        if (lane >= o) incl += v;
+    }
+    const int excl = incl - cnt;
+    if (blockIdx.x == 0 && threadIdx.x < 64 && lane < n_groups) {
+        a.table[2 * lane] = excl;
+        a.table[2 * lane + 1] = nsp;
+    }
+    const unsigned long long hit = __ballot(cnt > 0 && item >= excl && item < incl);
+    if (hit == 0ull) return PrefillItem{0, 0, 0, 0, 0};
+    const int src = __builtin_ctzll(hit);
+    const int local = item - __shfl(excl, src);
+    return PrefillItem{src / a.n_qtiles, src % a.n_qtiles, local % a.n_kv, local / a.n_kv, __shfl(nsp, src)};
+}
+
 // NW waves of 32 query rows each share every K/V tile.  With 8 waves each
 // thread stages half a tile's worth of K and V, which leaves room for two
 // staging sets: the global loads of a tile are then issued two tiles before
@@ -123,14 +208,20 @@ __global__ __launch_bounds__(NW * 64, 8 / NW) void prefill_bf16_kernel(PrefillAr
     const int hf = lane >> 5;                     // wave half
     const int rl = lane & 31;
 
-    int id = blockIdx.x;
-    const int g = id % a.n_kv;
-    id /= a.n_kv;
-    const int s = id % a.n_splits;
-    id /= a.n_splits;
-    const int qt = a.n_qtiles - 1 - (id % a.n_qtiles);   // long rows first
-    const int b = id / a.n_qtiles;
-    if (b >= a.n_seq) return;
+    const int item = blockIdx.x;
+    PrefillItem itm;
+    if (a.split) {
+        itm = split_schedule(a, item);
+    } else {
+        // KV group fastest, long row tiles first
+        itm.g = item % a.n_kv;
+        itm.qt = a.n_qtiles - 1 - (item / a.n_kv) % a.n_qtiles;
+        itm.b = item / (a.n_kv * a.n_qtiles);
+        itm.part = 0;
+        itm.nsp = 1;
+    }
+    if (itm.nsp <= 0) return;
+    const int b = itm.b, qt = itm.qt, g = itm.g, s = itm.part, nsp = itm.nsp;
 
     const int G = a.group;
     const int t0 = a.cu_seq[b];
@@ -143,7 +234,8 @@ __global__ __launch_bounds__(NW * 64, 8 / NW) void prefill_bf16_kernel(PrefillAr
     const int r_last = min(r_tile0 + TILE_ROWS, rows_b) - 1;
     const int n_keys = min(p0 + r_last / G + 1, a.cap);
     const int n_tiles = (n_keys + kTK - 1) / kTK;
-    const int per = (n_tiles + a.n_splits - 1) / a.n_splits;
+    // this item's part of the row tile's key tiles, parts of equal length
+    const int per = (n_tiles + nsp - 1) / nsp;
     const int tb = s * per;
     const int te = min(tb + per, n_tiles);
 
@@ -389,7 +481,7 @@ __global__ __launch_bounds__(NW * 64, 8 / NW) void prefill_bf16_kernel(PrefillAr
 
     const float l_tot = l_run + __shfl_xor(l_run, 32);
     if (!row_ok) return;
-    if (a.n_splits == 1) {
+    if (nsp <= 1) {
         const float inv = 1.f / l_tot;
         float* orow = a.out + ((size_t)t * a.n_heads + h) * HD;
 #pragma unroll
@@ -401,7 +493,8 @@ __global__ __launch_bounds__(NW * 64, 8 / NW) void prefill_bf16_kernel(PrefillAr
                 *reinterpret_cast<float4*>(orow + db * 32 + 8 * q4 + 4 * hf) = v;
             }
     } else {
-        float* pr = a.part + (((size_t)t * a.n_heads + h) * a.n_splits + s) * (HD + kPartPad);
+        // partial of this item's row r - r_tile0
+        float* pr = a.part + ((size_t)item * TILE_ROWS + (r - r_tile0)) * (HD + kPartPad);
         if (hf == 0) *reinterpret_cast<float2*>(pr) = make_float2(m_run, l_tot);
 #pragma unroll
         for (int db = 0; db < NDB; ++db)
@@ -415,83 +508,113 @@ __global__ __launch_bounds__(NW * 64, 8 / NW) void prefill_bf16_kernel(PrefillAr
 }
 
 // Merge split partials (m, l, O) of each row: m* = max m_s,
-// l* = sum l_s 2^(m_s - m*), out = sum O_s 2^(m_s - m*) / l*.
+// l* = sum l_s 2^(m_s - m*), out = sum O_s 2^(m_s - m*) / l*.  One wave per
+// row: workgroup (x, sequence) takes 4 rows of the row tile x / (n_kv * R/4)
+// and KV group x % n_kv; row tiles that were not split were written by the
+// attention kernel.
 template <int HD>
 __global__ __launch_bounds__(256) void prefill_combine_kernel(PrefillArgs a) {
-    const int row = blockIdx.x * 4 + (threadIdx.x >> 6);
+    const int b = blockIdx.y;
+    const int R = a.rows_per_tile;
+    const int g = blockIdx.x % a.n_kv;
+    const int rblk = (blockIdx.x / a.n_kv) % (R / 4);
+    const int qt = blockIdx.x / a.n_kv / (R / 4);
+    if (b >= a.n_seq || qt >= a.n_qtiles) return;
+    const int first = a.table[2 * (b * a.n_qtiles + qt)];
+    const int S = a.table[2 * (b * a.n_qtiles + qt) + 1];
+    if (S <= 1) return;
+    const int G = a.group;
+    const int t0 = a.cu_seq[b];
+    const int len = min(a.cu_seq[b + 1] - t0, a.max_chunk);
+    const int rows_b = len * G;
     const int lane = threadIdx.x & 63;
-    if (row >= a.n_tok * a.n_heads) return;
-    const int S = a.n_splits;
-    const float* pr = a.part + (size_t)row * S * (HD + kPartPad);
-    float m = -INFINITY;
-    for (int s = 0; s < S; ++s) m = fmaxf(m, pr[(size_t)s * (HD + kPartPad)]);
-    const float m_use = m == -INFINITY ? 0.f : m;
-    float l = 0.f;
     constexpr int PER = HD / 64;
-    float o[PER];
+    constexpr int PS = HD + kPartPad;
+    {
+        const int rl = rblk * 4 + (threadIdx.x >> 6);
+        const int r = qt * R + rl;
+        if (r >= rows_b) return;
+        const int i = r / G;
+        const int h = g * G + (r - i * G);
+        const int t = t0 + i;
+        if (t < 0 || t >= a.n_tok) return;
+        // part p of this row tile and group is item first + p * n_kv + g
+        auto prow = [&](int p) { return a.part + ((size_t)(first + p * a.n_kv + g) * R + rl) * PS; };
+        float m = -INFINITY;
+        for (int p = 0; p < S; ++p) m = fmaxf(m, prow(p)[0]);
+        const float m_use = m == -INFINITY ? 0.f : m;
+        float l = 0.f;
+        float o[PER];
 #pragma unroll
-    for (int e = 0; e < PER; ++e) o[e] = 0.f;
-    for (int s = 0; s < S; ++s) {
-        const float* p = pr + (size_t)s * (HD + kPartPad);
-        const float w = __builtin_amdgcn_exp2f(p[0] - m_use);
-        l += p[1] * w;
+        for (int e = 0; e < PER; ++e) o[e] = 0.f;
+        for (int p = 0; p < S; ++p) {
+            const float* pp = prow(p);
+            const float w = __builtin_amdgcn_exp2f(pp[0] - m_use);
+            l += pp[1] * w;
 #pragma unroll
-        for (int e = 0; e < PER; ++e) o[e] += p[kPartPad + lane + 64 * e] * w;
+            for (int e = 0; e < PER; ++e) o[e] += pp[kPartPad + lane + 64 * e] * w;
+        }
+        const float inv = l > 0.f ? 1.f / l : 0.f;
+        float* orow = a.out + ((size_t)t * a.n_heads + h) * HD;
+#pragma unroll
+        for (int e = 0; e < PER; ++e) orow[lane + 64 * e] = o[e] * inv;
     }
-    const float inv = l > 0.f ? 1.f / l : 0.f;
-    float* orow = a.out + (size_t)row * HD;
-#pragma unroll
-    for (int e = 0; e < PER; ++e) orow[lane + 64 * e] = o[e] * inv;
 }
 
 
-// Split choice: 128-row tiles; when they are too few to keep about two
-// workgroups per CU busy, the key range is split, each part keeping at least
-// kMinTilesPerSplit key tiles.
-#ifndef ATTN_PREFILL_TARGET_BLOCKS
-#define ATTN_PREFILL_TARGET_BLOCKS 512
-#endif
-#ifndef ATTN_PREFILL_MIN_TILES_PER_SPLIT
-#define ATTN_PREFILL_MIN_TILES_PER_SPLIT 4
-#endif
+// Launch plan.  256-row workgroups (8 waves, deeper prefetch) when they
+// alone give every CU a workgroup; otherwise 128-row workgroups.  When the
+// row tiles are too few for the GPU (an upper bound from host scalars: every
+// sequence with max_chunk tokens) and the longest key range spans more than
+// kMinTilesPerSplit tiles, the call splits: a persistent grid of one
+// workgroup per CU slot, with the part length chosen on the device from the
+// actual lengths (see the schedule above).
 #ifndef ATTN_PREFILL_BIG_TILE_BLOCKS
-#define ATTN_PREFILL_BIG_TILE_BLOCKS 256
+#define ATTN_PREFILL_BIG_TILE_BLOCKS 512
 #endif
-constexpr int kTargetBlocks = ATTN_PREFILL_TARGET_BLOCKS;
-constexpr int kMinTilesPerSplit = ATTN_PREFILL_MIN_TILES_PER_SPLIT;
 constexpr int kBigTileBlocks = ATTN_PREFILL_BIG_TILE_BLOCKS;
-constexpr int kMaxSplits = 32;
+constexpr int kMaxSplitGroups = 64;      // (sequence, row tile) pairs: one per lane
+
+static int device_cus() {
+    int dev = 0, cus = 0;
+    if (hipGetDevice(&dev) != hipSuccess ||
+        hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cus <= 0)
+        cus = 256;
+    return cus;
+}
 
 PrefillPlan plan_prefill(int n_seq, int n_heads, int n_kv, int head_dim, int n_tok, int max_chunk,
                          int max_end, size_t ws_available) {
     const long group = n_heads / n_kv;
     const long rows = (long)max_chunk * group;
-    // 256-row workgroups (8 waves, deeper prefetch) when they alone give every
-    // CU a workgroup; otherwise 128-row workgroups, split along the keys
-    const long big = (long)n_seq * ((rows + 255) / 256) * n_kv;
-    if (big >= kBigTileBlocks) return PrefillPlan{256, (int)((rows + 255) / 256), 1, 0};
-    PrefillPlan p{128, (int)((rows + 127) / 128), 1, 0};
-    const long base = (long)n_seq * p.n_qtiles * n_kv;
     const long tiles = ((long)max_end + kTK - 1) / kTK;
-    long sp = base > 0 ? (kTargetBlocks + base - 1) / base : 1;
-    long by_len = tiles / kMinTilesPerSplit;
-    if (by_len < 1) by_len = 1;
-    if (sp > by_len) sp = by_len;
-    if (sp > kMaxSplits) sp = kMaxSplits;
-    if (sp < 1) sp = 1;
-    const size_t per = (size_t)n_tok * n_heads * (head_dim + kPartPad) * sizeof(float);
-    if (sp > 1 && per > 0) {
-        const size_t fit = ws_available / per;
-        if ((size_t)sp > fit) sp = (long)fit;
-        if (sp < 1) sp = 1;
+    const long big = (long)n_seq * ((rows + 255) / 256) * n_kv;
+    PrefillPlan p{};
+    p.rows_per_tile = big >= kBigTileBlocks / 2 ? 256 : 128;
+    p.n_qtiles = (int)((rows + p.rows_per_tile - 1) / p.rows_per_tile);
+    const long base = (long)n_seq * p.n_qtiles * n_kv;
+    p.split = 0;
+    p.grid = (int)base;
+    p.ws_bytes = 0;
+    p.table_bytes = 0;
+    if (base < kBigTileBlocks && tiles > kMinTilesPerSplit && (long)n_seq * p.n_qtiles <= kMaxSplitGroups) {
+        const long slots = (long)device_cus() * (p.rows_per_tile == 256 ? 1 : 2);
+        const size_t table = ((size_t)n_seq * p.n_qtiles * 2 * sizeof(int) + 255) / 256 * 256;
+        // items <= slots + one extra part per row tile (ceil) -- see split_schedule
+        const size_t parts = (size_t)(slots + base) * p.rows_per_tile * (head_dim + kPartPad) * sizeof(float);
+        if (table + parts <= ws_available) {
+            p.split = 1;
+            p.slots = (int)slots;
+            p.grid = (int)(slots + base);
+            p.table_bytes = table;
+            p.ws_bytes = table + parts;
+        }
     }
-    p.n_splits = (int)sp;
-    p.ws_bytes = sp > 1 ? per * (size_t)sp : 0;
     return p;
 }
 
 hipError_t launch_prefill_bf16(const PrefillArgs& a, hipStream_t stream) {
-    const long blocks = (long)a.n_seq * a.n_qtiles * a.n_splits * a.n_kv;
+    const long blocks = a.grid;
     if (blocks <= 0) return hipSuccess;
     const dim3 grid((unsigned)blocks);
     if (a.rows_per_tile == 256) {
@@ -505,13 +628,12 @@ hipError_t launch_prefill_bf16(const PrefillArgs& a, hipStream_t stream) {
 }
 
 hipError_t launch_prefill_combine(const PrefillArgs& a, hipStream_t stream) {
-    const long rows = (long)a.n_tok * a.n_heads;
-    const long blocks = (rows + 3) / 4;
-    if (blocks <= 0) return hipSuccess;
+    if (!a.split || a.n_seq <= 0) return hipSuccess;
+    const dim3 grid((unsigned)(a.n_qtiles * a.n_kv * (a.rows_per_tile / 4)), (unsigned)a.n_seq);
     if (a.head_dim == 128)
-        prefill_combine_kernel<128><<<dim3((unsigned)blocks), dim3(256), 0, stream>>>(a);
+        prefill_combine_kernel<128><<<grid, dim3(256), 0, stream>>>(a);
     else
-        prefill_combine_kernel<64><<<dim3((unsigned)blocks), dim3(256), 0, stream>>>(a);
+        prefill_combine_kernel<64><<<grid, dim3(256), 0, stream>>>(a);
     return hipGetLastError();
 }
 
