@@ -48,6 +48,8 @@ def lib() -> ctypes.CDLL:
     L.attn_rope_apply.argtypes = [vp, vp, i, i, i, i, i, vp, vp, i, vp, i, f, i, vp, d, vp]
     L.attn_kv_append.argtypes = [vp, vp, i, i, i, i, i, vp, vp, i, vp, vp, i, i, vp, i, f, i, vp,
                                  d, vp]
+    L.attn_rope_qkv.argtypes = [vp, vp, i, vp, vp, vp, vp, i, i, i, i, i, i, vp, vp, i, i, vp, i, f,
+                                i, vp, vp, d, vp]
     L.attn_prefill_chunk.argtypes = [vp, vp, vp, i, i, i, i, i, i, i, vp, vp, i, i, f, vp, vp, sz,
                                      vp]
     L.attn_prefill_workspace_bytes.argtypes = [i, i, i, i, i, i, i]
@@ -59,7 +61,7 @@ def lib() -> ctypes.CDLL:
     L.attn_status_string.restype = ctypes.c_char_p
     L.attn_version.restype = ctypes.c_char_p
     for name in ("attn_rope_inv_freq", "attn_yarn_inv_freq", "attn_rope_apply", "attn_kv_append",
-                 "attn_prefill_chunk", "attn_decode"):
+                 "attn_rope_qkv", "attn_prefill_chunk", "attn_decode"):
         getattr(L, name).restype = i
     _lib = L
     return L
@@ -166,6 +168,29 @@ def kv_append(k_cache: torch.Tensor, v_cache: torch.Tensor, k_new: torch.Tensor,
         _dev(inv_freq, "inv_freq", torch.float32) if rotary_dim else None, rotary_dim,
         rope_scale, norm, _dev(norm_w, "norm_w", torch.float32), eps, _stream())
     _check("attn_kv_append", st)
+
+
+def rope_qkv(q: torch.Tensor, q_out: torch.Tensor, k_cache: torch.Tensor, v_cache: torch.Tensor,
+             k_new: torch.Tensor, v_new: torch.Tensor, batch: Batch, inv_freq: torch.Tensor,
+             rotary_dim: int, rope_scale: float = 1.0, norm: int = NORM_NONE,
+             q_norm_w: torch.Tensor | None = None, k_norm_w: torch.Tensor | None = None,
+             eps: float = 1e-6):
+    """rope_apply(q -> q_out) and kv_append(k_new, v_new) of one chunk in one call."""
+    n_tok, n_heads, hd = q.shape
+    assert q_out.shape == q.shape and q_out.dtype == q.dtype and n_tok >= batch.n_tok
+    n_seq_c, n_kv, cap, hd2 = k_cache.shape
+    assert hd2 == hd and v_cache.shape == k_cache.shape and n_seq_c >= batch.n_seq
+    assert k_new.shape == (n_tok, n_kv, hd) and v_new.shape == k_new.shape
+    assert k_new.dtype == k_cache.dtype == v_cache.dtype == v_new.dtype == q.dtype
+    st = lib().attn_rope_qkv(
+        _dev(q, "q"), _dev(q_out, "q_out"), n_heads, _dev(k_cache, "k_cache"),
+        _dev(v_cache, "v_cache"), _dev(k_new, "k_new"), _dev(v_new, "v_new"), n_kv, cap,
+        _dtype_code(q), n_tok, hd, batch.n_seq, _dev(batch.cu_seq, "cu_seq", torch.int32),
+        _dev(batch.start, "start", torch.int32), batch.max_chunk, batch.max_end,
+        _dev(inv_freq, "inv_freq", torch.float32) if rotary_dim else None, rotary_dim,
+        rope_scale, norm, _dev(q_norm_w, "q_norm_w", torch.float32),
+        _dev(k_norm_w, "k_norm_w", torch.float32), eps, _stream())
+    _check("attn_rope_qkv", st)
 
 
 def prefill_workspace_bytes(batch: Batch, n_heads: int, n_kv: int, head_dim: int) -> int:

@@ -165,6 +165,51 @@ int attn_kv_append(void* k_cache, void* v_cache, int dtype, int n_seq, int n_kv,
     return status_of(attn::launch_rope_rows(a, dtype, true, (hipStream_t)stream));
 }
 
+int attn_rope_qkv(const void* q, void* q_out, int n_heads, void* k_cache, void* v_cache,
+                  const void* k_new, const void* v_new, int n_kv, int cap, int dtype, int n_tok,
+                  int head_dim, int n_seq, const int32_t* cu_seq, const int32_t* start, int max_chunk,
+                  int max_end, const float* inv_freq, int rotary_dim, float rope_scale, int norm,
+                  const float* q_norm_w, const float* k_norm_w, double eps, void* stream) {
+    int st = check_rope(dtype, n_tok, n_heads, head_dim, n_seq, cu_seq, start, max_chunk, inv_freq,
+                        rotary_dim, norm, q_norm_w);
+    if (st != ATTN_OK) return st;
+    st = check_rope(dtype, n_tok, n_kv, head_dim, n_seq, cu_seq, start, max_chunk, inv_freq,
+                    rotary_dim, norm, k_norm_w);
+    if (st != ATTN_OK) return st;
+    if (cap <= 0 || max_end < 0) return ATTN_EINVAL;
+    if (max_end > cap) return ATTN_ECAPACITY;
+    if (n_seq == 0 || n_tok == 0 || max_chunk == 0) return ATTN_OK;
+    if (!q || !q_out || !k_cache || !v_cache || !k_new || !v_new) return ATTN_EINVAL;
+    attn::RopeArgs aq{};
+    aq.x = q;
+    aq.y = q_out;
+    aq.norm_w = q_norm_w;
+    aq.n_heads = n_heads;
+    aq.cap = 0;
+    attn::RopeArgs ak{};
+    ak.x = k_new;
+    ak.y = k_cache;
+    ak.v_src = v_new;
+    ak.v_dst = v_cache;
+    ak.norm_w = k_norm_w;
+    ak.n_heads = n_kv;
+    ak.cap = cap;
+    for (attn::RopeArgs* a : {&aq, &ak}) {
+        a->cu_seq = cu_seq;
+        a->start = start;
+        a->inv_freq = inv_freq;
+        a->eps = eps;
+        a->rope_scale = rope_scale;
+        a->n_tok = n_tok;
+        a->head_dim = head_dim;
+        a->n_seq = n_seq;
+        a->max_chunk = max_chunk;
+        a->rotary_dim = rotary_dim < head_dim ? rotary_dim : head_dim;
+        a->norm = norm;
+    }
+    return status_of(attn::launch_rope_qkv(aq, ak, dtype, (hipStream_t)stream));
+}
+
 size_t attn_prefill_workspace_bytes(int n_seq, int n_heads, int n_kv, int head_dim, int n_tok,
                                     int max_chunk, int max_end) {
     if (n_seq <= 0 || n_heads <= 0 || n_kv <= 0 || n_heads % n_kv || n_tok <= 0 || max_chunk <= 0 ||

@@ -23,6 +23,9 @@ struct RopeArgs {
     int n_tok, n_heads, head_dim, cap, n_seq, max_chunk, rotary_dim, norm;
 };
 hipError_t launch_rope_rows(const RopeArgs& a, int dtype, bool kv, hipStream_t stream);
+// Both finishes of a chunk (queries, then keys/values into the cache) in as
+// few launches as the layout allows.
+hipError_t launch_rope_qkv(const RopeArgs& q, const RopeArgs& kv, int dtype, hipStream_t stream);
 
 // Causal attention of packed chunk rows over the head-major cache.
 struct PrefillArgs {

@@ -187,8 +187,30 @@ __device__ __forceinline__ double group_sum(double v) {
 constexpr int kTokThreads = 256;
 constexpr int kTokPasses = 4;       // head passes whose loads are issued up front
 
-template <typename T, bool KV, int HD>
-__global__ __launch_bounds__(kTokThreads) void rope_token_kernel(RopeArgs a) {
+// One launch can finish a token's query heads (token-major, written to qy)
+// and its key heads (into the cache, values copied alongside): "virtual"
+// heads 0..nq-1 are the queries, nq..nq+nk-1 the keys.
+struct RopeTokArgs {
+    const void* qx;
+    void* qy;
+    const float* qw;
+    int nq;
+    const void* kx;
+    const void* vx;
+    void* kc;
+    void* vc;
+    const float* kw;
+    int nk;
+    const int32_t* cu_seq;
+    const int32_t* start;
+    const float* inv_freq;
+    double eps;
+    float rope_scale;
+    int n_tok, cap, rotary_dim, norm;
+};
+
+template <typename T, int HD>
+__global__ __launch_bounds__(kTokThreads) void rope_token_kernel(RopeTokArgs a) {
     constexpr int TPH = HD / 8;                // lanes per head row
     constexpr int HPP = kTokThreads / TPH;     // head rows per pass
     __shared__ double cs_cos[HD / 2];
@@ -202,7 +224,10 @@ __global__ __launch_bounds__(kTokThreads) void rope_token_kernel(RopeArgs a) {
     const int t = seq0 + i;
     const int pos = a.start[b] + i;
     if (t < 0 || t >= a.n_tok || pos < 0) return;
-    if (KV && pos >= a.cap) return;
+    const int nq = a.nq;
+    const int nk = pos < a.cap ? a.nk : 0;     // no cache row past the capacity
+    const int n_all = nq + nk;
+    if (n_all == 0) return;
 
     const int rd = a.rotary_dim;
     const int half = rd / 2;
@@ -212,28 +237,29 @@ __global__ __launch_bounds__(kTokThreads) void rope_token_kernel(RopeArgs a) {
     const bool pair = c < np;
     // first dim of this lane's 8 (pair: 4 + 4 at d0 and d0 + half)
     const int d0 = pair ? 4 * c : rd + 8 * (c - np);
-    const T* src = reinterpret_cast<const T*>(a.x) + (size_t)t * a.n_heads * HD;
+    const T* qsrc = reinterpret_cast<const T*>(a.qx) + (size_t)t * nq * HD;
+    const T* ksrc = reinterpret_cast<const T*>(a.kx) + (size_t)t * a.nk * HD;
     const double rs = (double)a.rope_scale;
     const bool scaled = a.rope_scale != 1.f;
-    // this lane's 8 norm weights (the same dims for every head), as the
-    // factor w or 1 + w
-    double wn[8];
+    // this lane's 8 norm weights for queries and for keys (the same dims for
+    // every head)
+    float wq[8], wk[8];
     if (a.norm != 0) {
 #pragma unroll
         for (int e = 0; e < 8; ++e) {
             const int d = pair ? d0 + (e & 3) + (e >> 2) * half : d0 + e;
-            const double w = (double)a.norm_w[d];
-            wn[e] = a.norm == 2 ? 1.0 + w : w;
+            wq[e] = nq > 0 ? a.qw[d] : 0.f;
+            wk[e] = nk > 0 ? a.kw[d] : 0.f;
         }
     }
 
-    for (int h0 = 0; h0 < a.n_heads; h0 += kTokPasses * HPP) {
+    for (int h0 = 0; h0 < n_all; h0 += kTokPasses * HPP) {
         Raw<T> raw[kTokPasses];
 #pragma unroll
         for (int ps = 0; ps < kTokPasses; ++ps) {
-            const int h = h0 + ps * HPP + tid / TPH;
-            if (h < a.n_heads) {
-                const T* row = src + (size_t)h * HD;
+            const int vh = h0 + ps * HPP + tid / TPH;
+            if (vh < n_all) {
+                const T* row = vh < nq ? qsrc + (size_t)vh * HD : ksrc + (size_t)(vh - nq) * HD;
                 if (pair) raw[ps].load4x2(row + d0, row + d0 + half);
                 else raw[ps].load8(row + d0);
             }
@@ -251,9 +277,10 @@ __global__ __launch_bounds__(kTokThreads) void rope_token_kernel(RopeArgs a) {
         }
 #pragma unroll
         for (int ps = 0; ps < kTokPasses; ++ps) {
-            const int h = h0 + ps * HPP + tid / TPH;
+            const int vh = h0 + ps * HPP + tid / TPH;
+            const bool is_q = vh < nq;
             // rows of one head are whole groups of TPH lanes, so a row is
-            // either entirely valid or entirely past n_heads
+            // either entirely valid or entirely past the last head
             double v[8];
 #pragma unroll
             for (int e = 0; e < 8; ++e) v[e] = raw[ps].get(e);
@@ -264,12 +291,15 @@ __global__ __launch_bounds__(kTokThreads) void rope_token_kernel(RopeArgs a) {
                 ss = group_sum<TPH>(ss);
                 const double r = 1.0 / sqrt(ss / (double)HD + a.eps);
 #pragma unroll
-                for (int e = 0; e < 8; ++e) v[e] = v[e] * r * wn[e];
+                for (int e = 0; e < 8; ++e) {
+                    const double w = (double)(is_q ? wq[e] : wk[e]);
+                    v[e] = v[e] * r * (a.norm == 2 ? 1.0 + w : w);
+                }
             }
-            if (h >= a.n_heads) continue;
-            T* dst;
-            if (KV) dst = reinterpret_cast<T*>(a.y) + (((size_t)b * a.n_heads + h) * a.cap + pos) * HD;
-            else dst = reinterpret_cast<T*>(a.y) + ((size_t)t * a.n_heads + h) * HD;
+            if (vh >= n_all) continue;
+            const int kh = vh - nq;
+            T* dst = is_q ? reinterpret_cast<T*>(a.qy) + ((size_t)t * nq + vh) * HD
+                          : reinterpret_cast<T*>(a.kc) + (((size_t)b * a.nk + kh) * a.cap + pos) * HD;
             if (pair) {
                 double y[8];
 #pragma unroll
@@ -287,10 +317,10 @@ __global__ __launch_bounds__(kTokThreads) void rope_token_kernel(RopeArgs a) {
             } else {
                 store_vals(dst + d0, v, 8);
             }
-            if (KV) {
+            if (!is_q) {
                 // the matching V row, copied unchanged
-                const T* vs = reinterpret_cast<const T*>(a.v_src) + ((size_t)t * a.n_heads + h) * HD;
-                T* vd = reinterpret_cast<T*>(a.v_dst) + (((size_t)b * a.n_heads + h) * a.cap + pos) * HD;
+                const T* vs = reinterpret_cast<const T*>(a.vx) + ((size_t)t * a.nk + kh) * HD;
+                T* vd = reinterpret_cast<T*>(a.vc) + (((size_t)b * a.nk + kh) * a.cap + pos) * HD;
                 constexpr int PER = 16 / sizeof(T);          // elements per 16 bytes
                 for (int e = c * PER; e < HD; e += TPH * PER) st16(vd + e, ld16(vs + e));
             }
@@ -298,13 +328,51 @@ __global__ __launch_bounds__(kTokThreads) void rope_token_kernel(RopeArgs a) {
     }
 }
 
+static bool token_path(const RopeArgs& a) {
+    return a.rotary_dim % 8 == 0 && (a.head_dim == 64 || a.head_dim == 128);
+}
+
+template <typename T>
+static void launch_token(const RopeTokArgs& t, int head_dim, int max_chunk, int n_seq, hipStream_t stream) {
+    const dim3 grid(max_chunk, 1, n_seq);
+    if (head_dim == 128) rope_token_kernel<T, 128><<<grid, dim3(kTokThreads), 0, stream>>>(t);
+    else rope_token_kernel<T, 64><<<grid, dim3(kTokThreads), 0, stream>>>(t);
+}
+
+static RopeTokArgs token_args(const RopeArgs* q, const RopeArgs* kv) {
+    const RopeArgs& r = q ? *q : *kv;
+    RopeTokArgs t{};
+    if (q) {
+        t.qx = q->x;
+        t.qy = q->y;
+        t.qw = q->norm_w;
+        t.nq = q->n_heads;
+    }
+    if (kv) {
+        t.kx = kv->x;
+        t.vx = kv->v_src;
+        t.kc = kv->y;
+        t.vc = kv->v_dst;
+        t.kw = kv->norm_w;
+        t.nk = kv->n_heads;
+        t.cap = kv->cap;
+    }
+    t.cu_seq = r.cu_seq;
+    t.start = r.start;
+    t.inv_freq = r.inv_freq;
+    t.eps = r.eps;
+    t.rope_scale = r.rope_scale;
+    t.n_tok = r.n_tok;
+    t.rotary_dim = r.rotary_dim;
+    t.norm = r.norm;
+    return t;
+}
+
 template <typename T, bool KV>
 static void launch_rope_typed(const RopeArgs& a, hipStream_t stream) {
-    const bool fast = a.rotary_dim % 8 == 0 && (a.head_dim == 64 || a.head_dim == 128);
-    if (fast) {
-        const dim3 grid(a.max_chunk, 1, a.n_seq);
-        if (a.head_dim == 128) rope_token_kernel<T, KV, 128><<<grid, dim3(kTokThreads), 0, stream>>>(a);
-        else rope_token_kernel<T, KV, 64><<<grid, dim3(kTokThreads), 0, stream>>>(a);
+    if (token_path(a)) {
+        launch_token<T>(token_args(KV ? nullptr : &a, KV ? &a : nullptr), a.head_dim, a.max_chunk, a.n_seq,
+                        stream);
     } else {
         const dim3 grid(a.max_chunk, (a.n_heads + kRopeWaves - 1) / kRopeWaves, a.n_seq);
         rope_rows_kernel<T, KV><<<grid, dim3(kRopeThreads), 0, stream>>>(a);
@@ -320,6 +388,20 @@ hipError_t launch_rope_rows(const RopeArgs& a, int dtype, bool kv, hipStream_t s
         else launch_rope_typed<uint16_t, false>(a, stream);
     }
     return hipGetLastError();
+}
+
+// Queries and keys/values of one chunk: one launch on the token path (both
+// share the position table), otherwise the two general launches.
+hipError_t launch_rope_qkv(const RopeArgs& q, const RopeArgs& kv, int dtype, hipStream_t stream) {
+    if (token_path(q)) {
+        const RopeTokArgs t = token_args(&q, &kv);
+        if (dtype == 0) launch_token<float>(t, q.head_dim, q.max_chunk, q.n_seq, stream);
+        else launch_token<uint16_t>(t, q.head_dim, q.max_chunk, q.n_seq, stream);
+        return hipGetLastError();
+    }
+    hipError_t e = launch_rope_rows(q, dtype, false, stream);
+    if (e == hipSuccess) e = launch_rope_rows(kv, dtype, true, stream);
+    return e;
 }
 
 }  // namespace attn

@@ -80,12 +80,19 @@ class ChunkedPrefill:
         ws = max(api.prefill_workspace_bytes(s["batch"], nh, nkv, hd) for s in self.steps)
         self.workspace = torch.empty(max(ws, 16) // 4 + 1, dtype=torch.float32, device=device)
 
-    def run_step(self, i: int, attend: bool = True):
+    def run_step(self, i: int, attend: bool = True, fused: bool = True):
+        """One chunk: finish Q and append K/V (one fused call, or the two
+        separate calls), then attend."""
         w, s = self.w, self.steps[i]
-        api.rope_apply(s["q"], s["q_rot"], s["batch"], self.inv_freq, w.rd, w.rope_scale,
-                       w.norm_style, self.q_norm_w, w.norm_eps)
-        api.kv_append(self.k_cache, self.v_cache, s["k"], s["v"], s["batch"], self.inv_freq, w.rd,
-                      w.rope_scale, w.norm_style, self.k_norm_w, w.norm_eps)
+        if fused:
+            api.rope_qkv(s["q"], s["q_rot"], self.k_cache, self.v_cache, s["k"], s["v"], s["batch"],
+                         self.inv_freq, w.rd, w.rope_scale, w.norm_style, self.q_norm_w,
+                         self.k_norm_w, w.norm_eps)
+        else:
+            api.rope_apply(s["q"], s["q_rot"], s["batch"], self.inv_freq, w.rd, w.rope_scale,
+                           w.norm_style, self.q_norm_w, w.norm_eps)
+            api.kv_append(self.k_cache, self.v_cache, s["k"], s["v"], s["batch"], self.inv_freq,
+                          w.rd, w.rope_scale, w.norm_style, self.k_norm_w, w.norm_eps)
         if attend:
             self.attend_step(i)
 
@@ -94,9 +101,9 @@ class ChunkedPrefill:
         api.prefill_chunk(s["q_rot"], self.k_cache, self.v_cache, s["batch"], self.w.scale,
                           s["out"], self.workspace)
 
-    def run_all(self):
+    def run_all(self, fused: bool = True):
         for i in range(len(self.steps)):
-            self.run_step(i)
+            self.run_step(i, fused=fused)
 
     def gather(self, key: str) -> torch.Tensor:
         """Per-token results of every step, back in the packed input order."""
@@ -144,10 +151,9 @@ class DecodeStep:
 
     def finish_and_append(self):
         w = self.w
-        api.rope_apply(self.q, self.q_rot, self.batch, self.inv_freq, w.rd, w.rope_scale,
-                       w.norm_style, self.q_norm_w, w.norm_eps)
-        api.kv_append(self.k_cache, self.v_cache, self.k, self.v, self.batch, self.inv_freq, w.rd,
-                      w.rope_scale, w.norm_style, self.k_norm_w, w.norm_eps)
+        api.rope_qkv(self.q, self.q_rot, self.k_cache, self.v_cache, self.k, self.v, self.batch,
+                     self.inv_freq, w.rd, w.rope_scale, w.norm_style, self.q_norm_w,
+                     self.k_norm_w, w.norm_eps)
 
     def attend(self):
         api.decode(self.q_rot, self.k_cache, self.v_cache, self.ctx, self.max_ctx, self.w.scale,

@@ -142,6 +142,25 @@ int attn_kv_append(void *k_cache, void *v_cache, int dtype, int n_seq, int n_kv,
                    const float *norm_w, double eps, void *stream);
 
 /*
+ * attn_rope_apply on the queries and attn_kv_append on the keys and values of
+ * the same chunk, in one call: the same results as the two calls (the
+ * queries' finish, then every K/V row of the chunk in the cache before any
+ * position attends), with one launch where the layout allows (rotary_dim a
+ * multiple of 8, head_dim 64 or 128) -- a token's cos/sin table then serves
+ * its query and key heads alike.  Arguments as in the two calls:
+ *   q, q_out  device [n_tok][n_heads][head_dim] (q_out == q is allowed)
+ *   k_cache, v_cache, k_new, v_new, n_kv, cap   as attn_kv_append
+ *   q_norm_w, k_norm_w   the two norm weights (NULL iff norm is NONE)
+ * Errors: the union of the two calls' errors.
+ */
+int attn_rope_qkv(const void *q, void *q_out, int n_heads, void *k_cache, void *v_cache,
+                  const void *k_new, const void *v_new, int n_kv, int cap, int dtype, int n_tok,
+                  int head_dim, int n_seq, const int32_t *cu_seq, const int32_t *start,
+                  int max_chunk, int max_end, const float *inv_freq, int rotary_dim,
+                  float rope_scale, int norm, const float *q_norm_w, const float *k_norm_w,
+                  double eps, void *stream);
+
+/*
  * Causal attention for the rows of a chunk whose keys and values are already
  * in the cache (call attn_kv_append first).  For row i of sequence b at
  * position p = start[b]+i and query head h, with g = h / (n_heads/n_kv):

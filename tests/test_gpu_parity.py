@@ -118,6 +118,44 @@ def test_kv_append_layout_and_sentinels(dtype):
     assert np.array_equal(gv[~written], before_v[~written])
 
 
+@pytest.mark.parametrize("dtype", [wl.F32, wl.BF16])
+@pytest.mark.parametrize("hd,rd,norm,scale,nh,nkv", [
+    (128, 128, wl.NORM_NONE, 1.0, 32, 8),        # one launch, 40 heads in 3 passes
+    (128, 64, wl.NORM_W, 1.0, 40, 8),            # partial rotary, qk-norm
+    (64, 64, wl.NORM_1PW, 1.1386294, 6, 2),
+    (128, 30, wl.NORM_W, 1.0, 6, 2),             # rotary_dim not a multiple of 8: two launches
+    (128, 128, wl.NORM_NONE, 1.0, 64, 8),        # 72 heads: more than one group of passes
+])
+def test_rope_qkv_equals_separate_calls(dtype, hd, rd, norm, scale, nh, nkv):
+    scale = float(np.float32(scale))
+    say(f"rope_qkv dtype={dtype} hd={hd} rd={rd} norm={norm} nh={nh} nkv={nkv}")
+    w = wl.Workload(name="qkv", dtype=dtype, n_heads=nh, n_kv=nkv, head_dim=hd, seed=13,
+                    rotary_dim=rd, norm_style=norm, rope_scale=scale, base=1e4,
+                    n_seq=3, len_range=(1, 40), chunk=40)
+    d = wl.gen_prefill(w)
+    cap = 200
+    starts = [0, 17, cap - d["lengths"][2]]
+    batch = api.Batch(starts, d["lengths"], device=DEV)
+    f = runner.tables(w, DEV)
+    qw = d["q_norm_w"].to(DEV) if norm else None
+    kw = d["k_norm_w"].to(DEV) if norm else None
+    q, k, v = d["q"].to(DEV), d["k"].to(DEV), d["v"].to(DEV)
+    outs = []
+    for fused in (False, True):
+        y = torch.full_like(q, float("nan"))
+        kc = torch.full((3, nkv, cap, hd), float("nan"), dtype=w.torch_dtype, device=DEV)
+        vc = torch.full_like(kc, float("nan"))
+        if fused:
+            api.rope_qkv(q, y, kc, vc, k, v, batch, f, rd, scale, norm, qw, kw, w.norm_eps)
+        else:
+            api.rope_apply(q, y, batch, f, rd, scale, norm, qw, w.norm_eps)
+            api.kv_append(kc, vc, k, v, batch, f, rd, scale, norm, kw, w.norm_eps)
+        torch.cuda.synchronize()
+        outs.append((_bits(y), _bits(kc), _bits(vc)))
+    for a, b in zip(*outs):
+        assert np.array_equal(a, b)
+
+
 # ------------------------------------------------------------------ f32 path
 
 def test_c0_f32_prefill_and_sequential_probs():
