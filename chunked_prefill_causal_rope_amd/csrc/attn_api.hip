@@ -279,6 +279,7 @@ int attn_prefill_chunk(const void* q, const void* k_cache, const void* v_cache, 
     a.split = plan.split;
     a.grid = plan.grid;
     a.slots = plan.slots;
+    a.part_tiles = plan.part_tiles;
     a.table = plan.split ? (int*)workspace : nullptr;
     a.part = plan.split ? (float*)((char*)workspace + plan.table_bytes) : nullptr;
     const long blocks = (long)n_seq * a.n_qtiles * n_kv;

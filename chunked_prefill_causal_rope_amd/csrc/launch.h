@@ -42,11 +42,12 @@ struct PrefillArgs {
     // rows per workgroup, row tiles per sequence, split call (persistent
     // grid with device-chosen key-range parts, merged by the combine kernel)
     int rows_per_tile, n_qtiles, split, grid, slots;
+    int part_tiles;        // split calls: part length chosen on the host (0: on the device)
 };
 // Launch plan of the bf16 prefill, from host scalars only: query rows per
 // workgroup (128 or 256), row tiles, whether to split, grid, workspace.
 struct PrefillPlan {
-    int rows_per_tile, n_qtiles, split, grid, slots;
+    int rows_per_tile, n_qtiles, split, grid, slots, part_tiles;
     size_t ws_bytes, table_bytes;
 };
 PrefillPlan plan_prefill(int n_seq, int n_heads, int n_kv, int head_dim, int n_tok, int max_chunk,

@@ -135,14 +135,27 @@ struct PrefillItem {
 // Schedule of a split call, computed by every wave alike: lane l holds row
 // tile group l = (b, qt) (at most 64 groups).  The part length T minimises
 // the estimated duration ceil(items / slots) * (T + 2) (2 tiles for an
-// item's start-up) over T = ceil(longest / k); then item -> group by a
-// prefix sum over the groups' item counts.  Lane 0 of workgroup 0 also
+// item's start-up) over T = ceil(longest / k) -- on the host when the call
+// has one sequence, whose sizes it knows; then item -> group by a prefix
+// sum over the groups' item counts.  Lane 0 of workgroup 0 also
 // writes, per group, its first item and part count for the combine kernel.
-__device__ PrefillItem split_schedule(const PrefillArgs& a, int item) {
-    const int lane = threadIdx.x & 63;
-    const int n_groups = a.n_seq * a.n_qtiles;
-    const int gt = lane < n_groups ? group_tiles(a, lane / a.n_qtiles, lane % a.n_qtiles) : 0;
-    const int gmax = max(wave_max(gt), 1);
+// Wave-wide sum and max of an int: DPP within each 16-lane row, then the
+// four row results (no LDS round trips).
+template <bool MAX>
+__device__ __forceinline__ int wave_reduce_dpp(int x) {
+    auto op = [](int u, int v) { return MAX ? max(u, v) : u + v; };
+    x = op(x, __builtin_amdgcn_update_dpp(x, x, 0xB1, 0xF, 0xF, false));    // quad_perm 1,0,3,2
+    x = op(x, __builtin_amdgcn_update_dpp(x, x, 0x4E, 0xF, 0xF, false));    // quad_perm 2,3,0,1
+    x = op(x, __builtin_amdgcn_update_dpp(x, x, 0x141, 0xF, 0xF, false));   // row_half_mirror
+    x = op(x, __builtin_amdgcn_update_dpp(x, x, 0x140, 0xF, 0xF, false));   // row_mirror
+    return op(op(__builtin_amdgcn_readlane(x, 0), __builtin_amdgcn_readlane(x, 16)),
+              op(__builtin_amdgcn_readlane(x, 32), __builtin_amdgcn_readlane(x, 48)));
+}
+
+// Part length for the groups' key tiles gt (one per lane): minimise the
+// estimated duration ceil(items / slots) * (T + 2) over T = ceil(longest / k).
+__device__ __forceinline__ int split_part_length(const PrefillArgs& a, int gt) {
+    const int gmax = max(wave_reduce_dpp<true>(gt), 1);
     const long slots = a.slots;
     int best_T = gmax;
     long best_cost = -1;
@@ -154,7 +167,7 @@ __device__ PrefillItem split_schedule(const PrefillArgs& a, int item) {
         if (T < kMinTilesPerSplit && k > 1) break;
         if (T == prev_T) continue;
         prev_T = T;
-        const int n = wave_sum(gt > 0 ? (gt + T - 1) / T : 0) * a.n_kv;
+        const int n = wave_reduce_dpp<false>(gt > 0 ? (gt + T - 1) / T : 0) * a.n_kv;
         if (n > a.grid) continue;             // one workgroup per item
         const long cost = (long)((n + slots - 1) / slots) * (T + 2);
         if (best_cost < 0 || cost < best_cost) {
@@ -162,7 +175,19 @@ __device__ PrefillItem split_schedule(const PrefillArgs& a, int item) {
             best_T = T;
         }
     }
-    const int T = best_T;
+    return best_T;
+}
+
+__device__ PrefillItem split_schedule(const PrefillArgs& a, int item) {
+    const int lane = threadIdx.x & 63;
+    const int n_groups = a.n_seq * a.n_qtiles;
+    const int gt = lane < n_groups ? group_tiles(a, lane / a.n_qtiles, lane % a.n_qtiles) : 0;
+    // a single sequence's lengths are host scalars: its part length comes
+    // with the launch (checked against the grid, in case the arrays and the
+    // host scalars disagree)
+    int T = a.part_tiles;
+    if (T <= 0 || wave_reduce_dpp<false>(gt > 0 ? (gt + T - 1) / T : 0) * a.n_kv > a.grid)
+        T = split_part_length(a, gt);
     const int nsp = gt > 0 ? (gt + T - 1) / T : 0;
     const int cnt = nsp * a.n_kv;
     // exclusive prefix sum of the groups' item counts
@@ -538,21 +563,51 @@ __global__ __launch_bounds__(256) void prefill_combine_kernel(PrefillArgs a) {
         const int h = g * G + (r - i * G);
         const int t = t0 + i;
         if (t < 0 || t >= a.n_tok) return;
-        // part p of this row tile and group is item first + p * n_kv + g
+        // part p of this row tile and group is item first + p * n_kv + g;
+        // lane p < S holds part p's (m, l), then its weight 2^(m_p - m)
         auto prow = [&](int p) { return a.part + ((size_t)(first + p * a.n_kv + g) * R + rl) * PS; };
-        float m = -INFINITY;
-        for (int p = 0; p < S; ++p) m = fmaxf(m, prow(p)[0]);
+        float mp = -INFINITY, lp = 0.f;
+        for (int p = lane; p < S; p += 64) {
+            const float2 ml = *reinterpret_cast<const float2*>(prow(p));
+            if (p < 64) { mp = ml.x; lp = ml.y; }
+            else { mp = fmaxf(mp, ml.x); }
+        }
+        const float m = wave_max(mp);
         const float m_use = m == -INFINITY ? 0.f : m;
-        float l = 0.f;
         float o[PER];
 #pragma unroll
         for (int e = 0; e < PER; ++e) o[e] = 0.f;
-        for (int p = 0; p < S; ++p) {
-            const float* pp = prow(p);
-            const float w = __builtin_amdgcn_exp2f(pp[0] - m_use);
-            l += pp[1] * w;
+        float l = 0.f;
+        if (S <= 64) {
+            const float wl = lane < S ? __builtin_amdgcn_exp2f(mp - m_use) : 0.f;
+            l = wave_sum(lp * wl);
+            int p = 0;
+            for (; p + 4 <= S; p += 4) {
+                float x[4][PER], w[4];
 #pragma unroll
-            for (int e = 0; e < PER; ++e) o[e] += pp[kPartPad + lane + 64 * e] * w;
+                for (int u = 0; u < 4; ++u) {
+                    w[u] = __shfl(wl, p + u);
+#pragma unroll
+                    for (int e = 0; e < PER; ++e) x[u][e] = prow(p + u)[kPartPad + lane + 64 * e];
+                }
+#pragma unroll
+                for (int u = 0; u < 4; ++u)
+#pragma unroll
+                    for (int e = 0; e < PER; ++e) o[e] += x[u][e] * w[u];
+            }
+            for (; p < S; ++p) {
+                const float w = __shfl(wl, p);
+#pragma unroll
+                for (int e = 0; e < PER; ++e) o[e] += prow(p)[kPartPad + lane + 64 * e] * w;
+            }
+        } else {
+            for (int p = 0; p < S; ++p) {
+                const float* pp = prow(p);
+                const float w = __builtin_amdgcn_exp2f(pp[0] - m_use);
+                l += pp[1] * w;
+#pragma unroll
+                for (int e = 0; e < PER; ++e) o[e] += pp[kPartPad + lane + 64 * e] * w;
+            }
         }
         const float inv = l > 0.f ? 1.f / l : 0.f;
         float* orow = a.out + ((size_t)t * a.n_heads + h) * HD;
@@ -608,6 +663,43 @@ PrefillPlan plan_prefill(int n_seq, int n_heads, int n_kv, int head_dim, int n_t
             p.grid = (int)(slots + base);
             p.table_bytes = table;
             p.ws_bytes = table + parts;
+            p.part_tiles = 0;
+            if (n_seq == 1) {
+                // the same choice the device would make, from exact sizes:
+                // len = n_tok rows starting at max_end - len
+                const long len = n_tok < max_chunk ? n_tok : max_chunk;
+                const long p0 = max_end - len;
+                long gt[kMaxSplitGroups];
+                long gmax = 1;
+                for (int qt = 0; qt < p.n_qtiles; ++qt) {
+                    const long r0 = (long)qt * p.rows_per_tile, rows_b = len * group;
+                    gt[qt] = 0;
+                    if (len > 0 && p0 >= 0 && r0 < rows_b) {
+                        const long r_last = (r0 + p.rows_per_tile < rows_b ? r0 + p.rows_per_tile : rows_b) - 1;
+                        const long nk = p0 + r_last / group + 1;
+                        gt[qt] = (nk + kTK - 1) / kTK;
+                    }
+                    if (gt[qt] > gmax) gmax = gt[qt];
+                }
+                long best_T = gmax, best_cost = -1, prev_T = 0;
+                const int cand[12] = {1, 2, 3, 4, 6, 8, 12, 16, 24, 32, 48, 64};
+                for (int k : cand) {
+                    const long T = (gmax + k - 1) / k;
+                    if (T < kMinTilesPerSplit && k > 1) break;
+                    if (T == prev_T) continue;
+                    prev_T = T;
+                    long n = 0;
+                    for (int qt = 0; qt < p.n_qtiles; ++qt) n += gt[qt] > 0 ? (gt[qt] + T - 1) / T : 0;
+                    n *= n_kv;
+                    if (n > p.grid) continue;
+                    const long cost = (n + slots - 1) / slots * (T + 2);
+                    if (best_cost < 0 || cost < best_cost) {
+                        best_cost = cost;
+                        best_T = T;
+                    }
+                }
+                p.part_tiles = (int)best_T;
+            }
         }
     }
     return p;
