@@ -54,28 +54,30 @@ __device__ __forceinline__ uint16_t f64_to_bf16_bits(double x) {
     return (uint16_t)(nan ? qnan : rounded);
 }
 
-// Out of line so the compiler keeps it off the common path below.
-__device__ __attribute__((noinline)) uint16_t f64_to_bf16_bits_rare(double x) { return f64_to_bf16_bits(x); }
-
-// The same rounding done on the double's bit pattern, for results in
-// bfloat16's normal range (|x| in [2^-126, 2^128), after rounding up to
-// infinity): round to nearest even on the 45 dropped mantissa bits, then
-// rebias the exponent.  Anything else (tiny, infinite, NaN) takes the
-// float path above.  Integer instructions only, on the common path.
-__device__ __forceinline__ uint16_t f64_to_bf16_bits_fast(double x) {
-    const uint64_t u = __builtin_bit_cast(uint64_t, x);
-    const uint32_t lo = (uint32_t)u, hi = (uint32_t)(u >> 32);
-    const uint32_t e = (hi >> 20) & 0x7ffu;
-    // dropped bits: hi[12:0] and lo; half = hi bit 12, kept lsb = hi bit 13
-    const bool half = (hi & 0x1000u) != 0;
-    const bool rest = ((hi & 0xfffu) | lo) != 0;
-    const bool lsb = (hi & 0x2000u) != 0;
-    const uint32_t rhi = (hi & ~0x1fffu) + ((half && (rest || lsb)) ? 0x2000u : 0u);
-    const uint32_t sign = (hi >> 16) & 0x8000u;
-    const uint32_t em = (rhi >> 13) & 0x3ffffu;          // exponent (11) : mantissa (7)
-    uint32_t b = em > (1150u << 7 | 0x7fu) ? 0x7f80u : em - (896u << 7);
-    if (__builtin_expect(e < 897u || e == 0x7ffu, 0)) return f64_to_bf16_bits_rare(x);
-    return (uint16_t)(sign | b);
+// n doubles (n even) to n/2 words of two bfloat16 (low half = even index),
+// each value rounded once, ties to even.  Common path: the hardware's
+// double->float and float->bfloat16 conversions, both ties to even.
+// Rounding twice can only differ from rounding once when the first result
+// lies exactly halfway between two bfloat16 neighbours (low 16 bits 0x8000);
+// if any value of the group does, in any active lane, the group is redone
+// with the exact conversion above (the test is a wave ballot, so the branch
+// is uniform and the common path carries no per-lane flags).
+template <int N>
+__device__ __forceinline__ void f64_to_bf16_packed(const double* v, uint32_t* u) {
+    float f[N];
+    uint64_t mid = 0;
+#pragma unroll
+    for (int j = 0; j < N; ++j) {
+        f[j] = (float)v[j];
+        mid |= __builtin_amdgcn_ballot_w64((__float_as_uint(f[j]) & 0xffffu) == 0x8000u);
+    }
+#pragma unroll
+    for (int j = 0; j < N / 2; ++j) u[j] = pack_bf16x2(f[2 * j], f[2 * j + 1]);
+    if (__builtin_expect(mid != 0, 0)) {
+#pragma unroll
+        for (int j = 0; j < N / 2; ++j)
+            u[j] = (uint32_t)f64_to_bf16_bits(v[2 * j]) | ((uint32_t)f64_to_bf16_bits(v[2 * j + 1]) << 16);
+    }
 }
 
 template <typename T> struct Elem;

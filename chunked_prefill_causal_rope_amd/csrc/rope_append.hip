@@ -23,6 +23,45 @@ constexpr int kRopeThreads = 256;
 constexpr int kRopeWaves = kRopeThreads / 64;
 constexpr int kMaxHd = 128;
 
+// sin and cos of theta = position x inverse frequency (finite, |theta| below
+// 2^40).  Cody-Waite reduction: k = theta * 2/pi rounded to an integer, and
+// r = theta - k pi/2 with pi/2 split into three doubles, each step one fused
+// multiply-add (absolute error of r near 2^-53).  On |r| <= pi/4 (plus
+// rounding) the Taylor series of sin to degree 17 and of cos to degree 18
+// truncate below 1e-19 relative; k mod 4 selects the quadrant's swap and
+// signs.  Short, branch-free and light on registers.
+constexpr double inv_factorial(int n) {
+    double f = 1.0;
+    for (int i = 2; i <= n; ++i) f *= (double)i;    // exact up to 18!
+    return 1.0 / f;
+}
+__device__ __forceinline__ void sincos_pos(double th, double* sn, double* cs) {
+    constexpr double kTwoOverPi = 0.6366197723675814;
+    constexpr double kPio2a = 1.5707963267948966;         // pi/2 rounded to double
+    constexpr double kPio2b = 6.123233995736766e-17;      // pi/2 - kPio2a, rounded
+    constexpr double kPio2c = -1.4973849048591698e-33;    // pi/2 - kPio2a - kPio2b, rounded
+    const double k = __builtin_rint(th * kTwoOverPi);
+    double r = __builtin_fma(-k, kPio2a, th);
+    r = __builtin_fma(-k, kPio2b, r);
+    r = __builtin_fma(-k, kPio2c, r);
+    const double z = r * r;
+    // sin r = r + r z (-1/3! + z/5! - ... + z^7/17!)
+    double ps = inv_factorial(17);
+#pragma unroll
+    for (int j = 7; j >= 1; --j) ps = __builtin_fma(ps, z, (j & 1 ? -1.0 : 1.0) * inv_factorial(2 * j + 1));
+    const double s = __builtin_fma(r * z, ps, r);
+    // cos r = 1 + z (-1/2! + z/4! - ... - z^8/18!)
+    double pc = -inv_factorial(18);
+#pragma unroll
+    for (int j = 8; j >= 1; --j) pc = __builtin_fma(pc, z, (j & 1 ? -1.0 : 1.0) * inv_factorial(2 * j));
+    const double c = __builtin_fma(z, pc, 1.0);
+    const int n = (int)(k - 4.0 * __builtin_floor(k * 0.25));     // k mod 4, exact
+    const double s1 = (n & 1) ? c : s;
+    const double c1 = (n & 1) ? s : c;
+    *sn = (n & 2) ? -s1 : s1;
+    *cs = ((n + 1) & 2) ? -c1 : c1;
+}
+
 template <typename T, bool KV>
 __global__ __launch_bounds__(kRopeThreads) void rope_rows_kernel(RopeArgs a) {
     __shared__ double cs_cos[kMaxHd / 2];
@@ -47,7 +86,7 @@ __global__ __launch_bounds__(kRopeThreads) void rope_rows_kernel(RopeArgs a) {
         // position * f_k is exact in double (integer times a float)
         double th = (double)pos * (double)a.inv_freq[k];
         double sn, c;
-        sincos(th, &sn, &c);
+        sincos_pos(th, &sn, &c);
         cs_cos[k] = c;
         cs_sin[k] = sn;
     }
@@ -112,13 +151,15 @@ __global__ __launch_bounds__(kRopeThreads) void rope_rows_kernel(RopeArgs a) {
     }
 }
 
-// Fast path, for rotary_dim a multiple of 8: one workgroup per token and all
-// of its heads, so the token's cos/sin table (double) is built once.  A head
-// row is handled by HD/8 consecutive lanes, each owning 8 of its dims: a
-// "pair" lane owns dims 4c..4c+3 and their RoPE partners 4c+rd/2.., a "pass"
-// lane 8 dims past the rotary part.  Every lane issues its loads before the
-// table is built, the norm's sum of squares is a reduction over the lanes of
-// one row, and stores are 8 or 16 bytes wide.
+// Fast path, for rotary_dim a multiple of 8: one workgroup per (token, group
+// of heads) with one pass and no loop.  A head row is handled by HD/8
+// consecutive lanes, each owning 8 of its dims: a "pair" lane owns dims
+// 4c..4c+3 and their RoPE partners 4c+rd/2.., a "pass" lane 8 dims past the
+// rotary part.  Every lane issues its loads (and the matching V chunk for a
+// key row) first; meanwhile the workgroup builds the token's cos/sin table
+// (double) and the effective norm weights (w or 1 + w, double) in LDS.  The
+// norm's sum of squares is a DPP reduction over the lanes of one row, and
+// stores are 8 or 16 bytes wide.
 template <typename T> struct Raw;
 template <> struct Raw<uint16_t> {
     // 8 bf16 = 16 bytes
@@ -150,13 +191,13 @@ template <> struct Raw<float> {
 __device__ __forceinline__ void store_vals(uint16_t* p, const double* v, int n) {
     // n = 4 (8 bytes) or 8 (16 bytes), each value rounded once to bf16
     uint32_t u[4];
-#pragma unroll
-    for (int j = 0; j < 4; ++j)
-        u[j] = j < n / 2 ? (uint32_t)f64_to_bf16_bits_fast(v[2 * j]) |
-                               ((uint32_t)f64_to_bf16_bits_fast(v[2 * j + 1]) << 16)
-                         : 0u;
-    if (n == 8) st16(p, u32x4_t{u[0], u[1], u[2], u[3]});
-    else *reinterpret_cast<u32x2_t*>(p) = u32x2_t{u[0], u[1]};
+    if (n == 8) {
+        f64_to_bf16_packed<8>(v, u);
+        st16(p, u32x4_t{u[0], u[1], u[2], u[3]});
+    } else {
+        f64_to_bf16_packed<4>(v, u);
+        *reinterpret_cast<u32x2_t*>(p) = u32x2_t{u[0], u[1]};
+    }
 }
 __device__ __forceinline__ void store_vals(float* p, const double* v, int n) {
     *reinterpret_cast<f32x4_t*>(p) = f32x4_t{(float)v[0], (float)v[1], (float)v[2], (float)v[3]};
@@ -185,7 +226,6 @@ __device__ __forceinline__ double group_sum(double v) {
 }
 
 constexpr int kTokThreads = 256;
-constexpr int kTokPasses = 4;       // head passes whose loads are issued up front
 
 // One launch can finish a token's query heads (token-major, written to qy)
 // and its key heads (into the cache, values copied alongside): "virtual"
@@ -212,9 +252,12 @@ struct RopeTokArgs {
 template <typename T, int HD>
 __global__ __launch_bounds__(kTokThreads) void rope_token_kernel(RopeTokArgs a) {
     constexpr int TPH = HD / 8;                // lanes per head row
-    constexpr int HPP = kTokThreads / TPH;     // head rows per pass
+    constexpr int HPB = kTokThreads / TPH;     // head rows per workgroup
+    constexpr int VPER = 16 / sizeof(T);       // elements per 16-byte chunk
+    constexpr int VCH = 8 / VPER;              // 16-byte V chunks per lane
     __shared__ double cs_cos[HD / 2];
     __shared__ double cs_sin[HD / 2];
+    __shared__ double w_eff[2][HD];            // query weights, then key weights
 
     const int b = blockIdx.z;
     const int i = blockIdx.x;
@@ -227,7 +270,8 @@ __global__ __launch_bounds__(kTokThreads) void rope_token_kernel(RopeTokArgs a) 
     const int nq = a.nq;
     const int nk = pos < a.cap ? a.nk : 0;     // no cache row past the capacity
     const int n_all = nq + nk;
-    if (n_all == 0) return;
+    const int h_base = blockIdx.y * HPB;
+    if (h_base >= n_all) return;               // uniform over the workgroup
 
     const int rd = a.rotary_dim;
     const int half = rd / 2;
@@ -237,94 +281,89 @@ __global__ __launch_bounds__(kTokThreads) void rope_token_kernel(RopeTokArgs a) 
     const bool pair = c < np;
     // first dim of this lane's 8 (pair: 4 + 4 at d0 and d0 + half)
     const int d0 = pair ? 4 * c : rd + 8 * (c - np);
-    const T* qsrc = reinterpret_cast<const T*>(a.qx) + (size_t)t * nq * HD;
-    const T* ksrc = reinterpret_cast<const T*>(a.kx) + (size_t)t * a.nk * HD;
-    const double rs = (double)a.rope_scale;
-    const bool scaled = a.rope_scale != 1.f;
-    // this lane's 8 norm weights for queries and for keys (the same dims for
-    // every head)
-    float wq[8], wk[8];
-    if (a.norm != 0) {
+    const int vh = h_base + tid / TPH;
+    // rows of one head are whole groups of TPH lanes (whole DPP rows or half
+    // rows), so a row is entirely valid or entirely past the last head, and
+    // the norm's group sum reads only its own row
+    const bool valid = vh < n_all;
+    const bool is_q = vh < nq;
+    const int kh = vh - nq;
+
+    Raw<T> raw;
+    u32x4_t vbuf[VCH];
+    if (valid) {
+        const T* row = is_q ? reinterpret_cast<const T*>(a.qx) + ((size_t)t * nq + vh) * HD
+                            : reinterpret_cast<const T*>(a.kx) + ((size_t)t * a.nk + kh) * HD;
+        if (pair) raw.load4x2(row + d0, row + d0 + half);
+        else raw.load8(row + d0);
+        if (!is_q) {
+            // this lane's share of the matching V row, copied unchanged
+            const T* vs = reinterpret_cast<const T*>(a.vx) + ((size_t)t * a.nk + kh) * HD + c * 8;
 #pragma unroll
-        for (int e = 0; e < 8; ++e) {
-            const int d = pair ? d0 + (e & 3) + (e >> 2) * half : d0 + e;
-            wq[e] = nq > 0 ? a.qw[d] : 0.f;
-            wk[e] = nk > 0 ? a.kw[d] : 0.f;
+            for (int j = 0; j < VCH; ++j) vbuf[j] = ld16(vs + j * VPER);
         }
     }
 
-    for (int h0 = 0; h0 < n_all; h0 += kTokPasses * HPP) {
-        Raw<T> raw[kTokPasses];
-#pragma unroll
-        for (int ps = 0; ps < kTokPasses; ++ps) {
-            const int vh = h0 + ps * HPP + tid / TPH;
-            if (vh < n_all) {
-                const T* row = vh < nq ? qsrc + (size_t)vh * HD : ksrc + (size_t)(vh - nq) * HD;
-                if (pair) raw[ps].load4x2(row + d0, row + d0 + half);
-                else raw[ps].load8(row + d0);
-            }
+    for (int k = tid; k < half; k += kTokThreads) {
+        // position * f_k is exact in double (integer times a float)
+        const double th = (double)pos * (double)a.inv_freq[k];
+        double sn, cn;
+        sincos_pos(th, &sn, &cn);
+        cs_cos[k] = cn;
+        cs_sin[k] = sn;
+    }
+    if (a.norm != 0) {
+        for (int k = tid; k < 2 * HD; k += kTokThreads) {
+            const bool q_side = k < HD;
+            if (q_side ? nq == 0 : nk == 0) continue;
+            const double w = (double)(q_side ? a.qw[k] : a.kw[k - HD]);
+            w_eff[q_side ? 0 : 1][k % HD] = a.norm == 2 ? 1.0 + w : w;
         }
-        if (h0 == 0) {
-            for (int k = tid; k < half; k += kTokThreads) {
-                // position * f_k is exact in double (integer times a float)
-                const double th = (double)pos * (double)a.inv_freq[k];
-                double sn, cn;
-                sincos(th, &sn, &cn);
-                cs_cos[k] = cn;
-                cs_sin[k] = sn;
-            }
-            __syncthreads();
+    }
+    __syncthreads();
+    if (!valid) return;
+
+    double v[8];
+#pragma unroll
+    for (int e = 0; e < 8; ++e) v[e] = raw.get(e);
+    if (a.norm != 0) {
+        double ss = 0.0;
+#pragma unroll
+        for (int e = 0; e < 8; ++e) ss += v[e] * v[e];
+        ss = group_sum<TPH>(ss);
+        const double r = 1.0 / sqrt(ss / (double)HD + a.eps);
+        const double* we = w_eff[is_q ? 0 : 1];
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+            const int d = pair ? d0 + (e & 3) + (e >> 2) * half : d0 + e;
+            v[e] = v[e] * r * we[d];
         }
+    }
+    T* dst = is_q ? reinterpret_cast<T*>(a.qy) + ((size_t)t * nq + vh) * HD
+                  : reinterpret_cast<T*>(a.kc) + (((size_t)b * a.nk + kh) * a.cap + pos) * HD;
+    if (pair) {
+        const double rs = (double)a.rope_scale;
+        const bool scaled = a.rope_scale != 1.f;
+        double y[8];
 #pragma unroll
-        for (int ps = 0; ps < kTokPasses; ++ps) {
-            const int vh = h0 + ps * HPP + tid / TPH;
-            const bool is_q = vh < nq;
-            // rows of one head are whole groups of TPH lanes, so a row is
-            // either entirely valid or entirely past the last head
-            double v[8];
-#pragma unroll
-            for (int e = 0; e < 8; ++e) v[e] = raw[ps].get(e);
-            if (a.norm != 0) {
-                double ss = 0.0;
-#pragma unroll
-                for (int e = 0; e < 8; ++e) ss += v[e] * v[e];
-                ss = group_sum<TPH>(ss);
-                const double r = 1.0 / sqrt(ss / (double)HD + a.eps);
-#pragma unroll
-                for (int e = 0; e < 8; ++e) {
-                    const double w = (double)(is_q ? wq[e] : wk[e]);
-                    v[e] = v[e] * r * (a.norm == 2 ? 1.0 + w : w);
-                }
-            }
-            if (vh >= n_all) continue;
-            const int kh = vh - nq;
-            T* dst = is_q ? reinterpret_cast<T*>(a.qy) + ((size_t)t * nq + vh) * HD
-                          : reinterpret_cast<T*>(a.kc) + (((size_t)b * a.nk + kh) * a.cap + pos) * HD;
-            if (pair) {
-                double y[8];
-#pragma unroll
-                for (int e = 0; e < 4; ++e) {
-                    const double cn = cs_cos[d0 + e], sn = cs_sin[d0 + e];
-                    y[e] = v[e] * cn - v[e + 4] * sn;
-                    y[e + 4] = v[e] * sn + v[e + 4] * cn;
-                }
-                if (scaled) {
-#pragma unroll
-                    for (int e = 0; e < 8; ++e) y[e] *= rs;
-                }
-                store_vals(dst + d0, y, 4);
-                store_vals(dst + d0 + half, y + 4, 4);
-            } else {
-                store_vals(dst + d0, v, 8);
-            }
-            if (!is_q) {
-                // the matching V row, copied unchanged
-                const T* vs = reinterpret_cast<const T*>(a.vx) + ((size_t)t * a.nk + kh) * HD;
-                T* vd = reinterpret_cast<T*>(a.vc) + (((size_t)b * a.nk + kh) * a.cap + pos) * HD;
-                constexpr int PER = 16 / sizeof(T);          // elements per 16 bytes
-                for (int e = c * PER; e < HD; e += TPH * PER) st16(vd + e, ld16(vs + e));
-            }
+        for (int e = 0; e < 4; ++e) {
+            const double cn = cs_cos[d0 + e], sn = cs_sin[d0 + e];
+            y[e] = v[e] * cn - v[e + 4] * sn;
+            y[e + 4] = v[e] * sn + v[e + 4] * cn;
         }
+        if (scaled) {
+#pragma unroll
+            for (int e = 0; e < 8; ++e) y[e] *= rs;
+        }
+        store_vals(dst + d0, y, 4);
+        store_vals(dst + d0 + half, y + 4, 4);
+    } else {
+        store_vals(dst + d0, v, 8);
+    }
+    if (!is_q) {
+        T* vd = reinterpret_cast<T*>(a.vc) + (((size_t)b * a.nk + kh) * a.cap + pos) * HD + c * 8;
+#pragma unroll
+        for (int j = 0; j < VCH; ++j) st16(vd + j * VPER, vbuf[j]);
     }
 }
 
@@ -334,7 +373,8 @@ static bool token_path(const RopeArgs& a) {
 
 template <typename T>
 static void launch_token(const RopeTokArgs& t, int head_dim, int max_chunk, int n_seq, hipStream_t stream) {
-    const dim3 grid(max_chunk, 1, n_seq);
+    const int per_block = kTokThreads / (head_dim / 8);
+    const dim3 grid(max_chunk, (t.nq + t.nk + per_block - 1) / per_block, n_seq);
     if (head_dim == 128) rope_token_kernel<T, 128><<<grid, dim3(kTokThreads), 0, stream>>>(t);
     else rope_token_kernel<T, 64><<<grid, dim3(kTokThreads), 0, stream>>>(t);
 }

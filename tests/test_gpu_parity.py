@@ -45,16 +45,18 @@ def _to_dtype_bits(x: np.ndarray, dtype) -> np.ndarray:
     (64, 64, wl.NORM_1PW, 1.1386294),
     (128, 32, wl.NORM_NONE, 1.1386294),
 ])
-def test_rope_apply_matches_oracle(dtype, hd, rd, norm, scale):
+@pytest.mark.parametrize("starts", [(0, 17, 131000), (5, 2**30 - 20, 2**31 - 50)])
+def test_rope_apply_matches_oracle(dtype, hd, rd, norm, scale, starts):
     # rope_scale crosses the ABI as a float (the page's f32 field): the oracle
-    # gets that same float value
+    # gets that same float value.  The second set of starts reaches angles
+    # near 2^31 radians (the largest positions an int32 holds).
     scale = float(np.float32(scale))
-    say(f"rope_apply dtype={dtype} hd={hd} rd={rd} norm={norm} scale={scale}")
+    say(f"rope_apply dtype={dtype} hd={hd} rd={rd} norm={norm} scale={scale} starts={starts}")
     w = wl.Workload(name="rope", dtype=dtype, n_heads=6, n_kv=2, head_dim=hd, seed=11,
                     rotary_dim=rd, norm_style=norm, rope_scale=scale, base=1e4,
                     n_seq=3, len_range=(1, 40), chunk=40)
     d = wl.gen_prefill(w)
-    starts = [0, 17, 131000]
+    starts = list(starts)
     batch = api.Batch(starts, d["lengths"], device=DEV)
     x = d["q"].to(DEV)
     y = torch.full_like(x, float("nan"))
@@ -154,6 +156,66 @@ def test_rope_qkv_equals_separate_calls(dtype, hd, rd, norm, scale, nh, nkv):
         outs.append((_bits(y), _bits(kc), _bits(vc)))
     for a, b in zip(*outs):
         assert np.array_equal(a, b)
+
+
+def _midpoint_inputs(n_scales: int):
+    """Pairs (rope_scale, bf16 inputs x) for which x * rope_scale (exact in
+    double) rounds to a float lying exactly halfway between two bfloat16
+    neighbours, while the product itself is not that midpoint, and for which
+    rounding through float gives a different bfloat16 than rounding once (the
+    oracle's).  Found by search over float scales near 1.1386 and every
+    finite non-zero bfloat16, subnormals included."""
+    bits = np.arange(1 << 16, dtype=np.uint32)
+    bits = bits[((bits >> 7) & 0xFF) != 0xFF]                # drop inf / NaN
+    bits = bits[(bits & 0x7FFF) != 0]                        # drop zeros
+    x = (bits << 16).view(np.float32).astype(np.float64)
+    x = x[np.abs(x) < 2.0 ** 120]
+    found = []
+    s = np.float32(1.1386294)
+    while len(found) < n_scales:
+        s = np.nextafter(s, np.float32(2.0))
+        p = x * float(s)
+        f = p.astype(np.float32)
+        mid = ((f.view(np.uint32) & 0xFFFF) == 0x8000) & (f.astype(np.float64) != p)
+        if not mid.any():
+            continue
+        via_float = torch.from_numpy(f[mid]).to(torch.bfloat16).float().numpy().astype(np.float64)
+        once = oracle.round_store(p[mid], oracle.STORE_BF16)
+        sel = x[mid][via_float != once]
+        if sel.size:
+            found.append((float(s), sel))
+    return found
+
+
+@pytest.mark.parametrize("hd,rd", [(128, 128), (128, 64), (64, 64), (128, 36)])
+def test_bf16_single_rounding_at_float_midpoints(hd, rd):
+    """At position 0 the rotation is the identity, so every rotary output is
+    x * rope_scale.  Inputs are chosen so that this product's float image is a
+    bfloat16 midpoint: the stored bits must still be the oracle's single
+    rounding, for queries and for keys.  (rd = 36 takes the general path.)"""
+    cases = _midpoint_inputs(4)
+    for scale, xs in cases:
+        say(f"midpoints hd={hd} rd={rd} scale={scale!r} n={xs.size}")
+        n_seq, nh = 5, 3
+        rng = np.random.default_rng(5)
+        # every sequence is one token at position 0; the chosen values fill
+        # the rotary dims of every head, cycled, the rest random
+        vals = rng.standard_normal((n_seq, nh, hd))
+        vals[:, :, :rd] = np.resize(xs, n_seq * nh * rd).reshape(n_seq, nh, rd)
+        x = torch.from_numpy(vals).to(torch.bfloat16)
+        batch = api.Batch([0] * n_seq, [1] * n_seq, device=DEV)
+        f = torch.from_numpy(oracle.rope_inv_freq(rd, 1e4)).to(DEV)
+        ref = oracle.finish_heads(np64(x), np.zeros(n_seq, np.int64), oracle.rope_inv_freq(rd, 1e4),
+                                  rd, scale, store=oracle.STORE_BF16)
+        want = _to_dtype_bits(ref, torch.bfloat16)
+        y = torch.full_like(x, float("nan"), device=DEV)
+        api.rope_apply(x.to(DEV), y, batch, f, rd, scale, 0, None, 1e-6)
+        kc = torch.full((n_seq, nh, 1, hd), float("nan"), dtype=torch.bfloat16, device=DEV)
+        vc = torch.full_like(kc, float("nan"))
+        api.kv_append(kc, vc, x.to(DEV), x.to(DEV), batch, f, rd, scale, 0, None, 1e-6)
+        torch.cuda.synchronize()
+        assert np.array_equal(_bits(y), want)
+        assert np.array_equal(_bits(kc)[:, :, 0, :], want)
 
 
 # ------------------------------------------------------------------ f32 path
