@@ -25,16 +25,20 @@
 //  * The running maximum only moves (and O is rescaled) when a score exceeds
 //    it by more than 2^8; until then probabilities are referenced to the old
 //    maximum, which leaves the softmax unchanged.
-//  * Each part leaves (m, l, O) in the workspace and, when asked, its raw
-//    log2-domain scores in the probabilities buffer; the combine kernel merges
-//    the parts with log-sum-exp and turns the scores into probabilities.
+//  * Each part leaves (m, l, O) in the workspace and, when asked, its
+//    unnormalised probabilities 2^(x - m) (x the log2-domain score, m the
+//    part's running maximum) as half-precision values packed at the start of
+//    each probabilities row -- half the bytes of the float scores, which
+//    matters because writes among the K/V read stream cost far more than
+//    their size.  The combine kernel merges the parts with log-sum-exp and
+//    widens each row in place to the normalised float probabilities.
 #include "device_common.h"
 #include "launch.h"
 
 namespace attn {
 
 constexpr int kDecKB = 32;      // keys per step
-constexpr int kPartPadD = 4;    // (m, l, pad, pad) before O in a partial
+constexpr int kPartPadD = 4;    // (m, l, l_half, pad) before O in a partial
 constexpr int kDecMaxGroup = 16;
 constexpr float kDecSlack = 8.f;
 // LDS floats per wave that hold a part's raw scores (16 KB)
@@ -91,7 +95,65 @@ __device__ __forceinline__ u32x4_t ld16_nt(const uint16_t* p) {
 // in flight, which are the next step's prefetch).
 __device__ __forceinline__ void lds_order() { asm volatile("" ::: "memory"); }
 
-template <int HD, int HPL, bool PROBS>
+// A part's raw scores x, [head][key] in LDS (PK keys per head), written as
+// half-precision 2^(x - m_h), m_h the head's running maximum in mr, to keys
+// [base, base+n) of the heads' 16-bit rows (p <= 2^8: a score never exceeds
+// the maximum by more than the slack).  The sums of the rounded values are
+// added to lh, so the probabilities normalised by them sum to 1 exactly (up
+// to float rounding).
+typedef uint32_t u32x4_a4_t __attribute__((ext_vector_type(4), aligned(4)));
+template <int PK>
+__device__ __forceinline__ void write_half_scores(const float* sb, const float* mr, float* lh, uint16_t* hrow,
+                                                  size_t hrow_ld, int G, int base, int n, int lane) {
+    for (int t = lane; t < G * (PK / 8); t += 64) {
+        const int hh = t / (PK / 8), kq = 8 * (t % (PK / 8));
+        if (kq >= n) continue;
+        const float m = mr[hh];
+        uint32_t w[4];
+        float sum = 0.f;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+            w[e] = pack_f16x2(__builtin_amdgcn_exp2f(sb[hh * PK + kq + 2 * e] - m),
+                              __builtin_amdgcn_exp2f(sb[hh * PK + kq + 2 * e + 1] - m));
+            // buffer entries past n hold nothing of this part
+            if (kq + 2 * e < n) sum += f16_value((uint16_t)w[e]);
+            if (kq + 2 * e + 1 < n) sum += f16_value((uint16_t)(w[e] >> 16));
+        }
+        atomicAdd(&lh[hh], sum);
+        uint16_t* dst = hrow + hh * hrow_ld + base + kq;
+        if (kq + 7 < n) {
+            *reinterpret_cast<u32x4_a4_t*>(dst) = u32x4_a4_t{w[0], w[1], w[2], w[3]};
+        } else {
+#pragma unroll
+            for (int e = 0; e < 7; ++e)
+                if (kq + e < n) dst[e] = (uint16_t)(w[e >> 1] >> (16 * (e & 1)));
+        }
+    }
+}
+
+// After the running maximum moved, the values a part already wrote (keys
+// [k_lo, k_lo + n)) are multiplied by the heads' factors fac, so every
+// written value stays referenced to the current maximum.  Only parts longer
+// than the LDS buffer write any before their end, and the maximum rarely
+// moves after the first PK keys.
+__device__ __forceinline__ void rescale_half_scores(const float* fac, float* lh, uint16_t* hrow, size_t hrow_ld,
+                                                    int G, int k_lo, int n, int lane) {
+    __threadfence();            // this wave's own earlier writes first
+    if (lane < G) lh[lane] *= fac[lane];
+    const int per = (n + 7) / 8;
+    for (int t = lane; t < G * per; t += 64) {
+        const int hh = t / per, kq = 8 * (t % per);
+        const float f = fac[hh];
+        uint16_t* dst = hrow + hh * hrow_ld + k_lo + kq;
+        for (int e = 0; e < 8 && kq + e < n; ++e) dst[e] = f16_bits(f16_value(dst[e]) * f);
+    }
+    __threadfence();
+}
+
+// LONG: parts may be longer than the raw-score buffer (a small workspace);
+// only that instance carries the mid-part writes and their rescale, which
+// would otherwise add to the streaming loop's registers.
+template <int HD, int HPL, bool PROBS, bool LONG>
 __global__ __launch_bounds__(64) void decode_split_kernel(DecodeArgs a) {
     constexpr int GQ = 4 * HPL;                 // query heads per group handled
     constexpr int NK = HD / 32;                 // K-steps per 16x16x32 product
@@ -100,6 +162,8 @@ __global__ __launch_bounds__(64) void decode_split_kernel(DecodeArgs a) {
     constexpr int NV = kDecKB / RPI;            // V loads per lane per step
     __shared__ __attribute__((aligned(16))) float pbuf[kDecKB * GQ];   // P[key][head]
     __shared__ __attribute__((aligned(16))) float abuf[GQ];
+    __shared__ float mref[GQ];                  // running maximum per head, for flushes
+    __shared__ float lhalf[GQ];                 // sums of the written half-precision values
     // the part's raw scores, [head][key], written out once the part is done
     __shared__ __attribute__((aligned(16))) float sbuf[PROBS ? kDecPartFloats : 4];
     constexpr int PK = kDecPartFloats / GQ;     // longest part with probabilities
@@ -116,6 +180,7 @@ __global__ __launch_bounds__(64) void decode_split_kernel(DecodeArgs a) {
     const int k_hi = min(k_lo + a.split_len, ctx);
     if (k_lo >= k_hi) return;
     const int G = a.group;
+    if (PROBS && lane < GQ) lhalf[lane] = 0.f;
 
     const int col = lane & 15;   // score layout: key within a 16-key block
     const int grp = lane >> 4;   // score layout: heads grp*HPL .. grp*HPL+HPL-1
@@ -139,7 +204,12 @@ __global__ __launch_bounds__(64) void decode_split_kernel(DecodeArgs a) {
     const size_t base = ((size_t)b * a.n_kv + g) * (size_t)a.cap * HD;
     const uint16_t* kc = reinterpret_cast<const uint16_t*>(a.k_cache) + base;
     const uint16_t* vcache = reinterpret_cast<const uint16_t*>(a.v_cache) + base;
-    float* prow = PROBS ? a.probs + ((size_t)b * a.n_heads + g * G) * a.probs_ld : nullptr;
+    // half-precision values of head hh, key k: element k of the row read as
+    // 16-bit words (bytes 2k..2k+1 of the float row, inside its first ctx
+    // entries)
+    uint16_t* hrow = PROBS ? reinterpret_cast<uint16_t*>(a.probs + ((size_t)b * a.n_heads + g * G) * a.probs_ld)
+                           : nullptr;
+    const size_t hrow_ld = 2 * (size_t)a.probs_ld;   // 16-bit words per row
 
     float m_run[HPL], l_run[HPL];
 #pragma unroll
@@ -175,23 +245,13 @@ __global__ __launch_bounds__(64) void decode_split_kernel(DecodeArgs a) {
     // Raw scores wait in LDS and are written once per PK keys (normally once
     // per part): a global write among the K/V reads stalls the read stream
     // far more than its size suggests (HBM read/write turnaround).
-    // flush: keys [base, base+n) of the buffer to the probabilities rows.
     auto flush = [&](int base, int n) __attribute__((always_inline)) {
-        lds_order();
-        for (int t = lane; t < G * (PK / 4); t += 64) {
-            const int hh = t / (PK / 4), kq = 4 * (t % (PK / 4));
-            if (kq < n) {
-                const f32x4_t v = *reinterpret_cast<const f32x4_t*>(&sbuf[hh * PK + kq]);
-                float* dst = prow + (size_t)hh * a.probs_ld + base + kq;
-                if (kq + 3 < n) {
-                    *reinterpret_cast<f32x4_a4_t*>(dst) = v;
-                } else {
+        if (col == 0) {
 #pragma unroll
-                    for (int e = 0; e < 3; ++e)
-                        if (kq + e < n) dst[e] = v[e];
-                }
-            }
+            for (int r = 0; r < HPL; ++r) mref[grp * HPL + r] = m_run[r];
         }
+        lds_order();
+        write_half_scores<PK>(sbuf, mref, lhalf, hrow, hrow_ld, G, base, n, lane);
         lds_order();
     };
 
@@ -227,6 +287,7 @@ __global__ __launch_bounds__(64) void decode_split_kernel(DecodeArgs a) {
                 for (int r = 0; r < HPL; ++r) abuf[grp * HPL + r] = al[r];
             }
             lds_order();
+            if (PROBS && LONG && k0 - k_lo >= PK) rescale_half_scores(abuf, lhalf, hrow, hrow_ld, G, k_lo, (k0 - k_lo) / PK * PK, lane);
 #pragma unroll
             for (int hq = 0; hq < GQ / 4; ++hq) {
                 const float4 f = *reinterpret_cast<const float4*>(&abuf[4 * hq]);
@@ -281,7 +342,7 @@ __global__ __launch_bounds__(64) void decode_split_kernel(DecodeArgs a) {
 #pragma unroll
                 for (int r = 0; r < HPL; ++r) sbuf[(grp * HPL + r) * PK + kb + 16 * blk + col] = x[blk][r];
             // a part longer than the buffer writes it out each time it fills
-            if (kb + kDecKB == PK && k0 + kDecKB < k_hi) flush(k0 + kDecKB - PK, PK);
+            if (LONG && kb + kDecKB == PK && k0 + kDecKB < k_hi) flush(k0 + kDecKB - PK, PK);
         }
     };
 
@@ -322,7 +383,9 @@ __global__ __launch_bounds__(64) void decode_split_kernel(DecodeArgs a) {
 #pragma unroll
         for (int r = 0; r < HPL; ++r) {
             const int hh = grp * HPL + r;
-            if (hh < G) *reinterpret_cast<float2*>(part + hh * head_stride) = make_float2(m_run[r], l_run[r]);
+            if (hh < G)
+                *reinterpret_cast<float4*>(part + hh * head_stride) =
+                    make_float4(m_run[r], l_run[r], PROBS ? lhalf[hh] : 0.f, 0.f);
         }
     }
     if (vr == 0) {
@@ -377,6 +440,13 @@ __global__ __launch_bounds__(256) void decode_combine_kernel(DecodeArgs a) {
         ll += pr[(size_t)s * PS + 1] * __builtin_amdgcn_exp2f(pr[(size_t)s * PS] - m);
     const float l = block_reduce(ll, red, false);
     const float inv = 1.f / l;
+    // the probabilities are normalised by the sum of the half-precision
+    // values the parts wrote, so each row sums to 1
+    float lh = 0.f;
+    if (a.probs)
+        for (int s = tid; s < n_parts; s += 256)
+            lh += pr[(size_t)s * PS + 2] * __builtin_amdgcn_exp2f(pr[(size_t)s * PS] - m);
+    const float inv_h = a.probs ? 1.f / block_reduce(lh, red, false) : 0.f;
     // O: thread -> (dim, phase); phases take every (256/HD)-th part
     {
         constexpr int PH = 256 / HD;
@@ -405,54 +475,65 @@ __global__ __launch_bounds__(256) void decode_combine_kernel(DecodeArgs a) {
         }
     }
     if (a.probs) {
-        // P_j = 2^(x_j - m) / l over the row's ctx entries; 16-byte accesses
-        // (four in flight per thread) between a scalar head, up to the first
-        // aligned element, and a scalar tail
+        // P_j = h_j 2^(m_s - m) / l_h, h_j the half-precision value part s
+        // (keys [s*split_len, ...)) left at 16-bit word j of the row.  The
+        // row is widened in place, in blocks of 2048 keys from the top down:
+        // float j covers words 2j and 2j+1, which belong to keys at or above
+        // j, so a block's writes only reach words of its own keys (read into
+        // registers before the barrier) or of blocks already done.
         float* prow = a.probs + (size_t)row * a.probs_ld;
-        const int head = min((int)((4 - (((uintptr_t)prow >> 2) & 3)) & 3), ctx);
-        for (int j = tid; j < head; j += 256) prow[j] = __builtin_amdgcn_exp2f(prow[j] - m) * inv;
-        f32x4_t* p4 = reinterpret_cast<f32x4_t*>(prow + head);
-        const int n4 = (ctx - head) >> 2;
-        int j = tid;
-        for (; j + 3 * 256 < n4; j += 4 * 256) {
-            f32x4_t v[4];
+        const uint16_t* hrow = reinterpret_cast<const uint16_t*>(prow);
+        typedef uint32_t u32x4_a4_t __attribute__((ext_vector_type(4), aligned(4)));
+        typedef float f32x4_a4_t __attribute__((ext_vector_type(4), aligned(4)));
+        constexpr int BLK = 256 * 8;
+        for (int lo = (ctx - 1) / BLK * BLK; lo >= 0; lo -= BLK) {
+            const int k = lo + 8 * tid;
+            float v[8];
+            if (k < ctx) {
+                const float f = __builtin_amdgcn_exp2f(pr[(size_t)(k / a.split_len) * PS] - m) * inv_h;
+                if (k + 8 <= ctx) {
+                    const u32x4_a4_t w = *reinterpret_cast<const u32x4_a4_t*>(hrow + k);
 #pragma unroll
-            for (int u = 0; u < 4; ++u) v[u] = __builtin_nontemporal_load(p4 + j + u * 256);
+                    for (int e = 0; e < 8; ++e) v[e] = f16_value((uint16_t)(w[e >> 1] >> (16 * (e & 1)))) * f;
+                } else {
 #pragma unroll
-            for (int u = 0; u < 4; ++u) {
+                    for (int e = 0; e < 8; ++e) v[e] = k + e < ctx ? f16_value(hrow[k + e]) * f : 0.f;
+                }
+            }
+            __syncthreads();
+            if (k < ctx) {
+                if (k + 8 <= ctx) {
+                    *reinterpret_cast<f32x4_a4_t*>(prow + k) = f32x4_a4_t{v[0], v[1], v[2], v[3]};
+                    *reinterpret_cast<f32x4_a4_t*>(prow + k + 4) = f32x4_a4_t{v[4], v[5], v[6], v[7]};
+                } else {
 #pragma unroll
-                for (int e = 0; e < 4; ++e) v[u][e] = __builtin_amdgcn_exp2f(v[u][e] - m) * inv;
-                __builtin_nontemporal_store(v[u], p4 + j + u * 256);
+                    for (int e = 0; e < 8; ++e)
+                        if (k + e < ctx) prow[k + e] = v[e];
+                }
             }
         }
-        for (; j < n4; j += 256) {
-            f32x4_t v = __builtin_nontemporal_load(p4 + j);
-#pragma unroll
-            for (int e = 0; e < 4; ++e) v[e] = __builtin_amdgcn_exp2f(v[e] - m) * inv;
-            __builtin_nontemporal_store(v, p4 + j);
-        }
-        for (int t = head + 4 * n4 + tid; t < ctx; t += 256)
-            prow[t] = __builtin_amdgcn_exp2f(prow[t] - m) * inv;
     }
 }
 
-template <int HD, bool PROBS>
+template <int HD, bool PROBS, bool LONG>
 static void launch_split(const DecodeArgs& a, hipStream_t stream) {
     const dim3 grid((unsigned)((long)a.n_seq * a.n_splits * a.n_kv));
     if (a.group <= 4)
-        decode_split_kernel<HD, 1, PROBS><<<grid, dim3(64), 0, stream>>>(a);
+        decode_split_kernel<HD, 1, PROBS, LONG><<<grid, dim3(64), 0, stream>>>(a);
     else if (a.group <= 8)
-        decode_split_kernel<HD, 2, PROBS><<<grid, dim3(64), 0, stream>>>(a);
+        decode_split_kernel<HD, 2, PROBS, LONG><<<grid, dim3(64), 0, stream>>>(a);
     else
-        decode_split_kernel<HD, 4, PROBS><<<grid, dim3(64), 0, stream>>>(a);
+        decode_split_kernel<HD, 4, PROBS, LONG><<<grid, dim3(64), 0, stream>>>(a);
 }
 
 template <int HD>
 static void launch_decode_hd(const DecodeArgs& a, hipStream_t stream) {
-    if (a.probs)
-        launch_split<HD, true>(a, stream);
+    if (!a.probs)
+        launch_split<HD, false, false>(a, stream);
+    else if (a.split_len <= decode_part_limit(a.group, true))
+        launch_split<HD, true, false>(a, stream);
     else
-        launch_split<HD, false>(a, stream);
+        launch_split<HD, true, true>(a, stream);
     decode_combine_kernel<HD><<<dim3((unsigned)(a.n_seq * a.n_heads)), dim3(256), 0, stream>>>(a);
 }
 

@@ -34,6 +34,13 @@ __device__ __forceinline__ uint32_t pack_bf16x2(float a, float b) {
     return __builtin_bit_cast(uint32_t, v);
 }
 
+// IEEE half precision (binary16), round to nearest even.
+__device__ __forceinline__ uint16_t f16_bits(float x) { return __builtin_bit_cast(uint16_t, (_Float16)x); }
+__device__ __forceinline__ float f16_value(uint16_t u) { return (float)__builtin_bit_cast(_Float16, u); }
+__device__ __forceinline__ uint32_t pack_f16x2(float a, float b) {
+    return (uint32_t)f16_bits(a) | ((uint32_t)f16_bits(b) << 16);
+}
+
 // Round a double to bfloat16, ties to even, in one rounding.  The double is
 // first narrowed to float with round-to-odd (truncate, then set the last bit
 // when inexact); float keeps more than bfloat16's 8 significant bits plus two,

@@ -211,7 +211,11 @@ size_t attn_prefill_workspace_bytes(int n_seq, int n_heads, int n_kv, int head_d
  *   probs  NULL, or device float[n_seq][n_heads][probs_ld]; row (b, h) gets
  *          ctx[b] entries summing to 1, entries past ctx[b] are not written.
  *          Any probs_ld >= max_ctx works; a multiple of 32 starts every row
- *          on a 128-byte line, which the 16-byte stores of the kernels use
+ *          on a 128-byte line, which the 16-byte stores of the kernels use.
+ *          bf16: the row's first ctx[b] entries also hold the intermediate
+ *          unnormalised values in half precision, so each probability
+ *          carries a relative rounding error below 2^-11 (and below 2^-24
+ *          of the row's largest in absolute terms); f32: float throughout
  *   workspace device scratch, clobbered, no initialisation needed.  bf16
  *          needs at least n_seq*n_heads*(head_dim+2)*4 bytes (one part per
  *          row, EINVAL below that); attn_decode_workspace_bytes() gives the

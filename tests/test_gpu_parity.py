@@ -400,18 +400,34 @@ def test_bf16_decode_matches_oracle(nh, nkv, hd, ld_mult):
         assert np.array_equal(_bits(step.v_cache[b, :, c - 1]), _bits(d["v"][b]))
 
 
-@pytest.mark.parametrize("nh,nkv,parts_per_row", [(32, 2, 1), (16, 2, 2)])
-def test_bf16_decode_small_workspace(nh, nkv, parts_per_row):
+@pytest.mark.parametrize("nh,nkv,parts_per_row,spike", [(32, 2, 1, False), (16, 2, 2, False),
+                                                         (32, 2, 1, True), (16, 4, 1, True)])
+def test_bf16_decode_small_workspace(nh, nkv, parts_per_row, spike):
     """A workspace for fewer parts makes each part longer than the on-chip
-    raw-score buffer of a wide group (16 or 8 heads), so the split kernel
-    writes the scores out several times per part."""
+    raw-score buffer of a wide group (16, 8 or 4 heads), so the split kernel
+    writes values out several times per part.  With a spike, a late key's
+    score for one head of each group exceeds everything before it by far, so
+    the running maximum moves after values were written and those are
+    rescaled."""
     ctx = [3000, 700, 1, 2049]
     hd = 128
     w = wl.Workload(name="dec-ws", dtype=wl.BF16, n_heads=nh, n_kv=nkv, head_dim=hd, seed=37,
                     n_seq=len(ctx), decode=True, ctx_range=(1, 3000), cap=3072, want_probs=True)
-    say(f"bf16 decode small workspace nh={nh} nkv={nkv} parts/row={parts_per_row} ctx={ctx}")
+    say(f"bf16 decode small workspace nh={nh} nkv={nkv} parts/row={parts_per_row} spike={spike} ctx={ctx}")
     d = wl.gen_decode(w)
     d["ctx"] = ctx
+    if spike:
+        # key c-100 of sequence b, for KV group g, is 1.5x the rotated query
+        # of head g*G (a score near 16 in log2 units above the rest)
+        f = oracle_table(w)
+        G = nh // nkv
+        for b, c in enumerate(ctx):
+            if c < 1000:
+                continue
+            q = oracle.finish_heads(np64(d["q"][b:b + 1]), np.array([c - 1]), f, w.rd,
+                                    store=oracle.STORE_BF16)[0]
+            for g in range(nkv):
+                d["k_cache"][b, g, c - 100] = torch.from_numpy(1.5 * q[g * G]).to(torch.bfloat16)
     step = runner.DecodeStep(w, d, device=DEV, probs_ld_multiple=1)
     step.workspace = torch.empty(len(ctx) * nh * (hd + 4) * parts_per_row, dtype=torch.float32,
                                  device=DEV)
