@@ -446,6 +446,15 @@ __global__ __launch_bounds__(NW * 64, 8 / NW) void prefill_bf16_kernel(PrefillAr
                 ATTN_INTERLEAVE(NKK, 2, 6);
             }
 
+            // With two staging sets the K/V data stored at this tile's end
+            // arrived during the previous tile: store it now, so the LDS
+            // writes overlap the P.V products (K[j+2] replaces K[j], read
+            // last in the previous tile; V[j+1] replaces V[j-1]).
+            if (PD == 2) {
+                store_k(rr, cur);
+                store_v(rr ^ 1, cur);
+            }
+
             // ---- O^T += V^T P^T: keys 0..31 while the probabilities of keys
             // 32..63 are computed, then keys 32..63; V^T fragments are read
             // one step ahead
@@ -487,8 +496,10 @@ __global__ __launch_bounds__(NW * 64, 8 / NW) void prefill_bf16_kernel(PrefillAr
             // the P.V product
             l_run += sum_bf16_pairs(pk);
 
-            store_k(rr, cur);
-            store_v(rr ^ 1, cur);
+            if (PD == 1) {
+                store_k(rr, cur);
+                store_v(rr ^ 1, cur);
+            }
             __syncthreads();
             S0 = N0;
             S1 = N1;
