@@ -42,6 +42,9 @@
 namespace attn {
 
 constexpr int kTK = 64;                 // keys per tile
+// Fourth word of a raw buffer resource on gfx9-family parts (32-bit data
+// format; byte offsets, no swizzle, no index).
+constexpr int kBufferWord3 = 0x00020000;
 constexpr int kPartPad = 4;             // (m, l, pad, pad) before O in a partial
 // A row's running maximum (log2 units) is only moved, and O rescaled, when a
 // new score exceeds it by more than this; until then probabilities are
@@ -246,7 +249,10 @@ __global__ __launch_bounds__(NW * 64, 8 / NW) void prefill_bf16_kernel(PrefillAr
         itm.nsp = 1;
     }
     if (itm.nsp <= 0) return;
-    const int b = itm.b, qt = itm.qt, g = itm.g, s = itm.part, nsp = itm.nsp;
+    // the item is the same in every lane: keep it in scalar registers
+    const int b = __builtin_amdgcn_readfirstlane(itm.b), qt = __builtin_amdgcn_readfirstlane(itm.qt),
+              g = __builtin_amdgcn_readfirstlane(itm.g), s = __builtin_amdgcn_readfirstlane(itm.part),
+              nsp = __builtin_amdgcn_readfirstlane(itm.nsp);
 
     const int G = a.group;
     const int t0 = a.cu_seq[b];
@@ -290,26 +296,38 @@ __global__ __launch_bounds__(NW * 64, 8 / NW) void prefill_bf16_kernel(PrefillAr
     const uint16_t* kc = reinterpret_cast<const uint16_t*>(a.k_cache) + kvbase;
     const uint16_t* vc = reinterpret_cast<const uint16_t*>(a.v_cache) + kvbase;
 
-    // staging: thread -> NCH (row, 16-byte chunk) pairs of a tile.  Rows past
-    // the last key re-read the last key's row (always in bounds): their scores
-    // are masked to -inf and their probabilities are exactly 0, so the copy
-    // never contributes.
+    // staging: thread -> NCH (row, 16-byte chunk) pairs of a tile, fetched
+    // with buffer loads whose resource starts at the tile and ends at the
+    // last key: the per-thread offsets are fixed, the tile moves in scalar
+    // registers, and rows past the last key read as zeros (their scores are
+    // masked to -inf and their probabilities are exactly 0).
     u32x4_t kreg[PD][NCH], vreg[PD][NCH];
-    auto row_off = [&](int j, int c) __attribute__((always_inline)) {
+    int voff[NCH];
+#pragma unroll
+    for (int c = 0; c < NCH; ++c) {
         const int idx = c * kThreads + tid;
-        return (size_t)min(j * kTK + idx / CH, n_keys - 1) * HD + (idx % CH) * 8;
+        voff[c] = ((idx / CH) * HD + (idx % CH) * 8) * 2;
+    }
+    auto tile_rsrc = [&](const uint16_t* base, int j) __attribute__((always_inline)) {
+        const int rows = max(n_keys - j * kTK, 0);
+        return __builtin_amdgcn_make_buffer_rsrc((void*)(base + (size_t)j * kTK * HD), (short)0, rows * HD * 2,
+                                                 kBufferWord3);
     };
     auto lds_off = [&](int c, int stride) __attribute__((always_inline)) {
         const int idx = c * kThreads + tid;
         return (idx / CH) * stride + (idx % CH) * 8;
     };
     auto load_k = [&](int j, auto set) __attribute__((always_inline)) {
+        const auto rs = tile_rsrc(kc, j);
 #pragma unroll
-        for (int c = 0; c < NCH; ++c) kreg[set.value][c] = ld16(kc + row_off(j, c));
+        for (int c = 0; c < NCH; ++c)
+            kreg[set.value][c] = __builtin_bit_cast(u32x4_t, __builtin_amdgcn_raw_buffer_load_b128(rs, voff[c], 0, 0));
     };
     auto load_v = [&](int j, auto set) __attribute__((always_inline)) {
+        const auto rs = tile_rsrc(vc, j);
 #pragma unroll
-        for (int c = 0; c < NCH; ++c) vreg[set.value][c] = ld16(vc + row_off(j, c));
+        for (int c = 0; c < NCH; ++c)
+            vreg[set.value][c] = __builtin_bit_cast(u32x4_t, __builtin_amdgcn_raw_buffer_load_b128(rs, voff[c], 0, 0));
     };
     auto store_k = [&](int buf, auto set) __attribute__((always_inline)) {
 #pragma unroll
