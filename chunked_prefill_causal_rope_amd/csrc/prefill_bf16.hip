@@ -107,16 +107,25 @@ __device__ __forceinline__ float sum_bf16_pairs(const uint32_t* pk) {
 // part of the row tile's key tiles; workgroup i takes item i.  Without
 // splitting there is one part per row tile.  With splitting (few row tiles)
 // every workgroup derives the same schedule from cu_seq/start: a row tile of
-// n key tiles gets ceil(n / T) parts of equal length, T being the smallest
-// length (at least kMinTilesPerSplit) that keeps the item count within one
-// workgroup per CU slot, so the longest sequence is spread over the CUs
-// instead of deciding the call's duration alone.  The grid has room for the
-// largest item count the schedule can produce; the workgroups past the
+// n key tiles gets ceil(n / T) parts of equal length, T (at least
+// min_tiles_per_split) minimising the estimated duration
+// ceil(items / slots) * (T + 2), so the longest sequence is spread over the
+// CUs instead of deciding the call's duration alone.  The grid has room for
+// the largest item count the schedule can produce; the workgroups past the
 // actual count exit.
-#ifndef ATTN_PREFILL_MIN_TILES_PER_SPLIT
-#define ATTN_PREFILL_MIN_TILES_PER_SPLIT 4
+// Shortest part, in key tiles: a part's start-up (Q and first K/V tiles,
+// partial write, its share of the combine) weighs more for the 256-row
+// workgroups, one per CU, than for the 128-row ones, two per CU (measured:
+// c3-shaped calls gain ~2 % from 12 over 4; c1-shaped lose beyond 6).
+#ifndef ATTN_PREFILL_MIN_TILES_128
+#define ATTN_PREFILL_MIN_TILES_128 6
 #endif
-constexpr int kMinTilesPerSplit = ATTN_PREFILL_MIN_TILES_PER_SPLIT;
+#ifndef ATTN_PREFILL_MIN_TILES_256
+#define ATTN_PREFILL_MIN_TILES_256 12
+#endif
+__host__ __device__ constexpr int min_tiles_per_split(int rows_per_tile) {
+    return rows_per_tile == 256 ? ATTN_PREFILL_MIN_TILES_256 : ATTN_PREFILL_MIN_TILES_128;
+}
 
 // key tiles of row tile qt of sequence b (0 if the row tile is empty)
 __device__ __forceinline__ int group_tiles(const PrefillArgs& a, int b, int qt) {
@@ -167,7 +176,7 @@ __device__ __forceinline__ int split_part_length(const PrefillArgs& a, int gt) {
     for (int ci = 0; ci < 12; ++ci) {
         const int k = kCand[ci];
         const int T = (gmax + k - 1) / k;
-        if (T < kMinTilesPerSplit && k > 1) break;
+        if (T < min_tiles_per_split(a.rows_per_tile) && k > 1) break;
         if (T == prev_T) continue;
         prev_T = T;
         const int n = wave_reduce_dpp<false>(gt > 0 ? (gt + T - 1) / T : 0) * a.n_kv;
@@ -650,7 +659,7 @@ __global__ __launch_bounds__(256) void prefill_combine_kernel(PrefillArgs a) {
 // alone give every CU a workgroup; otherwise 128-row workgroups.  When the
 // row tiles are too few for the GPU (an upper bound from host scalars: every
 // sequence with max_chunk tokens) and the longest key range spans more than
-// kMinTilesPerSplit tiles, the call splits: a persistent grid of one
+// min_tiles_per_split tiles, the call splits: a persistent grid of one
 // workgroup per CU slot, with the part length chosen on the device from the
 // actual lengths (see the schedule above).
 #ifndef ATTN_PREFILL_BIG_TILE_BLOCKS
@@ -681,7 +690,8 @@ PrefillPlan plan_prefill(int n_seq, int n_heads, int n_kv, int head_dim, int n_t
     p.grid = (int)base;
     p.ws_bytes = 0;
     p.table_bytes = 0;
-    if (base < kBigTileBlocks && tiles > kMinTilesPerSplit && (long)n_seq * p.n_qtiles <= kMaxSplitGroups) {
+    if (base < kBigTileBlocks && tiles > min_tiles_per_split(p.rows_per_tile) &&
+        (long)n_seq * p.n_qtiles <= kMaxSplitGroups) {
         const long slots = (long)device_cus() * (p.rows_per_tile == 256 ? 1 : 2);
         const size_t table = ((size_t)n_seq * p.n_qtiles * 2 * sizeof(int) + 255) / 256 * 256;
         // items <= slots + one extra part per row tile (ceil) -- see split_schedule
@@ -714,7 +724,7 @@ PrefillPlan plan_prefill(int n_seq, int n_heads, int n_kv, int head_dim, int n_t
                 const int cand[12] = {1, 2, 3, 4, 6, 8, 12, 16, 24, 32, 48, 64};
                 for (int k : cand) {
                     const long T = (gmax + k - 1) / k;
-                    if (T < kMinTilesPerSplit && k > 1) break;
+                    if (T < min_tiles_per_split(p.rows_per_tile) && k > 1) break;
                     if (T == prev_T) continue;
                     prev_T = T;
                     long n = 0;
