@@ -14,7 +14,9 @@ Prints ONE JSON line.  `value` is the whole-step throughput (algorithmic
 FLOP/s for prefill, K/V bytes read per second for decode); `roofline` is the
 attention call measured per launch with HIP events on its stream;
 `cpu_baseline` is the CPU oracle timed on a bounded sample of the same
-workload on this host.
+workload on this host.  The decode line also carries `importance`: the
+per-position importance call (sum over heads of the step's probabilities),
+timed per launch after the step, outside it.
 """
 from __future__ import annotations
 
@@ -278,6 +280,22 @@ def bench_decode(torch, w, args, stream):
                       "head_dim": w.head_dim, "ctx_total": sum(d["ctx"]),
                       "probs": w.want_probs},
            "roofline": roof}
+    if w.want_probs:
+        # per-position importance of the step (sum over heads of the
+        # probabilities): a separate call after the decode, not part of the
+        # step above; its algorithmic bytes are the probabilities read once
+        # and the importance vector read and written
+        from chunked_prefill_causal_rope_amd import api
+        imp = torch.zeros((w.n_seq, step.max_ctx), dtype=torch.float32, device="cuda")
+        call = lambda: api.decode_importance(step.probs, step.ctx, step.max_ctx, imp)
+        for _ in range(2):
+            per = time_launches(torch, [call] * max(3, args.steps), stream)
+        imp_ms = sum(per) / len(per)
+        imp_bytes = 4.0 * sum(d["ctx"]) * (w.n_heads + 2)
+        out["importance"] = {"kernel": "attn_decode_importance (decode_importance_kernel)",
+                             "avg_launch_ms": round(imp_ms, 4), "bytes_per_launch": imp_bytes,
+                             "achieved_gbs": round(imp_bytes / (imp_ms * 1e-3) / 1e9, 1),
+                             "frac": round(imp_bytes / (imp_ms * 1e-3) / 1e9 / PEAK_HBM_GBS, 4)}
     return out, d
 
 
@@ -312,7 +330,7 @@ def main():
                "steps": args.steps, "warmup": args.warmup, "ms_per_step": res["ms_per_step"],
                "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "bf16",
                "data": "synthetic", "config": dict(res["config"], workload=w.name),
-               "roofline": res["roofline"]}
+               "roofline": res["roofline"], **({"importance": res["importance"]} if "importance" in res else {})}
         if not args.no_cpu:
             res["cpu_baseline"] = cpu_baseline_decode(w, d, args.cpu_seconds)
     else:

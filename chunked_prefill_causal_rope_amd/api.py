@@ -23,8 +23,9 @@ _STATUS = {0: "ok", -1: "invalid argument", -2: "exceeds cache capacity",
 _lib = None
 
 EXPORTS = ("attn_rope_inv_freq", "attn_yarn_inv_freq", "attn_rope_apply", "attn_kv_append",
-           "attn_prefill_chunk", "attn_prefill_workspace_bytes", "attn_decode",
-           "attn_decode_workspace_bytes", "attn_status_string", "attn_version")
+           "attn_rope_qkv", "attn_prefill_chunk", "attn_prefill_workspace_bytes", "attn_decode",
+           "attn_decode_workspace_bytes", "attn_decode_importance", "attn_status_string",
+           "attn_version")
 
 
 class AttnError(RuntimeError):
@@ -56,6 +57,8 @@ def lib() -> ctypes.CDLL:
     L.attn_prefill_workspace_bytes.restype = sz
     L.attn_decode.argtypes = [vp, vp, vp, i, i, i, i, i, i, vp, i, f, vp, vp, i, vp, sz, vp]
     L.attn_decode_workspace_bytes.argtypes = [i, i, i, i, i]
+    L.attn_decode_importance.argtypes = [vp, i, i, i, vp, i, vp, i, i, vp]
+    L.attn_decode_importance.restype = i
     L.attn_decode_workspace_bytes.restype = sz
     L.attn_status_string.argtypes = [i]
     L.attn_status_string.restype = ctypes.c_char_p
@@ -216,6 +219,17 @@ def prefill_chunk(q: torch.Tensor, k_cache: torch.Tensor, v_cache: torch.Tensor,
 
 def decode_workspace_bytes(n_seq: int, n_heads: int, n_kv: int, head_dim: int, max_ctx: int) -> int:
     return int(lib().attn_decode_workspace_bytes(n_seq, n_heads, n_kv, head_dim, max_ctx))
+
+
+def decode_importance(probs: torch.Tensor, ctx: torch.Tensor, max_ctx: int, imp: torch.Tensor,
+                      accumulate: bool = True):
+    """imp[b][j] (+)= sum over heads of probs[b][h][j], j < ctx[b]."""
+    n_seq, nh, ld = probs.shape
+    assert probs.dtype == torch.float32 and imp.dtype == torch.float32
+    assert imp.dim() == 2 and imp.shape[0] >= n_seq and ctx.shape == (n_seq,) and ctx.dtype == torch.int32
+    st = lib().attn_decode_importance(_dev(probs, "probs"), n_seq, nh, ld, _dev(ctx, "ctx"), max_ctx,
+                                      _dev(imp, "imp"), imp.shape[1], 1 if accumulate else 0, _stream())
+    _check("attn_decode_importance", st)
 
 
 def decode(q: torch.Tensor, k_cache: torch.Tensor, v_cache: torch.Tensor, ctx: torch.Tensor,

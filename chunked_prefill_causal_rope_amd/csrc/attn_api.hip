@@ -363,4 +363,23 @@ int attn_decode(const void* q, const void* k_cache, const void* v_cache, int dty
     return status_of(attn::launch_decode_bf16(a, s));
 }
 
+int attn_decode_importance(const float* probs, int n_seq, int n_heads, int probs_ld,
+                           const int32_t* ctx, int max_ctx, float* imp, int imp_ld, int accumulate,
+                           void* stream) {
+    if (n_seq < 0 || n_heads <= 0 || max_ctx < 0) return ATTN_EINVAL;
+    if (n_seq == 0 || max_ctx == 0) return ATTN_OK;
+    if (!probs || !ctx || !imp || probs_ld < max_ctx || imp_ld < max_ctx) return ATTN_EINVAL;
+    attn::ImportanceArgs a{};
+    a.probs = probs;
+    a.ctx = ctx;
+    a.imp = imp;
+    a.n_seq = n_seq;
+    a.n_heads = n_heads;
+    a.probs_ld = probs_ld;
+    a.max_ctx = max_ctx;
+    a.imp_ld = imp_ld;
+    a.accumulate = accumulate ? 1 : 0;
+    return status_of(attn::launch_decode_importance(a, (hipStream_t)stream));
+}
+
 }  // extern "C"

@@ -89,4 +89,14 @@ int decode_group_limit();
 int decode_part_limit(int group, bool probs);
 hipError_t launch_decode_bf16(const DecodeArgs& a, hipStream_t stream);
 
+// Per-position importance of a decode step: sum over heads of the
+// probabilities.
+struct ImportanceArgs {
+    const float* probs;    // [n_seq][n_heads][probs_ld]
+    const int32_t* ctx;    // [n_seq]
+    float* imp;            // [n_seq][imp_ld]
+    int n_seq, n_heads, probs_ld, max_ctx, imp_ld, accumulate;
+};
+hipError_t launch_decode_importance(const ImportanceArgs& a, hipStream_t stream);
+
 }  // namespace attn

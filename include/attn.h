@@ -231,6 +231,27 @@ int attn_decode(const void *q, const void *k_cache, const void *v_cache, int dty
 
 size_t attn_decode_workspace_bytes(int n_seq, int n_heads, int n_kv, int head_dim, int max_ctx);
 
+/*
+ * Importance of each cached position after a decode step ([ATT] the decode
+ * attention adds every head's probability row into one vector before the
+ * cache accumulates it for eviction: "a position's importance is the
+ * probability mass that reads it"):
+ *   imp[b][j] = (accumulate ? imp[b][j] : 0) + sum_h probs[b][h][j],
+ * for j < min(ctx[b], max_ctx); entries past that are not written.  Heads are
+ * summed in order in float.
+ *   probs  device float[n_seq][n_heads][probs_ld], as attn_decode returned
+ *          them, read
+ *   ctx    device int32[n_seq], the same array attn_decode used
+ *   imp    device float[n_seq][imp_ld], read (when accumulating) and written
+ * Ownership: the caller's buffers; nothing is allocated.  The call is
+ * ordered after attn_decode on the same stream.
+ * Errors: EINVAL (null pointer, probs_ld or imp_ld < max_ctx, n_heads <= 0,
+ * negative sizes), EDEVICE.  n_seq == 0 or max_ctx == 0: ATTN_OK, no launch.
+ */
+int attn_decode_importance(const float *probs, int n_seq, int n_heads, int probs_ld,
+                           const int32_t *ctx, int max_ctx, float *imp, int imp_ld,
+                           int accumulate, void *stream);
+
 /* Static, human-readable name of a status code. */
 const char *attn_status_string(int status);
 

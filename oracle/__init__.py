@@ -69,6 +69,8 @@ def _load():
                                ctypes.c_int, ctypes.c_long, _ip, ctypes.c_double, _dp, _dp,
                                ctypes.c_long, ctypes.c_int]
     lib.orc_attend.restype = ctypes.c_int
+    lib.orc_head_importance.argtypes = [_dp, ctypes.c_int, ctypes.c_long, ctypes.c_long, _dp]
+    lib.orc_head_importance.restype = ctypes.c_int
     _lib = lib
     return lib
 
@@ -169,6 +171,20 @@ def attend(q, k_cache, v_cache, qpos, scale: float, want_probs: bool = False,
     if rc != 0:
         raise ValueError("oracle attend: bad arguments")
     return out, probs
+
+
+def head_importance(probs, ctx: int) -> np.ndarray:
+    """Importance of each of the first ctx positions for one decode step:
+    the sum over heads of the probability rows, probs [nh][>= ctx].  [ATT]
+    the per-head loop of the decode attention (each head's probabilities are
+    added into one vector; "a position's importance is the probability mass
+    that reads it")."""
+    pa = _f64(probs)
+    nh, ld = pa.shape
+    imp = np.zeros(ctx, dtype=np.float64)
+    if _load().orc_head_importance(pa.ctypes.data_as(_dp), nh, ctx, ld, imp.ctypes.data_as(_dp)) != 0:
+        raise ValueError("oracle head_importance: bad arguments")
+    return imp
 
 
 def prefill_sequence(q_raw, k_raw, v_raw, chunk: int, inv_freq, rotary_dim: int,

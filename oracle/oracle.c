@@ -386,3 +386,24 @@ int orc_attend(const double *q, const double *kc, const double *vc, int n_tok, i
     free(th);
     return rc;
 }
+
+/*
+ * Importance of each cached position for one decode step ([ATT] the
+ * per-head loop of the decode attention adds every head's probability row
+ * into one vector, "a position's importance is the probability mass that
+ * reads it"): imp[j] = sum over heads h of probs[h][j], j < ctx, heads in
+ * order, in double.  probs [nh][probs_ld].  Returns 0, or -1 on bad
+ * arguments.
+ */
+int orc_head_importance(const double *probs, int nh, long ctx, long probs_ld, double *imp)
+{
+    if (nh <= 0 || ctx < 0 || probs_ld < ctx)
+        return -1;
+    for (long j = 0; j < ctx; j++) {
+        double s = 0.0;
+        for (int h = 0; h < nh; h++)
+            s += probs[(long)h * probs_ld + j];
+        imp[j] = s;
+    }
+    return 0;
+}

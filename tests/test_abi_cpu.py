@@ -176,3 +176,22 @@ def test_workspace_sizes():
     # table, then one partial (128 rows x (128 + 4) floats) per work item
     n = L.attn_prefill_workspace_bytes(1, 32, 8, 128, 128, 128, 4096)
     assert n > 256 and (n - 256) % (128 * 132 * 4) == 0
+
+
+def importance(**kw):
+    a = dict(probs=P, n_seq=4, nh=32, ld=4096, ctx=P, max_ctx=4096, imp=P, imp_ld=4096, acc=1)
+    a.update(kw)
+    return api.lib().attn_decode_importance(a["probs"], a["n_seq"], a["nh"], a["ld"], a["ctx"],
+                                            a["max_ctx"], a["imp"], a["imp_ld"], a["acc"], None)
+
+
+def test_importance_validation():
+    assert importance(probs=None) == EINVAL
+    assert importance(imp=None) == EINVAL
+    assert importance(ctx=None) == EINVAL
+    assert importance(ld=4095) == EINVAL
+    assert importance(imp_ld=100) == EINVAL
+    assert importance(nh=0) == EINVAL
+    assert importance(n_seq=-1) == EINVAL
+    assert importance(n_seq=0) == OK
+    assert importance(max_ctx=0) == OK

@@ -454,6 +454,58 @@ def test_bf16_decode_small_workspace(nh, nkv, parts_per_row, spike):
         assert dp.max() <= 2e-2, dp.max()
 
 
+# ------------------------------------------------------------------ importance
+
+@pytest.mark.parametrize("dtype", [wl.BF16, wl.F32])
+def test_decode_importance_matches_oracle(dtype):
+    """Per-position importance after a decode step: the sum over heads of
+    the probabilities.  Against the GPU's own probabilities summed in head
+    order in float (bit for bit), against the oracle's importance (within the
+    probabilities' tolerance, summed over heads), accumulating twice doubles
+    it exactly, and entries past ctx stay untouched."""
+    ctx = [1, 63, 64, 65, 1025, 3000]
+    nh, nkv, hd = 32, 8, 128
+    w = wl.Workload(name="imp", dtype=dtype, n_heads=nh, n_kv=nkv, head_dim=hd, seed=43,
+                    n_seq=len(ctx), decode=True, ctx_range=(1, 3000), cap=3072, want_probs=True)
+    say(f"decode importance dtype={dtype} ctx={ctx}")
+    d = wl.gen_decode(w)
+    d["ctx"] = ctx
+    step = runner.DecodeStep(w, d, device=DEV, probs_ld_multiple=1)
+    step.run()
+    imp = torch.full((len(ctx), 3100), float("nan"), device=DEV)
+    api.decode_importance(step.probs, step.ctx, step.max_ctx, imp, accumulate=False)
+    torch.cuda.synchronize()
+    gp = step.probs.detach().cpu().numpy()
+    gi = imp.detach().cpu().numpy()
+    f = oracle_table(w)
+    for b, c in enumerate(ctx):
+        own = np.zeros(c, dtype=np.float32)
+        for h in range(nh):
+            own += gp[b, h, :c]
+        assert np.array_equal(gi[b, :c], own), f"seq {b}: not the head-ordered float sum"
+        assert np.all(np.isnan(gi[b, c:])), "entries past ctx must stay untouched"
+        pos = np.array([c - 1])
+        kc = np64(d["k_cache"][b])[:, :c].copy()
+        vc = np64(d["v_cache"][b])[:, :c].copy()
+        store = store_of(w)
+        kc[:, c - 1] = oracle.finish_heads(np64(d["k"][b:b + 1]), pos, f, w.rd, store=store)[0]
+        vc[:, c - 1] = np64(d["v"][b])
+        q = oracle.finish_heads(np64(d["q"][b:b + 1]), pos, f, w.rd, store=store)
+        _, P = oracle.attend(q, kc, vc, pos, w.scale, want_probs=True)
+        ref = oracle.head_importance(P[0], c)
+        tol = (2e-2 * np.sqrt(np.mean(P[0] ** 2, axis=-1))).sum() if dtype == wl.BF16 else nh * 1e-4
+        err = float(np.max(np.abs(gi[b, :c] - ref)))
+        say(f"  seq {b} ctx {c}: max |d imp| {err:.3e} (tol {tol:.3e}), sum {gi[b, :c].sum():.6f}")
+        assert err <= tol
+        assert abs(float(gi[b, :c].astype(np.float64).sum()) - nh) <= 1e-4 * nh
+    # accumulating adds the same vector again: exactly twice the first
+    first = imp.clone()
+    api.decode_importance(step.probs, step.ctx, step.max_ctx, imp, accumulate=True)
+    torch.cuda.synchronize()
+    for b, c in enumerate(ctx):
+        assert torch.equal(imp[b, :c], 2 * first[b, :c])
+
+
 # ------------------------------------------------------------------ graphs
 
 def test_graph_replay_matches_eager():

@@ -371,6 +371,42 @@ def test_prefill_matches_brute_force_end_to_end():
 # Plant a mistake in a copy of oracle.c, build it, and show that a pin above
 # catches it.  The real oracle is untouched.
 
+def test_head_importance_mass_and_special_cases():
+    """Importance = sum over heads of the probability rows ([ATT] decode
+    loop, Born-rule comment).  Pinned by what the softmax fixes: every row
+    sums to 1, so the importances of one step sum to the number of heads; a
+    single key gets all of it; equal keys share it equally; and a head whose
+    query is orthogonal to every key but one near-duplicate contributes
+    (almost) only there."""
+    rng = np.random.default_rng(41)
+    nh, nkv, hd, ctx = 8, 2, 16, 37
+    q = rng.standard_normal((1, nh, hd))
+    kc = rng.standard_normal((nkv, ctx, hd))
+    vc = rng.standard_normal((nkv, ctx, hd))
+    _, P = oracle.attend(q, kc, vc, np.array([ctx - 1]), 0.25, want_probs=True)
+    imp = oracle.head_importance(P[0], ctx)
+    assert imp.shape == (ctx,)
+    assert abs(imp.sum() - nh) < 1e-12
+    assert np.all(imp >= 0) and np.all(imp <= nh)
+    # one key: every head reads it with probability 1
+    _, P1 = oracle.attend(q, kc[:, :1], vc[:, :1], np.array([0]), 0.25, want_probs=True)
+    assert np.array_equal(oracle.head_importance(P1[0], 1), [float(nh)])
+    # equal keys: uniform probabilities, importance nh / ctx each
+    keq = np.repeat(kc[:, :1], ctx, axis=1)
+    _, Pe = oracle.attend(q, keq, vc, np.array([ctx - 1]), 0.25, want_probs=True)
+    assert np.allclose(oracle.head_importance(Pe[0], ctx), nh / ctx, rtol=0, atol=1e-12)
+    # a spiked key read by one head only: that head puts ~all of its mass there
+    qs = np.zeros((1, nh, hd))
+    ks = np.zeros((nkv, ctx, hd))
+    qs[0, 3, 0] = 40.0
+    ks[3 // (nh // nkv), 5, 0] = 1.0
+    _, Ps = oracle.attend(qs, ks, vc, np.array([ctx - 1]), 1.0, want_probs=True)
+    imps = oracle.head_importance(Ps[0], ctx)
+    other = (nh - 1) / ctx          # the other heads see all-zero scores: uniform
+    assert abs(imps[5] - (1.0 + other)) < 1e-9
+    assert np.allclose(np.delete(imps, 5), other, atol=1e-9)
+
+
 MUTATIONS = {
     "mask_off_by_one": ("(long)jb->qpos[t] + 1, jb->scale", "(long)jb->qpos[t], jb->scale"),
     "gqa_modulo": ("int g = h / group;", "int g = h % jb->nkv;"),
@@ -379,6 +415,7 @@ MUTATIONS = {
     "norm_without_mean": ("double r = 1.0 / sqrt(ss / (double)hd + eps);", "double r = 1.0 / sqrt(ss + eps);"),
     "probs_not_normalised": ("scratch[j] /= l;", "scratch[j] /= (l + 1e-3);"),
     "bf16_truncation": ("double r = nearbyint(ldexp(x, -q));", "double r = trunc(ldexp(x, -q));"),
+    "importance_skips_a_head": ("for (int h = 0; h < nh; h++)\n            s += probs", "for (int h = 1; h < nh; h++)\n            s += probs"),
 }
 
 
@@ -399,7 +436,8 @@ def _pins_pass():
     checks = [test_rope_worked_example, test_rope_is_complex_multiplication,
               test_rmsnorm_worked_example_and_styles, test_rmsnorm_unit_rms_then_rope_order,
               lambda: test_brute_force_matrix_softmax(5, 7), test_gqa_equals_mha_with_repeated_kv,
-              test_attention_head_uniform_page_example, test_bf16_rounding_matches_torch_on_float32_values]
+              test_attention_head_uniform_page_example, test_bf16_rounding_matches_torch_on_float32_values,
+              test_head_importance_mass_and_special_cases]
     for c in checks:
         try:
             c()
