@@ -69,6 +69,10 @@ def _load():
                                ctypes.c_int, ctypes.c_long, _ip, ctypes.c_double, _dp, _dp,
                                ctypes.c_long, ctypes.c_int]
     lib.orc_attend.restype = ctypes.c_int
+    lib.orc_attend_window.argtypes = [_dp, _dp, _dp, ctypes.c_int, ctypes.c_int, ctypes.c_int,
+                                      ctypes.c_int, ctypes.c_long, _ip, ctypes.c_double, _dp, _dp,
+                                      ctypes.c_long, ctypes.c_long, ctypes.c_int]
+    lib.orc_attend_window.restype = ctypes.c_int
     lib.orc_head_importance.argtypes = [_dp, ctypes.c_int, ctypes.c_long, ctypes.c_long, _dp]
     lib.orc_head_importance.restype = ctypes.c_int
     _lib = lib
@@ -149,11 +153,12 @@ def finish_heads(x, pos, inv_freq, rotary_dim: int, rope_scale: float = 1.0,
 # --------------------------------------------------------------------------
 
 def attend(q, k_cache, v_cache, qpos, scale: float, want_probs: bool = False,
-           n_threads: int | None = None):
+           n_threads: int | None = None, window: int = 0):
     """q [n_tok][nh][hd]; k_cache, v_cache [nkv][cap][hd] of one sequence;
-    row t attends keys 0..qpos[t].  Returns (out [n_tok][nh][hd], probs) where
-    probs is a list-of-rows array [n_tok][nh][max(qpos)+1] (zero past each
-    row's length) or None."""
+    row t attends keys 0..qpos[t] -- or, with window > 0, the last `window`
+    of them ([ATT] QwenAttnCfg.window; zero probability before).  Returns
+    (out [n_tok][nh][hd], probs) where probs is a list-of-rows array
+    [n_tok][nh][max(qpos)+1] (zero past each row's length) or None."""
     qa, ka, va = _f64(q), _f64(k_cache), _f64(v_cache)
     n_tok, nh, hd = qa.shape
     nkv, cap, hd2 = ka.shape
@@ -163,11 +168,11 @@ def attend(q, k_cache, v_cache, qpos, scale: float, want_probs: bool = False,
     out = np.zeros((n_tok, nh, hd), dtype=np.float64)
     ld = int(qp.max()) + 1 if n_tok else 1
     probs = np.zeros((n_tok, nh, ld), dtype=np.float64) if want_probs else None
-    rc = _load().orc_attend(qa.ctypes.data_as(_dp), ka.ctypes.data_as(_dp),
-                            va.ctypes.data_as(_dp), n_tok, nh, nkv, hd, cap,
-                            qp.ctypes.data_as(_ip), scale, out.ctypes.data_as(_dp),
-                            probs.ctypes.data_as(_dp) if probs is not None else None, ld,
-                            n_threads or default_threads())
+    rc = _load().orc_attend_window(qa.ctypes.data_as(_dp), ka.ctypes.data_as(_dp),
+                                   va.ctypes.data_as(_dp), n_tok, nh, nkv, hd, cap,
+                                   qp.ctypes.data_as(_ip), scale, out.ctypes.data_as(_dp),
+                                   probs.ctypes.data_as(_dp) if probs is not None else None, ld,
+                                   int(window), n_threads or default_threads())
     if rc != 0:
         raise ValueError("oracle attend: bad arguments")
     return out, probs
@@ -191,7 +196,7 @@ def prefill_sequence(q_raw, k_raw, v_raw, chunk: int, inv_freq, rotary_dim: int,
                      scale: float, store: int, cap: int | None = None, start: int = 0,
                      rope_scale: float = 1.0, norm_style: int = NORM_NONE, q_norm_w=None,
                      k_norm_w=None, eps: float = 1e-6, want_probs: bool = False,
-                     k_cache=None, v_cache=None, n_threads: int | None = None):
+                     k_cache=None, v_cache=None, n_threads: int | None = None, window: int = 0):
     """Chunked prefill of one prompt.  For each chunk of `chunk` tokens, the
     chunk's K rows are finished (norm, RoPE, rounding) and written with its V
     rows into the head-major cache at their absolute positions BEFORE any of
@@ -228,7 +233,7 @@ def prefill_sequence(q_raw, k_raw, v_raw, chunk: int, inv_freq, rotary_dim: int,
         # write the whole chunk first: cache[g][pos] = K'[pos][g], V[pos][g]
         kc[:, start + c0:start + c1, :] = kcn.transpose(1, 0, 2)
         vc[:, start + c0:start + c1, :] = vr[c0:c1].transpose(1, 0, 2)
-        o, pr = attend(qc, kc, vc, pos, scale, want_probs, n_threads)
+        o, pr = attend(qc, kc, vc, pos, scale, want_probs, n_threads, window)
         out[c0:c1] = o
         q_rot[c0:c1] = qc
         if want_probs:

@@ -293,6 +293,7 @@ typedef struct {
     double scale;
     double *out, *probs;
     long probs_ld;
+    long window;
     int n_threads, tid;
     int status;
 } attend_job;
@@ -318,8 +319,17 @@ static void *attend_worker(void *arg)
         const double *kc = jb->kc + (long)g * jb->cap * jb->hd;
         const double *vc = jb->vc + (long)g * jb->cap * jb->hd;
         double *pr = jb->probs ? jb->probs + r * jb->probs_ld : NULL;
-        attend_row(q, kc, vc, jb->hd, (long)jb->qpos[t] + 1, jb->scale, jb->out + r * jb->hd,
-                   pr, scratch);
+        /* sliding window ([ATT] QwenAttnCfg.window, "attend only the last N
+         * positions"; the decode loop starts at stored - window): keys
+         * first..p, probabilities of the keys before it are 0 */
+        long first = 0;
+        if (jb->window > 0 && (long)jb->qpos[t] + 1 > jb->window)
+            first = (long)jb->qpos[t] + 1 - jb->window;
+        if (pr)
+            for (long j = 0; j < first; j++)
+                pr[j] = 0.0;
+        attend_row(q, kc + first * jb->hd, vc + first * jb->hd, jb->hd, (long)jb->qpos[t] + 1 - first,
+                   jb->scale, jb->out + r * jb->hd, pr ? pr + first : NULL, scratch);
     }
     free(scratch);
     jb->status = 0;
@@ -336,10 +346,28 @@ static void *attend_worker(void *arg)
  *   probs NULL or [n_tok][nh][probs_ld]; row (t,h) gets qpos[t]+1 entries
  * Returns 0, or -1 on bad arguments / allocation failure.
  */
+int orc_attend_window(const double *q, const double *kc, const double *vc, int n_tok, int nh,
+                      int nkv, int hd, long cap, const int64_t *qpos, double scale, double *out,
+                      double *probs, long probs_ld, long window, int n_threads);
+
 int orc_attend(const double *q, const double *kc, const double *vc, int n_tok, int nh, int nkv,
                int hd, long cap, const int64_t *qpos, double scale, double *out, double *probs,
                long probs_ld, int n_threads)
 {
+    return orc_attend_window(q, kc, vc, n_tok, nh, nkv, hd, cap, qpos, scale, out, probs, probs_ld,
+                             0, n_threads);
+}
+
+/*
+ * The same with a sliding window: window > 0 limits row t to the keys
+ * max(0, qpos[t] + 1 - window) .. qpos[t]; 0 means the whole prefix.
+ */
+int orc_attend_window(const double *q, const double *kc, const double *vc, int n_tok, int nh,
+                      int nkv, int hd, long cap, const int64_t *qpos, double scale, double *out,
+                      double *probs, long probs_ld, long window, int n_threads)
+{
+    if (window < 0)
+        return -1;
     if (n_tok < 0 || nh <= 0 || nkv <= 0 || hd <= 0 || nh % nkv != 0)
         return -1;
     for (int t = 0; t < n_tok; t++)
@@ -362,7 +390,7 @@ int orc_attend(const double *q, const double *kc, const double *vc, int n_tok, i
     int rc = 0;
     for (int i = 0; i < n_threads; i++) {
         attend_job j = {q, kc, vc, n_tok, nh, nkv, hd, cap, qpos, scale, out, probs, probs_ld,
-                        n_threads, i, 0};
+                        window, n_threads, i, 0};
         jobs[i] = j;
     }
     int started = 0;

@@ -407,8 +407,53 @@ def test_head_importance_mass_and_special_cases():
     assert np.allclose(np.delete(imps, 5), other, atol=1e-9)
 
 
+def test_sliding_window_special_cases():
+    """Sliding window ([ATT] QwenAttnCfg.window: attend only the last N
+    positions; the decode loop starts at stored - window).  Pinned by: a
+    window as long as the prefix is the full attention; window 1 returns the
+    row's own V; a brute-force banded softmax on tiny inputs; the
+    probabilities before the window are exactly 0 and each row still sums
+    to 1; and chunked = sequential under the window."""
+    rng = np.random.default_rng(51)
+    nh, nkv, hd, T = 4, 2, 8, 23
+    q = rng.standard_normal((T, nh, hd))
+    kc = rng.standard_normal((nkv, T, hd))
+    vc = rng.standard_normal((nkv, T, hd))
+    pos = np.arange(T)
+    full, Pf = oracle.attend(q, kc, vc, pos, 0.35, want_probs=True)
+    same, Ps = oracle.attend(q, kc, vc, pos, 0.35, want_probs=True, window=T)
+    assert np.array_equal(full, same) and np.array_equal(Pf, Ps)
+    own, _ = oracle.attend(q, kc, vc, pos, 0.35, window=1)
+    for t in range(T):
+        for h in range(nh):
+            assert np.array_equal(own[t, h], vc[h // (nh // nkv), t])
+    W = 5
+    ow, Pw = oracle.attend(q, kc, vc, pos, 0.35, want_probs=True, window=W)
+    for t in range(T):
+        lo = max(0, t - W + 1)
+        for h in range(nh):
+            g = h // (nh // nkv)
+            s = np.array([0.35 * float(q[t, h] @ kc[g, j]) for j in range(T)])
+            s[:lo] = -np.inf
+            s[t + 1:] = -np.inf
+            e = np.exp(s - s.max())
+            P = e / e.sum()
+            assert np.allclose(ow[t, h], P @ vc[g], rtol=1e-12, atol=1e-12)
+            assert np.allclose(Pw[t, h, :t + 1], P[:t + 1], rtol=1e-12, atol=1e-14)
+            assert np.all(Pw[t, h, :lo] == 0.0)
+            assert abs(Pw[t, h, :t + 1].sum() - 1.0) < 1e-12
+    # chunked = sequential with the window (the cache holds every position)
+    f = oracle.rope_inv_freq(hd, 1e4)
+    kr = rng.standard_normal((T, nkv, hd))
+    vr = rng.standard_normal((T, nkv, hd))
+    seq = oracle.prefill_sequence(q, kr, vr, 1, f, hd, 0.35, oracle.STORE_F32, window=W)
+    chk = oracle.prefill_sequence(q, kr, vr, 6, f, hd, 0.35, oracle.STORE_F32, window=W)
+    assert np.array_equal(seq["out"], chk["out"])
+
+
 MUTATIONS = {
-    "mask_off_by_one": ("(long)jb->qpos[t] + 1, jb->scale", "(long)jb->qpos[t], jb->scale"),
+    "mask_off_by_one": ("(long)jb->qpos[t] + 1 - first,", "(long)jb->qpos[t] - first,"),
+    "window_one_short": ("first = (long)jb->qpos[t] + 1 - jb->window;", "first = (long)jb->qpos[t] + 2 - jb->window;"),
     "gqa_modulo": ("int g = h / group;", "int g = h % jb->nkv;"),
     "rope_sign": ("x[i + h] = (a * sn + b * c) * s;", "x[i + h] = (b * c - a * sn) * s;"),
     "rope_interleaved": ("double a = x[i], b = x[i + h];", "double a = x[2 * i], b = x[2 * i + 1];"),
@@ -437,7 +482,7 @@ def _pins_pass():
               test_rmsnorm_worked_example_and_styles, test_rmsnorm_unit_rms_then_rope_order,
               lambda: test_brute_force_matrix_softmax(5, 7), test_gqa_equals_mha_with_repeated_kv,
               test_attention_head_uniform_page_example, test_bf16_rounding_matches_torch_on_float32_values,
-              test_head_importance_mass_and_special_cases]
+              test_head_importance_mass_and_special_cases, test_sliding_window_special_cases]
     for c in checks:
         try:
             c()
