@@ -80,11 +80,10 @@ def recorded_traffic(workload):
 
 def step_flops(w, run, i):
     """Algorithmic causal FLOPs of one chunk call: 4*hd per (row, head, key)."""
+    from chunked_prefill_causal_rope_amd import workloads as wl
     b = run.steps[i]["batch"]
-    tot = 0
-    for s, n in zip(b.starts, b.lens):
-        # rows at positions s..s+n-1 see p+1 keys each
-        tot += n * s + n * (n + 1) // 2
+    # rows at positions s..s+n-1 see p+1 keys each (at most window)
+    tot = sum(wl.keys_read(s, n, w.window) for s, n in zip(b.starts, b.lens))
     return 4.0 * w.head_dim * w.n_heads * tot
 
 
@@ -242,7 +241,8 @@ def bench_prefill(torch, w, args, stream):
     cfg = {"workload": w.name, "n_heads": w.n_heads, "n_kv": w.n_kv, "head_dim": w.head_dim,
            "n_seq": w.n_seq, "tokens": sum(d["lengths"]), "chunk": w.chunk,
            "chunks": n_steps, "rotary_dim": w.rd, "yarn": w.yarn is not None,
-           "qk_norm": bool(w.norm_style), "graph": not args.eager}
+           "qk_norm": bool(w.norm_style), "graph": not args.eager,
+           **({"window": w.window} if w.window else {})}
     out = {"metric": METRIC, "value": round(value, 3), "unit": "TFLOP/s", "n_gpus": 1,
            "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(sec * 1e3, 4),
            "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
@@ -252,7 +252,9 @@ def bench_prefill(torch, w, args, stream):
 
 
 def decode_bytes(w, ctx):
-    kv = 2.0 * sum(ctx) * w.n_kv * w.head_dim * 2
+    # K and V of the keys read (the last `window` with a window); the
+    # probability rows are written whole (zeros before the window)
+    kv = 2.0 * sum(min(c, w.window) if w.window > 0 else c for c in ctx) * w.n_kv * w.head_dim * 2
     probs = 4.0 * sum(ctx) * w.n_heads if w.want_probs else 0.0
     small = len(ctx) * w.n_heads * w.head_dim * (2 + 4)
     return kv, kv + probs + small
@@ -278,7 +280,7 @@ def bench_decode(torch, w, args, stream):
            "ms_per_step": round(sec * 1e3, 4), "workload": w.name,
            "config": {"n_seq": w.n_seq, "n_heads": w.n_heads, "n_kv": w.n_kv,
                       "head_dim": w.head_dim, "ctx_total": sum(d["ctx"]),
-                      "probs": w.want_probs},
+                      "probs": w.want_probs, **({"window": w.window} if w.window else {})},
            "roofline": roof}
     if w.want_probs:
         # per-position importance of the step (sum over heads of the

@@ -51,11 +51,11 @@ def lib() -> ctypes.CDLL:
                                  d, vp]
     L.attn_rope_qkv.argtypes = [vp, vp, i, vp, vp, vp, vp, i, i, i, i, i, i, vp, vp, i, i, vp, i, f,
                                 i, vp, vp, d, vp]
-    L.attn_prefill_chunk.argtypes = [vp, vp, vp, i, i, i, i, i, i, i, vp, vp, i, i, f, vp, vp, sz,
-                                     vp]
+    L.attn_prefill_chunk.argtypes = [vp, vp, vp, i, i, i, i, i, i, i, vp, vp, i, i, f, i, vp, vp,
+                                     sz, vp]
     L.attn_prefill_workspace_bytes.argtypes = [i, i, i, i, i, i, i]
     L.attn_prefill_workspace_bytes.restype = sz
-    L.attn_decode.argtypes = [vp, vp, vp, i, i, i, i, i, i, vp, i, f, vp, vp, i, vp, sz, vp]
+    L.attn_decode.argtypes = [vp, vp, vp, i, i, i, i, i, i, vp, i, f, i, vp, vp, i, vp, sz, vp]
     L.attn_decode_workspace_bytes.argtypes = [i, i, i, i, i]
     L.attn_decode_importance.argtypes = [vp, i, i, i, vp, i, vp, i, i, vp]
     L.attn_decode_importance.restype = i
@@ -202,7 +202,9 @@ def prefill_workspace_bytes(batch: Batch, n_heads: int, n_kv: int, head_dim: int
 
 
 def prefill_chunk(q: torch.Tensor, k_cache: torch.Tensor, v_cache: torch.Tensor, batch: Batch,
-                  scale: float, out: torch.Tensor, workspace: torch.Tensor | None = None):
+                  scale: float, out: torch.Tensor, workspace: torch.Tensor | None = None,
+                  window: int = 0):
+    """Causal attention of a chunk batch; window > 0 keeps keys p-window+1..p."""
     n_tok, nh, hd = q.shape
     n_seq_c, n_kv, cap, hd2 = k_cache.shape
     assert hd2 == hd and out.shape == (n_tok, nh, hd) and out.dtype == torch.float32
@@ -212,7 +214,7 @@ def prefill_chunk(q: torch.Tensor, k_cache: torch.Tensor, v_cache: torch.Tensor,
     st = lib().attn_prefill_chunk(
         _dev(q, "q"), _dev(k_cache, "k_cache"), _dev(v_cache, "v_cache"), _dtype_code(q),
         batch.n_seq, nh, n_kv, hd, cap, n_tok, _dev(batch.cu_seq, "cu_seq", torch.int32),
-        _dev(batch.start, "start", torch.int32), batch.max_chunk, batch.max_end, scale,
+        _dev(batch.start, "start", torch.int32), batch.max_chunk, batch.max_end, scale, window,
         _dev(out, "out"), ws, wsb, _stream())
     _check("attn_prefill_chunk", st)
 
@@ -234,7 +236,8 @@ def decode_importance(probs: torch.Tensor, ctx: torch.Tensor, max_ctx: int, imp:
 
 def decode(q: torch.Tensor, k_cache: torch.Tensor, v_cache: torch.Tensor, ctx: torch.Tensor,
            max_ctx: int, scale: float, out: torch.Tensor, probs: torch.Tensor | None = None,
-           workspace: torch.Tensor | None = None):
+           workspace: torch.Tensor | None = None, window: int = 0):
+    """One-query attention over ctx[b] keys; window > 0 keeps the last window keys."""
     n_seq, nh, hd = q.shape
     n_seq_c, n_kv, cap, hd2 = k_cache.shape
     assert hd2 == hd and n_seq_c >= n_seq and out.shape == (n_seq, nh, hd)
@@ -247,6 +250,6 @@ def decode(q: torch.Tensor, k_cache: torch.Tensor, v_cache: torch.Tensor, ctx: t
     wsb = workspace.numel() * workspace.element_size() if workspace is not None else 0
     st = lib().attn_decode(
         _dev(q, "q"), _dev(k_cache, "k_cache"), _dev(v_cache, "v_cache"), _dtype_code(q), n_seq,
-        nh, n_kv, hd, cap, _dev(ctx, "ctx"), max_ctx, scale, _dev(out, "out"),
+        nh, n_kv, hd, cap, _dev(ctx, "ctx"), max_ctx, scale, window, _dev(out, "out"),
         _dev(probs, "probs"), ld, ws, wsb, _stream())
     _check("attn_decode", st)

@@ -5,8 +5,10 @@
 // cortiq-engine 0.5.39 src/attention.rs, fn attention_head: scores
 // q.K_j * scale over the stored keys, max-subtracted softmax, probabilities
 // returned; the batched causal attend of fn qwen_attention_batch limits row bi
-// to keys < s0+bi+1.  Keys are taken 64 at a time (one per lane) with an
-// online maximum; each lane owns head_dim/64 output dims for the P.V sum.
+// to keys < s0+bi+1; with a sliding window (QwenAttnCfg.window) a row reads
+// only its last `window` keys.  Keys are taken 64 at a time (one per lane)
+// with an online maximum; each lane owns head_dim/64 output dims for the P.V
+// sum.
 #include "device_common.h"
 #include "launch.h"
 
@@ -55,6 +57,8 @@ __global__ __launch_bounds__(256) void attend_f32_kernel(AttendF32Args a) {
     const float* kc = a.k_cache + base;
     const float* vc = a.v_cache + base;
     const int n = pos + 1;
+    // first key of the row's window (0 without one)
+    const int first = a.window > 0 && n > a.window ? n - a.window : 0;
     const float sl = a.scale * kLog2e;
 
     auto score = [&](int j) -> float {
@@ -74,7 +78,7 @@ __global__ __launch_bounds__(256) void attend_f32_kernel(AttendF32Args a) {
     float o[PER];
 #pragma unroll
     for (int e = 0; e < PER; ++e) o[e] = 0.f;
-    for (int j0 = 0; j0 < n; j0 += 64) {
+    for (int j0 = first; j0 < n; j0 += 64) {
         const int j = j0 + lane;
         const float x = j < n ? score(j) : -INFINITY;
         const float m_new = fmaxf(m, wave_max(x));
@@ -99,7 +103,7 @@ __global__ __launch_bounds__(256) void attend_f32_kernel(AttendF32Args a) {
 
     if (a.decode && a.probs) {
         float* prow = a.probs + ((size_t)b * a.n_heads + h) * a.probs_ld;
-        for (int j = lane; j < n; j += 64) prow[j] = exp2f(score(j) - m) * inv;
+        for (int j = lane; j < n; j += 64) prow[j] = j < first ? 0.f : exp2f(score(j) - m) * inv;
     }
 }
 

@@ -215,18 +215,18 @@ size_t attn_prefill_workspace_bytes(int n_seq, int n_heads, int n_kv, int head_d
     if (n_seq <= 0 || n_heads <= 0 || n_kv <= 0 || n_heads % n_kv || n_tok <= 0 || max_chunk <= 0 ||
         max_end <= 0 || !hd_ok(head_dim))
         return 0;
-    return attn::plan_prefill(n_seq, n_heads, n_kv, head_dim, n_tok, max_chunk, max_end,
+    return attn::plan_prefill(n_seq, n_heads, n_kv, head_dim, n_tok, max_chunk, max_end, 0,
                               (size_t)-1).ws_bytes;
 }
 
 int attn_prefill_chunk(const void* q, const void* k_cache, const void* v_cache, int dtype,
                        int n_seq, int n_heads, int n_kv, int head_dim, int cap, int n_tok,
                        const int32_t* cu_seq, const int32_t* start, int max_chunk, int max_end,
-                       float scale, float* out, void* workspace, size_t workspace_bytes,
-                       void* stream) {
+                       float scale, int window, float* out, void* workspace,
+                       size_t workspace_bytes, void* stream) {
     if (!dtype_ok(dtype) || !hd_ok(head_dim)) return ATTN_EUNSUPPORTED;
     if (n_seq < 0 || n_tok < 0 || max_chunk < 0 || max_end < 0 || n_heads <= 0 || n_kv <= 0 ||
-        cap <= 0 || n_heads % n_kv != 0 || !isfinite(scale))
+        cap <= 0 || n_heads % n_kv != 0 || !isfinite(scale) || window < 0)
         return ATTN_EINVAL;
     if (max_end > cap) return ATTN_ECAPACITY;
     if (n_seq == 0 || n_tok == 0 || max_chunk == 0) return ATTN_OK;
@@ -252,6 +252,7 @@ int attn_prefill_chunk(const void* q, const void* k_cache, const void* v_cache, 
         a.cap = cap;
         a.n_tok = n_tok;
         a.max_chunk = max_chunk;
+        a.window = window;
         return status_of(attn::launch_attend_f32(a, s));
     }
     attn::PrefillArgs a{};
@@ -271,8 +272,9 @@ int attn_prefill_chunk(const void* q, const void* k_cache, const void* v_cache, 
     a.n_tok = n_tok;
     a.max_chunk = max_chunk;
     a.max_end = max_end;
+    a.window = window;
     const attn::PrefillPlan plan = attn::plan_prefill(n_seq, n_heads, n_kv, head_dim, n_tok,
-                                                      max_chunk, max_end,
+                                                      max_chunk, max_end, window,
                                                       workspace ? workspace_bytes : 0);
     a.rows_per_tile = plan.rows_per_tile;
     a.n_qtiles = plan.n_qtiles;
@@ -298,11 +300,11 @@ size_t attn_decode_workspace_bytes(int n_seq, int n_heads, int n_kv, int head_di
 
 int attn_decode(const void* q, const void* k_cache, const void* v_cache, int dtype, int n_seq,
                 int n_heads, int n_kv, int head_dim, int cap, const int32_t* ctx, int max_ctx,
-                float scale, float* out, float* probs, int probs_ld, void* workspace,
+                float scale, int window, float* out, float* probs, int probs_ld, void* workspace,
                 size_t workspace_bytes, void* stream) {
     if (!dtype_ok(dtype) || !hd_ok(head_dim)) return ATTN_EUNSUPPORTED;
     if (n_seq < 0 || max_ctx < 0 || n_heads <= 0 || n_kv <= 0 || cap <= 0 ||
-        n_heads % n_kv != 0 || !isfinite(scale))
+        n_heads % n_kv != 0 || !isfinite(scale) || window < 0)
         return ATTN_EINVAL;
     if (max_ctx > cap) return ATTN_ECAPACITY;
     if (n_seq == 0 || max_ctx == 0) return ATTN_OK;
@@ -329,17 +331,20 @@ int attn_decode(const void* q, const void* k_cache, const void* v_cache, int dty
         a.n_tok = n_seq;
         a.max_ctx = max_ctx;
         a.probs_ld = probs_ld;
+        a.window = window;
         return status_of(attn::launch_attend_f32(a, s));
     }
     if (group > attn::decode_group_limit()) return ATTN_EUNSUPPORTED;
     const size_t per = decode_part_bytes(n_seq, n_heads, head_dim, 1);
     if (!workspace || workspace_bytes < per) return ATTN_EINVAL;
-    int splits = decode_splits_full(max_ctx, group);
+    // a window bounds the keys any row reads
+    const int span = attn::decode_key_span(max_ctx, window);
+    int splits = decode_splits_full(span, group);
     const size_t fit = workspace_bytes / per;
     if ((size_t)splits > fit) splits = (int)fit;
-    int split_len = (max_ctx + splits - 1) / splits;
+    int split_len = (span + splits - 1) / splits;
     split_len = (split_len + 63) / 64 * 64;
-    splits = (max_ctx + split_len - 1) / split_len;
+    splits = (span + split_len - 1) / split_len;
     attn::DecodeArgs a{};
     a.q = q;
     a.k_cache = k_cache;
@@ -359,6 +364,7 @@ int attn_decode(const void* q, const void* k_cache, const void* v_cache, int dty
     a.probs_ld = probs ? probs_ld : 0;
     a.split_len = split_len;
     a.n_splits = splits;
+    a.window = window;
     if ((long)n_seq * splits * n_kv > 0x7fffffffL) return ATTN_EINVAL;
     return status_of(attn::launch_decode_bf16(a, s));
 }

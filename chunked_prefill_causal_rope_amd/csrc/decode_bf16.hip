@@ -32,6 +32,8 @@
 //    matters because writes among the K/V read stream cost far more than
 //    their size.  The combine kernel merges the parts with log-sum-exp and
 //    widens each row in place to the normalised float probabilities.
+#include <algorithm>
+
 #include "device_common.h"
 #include "launch.h"
 
@@ -45,6 +47,20 @@ constexpr float kDecSlack = 8.f;
 constexpr int kDecPartFloats = 4096;
 
 int decode_group_limit() { return kDecMaxGroup; }
+
+// Sliding window: a row reads keys [ctx - W, ctx).  The parts start at that
+// first key rounded down to a step, so they begin on a step (and a 16-byte
+// boundary of the half-precision rows) and the first step holds a key of the
+// window; the keys between the part start and the window are masked.
+__host__ __device__ constexpr int decode_window_first(int ctx, int window) {
+    return window > 0 && ctx > window ? ctx - window : 0;
+}
+__host__ __device__ constexpr int decode_part_base(int ctx, int window) {
+    return decode_window_first(ctx, window) / kDecKB * kDecKB;
+}
+int decode_key_span(int max_ctx, int window) {
+    return window > 0 && window < max_ctx ? std::min(window + kDecKB - 1, max_ctx) : max_ctx;
+}
 
 // Heads handled per KV group by the kernel instance (4, 8 or 16); with
 // probabilities a part holds at most kDecPartFloats / that many keys.
@@ -176,7 +192,8 @@ __global__ __launch_bounds__(64) void decode_split_kernel(DecodeArgs a) {
     const int b = id / a.n_splits;
     if (b >= a.n_seq) return;
     const int ctx = min(min(a.ctx[b], a.max_ctx), a.cap);
-    const int k_lo = s * a.split_len;
+    const int k_first = decode_window_first(ctx, a.window);
+    const int k_lo = decode_part_base(ctx, a.window) + s * a.split_len;
     const int k_hi = min(k_lo + a.split_len, ctx);
     if (k_lo >= k_hi) return;
     const int G = a.group;
@@ -262,7 +279,8 @@ __global__ __launch_bounds__(64) void decode_split_kernel(DecodeArgs a) {
             f32x4_t S = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
             for (int k = 0; k < NK; ++k) S = mfma16(qa[k], __builtin_bit_cast(bf16x8_t, kf[buf][blk][k]), S);
-            const bool ok = k0 + 16 * blk + col < k_hi;
+            const int key = k0 + 16 * blk + col;
+            const bool ok = key < k_hi && key >= k_first;
 #pragma unroll
             for (int r = 0; r < HPL; ++r) x[blk][r] = ok ? S[r] * sl : -INFINITY;
         }
@@ -270,7 +288,7 @@ __global__ __launch_bounds__(64) void decode_split_kernel(DecodeArgs a) {
         float mt[HPL];
 #pragma unroll
         for (int r = 0; r < HPL; ++r) {
-            mt[r] = row16_max(fmaxf(x[0][r], x[1][r]));   // finite: key k0 is in range
+            mt[r] = row16_max(fmaxf(x[0][r], x[1][r]));   // finite in a part's first step
             grow_any |= mt[r] > m_run[r] + kDecSlack;
         }
         if (__any(grow_any)) {
@@ -430,7 +448,9 @@ __global__ __launch_bounds__(256) void decode_combine_kernel(DecodeArgs a) {
         return;
     }
     constexpr int PS = HD + kPartPadD;
-    const int n_parts = min((ctx + a.split_len - 1) / a.split_len, a.n_splits);
+    const int k_first = decode_window_first(ctx, a.window);
+    const int k_base = decode_part_base(ctx, a.window);
+    const int n_parts = min((ctx - k_base + a.split_len - 1) / a.split_len, a.n_splits);
     const float* pr = a.part + (size_t)row * a.n_splits * PS;
     float mm = -INFINITY;
     for (int s = tid; s < n_parts; s += 256) mm = fmaxf(mm, pr[(size_t)s * PS]);
@@ -476,11 +496,13 @@ __global__ __launch_bounds__(256) void decode_combine_kernel(DecodeArgs a) {
     }
     if (a.probs) {
         // P_j = h_j 2^(m_s - m) / l_h, h_j the half-precision value part s
-        // (keys [s*split_len, ...)) left at 16-bit word j of the row.  The
-        // row is widened in place, in blocks of 2048 keys from the top down:
-        // float j covers words 2j and 2j+1, which belong to keys at or above
-        // j, so a block's writes only reach words of its own keys (read into
-        // registers before the barrier) or of blocks already done.
+        // (keys [k_base + s*split_len, ...)) left at 16-bit word j of the
+        // row; keys before the window get 0.  The row is widened in place,
+        // in blocks of 2048 keys from the top down: float j covers words 2j
+        // and 2j+1, which belong to keys at or above j, so a block's writes
+        // only reach words of its own keys (read into registers before the
+        // barrier) or of blocks already done.  Part bounds are multiples of
+        // 8 keys, so 8 consecutive keys share one part.
         float* prow = a.probs + (size_t)row * a.probs_ld;
         const uint16_t* hrow = reinterpret_cast<const uint16_t*>(prow);
         typedef uint32_t u32x4_a4_t __attribute__((ext_vector_type(4), aligned(4)));
@@ -489,8 +511,11 @@ __global__ __launch_bounds__(256) void decode_combine_kernel(DecodeArgs a) {
         for (int lo = (ctx - 1) / BLK * BLK; lo >= 0; lo -= BLK) {
             const int k = lo + 8 * tid;
             float v[8];
-            if (k < ctx) {
-                const float f = __builtin_amdgcn_exp2f(pr[(size_t)(k / a.split_len) * PS] - m) * inv_h;
+            if (k + 8 <= k_base) {
+#pragma unroll
+                for (int e = 0; e < 8; ++e) v[e] = 0.f;
+            } else if (k < ctx) {
+                const float f = __builtin_amdgcn_exp2f(pr[(size_t)((k - k_base) / a.split_len) * PS] - m) * inv_h;
                 if (k + 8 <= ctx) {
                     const u32x4_a4_t w = *reinterpret_cast<const u32x4_a4_t*>(hrow + k);
 #pragma unroll
@@ -499,6 +524,9 @@ __global__ __launch_bounds__(256) void decode_combine_kernel(DecodeArgs a) {
 #pragma unroll
                     for (int e = 0; e < 8; ++e) v[e] = k + e < ctx ? f16_value(hrow[k + e]) * f : 0.f;
                 }
+#pragma unroll
+                for (int e = 0; e < 8; ++e)
+                    if (k + e < k_first) v[e] = 0.f;
             }
             __syncthreads();
             if (k < ctx) {

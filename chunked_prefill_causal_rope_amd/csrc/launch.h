@@ -39,6 +39,7 @@ struct PrefillArgs {
     const int32_t* start;
     float scale;
     int n_seq, n_heads, n_kv, group, head_dim, cap, n_tok, max_chunk, max_end;
+    int window;            // 0: all keys <= p; W: keys p-W+1..p
     // rows per workgroup, row tiles per sequence, split call (persistent
     // grid with device-chosen key-range parts, merged by the combine kernel)
     int rows_per_tile, n_qtiles, split, grid, slots;
@@ -51,7 +52,7 @@ struct PrefillPlan {
     size_t ws_bytes, table_bytes;
 };
 PrefillPlan plan_prefill(int n_seq, int n_heads, int n_kv, int head_dim, int n_tok, int max_chunk,
-                         int max_end, size_t ws_available);
+                         int max_end, int window, size_t ws_available);
 hipError_t launch_prefill_bf16(const PrefillArgs& a, hipStream_t stream);
 hipError_t launch_prefill_combine(const PrefillArgs& a, hipStream_t stream);
 
@@ -68,6 +69,7 @@ struct AttendF32Args {
     float scale;
     int decode;
     int n_seq, n_heads, n_kv, group, head_dim, cap, n_tok, max_chunk, max_ctx, probs_ld;
+    int window;            // 0: all keys <= p; W: keys p-W+1..p
 };
 hipError_t launch_attend_f32(const AttendF32Args& a, hipStream_t stream);
 
@@ -82,9 +84,13 @@ struct DecodeArgs {
     const int32_t* ctx;
     float scale;
     int n_seq, n_heads, n_kv, group, head_dim, cap, max_ctx, probs_ld;
-    int split_len, n_splits;
+    int split_len, n_splits;   // parts of split_len keys from the row's first key
+    int window;                // 0: all ctx keys; W: the last W
 };
 int decode_group_limit();
+// Keys one decode row may read, from its part start on: max_ctx, or with a
+// window W the W keys plus the alignment of the first part's start.
+int decode_key_span(int max_ctx, int window);
 // Longest key range one decode part may cover (a multiple of 64).
 int decode_part_limit(int group, bool probs);
 hipError_t launch_decode_bf16(const DecodeArgs& a, hipStream_t stream);

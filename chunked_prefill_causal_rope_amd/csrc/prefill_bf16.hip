@@ -34,6 +34,8 @@
 //    range is split and the parts are merged by a log-sum-exp combine.
 //  * blockIdx -> (group, split, row tile, sequence) with the group fastest,
 //    so with 8 KV groups every XCD streams one group's K/V from its own L2.
+#include <algorithm>
+#include <climits>
 #include <type_traits>
 
 #include "device_common.h"
@@ -127,6 +129,13 @@ __host__ __device__ constexpr int min_tiles_per_split(int rows_per_tile) {
     return rows_per_tile == 256 ? ATTN_PREFILL_MIN_TILES_256 : ATTN_PREFILL_MIN_TILES_128;
 }
 
+// First key tile a row tile reads: with a sliding window of W keys its
+// first row (position p_first) starts at key p_first - W + 1, and every later
+// row of the tile starts at or after it.
+__host__ __device__ constexpr int first_key_tile(int p_first, int window) {
+    return window > 0 && p_first >= window ? (p_first - window + 1) / kTK : 0;
+}
+
 // key tiles of row tile qt of sequence b (0 if the row tile is empty)
 __device__ __forceinline__ int group_tiles(const PrefillArgs& a, int b, int qt) {
     const int t0 = a.cu_seq[b];
@@ -137,7 +146,8 @@ __device__ __forceinline__ int group_tiles(const PrefillArgs& a, int b, int qt) 
     if (len <= 0 || p0 < 0 || r0 >= rows_b) return 0;
     const int r_last = min(r0 + a.rows_per_tile, rows_b) - 1;
     const int n_keys = min(p0 + r_last / a.group + 1, a.cap);
-    return (n_keys + kTK - 1) / kTK;
+    const int n_tiles = (n_keys + kTK - 1) / kTK;
+    return n_tiles - min(first_key_tile(p0 + r0 / a.group, a.window), n_tiles);
 }
 
 struct PrefillItem {
@@ -224,8 +234,9 @@ __device__ PrefillItem split_schedule(const PrefillArgs& a, int item) {
 // NW waves of 32 query rows each share every K/V tile.  With 8 waves each
 // thread stages half a tile's worth of K and V, which leaves room for two
 // staging sets: the global loads of a tile are then issued two tiles before
-// they are stored to LDS (PD = 2) instead of one.
-template <int HD, int NW>
+// they are stored to LDS (PD = 2) instead of one.  WIN: the call has a
+// sliding window (only that instance carries the lower mask).
+template <int HD, int NW, bool WIN>
 __global__ __launch_bounds__(NW * 64, 8 / NW) void prefill_bf16_kernel(PrefillArgs a) {
     using Sm = PrefillSmem<HD>;
     constexpr int kThreads = NW * 64;
@@ -274,9 +285,11 @@ __global__ __launch_bounds__(NW * 64, 8 / NW) void prefill_bf16_kernel(PrefillAr
     const int r_last = min(r_tile0 + TILE_ROWS, rows_b) - 1;
     const int n_keys = min(p0 + r_last / G + 1, a.cap);
     const int n_tiles = (n_keys + kTK - 1) / kTK;
-    // this item's part of the row tile's key tiles, parts of equal length
-    const int per = (n_tiles + nsp - 1) / nsp;
-    const int tb = s * per;
+    // this item's part of the row tile's key tiles (from the first one its
+    // window reaches), parts of equal length
+    const int t_first = WIN ? min(first_key_tile(p0 + r_tile0 / G, a.window), n_tiles) : 0;
+    const int per = (n_tiles - t_first + nsp - 1) / nsp;
+    const int tb = t_first + s * per;
     const int te = min(tb + per, n_tiles);
 
     // this lane's query row (position-major within the group) and its wave's
@@ -288,6 +301,9 @@ __global__ __launch_bounds__(NW * 64, 8 / NW) void prefill_bf16_kernel(PrefillAr
     const int pos = row_ok ? p0 + i : -1;
     const int rw0 = r_tile0 + wave * 32;
     const int pw_lo = p0 + rw0 / G;
+    // a key tile below key pw_hi - W + 1 misses the window of some row of
+    // the wave (pw_hi bounds the wave's positions from above)
+    const int win_lo = WIN ? p0 + (rw0 + 31) / G - a.window + 1 : INT_MIN;
 
     bf16x8_t qf[NKK];
     {
@@ -415,6 +431,16 @@ __global__ __launch_bounds__(NW * 64, 8 / NW) void prefill_bf16_kernel(PrefillAr
                     const int off = 8 * (q >> 2) + (q & 3);
                     if (off > lim) S0[q] = -INFINITY;
                     if (off + 32 > lim) S1[q] = -INFINITY;
+                }
+            }
+            // ---- sliding window: keys below pos - W + 1
+            if (WIN && k0 < win_lo) {
+                const int llim = pos - a.window + 1 - k0 - 4 * hf;
+#pragma unroll
+                for (int q = 0; q < 16; ++q) {
+                    const int off = 8 * (q >> 2) + (q & 3);
+                    if (off < llim) S0[q] = -INFINITY;
+                    if (off + 32 < llim) S1[q] = -INFINITY;
                 }
             }
 
@@ -677,10 +703,13 @@ static int device_cus() {
 }
 
 PrefillPlan plan_prefill(int n_seq, int n_heads, int n_kv, int head_dim, int n_tok, int max_chunk,
-                         int max_end, size_t ws_available) {
+                         int max_end, int window, size_t ws_available) {
     const long group = n_heads / n_kv;
     const long rows = (long)max_chunk * group;
-    const long tiles = ((long)max_end + kTK - 1) / kTK;
+    long tiles = ((long)max_end + kTK - 1) / kTK;
+    // a window bounds a row tile's key range by W plus its own positions
+    // (at most 256 rows) and the alignment of both ends
+    if (window > 0) tiles = std::min(tiles, ((long)window + 256 + 2 * kTK - 2) / kTK + 1);
     const long big = (long)n_seq * ((rows + 255) / 256) * n_kv;
     PrefillPlan p{};
     p.rows_per_tile = big >= kBigTileBlocks / 2 ? 256 : 128;
@@ -716,7 +745,8 @@ PrefillPlan plan_prefill(int n_seq, int n_heads, int n_kv, int head_dim, int n_t
                     if (len > 0 && p0 >= 0 && r0 < rows_b) {
                         const long r_last = (r0 + p.rows_per_tile < rows_b ? r0 + p.rows_per_tile : rows_b) - 1;
                         const long nk = p0 + r_last / group + 1;
-                        gt[qt] = (nk + kTK - 1) / kTK;
+                        const long nt = (nk + kTK - 1) / kTK;
+                        gt[qt] = nt - std::min((long)first_key_tile((int)(p0 + r0 / group), window), nt);
                     }
                     if (gt[qt] > gmax) gmax = gt[qt];
                 }
@@ -744,17 +774,25 @@ PrefillPlan plan_prefill(int n_seq, int n_heads, int n_kv, int head_dim, int n_t
     return p;
 }
 
+template <bool WIN>
+static void launch_prefill_win(const PrefillArgs& a, dim3 grid, hipStream_t stream) {
+    if (a.rows_per_tile == 256) {
+        if (a.head_dim == 128) prefill_bf16_kernel<128, 8, WIN><<<grid, dim3(512), 0, stream>>>(a);
+        else prefill_bf16_kernel<64, 8, WIN><<<grid, dim3(512), 0, stream>>>(a);
+    } else {
+        if (a.head_dim == 128) prefill_bf16_kernel<128, 4, WIN><<<grid, dim3(256), 0, stream>>>(a);
+        else prefill_bf16_kernel<64, 4, WIN><<<grid, dim3(256), 0, stream>>>(a);
+    }
+}
+
 hipError_t launch_prefill_bf16(const PrefillArgs& a, hipStream_t stream) {
     const long blocks = a.grid;
     if (blocks <= 0) return hipSuccess;
     const dim3 grid((unsigned)blocks);
-    if (a.rows_per_tile == 256) {
-        if (a.head_dim == 128) prefill_bf16_kernel<128, 8><<<grid, dim3(512), 0, stream>>>(a);
-        else prefill_bf16_kernel<64, 8><<<grid, dim3(512), 0, stream>>>(a);
-    } else {
-        if (a.head_dim == 128) prefill_bf16_kernel<128, 4><<<grid, dim3(256), 0, stream>>>(a);
-        else prefill_bf16_kernel<64, 4><<<grid, dim3(256), 0, stream>>>(a);
-    }
+    if (a.window > 0)
+        launch_prefill_win<true>(a, grid, stream);
+    else
+        launch_prefill_win<false>(a, grid, stream);
     return hipGetLastError();
 }
 

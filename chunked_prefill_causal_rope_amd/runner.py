@@ -99,7 +99,7 @@ class ChunkedPrefill:
     def attend_step(self, i: int):
         s = self.steps[i]
         api.prefill_chunk(s["q_rot"], self.k_cache, self.v_cache, s["batch"], self.w.scale,
-                          s["out"], self.workspace)
+                          s["out"], self.workspace, window=self.w.window)
 
     def run_all(self, fused: bool = True):
         for i in range(len(self.steps)):
@@ -157,7 +157,7 @@ class DecodeStep:
 
     def attend(self):
         api.decode(self.q_rot, self.k_cache, self.v_cache, self.ctx, self.max_ctx, self.w.scale,
-                   self.out, self.probs, self.workspace)
+                   self.out, self.probs, self.workspace, window=self.w.window)
 
     def run(self):
         self.finish_and_append()

@@ -36,6 +36,7 @@ class Workload:
     rope_scale: float = 1.0
     norm_style: int = NORM_NONE
     norm_eps: float = 1e-6
+    window: int = 0                        # 0: full causal; W: the last W keys only
     # prefill
     n_seq: int = 1
     prompt_len: int = 0                    # fixed length when len_range is None
@@ -86,6 +87,11 @@ CONFIGS = {
         base=1e6, yarn=(4.0, 32768, 32.0, 1.0), rope_scale=0.1 * math.log(4.0) + 1.0,
         prompt_len=131072, chunk=2048),
 }
+# Sliding-window variants (keys p-W+1..p, W = 4096) of the long prefill and
+# of the decode batch.
+CONFIGS["c4_yarn_128k_sw4096"] = CONFIGS["c4_yarn_128k"].replace(name="c4_yarn_128k_sw4096",
+                                                                 window=4096)
+CONFIGS["c2_decode_sw4096"] = CONFIGS["c2_decode"].replace(name="c2_decode_sw4096", window=4096)
 
 
 def _gen(seed: int, device) -> torch.Generator:
@@ -166,7 +172,15 @@ def chunk_schedule(lengths: list[int], chunk: int) -> list[list[tuple[int, int, 
     return steps
 
 
+def keys_read(start: int, n: int, window: int = 0) -> int:
+    """Unmasked (row, key) pairs of rows at positions start..start+n-1: row p
+    reads p+1 keys, or min(p+1, window) with a window."""
+    end = start + n
+    lo = end if window <= 0 else min(max(window, start), end)   # rows >= lo read `window` keys
+    return (lo * (lo + 1) - start * (start + 1)) // 2 + (end - lo) * max(window, 0)
+
+
 def prefill_flops(w: Workload, lengths: list[int]) -> float:
     """Algorithmic causal attention FLOPs: 4*hd per (row, head, unmasked key);
-    row p has p+1 keys."""
-    return float(sum(4 * w.head_dim * w.n_heads * n * (n + 1) // 2 for n in lengths))
+    row p has p+1 keys (min(p+1, window) with a window)."""
+    return float(sum(4 * w.head_dim * w.n_heads * keys_read(0, n, w.window) for n in lengths))

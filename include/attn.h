@@ -175,22 +175,27 @@ int attn_rope_qkv(const void *q, void *q_out, int n_heads, void *k_cache, void *
  *   q        device [n_tok][n_heads][head_dim] (rotated), read
  *   out      device float[n_tok][n_heads][head_dim], written
  *   scale    the score scale, normally 1/sqrt(head_dim)
+ *   window   0: every key <= p; W > 0: a sliding window, keys
+ *            max(0, p-W+1)..p only ([ATT] QwenAttnCfg.window, "attend only
+ *            the last N positions").  The cache still holds every position.
  *   workspace device scratch of workspace_bytes (may be NULL/0); with less
  *            than attn_prefill_workspace_bytes() the key range is split into
  *            fewer parts (never an error).  Contents need no initialisation
  *            and are clobbered.  Calls that share a workspace must be ordered
  *            on one stream.
- * Errors: ECAPACITY if max_end > cap; EINVAL, EUNSUPPORTED, EDEVICE.
+ * Errors: ECAPACITY if max_end > cap; EINVAL (window < 0, ...), EUNSUPPORTED,
+ * EDEVICE.
  */
 int attn_prefill_chunk(const void *q, const void *k_cache, const void *v_cache, int dtype,
                        int n_seq, int n_heads, int n_kv, int head_dim, int cap, int n_tok,
                        const int32_t *cu_seq, const int32_t *start, int max_chunk, int max_end,
-                       float scale, float *out, void *workspace, size_t workspace_bytes,
-                       void *stream);
+                       float scale, int window, float *out, void *workspace,
+                       size_t workspace_bytes, void *stream);
 
 /*
  * Workspace that lets attn_prefill_chunk split the key range as far as it
- * chooses for these sizes (bytes; 0 when it would not split).
+ * chooses for these sizes (bytes; 0 when it would not split).  Enough for any
+ * window.
  */
 size_t attn_prefill_workspace_bytes(int n_seq, int n_heads, int n_kv, int head_dim, int n_tok,
                                     int max_chunk, int max_end);
@@ -207,6 +212,9 @@ size_t attn_prefill_workspace_bytes(int n_seq, int n_heads, int n_kv, int head_d
  *   q      device [n_seq][n_heads][head_dim] (rotated), read
  *   ctx    device int32[n_seq], 1 <= ctx[b] <= max_ctx (values above max_ctx
  *          are clamped to it; a row with ctx[b] < 1 gets zeros)
+ *   window 0: all ctx[b] keys; W > 0: only the last W (a sliding window,
+ *          [ATT] the decode loop starts at stored - window); the
+ *          probabilities of the keys before it are written as 0
  *   out    device float[n_seq][n_heads][head_dim], written
  *   probs  NULL, or device float[n_seq][n_heads][probs_ld]; row (b, h) gets
  *          ctx[b] entries summing to 1, entries past ctx[b] are not written.
@@ -221,13 +229,13 @@ size_t attn_prefill_workspace_bytes(int n_seq, int n_heads, int n_kv, int head_d
  *          row, EINVAL below that); attn_decode_workspace_bytes() gives the
  *          size for the full split, and a smaller one means fewer, longer
  *          parts.  f32 needs none.
- * Errors: ECAPACITY if max_ctx > cap; EINVAL (probs_ld < max_ctx, ...),
- * EUNSUPPORTED (bf16 with more than 16 query heads per KV head), EDEVICE.
+ * Errors: ECAPACITY if max_ctx > cap; EINVAL (probs_ld < max_ctx, window < 0,
+ * ...), EUNSUPPORTED (bf16 with more than 16 query heads per KV head), EDEVICE.
  */
 int attn_decode(const void *q, const void *k_cache, const void *v_cache, int dtype, int n_seq,
                 int n_heads, int n_kv, int head_dim, int cap, const int32_t *ctx, int max_ctx,
-                float scale, float *out, float *probs, int probs_ld, void *workspace,
-                size_t workspace_bytes, void *stream);
+                float scale, int window, float *out, float *probs, int probs_ld,
+                void *workspace, size_t workspace_bytes, void *stream);
 
 size_t attn_decode_workspace_bytes(int n_seq, int n_heads, int n_kv, int head_dim, int max_ctx);
 

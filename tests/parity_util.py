@@ -56,7 +56,7 @@ def oracle_prefill_packed(w, d, chunk, want_probs=False):
             np64(d["q"][sl]), np64(d["k"][sl]), np64(d["v"][sl]), chunk, f, w.rd, w.scale,
             store_of(w), rope_scale=w.rope_scale,
             norm_style=qn.get("norm_style", 0), q_norm_w=qn.get("norm_w"),
-            k_norm_w=kn.get("norm_w"), eps=w.norm_eps, want_probs=want_probs)
+            k_norm_w=kn.get("norm_w"), eps=w.norm_eps, want_probs=want_probs, window=w.window)
         outs.append(r["out"])
         caches.append((r["k_cache"], r["v_cache"]))
         qrots.append(r["q_rot"])
@@ -82,7 +82,7 @@ def oracle_rows(w, d, b, positions, heads=None):
     q_raw = np64(d["q"][idx])
     q = oracle.finish_heads(q_raw, positions, f, w.rd, w.rope_scale, store=store_of(w), **qn)
     out, _ = oracle.attend(q, kc.transpose(1, 0, 2).copy(), v_raw.transpose(1, 0, 2).copy(),
-                           positions, w.scale)
+                           positions, w.scale, window=w.window)
     return positions, out
 
 

@@ -79,12 +79,12 @@ P = ctypes.c_void_p(4096)
 
 def prefill(**kw):
     a = dict(q=P, k=P, v=P, dtype=1, n_seq=1, nh=8, nkv=2, hd=128, cap=256, n_tok=16, cu=P, st=P,
-             max_chunk=16, max_end=64, scale=0.088, out=P, ws=None, wsb=0, stream=None)
+             max_chunk=16, max_end=64, scale=0.088, window=0, out=P, ws=None, wsb=0, stream=None)
     a.update(kw)
     return api.lib().attn_prefill_chunk(a["q"], a["k"], a["v"], a["dtype"], a["n_seq"], a["nh"],
                                         a["nkv"], a["hd"], a["cap"], a["n_tok"], a["cu"], a["st"],
-                                        a["max_chunk"], a["max_end"], a["scale"], a["out"],
-                                        a["ws"], a["wsb"], a["stream"])
+                                        a["max_chunk"], a["max_end"], a["scale"], a["window"],
+                                        a["out"], a["ws"], a["wsb"], a["stream"])
 
 
 def test_prefill_validation():
@@ -94,6 +94,7 @@ def test_prefill_validation():
     assert prefill(nkv=0) == EINVAL
     assert prefill(max_end=257) == ECAP
     assert prefill(scale=float("nan")) == EINVAL
+    assert prefill(window=-1) == EINVAL
     assert prefill(q=None) == EINVAL
     assert prefill(cu=None) == EINVAL
     # empty work: OK and nothing launched
@@ -146,11 +147,12 @@ def test_rope_validation():
 
 def decode(**kw):
     a = dict(q=P, k=P, v=P, dtype=1, n_seq=4, nh=32, nkv=8, hd=128, cap=4096, ctx=P, max_ctx=4096,
-             scale=0.088, out=P, probs=None, ld=0, ws=P, wsb=1 << 30)
+             scale=0.088, window=0, out=P, probs=None, ld=0, ws=P, wsb=1 << 30)
     a.update(kw)
     return api.lib().attn_decode(a["q"], a["k"], a["v"], a["dtype"], a["n_seq"], a["nh"],
                                  a["nkv"], a["hd"], a["cap"], a["ctx"], a["max_ctx"], a["scale"],
-                                 a["out"], a["probs"], a["ld"], a["ws"], a["wsb"], None)
+                                 a["window"], a["out"], a["probs"], a["ld"], a["ws"], a["wsb"],
+                                 None)
 
 
 def test_decode_validation():
@@ -161,6 +163,7 @@ def test_decode_validation():
     assert decode(ws=None, wsb=0) == EINVAL      # bf16 needs a workspace
     assert decode(wsb=16) == EINVAL
     assert decode(hd=256) == EUNSUP
+    assert decode(window=-5) == EINVAL
     assert decode(n_seq=0) == OK
     assert decode(max_ctx=0) == OK
 

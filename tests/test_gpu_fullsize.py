@@ -25,9 +25,12 @@ def _gpu():
     torch.cuda.empty_cache()
 
 
-def sample_positions(n, chunk, seed, extra=12):
+def sample_positions(n, chunk, seed, extra=12, window=0):
     rng = np.random.default_rng(seed)
     pos = {0, 1, n - 1, n - 2}
+    if window:
+        # the first rows whose window no longer reaches key 0
+        pos.update({window - 1, window, window + 1, window + 63})
     for c in (chunk, 2 * chunk, (n // chunk // 2) * chunk, (n // chunk - 1) * chunk):
         if 0 < c < n:
             pos.update({c - 1, c})
@@ -51,7 +54,7 @@ def run_prefill(name):
 
 def check_sequence(w, d, run, b, seed, label, check_cache=True):
     n = d["lengths"][b]
-    positions = sample_positions(n, w.chunk, seed)
+    positions = sample_positions(n, w.chunk, seed, window=w.window)
     pos, ref = oracle_rows(w, d, b, positions)
     got_all = run.gather("out")
     idx = torch.as_tensor(d["cu_seq"][b] + pos, device=got_all.device)
@@ -99,8 +102,8 @@ def test_c4_yarn_128k_full():
     assert np.array_equal(_bits(got), want.view(torch.int16).numpy())
 
 
-def test_c2_decode_full():
-    w = wl.CONFIGS["c2_decode"]
+def check_decode(name):
+    w = wl.CONFIGS[name]
     say(f"full-size decode: {w}")
     d = wl.gen_decode(w, device=DEV)
     step = runner.DecodeStep(w, d, device=DEV)
@@ -123,11 +126,14 @@ def test_c2_decode_full():
                                            store=oracle.STORE_BF16)[0]
         vc[:, c - 1] = np64(d["v"][b])
         q = oracle.finish_heads(np64(d["q"][b:b + 1]), pos, f, w.rd, store=oracle.STORE_BF16)
-        o, P = oracle.attend(q, kc, vc, pos, w.scale, want_probs=True)
-        check_bf16_rows(out[b], o[0], f"c2 seq {b} ctx {c}")
+        o, P = oracle.attend(q, kc, vc, pos, w.scale, want_probs=True, window=w.window)
+        check_bf16_rows(out[b], o[0], f"{name} seq {b} ctx {c}")
         pg = np64(step.probs[b])
         assert np.all(np.isnan(pg[:, c:])), "entries past ctx must stay untouched"
         pg = pg[:, :c]
+        if w.window and c > w.window:
+            # keys before the window: probability exactly 0
+            assert np.all(pg[:, :c - w.window] == 0.0)
         assert np.allclose(pg.sum(-1), 1.0, atol=1e-5)
         rel = np.max(np.abs(pg - P[0]), axis=-1) / np.sqrt(np.mean(P[0] ** 2, axis=-1))
         say(f"    probs worst row err/rms {rel.max():.3e}")
@@ -136,3 +142,18 @@ def test_c2_decode_full():
     assert np.all(np.isfinite(out))
     for b, c in enumerate(ctx):
         assert torch.equal(step.v_cache[b, :, c - 1], d["v"][b].to(DEV))
+
+
+def test_c2_decode_full():
+    check_decode("c2_decode")
+
+
+def test_c2_decode_sw4096_full():
+    check_decode("c2_decode_sw4096")
+
+
+def test_c4_yarn_128k_sw4096_full():
+    # sliding window of 4096 keys over the 128K prompt: sampled rows on both
+    # sides of chunk boundaries, before and after the window fills
+    w, d, run = run_prefill("c4_yarn_128k_sw4096")
+    check_sequence(w, d, run, 0, 405, "c4 window", check_cache=False)

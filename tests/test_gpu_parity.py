@@ -454,6 +454,129 @@ def test_bf16_decode_small_workspace(nh, nkv, parts_per_row, spike):
         assert dp.max() <= 2e-2, dp.max()
 
 
+# ------------------------------------------------------------------ sliding window
+
+WINDOW_CASES = [
+    # name, nh, nkv, hd, T, chunk, window
+    ("w100_chunk128", 8, 2, 128, 700, 128, 100),      # window below the chunk
+    ("w300_chunk256", 8, 2, 128, 700, 256, 300),
+    ("w64_mha_hd64", 3, 3, 64, 500, 64, 64),          # window = one key tile
+    ("w1_gqa8_hd64", 16, 2, 64, 400, 130, 1),         # every row reads only itself
+    ("w777_long_split", 2, 2, 128, 2100, 37, 777),    # small chunks, split key range
+    ("w2000_long_split", 8, 8, 128, 2100, 64, 2000),
+]
+
+
+@pytest.mark.parametrize("name,nh,nkv,hd,T,chunk,window", WINDOW_CASES)
+def test_bf16_prefill_window_matches_oracle(name, nh, nkv, hd, T, chunk, window):
+    say(f"bf16 prefill window {name}: nh={nh} nkv={nkv} hd={hd} T={T} chunk={chunk} W={window}")
+    w = wl.Workload(name=name, dtype=wl.BF16, n_heads=nh, n_kv=nkv, head_dim=hd, seed=41,
+                    prompt_len=T, chunk=chunk, window=window)
+    d = wl.gen_prefill(w)
+    run = runner.ChunkedPrefill(w, d, device=DEV)
+    run.run_all()
+    torch.cuda.synchronize()
+    got = np64(run.gather("out"))
+    ref = oracle_prefill_packed(w, d, chunk)
+    check_bf16_rows(got, ref["out"], name)
+    if window == 1:
+        # one key: the output is that position's V row exactly
+        v = np64(d["v"])
+        for h in range(nh):
+            assert np.array_equal(got[:, h], v[:, h // (nh // nkv)])
+
+
+def test_bf16_prefill_window_varlen_and_wide_window():
+    """Ragged prompts with a window, in 128- and 256-row workgroups; a window
+    at least as long as every prompt gives the unwindowed result bit for bit."""
+    for n_seq, chunk, window in ((4, 256, 200), (32, 64, 50)):
+        w = wl.Workload(name="varlen-w", dtype=wl.BF16, n_heads=32 if n_seq == 32 else 10,
+                        n_kv=8 if n_seq == 32 else 2, head_dim=128, seed=43, base=1e6,
+                        rotary_dim=64, norm_style=wl.NORM_W, n_seq=n_seq,
+                        len_range=(1, 700), chunk=chunk, cap=700, window=window)
+        say(f"bf16 varlen window {w}")
+        d = wl.gen_prefill(w)
+        run = runner.ChunkedPrefill(w, d, device=DEV)
+        run.run_all()
+        torch.cuda.synchronize()
+        ref = oracle_prefill_packed(w, d, chunk)
+        check_bf16_rows(np64(run.gather("out")), ref["out"], f"varlen window {window}")
+    w = wl.Workload(name="wide-w", dtype=wl.BF16, n_heads=8, n_kv=2, head_dim=128, seed=44,
+                    prompt_len=600, chunk=96)
+    d = wl.gen_prefill(w)
+    outs = []
+    for window in (0, 600, 10 ** 6):
+        run = runner.ChunkedPrefill(w.replace(window=window), d, device=DEV)
+        run.run_all()
+        torch.cuda.synchronize()
+        outs.append(_bits(run.gather("out")))
+    assert np.array_equal(outs[0], outs[1]) and np.array_equal(outs[0], outs[2])
+
+
+def test_f32_prefill_window_and_probs():
+    w = wl.CONFIGS["c0_f32_small"].replace(window=20)
+    d = wl.gen_prefill(w)
+    ref = oracle_prefill_packed(w, d, 16, want_probs=True)
+    for chunk in (16, 1, 64):
+        run = runner.ChunkedPrefill(w, d, device=DEV, chunk=chunk)
+        run.run_all()
+        torch.cuda.synchronize()
+        check_f32(np64(run.gather("out")), ref["out"], f"f32 window chunk {chunk}")
+
+
+def _decode_reference(w, d, b, c):
+    f = oracle_table(w)
+    pos = np.array([c - 1])
+    kc = np64(d["k_cache"][b])[:, :c].copy()
+    vc = np64(d["v_cache"][b])[:, :c].copy()
+    kc[:, c - 1] = oracle.finish_heads(np64(d["k"][b:b + 1]), pos, f, w.rd,
+                                       store=store_of(w))[0]
+    vc[:, c - 1] = np64(d["v"][b])
+    q = oracle.finish_heads(np64(d["q"][b:b + 1]), pos, f, w.rd, store=store_of(w))
+    o, P = oracle.attend(q, kc, vc, pos, w.scale, want_probs=True, window=w.window)
+    return o[0], P[0]
+
+
+@pytest.mark.parametrize("dtype,nh,nkv,window,parts_per_row", [
+    (wl.BF16, 32, 8, 1, 0), (wl.BF16, 32, 8, 33, 0), (wl.BF16, 16, 2, 100, 0),
+    (wl.BF16, 40, 8, 1024, 0), (wl.BF16, 8, 8, 5000, 0),
+    (wl.BF16, 32, 2, 2500, 1),             # one part per row, longer than the on-chip buffer
+    (wl.F32, 8, 2, 100, 0)])
+def test_decode_window_matches_oracle(dtype, nh, nkv, window, parts_per_row):
+    ctx = [1, 63, 64, 65, 1025, 3000, 2049, 97]
+    hd = 128
+    w = wl.Workload(name="dec-w", dtype=dtype, n_heads=nh, n_kv=nkv, head_dim=hd, seed=47,
+                    n_seq=len(ctx), decode=True, ctx_range=(1, 3000), cap=3072, want_probs=True,
+                    window=window)
+    say(f"decode window {dtype} nh={nh} nkv={nkv} W={window} parts/row={parts_per_row} ctx={ctx}")
+    d = wl.gen_decode(w)
+    d["ctx"] = ctx
+    step = runner.DecodeStep(w, d, device=DEV, probs_ld_multiple=1)
+    if parts_per_row:
+        step.workspace = torch.empty(len(ctx) * nh * (hd + 4) * parts_per_row,
+                                     dtype=torch.float32, device=DEV)
+    step.probs.fill_(float("nan"))
+    step.run()
+    torch.cuda.synchronize()
+    got_o = np64(step.out)
+    got_p = np64(step.probs)
+    for b, c in enumerate(ctx):
+        o, P = _decode_reference(w, d, b, c)
+        if dtype == wl.BF16:
+            check_bf16_rows(got_o[b], o, f"seq {b} ctx {c}")
+        else:
+            check_f32(got_o[b], o, f"seq {b} ctx {c}")
+        assert np.all(np.isnan(got_p[b, :, c:])), "entries past ctx must stay untouched"
+        pg = got_p[b, :, :c]
+        first = max(0, c - window)
+        assert np.all(pg[:, :first] == 0.0), "keys before the window get probability 0"
+        assert np.allclose(pg.sum(-1), 1.0, atol=1e-5)
+        if window == 1:
+            assert np.all(pg[:, c - 1] == 1.0)
+        dp = np.max(np.abs(pg - P), axis=-1) / np.sqrt(np.mean(P ** 2, axis=-1))
+        assert dp.max() <= (2e-2 if dtype == wl.BF16 else 1e-4), dp.max()
+
+
 # ------------------------------------------------------------------ importance
 
 @pytest.mark.parametrize("dtype", [wl.BF16, wl.F32])
