@@ -239,3 +239,62 @@ def prefill_sequence(q_raw, k_raw, v_raw, chunk: int, inv_freq, rotary_dim: int,
         if want_probs:
             probs[c0:c1, :, :pr.shape[2]] = pr
     return dict(out=out, q_rot=q_rot, k_cache=kc, v_cache=vc, probs=probs)
+
+
+def prefill_sequence_ring(q_raw, k_raw, v_raw, chunk: int, inv_freq, rotary_dim: int,
+                          scale: float, store: int, ring: int, window: int,
+                          interleaved: bool = False, rope_scale: float = 1.0,
+                          norm_style: int = NORM_NONE, q_norm_w=None, k_norm_w=None,
+                          eps: float = 1e-6, n_threads: int | None = None):
+    """Chunked prefill of one prompt over a ring cache of `ring` slots per KV
+    head: position p is stored in slot p mod ring, overwriting position
+    p - ring ([NDL] the per-chunk loop's note on the KV ring: writing p+1
+    overwrites the slot of p+1-window, still inside p's window).  A row at
+    position p attends keys lo..p, lo = max(0, p-window+1) (lo = 0 without a
+    window), each read from its slot.
+
+    interleaved=True is the pages' order: write position p, then attend it,
+    one position at a time, which a ring of `window` slots supports.
+    interleaved=False writes the whole chunk first, then attends its rows;
+    that reads the same keys only while ring >= window + chunk - 1.
+
+    Returns dict(out, q_rot, k_cache, v_cache) with the ring caches
+    [nkv][ring][hd] (never-written slots are NaN)."""
+    qr, kr, vr = _f64(q_raw), _f64(k_raw), _f64(v_raw)
+    T, nh, hd = qr.shape
+    nkv = kr.shape[1]
+    kc = np.full((nkv, ring, hd), np.nan)
+    vc = np.full((nkv, ring, hd), np.nan)
+    out = np.zeros((T, nh, hd))
+    q_rot = np.zeros((T, nh, hd))
+    chunk = max(1, int(chunk))
+
+    def attend_row(qrow, p):
+        lo = max(0, p - window + 1) if window > 0 else 0
+        slots = np.arange(lo, p + 1) % ring
+        o, _ = attend(qrow[None], kc[:, slots, :].copy(), vc[:, slots, :].copy(),
+                      np.array([p - lo]), scale, n_threads=n_threads)
+        return o[0]
+
+    def write(i, p, kcn, c0):
+        kc[:, p % ring, :] = kcn[i - c0]
+        vc[:, p % ring, :] = vr[i]
+
+    for c0 in range(0, T, chunk):
+        c1 = min(T, c0 + chunk)
+        pos = np.arange(c0, c1, dtype=np.int64)
+        qc = finish_heads(qr[c0:c1], pos, inv_freq, rotary_dim, rope_scale, norm_style,
+                          q_norm_w, eps, store)
+        kcn = finish_heads(kr[c0:c1], pos, inv_freq, rotary_dim, rope_scale, norm_style,
+                           k_norm_w, eps, store)
+        if interleaved:
+            for i in range(c0, c1):
+                write(i, i, kcn, c0)
+                out[i] = attend_row(qc[i - c0], i)
+        else:
+            for i in range(c0, c1):
+                write(i, i, kcn, c0)
+            for i in range(c0, c1):
+                out[i] = attend_row(qc[i - c0], i)
+        q_rot[c0:c1] = qc
+    return dict(out=out, q_rot=q_rot, k_cache=kc, v_cache=vc)

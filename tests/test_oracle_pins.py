@@ -451,6 +451,39 @@ def test_sliding_window_special_cases():
     assert np.array_equal(seq["out"], chk["out"])
 
 
+def test_ring_cache_orders():
+    """Ring cache ([NDL] the per-chunk loop over a KV ring of `window`
+    positions: writing p+1 overwrites the slot of p+1-window, which p still
+    reads, so write and attend are interleaved there).  Pinned by: the pages'
+    interleaved order over a ring of exactly `window` slots equals windowed
+    attention over a linear cache bit for bit; writing each chunk first equals
+    it too once the ring holds window + chunk - 1 slots, and one slot fewer
+    changes some row (the hazard the pages describe); every slot ends holding
+    the last position congruent to it."""
+    rng = np.random.default_rng(57)
+    T, nh, nkv, hd, W, C = 61, 4, 2, 16, 9, 7
+    q = rng.standard_normal((T, nh, hd))
+    k = rng.standard_normal((T, nkv, hd))
+    v = rng.standard_normal((T, nkv, hd))
+    f = oracle.rope_inv_freq(hd, 1e4)
+    lin = oracle.prefill_sequence(q, k, v, C, f, hd, 0.3, oracle.STORE_F32, window=W)
+    pages = oracle.prefill_sequence_ring(q, k, v, C, f, hd, 0.3, oracle.STORE_F32, ring=W,
+                                         window=W, interleaved=True)
+    assert np.array_equal(pages["out"], lin["out"])
+    first = oracle.prefill_sequence_ring(q, k, v, C, f, hd, 0.3, oracle.STORE_F32, ring=W + C - 1,
+                                         window=W)
+    assert np.array_equal(first["out"], lin["out"])
+    assert np.array_equal(first["q_rot"], lin["q_rot"])
+    short = oracle.prefill_sequence_ring(q, k, v, C, f, hd, 0.3, oracle.STORE_F32, ring=W + C - 2,
+                                         window=W)
+    assert np.abs(short["out"] - lin["out"]).max() > 1e-3
+    R = W + C - 1
+    for s in range(R):
+        p = max(x for x in range(T) if x % R == s)
+        assert np.array_equal(first["k_cache"][:, s], lin["k_cache"][:, p])
+        assert np.array_equal(first["v_cache"][:, s], lin["v_cache"][:, p])
+
+
 MUTATIONS = {
     "mask_off_by_one": ("(long)jb->qpos[t] + 1 - first,", "(long)jb->qpos[t] - first,"),
     "window_one_short": ("first = (long)jb->qpos[t] + 1 - jb->window;", "first = (long)jb->qpos[t] + 2 - jb->window;"),
