@@ -47,15 +47,15 @@ def lib() -> ctypes.CDLL:
     L.attn_rope_inv_freq.argtypes = [i, d, fp]
     L.attn_yarn_inv_freq.argtypes = [i, d, d, i, d, d, fp]
     L.attn_rope_apply.argtypes = [vp, vp, i, i, i, i, i, vp, vp, i, vp, i, f, i, vp, d, vp]
-    L.attn_kv_append.argtypes = [vp, vp, i, i, i, i, i, vp, vp, i, vp, vp, i, i, vp, i, f, i, vp,
-                                 d, vp]
-    L.attn_rope_qkv.argtypes = [vp, vp, i, vp, vp, vp, vp, i, i, i, i, i, i, vp, vp, i, i, vp, i, f,
-                                i, vp, vp, d, vp]
-    L.attn_prefill_chunk.argtypes = [vp, vp, vp, i, i, i, i, i, i, i, vp, vp, i, i, f, i, vp, vp,
-                                     sz, vp]
+    L.attn_kv_append.argtypes = [vp, vp, i, i, i, i, i, i, vp, vp, i, vp, vp, i, i, vp, i, f, i,
+                                 vp, d, vp]
+    L.attn_rope_qkv.argtypes = [vp, vp, i, vp, vp, vp, vp, i, i, i, i, i, i, i, vp, vp, i, i, vp, i,
+                                f, i, vp, vp, d, vp]
+    L.attn_prefill_chunk.argtypes = [vp, vp, vp, i, i, i, i, i, i, i, i, vp, vp, i, i, f, i, vp,
+                                     vp, sz, vp]
     L.attn_prefill_workspace_bytes.argtypes = [i, i, i, i, i, i, i]
     L.attn_prefill_workspace_bytes.restype = sz
-    L.attn_decode.argtypes = [vp, vp, vp, i, i, i, i, i, i, vp, i, f, i, vp, vp, i, vp, sz, vp]
+    L.attn_decode.argtypes = [vp, vp, vp, i, i, i, i, i, i, i, vp, i, f, i, vp, vp, i, vp, sz, vp]
     L.attn_decode_workspace_bytes.argtypes = [i, i, i, i, i]
     L.attn_decode_importance.argtypes = [vp, i, i, i, vp, i, vp, i, i, vp]
     L.attn_decode_importance.restype = i
@@ -157,7 +157,9 @@ def rope_apply(x: torch.Tensor, y: torch.Tensor, batch: Batch, inv_freq: torch.T
 def kv_append(k_cache: torch.Tensor, v_cache: torch.Tensor, k_new: torch.Tensor,
               v_new: torch.Tensor, batch: Batch, inv_freq: torch.Tensor, rotary_dim: int,
               rope_scale: float = 1.0, norm: int = NORM_NONE,
-              norm_w: torch.Tensor | None = None, eps: float = 1e-6):
+              norm_w: torch.Tensor | None = None, eps: float = 1e-6, ring: bool = False):
+    """Finish K rows and write them with the V rows at their positions (row
+    p mod cap with ring=True)."""
     n_seq_c, n_kv, cap, hd = k_cache.shape
     assert v_cache.shape == k_cache.shape and n_seq_c >= batch.n_seq
     n_tok = k_new.shape[0]
@@ -165,7 +167,7 @@ def kv_append(k_cache: torch.Tensor, v_cache: torch.Tensor, k_new: torch.Tensor,
     assert k_new.dtype == k_cache.dtype == v_cache.dtype == v_new.dtype
     st = lib().attn_kv_append(
         _dev(k_cache, "k_cache"), _dev(v_cache, "v_cache"), _dtype_code(k_cache), batch.n_seq,
-        n_kv, hd, cap, _dev(k_new, "k_new"), _dev(v_new, "v_new"), n_tok,
+        n_kv, hd, cap, int(ring), _dev(k_new, "k_new"), _dev(v_new, "v_new"), n_tok,
         _dev(batch.cu_seq, "cu_seq", torch.int32), _dev(batch.start, "start", torch.int32),
         batch.max_chunk, batch.max_end,
         _dev(inv_freq, "inv_freq", torch.float32) if rotary_dim else None, rotary_dim,
@@ -177,7 +179,7 @@ def rope_qkv(q: torch.Tensor, q_out: torch.Tensor, k_cache: torch.Tensor, v_cach
              k_new: torch.Tensor, v_new: torch.Tensor, batch: Batch, inv_freq: torch.Tensor,
              rotary_dim: int, rope_scale: float = 1.0, norm: int = NORM_NONE,
              q_norm_w: torch.Tensor | None = None, k_norm_w: torch.Tensor | None = None,
-             eps: float = 1e-6):
+             eps: float = 1e-6, ring: bool = False):
     """rope_apply(q -> q_out) and kv_append(k_new, v_new) of one chunk in one call."""
     n_tok, n_heads, hd = q.shape
     assert q_out.shape == q.shape and q_out.dtype == q.dtype and n_tok >= batch.n_tok
@@ -188,7 +190,7 @@ def rope_qkv(q: torch.Tensor, q_out: torch.Tensor, k_cache: torch.Tensor, v_cach
     st = lib().attn_rope_qkv(
         _dev(q, "q"), _dev(q_out, "q_out"), n_heads, _dev(k_cache, "k_cache"),
         _dev(v_cache, "v_cache"), _dev(k_new, "k_new"), _dev(v_new, "v_new"), n_kv, cap,
-        _dtype_code(q), n_tok, hd, batch.n_seq, _dev(batch.cu_seq, "cu_seq", torch.int32),
+        int(ring), _dtype_code(q), n_tok, hd, batch.n_seq, _dev(batch.cu_seq, "cu_seq", torch.int32),
         _dev(batch.start, "start", torch.int32), batch.max_chunk, batch.max_end,
         _dev(inv_freq, "inv_freq", torch.float32) if rotary_dim else None, rotary_dim,
         rope_scale, norm, _dev(q_norm_w, "q_norm_w", torch.float32),
@@ -203,8 +205,9 @@ def prefill_workspace_bytes(batch: Batch, n_heads: int, n_kv: int, head_dim: int
 
 def prefill_chunk(q: torch.Tensor, k_cache: torch.Tensor, v_cache: torch.Tensor, batch: Batch,
                   scale: float, out: torch.Tensor, workspace: torch.Tensor | None = None,
-                  window: int = 0):
-    """Causal attention of a chunk batch; window > 0 keeps keys p-window+1..p."""
+                  window: int = 0, ring: bool = False):
+    """Causal attention of a chunk batch; window > 0 keeps keys p-window+1..p;
+    ring=True reads key j from cache row j mod cap."""
     n_tok, nh, hd = q.shape
     n_seq_c, n_kv, cap, hd2 = k_cache.shape
     assert hd2 == hd and out.shape == (n_tok, nh, hd) and out.dtype == torch.float32
@@ -213,7 +216,7 @@ def prefill_chunk(q: torch.Tensor, k_cache: torch.Tensor, v_cache: torch.Tensor,
     wsb = workspace.numel() * workspace.element_size() if workspace is not None else 0
     st = lib().attn_prefill_chunk(
         _dev(q, "q"), _dev(k_cache, "k_cache"), _dev(v_cache, "v_cache"), _dtype_code(q),
-        batch.n_seq, nh, n_kv, hd, cap, n_tok, _dev(batch.cu_seq, "cu_seq", torch.int32),
+        batch.n_seq, nh, n_kv, hd, cap, int(ring), n_tok, _dev(batch.cu_seq, "cu_seq", torch.int32),
         _dev(batch.start, "start", torch.int32), batch.max_chunk, batch.max_end, scale, window,
         _dev(out, "out"), ws, wsb, _stream())
     _check("attn_prefill_chunk", st)
@@ -236,8 +239,9 @@ def decode_importance(probs: torch.Tensor, ctx: torch.Tensor, max_ctx: int, imp:
 
 def decode(q: torch.Tensor, k_cache: torch.Tensor, v_cache: torch.Tensor, ctx: torch.Tensor,
            max_ctx: int, scale: float, out: torch.Tensor, probs: torch.Tensor | None = None,
-           workspace: torch.Tensor | None = None, window: int = 0):
-    """One-query attention over ctx[b] keys; window > 0 keeps the last window keys."""
+           workspace: torch.Tensor | None = None, window: int = 0, ring: bool = False):
+    """One-query attention over ctx[b] keys; window > 0 keeps the last window keys;
+    ring=True reads key j from cache row j mod cap."""
     n_seq, nh, hd = q.shape
     n_seq_c, n_kv, cap, hd2 = k_cache.shape
     assert hd2 == hd and n_seq_c >= n_seq and out.shape == (n_seq, nh, hd)
@@ -250,6 +254,6 @@ def decode(q: torch.Tensor, k_cache: torch.Tensor, v_cache: torch.Tensor, ctx: t
     wsb = workspace.numel() * workspace.element_size() if workspace is not None else 0
     st = lib().attn_decode(
         _dev(q, "q"), _dev(k_cache, "k_cache"), _dev(v_cache, "v_cache"), _dtype_code(q), n_seq,
-        nh, n_kv, hd, cap, _dev(ctx, "ctx"), max_ctx, scale, window, _dev(out, "out"),
+        nh, n_kv, hd, cap, int(ring), _dev(ctx, "ctx"), max_ctx, scale, window, _dev(out, "out"),
         _dev(probs, "probs"), ld, ws, wsb, _stream())
     _check("attn_decode", st)

@@ -27,7 +27,7 @@ __global__ __launch_bounds__(256) void attend_f32_kernel(AttendF32Args a) {
         b = item / a.n_heads;
         h = item % a.n_heads;
         if (b >= a.n_seq) return;
-        const int ctx = min(min(a.ctx[b], a.max_ctx), a.cap);
+        const int ctx = a.ring ? min(a.ctx[b], a.max_ctx) : min(min(a.ctx[b], a.max_ctx), a.cap);
         if (ctx < 1) {
             float* orow = a.out + ((size_t)b * a.n_heads + h) * HD;
             for (int e = lane; e < HD; e += 64) orow[e] = 0.f;
@@ -44,7 +44,7 @@ __global__ __launch_bounds__(256) void attend_f32_kernel(AttendF32Args a) {
         if (i >= len) return;
         t = t0 + i;
         pos = a.start[b] + i;
-        if (t < 0 || t >= a.n_tok || pos < 0 || pos >= a.cap) return;
+        if (t < 0 || t >= a.n_tok || pos < 0 || (!a.ring && pos >= a.cap)) return;
     }
     const int g = h / a.group;
     const float* q = a.q + ((size_t)t * a.n_heads + h) * HD;
@@ -60,9 +60,11 @@ __global__ __launch_bounds__(256) void attend_f32_kernel(AttendF32Args a) {
     // first key of the row's window (0 without one)
     const int first = a.window > 0 && n > a.window ? n - a.window : 0;
     const float sl = a.scale * kLog2e;
+    // cache row of key j
+    auto slot = [&](int j) { return a.ring ? j % a.cap : j; };
 
     auto score = [&](int j) -> float {
-        const float4* kr = reinterpret_cast<const float4*>(kc + (size_t)j * HD);
+        const float4* kr = reinterpret_cast<const float4*>(kc + (size_t)slot(j) * HD);
         const float4* qr = reinterpret_cast<const float4*>(qs[wave]);
         float acc = 0.f;
 #pragma unroll 8
@@ -90,7 +92,7 @@ __global__ __launch_bounds__(256) void attend_f32_kernel(AttendF32Args a) {
         const int cnt = min(64, n - j0);
         for (int jj = 0; jj < cnt; ++jj) {
             const float pj = __shfl(p, jj);
-            const float* vr = vc + (size_t)(j0 + jj) * HD;
+            const float* vr = vc + (size_t)slot(j0 + jj) * HD;
 #pragma unroll
             for (int e = 0; e < PER; ++e) o[e] += pj * vr[lane + 64 * e];
         }

@@ -132,15 +132,15 @@ int attn_rope_apply(const void* x, void* y, int dtype, int n_tok, int n_heads, i
 }
 
 int attn_kv_append(void* k_cache, void* v_cache, int dtype, int n_seq, int n_kv, int head_dim,
-                   int cap, const void* k_new, const void* v_new, int n_tok,
+                   int cap, int ring, const void* k_new, const void* v_new, int n_tok,
                    const int32_t* cu_seq, const int32_t* start, int max_chunk, int max_end,
                    const float* inv_freq, int rotary_dim, float rope_scale, int norm,
                    const float* norm_w, double eps, void* stream) {
     int st = check_rope(dtype, n_tok, n_kv, head_dim, n_seq, cu_seq, start, max_chunk, inv_freq,
                         rotary_dim, norm, norm_w);
     if (st != ATTN_OK) return st;
-    if (cap <= 0 || max_end < 0) return ATTN_EINVAL;
-    if (max_end > cap) return ATTN_ECAPACITY;
+    if (cap <= 0 || max_end < 0 || (ring != 0 && ring != 1)) return ATTN_EINVAL;
+    if (!ring && max_end > cap) return ATTN_ECAPACITY;
     if (n_seq == 0 || n_tok == 0 || max_chunk == 0) return ATTN_OK;
     if (!k_cache || !v_cache || !k_new || !v_new) return ATTN_EINVAL;
     attn::RopeArgs a{};
@@ -158,6 +158,7 @@ int attn_kv_append(void* k_cache, void* v_cache, int dtype, int n_seq, int n_kv,
     a.n_heads = n_kv;
     a.head_dim = head_dim;
     a.cap = cap;
+    a.ring = ring && max_end > cap;
     a.n_seq = n_seq;
     a.max_chunk = max_chunk;
     a.rotary_dim = rotary_dim < head_dim ? rotary_dim : head_dim;
@@ -166,7 +167,7 @@ int attn_kv_append(void* k_cache, void* v_cache, int dtype, int n_seq, int n_kv,
 }
 
 int attn_rope_qkv(const void* q, void* q_out, int n_heads, void* k_cache, void* v_cache,
-                  const void* k_new, const void* v_new, int n_kv, int cap, int dtype, int n_tok,
+                  const void* k_new, const void* v_new, int n_kv, int cap, int ring, int dtype, int n_tok,
                   int head_dim, int n_seq, const int32_t* cu_seq, const int32_t* start, int max_chunk,
                   int max_end, const float* inv_freq, int rotary_dim, float rope_scale, int norm,
                   const float* q_norm_w, const float* k_norm_w, double eps, void* stream) {
@@ -176,8 +177,8 @@ int attn_rope_qkv(const void* q, void* q_out, int n_heads, void* k_cache, void* 
     st = check_rope(dtype, n_tok, n_kv, head_dim, n_seq, cu_seq, start, max_chunk, inv_freq,
                     rotary_dim, norm, k_norm_w);
     if (st != ATTN_OK) return st;
-    if (cap <= 0 || max_end < 0) return ATTN_EINVAL;
-    if (max_end > cap) return ATTN_ECAPACITY;
+    if (cap <= 0 || max_end < 0 || (ring != 0 && ring != 1)) return ATTN_EINVAL;
+    if (!ring && max_end > cap) return ATTN_ECAPACITY;
     if (n_seq == 0 || n_tok == 0 || max_chunk == 0) return ATTN_OK;
     if (!q || !q_out || !k_cache || !v_cache || !k_new || !v_new) return ATTN_EINVAL;
     attn::RopeArgs aq{};
@@ -194,6 +195,7 @@ int attn_rope_qkv(const void* q, void* q_out, int n_heads, void* k_cache, void* 
     ak.norm_w = k_norm_w;
     ak.n_heads = n_kv;
     ak.cap = cap;
+    ak.ring = ring && max_end > cap;
     for (attn::RopeArgs* a : {&aq, &ak}) {
         a->cu_seq = cu_seq;
         a->start = start;
@@ -220,15 +222,21 @@ size_t attn_prefill_workspace_bytes(int n_seq, int n_heads, int n_kv, int head_d
 }
 
 int attn_prefill_chunk(const void* q, const void* k_cache, const void* v_cache, int dtype,
-                       int n_seq, int n_heads, int n_kv, int head_dim, int cap, int n_tok,
+                       int n_seq, int n_heads, int n_kv, int head_dim, int cap, int ring, int n_tok,
                        const int32_t* cu_seq, const int32_t* start, int max_chunk, int max_end,
                        float scale, int window, float* out, void* workspace,
                        size_t workspace_bytes, void* stream) {
     if (!dtype_ok(dtype) || !hd_ok(head_dim)) return ATTN_EUNSUPPORTED;
     if (n_seq < 0 || n_tok < 0 || max_chunk < 0 || max_end < 0 || n_heads <= 0 || n_kv <= 0 ||
-        cap <= 0 || n_heads % n_kv != 0 || !isfinite(scale) || window < 0)
+        cap <= 0 || n_heads % n_kv != 0 || !isfinite(scale) || window < 0 || (ring != 0 && ring != 1))
         return ATTN_EINVAL;
-    if (max_end > cap) return ATTN_ECAPACITY;
+    // A ring that has wrapped still holds every key the chunk reads only if
+    // the window plus the chunk's other rows fit in it (the chunk is written
+    // before it attends).  Until it wraps it is a plain cache.
+    const bool wrapped = ring && max_end > cap;
+    if (!wrapped && max_end > cap) return ATTN_ECAPACITY;
+    if (wrapped && (window <= 0 || (long)window + max_chunk - 1 > cap)) return ATTN_ECAPACITY;
+    if (wrapped && dtype == ATTN_BF16 && cap % 64 != 0) return ATTN_EUNSUPPORTED;
     if (n_seq == 0 || n_tok == 0 || max_chunk == 0) return ATTN_OK;
     if (!q || !k_cache || !v_cache || !out || !cu_seq || !start) return ATTN_EINVAL;
     if (n_seq > 65535) return ATTN_EINVAL;
@@ -253,6 +261,7 @@ int attn_prefill_chunk(const void* q, const void* k_cache, const void* v_cache, 
         a.n_tok = n_tok;
         a.max_chunk = max_chunk;
         a.window = window;
+        a.ring = wrapped;
         return status_of(attn::launch_attend_f32(a, s));
     }
     attn::PrefillArgs a{};
@@ -273,6 +282,7 @@ int attn_prefill_chunk(const void* q, const void* k_cache, const void* v_cache, 
     a.max_chunk = max_chunk;
     a.max_end = max_end;
     a.window = window;
+    a.ring = wrapped;
     const attn::PrefillPlan plan = attn::plan_prefill(n_seq, n_heads, n_kv, head_dim, n_tok,
                                                       max_chunk, max_end, window,
                                                       workspace ? workspace_bytes : 0);
@@ -299,14 +309,17 @@ size_t attn_decode_workspace_bytes(int n_seq, int n_heads, int n_kv, int head_di
 }
 
 int attn_decode(const void* q, const void* k_cache, const void* v_cache, int dtype, int n_seq,
-                int n_heads, int n_kv, int head_dim, int cap, const int32_t* ctx, int max_ctx,
-                float scale, int window, float* out, float* probs, int probs_ld, void* workspace,
+                int n_heads, int n_kv, int head_dim, int cap, int ring, const int32_t* ctx,
+                int max_ctx, float scale, int window, float* out, float* probs, int probs_ld, void* workspace,
                 size_t workspace_bytes, void* stream) {
     if (!dtype_ok(dtype) || !hd_ok(head_dim)) return ATTN_EUNSUPPORTED;
     if (n_seq < 0 || max_ctx < 0 || n_heads <= 0 || n_kv <= 0 || cap <= 0 ||
-        n_heads % n_kv != 0 || !isfinite(scale) || window < 0)
+        n_heads % n_kv != 0 || !isfinite(scale) || window < 0 || (ring != 0 && ring != 1))
         return ATTN_EINVAL;
-    if (max_ctx > cap) return ATTN_ECAPACITY;
+    // a wrapped ring holds the last cap keys: enough for a window of at most cap
+    const bool wrapped = ring && max_ctx > cap;
+    if (!wrapped && max_ctx > cap) return ATTN_ECAPACITY;
+    if (wrapped && (window <= 0 || window > cap)) return ATTN_ECAPACITY;
     if (n_seq == 0 || max_ctx == 0) return ATTN_OK;
     if (!q || !k_cache || !v_cache || !out || !ctx) return ATTN_EINVAL;
     if (probs && probs_ld < max_ctx) return ATTN_EINVAL;
@@ -332,6 +345,7 @@ int attn_decode(const void* q, const void* k_cache, const void* v_cache, int dty
         a.max_ctx = max_ctx;
         a.probs_ld = probs_ld;
         a.window = window;
+        a.ring = wrapped;
         return status_of(attn::launch_attend_f32(a, s));
     }
     if (group > attn::decode_group_limit()) return ATTN_EUNSUPPORTED;
@@ -365,6 +379,7 @@ int attn_decode(const void* q, const void* k_cache, const void* v_cache, int dty
     a.split_len = split_len;
     a.n_splits = splits;
     a.window = window;
+    a.ring = wrapped;
     if ((long)n_seq * splits * n_kv > 0x7fffffffL) return ATTN_EINVAL;
     return status_of(attn::launch_decode_bf16(a, s));
 }

@@ -168,8 +168,9 @@ __device__ __forceinline__ void rescale_half_scores(const float* fac, float* lh,
 
 // LONG: parts may be longer than the raw-score buffer (a small workspace);
 // only that instance carries the mid-part writes and their rescale, which
-// would otherwise add to the streaming loop's registers.
-template <int HD, int HPL, bool PROBS, bool LONG>
+// would otherwise add to the streaming loop's registers.  RING: the cache is
+// a ring of cap rows (key k in row k mod cap) that has wrapped.
+template <int HD, int HPL, bool PROBS, bool LONG, bool RING>
 __global__ __launch_bounds__(64) void decode_split_kernel(DecodeArgs a) {
     constexpr int GQ = 4 * HPL;                 // query heads per group handled
     constexpr int NK = HD / 32;                 // K-steps per 16x16x32 product
@@ -191,7 +192,7 @@ __global__ __launch_bounds__(64) void decode_split_kernel(DecodeArgs a) {
     const int s = id % a.n_splits;
     const int b = id / a.n_splits;
     if (b >= a.n_seq) return;
-    const int ctx = min(min(a.ctx[b], a.max_ctx), a.cap);
+    const int ctx = a.ring ? min(a.ctx[b], a.max_ctx) : min(min(a.ctx[b], a.max_ctx), a.cap);
     const int k_first = decode_window_first(ctx, a.window);
     const int k_lo = decode_part_base(ctx, a.window) + s * a.split_len;
     const int k_hi = min(k_lo + a.split_len, ctx);
@@ -241,6 +242,16 @@ __global__ __launch_bounds__(64) void decode_split_kernel(DecodeArgs a) {
         for (int e = 0; e < 8; ++e) o[hh][e] = 0.f;
     const float sl = a.scale * kLog2e;
     const int last = k_hi - 1;
+    // Ring: the keys of the window this part reads, [key_lo, k_hi), span at
+    // most cap rows, so key k (clamped up to key_lo: keys below the window
+    // are masked) lives in row k - wrap, less cap once past the ring's end.
+    const int key_lo = max(k_lo, k_first);
+    const int wrap = RING ? key_lo - key_lo % a.cap : 0;
+    auto row_of = [&](int key) __attribute__((always_inline)) {
+        if (!RING) return key;
+        const int r = max(key, key_lo) - wrap;
+        return r >= a.cap ? r - a.cap : r;
+    };
 
     // Rows past the part's end re-read its last row (in bounds); their
     // scores are masked to -inf so their probabilities are exactly 0.
@@ -248,13 +259,13 @@ __global__ __launch_bounds__(64) void decode_split_kernel(DecodeArgs a) {
     auto load = [&](int k0, int buf) __attribute__((always_inline)) {
 #pragma unroll
         for (int blk = 0; blk < 2; ++blk) {
-            const int key = min(k0 + 16 * blk + col, last);
+            const int key = row_of(min(k0 + 16 * blk + col, last));
 #pragma unroll
             for (int k = 0; k < NK; ++k) kf[buf][blk][k] = ld16_nt(kc + (size_t)key * HD + 32 * k + 8 * grp);
         }
 #pragma unroll
         for (int i = 0; i < NV; ++i) {
-            const int key = min(k0 + RPI * i + vr, last);
+            const int key = row_of(min(k0 + RPI * i + vr, last));
             vf[buf][i] = ld16_nt(vcache + (size_t)key * HD + 8 * vc_);
         }
     };
@@ -441,7 +452,7 @@ __global__ __launch_bounds__(256) void decode_combine_kernel(DecodeArgs a) {
     const int b = row / a.n_heads;
     const int tid = threadIdx.x;
     if (b >= a.n_seq) return;
-    const int ctx = min(min(a.ctx[b], a.max_ctx), a.cap);
+    const int ctx = a.ring ? min(a.ctx[b], a.max_ctx) : min(min(a.ctx[b], a.max_ctx), a.cap);
     float* orow = a.out + (size_t)row * HD;
     if (ctx < 1) {
         for (int d = tid; d < HD; d += 256) orow[d] = 0.f;
@@ -592,25 +603,33 @@ hipError_t launch_decode_importance(const ImportanceArgs& a, hipStream_t stream)
     return hipGetLastError();
 }
 
-template <int HD, bool PROBS, bool LONG>
+template <int HD, bool PROBS, bool LONG, bool RING>
 static void launch_split(const DecodeArgs& a, hipStream_t stream) {
     const dim3 grid((unsigned)((long)a.n_seq * a.n_splits * a.n_kv));
     if (a.group <= 4)
-        decode_split_kernel<HD, 1, PROBS, LONG><<<grid, dim3(64), 0, stream>>>(a);
+        decode_split_kernel<HD, 1, PROBS, LONG, RING><<<grid, dim3(64), 0, stream>>>(a);
     else if (a.group <= 8)
-        decode_split_kernel<HD, 2, PROBS, LONG><<<grid, dim3(64), 0, stream>>>(a);
+        decode_split_kernel<HD, 2, PROBS, LONG, RING><<<grid, dim3(64), 0, stream>>>(a);
     else
-        decode_split_kernel<HD, 4, PROBS, LONG><<<grid, dim3(64), 0, stream>>>(a);
+        decode_split_kernel<HD, 4, PROBS, LONG, RING><<<grid, dim3(64), 0, stream>>>(a);
+}
+
+template <int HD, bool RING>
+static void launch_split_any(const DecodeArgs& a, hipStream_t stream) {
+    if (!a.probs)
+        launch_split<HD, false, false, RING>(a, stream);
+    else if (a.split_len <= decode_part_limit(a.group, true))
+        launch_split<HD, true, false, RING>(a, stream);
+    else
+        launch_split<HD, true, true, RING>(a, stream);
 }
 
 template <int HD>
 static void launch_decode_hd(const DecodeArgs& a, hipStream_t stream) {
-    if (!a.probs)
-        launch_split<HD, false, false>(a, stream);
-    else if (a.split_len <= decode_part_limit(a.group, true))
-        launch_split<HD, true, false>(a, stream);
+    if (a.ring)
+        launch_split_any<HD, true>(a, stream);
     else
-        launch_split<HD, true, true>(a, stream);
+        launch_split_any<HD, false>(a, stream);
     decode_combine_kernel<HD><<<dim3((unsigned)(a.n_seq * a.n_heads)), dim3(256), 0, stream>>>(a);
 }
 

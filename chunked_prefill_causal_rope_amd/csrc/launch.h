@@ -21,6 +21,7 @@ struct RopeArgs {
     double eps;
     float rope_scale;
     int n_tok, n_heads, head_dim, cap, n_seq, max_chunk, rotary_dim, norm;
+    int ring;              // KV: position p in cache row p mod cap (else row p < cap)
 };
 hipError_t launch_rope_rows(const RopeArgs& a, int dtype, bool kv, hipStream_t stream);
 // Both finishes of a chunk (queries, then keys/values into the cache) in as
@@ -40,6 +41,7 @@ struct PrefillArgs {
     float scale;
     int n_seq, n_heads, n_kv, group, head_dim, cap, n_tok, max_chunk, max_end;
     int window;            // 0: all keys <= p; W: keys p-W+1..p
+    int ring;              // key j in cache row j mod cap (needs a window; cap % 64 == 0)
     // rows per workgroup, row tiles per sequence, split call (persistent
     // grid with device-chosen key-range parts, merged by the combine kernel)
     int rows_per_tile, n_qtiles, split, grid, slots;
@@ -70,6 +72,7 @@ struct AttendF32Args {
     int decode;
     int n_seq, n_heads, n_kv, group, head_dim, cap, n_tok, max_chunk, max_ctx, probs_ld;
     int window;            // 0: all keys <= p; W: keys p-W+1..p
+    int ring;              // key j in cache row j mod cap
 };
 hipError_t launch_attend_f32(const AttendF32Args& a, hipStream_t stream);
 
@@ -86,6 +89,7 @@ struct DecodeArgs {
     int n_seq, n_heads, n_kv, group, head_dim, cap, max_ctx, probs_ld;
     int split_len, n_splits;   // parts of split_len keys from the row's first key
     int window;                // 0: all ctx keys; W: the last W
+    int ring;                  // key j in cache row j mod cap (needs W <= cap)
 };
 int decode_group_limit();
 // Keys one decode row may read, from its part start on: max_ctx, or with a

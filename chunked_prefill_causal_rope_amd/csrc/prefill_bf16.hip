@@ -145,7 +145,7 @@ __device__ __forceinline__ int group_tiles(const PrefillArgs& a, int b, int qt) 
     const int r0 = qt * a.rows_per_tile;
     if (len <= 0 || p0 < 0 || r0 >= rows_b) return 0;
     const int r_last = min(r0 + a.rows_per_tile, rows_b) - 1;
-    const int n_keys = min(p0 + r_last / a.group + 1, a.cap);
+    const int n_keys = a.ring ? p0 + r_last / a.group + 1 : min(p0 + r_last / a.group + 1, a.cap);
     const int n_tiles = (n_keys + kTK - 1) / kTK;
     return n_tiles - min(first_key_tile(p0 + r0 / a.group, a.window), n_tiles);
 }
@@ -283,7 +283,8 @@ __global__ __launch_bounds__(NW * 64, 8 / NW) void prefill_bf16_kernel(PrefillAr
     if (len <= 0 || p0 < 0 || r_tile0 >= rows_b) return;
 
     const int r_last = min(r_tile0 + TILE_ROWS, rows_b) - 1;
-    const int n_keys = min(p0 + r_last / G + 1, a.cap);
+    // keys 0..n_keys-1 (a ring cache holds positions past its capacity)
+    const int n_keys = WIN && a.ring ? p0 + r_last / G + 1 : min(p0 + r_last / G + 1, a.cap);
     const int n_tiles = (n_keys + kTK - 1) / kTK;
     // this item's part of the row tile's key tiles (from the first one its
     // window reaches), parts of equal length
@@ -333,9 +334,13 @@ __global__ __launch_bounds__(NW * 64, 8 / NW) void prefill_bf16_kernel(PrefillAr
         const int idx = c * kThreads + tid;
         voff[c] = ((idx / CH) * HD + (idx % CH) * 8) * 2;
     }
+    // a ring cache (capacity a multiple of kTK) keeps key tile j at tile
+    // j mod (cap / kTK), never split by the ring's end
+    const int ring_tiles = a.cap / kTK;
     auto tile_rsrc = [&](const uint16_t* base, int j) __attribute__((always_inline)) {
-        const int rows = max(n_keys - j * kTK, 0);
-        return __builtin_amdgcn_make_buffer_rsrc((void*)(base + (size_t)j * kTK * HD), (short)0, rows * HD * 2,
+        const int rows = min(max(n_keys - j * kTK, 0), kTK);
+        const int jt = WIN && a.ring ? j % ring_tiles : j;
+        return __builtin_amdgcn_make_buffer_rsrc((void*)(base + (size_t)jt * kTK * HD), (short)0, rows * HD * 2,
                                                  kBufferWord3);
     };
     auto lds_off = [&](int c, int stride) __attribute__((always_inline)) {

@@ -76,7 +76,8 @@ __global__ __launch_bounds__(kRopeThreads) void rope_rows_kernel(RopeArgs a) {
     const int t = seq0 + i;
     const int pos = a.start[b] + i;
     if (t < 0 || t >= a.n_tok || pos < 0) return;
-    if (KV && pos >= a.cap) return;
+    if (KV && !a.ring && pos >= a.cap) return;
+    const int slot = KV && a.ring ? pos % a.cap : pos;   // cache row of the position
 
     const int hd = a.head_dim;
     const int rd = a.rotary_dim;
@@ -125,7 +126,7 @@ __global__ __launch_bounds__(kRopeThreads) void rope_rows_kernel(RopeArgs a) {
 
     T* yd;
     if (KV) {
-        yd = dst + (((size_t)b * a.n_heads + h) * a.cap + pos) * hd;
+        yd = dst + (((size_t)b * a.n_heads + h) * a.cap + slot) * hd;
     } else {
         yd = dst + ((size_t)t * a.n_heads + h) * hd;
     }
@@ -146,7 +147,7 @@ __global__ __launch_bounds__(kRopeThreads) void rope_rows_kernel(RopeArgs a) {
     }
     if (KV) {
         const T* vs = reinterpret_cast<const T*>(a.v_src) + ((size_t)t * a.n_heads + h) * hd;
-        T* vd = reinterpret_cast<T*>(a.v_dst) + (((size_t)b * a.n_heads + h) * a.cap + pos) * hd;
+        T* vd = reinterpret_cast<T*>(a.v_dst) + (((size_t)b * a.n_heads + h) * a.cap + slot) * hd;
         for (int e = lane; e < hd; e += 64) vd[e] = vs[e];
     }
 }
@@ -246,7 +247,7 @@ struct RopeTokArgs {
     const float* inv_freq;
     double eps;
     float rope_scale;
-    int n_tok, cap, rotary_dim, norm;
+    int n_tok, cap, rotary_dim, norm, ring;
 };
 
 template <typename T, int HD>
@@ -268,7 +269,9 @@ __global__ __launch_bounds__(kTokThreads) void rope_token_kernel(RopeTokArgs a) 
     const int pos = a.start[b] + i;
     if (t < 0 || t >= a.n_tok || pos < 0) return;
     const int nq = a.nq;
-    const int nk = pos < a.cap ? a.nk : 0;     // no cache row past the capacity
+    // no cache row past the capacity (a ring has a row for every position)
+    const int nk = a.ring || pos < a.cap ? a.nk : 0;
+    const int slot = a.ring && a.nk ? pos % a.cap : pos;
     const int n_all = nq + nk;
     const int h_base = blockIdx.y * HPB;
     if (h_base >= n_all) return;               // uniform over the workgroup
@@ -340,7 +343,7 @@ __global__ __launch_bounds__(kTokThreads) void rope_token_kernel(RopeTokArgs a) 
         }
     }
     T* dst = is_q ? reinterpret_cast<T*>(a.qy) + ((size_t)t * nq + vh) * HD
-                  : reinterpret_cast<T*>(a.kc) + (((size_t)b * a.nk + kh) * a.cap + pos) * HD;
+                  : reinterpret_cast<T*>(a.kc) + (((size_t)b * a.nk + kh) * a.cap + slot) * HD;
     if (pair) {
         const double rs = (double)a.rope_scale;
         const bool scaled = a.rope_scale != 1.f;
@@ -361,7 +364,7 @@ __global__ __launch_bounds__(kTokThreads) void rope_token_kernel(RopeTokArgs a) 
         store_vals(dst + d0, v, 8);
     }
     if (!is_q) {
-        T* vd = reinterpret_cast<T*>(a.vc) + (((size_t)b * a.nk + kh) * a.cap + pos) * HD + c * 8;
+        T* vd = reinterpret_cast<T*>(a.vc) + (((size_t)b * a.nk + kh) * a.cap + slot) * HD + c * 8;
 #pragma unroll
         for (int j = 0; j < VCH; ++j) st16(vd + j * VPER, vbuf[j]);
     }
@@ -396,6 +399,7 @@ static RopeTokArgs token_args(const RopeArgs* q, const RopeArgs* kv) {
         t.kw = kv->norm_w;
         t.nk = kv->n_heads;
         t.cap = kv->cap;
+        t.ring = kv->ring;
     }
     t.cu_seq = r.cu_seq;
     t.start = r.start;

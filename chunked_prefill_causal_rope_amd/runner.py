@@ -87,19 +87,19 @@ class ChunkedPrefill:
         if fused:
             api.rope_qkv(s["q"], s["q_rot"], self.k_cache, self.v_cache, s["k"], s["v"], s["batch"],
                          self.inv_freq, w.rd, w.rope_scale, w.norm_style, self.q_norm_w,
-                         self.k_norm_w, w.norm_eps)
+                         self.k_norm_w, w.norm_eps, ring=w.ring)
         else:
             api.rope_apply(s["q"], s["q_rot"], s["batch"], self.inv_freq, w.rd, w.rope_scale,
                            w.norm_style, self.q_norm_w, w.norm_eps)
             api.kv_append(self.k_cache, self.v_cache, s["k"], s["v"], s["batch"], self.inv_freq,
-                          w.rd, w.rope_scale, w.norm_style, self.k_norm_w, w.norm_eps)
+                          w.rd, w.rope_scale, w.norm_style, self.k_norm_w, w.norm_eps, ring=w.ring)
         if attend:
             self.attend_step(i)
 
     def attend_step(self, i: int):
         s = self.steps[i]
         api.prefill_chunk(s["q_rot"], self.k_cache, self.v_cache, s["batch"], self.w.scale,
-                          s["out"], self.workspace, window=self.w.window)
+                          s["out"], self.workspace, window=self.w.window, ring=self.w.ring)
 
     def run_all(self, fused: bool = True):
         for i in range(len(self.steps)):
@@ -153,11 +153,11 @@ class DecodeStep:
         w = self.w
         api.rope_qkv(self.q, self.q_rot, self.k_cache, self.v_cache, self.k, self.v, self.batch,
                      self.inv_freq, w.rd, w.rope_scale, w.norm_style, self.q_norm_w,
-                     self.k_norm_w, w.norm_eps)
+                     self.k_norm_w, w.norm_eps, ring=w.ring)
 
     def attend(self):
         api.decode(self.q_rot, self.k_cache, self.v_cache, self.ctx, self.max_ctx, self.w.scale,
-                   self.out, self.probs, self.workspace, window=self.w.window)
+                   self.out, self.probs, self.workspace, window=self.w.window, ring=self.w.ring)
 
     def run(self):
         self.finish_and_append()

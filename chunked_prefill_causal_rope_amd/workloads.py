@@ -37,6 +37,7 @@ class Workload:
     norm_style: int = NORM_NONE
     norm_eps: float = 1e-6
     window: int = 0                        # 0: full causal; W: the last W keys only
+    ring: bool = False                     # cache of `cap` rows, position p in row p mod cap
     # prefill
     n_seq: int = 1
     prompt_len: int = 0                    # fixed length when len_range is None
@@ -92,6 +93,13 @@ CONFIGS = {
 CONFIGS["c4_yarn_128k_sw4096"] = CONFIGS["c4_yarn_128k"].replace(name="c4_yarn_128k_sw4096",
                                                                  window=4096)
 CONFIGS["c2_decode_sw4096"] = CONFIGS["c2_decode"].replace(name="c2_decode_sw4096", window=4096)
+# The same windows over a ring cache: 4096 + 2048 - 1 rows rounded up to a
+# multiple of 64 for the prefill (a chunk is written before it attends), 4096
+# rows for decode.
+CONFIGS["c4_yarn_128k_sw4096_ring"] = CONFIGS["c4_yarn_128k_sw4096"].replace(
+    name="c4_yarn_128k_sw4096_ring", ring=True, cap=6144)
+CONFIGS["c2_decode_sw4096_ring"] = CONFIGS["c2_decode_sw4096"].replace(
+    name="c2_decode_sw4096_ring", ring=True, cap=4096)
 
 
 def _gen(seed: int, device) -> torch.Generator:
@@ -135,8 +143,9 @@ def gen_prefill(w: Workload, device="cpu"):
 
 def gen_decode(w: Workload, device="cpu"):
     """Decode inputs: ctx[b] counts the new token, the cache holds ctx[b]-1
-    prior rows (already rotated; every cache row is drawn), and the new token's
-    q/k/v sit at position ctx[b]-1."""
+    prior rows (already rotated; every cache row is drawn; with a ring, row r
+    holds the latest position congruent to r), and the new token's q/k/v sit
+    at position ctx[b]-1."""
     g = _gen(w.seed, device)
     lo, hi = w.ctx_range
     ctx = [int(x) for x in torch.randint(lo, hi + 1, (w.n_seq,), generator=g, device=device)]

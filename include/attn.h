@@ -26,8 +26,16 @@
  *   sequence's token count; max_end (host) bounds every start[b]+len_b.  The
  *   host checks sizes from these host scalars; the device arrays are trusted
  *   to agree with them, and kernels skip any row outside [0, n_tok) or any
- *   position outside [0, cap) so a disagreeing array can never write out of
- *   bounds.
+ *   position outside [0, cap) (below 0 with a ring) so a disagreeing array
+ *   can never write out of bounds.
+ * - Ring cache (ring = 1, on the calls that take `ring`): position p lives in
+ *   cache row p mod cap, overwriting position p - cap ([NDL] the per-chunk
+ *   loop keeps a ring of window positions: writing p+1 overwrites the slot of
+ *   p+1-window).  The pages write and attend one position at a time over a
+ *   ring of exactly the window; here a chunk is written whole before it
+ *   attends, which reads the same keys when cap >= window + max_chunk - 1 --
+ *   the attention calls check that bound.  While every position is below cap
+ *   a ring is an ordinary cache.  ring = 0: row p, p < cap.
  * - Layouts (row-major, innermost last):
  *     Q, output            [n_tok][n_heads][head_dim]
  *     new K, new V         [n_tok][n_kv][head_dim]
@@ -131,12 +139,14 @@ int attn_rope_apply(const void *x, void *y, int dtype, int n_tok, int n_heads, i
  * position of the chunk before the batched attend).  Rows outside
  * [start[b], start[b]+len_b) are not touched.
  *   k_cache, v_cache device [n_seq][n_kv][cap][head_dim], updated
+ *   ring             0: position p in row p; 1: row p mod cap (see above)
  *   k_new, v_new     device [n_tok][n_kv][head_dim], read
  *   norm_w           the k-norm weight, device float[head_dim] or NULL
- * Errors: ECAPACITY if max_end > cap; otherwise as attn_rope_apply.
+ * Errors: ECAPACITY if max_end > cap without a ring; EINVAL (ring not 0/1);
+ * otherwise as attn_rope_apply.
  */
 int attn_kv_append(void *k_cache, void *v_cache, int dtype, int n_seq, int n_kv, int head_dim,
-                   int cap, const void *k_new, const void *v_new, int n_tok,
+                   int cap, int ring, const void *k_new, const void *v_new, int n_tok,
                    const int32_t *cu_seq, const int32_t *start, int max_chunk, int max_end,
                    const float *inv_freq, int rotary_dim, float rope_scale, int norm,
                    const float *norm_w, double eps, void *stream);
@@ -149,12 +159,13 @@ int attn_kv_append(void *k_cache, void *v_cache, int dtype, int n_seq, int n_kv,
  * multiple of 8, head_dim 64 or 128) -- a token's cos/sin table then serves
  * its query and key heads alike.  Arguments as in the two calls:
  *   q, q_out  device [n_tok][n_heads][head_dim] (q_out == q is allowed)
- *   k_cache, v_cache, k_new, v_new, n_kv, cap   as attn_kv_append
+ *   k_cache, v_cache, k_new, v_new, n_kv, cap, ring   as attn_kv_append
  *   q_norm_w, k_norm_w   the two norm weights (NULL iff norm is NONE)
  * Errors: the union of the two calls' errors.
  */
 int attn_rope_qkv(const void *q, void *q_out, int n_heads, void *k_cache, void *v_cache,
-                  const void *k_new, const void *v_new, int n_kv, int cap, int dtype, int n_tok,
+                  const void *k_new, const void *v_new, int n_kv, int cap, int ring, int dtype,
+                  int n_tok,
                   int head_dim, int n_seq, const int32_t *cu_seq, const int32_t *start,
                   int max_chunk, int max_end, const float *inv_freq, int rotary_dim,
                   float rope_scale, int norm, const float *q_norm_w, const float *k_norm_w,
@@ -175,19 +186,24 @@ int attn_rope_qkv(const void *q, void *q_out, int n_heads, void *k_cache, void *
  *   q        device [n_tok][n_heads][head_dim] (rotated), read
  *   out      device float[n_tok][n_heads][head_dim], written
  *   scale    the score scale, normally 1/sqrt(head_dim)
+ *   ring     0: key j in cache row j; 1: row j mod cap.  A ring with
+ *            max_end > cap needs 0 < window and window + max_chunk - 1 <= cap
+ *            (ECAPACITY otherwise) and, for bf16, cap a multiple of 64
+ *            (EUNSUPPORTED otherwise)
  *   window   0: every key <= p; W > 0: a sliding window, keys
  *            max(0, p-W+1)..p only ([ATT] QwenAttnCfg.window, "attend only
- *            the last N positions").  The cache still holds every position.
+ *            the last N positions").
  *   workspace device scratch of workspace_bytes (may be NULL/0); with less
  *            than attn_prefill_workspace_bytes() the key range is split into
  *            fewer parts (never an error).  Contents need no initialisation
  *            and are clobbered.  Calls that share a workspace must be ordered
  *            on one stream.
- * Errors: ECAPACITY if max_end > cap; EINVAL (window < 0, ...), EUNSUPPORTED,
- * EDEVICE.
+ * Errors: ECAPACITY if max_end > cap without a ring (see ring); EINVAL
+ * (window < 0, ring not 0/1, ...), EUNSUPPORTED, EDEVICE.
  */
 int attn_prefill_chunk(const void *q, const void *k_cache, const void *v_cache, int dtype,
-                       int n_seq, int n_heads, int n_kv, int head_dim, int cap, int n_tok,
+                       int n_seq, int n_heads, int n_kv, int head_dim, int cap, int ring,
+                       int n_tok,
                        const int32_t *cu_seq, const int32_t *start, int max_chunk, int max_end,
                        float scale, int window, float *out, void *workspace,
                        size_t workspace_bytes, void *stream);
@@ -212,6 +228,8 @@ size_t attn_prefill_workspace_bytes(int n_seq, int n_heads, int n_kv, int head_d
  *   q      device [n_seq][n_heads][head_dim] (rotated), read
  *   ctx    device int32[n_seq], 1 <= ctx[b] <= max_ctx (values above max_ctx
  *          are clamped to it; a row with ctx[b] < 1 gets zeros)
+ *   ring   0: key j in cache row j; 1: row j mod cap.  A ring with
+ *          max_ctx > cap needs 0 < window <= cap (ECAPACITY otherwise)
  *   window 0: all ctx[b] keys; W > 0: only the last W (a sliding window,
  *          [ATT] the decode loop starts at stored - window); the
  *          probabilities of the keys before it are written as 0
@@ -222,19 +240,23 @@ size_t attn_prefill_workspace_bytes(int n_seq, int n_heads, int n_kv, int head_d
  *          on a 128-byte line, which the 16-byte stores of the kernels use.
  *          bf16: the row's first ctx[b] entries also hold the intermediate
  *          unnormalised values in half precision, so each probability
- *          carries a relative rounding error below 2^-11 (and below 2^-24
- *          of the row's largest in absolute terms); f32: float throughout
+ *          carries a relative error below 2^-10 (2^-11 from its own
+ *          rounding, 2^-11 from the sum of rounded values that normalises
+ *          it) plus, for values below half precision's normal range, an
+ *          absolute one below 2^-24 of the row's largest; f32: float
+ *          throughout
  *   workspace device scratch, clobbered, no initialisation needed.  bf16
- *          needs at least n_seq*n_heads*(head_dim+2)*4 bytes (one part per
+ *          needs at least n_seq*n_heads*(head_dim+4)*4 bytes (one part per
  *          row, EINVAL below that); attn_decode_workspace_bytes() gives the
  *          size for the full split, and a smaller one means fewer, longer
  *          parts.  f32 needs none.
- * Errors: ECAPACITY if max_ctx > cap; EINVAL (probs_ld < max_ctx, window < 0,
- * ...), EUNSUPPORTED (bf16 with more than 16 query heads per KV head), EDEVICE.
+ * Errors: ECAPACITY if max_ctx > cap without a ring (see ring); EINVAL
+ * (probs_ld < max_ctx, window < 0, ring not 0/1, ...), EUNSUPPORTED (bf16
+ * with more than 16 query heads per KV head), EDEVICE.
  */
 int attn_decode(const void *q, const void *k_cache, const void *v_cache, int dtype, int n_seq,
-                int n_heads, int n_kv, int head_dim, int cap, const int32_t *ctx, int max_ctx,
-                float scale, int window, float *out, float *probs, int probs_ld,
+                int n_heads, int n_kv, int head_dim, int cap, int ring, const int32_t *ctx,
+                int max_ctx, float scale, int window, float *out, float *probs, int probs_ld,
                 void *workspace, size_t workspace_bytes, void *stream);
 
 size_t attn_decode_workspace_bytes(int n_seq, int n_heads, int n_kv, int head_dim, int max_ctx);

@@ -52,6 +52,17 @@ def oracle_prefill_packed(w, d, chunk, want_probs=False):
         sl = slice(cu[b], cu[b] + n)
         qn = norm_kwargs(w, d, "q_norm_w")
         kn = norm_kwargs(w, d, "k_norm_w")
+        if w.ring:
+            r = oracle.prefill_sequence_ring(
+                np64(d["q"][sl]), np64(d["k"][sl]), np64(d["v"][sl]), chunk, f, w.rd, w.scale,
+                store_of(w), ring=d["cap"], window=w.window, rope_scale=w.rope_scale,
+                norm_style=qn.get("norm_style", 0), q_norm_w=qn.get("norm_w"),
+                k_norm_w=kn.get("norm_w"), eps=w.norm_eps)
+            outs.append(r["out"])
+            caches.append((r["k_cache"], r["v_cache"]))
+            qrots.append(r["q_rot"])
+            probs.append(None)
+            continue
         r = oracle.prefill_sequence(
             np64(d["q"][sl]), np64(d["k"][sl]), np64(d["v"][sl]), chunk, f, w.rd, w.scale,
             store_of(w), rope_scale=w.rope_scale,
@@ -101,9 +112,61 @@ def check_bf16_rows(got: np.ndarray, ref: np.ndarray, label=""):
     return worst, tensor, rrmse
 
 
+# bf16 decode probabilities pass through half-precision intermediates: each
+# value carries a relative error below 2^-10 (its own rounding and the rounded
+# normalising sum's, 2^-11 each) and, below half precision's normal range, an
+# absolute error below 2^-24 of its row's largest value.
+PROB_REL_TOL = 2.0 ** -10 * 1.01
+PROB_ABS_FRAC = 2.0 ** -24
+
+
+def check_probs(got: np.ndarray, ref: np.ndarray, bf16: bool, label=""):
+    """got/ref [rows][n]: each row sums to 1 within 1e-5; bf16: elementwise
+    |dP| <= PROB_REL_TOL * P + PROB_ABS_FRAC * max(P_row); f32: max |dP| <=
+    1e-4 of the row's RMS."""
+    got = got.reshape(-1, got.shape[-1])
+    ref = ref.reshape(-1, ref.shape[-1])
+    assert np.all(np.isfinite(got)), f"{label}: non-finite probability"
+    assert np.allclose(got.sum(-1), 1.0, atol=1e-5), f"{label}: row sums"
+    err = np.abs(got - ref)
+    if bf16:
+        bound = PROB_REL_TOL * ref + PROB_ABS_FRAC * ref.max(-1, keepdims=True)
+        worst = float(np.max(err / bound))
+        say(f"  {label}: probs worst err/bound {worst:.3f}")
+        assert worst <= 1.0, f"{label}: probability error {worst} of the bound"
+    else:
+        rel = float(np.max(np.max(err, -1) / np.sqrt(np.mean(ref ** 2, -1))))
+        say(f"  {label}: probs worst err/rms {rel:.3e}")
+        assert rel <= 1e-4, f"{label}: probability error {rel}"
+
+
 def check_f32(got: np.ndarray, ref: np.ndarray, label=""):
     assert np.all(np.isfinite(got)), f"{label}: non-finite output"
     e = float(np.max(np.abs(got - ref)))
     say(f"  {label}: max abs err {e:.3e}")
     assert e <= F32_ABS_TOL, f"{label}: max abs err {e}"
     return e
+
+
+def oracle_decode_row(w, d, b, c):
+    """Oracle (out [nh][hd], probs [nh][c]) of decode row b with context c:
+    the new token's K (finished) and V go to position c-1, the prior rows come
+    from the drawn cache (row j mod cap with a ring), keys max(0, c-W)..c-1
+    with a window."""
+    f = oracle_table(w)
+    cap = d["k_cache"].shape[2]
+    lo = max(0, c - w.window) if w.window else 0
+    pos = np.arange(lo, c)
+    rows = torch.as_tensor(pos % cap if w.ring else pos, device=d["k_cache"].device)
+    kc = np64(d["k_cache"][b][:, rows]).copy()
+    vc = np64(d["v_cache"][b][:, rows]).copy()
+    last = np.array([c - 1])
+    kc[:, -1] = oracle.finish_heads(np64(d["k"][b:b + 1]), last, f, w.rd, w.rope_scale,
+                                    store=store_of(w))[0]
+    vc[:, -1] = np64(d["v"][b])
+    q = oracle.finish_heads(np64(d["q"][b:b + 1]), last, f, w.rd, w.rope_scale, store=store_of(w))
+    # keys lo..c-1 re-indexed from 0: the row sits at c-1-lo and reads them all
+    o, P = oracle.attend(q, kc, vc, np.array([c - 1 - lo]), w.scale, want_probs=True)
+    probs = np.zeros((w.n_heads, c))
+    probs[:, lo:] = P[0]
+    return o[0], probs

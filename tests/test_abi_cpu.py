@@ -78,11 +78,11 @@ P = ctypes.c_void_p(4096)
 
 
 def prefill(**kw):
-    a = dict(q=P, k=P, v=P, dtype=1, n_seq=1, nh=8, nkv=2, hd=128, cap=256, n_tok=16, cu=P, st=P,
+    a = dict(q=P, k=P, v=P, dtype=1, n_seq=1, nh=8, nkv=2, hd=128, cap=256, ring=0, n_tok=16, cu=P, st=P,
              max_chunk=16, max_end=64, scale=0.088, window=0, out=P, ws=None, wsb=0, stream=None)
     a.update(kw)
     return api.lib().attn_prefill_chunk(a["q"], a["k"], a["v"], a["dtype"], a["n_seq"], a["nh"],
-                                        a["nkv"], a["hd"], a["cap"], a["n_tok"], a["cu"], a["st"],
+                                        a["nkv"], a["hd"], a["cap"], a["ring"], a["n_tok"], a["cu"], a["st"],
                                         a["max_chunk"], a["max_end"], a["scale"], a["window"],
                                         a["out"], a["ws"], a["wsb"], a["stream"])
 
@@ -95,6 +95,12 @@ def test_prefill_validation():
     assert prefill(max_end=257) == ECAP
     assert prefill(scale=float("nan")) == EINVAL
     assert prefill(window=-1) == EINVAL
+    assert prefill(ring=2) == EINVAL
+    # a ring that has wrapped needs a window, and window + max_chunk - 1 rows
+    assert prefill(ring=1, max_end=300) == ECAP
+    assert prefill(ring=1, max_end=300, window=250) == ECAP
+    # bf16 ring rows come in whole 64-key tiles
+    assert prefill(ring=1, max_end=300, window=100, cap=200) == EUNSUP
     assert prefill(q=None) == EINVAL
     assert prefill(cu=None) == EINVAL
     # empty work: OK and nothing launched
@@ -104,17 +110,19 @@ def test_prefill_validation():
 
 
 def append(**kw):
-    a = dict(kc=P, vc=P, dtype=1, n_seq=1, nkv=2, hd=128, cap=256, kn=P, vn=P, n_tok=16, cu=P,
+    a = dict(kc=P, vc=P, dtype=1, n_seq=1, nkv=2, hd=128, cap=256, ring=0, kn=P, vn=P, n_tok=16, cu=P,
              st=P, max_chunk=16, max_end=64, f=P, rd=128, rs=1.0, norm=0, w=None, eps=1e-6)
     a.update(kw)
     return api.lib().attn_kv_append(a["kc"], a["vc"], a["dtype"], a["n_seq"], a["nkv"], a["hd"],
-                                    a["cap"], a["kn"], a["vn"], a["n_tok"], a["cu"], a["st"],
+                                    a["cap"], a["ring"], a["kn"], a["vn"], a["n_tok"], a["cu"], a["st"],
                                     a["max_chunk"], a["max_end"], a["f"], a["rd"], a["rs"],
                                     a["norm"], a["w"], a["eps"], None)
 
 
 def test_append_validation():
     assert append(max_end=300) == ECAP
+    assert append(ring=3) == EINVAL
+    assert append(ring=1, max_end=300, n_seq=0) == OK     # a ring has a row for every position
     assert append(rd=63) == EINVAL
     assert append(f=None) == EINVAL
     assert append(norm=1, w=None) == EINVAL
@@ -146,11 +154,11 @@ def test_rope_validation():
 
 
 def decode(**kw):
-    a = dict(q=P, k=P, v=P, dtype=1, n_seq=4, nh=32, nkv=8, hd=128, cap=4096, ctx=P, max_ctx=4096,
+    a = dict(q=P, k=P, v=P, dtype=1, n_seq=4, nh=32, nkv=8, hd=128, cap=4096, ring=0, ctx=P, max_ctx=4096,
              scale=0.088, window=0, out=P, probs=None, ld=0, ws=P, wsb=1 << 30)
     a.update(kw)
     return api.lib().attn_decode(a["q"], a["k"], a["v"], a["dtype"], a["n_seq"], a["nh"],
-                                 a["nkv"], a["hd"], a["cap"], a["ctx"], a["max_ctx"], a["scale"],
+                                 a["nkv"], a["hd"], a["cap"], a["ring"], a["ctx"], a["max_ctx"], a["scale"],
                                  a["window"], a["out"], a["probs"], a["ld"], a["ws"], a["wsb"],
                                  None)
 
@@ -164,6 +172,10 @@ def test_decode_validation():
     assert decode(wsb=16) == EINVAL
     assert decode(hd=256) == EUNSUP
     assert decode(window=-5) == EINVAL
+    assert decode(ring=-1) == EINVAL
+    # a wrapped ring holds the last cap keys: 0 < window <= cap
+    assert decode(ring=1, max_ctx=5000, probs=P, ld=5000) == ECAP
+    assert decode(ring=1, max_ctx=5000, window=4097) == ECAP
     assert decode(n_seq=0) == OK
     assert decode(max_ctx=0) == OK
 

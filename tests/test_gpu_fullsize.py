@@ -9,7 +9,8 @@ import torch
 
 import oracle
 from chunked_prefill_causal_rope_amd import runner, workloads as wl
-from parity_util import check_bf16_rows, np64, oracle_rows, oracle_table, say
+from parity_util import (check_bf16_rows, check_probs, np64, oracle_decode_row, oracle_rows,
+                         oracle_table, say)
 
 pytestmark = pytest.mark.gpu
 DEV = "cuda:0"
@@ -115,33 +116,24 @@ def check_decode(name):
     picks = sorted({int(order[0]), int(order[1]), int(order[-1]), int(order[-2]),
                     int(order[len(ctx) // 2]), 7})
     say(f"  checking sequences {picks} with ctx {[ctx[b] for b in picks]}")
-    f = oracle_table(w)
     out = np64(step.out)
+    cap = step.cap
     for b in picks:
         c = ctx[b]
-        pos = np.array([c - 1])
-        kc = np64(d["k_cache"][b, :, :c])
-        vc = np64(d["v_cache"][b, :, :c])
-        kc[:, c - 1] = oracle.finish_heads(np64(d["k"][b:b + 1]), pos, f, w.rd,
-                                           store=oracle.STORE_BF16)[0]
-        vc[:, c - 1] = np64(d["v"][b])
-        q = oracle.finish_heads(np64(d["q"][b:b + 1]), pos, f, w.rd, store=oracle.STORE_BF16)
-        o, P = oracle.attend(q, kc, vc, pos, w.scale, want_probs=True, window=w.window)
-        check_bf16_rows(out[b], o[0], f"{name} seq {b} ctx {c}")
+        o, P = oracle_decode_row(w, d, b, c)
+        check_bf16_rows(out[b], o, f"{name} seq {b} ctx {c}")
         pg = np64(step.probs[b])
         assert np.all(np.isnan(pg[:, c:])), "entries past ctx must stay untouched"
         pg = pg[:, :c]
         if w.window and c > w.window:
             # keys before the window: probability exactly 0
             assert np.all(pg[:, :c - w.window] == 0.0)
-        assert np.allclose(pg.sum(-1), 1.0, atol=1e-5)
-        rel = np.max(np.abs(pg - P[0]), axis=-1) / np.sqrt(np.mean(P[0] ** 2, axis=-1))
-        say(f"    probs worst row err/rms {rel.max():.3e}")
-        assert rel.max() <= 2e-2
+        check_probs(pg, P, True, f"{name} seq {b} ctx {c}")
     # all outputs finite, every appended row in place
     assert np.all(np.isfinite(out))
     for b, c in enumerate(ctx):
-        assert torch.equal(step.v_cache[b, :, c - 1], d["v"][b].to(DEV))
+        row = (c - 1) % cap if w.ring else c - 1
+        assert torch.equal(step.v_cache[b, :, row], d["v"][b].to(DEV))
 
 
 def test_c2_decode_full():
@@ -157,3 +149,22 @@ def test_c4_yarn_128k_sw4096_full():
     # sides of chunk boundaries, before and after the window fills
     w, d, run = run_prefill("c4_yarn_128k_sw4096")
     check_sequence(w, d, run, 0, 405, "c4 window", check_cache=False)
+
+
+def test_c2_decode_sw4096_ring_full():
+    check_decode("c2_decode_sw4096_ring")
+
+
+def test_c4_yarn_128k_sw4096_ring_full():
+    # the 128K prompt through a 6144-row ring: sampled rows against the
+    # oracle, and every output bit-equal to the run over a full-length cache
+    w, d, run = run_prefill("c4_yarn_128k_sw4096_ring")
+    assert run.k_cache.shape[2] == 6144
+    check_sequence(w, d, run, 0, 406, "c4 ring", check_cache=False)
+    got = run.gather("out")
+    del run
+    torch.cuda.empty_cache()
+    lin = runner.ChunkedPrefill(wl.CONFIGS["c4_yarn_128k_sw4096"], dict(d, cap=None), device=DEV)
+    lin.run_all()
+    torch.cuda.synchronize()
+    assert torch.equal(got.view(torch.int32), lin.gather("out").view(torch.int32))
