@@ -75,6 +75,10 @@ def _load():
     lib.orc_attend_window.restype = ctypes.c_int
     lib.orc_head_importance.argtypes = [_dp, ctypes.c_int, ctypes.c_long, ctypes.c_long, _dp]
     lib.orc_head_importance.restype = ctypes.c_int
+    lib.orc_vnorm_heads.argtypes = [_dp, ctypes.c_long, ctypes.c_int, ctypes.c_double, ctypes.c_int]
+    lib.orc_vnorm_heads.restype = None
+    lib.orc_output_gate.argtypes = [_dp, _dp, ctypes.c_long, ctypes.c_int, ctypes.c_long, ctypes.c_int]
+    lib.orc_output_gate.restype = ctypes.c_int
     _lib = lib
     return lib
 
@@ -146,6 +150,35 @@ def finish_heads(x, pos, inv_freq, rotary_dim: int, rope_scale: float = 1.0,
                              f.ctypes.data_as(_fp), rd, rope_scale, norm_style, wp, eps, store,
                              n_threads or default_threads())
     return a
+
+
+GATE_NONE, GATE_SIGMOID, GATE_SOFTPLUS_HEAD, GATE_SOFTPLUS = 0, 1, 2, 3
+
+
+def vnorm_heads(v, eps: float = 1e-6, store: int = STORE_F32) -> np.ndarray:
+    """Scale-less RMS norm of every V head row, v [..][hd]: v / sqrt(mean v^2
+    + eps), then the storage rounding.  [ATT] fn vnorm_head."""
+    a = _f64(v).copy()
+    hd = a.shape[-1]
+    _load().orc_vnorm_heads(a.ctypes.data_as(_dp), a.size // hd, hd, eps, store)
+    return a
+
+
+def output_gate(out, gate, mode: int) -> np.ndarray:
+    """Gate the attention output out [n][nh][hd] (a new array): mode 1
+    multiplies by sigmoid(gate) elementwise, gate [n][nh][hd] ([ATT] fn
+    apply_gate); mode 2 by softplus of one value per head, gate [n][nh];
+    mode 3 by softplus elementwise ([ATT] fn apply_projected_gate)."""
+    o = _f64(out).copy()
+    hd = o.shape[-1]
+    rows = o.size // hd
+    g = _f64(gate).reshape(rows, -1).copy()
+    if mode == GATE_NONE:
+        return o
+    if _load().orc_output_gate(o.ctypes.data_as(_dp), g.ctypes.data_as(_dp), rows, hd,
+                               g.shape[1], mode) != 0:
+        raise ValueError("oracle output_gate: bad mode")
+    return o
 
 
 # --------------------------------------------------------------------------

@@ -435,3 +435,63 @@ int orc_head_importance(const double *probs, int nh, long ctx, long probs_ld, do
     }
     return 0;
 }
+
+/* ------------------------------------------------------------------------ */
+/* V-norm and output gates                                                   */
+/* ------------------------------------------------------------------------ */
+
+/*
+ * [ATT] fn vnorm_head (Gemma-4): scale-less RMS normalisation of one V head
+ * before it enters the cache, x <- x / sqrt(mean(x^2) + eps) -- no weight, no
+ * "+1".  x: rows of hd values, in place, then the storage rounding.
+ * Reading: evaluated in double and rounded once, like the qk-norm.
+ */
+void orc_vnorm_heads(double *x, long rows, int hd, double eps, int store_dtype)
+{
+    for (long r = 0; r < rows; r++) {
+        double *row = x + r * hd;
+        double ss = 0.0;
+        for (int d = 0; d < hd; d++)
+            ss += row[d] * row[d];
+        double inv = 1.0 / sqrt(ss / (double)hd + eps);
+        for (int d = 0; d < hd; d++)
+            row[d] = round_store(row[d] * inv, store_dtype);
+    }
+}
+
+/* [ATT] fn softplus: max(x, 0) + log(1 + exp(-|x|)) */
+static double softplus(double x)
+{
+    return fmax(x, 0.0) + log1p(exp(-fabs(x)));
+}
+
+/*
+ * Output gates on the attention output out [rows][hd], rows = (token, head)
+ * pairs, gate row r at gate + r * gate_ld:
+ *   mode 1: out *= 1 / (1 + exp(-g_d))     ([ATT] fn apply_gate: the
+ *           Qwen3.5 output gate, the second half of each head's q rows)
+ *   mode 2: out *= softplus(g_0)           ([ATT] fn apply_projected_gate,
+ *           per-head gain broadcast across head_dim)
+ *   mode 3: out *= softplus(g_d)           (the same, per element)
+ * Returns 0, or -1 on a bad mode.
+ */
+int orc_output_gate(double *out, const double *gate, long rows, int hd, long gate_ld, int mode)
+{
+    if (mode < 1 || mode > 3)
+        return -1;
+    for (long r = 0; r < rows; r++) {
+        const double *g = gate + r * gate_ld;
+        double *o = out + r * hd;
+        for (int d = 0; d < hd; d++) {
+            double f;
+            if (mode == 1)
+                f = 1.0 / (1.0 + exp(-g[d]));
+            else if (mode == 2)
+                f = softplus(g[0]);
+            else
+                f = softplus(g[d]);
+            o[d] *= f;
+        }
+    }
+    return 0;
+}

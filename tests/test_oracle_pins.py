@@ -484,6 +484,62 @@ def test_ring_cache_orders():
         assert np.array_equal(first["v_cache"][:, s], lin["v_cache"][:, p])
 
 
+def test_vnorm_worked_example_and_invariants():
+    """V-norm ([ATT] fn vnorm_head: x / sqrt(mean(x^2) + eps), no weight, no
+    +1).  Pinned by a worked example, unit mean square, scale invariance, and
+    its equality with the Qwen-style qk-norm at unit weight (the pages'
+    "pure normalization")."""
+    got = oracle.vnorm_heads(np.array([[3.0, 4.0]]), eps=0.0)
+    # mean square (9 + 16) / 2 = 12.5; stored as float32
+    want = np.array([[3.0 / np.sqrt(12.5), 4.0 / np.sqrt(12.5)]], dtype=np.float32)
+    assert np.array_equal(got, want.astype(np.float64))
+    rng = np.random.default_rng(71)
+    x = rng.standard_normal((5, 3, 64)) * 3.0
+    y = oracle.vnorm_heads(x, eps=1e-6)
+    ms = np.mean(x ** 2, -1)
+    assert np.allclose(np.mean(y ** 2, -1), ms / (ms + 1e-6), rtol=3e-7)
+    assert np.allclose(oracle.vnorm_heads(7.5 * x, eps=0.0), oracle.vnorm_heads(x, eps=0.0),
+                       rtol=2e-7, atol=0)
+    unit = oracle.finish_heads(x, np.arange(5), np.zeros(0, np.float32), 0,
+                               norm_style=oracle.NORM_W, norm_w=np.ones(64, np.float32), eps=1e-6,
+                               store=oracle.STORE_F32)
+    assert np.array_equal(oracle.vnorm_heads(x, eps=1e-6, store=oracle.STORE_F32), unit)
+    # stored in bf16: each element rounded once
+    yb = oracle.vnorm_heads(x, eps=1e-6, store=oracle.STORE_BF16)
+    assert np.array_equal(yb, oracle.round_store(oracle.vnorm_heads(x, eps=1e-6), oracle.STORE_BF16))
+
+
+def test_output_gates():
+    """Output gates ([ATT] fn apply_gate: out * 1/(1+exp(-g)); fn softplus and
+    fn apply_projected_gate: out * softplus(g), per head or per element).
+    Pinned by sigmoid(0) = 1/2, sigmoid(g) + sigmoid(-g) = 1, softplus(0) =
+    ln 2, softplus(x) - softplus(-x) = x, the library routines
+    scipy.special.expit and numpy.logaddexp(0, x), and the per-head mode
+    equal to the per-element one with the value broadcast."""
+    from scipy.special import expit
+    rng = np.random.default_rng(73)
+    n, nh, hd = 3, 4, 16
+    out = rng.standard_normal((n, nh, hd))
+    zero = np.zeros((n, nh, hd))
+    assert np.array_equal(oracle.output_gate(out, zero, oracle.GATE_SIGMOID), out * 0.5)
+    g = rng.standard_normal((n, nh, hd)) * 6.0
+    ones = np.ones((n, nh, hd))
+    s_pos = oracle.output_gate(ones, g, oracle.GATE_SIGMOID)
+    s_neg = oracle.output_gate(ones, -g, oracle.GATE_SIGMOID)
+    assert np.allclose(s_pos + s_neg, 1.0, rtol=0, atol=1e-15)
+    assert np.allclose(oracle.output_gate(out, g, oracle.GATE_SIGMOID), out * expit(g), rtol=1e-14, atol=0)
+    assert np.allclose(oracle.output_gate(ones, zero, oracle.GATE_SOFTPLUS), np.log(2.0), rtol=1e-15, atol=0)
+    x = np.linspace(-50.0, 50.0, n * nh * hd).reshape(n, nh, hd)
+    sp = oracle.output_gate(ones, x, oracle.GATE_SOFTPLUS)
+    sm = oracle.output_gate(ones, -x, oracle.GATE_SOFTPLUS)
+    assert np.allclose(sp - sm, x, rtol=1e-14, atol=1e-13)
+    assert np.allclose(sp, np.logaddexp(0.0, x), rtol=1e-14, atol=0)
+    gh = rng.standard_normal((n, nh)) * 4.0
+    per_head = oracle.output_gate(out, gh, oracle.GATE_SOFTPLUS_HEAD)
+    broadcast = oracle.output_gate(out, np.repeat(gh[..., None], hd, -1), oracle.GATE_SOFTPLUS)
+    assert np.array_equal(per_head, broadcast)
+
+
 MUTATIONS = {
     "mask_off_by_one": ("(long)jb->qpos[t] + 1 - first,", "(long)jb->qpos[t] - first,"),
     "window_one_short": ("first = (long)jb->qpos[t] + 1 - jb->window;", "first = (long)jb->qpos[t] + 2 - jb->window;"),
@@ -494,6 +550,10 @@ MUTATIONS = {
     "probs_not_normalised": ("scratch[j] /= l;", "scratch[j] /= (l + 1e-3);"),
     "bf16_truncation": ("double r = nearbyint(ldexp(x, -q));", "double r = trunc(ldexp(x, -q));"),
     "importance_skips_a_head": ("for (int h = 0; h < nh; h++)\n            s += probs", "for (int h = 1; h < nh; h++)\n            s += probs"),
+    "vnorm_sum_not_mean": ("double inv = 1.0 / sqrt(ss / (double)hd + eps);", "double inv = 1.0 / sqrt(ss + eps);"),
+    "sigmoid_sign": ("f = 1.0 / (1.0 + exp(-g[d]));", "f = 1.0 / (1.0 + exp(g[d]));"),
+    "softplus_without_max": ("return fmax(x, 0.0) + log1p(exp(-fabs(x)));", "return log1p(exp(-fabs(x)));"),
+    "softplus_head_per_element": ("f = softplus(g[0]);", "f = softplus(g[d]);"),
 }
 
 
@@ -515,7 +575,8 @@ def _pins_pass():
               test_rmsnorm_worked_example_and_styles, test_rmsnorm_unit_rms_then_rope_order,
               lambda: test_brute_force_matrix_softmax(5, 7), test_gqa_equals_mha_with_repeated_kv,
               test_attention_head_uniform_page_example, test_bf16_rounding_matches_torch_on_float32_values,
-              test_head_importance_mass_and_special_cases, test_sliding_window_special_cases]
+              test_head_importance_mass_and_special_cases, test_sliding_window_special_cases,
+              test_vnorm_worked_example_and_invariants, test_output_gates]
     for c in checks:
         try:
             c()
