@@ -48,14 +48,15 @@ def lib() -> ctypes.CDLL:
     L.attn_yarn_inv_freq.argtypes = [i, d, d, i, d, d, fp]
     L.attn_rope_apply.argtypes = [vp, vp, i, i, i, i, i, vp, vp, i, vp, i, f, i, vp, d, vp]
     L.attn_kv_append.argtypes = [vp, vp, i, i, i, i, i, i, vp, vp, i, vp, vp, i, i, vp, i, f, i,
-                                 vp, d, vp]
+                                 vp, d, i, vp]
     L.attn_rope_qkv.argtypes = [vp, vp, i, vp, vp, vp, vp, i, i, i, i, i, i, i, vp, vp, i, i, vp, i,
-                                f, i, vp, vp, d, vp]
-    L.attn_prefill_chunk.argtypes = [vp, vp, vp, i, i, i, i, i, i, i, i, vp, vp, i, i, f, i, vp,
-                                     vp, sz, vp]
+                                f, i, vp, vp, d, i, vp]
+    L.attn_prefill_chunk.argtypes = [vp, vp, vp, i, i, i, i, i, i, i, i, vp, vp, i, i, f, i, vp, i,
+                                     i, vp, vp, sz, vp]
     L.attn_prefill_workspace_bytes.argtypes = [i, i, i, i, i, i, i]
     L.attn_prefill_workspace_bytes.restype = sz
-    L.attn_decode.argtypes = [vp, vp, vp, i, i, i, i, i, i, i, vp, i, f, i, vp, vp, i, vp, sz, vp]
+    L.attn_decode.argtypes = [vp, vp, vp, i, i, i, i, i, i, i, vp, i, f, i, vp, i, i, vp, vp, i, vp,
+                              sz, vp]
     L.attn_decode_workspace_bytes.argtypes = [i, i, i, i, i]
     L.attn_decode_importance.argtypes = [vp, i, i, i, vp, i, vp, i, i, vp]
     L.attn_decode_importance.restype = i
@@ -93,6 +94,28 @@ def _dev(t: torch.Tensor | None, name: str, dtype=None):
     if dtype is not None and t.dtype != dtype:
         raise TypeError(f"{name} must be {dtype}, got {t.dtype}")
     return t.data_ptr()
+
+
+GATE_NONE, GATE_SIGMOID, GATE_SOFTPLUS_HEAD, GATE_SOFTPLUS = 0, 1, 2, 3
+
+
+def _gate(gate: torch.Tensor | None, mode: int, n_rows: int, n_heads: int, head_dim: int, dtype):
+    """(pointer, mode, gate_ld) of an output gate: [n_rows][n_heads][>= head_dim]
+    per element, [n_rows][n_heads] (or [..][..][1+]) per head; the innermost
+    dim must be contiguous and the heads evenly strided (a view of the raw
+    query projection's second halves is fine)."""
+    if mode == GATE_NONE or gate is None:
+        return None, GATE_NONE, 0
+    if not gate.is_cuda or gate.dtype != dtype:
+        raise ValueError("gate must be a device tensor of the call's dtype")
+    g = gate if gate.dim() == 3 else gate.unsqueeze(-1)
+    assert g.shape[0] >= n_rows and g.shape[1] == n_heads
+    assert g.stride(-1) == 1 or g.shape[-1] == 1
+    ld = g.stride(1)
+    assert g.stride(0) == n_heads * ld, "heads must be evenly strided across rows"
+    if mode != GATE_SOFTPLUS_HEAD:
+        assert g.shape[2] >= head_dim
+    return g.data_ptr(), mode, ld
 
 
 def _stream():
@@ -157,9 +180,10 @@ def rope_apply(x: torch.Tensor, y: torch.Tensor, batch: Batch, inv_freq: torch.T
 def kv_append(k_cache: torch.Tensor, v_cache: torch.Tensor, k_new: torch.Tensor,
               v_new: torch.Tensor, batch: Batch, inv_freq: torch.Tensor, rotary_dim: int,
               rope_scale: float = 1.0, norm: int = NORM_NONE,
-              norm_w: torch.Tensor | None = None, eps: float = 1e-6, ring: bool = False):
+              norm_w: torch.Tensor | None = None, eps: float = 1e-6, ring: bool = False,
+              v_norm: bool = False):
     """Finish K rows and write them with the V rows at their positions (row
-    p mod cap with ring=True)."""
+    p mod cap with ring=True); v_norm RMS-normalises the V rows first."""
     n_seq_c, n_kv, cap, hd = k_cache.shape
     assert v_cache.shape == k_cache.shape and n_seq_c >= batch.n_seq
     n_tok = k_new.shape[0]
@@ -171,7 +195,7 @@ def kv_append(k_cache: torch.Tensor, v_cache: torch.Tensor, k_new: torch.Tensor,
         _dev(batch.cu_seq, "cu_seq", torch.int32), _dev(batch.start, "start", torch.int32),
         batch.max_chunk, batch.max_end,
         _dev(inv_freq, "inv_freq", torch.float32) if rotary_dim else None, rotary_dim,
-        rope_scale, norm, _dev(norm_w, "norm_w", torch.float32), eps, _stream())
+        rope_scale, norm, _dev(norm_w, "norm_w", torch.float32), eps, int(v_norm), _stream())
     _check("attn_kv_append", st)
 
 
@@ -179,7 +203,7 @@ def rope_qkv(q: torch.Tensor, q_out: torch.Tensor, k_cache: torch.Tensor, v_cach
              k_new: torch.Tensor, v_new: torch.Tensor, batch: Batch, inv_freq: torch.Tensor,
              rotary_dim: int, rope_scale: float = 1.0, norm: int = NORM_NONE,
              q_norm_w: torch.Tensor | None = None, k_norm_w: torch.Tensor | None = None,
-             eps: float = 1e-6, ring: bool = False):
+             eps: float = 1e-6, ring: bool = False, v_norm: bool = False):
     """rope_apply(q -> q_out) and kv_append(k_new, v_new) of one chunk in one call."""
     n_tok, n_heads, hd = q.shape
     assert q_out.shape == q.shape and q_out.dtype == q.dtype and n_tok >= batch.n_tok
@@ -194,7 +218,7 @@ def rope_qkv(q: torch.Tensor, q_out: torch.Tensor, k_cache: torch.Tensor, v_cach
         _dev(batch.start, "start", torch.int32), batch.max_chunk, batch.max_end,
         _dev(inv_freq, "inv_freq", torch.float32) if rotary_dim else None, rotary_dim,
         rope_scale, norm, _dev(q_norm_w, "q_norm_w", torch.float32),
-        _dev(k_norm_w, "k_norm_w", torch.float32), eps, _stream())
+        _dev(k_norm_w, "k_norm_w", torch.float32), eps, int(v_norm), _stream())
     _check("attn_rope_qkv", st)
 
 
@@ -205,9 +229,11 @@ def prefill_workspace_bytes(batch: Batch, n_heads: int, n_kv: int, head_dim: int
 
 def prefill_chunk(q: torch.Tensor, k_cache: torch.Tensor, v_cache: torch.Tensor, batch: Batch,
                   scale: float, out: torch.Tensor, workspace: torch.Tensor | None = None,
-                  window: int = 0, ring: bool = False):
+                  window: int = 0, ring: bool = False, gate: torch.Tensor | None = None,
+                  gate_mode: int = GATE_NONE):
     """Causal attention of a chunk batch; window > 0 keeps keys p-window+1..p;
-    ring=True reads key j from cache row j mod cap."""
+    ring=True reads key j from cache row j mod cap; gate/gate_mode gate the
+    output rows."""
     n_tok, nh, hd = q.shape
     n_seq_c, n_kv, cap, hd2 = k_cache.shape
     assert hd2 == hd and out.shape == (n_tok, nh, hd) and out.dtype == torch.float32
@@ -218,7 +244,7 @@ def prefill_chunk(q: torch.Tensor, k_cache: torch.Tensor, v_cache: torch.Tensor,
         _dev(q, "q"), _dev(k_cache, "k_cache"), _dev(v_cache, "v_cache"), _dtype_code(q),
         batch.n_seq, nh, n_kv, hd, cap, int(ring), n_tok, _dev(batch.cu_seq, "cu_seq", torch.int32),
         _dev(batch.start, "start", torch.int32), batch.max_chunk, batch.max_end, scale, window,
-        _dev(out, "out"), ws, wsb, _stream())
+        *_gate(gate, gate_mode, n_tok, nh, hd, q.dtype), _dev(out, "out"), ws, wsb, _stream())
     _check("attn_prefill_chunk", st)
 
 
@@ -239,9 +265,11 @@ def decode_importance(probs: torch.Tensor, ctx: torch.Tensor, max_ctx: int, imp:
 
 def decode(q: torch.Tensor, k_cache: torch.Tensor, v_cache: torch.Tensor, ctx: torch.Tensor,
            max_ctx: int, scale: float, out: torch.Tensor, probs: torch.Tensor | None = None,
-           workspace: torch.Tensor | None = None, window: int = 0, ring: bool = False):
+           workspace: torch.Tensor | None = None, window: int = 0, ring: bool = False,
+           gate: torch.Tensor | None = None, gate_mode: int = GATE_NONE):
     """One-query attention over ctx[b] keys; window > 0 keeps the last window keys;
-    ring=True reads key j from cache row j mod cap."""
+    ring=True reads key j from cache row j mod cap; gate/gate_mode gate the
+    output rows."""
     n_seq, nh, hd = q.shape
     n_seq_c, n_kv, cap, hd2 = k_cache.shape
     assert hd2 == hd and n_seq_c >= n_seq and out.shape == (n_seq, nh, hd)
@@ -254,6 +282,7 @@ def decode(q: torch.Tensor, k_cache: torch.Tensor, v_cache: torch.Tensor, ctx: t
     wsb = workspace.numel() * workspace.element_size() if workspace is not None else 0
     st = lib().attn_decode(
         _dev(q, "q"), _dev(k_cache, "k_cache"), _dev(v_cache, "v_cache"), _dtype_code(q), n_seq,
-        nh, n_kv, hd, cap, int(ring), _dev(ctx, "ctx"), max_ctx, scale, window, _dev(out, "out"),
+        nh, n_kv, hd, cap, int(ring), _dev(ctx, "ctx"), max_ctx, scale, window,
+        *_gate(gate, gate_mode, n_seq, nh, hd, q.dtype), _dev(out, "out"),
         _dev(probs, "probs"), ld, ws, wsb, _stream())
     _check("attn_decode", st)

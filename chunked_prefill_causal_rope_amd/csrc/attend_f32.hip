@@ -101,7 +101,11 @@ __global__ __launch_bounds__(256) void attend_f32_kernel(AttendF32Args a) {
     const float inv = 1.f / l;
     float* orow = a.out + ((size_t)t * a.n_heads + h) * HD;
 #pragma unroll
-    for (int e = 0; e < PER; ++e) orow[lane + 64 * e] = o[e] * inv;
+    for (int e = 0; e < PER; ++e) {
+        float y = o[e] * inv;
+        if (a.gate.mode) y *= gate_factor(a.gate, (size_t)t * a.n_heads + h, lane + 64 * e);
+        orow[lane + 64 * e] = y;
+    }
 
     if (a.decode && a.probs) {
         float* prow = a.probs + ((size_t)b * a.n_heads + h) * a.probs_ld;

@@ -52,6 +52,14 @@ size_t decode_part_bytes(int n_seq, int n_heads, int head_dim, int splits) {
     return (size_t)n_seq * n_heads * splits * (head_dim + kDecodePartPad) * sizeof(float);
 }
 
+// Output gate arguments: mode 0 needs nothing; per-element modes read
+// head_dim values per row (ld >= head_dim), the per-head mode one (ld >= 1).
+bool gate_ok(const void* gate, int mode, int ld, int head_dim) {
+    if (mode == attn::kGateNone) return true;
+    if (!gate || mode < attn::kGateSigmoid || mode > attn::kGateSoftplus) return false;
+    return mode == attn::kGateSoftplusHead ? ld >= 1 : ld >= head_dim;
+}
+
 }  // namespace
 
 extern "C" {
@@ -135,11 +143,12 @@ int attn_kv_append(void* k_cache, void* v_cache, int dtype, int n_seq, int n_kv,
                    int cap, int ring, const void* k_new, const void* v_new, int n_tok,
                    const int32_t* cu_seq, const int32_t* start, int max_chunk, int max_end,
                    const float* inv_freq, int rotary_dim, float rope_scale, int norm,
-                   const float* norm_w, double eps, void* stream) {
+                   const float* norm_w, double eps, int v_norm, void* stream) {
     int st = check_rope(dtype, n_tok, n_kv, head_dim, n_seq, cu_seq, start, max_chunk, inv_freq,
                         rotary_dim, norm, norm_w);
     if (st != ATTN_OK) return st;
-    if (cap <= 0 || max_end < 0 || (ring != 0 && ring != 1)) return ATTN_EINVAL;
+    if (cap <= 0 || max_end < 0 || (ring != 0 && ring != 1) || (v_norm != 0 && v_norm != 1))
+        return ATTN_EINVAL;
     if (!ring && max_end > cap) return ATTN_ECAPACITY;
     if (n_seq == 0 || n_tok == 0 || max_chunk == 0) return ATTN_OK;
     if (!k_cache || !v_cache || !k_new || !v_new) return ATTN_EINVAL;
@@ -159,6 +168,7 @@ int attn_kv_append(void* k_cache, void* v_cache, int dtype, int n_seq, int n_kv,
     a.head_dim = head_dim;
     a.cap = cap;
     a.ring = ring && max_end > cap;
+    a.v_norm = v_norm;
     a.n_seq = n_seq;
     a.max_chunk = max_chunk;
     a.rotary_dim = rotary_dim < head_dim ? rotary_dim : head_dim;
@@ -170,14 +180,16 @@ int attn_rope_qkv(const void* q, void* q_out, int n_heads, void* k_cache, void* 
                   const void* k_new, const void* v_new, int n_kv, int cap, int ring, int dtype, int n_tok,
                   int head_dim, int n_seq, const int32_t* cu_seq, const int32_t* start, int max_chunk,
                   int max_end, const float* inv_freq, int rotary_dim, float rope_scale, int norm,
-                  const float* q_norm_w, const float* k_norm_w, double eps, void* stream) {
+                  const float* q_norm_w, const float* k_norm_w, double eps, int v_norm,
+                  void* stream) {
     int st = check_rope(dtype, n_tok, n_heads, head_dim, n_seq, cu_seq, start, max_chunk, inv_freq,
                         rotary_dim, norm, q_norm_w);
     if (st != ATTN_OK) return st;
     st = check_rope(dtype, n_tok, n_kv, head_dim, n_seq, cu_seq, start, max_chunk, inv_freq,
                     rotary_dim, norm, k_norm_w);
     if (st != ATTN_OK) return st;
-    if (cap <= 0 || max_end < 0 || (ring != 0 && ring != 1)) return ATTN_EINVAL;
+    if (cap <= 0 || max_end < 0 || (ring != 0 && ring != 1) || (v_norm != 0 && v_norm != 1))
+        return ATTN_EINVAL;
     if (!ring && max_end > cap) return ATTN_ECAPACITY;
     if (n_seq == 0 || n_tok == 0 || max_chunk == 0) return ATTN_OK;
     if (!q || !q_out || !k_cache || !v_cache || !k_new || !v_new) return ATTN_EINVAL;
@@ -196,6 +208,7 @@ int attn_rope_qkv(const void* q, void* q_out, int n_heads, void* k_cache, void* 
     ak.n_heads = n_kv;
     ak.cap = cap;
     ak.ring = ring && max_end > cap;
+    ak.v_norm = v_norm;
     for (attn::RopeArgs* a : {&aq, &ak}) {
         a->cu_seq = cu_seq;
         a->start = start;
@@ -224,8 +237,8 @@ size_t attn_prefill_workspace_bytes(int n_seq, int n_heads, int n_kv, int head_d
 int attn_prefill_chunk(const void* q, const void* k_cache, const void* v_cache, int dtype,
                        int n_seq, int n_heads, int n_kv, int head_dim, int cap, int ring, int n_tok,
                        const int32_t* cu_seq, const int32_t* start, int max_chunk, int max_end,
-                       float scale, int window, float* out, void* workspace,
-                       size_t workspace_bytes, void* stream) {
+                       float scale, int window, const void* gate, int gate_mode, int gate_ld,
+                       float* out, void* workspace, size_t workspace_bytes, void* stream) {
     if (!dtype_ok(dtype) || !hd_ok(head_dim)) return ATTN_EUNSUPPORTED;
     if (n_seq < 0 || n_tok < 0 || max_chunk < 0 || max_end < 0 || n_heads <= 0 || n_kv <= 0 ||
         cap <= 0 || n_heads % n_kv != 0 || !isfinite(scale) || window < 0 || (ring != 0 && ring != 1))
@@ -237,7 +250,9 @@ int attn_prefill_chunk(const void* q, const void* k_cache, const void* v_cache, 
     if (!wrapped && max_end > cap) return ATTN_ECAPACITY;
     if (wrapped && (window <= 0 || (long)window + max_chunk - 1 > cap)) return ATTN_ECAPACITY;
     if (wrapped && dtype == ATTN_BF16 && cap % 64 != 0) return ATTN_EUNSUPPORTED;
+    if (!gate_ok(gate, gate_mode, gate_ld, head_dim)) return ATTN_EINVAL;
     if (n_seq == 0 || n_tok == 0 || max_chunk == 0) return ATTN_OK;
+    const attn::GateRef gref{gate, gate_mode, gate_ld, dtype == ATTN_BF16};
     if (!q || !k_cache || !v_cache || !out || !cu_seq || !start) return ATTN_EINVAL;
     if (n_seq > 65535) return ATTN_EINVAL;
     hipStream_t s = (hipStream_t)stream;
@@ -262,6 +277,7 @@ int attn_prefill_chunk(const void* q, const void* k_cache, const void* v_cache, 
         a.max_chunk = max_chunk;
         a.window = window;
         a.ring = wrapped;
+        a.gate = gref;
         return status_of(attn::launch_attend_f32(a, s));
     }
     attn::PrefillArgs a{};
@@ -283,6 +299,7 @@ int attn_prefill_chunk(const void* q, const void* k_cache, const void* v_cache, 
     a.max_end = max_end;
     a.window = window;
     a.ring = wrapped;
+    a.gate = gref;
     const attn::PrefillPlan plan = attn::plan_prefill(n_seq, n_heads, n_kv, head_dim, n_tok,
                                                       max_chunk, max_end, window,
                                                       workspace ? workspace_bytes : 0);
@@ -310,7 +327,8 @@ size_t attn_decode_workspace_bytes(int n_seq, int n_heads, int n_kv, int head_di
 
 int attn_decode(const void* q, const void* k_cache, const void* v_cache, int dtype, int n_seq,
                 int n_heads, int n_kv, int head_dim, int cap, int ring, const int32_t* ctx,
-                int max_ctx, float scale, int window, float* out, float* probs, int probs_ld, void* workspace,
+                int max_ctx, float scale, int window, const void* gate, int gate_mode, int gate_ld,
+                float* out, float* probs, int probs_ld, void* workspace,
                 size_t workspace_bytes, void* stream) {
     if (!dtype_ok(dtype) || !hd_ok(head_dim)) return ATTN_EUNSUPPORTED;
     if (n_seq < 0 || max_ctx < 0 || n_heads <= 0 || n_kv <= 0 || cap <= 0 ||
@@ -320,6 +338,8 @@ int attn_decode(const void* q, const void* k_cache, const void* v_cache, int dty
     const bool wrapped = ring && max_ctx > cap;
     if (!wrapped && max_ctx > cap) return ATTN_ECAPACITY;
     if (wrapped && (window <= 0 || window > cap)) return ATTN_ECAPACITY;
+    if (!gate_ok(gate, gate_mode, gate_ld, head_dim)) return ATTN_EINVAL;
+    const attn::GateRef gref{gate, gate_mode, gate_ld, dtype == ATTN_BF16};
     if (n_seq == 0 || max_ctx == 0) return ATTN_OK;
     if (!q || !k_cache || !v_cache || !out || !ctx) return ATTN_EINVAL;
     if (probs && probs_ld < max_ctx) return ATTN_EINVAL;
@@ -346,6 +366,7 @@ int attn_decode(const void* q, const void* k_cache, const void* v_cache, int dty
         a.probs_ld = probs_ld;
         a.window = window;
         a.ring = wrapped;
+        a.gate = gref;
         return status_of(attn::launch_attend_f32(a, s));
     }
     if (group > attn::decode_group_limit()) return ATTN_EUNSUPPORTED;
@@ -380,6 +401,7 @@ int attn_decode(const void* q, const void* k_cache, const void* v_cache, int dty
     a.n_splits = splits;
     a.window = window;
     a.ring = wrapped;
+    a.gate = gref;
     if ((long)n_seq * splits * n_kv > 0x7fffffffL) return ATTN_EINVAL;
     return status_of(attn::launch_decode_bf16(a, s));
 }

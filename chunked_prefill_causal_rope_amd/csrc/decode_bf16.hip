@@ -462,6 +462,8 @@ __global__ __launch_bounds__(256) void decode_combine_kernel(DecodeArgs a) {
     const int k_first = decode_window_first(ctx, a.window);
     const int k_base = decode_part_base(ctx, a.window);
     const int n_parts = min((ctx - k_base + a.split_len - 1) / a.split_len, a.n_splits);
+    // output gate factor of this thread's dim, loaded before the merge
+    const float gf = a.gate.mode && tid < HD ? gate_factor_bf16(a.gate, (size_t)row, tid) : 1.f;
     const float* pr = a.part + (size_t)row * a.n_splits * PS;
     float mm = -INFINITY;
     for (int s = tid; s < n_parts; s += 256) mm = fmaxf(mm, pr[(size_t)s * PS]);
@@ -502,7 +504,7 @@ __global__ __launch_bounds__(256) void decode_combine_kernel(DecodeArgs a) {
             float t = 0.f;
 #pragma unroll
             for (int q = 0; q < PH; ++q) t += osum[q * HD + tid];
-            orow[tid] = t * inv;
+            orow[tid] = t * inv * gf;
         }
     }
     if (a.probs) {

@@ -87,6 +87,38 @@ __device__ __forceinline__ void f64_to_bf16_packed(const double* v, uint32_t* u)
     }
 }
 
+// Output gate of the attention output ([ATT] fn apply_gate: times
+// sigmoid(g) per element; fn apply_projected_gate: times softplus(g), one g
+// per head or per element).  The gate value of output row `row` (token *
+// n_heads + head), dim d, is at p[row * ld + d] (p[row * ld] per head), in
+// the call's dtype.
+enum { kGateNone = 0, kGateSigmoid = 1, kGateSoftplusHead = 2, kGateSoftplus = 3 };
+struct GateRef {
+    const void* p;
+    int mode, ld, bf16;
+};
+__device__ __forceinline__ float gate_factor(const GateRef& g, size_t row, int d) {
+    const size_t i = row * (size_t)g.ld + (g.mode == kGateSoftplusHead ? 0 : d);
+    const float x = g.bf16 ? bf16_to_f32(reinterpret_cast<const uint16_t*>(g.p)[i])
+                           : reinterpret_cast<const float*>(g.p)[i];
+    if (g.mode == kGateSigmoid) return 1.f / (1.f + expf(-x));
+    return fmaxf(x, 0.f) + log1pf(expf(-fabsf(x)));
+}
+// The same factors from the hardware exp2/log2/reciprocal (relative error a
+// few float ulps; softplus of very negative x loses relative accuracy but
+// not absolute), for the bf16 kernels' epilogues.
+constexpr float kLn2 = 0.6931471805599453f;
+__device__ __forceinline__ float gate_fast(int mode, float x) {
+    if (mode == kGateSigmoid) return __builtin_amdgcn_rcpf(1.f + __builtin_amdgcn_exp2f(-x * kLog2e));
+    const float e = __builtin_amdgcn_exp2f(-__builtin_fabsf(x) * kLog2e);
+    return fmaxf(x, 0.f) + __builtin_amdgcn_logf(1.f + e) * kLn2;
+}
+// bf16 gate value of (row, d) and its factor, fast form
+__device__ __forceinline__ float gate_factor_bf16(const GateRef& g, size_t row, int d) {
+    const size_t i = row * (size_t)g.ld + (g.mode == kGateSoftplusHead ? 0 : d);
+    return gate_fast(g.mode, bf16_to_f32(reinterpret_cast<const uint16_t*>(g.p)[i]));
+}
+
 template <typename T> struct Elem;
 template <> struct Elem<float> {
     __device__ static double load(const float* p) { return (double)*p; }

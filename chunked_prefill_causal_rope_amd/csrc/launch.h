@@ -5,6 +5,8 @@
 #include <stddef.h>
 #include <stdint.h>
 
+#include "device_common.h"
+
 namespace attn {
 
 // Per-head finish (norm + RoPE + rounding) of Q rows, or of K rows into the
@@ -22,6 +24,7 @@ struct RopeArgs {
     float rope_scale;
     int n_tok, n_heads, head_dim, cap, n_seq, max_chunk, rotary_dim, norm;
     int ring;              // KV: position p in cache row p mod cap (else row p < cap)
+    int v_norm;            // KV: V rows scale-less RMS-normalised before the cache
 };
 hipError_t launch_rope_rows(const RopeArgs& a, int dtype, bool kv, hipStream_t stream);
 // Both finishes of a chunk (queries, then keys/values into the cache) in as
@@ -42,6 +45,7 @@ struct PrefillArgs {
     int n_seq, n_heads, n_kv, group, head_dim, cap, n_tok, max_chunk, max_end;
     int window;            // 0: all keys <= p; W: keys p-W+1..p
     int ring;              // key j in cache row j mod cap (needs a window; cap % 64 == 0)
+    GateRef gate;          // output gate (mode 0: none)
     // rows per workgroup, row tiles per sequence, split call (persistent
     // grid with device-chosen key-range parts, merged by the combine kernel)
     int rows_per_tile, n_qtiles, split, grid, slots;
@@ -73,6 +77,7 @@ struct AttendF32Args {
     int n_seq, n_heads, n_kv, group, head_dim, cap, n_tok, max_chunk, max_ctx, probs_ld;
     int window;            // 0: all keys <= p; W: keys p-W+1..p
     int ring;              // key j in cache row j mod cap
+    GateRef gate;          // output gate (mode 0: none)
 };
 hipError_t launch_attend_f32(const AttendF32Args& a, hipStream_t stream);
 
@@ -90,6 +95,7 @@ struct DecodeArgs {
     int split_len, n_splits;   // parts of split_len keys from the row's first key
     int window;                // 0: all ctx keys; W: the last W
     int ring;                  // key j in cache row j mod cap (needs W <= cap)
+    GateRef gate;              // output gate (mode 0: none)
 };
 int decode_group_limit();
 // Keys one decode row may read, from its part start on: max_ctx, or with a

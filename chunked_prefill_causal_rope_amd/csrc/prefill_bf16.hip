@@ -578,12 +578,54 @@ __global__ __launch_bounds__(NW * 64, 8 / NW) void prefill_bf16_kernel(PrefillAr
     if (nsp <= 1) {
         const float inv = 1.f / l_tot;
         float* orow = a.out + ((size_t)t * a.n_heads + h) * HD;
+        if (a.gate.mode) {
+            // output gate: this lane's dims db*32 + 8*q4 + 4*hf + 0..3, all
+            // loads issued before any factor is formed
+            const size_t grow = (size_t)t * a.n_heads + h;
+            const uint16_t* gp = reinterpret_cast<const uint16_t*>(a.gate.p) + grow * (size_t)a.gate.ld;
+            if (a.gate.mode == kGateSoftplusHead) {
+                const float f = gate_fast(a.gate.mode, bf16_to_f32(gp[0])) * inv;
+#pragma unroll
+                for (int db = 0; db < NDB; ++db)
+#pragma unroll
+                    for (int q = 0; q < 16; ++q) O[db][q] *= f;
+            } else {
+                u32x2_t graw[NDB][4];
+                const bool vec = ((a.gate.ld & 3) == 0) && ((reinterpret_cast<uintptr_t>(a.gate.p) & 7) == 0);
+#pragma unroll
+                for (int db = 0; db < NDB; ++db)
+#pragma unroll
+                    for (int q4 = 0; q4 < 4; ++q4) {
+                        const uint16_t* p = gp + db * 32 + 8 * q4 + 4 * hf;
+                        if (vec) {
+                            graw[db][q4] = *reinterpret_cast<const u32x2_t*>(p);
+                        } else {
+                            graw[db][q4] = u32x2_t{(uint32_t)p[0] | ((uint32_t)p[1] << 16),
+                                                   (uint32_t)p[2] | ((uint32_t)p[3] << 16)};
+                        }
+                    }
+#pragma unroll
+                for (int db = 0; db < NDB; ++db)
+#pragma unroll
+                    for (int q4 = 0; q4 < 4; ++q4) {
+                        O[db][4 * q4] *= gate_fast(a.gate.mode, bf16_lo(graw[db][q4].x)) * inv;
+                        O[db][4 * q4 + 1] *= gate_fast(a.gate.mode, bf16_hi(graw[db][q4].x)) * inv;
+                        O[db][4 * q4 + 2] *= gate_fast(a.gate.mode, bf16_lo(graw[db][q4].y)) * inv;
+                        O[db][4 * q4 + 3] *= gate_fast(a.gate.mode, bf16_hi(graw[db][q4].y)) * inv;
+                    }
+            }
+        } else {
+#pragma unroll
+            for (int db = 0; db < NDB; ++db)
+#pragma unroll
+                for (int q = 0; q < 16; ++q) O[db][q] *= inv;
+        }
 #pragma unroll
         for (int db = 0; db < NDB; ++db)
 #pragma unroll
             for (int q4 = 0; q4 < 4; ++q4) {
-                float4 v = make_float4(O[db][4 * q4] * inv, O[db][4 * q4 + 1] * inv,
-                                       O[db][4 * q4 + 2] * inv, O[db][4 * q4 + 3] * inv);
+                const float4 v = make_float4(O[db][4 * q4], O[db][4 * q4 + 1], O[db][4 * q4 + 2],
+                                             O[db][4 * q4 + 3]);
                 *reinterpret_cast<float4*>(orow + db * 32 + 8 * q4 + 4 * hf) = v;
             }
     } else {
@@ -635,6 +677,11 @@ __global__ __launch_bounds__(256) void prefill_combine_kernel(PrefillArgs a) {
         // part p of this row tile and group is item first + p * n_kv + g;
         // lane p < S holds part p's (m, l), then its weight 2^(m_p - m)
         auto prow = [&](int p) { return a.part + ((size_t)(first + p * a.n_kv + g) * R + rl) * PS; };
+        // output gate factors first, so their loads overlap the merge
+        float gf[PER];
+#pragma unroll
+        for (int e = 0; e < PER; ++e)
+            gf[e] = a.gate.mode ? gate_factor_bf16(a.gate, (size_t)t * a.n_heads + h, lane + 64 * e) : 1.f;
         float mp = -INFINITY, lp = 0.f;
         for (int p = lane; p < S; p += 64) {
             const float2 ml = *reinterpret_cast<const float2*>(prow(p));
@@ -681,7 +728,7 @@ __global__ __launch_bounds__(256) void prefill_combine_kernel(PrefillArgs a) {
         const float inv = l > 0.f ? 1.f / l : 0.f;
         float* orow = a.out + ((size_t)t * a.n_heads + h) * HD;
 #pragma unroll
-        for (int e = 0; e < PER; ++e) orow[lane + 64 * e] = o[e] * inv;
+        for (int e = 0; e < PER; ++e) orow[lane + 64 * e] = o[e] * inv * gf[e];
     }
 }
 

@@ -148,7 +148,16 @@ __global__ __launch_bounds__(kRopeThreads) void rope_rows_kernel(RopeArgs a) {
     if (KV) {
         const T* vs = reinterpret_cast<const T*>(a.v_src) + ((size_t)t * a.n_heads + h) * hd;
         T* vd = reinterpret_cast<T*>(a.v_dst) + (((size_t)b * a.n_heads + h) * a.cap + slot) * hd;
-        for (int e = lane; e < hd; e += 64) vd[e] = vs[e];
+        if (a.v_norm) {
+            // scale-less RMS norm of the V row, in double, rounded once
+            const double v0 = lane < hd ? Elem<T>::load(vs + lane) : 0.0;
+            const double v1 = lane + 64 < hd ? Elem<T>::load(vs + lane + 64) : 0.0;
+            const double r = 1.0 / sqrt(wave_sum(v0 * v0 + v1 * v1) / (double)hd + a.eps);
+            if (lane < hd) Elem<T>::store(vd + lane, v0 * r);
+            if (lane + 64 < hd) Elem<T>::store(vd + lane + 64, v1 * r);
+        } else {
+            for (int e = lane; e < hd; e += 64) vd[e] = vs[e];
+        }
     }
 }
 
@@ -171,6 +180,8 @@ template <> struct Raw<uint16_t> {
         w = u32x4_t{a.x, a.y, b.x, b.y};
     }
     __device__ void load8(const uint16_t* p) { w = ld16(p); }
+    // 8 values already in registers as 16-byte chunks (one for bf16)
+    __device__ void from_chunks(const u32x4_t* c) { w = c[0]; }
     __device__ double get(int e) const {
         const uint32_t u = w[e >> 1];
         return (double)((e & 1) ? bf16_hi(u) : bf16_lo(u));
@@ -185,6 +196,10 @@ template <> struct Raw<float> {
     __device__ void load8(const float* p) {
         lo = *reinterpret_cast<const f32x4_t*>(p);
         hi = *reinterpret_cast<const f32x4_t*>(p + 4);
+    }
+    __device__ void from_chunks(const u32x4_t* c) {
+        lo = __builtin_bit_cast(f32x4_t, c[0]);
+        hi = __builtin_bit_cast(f32x4_t, c[1]);
     }
     __device__ double get(int e) const { return (double)(e < 4 ? lo[e] : hi[e - 4]); }
 };
@@ -247,7 +262,7 @@ struct RopeTokArgs {
     const float* inv_freq;
     double eps;
     float rope_scale;
-    int n_tok, cap, rotary_dim, norm, ring;
+    int n_tok, cap, rotary_dim, norm, ring, v_norm;
 };
 
 template <typename T, int HD>
@@ -293,7 +308,7 @@ __global__ __launch_bounds__(kTokThreads) void rope_token_kernel(RopeTokArgs a) 
     const int kh = vh - nq;
 
     Raw<T> raw;
-    u32x4_t vbuf[VCH];
+    u32x4_t vbuf[VCH] = {};
     if (valid) {
         const T* row = is_q ? reinterpret_cast<const T*>(a.qx) + ((size_t)t * nq + vh) * HD
                             : reinterpret_cast<const T*>(a.kx) + ((size_t)t * a.nk + kh) * HD;
@@ -363,7 +378,24 @@ __global__ __launch_bounds__(kTokThreads) void rope_token_kernel(RopeTokArgs a) 
     } else {
         store_vals(dst + d0, v, 8);
     }
-    if (!is_q) {
+    if (a.v_norm) {
+        // V rows: scale-less RMS norm over the row's lanes (dims 8c..8c+7
+        // each), in double, each value rounded once; query rows of the wave
+        // take part in the row sums with their own (unused) groups
+        Raw<T> vr;
+        vr.from_chunks(vbuf);
+        double w[8], ss = 0.0;
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+            w[e] = vr.get(e);
+            ss += w[e] * w[e];
+        }
+        ss = group_sum<TPH>(ss);
+        const double r = 1.0 / sqrt(ss / (double)HD + a.eps);
+#pragma unroll
+        for (int e = 0; e < 8; ++e) w[e] *= r;
+        if (!is_q) store_vals(reinterpret_cast<T*>(a.vc) + (((size_t)b * a.nk + kh) * a.cap + slot) * HD + c * 8, w, 8);
+    } else if (!is_q) {
         T* vd = reinterpret_cast<T*>(a.vc) + (((size_t)b * a.nk + kh) * a.cap + slot) * HD + c * 8;
 #pragma unroll
         for (int j = 0; j < VCH; ++j) st16(vd + j * VPER, vbuf[j]);
@@ -400,6 +432,7 @@ static RopeTokArgs token_args(const RopeArgs* q, const RopeArgs* kv) {
         t.nk = kv->n_heads;
         t.cap = kv->cap;
         t.ring = kv->ring;
+        t.v_norm = kv->v_norm;
     }
     t.cu_seq = r.cu_seq;
     t.start = r.start;

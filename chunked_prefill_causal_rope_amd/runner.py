@@ -54,6 +54,7 @@ class ChunkedPrefill:
         self.q_norm_w = data["q_norm_w"].to(device) if data.get("q_norm_w") is not None else None
         self.k_norm_w = data["k_norm_w"].to(device) if data.get("k_norm_w") is not None else None
         q, k, v = data["q"], data["k"], data["v"]
+        gate = data.get("gate")
         self.steps = []
         for step in chunk_schedule(lengths, self.chunk):
             per_seq = {b: (p, c) for b, p, c in step}
@@ -68,13 +69,16 @@ class ChunkedPrefill:
             if rows == list(range(r0, r1)):
                 sl = slice(r0, r1)
                 qs, ks, vs = q[sl], k[sl], v[sl]
+                gs = gate[sl] if gate is not None else None
             else:
                 idx = torch.tensor(rows, dtype=torch.long, device=q.device)
                 qs, ks, vs = q[idx], k[idx], v[idx]
+                gs = gate[idx] if gate is not None else None
             qs, ks, vs = (x.to(device).contiguous() for x in (qs, ks, vs))
+            gs = gs.to(device).contiguous() if gs is not None else None
             n_tok = len(rows)
             self.steps.append(dict(
-                batch=batch, rows=rows, q=qs, k=ks, v=vs,
+                batch=batch, rows=rows, q=qs, k=ks, v=vs, gate=gs,
                 q_rot=torch.empty_like(qs),
                 out=torch.empty((n_tok, nh, hd), dtype=torch.float32, device=device)))
         ws = max(api.prefill_workspace_bytes(s["batch"], nh, nkv, hd) for s in self.steps)
@@ -87,19 +91,21 @@ class ChunkedPrefill:
         if fused:
             api.rope_qkv(s["q"], s["q_rot"], self.k_cache, self.v_cache, s["k"], s["v"], s["batch"],
                          self.inv_freq, w.rd, w.rope_scale, w.norm_style, self.q_norm_w,
-                         self.k_norm_w, w.norm_eps, ring=w.ring)
+                         self.k_norm_w, w.norm_eps, ring=w.ring, v_norm=w.v_norm)
         else:
             api.rope_apply(s["q"], s["q_rot"], s["batch"], self.inv_freq, w.rd, w.rope_scale,
                            w.norm_style, self.q_norm_w, w.norm_eps)
             api.kv_append(self.k_cache, self.v_cache, s["k"], s["v"], s["batch"], self.inv_freq,
-                          w.rd, w.rope_scale, w.norm_style, self.k_norm_w, w.norm_eps, ring=w.ring)
+                          w.rd, w.rope_scale, w.norm_style, self.k_norm_w, w.norm_eps, ring=w.ring,
+                          v_norm=w.v_norm)
         if attend:
             self.attend_step(i)
 
     def attend_step(self, i: int):
         s = self.steps[i]
         api.prefill_chunk(s["q_rot"], self.k_cache, self.v_cache, s["batch"], self.w.scale,
-                          s["out"], self.workspace, window=self.w.window, ring=self.w.ring)
+                          s["out"], self.workspace, window=self.w.window, ring=self.w.ring,
+                          gate=s["gate"], gate_mode=self.w.gate_mode)
 
     def run_all(self, fused: bool = True):
         for i in range(len(self.steps)):
@@ -137,6 +143,7 @@ class DecodeStep:
         self.inv_freq = tables(w, device)
         self.q_norm_w = data["q_norm_w"].to(device) if data.get("q_norm_w") is not None else None
         self.k_norm_w = data["k_norm_w"].to(device) if data.get("k_norm_w") is not None else None
+        self.gate = data["gate"].to(device).contiguous() if data.get("gate") is not None else None
         self.batch = api.Batch([c - 1 for c in ctx], [1] * n_seq, device=device)
         self.ctx = torch.tensor(ctx, dtype=torch.int32, device=device)
         self.out = torch.empty((n_seq, w.n_heads, w.head_dim), dtype=torch.float32, device=device)
@@ -153,11 +160,12 @@ class DecodeStep:
         w = self.w
         api.rope_qkv(self.q, self.q_rot, self.k_cache, self.v_cache, self.k, self.v, self.batch,
                      self.inv_freq, w.rd, w.rope_scale, w.norm_style, self.q_norm_w,
-                     self.k_norm_w, w.norm_eps, ring=w.ring)
+                     self.k_norm_w, w.norm_eps, ring=w.ring, v_norm=w.v_norm)
 
     def attend(self):
         api.decode(self.q_rot, self.k_cache, self.v_cache, self.ctx, self.max_ctx, self.w.scale,
-                   self.out, self.probs, self.workspace, window=self.w.window, ring=self.w.ring)
+                   self.out, self.probs, self.workspace, window=self.w.window, ring=self.w.ring,
+                   gate=self.gate, gate_mode=self.w.gate_mode)
 
     def run(self):
         self.finish_and_append()

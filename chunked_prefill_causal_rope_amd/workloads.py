@@ -7,8 +7,9 @@ path and the CPU oracle can be fed the very same tensors.
 Draw order, per workload, from one generator seeded with ``Workload.seed``:
 prompt lengths (or decode context lengths), then Q, K, V (or, for decode, the
 K cache, the V cache, then the new token's q, k, v), then the q-norm and
-k-norm weights when the workload has qk-norm.  Values are N(0, 1) drawn in
-float32 and cast to the workload dtype; norm weights are 1 + 0.1 * N(0, 1).
+k-norm weights when the workload has qk-norm, then the output gate when it
+has one.  Values are N(0, 1) drawn in float32 and cast to the workload dtype;
+norm weights are 1 + 0.1 * N(0, 1).
 """
 from __future__ import annotations
 
@@ -38,6 +39,8 @@ class Workload:
     norm_eps: float = 1e-6
     window: int = 0                        # 0: full causal; W: the last W keys only
     ring: bool = False                     # cache of `cap` rows, position p in row p mod cap
+    gate_mode: int = 0                     # output gate: 0 none, 1 sigmoid, 2 softplus/head, 3 softplus
+    v_norm: bool = False                   # V rows RMS-normalised before the cache
     # prefill
     n_seq: int = 1
     prompt_len: int = 0                    # fixed length when len_range is None
@@ -93,6 +96,10 @@ CONFIGS = {
 CONFIGS["c4_yarn_128k_sw4096"] = CONFIGS["c4_yarn_128k"].replace(name="c4_yarn_128k_sw4096",
                                                                  window=4096)
 CONFIGS["c2_decode_sw4096"] = CONFIGS["c2_decode"].replace(name="c2_decode_sw4096", window=4096)
+# The Qwen-style varlen prefill with the Qwen3.5 output gate (sigmoid per
+# element).
+CONFIGS["c3_qwen_varlen_gate"] = CONFIGS["c3_qwen_varlen"].replace(name="c3_qwen_varlen_gate",
+                                                                   gate_mode=1)
 # The same windows over a ring cache: 4096 + 2048 - 1 rows rounded up to a
 # multiple of 64 for the prefill (a chunk is written before it attends), 4096
 # rows for decode.
@@ -110,6 +117,14 @@ def _gen(seed: int, device) -> torch.Generator:
 
 def _normal(shape, g, device, dtype):
     return torch.randn(shape, generator=g, device=device, dtype=torch.float32).to(dtype)
+
+
+def _gate(w: Workload, rows: int, g, device):
+    """Output gate values: [rows][n_heads][head_dim], or [rows][n_heads] per head."""
+    if not w.gate_mode:
+        return None
+    shape = (rows, w.n_heads) if w.gate_mode == 2 else (rows, w.n_heads, w.head_dim)
+    return _normal(shape, g, device, w.torch_dtype)
 
 
 def prompt_lengths(w: Workload, g=None, device="cpu") -> list[int]:
@@ -138,7 +153,9 @@ def gen_prefill(w: Workload, device="cpu"):
     for n in lengths:
         cu.append(cu[-1] + n)
     cap = w.cap if w.cap is not None else max(lengths)
-    return dict(q=q, k=k, v=v, lengths=lengths, cu_seq=cu, q_norm_w=qw, k_norm_w=kw, cap=cap)
+    gate = _gate(w, T, g, device)
+    return dict(q=q, k=k, v=v, lengths=lengths, cu_seq=cu, q_norm_w=qw, k_norm_w=kw, cap=cap,
+                gate=gate)
 
 
 def gen_decode(w: Workload, device="cpu"):
@@ -160,8 +177,9 @@ def gen_decode(w: Workload, device="cpu"):
     if w.norm_style != NORM_NONE:
         qw = (1.0 + 0.1 * torch.randn((w.head_dim,), generator=g, device=device)).float()
         kw = (1.0 + 0.1 * torch.randn((w.head_dim,), generator=g, device=device)).float()
+    gate = _gate(w, w.n_seq, g, device)
     return dict(ctx=ctx, k_cache=kc, v_cache=vc, q=q, k=k, v=v, q_norm_w=qw, k_norm_w=kw,
-                cap=cap)
+                cap=cap, gate=gate)
 
 
 def chunk_schedule(lengths: list[int], chunk: int) -> list[list[tuple[int, int, int]]]:

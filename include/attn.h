@@ -78,6 +78,26 @@ typedef enum {
 } attn_norm;
 
 /*
+ * Output gates, applied to the normalised attention output as it is written
+ * (attn_prefill_chunk, attn_decode).  The gate has the call's dtype; the
+ * value for output row (token t, head h), dim d, is
+ *   gate[(t * n_heads + h) * gate_ld + d]      (per element), or
+ *   gate[(t * n_heads + h) * gate_ld]          (per head),
+ * t the packed row (prefill) or the sequence (decode).  gate_ld = head_dim
+ * for a [n_tok][n_heads][head_dim] gate; 2 * head_dim with gate = the raw
+ * query projection + head_dim reads the Qwen3.5 layout, each head's rows
+ * [q(head_dim); gate(head_dim)] ([ATT] QwenAttnCfg.output_gate, the gate
+ * split).
+ */
+typedef enum {
+    ATTN_GATE_NONE = 0,
+    ATTN_GATE_SIGMOID = 1,      /* out *= 1 / (1 + exp(-g)), per element ([ATT] fn apply_gate) */
+    ATTN_GATE_SOFTPLUS_HEAD = 2,/* out *= softplus(g), one g per head   ([ATT] fn apply_projected_gate) */
+    ATTN_GATE_SOFTPLUS = 3      /* out *= softplus(g), per element; softplus(x) = max(x, 0) +
+                                   log(1 + exp(-|x|)) ([ATT] fn softplus) */
+} attn_gate;
+
+/*
  * RoPE inverse-frequency table.  [ATT] fn rope_inv_freq:
  *   inv_freq[i] = 1 / base^(2i / rotary_dim),  i < rotary_dim / 2,
  * evaluated in double and rounded once to float.
@@ -142,14 +162,17 @@ int attn_rope_apply(const void *x, void *y, int dtype, int n_tok, int n_heads, i
  *   ring             0: position p in row p; 1: row p mod cap (see above)
  *   k_new, v_new     device [n_tok][n_kv][head_dim], read
  *   norm_w           the k-norm weight, device float[head_dim] or NULL
- * Errors: ECAPACITY if max_end > cap without a ring; EINVAL (ring not 0/1);
- * otherwise as attn_rope_apply.
+ *   v_norm           1: each V row is scale-less RMS-normalised first,
+ *                    v / sqrt(mean(v^2) + eps), in double and rounded once
+ *                    ([ATT] fn vnorm_head, Gemma-4); 0: copied bit for bit
+ * Errors: ECAPACITY if max_end > cap without a ring; EINVAL (ring or v_norm
+ * not 0/1); otherwise as attn_rope_apply.
  */
 int attn_kv_append(void *k_cache, void *v_cache, int dtype, int n_seq, int n_kv, int head_dim,
                    int cap, int ring, const void *k_new, const void *v_new, int n_tok,
                    const int32_t *cu_seq, const int32_t *start, int max_chunk, int max_end,
                    const float *inv_freq, int rotary_dim, float rope_scale, int norm,
-                   const float *norm_w, double eps, void *stream);
+                   const float *norm_w, double eps, int v_norm, void *stream);
 
 /*
  * attn_rope_apply on the queries and attn_kv_append on the keys and values of
@@ -159,7 +182,7 @@ int attn_kv_append(void *k_cache, void *v_cache, int dtype, int n_seq, int n_kv,
  * multiple of 8, head_dim 64 or 128) -- a token's cos/sin table then serves
  * its query and key heads alike.  Arguments as in the two calls:
  *   q, q_out  device [n_tok][n_heads][head_dim] (q_out == q is allowed)
- *   k_cache, v_cache, k_new, v_new, n_kv, cap, ring   as attn_kv_append
+ *   k_cache, v_cache, k_new, v_new, n_kv, cap, ring, v_norm   as attn_kv_append
  *   q_norm_w, k_norm_w   the two norm weights (NULL iff norm is NONE)
  * Errors: the union of the two calls' errors.
  */
@@ -169,7 +192,7 @@ int attn_rope_qkv(const void *q, void *q_out, int n_heads, void *k_cache, void *
                   int head_dim, int n_seq, const int32_t *cu_seq, const int32_t *start,
                   int max_chunk, int max_end, const float *inv_freq, int rotary_dim,
                   float rope_scale, int norm, const float *q_norm_w, const float *k_norm_w,
-                  double eps, void *stream);
+                  double eps, int v_norm, void *stream);
 
 /*
  * Causal attention for the rows of a chunk whose keys and values are already
@@ -193,20 +216,22 @@ int attn_rope_qkv(const void *q, void *q_out, int n_heads, void *k_cache, void *
  *   window   0: every key <= p; W > 0: a sliding window, keys
  *            max(0, p-W+1)..p only ([ATT] QwenAttnCfg.window, "attend only
  *            the last N positions").
+ *   gate, gate_mode, gate_ld   output gate (see attn_gate; NULL/0 for none)
  *   workspace device scratch of workspace_bytes (may be NULL/0); with less
  *            than attn_prefill_workspace_bytes() the key range is split into
  *            fewer parts (never an error).  Contents need no initialisation
  *            and are clobbered.  Calls that share a workspace must be ordered
  *            on one stream.
  * Errors: ECAPACITY if max_end > cap without a ring (see ring); EINVAL
- * (window < 0, ring not 0/1, ...), EUNSUPPORTED, EDEVICE.
+ * (window < 0, ring not 0/1, a gate mode without a gate or with gate_ld too
+ * small, ...), EUNSUPPORTED, EDEVICE.
  */
 int attn_prefill_chunk(const void *q, const void *k_cache, const void *v_cache, int dtype,
                        int n_seq, int n_heads, int n_kv, int head_dim, int cap, int ring,
                        int n_tok,
                        const int32_t *cu_seq, const int32_t *start, int max_chunk, int max_end,
-                       float scale, int window, float *out, void *workspace,
-                       size_t workspace_bytes, void *stream);
+                       float scale, int window, const void *gate, int gate_mode, int gate_ld,
+                       float *out, void *workspace, size_t workspace_bytes, void *stream);
 
 /*
  * Workspace that lets attn_prefill_chunk split the key range as far as it
@@ -233,6 +258,8 @@ size_t attn_prefill_workspace_bytes(int n_seq, int n_heads, int n_kv, int head_d
  *   window 0: all ctx[b] keys; W > 0: only the last W (a sliding window,
  *          [ATT] the decode loop starts at stored - window); the
  *          probabilities of the keys before it are written as 0
+ *   gate, gate_mode, gate_ld   output gate of row (b, h) (see attn_gate);
+ *          the probabilities are not gated
  *   out    device float[n_seq][n_heads][head_dim], written
  *   probs  NULL, or device float[n_seq][n_heads][probs_ld]; row (b, h) gets
  *          ctx[b] entries summing to 1, entries past ctx[b] are not written.
@@ -251,12 +278,13 @@ size_t attn_prefill_workspace_bytes(int n_seq, int n_heads, int n_kv, int head_d
  *          size for the full split, and a smaller one means fewer, longer
  *          parts.  f32 needs none.
  * Errors: ECAPACITY if max_ctx > cap without a ring (see ring); EINVAL
- * (probs_ld < max_ctx, window < 0, ring not 0/1, ...), EUNSUPPORTED (bf16
+ * (probs_ld < max_ctx, window < 0, ring not 0/1, a bad gate, ...), EUNSUPPORTED (bf16
  * with more than 16 query heads per KV head), EDEVICE.
  */
 int attn_decode(const void *q, const void *k_cache, const void *v_cache, int dtype, int n_seq,
                 int n_heads, int n_kv, int head_dim, int cap, int ring, const int32_t *ctx,
-                int max_ctx, float scale, int window, float *out, float *probs, int probs_ld,
+                int max_ctx, float scale, int window, const void *gate, int gate_mode,
+                int gate_ld, float *out, float *probs, int probs_ld,
                 void *workspace, size_t workspace_bytes, void *stream);
 
 size_t attn_decode_workspace_bytes(int n_seq, int n_heads, int n_kv, int head_dim, int max_ctx);

@@ -42,6 +42,19 @@ def norm_kwargs(w, d, which):
     return dict(norm_style=w.norm_style, norm_w=d[which].cpu().numpy(), eps=w.norm_eps)
 
 
+def v_rows(w, v):
+    """The V rows the cache should hold: the inputs, or their V-norm."""
+    v = np64(v)
+    return oracle.vnorm_heads(v, w.norm_eps, store_of(w)) if w.v_norm else v
+
+
+def gated(w, out, gate):
+    """The oracle output after the workload's output gate (if any)."""
+    if not w.gate_mode:
+        return out
+    return oracle.output_gate(out, np64(gate), w.gate_mode)
+
+
 def oracle_prefill_packed(w, d, chunk, want_probs=False):
     """Oracle chunked prefill of every sequence of a packed batch; returns
     out [T][nh][hd] in packed order plus per-sequence caches."""
@@ -52,26 +65,24 @@ def oracle_prefill_packed(w, d, chunk, want_probs=False):
         sl = slice(cu[b], cu[b] + n)
         qn = norm_kwargs(w, d, "q_norm_w")
         kn = norm_kwargs(w, d, "k_norm_w")
+        v_in = v_rows(w, d["v"][sl])
         if w.ring:
             r = oracle.prefill_sequence_ring(
-                np64(d["q"][sl]), np64(d["k"][sl]), np64(d["v"][sl]), chunk, f, w.rd, w.scale,
+                np64(d["q"][sl]), np64(d["k"][sl]), v_in, chunk, f, w.rd, w.scale,
                 store_of(w), ring=d["cap"], window=w.window, rope_scale=w.rope_scale,
                 norm_style=qn.get("norm_style", 0), q_norm_w=qn.get("norm_w"),
                 k_norm_w=kn.get("norm_w"), eps=w.norm_eps)
-            outs.append(r["out"])
-            caches.append((r["k_cache"], r["v_cache"]))
-            qrots.append(r["q_rot"])
             probs.append(None)
-            continue
-        r = oracle.prefill_sequence(
-            np64(d["q"][sl]), np64(d["k"][sl]), np64(d["v"][sl]), chunk, f, w.rd, w.scale,
-            store_of(w), rope_scale=w.rope_scale,
-            norm_style=qn.get("norm_style", 0), q_norm_w=qn.get("norm_w"),
-            k_norm_w=kn.get("norm_w"), eps=w.norm_eps, want_probs=want_probs, window=w.window)
-        outs.append(r["out"])
+        else:
+            r = oracle.prefill_sequence(
+                np64(d["q"][sl]), np64(d["k"][sl]), v_in, chunk, f, w.rd, w.scale,
+                store_of(w), rope_scale=w.rope_scale,
+                norm_style=qn.get("norm_style", 0), q_norm_w=qn.get("norm_w"),
+                k_norm_w=kn.get("norm_w"), eps=w.norm_eps, want_probs=want_probs, window=w.window)
+            probs.append(r["probs"])
+        outs.append(gated(w, r["out"], d["gate"][sl] if w.gate_mode else None))
         caches.append((r["k_cache"], r["v_cache"]))
         qrots.append(r["q_rot"])
-        probs.append(r["probs"])
     return dict(out=np.concatenate(outs), caches=caches, q_rot=np.concatenate(qrots), probs=probs)
 
 
@@ -86,15 +97,15 @@ def oracle_rows(w, d, b, positions, heads=None):
     kn = norm_kwargs(w, d, "k_norm_w")
     qn = norm_kwargs(w, d, "q_norm_w")
     k_raw = np64(d["k"][t0:t0 + pmax + 1])
-    v_raw = np64(d["v"][t0:t0 + pmax + 1])
+    v_in = v_rows(w, d["v"][t0:t0 + pmax + 1])
     kc = oracle.finish_heads(k_raw, np.arange(pmax + 1), f, w.rd, w.rope_scale,
                              store=store_of(w), **kn)
     idx = torch.as_tensor(t0 + positions, device=d["q"].device)
     q_raw = np64(d["q"][idx])
     q = oracle.finish_heads(q_raw, positions, f, w.rd, w.rope_scale, store=store_of(w), **qn)
-    out, _ = oracle.attend(q, kc.transpose(1, 0, 2).copy(), v_raw.transpose(1, 0, 2).copy(),
+    out, _ = oracle.attend(q, kc.transpose(1, 0, 2).copy(), v_in.transpose(1, 0, 2).copy(),
                            positions, w.scale, window=w.window)
-    return positions, out
+    return positions, gated(w, out, d["gate"][idx] if w.gate_mode else None)
 
 
 def check_bf16_rows(got: np.ndarray, ref: np.ndarray, label=""):
@@ -163,10 +174,10 @@ def oracle_decode_row(w, d, b, c):
     last = np.array([c - 1])
     kc[:, -1] = oracle.finish_heads(np64(d["k"][b:b + 1]), last, f, w.rd, w.rope_scale,
                                     store=store_of(w))[0]
-    vc[:, -1] = np64(d["v"][b])
+    vc[:, -1] = v_rows(w, d["v"][b])
     q = oracle.finish_heads(np64(d["q"][b:b + 1]), last, f, w.rd, w.rope_scale, store=store_of(w))
     # keys lo..c-1 re-indexed from 0: the row sits at c-1-lo and reads them all
     o, P = oracle.attend(q, kc, vc, np.array([c - 1 - lo]), w.scale, want_probs=True)
     probs = np.zeros((w.n_heads, c))
     probs[:, lo:] = P[0]
-    return o[0], probs
+    return gated(w, o, d["gate"][b:b + 1] if w.gate_mode else None)[0], probs

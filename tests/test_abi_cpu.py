@@ -79,11 +79,13 @@ P = ctypes.c_void_p(4096)
 
 def prefill(**kw):
     a = dict(q=P, k=P, v=P, dtype=1, n_seq=1, nh=8, nkv=2, hd=128, cap=256, ring=0, n_tok=16, cu=P, st=P,
-             max_chunk=16, max_end=64, scale=0.088, window=0, out=P, ws=None, wsb=0, stream=None)
+             max_chunk=16, max_end=64, scale=0.088, window=0, gate=None, gate_mode=0, gate_ld=0,
+             out=P, ws=None, wsb=0, stream=None)
     a.update(kw)
     return api.lib().attn_prefill_chunk(a["q"], a["k"], a["v"], a["dtype"], a["n_seq"], a["nh"],
                                         a["nkv"], a["hd"], a["cap"], a["ring"], a["n_tok"], a["cu"], a["st"],
                                         a["max_chunk"], a["max_end"], a["scale"], a["window"],
+                                        a["gate"], a["gate_mode"], a["gate_ld"],
                                         a["out"], a["ws"], a["wsb"], a["stream"])
 
 
@@ -96,6 +98,12 @@ def test_prefill_validation():
     assert prefill(scale=float("nan")) == EINVAL
     assert prefill(window=-1) == EINVAL
     assert prefill(ring=2) == EINVAL
+    # output gates: a mode needs a gate, per-element modes a full row
+    assert prefill(gate_mode=1) == EINVAL
+    assert prefill(gate_mode=4, gate=P, gate_ld=128) == EINVAL
+    assert prefill(gate_mode=1, gate=P, gate_ld=127) == EINVAL
+    assert prefill(gate_mode=2, gate=P, gate_ld=0) == EINVAL
+    assert prefill(gate_mode=2, gate=P, gate_ld=1, n_tok=0) == OK
     # a ring that has wrapped needs a window, and window + max_chunk - 1 rows
     assert prefill(ring=1, max_end=300) == ECAP
     assert prefill(ring=1, max_end=300, window=250) == ECAP
@@ -111,17 +119,18 @@ def test_prefill_validation():
 
 def append(**kw):
     a = dict(kc=P, vc=P, dtype=1, n_seq=1, nkv=2, hd=128, cap=256, ring=0, kn=P, vn=P, n_tok=16, cu=P,
-             st=P, max_chunk=16, max_end=64, f=P, rd=128, rs=1.0, norm=0, w=None, eps=1e-6)
+             st=P, max_chunk=16, max_end=64, f=P, rd=128, rs=1.0, norm=0, w=None, eps=1e-6, v_norm=0)
     a.update(kw)
     return api.lib().attn_kv_append(a["kc"], a["vc"], a["dtype"], a["n_seq"], a["nkv"], a["hd"],
                                     a["cap"], a["ring"], a["kn"], a["vn"], a["n_tok"], a["cu"], a["st"],
                                     a["max_chunk"], a["max_end"], a["f"], a["rd"], a["rs"],
-                                    a["norm"], a["w"], a["eps"], None)
+                                    a["norm"], a["w"], a["eps"], a["v_norm"], None)
 
 
 def test_append_validation():
     assert append(max_end=300) == ECAP
     assert append(ring=3) == EINVAL
+    assert append(v_norm=2) == EINVAL
     assert append(ring=1, max_end=300, n_seq=0) == OK     # a ring has a row for every position
     assert append(rd=63) == EINVAL
     assert append(f=None) == EINVAL
@@ -155,12 +164,13 @@ def test_rope_validation():
 
 def decode(**kw):
     a = dict(q=P, k=P, v=P, dtype=1, n_seq=4, nh=32, nkv=8, hd=128, cap=4096, ring=0, ctx=P, max_ctx=4096,
-             scale=0.088, window=0, out=P, probs=None, ld=0, ws=P, wsb=1 << 30)
+             scale=0.088, window=0, gate=None, gate_mode=0, gate_ld=0, out=P, probs=None, ld=0, ws=P,
+             wsb=1 << 30)
     a.update(kw)
     return api.lib().attn_decode(a["q"], a["k"], a["v"], a["dtype"], a["n_seq"], a["nh"],
                                  a["nkv"], a["hd"], a["cap"], a["ring"], a["ctx"], a["max_ctx"], a["scale"],
-                                 a["window"], a["out"], a["probs"], a["ld"], a["ws"], a["wsb"],
-                                 None)
+                                 a["window"], a["gate"], a["gate_mode"], a["gate_ld"], a["out"],
+                                 a["probs"], a["ld"], a["ws"], a["wsb"], None)
 
 
 def test_decode_validation():
@@ -173,6 +183,8 @@ def test_decode_validation():
     assert decode(hd=256) == EUNSUP
     assert decode(window=-5) == EINVAL
     assert decode(ring=-1) == EINVAL
+    assert decode(gate_mode=3, gate=None, gate_ld=128) == EINVAL
+    assert decode(gate_mode=3, gate=P, gate_ld=64) == EINVAL
     # a wrapped ring holds the last cap keys: 0 < window <= cap
     assert decode(ring=1, max_ctx=5000, probs=P, ld=5000) == ECAP
     assert decode(ring=1, max_ctx=5000, window=4097) == ECAP

@@ -168,3 +168,10 @@ def test_c4_yarn_128k_sw4096_ring_full():
     lin.run_all()
     torch.cuda.synchronize()
     assert torch.equal(got.view(torch.int32), lin.gather("out").view(torch.int32))
+
+
+def test_c3_qwen_varlen_gate_full():
+    # the varlen Qwen-style prefill with the Qwen3.5 output gate (sigmoid per element)
+    w, d, run = run_prefill("c3_qwen_varlen_gate")
+    for b in (0, 3, 7):
+        check_sequence(w, d, run, b, 500 + b, "c3 gate", check_cache=False)

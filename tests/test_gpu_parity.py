@@ -664,6 +664,91 @@ def test_decode_ring_matches_oracle(dtype, nh, nkv, window, ring, parts_per_row)
         assert np.array_equal(_bits(step.v_cache[b, :, (c - 1) % ring]), _bits(d["v"][b]))
 
 
+# ------------------------------------------------------------------ gates and V-norm
+
+GATE_CASES = [
+    # name, nh, nkv, hd, T, chunk, gate mode, v_norm
+    ("sigmoid_vnorm", 8, 2, 128, 300, 128, 1, True),
+    ("softplus_head", 10, 2, 128, 261, 96, 2, False),
+    ("softplus_elem_hd64", 16, 2, 64, 130, 130, 3, True),
+    ("sigmoid_long_split", 2, 2, 128, 2100, 37, 1, False),     # gate in the combine kernel
+]
+
+
+@pytest.mark.parametrize("name,nh,nkv,hd,T,chunk,mode,v_norm", GATE_CASES)
+def test_bf16_prefill_gates_and_vnorm(name, nh, nkv, hd, T, chunk, mode, v_norm):
+    say(f"bf16 prefill gate {name}: mode={mode} v_norm={v_norm}")
+    w = wl.Workload(name=name, dtype=wl.BF16, n_heads=nh, n_kv=nkv, head_dim=hd, seed=81,
+                    prompt_len=T, chunk=chunk, gate_mode=mode, v_norm=v_norm)
+    d = wl.gen_prefill(w)
+    run = runner.ChunkedPrefill(w, d, device=DEV)
+    run.run_all()
+    torch.cuda.synchronize()
+    ref = oracle_prefill_packed(w, d, chunk)
+    check_bf16_rows(np64(run.gather("out")), ref["out"], name)
+    kc_ref, vc_ref = ref["caches"][0]
+    want_v = _to_dtype_bits(vc_ref, torch.bfloat16)
+    mism = int((_bits(run.v_cache[0]) != want_v).sum())
+    assert mism <= max(1, want_v.size // 1_000_000), f"V cache: {mism} rows differ"
+    if not v_norm:
+        assert mism == 0
+
+
+def test_gate_view_of_raw_query_projection():
+    """The Qwen3.5 layout: each head's raw projection rows [q(hd); gate(hd)];
+    a gate read in place through gate_ld = 2*hd gives the same bits as the
+    gate copied out."""
+    w = wl.Workload(name="qwen-gate", dtype=wl.BF16, n_heads=8, n_kv=2, head_dim=128, seed=82,
+                    prompt_len=200, chunk=200, gate_mode=1)
+    d = wl.gen_prefill(w)
+    run = runner.ChunkedPrefill(w, d, device=DEV)
+    run.run_all()
+    s = run.steps[0]
+    raw = torch.cat([s["q"], s["gate"]], dim=-1)          # [T][nh][2*hd]
+    out2 = torch.empty_like(s["out"])
+    api.prefill_chunk(s["q_rot"], run.k_cache, run.v_cache, s["batch"], w.scale, out2,
+                      run.workspace, gate=raw[..., 128:], gate_mode=api.GATE_SIGMOID)
+    torch.cuda.synchronize()
+    assert torch.equal(out2, s["out"])
+
+
+def test_f32_prefill_and_decode_gates():
+    for mode in (1, 2, 3):
+        w = wl.CONFIGS["c0_f32_small"].replace(gate_mode=mode, v_norm=mode == 3)
+        d = wl.gen_prefill(w)
+        ref = oracle_prefill_packed(w, d, 16)
+        run = runner.ChunkedPrefill(w, d, device=DEV)
+        run.run_all()
+        torch.cuda.synchronize()
+        check_f32(np64(run.gather("out")), ref["out"], f"f32 prefill gate {mode}")
+
+
+@pytest.mark.parametrize("dtype,mode,v_norm,window", [
+    (wl.BF16, 1, True, 0), (wl.BF16, 2, False, 100), (wl.BF16, 3, False, 0), (wl.F32, 1, True, 0),
+    (wl.F32, 2, False, 0)])
+def test_decode_gates_and_vnorm(dtype, mode, v_norm, window):
+    ctx = [1, 63, 64, 65, 1025, 3000]
+    w = wl.Workload(name="dec-gate", dtype=dtype, n_heads=32, n_kv=8, head_dim=128, seed=83,
+                    n_seq=len(ctx), decode=True, ctx_range=(1, 3000), cap=3072, want_probs=True,
+                    gate_mode=mode, v_norm=v_norm, window=window)
+    say(f"decode gate {dtype} mode={mode} v_norm={v_norm} W={window}")
+    d = wl.gen_decode(w)
+    d["ctx"] = ctx
+    step = runner.DecodeStep(w, d, device=DEV, probs_ld_multiple=1)
+    step.run()
+    torch.cuda.synchronize()
+    got_o = np64(step.out)
+    got_p = np64(step.probs)
+    for b, c in enumerate(ctx):
+        o, P = oracle_decode_row(w, d, b, c)
+        if dtype == wl.BF16:
+            check_bf16_rows(got_o[b], o, f"seq {b} ctx {c}")
+        else:
+            check_f32(got_o[b], o, f"seq {b} ctx {c}")
+        # the probabilities are not gated
+        check_probs(got_p[b, :, :c], P, dtype == wl.BF16, f"seq {b} ctx {c}")
+
+
 # ------------------------------------------------------------------ importance
 
 @pytest.mark.parametrize("dtype", [wl.BF16, wl.F32])
