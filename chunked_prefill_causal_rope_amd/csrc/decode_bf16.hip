@@ -559,8 +559,8 @@ __global__ __launch_bounds__(256) void decode_combine_kernel(DecodeArgs a) {
 // Importance of each cached position for one decode step, from the
 // probabilities the decode call returned: imp[b][j] (+)= sum over heads of
 // probs[b][h][j], j < ctx[b] ([ATT] the per-head loop of the decode attention
-// adds every head's probability row into one vector: "a position's
-// importance is the probability mass that reads it").  Heads are summed in
+// adds every head's probability row into one vector, so a position's
+// importance is the total probability the heads give it).  Heads are summed in
 // order, in float, each thread over 4 consecutive positions; the
 // probabilities are read once (16-byte loads, every head's row in flight).
 __global__ __launch_bounds__(256) void decode_importance_kernel(ImportanceArgs a) {

@@ -214,8 +214,8 @@ int attn_rope_qkv(const void *q, void *q_out, int n_heads, void *k_cache, void *
  *            (ECAPACITY otherwise) and, for bf16, cap a multiple of 64
  *            (EUNSUPPORTED otherwise)
  *   window   0: every key <= p; W > 0: a sliding window, keys
- *            max(0, p-W+1)..p only ([ATT] QwenAttnCfg.window, "attend only
- *            the last N positions").
+ *            max(0, p-W+1)..p only ([ATT] QwenAttnCfg.window: a row reads
+ *            just the most recent W positions).
  *   gate, gate_mode, gate_ld   output gate (see attn_gate; NULL/0 for none)
  *   workspace device scratch of workspace_bytes (may be NULL/0); with less
  *            than attn_prefill_workspace_bytes() the key range is split into
@@ -292,8 +292,8 @@ size_t attn_decode_workspace_bytes(int n_seq, int n_heads, int n_kv, int head_di
 /*
  * Importance of each cached position after a decode step ([ATT] the decode
  * attention adds every head's probability row into one vector before the
- * cache accumulates it for eviction: "a position's importance is the
- * probability mass that reads it"):
+ * cache accumulates it for eviction; a position's importance is the total
+ * probability the step's heads give it):
  *   imp[b][j] = (accumulate ? imp[b][j] : 0) + sum_h probs[b][h][j],
  * for j < min(ctx[b], max_ctx); entries past that are not written.  Heads are
  * summed in order in float.

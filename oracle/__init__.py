@@ -215,8 +215,7 @@ def head_importance(probs, ctx: int) -> np.ndarray:
     """Importance of each of the first ctx positions for one decode step:
     the sum over heads of the probability rows, probs [nh][>= ctx].  [ATT]
     the per-head loop of the decode attention (each head's probabilities are
-    added into one vector; "a position's importance is the probability mass
-    that reads it")."""
+    added into one vector, the total probability each position receives)."""
     pa = _f64(probs)
     nh, ld = pa.shape
     imp = np.zeros(ctx, dtype=np.float64)

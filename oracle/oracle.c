@@ -319,8 +319,8 @@ static void *attend_worker(void *arg)
         const double *kc = jb->kc + (long)g * jb->cap * jb->hd;
         const double *vc = jb->vc + (long)g * jb->cap * jb->hd;
         double *pr = jb->probs ? jb->probs + r * jb->probs_ld : NULL;
-        /* sliding window ([ATT] QwenAttnCfg.window, "attend only the last N
-         * positions"; the decode loop starts at stored - window): keys
+        /* sliding window ([ATT] QwenAttnCfg.window: only the most recent W
+         * positions are read; the decode loop starts at stored - window): keys
          * first..p, probabilities of the keys before it are 0 */
         long first = 0;
         if (jb->window > 0 && (long)jb->qpos[t] + 1 > jb->window)
@@ -418,8 +418,8 @@ int orc_attend_window(const double *q, const double *kc, const double *vc, int n
 /*
  * Importance of each cached position for one decode step ([ATT] the
  * per-head loop of the decode attention adds every head's probability row
- * into one vector, "a position's importance is the probability mass that
- * reads it"): imp[j] = sum over heads h of probs[h][j], j < ctx, heads in
+ * into one vector, so a position's importance is the total probability the
+ * heads give it): imp[j] = sum over heads h of probs[h][j], j < ctx, heads in
  * order, in double.  probs [nh][probs_ld].  Returns 0, or -1 on bad
  * arguments.
  */

@@ -408,8 +408,8 @@ def test_head_importance_mass_and_special_cases():
 
 
 def test_sliding_window_special_cases():
-    """Sliding window ([ATT] QwenAttnCfg.window: attend only the last N
-    positions; the decode loop starts at stored - window).  Pinned by: a
+    """Sliding window ([ATT] QwenAttnCfg.window: only the most recent W
+    positions are read; the decode loop starts at stored - window).  Pinned by: a
     window as long as the prefix is the full attention; window 1 returns the
     row's own V; a brute-force banded softmax on tiny inputs; the
     probabilities before the window are exactly 0 and each row still sums
