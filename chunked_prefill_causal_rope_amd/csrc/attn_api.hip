@@ -11,7 +11,8 @@
 
 namespace {
 
-constexpr int kDecodePartPad = 4;
+// a decode partial row: 4 header floats, then head_dim halves
+constexpr int kDecodePartHead = 4;
 #ifndef ATTN_DECODE_SPLIT
 #define ATTN_DECODE_SPLIT 1024
 #endif
@@ -49,7 +50,7 @@ int decode_splits_full(int max_ctx, int group) {
 }
 
 size_t decode_part_bytes(int n_seq, int n_heads, int head_dim, int splits) {
-    return (size_t)n_seq * n_heads * splits * (head_dim + kDecodePartPad) * sizeof(float);
+    return (size_t)n_seq * n_heads * splits * (head_dim / 2 + kDecodePartHead) * sizeof(float);
 }
 
 // Output gate arguments: mode 0 needs nothing; per-element modes read

@@ -40,7 +40,10 @@
 namespace attn {
 
 constexpr int kDecKB = 32;      // keys per step
-constexpr int kPartPadD = 4;    // (m, l, l_half, pad) before O in a partial
+// A partial: (m, l, l_half, e) as floats, then O/l * 2^-e as head_dim halves
+// (see part_scale_exp).
+constexpr int kPartHeadD = 4;
+__host__ __device__ constexpr int dec_part_words(int hd) { return kPartHeadD + hd / 2; }
 constexpr int kDecMaxGroup = 16;
 constexpr float kDecSlack = 8.f;
 // LDS floats per wave that hold a part's raw scores (16 KB)
@@ -405,7 +408,26 @@ __global__ __launch_bounds__(64) void decode_split_kernel(DecodeArgs a) {
 #pragma unroll
             for (int off = CPR; off < 64; off <<= 1) o[hh][e] += __shfl_xor(o[hh][e], off);
 
-    constexpr int PS = HD + kPartPadD;
+    // every head's l to every lane (through LDS), then each head's O/l in
+    // half precision with its scale exponent
+    if (col == 0) {
+#pragma unroll
+        for (int r = 0; r < HPL; ++r) abuf[grp * HPL + r] = l_run[r];
+    }
+    lds_order();
+    float linv[GQ];
+    int ex[GQ];
+#pragma unroll
+    for (int hh = 0; hh < GQ; ++hh) {
+        const float lv = abuf[hh];
+        linv[hh] = lv > 0.f ? 1.f / lv : 0.f;
+        float mx = 0.f;
+#pragma unroll
+        for (int e = 0; e < 8; ++e) mx = fmaxf(mx, fabsf(o[hh][e]));
+        // lanes 16j..16j+15 hold every dim of the row (lanes CPR apart repeat)
+        ex[hh] = part_scale_exp(row16_max(mx) * linv[hh]);
+    }
+    constexpr int PS = dec_part_words(HD);
     float* part = a.part + (((size_t)b * a.n_heads + g * G) * a.n_splits + s) * PS;
     const size_t head_stride = (size_t)a.n_splits * PS;
     if (col == 0) {
@@ -414,16 +436,18 @@ __global__ __launch_bounds__(64) void decode_split_kernel(DecodeArgs a) {
             const int hh = grp * HPL + r;
             if (hh < G)
                 *reinterpret_cast<float4*>(part + hh * head_stride) =
-                    make_float4(m_run[r], l_run[r], PROBS ? lhalf[hh] : 0.f, 0.f);
+                    make_float4(m_run[r], l_run[r], PROBS ? lhalf[hh] : 0.f, (float)ex[hh]);
         }
     }
     if (vr == 0) {
 #pragma unroll
         for (int hh = 0; hh < GQ; ++hh) {
             if (hh < G) {
-                float* dst = part + hh * head_stride + kPartPadD + 8 * vc_;
-                *reinterpret_cast<float4*>(dst) = make_float4(o[hh][0], o[hh][1], o[hh][2], o[hh][3]);
-                *reinterpret_cast<float4*>(dst + 4) = make_float4(o[hh][4], o[hh][5], o[hh][6], o[hh][7]);
+                const float sc = __builtin_amdgcn_ldexpf(linv[hh], -ex[hh]);
+                uint32_t* dst = reinterpret_cast<uint32_t*>(part + hh * head_stride + kPartHeadD) + 4 * vc_;
+                *reinterpret_cast<u32x4_t*>(dst) =
+                    u32x4_t{pack_f16x2(o[hh][0] * sc, o[hh][1] * sc), pack_f16x2(o[hh][2] * sc, o[hh][3] * sc),
+                            pack_f16x2(o[hh][4] * sc, o[hh][5] * sc), pack_f16x2(o[hh][6] * sc, o[hh][7] * sc)};
             }
         }
     }
@@ -458,7 +482,7 @@ __global__ __launch_bounds__(256) void decode_combine_kernel(DecodeArgs a) {
         for (int d = tid; d < HD; d += 256) orow[d] = 0.f;
         return;
     }
-    constexpr int PS = HD + kPartPadD;
+    constexpr int PS = dec_part_words(HD);
     const int k_first = decode_window_first(ctx, a.window);
     const int k_base = decode_part_base(ctx, a.window);
     const int n_parts = min((ctx - k_base + a.split_len - 1) / a.split_len, a.n_splits);
@@ -480,24 +504,32 @@ __global__ __launch_bounds__(256) void decode_combine_kernel(DecodeArgs a) {
         for (int s = tid; s < n_parts; s += 256)
             lh += pr[(size_t)s * PS + 2] * __builtin_amdgcn_exp2f(pr[(size_t)s * PS] - m);
     const float inv_h = a.probs ? 1.f / block_reduce(lh, red, false) : 0.f;
-    // O: thread -> (dim, phase); phases take every (256/HD)-th part
+    // O: thread -> (dim, phase); phases take every (256/HD)-th part; part s
+    // adds its O/l (halves, scaled by 2^-e) with weight l_s 2^(m_s - m) 2^e
     {
         constexpr int PH = 256 / HD;
         const int d = tid % HD, ph = tid / HD;
+        auto term = [&](const float4 hdr, uint16_t v) __attribute__((always_inline)) {
+            return f16_value(v) * __builtin_amdgcn_ldexpf(hdr.y * __builtin_amdgcn_exp2f(hdr.x - m), (int)hdr.w);
+        };
         float acc = 0.f;
         int s = ph;
         for (; s + 3 * PH < n_parts; s += 4 * PH) {
-            float w[4], x[4];
+            float4 w[4];
+            uint16_t x[4];
 #pragma unroll
             for (int u = 0; u < 4; ++u) {
                 const float* p = pr + (size_t)(s + u * PH) * PS;
-                w[u] = p[0];
-                x[u] = p[kPartPadD + d];
+                w[u] = *reinterpret_cast<const float4*>(p);
+                x[u] = reinterpret_cast<const uint16_t*>(p + kPartHeadD)[d];
             }
 #pragma unroll
-            for (int u = 0; u < 4; ++u) acc += x[u] * __builtin_amdgcn_exp2f(w[u] - m);
+            for (int u = 0; u < 4; ++u) acc += term(w[u], x[u]);
         }
-        for (; s < n_parts; s += PH) acc += pr[(size_t)s * PS + kPartPadD + d] * __builtin_amdgcn_exp2f(pr[(size_t)s * PS] - m);
+        for (; s < n_parts; s += PH) {
+            const float* p = pr + (size_t)s * PS;
+            acc += term(*reinterpret_cast<const float4*>(p), reinterpret_cast<const uint16_t*>(p + kPartHeadD)[d]);
+        }
         osum[tid] = acc;
         __syncthreads();
         if (tid < HD) {

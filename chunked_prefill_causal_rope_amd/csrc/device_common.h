@@ -87,6 +87,16 @@ __device__ __forceinline__ void f64_to_bf16_packed(const double* v, uint32_t* u)
     }
 }
 
+// Split partials keep a row's output normalised by its own row sum, O/l (a
+// convex combination of V rows), as half precision, scaled by 2^-e when the
+// row's largest magnitude would not fit (e >= 0, kept beside m and l): half
+// the bytes of float partials, relative rounding 2^-11 of the row's largest.
+__device__ __forceinline__ int part_scale_exp(float maxabs) {
+    // maxabs < 2^k; keep scaled values below 2^15 (half's largest is ~2^16)
+    const int k = __builtin_amdgcn_frexp_expf(maxabs);
+    return k > 15 ? k - 15 : 0;
+}
+
 // Output gate of the attention output ([ATT] fn apply_gate: times
 // sigmoid(g) per element; fn apply_projected_gate: times softplus(g), one g
 // per head or per element).  The gate value of output row `row` (token *

@@ -47,7 +47,10 @@ constexpr int kTK = 64;                 // keys per tile
 // Fourth word of a raw buffer resource on gfx9-family parts (32-bit data
 // format; byte offsets, no swizzle, no index).
 constexpr int kBufferWord3 = 0x00020000;
-constexpr int kPartPad = 4;             // (m, l, pad, pad) before O in a partial
+// A split partial row: (m, l, e, 0) as floats, then O/l * 2^-e as head_dim
+// halves (see part_scale_exp).
+constexpr int kPartHead = 4;
+__host__ __device__ constexpr int part_row_words(int hd) { return kPartHead + hd / 2; }
 // A row's running maximum (log2 units) is only moved, and O rescaled, when a
 // new score exceeds it by more than this; until then probabilities are
 // referenced to the old maximum and stay below 2^8.  The softmax is unchanged:
@@ -629,25 +632,37 @@ __global__ __launch_bounds__(NW * 64, 8 / NW) void prefill_bf16_kernel(PrefillAr
                 *reinterpret_cast<float4*>(orow + db * 32 + 8 * q4 + 4 * hf) = v;
             }
     } else {
-        // partial of this item's row r - r_tile0
-        float* pr = a.part + ((size_t)item * TILE_ROWS + (r - r_tile0)) * (HD + kPartPad);
-        if (hf == 0) *reinterpret_cast<float2*>(pr) = make_float2(m_run, l_tot);
+        // partial of this item's row r - r_tile0: O/l in half precision
+        // (a part whose keys are all masked for the row has l = 0, O = 0)
+        float* pr = a.part + ((size_t)item * TILE_ROWS + (r - r_tile0)) * part_row_words(HD);
+        const float inv = l_tot > 0.f ? 1.f / l_tot : 0.f;
+        float mx = 0.f;
+#pragma unroll
+        for (int db = 0; db < NDB; ++db)
+#pragma unroll
+            for (int q = 0; q < 16; ++q) mx = fmaxf(mx, fabsf(O[db][q]));
+        mx = fmaxf(mx, __shfl_xor(mx, 32)) * inv;
+        const int ex = part_scale_exp(mx);
+        const float sc = __builtin_amdgcn_ldexpf(inv, -ex);
+        if (hf == 0) *reinterpret_cast<float4*>(pr) = make_float4(m_run, l_tot, (float)ex, 0.f);
+        uint32_t* ph = reinterpret_cast<uint32_t*>(pr + kPartHead);
 #pragma unroll
         for (int db = 0; db < NDB; ++db)
 #pragma unroll
             for (int q4 = 0; q4 < 4; ++q4) {
-                float4 v = make_float4(O[db][4 * q4], O[db][4 * q4 + 1], O[db][4 * q4 + 2],
-                                       O[db][4 * q4 + 3]);
-                *reinterpret_cast<float4*>(pr + kPartPad + db * 32 + 8 * q4 + 4 * hf) = v;
+                const u32x2_t v = {pack_f16x2(O[db][4 * q4] * sc, O[db][4 * q4 + 1] * sc),
+                                   pack_f16x2(O[db][4 * q4 + 2] * sc, O[db][4 * q4 + 3] * sc)};
+                *reinterpret_cast<u32x2_t*>(ph + (db * 32 + 8 * q4 + 4 * hf) / 2) = v;
             }
     }
 }
 
-// Merge split partials (m, l, O) of each row: m* = max m_s,
-// l* = sum l_s 2^(m_s - m*), out = sum O_s 2^(m_s - m*) / l*.  One wave per
-// row: workgroup (x, sequence) takes 4 rows of the row tile x / (n_kv * R/4)
-// and KV group x % n_kv; row tiles that were not split were written by the
-// attention kernel.
+// Merge split partials (m, l, O/l) of each row: m* = max m_s,
+// l* = sum l_s 2^(m_s - m*), out = sum (O/l)_s l_s 2^(m_s - m*) / l*.  One
+// wave per row, each lane over HD/64 consecutive dims: workgroup
+// (x, sequence) takes 4 rows of the row tile x / (n_kv * R/4) and KV group
+// x % n_kv; row tiles that were not split were written by the attention
+// kernel.
 template <int HD>
 __global__ __launch_bounds__(256) void prefill_combine_kernel(PrefillArgs a) {
     const int b = blockIdx.y;
@@ -664,8 +679,8 @@ __global__ __launch_bounds__(256) void prefill_combine_kernel(PrefillArgs a) {
     const int len = min(a.cu_seq[b + 1] - t0, a.max_chunk);
     const int rows_b = len * G;
     const int lane = threadIdx.x & 63;
-    constexpr int PER = HD / 64;
-    constexpr int PS = HD + kPartPad;
+    constexpr int PER = HD / 64;                  // dims lane*PER .. lane*PER+PER-1
+    constexpr int PS = part_row_words(HD);
     {
         const int rl = rblk * 4 + (threadIdx.x >> 6);
         const int r = qt * R + rl;
@@ -675,17 +690,28 @@ __global__ __launch_bounds__(256) void prefill_combine_kernel(PrefillArgs a) {
         const int t = t0 + i;
         if (t < 0 || t >= a.n_tok) return;
         // part p of this row tile and group is item first + p * n_kv + g;
-        // lane p < S holds part p's (m, l), then its weight 2^(m_p - m)
+        // lane p < S holds part p's (m, l, e), then its weights
         auto prow = [&](int p) { return a.part + ((size_t)(first + p * a.n_kv + g) * R + rl) * PS; };
+        // this lane's PER halves of part p's O/l
+        auto vals = [&](int p, float* x) __attribute__((always_inline)) {
+            const uint16_t* ph = reinterpret_cast<const uint16_t*>(prow(p) + kPartHead) + lane * PER;
+            if (PER == 2) {
+                const uint32_t u = *reinterpret_cast<const uint32_t*>(ph);
+                x[0] = f16_value((uint16_t)u);
+                x[PER - 1] = f16_value((uint16_t)(u >> 16));
+            } else {
+                x[0] = f16_value(ph[0]);
+            }
+        };
         // output gate factors first, so their loads overlap the merge
         float gf[PER];
 #pragma unroll
         for (int e = 0; e < PER; ++e)
-            gf[e] = a.gate.mode ? gate_factor_bf16(a.gate, (size_t)t * a.n_heads + h, lane + 64 * e) : 1.f;
-        float mp = -INFINITY, lp = 0.f;
+            gf[e] = a.gate.mode ? gate_factor_bf16(a.gate, (size_t)t * a.n_heads + h, lane * PER + e) : 1.f;
+        float mp = -INFINITY, lp = 0.f, ep = 0.f;
         for (int p = lane; p < S; p += 64) {
-            const float2 ml = *reinterpret_cast<const float2*>(prow(p));
-            if (p < 64) { mp = ml.x; lp = ml.y; }
+            const float4 ml = *reinterpret_cast<const float4*>(prow(p));
+            if (p < 64) { mp = ml.x; lp = ml.y; ep = ml.z; }
             else { mp = fmaxf(mp, ml.x); }
         }
         const float m = wave_max(mp);
@@ -695,16 +721,17 @@ __global__ __launch_bounds__(256) void prefill_combine_kernel(PrefillArgs a) {
         for (int e = 0; e < PER; ++e) o[e] = 0.f;
         float l = 0.f;
         if (S <= 64) {
-            const float wl = lane < S ? __builtin_amdgcn_exp2f(mp - m_use) : 0.f;
-            l = wave_sum(lp * wl);
+            // part weight in l: l_p 2^(m_p - m); on the stored values also 2^e_p
+            const float wl = lane < S ? lp * __builtin_amdgcn_exp2f(mp - m_use) : 0.f;
+            const float wo = __builtin_amdgcn_ldexpf(wl, (int)ep);
+            l = wave_sum(wl);
             int p = 0;
             for (; p + 4 <= S; p += 4) {
                 float x[4][PER], w[4];
 #pragma unroll
                 for (int u = 0; u < 4; ++u) {
-                    w[u] = __shfl(wl, p + u);
-#pragma unroll
-                    for (int e = 0; e < PER; ++e) x[u][e] = prow(p + u)[kPartPad + lane + 64 * e];
+                    w[u] = __shfl(wo, p + u);
+                    vals(p + u, x[u]);
                 }
 #pragma unroll
                 for (int u = 0; u < 4; ++u)
@@ -712,23 +739,30 @@ __global__ __launch_bounds__(256) void prefill_combine_kernel(PrefillArgs a) {
                     for (int e = 0; e < PER; ++e) o[e] += x[u][e] * w[u];
             }
             for (; p < S; ++p) {
-                const float w = __shfl(wl, p);
+                float x[PER];
+                vals(p, x);
+                const float w = __shfl(wo, p);
 #pragma unroll
-                for (int e = 0; e < PER; ++e) o[e] += prow(p)[kPartPad + lane + 64 * e] * w;
+                for (int e = 0; e < PER; ++e) o[e] += x[e] * w;
             }
         } else {
             for (int p = 0; p < S; ++p) {
-                const float* pp = prow(p);
-                const float w = __builtin_amdgcn_exp2f(pp[0] - m_use);
-                l += pp[1] * w;
+                const float4 hd4 = *reinterpret_cast<const float4*>(prow(p));
+                const float w = hd4.y * __builtin_amdgcn_exp2f(hd4.x - m_use);
+                l += w;
+                float x[PER];
+                vals(p, x);
+                const float wv = __builtin_amdgcn_ldexpf(w, (int)hd4.z);
 #pragma unroll
-                for (int e = 0; e < PER; ++e) o[e] += pp[kPartPad + lane + 64 * e] * w;
+                for (int e = 0; e < PER; ++e) o[e] += x[e] * wv;
             }
         }
         const float inv = l > 0.f ? 1.f / l : 0.f;
-        float* orow = a.out + ((size_t)t * a.n_heads + h) * HD;
-#pragma unroll
-        for (int e = 0; e < PER; ++e) orow[lane + 64 * e] = o[e] * inv * gf[e];
+        float* orow = a.out + ((size_t)t * a.n_heads + h) * HD + lane * PER;
+        if (PER == 2)
+            *reinterpret_cast<float2*>(orow) = make_float2(o[0] * inv * gf[0], o[PER - 1] * inv * gf[PER - 1]);
+        else
+            orow[0] = o[0] * inv * gf[0];
     }
 }
 
@@ -776,7 +810,7 @@ PrefillPlan plan_prefill(int n_seq, int n_heads, int n_kv, int head_dim, int n_t
         const long slots = (long)device_cus() * (p.rows_per_tile == 256 ? 1 : 2);
         const size_t table = ((size_t)n_seq * p.n_qtiles * 2 * sizeof(int) + 255) / 256 * 256;
         // items <= slots + one extra part per row tile (ceil) -- see split_schedule
-        const size_t parts = (size_t)(slots + base) * p.rows_per_tile * (head_dim + kPartPad) * sizeof(float);
+        const size_t parts = (size_t)(slots + base) * p.rows_per_tile * part_row_words(head_dim) * sizeof(float);
         if (table + parts <= ws_available) {
             p.split = 1;
             p.slots = (int)slots;

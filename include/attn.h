@@ -273,7 +273,7 @@ size_t attn_prefill_workspace_bytes(int n_seq, int n_heads, int n_kv, int head_d
  *          absolute one below 2^-24 of the row's largest; f32: float
  *          throughout
  *   workspace device scratch, clobbered, no initialisation needed.  bf16
- *          needs at least n_seq*n_heads*(head_dim+4)*4 bytes (one part per
+ *          needs at least n_seq*n_heads*(2*head_dim+16) bytes (one part per
  *          row, EINVAL below that); attn_decode_workspace_bytes() gives the
  *          size for the full split, and a smaller one means fewer, longer
  *          parts.  f32 needs none.

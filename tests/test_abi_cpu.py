@@ -194,15 +194,16 @@ def test_decode_validation():
 
 def test_workspace_sizes():
     L = api.lib()
-    # decode: one part per 1024 keys
-    assert L.attn_decode_workspace_bytes(64, 32, 8, 128, 32768) == 64 * 32 * 32 * 132 * 4
+    # decode: one part per 1024 keys, each a 16-byte header and head_dim halves
+    assert L.attn_decode_workspace_bytes(64, 32, 8, 128, 32768) == 64 * 32 * 32 * (16 + 2 * 128)
     assert L.attn_decode_workspace_bytes(0, 32, 8, 128, 32768) == 0
     # prefill: a large grid needs no split
     assert L.attn_prefill_workspace_bytes(1, 64, 8, 128, 2048, 2048, 4096) == 0
     # a small chunk over a long context splits the key range: a 256-byte
-    # table, then one partial (128 rows x (128 + 4) floats) per work item
+    # table, then one partial (128 rows of a 16-byte header and 128 halves)
+    # per work item
     n = L.attn_prefill_workspace_bytes(1, 32, 8, 128, 128, 128, 4096)
-    assert n > 256 and (n - 256) % (128 * 132 * 4) == 0
+    assert n > 256 and (n - 256) % (128 * (16 + 2 * 128)) == 0
 
 
 def importance(**kw):
