@@ -120,16 +120,26 @@ __device__ __forceinline__ float sum_bf16_pairs(const uint32_t* pk) {
 // actual count exit.
 // Shortest part, in key tiles: a part's start-up (Q and first K/V tiles,
 // partial write, its share of the combine) weighs more for the 256-row
-// workgroups, one per CU, than for the 128-row ones, two per CU (measured:
-// c3-shaped calls gain ~2 % from 12 over 4; c1-shaped lose beyond 6).
+// workgroups than for the 128-row key-split ones (measured: c3-shaped calls
+// gain ~2 % from 12 over 4 at 256 rows; c1-shaped calls gain ~3 % from 4
+// over 6 at 128 rows, 2 and 3 are no better).
 #ifndef ATTN_PREFILL_MIN_TILES_128
-#define ATTN_PREFILL_MIN_TILES_128 6
+#define ATTN_PREFILL_MIN_TILES_128 4
 #endif
 #ifndef ATTN_PREFILL_MIN_TILES_256
 #define ATTN_PREFILL_MIN_TILES_256 12
 #endif
 __host__ __device__ constexpr int min_tiles_per_split(int rows_per_tile) {
     return rows_per_tile == 256 ? ATTN_PREFILL_MIN_TILES_256 : ATTN_PREFILL_MIN_TILES_128;
+}
+// An item's fixed cost (schedule, Q and first tiles, merge and partial
+// write), in key tiles, in the duration estimate: the 128-row key-split
+// items merge their halves and run each tile in about half the time.
+#ifndef ATTN_PREFILL_ITEM_COST_128
+#define ATTN_PREFILL_ITEM_COST_128 4
+#endif
+__host__ __device__ constexpr int item_cost_tiles(int rows_per_tile) {
+    return rows_per_tile == 256 ? 2 : ATTN_PREFILL_ITEM_COST_128;
 }
 
 // First key tile a row tile reads: with a sliding window of W keys its
@@ -194,7 +204,7 @@ __device__ __forceinline__ int split_part_length(const PrefillArgs& a, int gt) {
         prev_T = T;
         const int n = wave_reduce_dpp<false>(gt > 0 ? (gt + T - 1) / T : 0) * a.n_kv;
         if (n > a.grid) continue;             // one workgroup per item
-        const long cost = (long)((n + slots - 1) / slots) * (T + 2);
+        const long cost = (long)((n + slots - 1) / slots) * (T + item_cost_tiles(a.rows_per_tile));
         if (best_cost < 0 || cost < best_cost) {
             best_cost = cost;
             best_T = T;
@@ -657,6 +667,390 @@ __global__ __launch_bounds__(NW * 64, 8 / NW) void prefill_bf16_kernel(PrefillAr
     }
 }
 
+// Key-split variant for 128-row work items: 8 waves, the waves w and w+4
+// hold the same 32 query rows and take the two 32-key halves of every tile
+// (kh = wave / 4), each with its own online softmax; the halves merge through
+// LDS at the end.  Against 4 waves of 32 rows over whole tiles it has two
+// waves per SIMD from one workgroup (one wave's matrix products overlap the
+// other's exponentials), the deeper prefetch of the 8-wave layout, and half
+// the serial work per wave and tile -- what a small call with one workgroup
+// per CU is limited by.
+template <int HD, bool WIN>
+__global__ __launch_bounds__(512, 1) void prefill_bf16_ks_kernel(PrefillArgs a) {
+    using Sm = PrefillSmem<HD>;
+    constexpr int kThreads = 512;
+    constexpr int PD = 2;                         // staging sets = prefetch depth
+    constexpr int KS = Sm::KS;
+    constexpr int VS = Sm::VS;
+    constexpr int CH = HD / 8;                    // 16-byte chunks per cache row
+    constexpr int NCH = kTK * CH / kThreads;      // K (and V) chunks per thread
+    constexpr int NDB = HD / 32;                  // 32-dim blocks of O
+    constexpr int NKK = HD / 16;                  // K-steps of a score product
+    constexpr int TILE_ROWS = 128;                // query rows per workgroup
+    __shared__ Sm sm;
+
+    const int tid = threadIdx.x;
+    const int lane = tid & 63;
+    const int wave = tid >> 6;
+    const int kh = wave >> 2;                     // key half of every tile
+    const int wr = wave & 3;                      // row block
+    const int hf = lane >> 5;                     // wave half
+    const int rl = lane & 31;
+
+    const int item = blockIdx.x;
+    PrefillItem itm;
+    if (a.split) {
+        itm = split_schedule(a, item);
+    } else {
+        itm.g = item % a.n_kv;
+        itm.qt = a.n_qtiles - 1 - (item / a.n_kv) % a.n_qtiles;
+        itm.b = item / (a.n_kv * a.n_qtiles);
+        itm.part = 0;
+        itm.nsp = 1;
+    }
+    if (itm.nsp <= 0) return;
+    const int b = __builtin_amdgcn_readfirstlane(itm.b), qt = __builtin_amdgcn_readfirstlane(itm.qt),
+              g = __builtin_amdgcn_readfirstlane(itm.g), s = __builtin_amdgcn_readfirstlane(itm.part),
+              nsp = __builtin_amdgcn_readfirstlane(itm.nsp);
+
+    const int G = a.group;
+    const int t0 = a.cu_seq[b];
+    const int len = min(a.cu_seq[b + 1] - t0, a.max_chunk);
+    const int p0 = a.start[b];
+    const int rows_b = len * G;
+    const int r_tile0 = qt * TILE_ROWS;
+    if (len <= 0 || p0 < 0 || r_tile0 >= rows_b) return;
+
+    const int r_last = min(r_tile0 + TILE_ROWS, rows_b) - 1;
+    const int n_keys = WIN && a.ring ? p0 + r_last / G + 1 : min(p0 + r_last / G + 1, a.cap);
+    const int n_tiles = (n_keys + kTK - 1) / kTK;
+    const int t_first = WIN ? min(first_key_tile(p0 + r_tile0 / G, a.window), n_tiles) : 0;
+    const int per = (n_tiles - t_first + nsp - 1) / nsp;
+    const int tb = t_first + s * per;
+    const int te = min(tb + per, n_tiles);
+
+    const int r = r_tile0 + wr * 32 + rl;
+    const int i = r / G;
+    const int t = t0 + i;
+    const int h = g * G + (r - i * G);
+    const bool row_ok = r < rows_b && t >= 0 && t < a.n_tok;
+    const int pos = row_ok ? p0 + i : -1;
+    const int rw0 = r_tile0 + wr * 32;
+    const int pw_lo = p0 + rw0 / G;
+    const int win_lo = WIN ? p0 + (rw0 + 31) / G - a.window + 1 : INT_MIN;
+    const int koff = 32 * kh;                     // this wave's keys inside a tile
+
+    bf16x8_t qf[NKK];
+    {
+        const uint16_t* qrow =
+            reinterpret_cast<const uint16_t*>(a.q) + ((size_t)t * a.n_heads + h) * HD;
+#pragma unroll
+        for (int k = 0; k < NKK; ++k) {
+            u32x4_t u = {0u, 0u, 0u, 0u};
+            if (row_ok) u = ld16(qrow + 16 * k + 8 * hf);
+            qf[k] = __builtin_bit_cast(bf16x8_t, u);
+        }
+    }
+
+    const size_t kvbase = ((size_t)b * a.n_kv + g) * (size_t)a.cap * HD;
+    const uint16_t* kc = reinterpret_cast<const uint16_t*>(a.k_cache) + kvbase;
+    const uint16_t* vc = reinterpret_cast<const uint16_t*>(a.v_cache) + kvbase;
+
+    // staging as in the full-tile kernel (buffer loads with the tile in
+    // scalar registers; rows past the last key read as zeros)
+    u32x4_t kreg[PD][NCH], vreg[PD][NCH];
+    int voff[NCH];
+#pragma unroll
+    for (int c = 0; c < NCH; ++c) {
+        const int idx = c * kThreads + tid;
+        voff[c] = ((idx / CH) * HD + (idx % CH) * 8) * 2;
+    }
+    const int ring_tiles = a.cap / kTK;
+    auto tile_rsrc = [&](const uint16_t* base, int j) __attribute__((always_inline)) {
+        const int rows = min(max(n_keys - j * kTK, 0), kTK);
+        const int jt = WIN && a.ring ? j % ring_tiles : j;
+        return __builtin_amdgcn_make_buffer_rsrc((void*)(base + (size_t)jt * kTK * HD), (short)0, rows * HD * 2,
+                                                 kBufferWord3);
+    };
+    auto lds_off = [&](int c, int stride) __attribute__((always_inline)) {
+        const int idx = c * kThreads + tid;
+        return (idx / CH) * stride + (idx % CH) * 8;
+    };
+    auto load_k = [&](int j, auto set) __attribute__((always_inline)) {
+        const auto rs = tile_rsrc(kc, j);
+#pragma unroll
+        for (int c = 0; c < NCH; ++c)
+            kreg[set.value][c] = __builtin_bit_cast(u32x4_t, __builtin_amdgcn_raw_buffer_load_b128(rs, voff[c], 0, 0));
+    };
+    auto load_v = [&](int j, auto set) __attribute__((always_inline)) {
+        const auto rs = tile_rsrc(vc, j);
+#pragma unroll
+        for (int c = 0; c < NCH; ++c)
+            vreg[set.value][c] = __builtin_bit_cast(u32x4_t, __builtin_amdgcn_raw_buffer_load_b128(rs, voff[c], 0, 0));
+    };
+    auto store_k = [&](int buf, auto set) __attribute__((always_inline)) {
+#pragma unroll
+        for (int c = 0; c < NCH; ++c) st16(&sm.k[buf][lds_off(c, KS)], kreg[set.value][c]);
+    };
+    auto store_v = [&](int buf, auto set) __attribute__((always_inline)) {
+#pragma unroll
+        for (int c = 0; c < NCH; ++c) st16(&sm.v[buf][lds_off(c, VS)], vreg[set.value][c]);
+    };
+    constexpr std::integral_constant<int, 0> set0{};
+    constexpr std::integral_constant<int, 1> set1{};
+    // scores of this wave's 32 keys of a tile: S[q] holds key
+    // koff + 4*hf + 8*(q/4) + q%4 of its row
+    auto scores = [&](const uint16_t* kl, f32x16_t& S) __attribute__((always_inline)) {
+#pragma unroll
+        for (int q = 0; q < 16; ++q) S[q] = 0.f;
+#pragma unroll
+        for (int kk = 0; kk < NKK; ++kk)
+            S = mfma32(__builtin_bit_cast(bf16x8_t, ld16(kl + (koff + rl) * KS + kk * 16 + hf * 8)), qf[kk], S);
+    };
+
+    const int tr_off = (koff + 4 * hf + ((lane & 15) >> 2)) * VS + 4 * (lane & 3) + 16 * ((lane >> 4) & 1);
+
+    f32x16_t O[NDB];
+#pragma unroll
+    for (int db = 0; db < NDB; ++db)
+#pragma unroll
+        for (int q = 0; q < 16; ++q) O[db][q] = 0.f;
+    float m_run = -INFINITY;
+    float l_run = 0.f;
+    const float sl = a.scale * kLog2e;
+
+    if (tb < te) {
+        // the first two K tiles and the first V tile in flight together
+        load_k(tb, set0);
+        load_v(tb, set0);
+        load_k(min(tb + 1, te - 1), set1);
+        store_k(0, set0);
+        store_v(0, set0);
+        store_k(1, set1);
+        __syncthreads();
+        f32x16_t S;
+        scores(sm.k[0], S);
+        load_k(min(tb + 2, te - 1), set0);
+        load_v(min(tb + 1, te - 1), set0);
+
+        auto tile = [&](int j, auto cur, auto nxt) __attribute__((always_inline)) {
+            const int rr = (j - tb) & 1;
+            load_k(min(j + 3, te - 1), nxt);
+            load_v(min(j + 2, te - 1), nxt);
+            const int k0 = j * kTK + koff;        // this wave's first key
+
+            // ---- causal mask (tiles crossing the diagonal), window mask
+            if (k0 + 31 > pw_lo) {
+                const int lim = pos - k0 - 4 * hf;
+#pragma unroll
+                for (int q = 0; q < 16; ++q)
+                    if (8 * (q >> 2) + (q & 3) > lim) S[q] = -INFINITY;
+            }
+            if (WIN && k0 < win_lo) {
+                const int llim = pos - a.window + 1 - k0 - 4 * hf;
+#pragma unroll
+                for (int q = 0; q < 16; ++q)
+                    if (8 * (q >> 2) + (q & 3) < llim) S[q] = -INFINITY;
+            }
+
+            // ---- row max of this wave's keys and the (rare) rescale of O
+            float mx = S[0];
+#pragma unroll
+            for (int q = 1; q < 16; ++q) mx = fmaxf(mx, S[q]);
+            mx = fmaxf(mx, __shfl_xor(mx, 32));
+            const float mt = mx * sl;
+            const bool grow = mt > m_run + kRescaleSlack;
+            const float m_new = grow ? mt : m_run;
+            const float m_use = m_new == -INFINITY ? 0.f : m_new;
+            if (__any(grow)) {
+                const float alpha = grow ? __builtin_amdgcn_exp2f(m_run - m_use) : 1.f;
+                l_run *= alpha;
+#pragma unroll
+                for (int db = 0; db < NDB; ++db)
+#pragma unroll
+                    for (int q = 0; q < 16; ++q) O[db][q] *= alpha;
+            }
+            m_run = m_new;
+            const float nm = -m_use;
+            uint32_t pk[8];
+
+            // ---- next tile's scores on the matrix cores while the vector
+            // ALU forms this tile's probabilities
+            f32x16_t N;
+            {
+                const uint16_t* kl = sm.k[rr ^ 1];
+#pragma unroll
+                for (int q = 0; q < 16; ++q) N[q] = 0.f;
+                u32x4_t a0 = ld16(kl + (koff + rl) * KS + hf * 8);
+#pragma unroll
+                for (int kk = 0; kk < NKK; ++kk) {
+                    u32x4_t b0 = a0;
+                    if (kk + 1 < NKK) b0 = ld16(kl + (koff + rl) * KS + (kk + 1) * 16 + hf * 8);
+                    N = mfma32(__builtin_bit_cast(bf16x8_t, a0), qf[kk], N);
+#pragma unroll
+                    for (int q = kk * 8 / NKK; q < (kk + 1) * 8 / NKK; ++q)
+                        pk[q] = pack_bf16x2(__builtin_amdgcn_exp2f(__builtin_fmaf(S[2 * q], sl, nm)),
+                                            __builtin_amdgcn_exp2f(__builtin_fmaf(S[2 * q + 1], sl, nm)));
+                    a0 = b0;
+                }
+                ATTN_INTERLEAVE(NKK, 1, 4);
+            }
+
+            // the K/V data stored at this tile's end arrived during the
+            // previous tile: K[j+2] replaces K[j], V[j+1] replaces V[j-1]
+            store_k(rr, cur);
+            store_v(rr ^ 1, cur);
+
+            // ---- O^T += V^T P^T over this wave's 32 keys
+            {
+                const uint16_t* vl = sm.v[rr] + tr_off;
+                auto vfrag = [&](int tt, int db) __attribute__((always_inline)) {
+                    const uint16_t* vrow = vl + (tt * 16) * VS + db * 32;
+                    const u32x2_t lo = lds_read_tr16(vrow);
+                    const u32x2_t hi = lds_read_tr16(vrow + 8 * VS);
+                    const u32x4_t vv = {lo.x, lo.y, hi.x, hi.y};
+                    return vv;
+                };
+                u32x4_t va = vfrag(0, 0);
+#pragma unroll
+                for (int st = 0; st < 2 * NDB; ++st) {          // st = (tt, db)
+                    const int tt = st / NDB, db = st % NDB;
+                    u32x4_t vn = va;
+                    if (st + 1 < 2 * NDB) vn = vfrag((st + 1) / NDB, (st + 1) % NDB);
+                    const u32x4_t pv = {pk[tt * 4], pk[tt * 4 + 1], pk[tt * 4 + 2], pk[tt * 4 + 3]};
+                    O[db] = mfma32(__builtin_bit_cast(bf16x8_t, va), __builtin_bit_cast(bf16x8_t, pv), O[db]);
+                    va = vn;
+                }
+            }
+            // the row sum is taken from the rounded probabilities
+            {
+                const bf16x2_t one = __builtin_bit_cast(bf16x2_t, 0x3f803f80u);
+                float s0 = 0.f, s1 = 0.f;
+#pragma unroll
+                for (int q = 0; q < 8; q += 2) {
+                    s0 = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, pk[q]), one, s0, false);
+                    s1 = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, pk[q + 1]), one, s1, false);
+                }
+                l_run += s0 + s1;
+            }
+            __syncthreads();
+            S = N;
+        };
+        for (int j = tb; j < te; ++j) {
+            tile(j, set0, set1);
+            if (++j >= te) break;
+            tile(j, set1, set0);
+        }
+    }
+
+    // ---- merge the key halves: waves 4..7 hand (m, l, O) of their rows to
+    // waves 0..3 through LDS (the tile buffers are free after the barrier)
+    __syncthreads();
+    float* xch = reinterpret_cast<float*>(&sm) + ((size_t)wr * 64 + lane) * (NDB * 16 + 2);
+    if (kh == 1) {
+        xch[0] = m_run;
+        xch[1] = l_run;
+#pragma unroll
+        for (int db = 0; db < NDB; ++db)
+#pragma unroll
+            for (int q = 0; q < 16; ++q) xch[2 + db * 16 + q] = O[db][q];
+    }
+    __syncthreads();
+    if (kh == 1) return;
+    {
+        const float m1 = xch[0], l1 = xch[1];
+        const float mm = fmaxf(m_run, m1);
+        const float mu = mm == -INFINITY ? 0.f : mm;
+        const float a0 = __builtin_amdgcn_exp2f(m_run - mu), a1 = __builtin_amdgcn_exp2f(m1 - mu);
+        l_run = l_run * a0 + l1 * a1;
+#pragma unroll
+        for (int db = 0; db < NDB; ++db)
+#pragma unroll
+            for (int q = 0; q < 16; ++q) O[db][q] = O[db][q] * a0 + xch[2 + db * 16 + q] * a1;
+        m_run = mm;
+    }
+
+    const float l_tot = l_run + __shfl_xor(l_run, 32);
+    if (!row_ok) return;
+    if (nsp <= 1) {
+        const float inv = 1.f / l_tot;
+        float* orow = a.out + ((size_t)t * a.n_heads + h) * HD;
+        if (a.gate.mode) {
+            // output gate: this lane's dims db*32 + 8*q4 + 4*hf + 0..3, all
+            // loads issued before any factor is formed
+            const size_t grow = (size_t)t * a.n_heads + h;
+            const uint16_t* gp = reinterpret_cast<const uint16_t*>(a.gate.p) + grow * (size_t)a.gate.ld;
+            if (a.gate.mode == kGateSoftplusHead) {
+                const float f = gate_fast(a.gate.mode, bf16_to_f32(gp[0])) * inv;
+#pragma unroll
+                for (int db = 0; db < NDB; ++db)
+#pragma unroll
+                    for (int q = 0; q < 16; ++q) O[db][q] *= f;
+            } else {
+                u32x2_t graw[NDB][4];
+                const bool vec = ((a.gate.ld & 3) == 0) && ((reinterpret_cast<uintptr_t>(a.gate.p) & 7) == 0);
+#pragma unroll
+                for (int db = 0; db < NDB; ++db)
+#pragma unroll
+                    for (int q4 = 0; q4 < 4; ++q4) {
+                        const uint16_t* p = gp + db * 32 + 8 * q4 + 4 * hf;
+                        if (vec) {
+                            graw[db][q4] = *reinterpret_cast<const u32x2_t*>(p);
+                        } else {
+                            graw[db][q4] = u32x2_t{(uint32_t)p[0] | ((uint32_t)p[1] << 16),
+                                                   (uint32_t)p[2] | ((uint32_t)p[3] << 16)};
+                        }
+                    }
+#pragma unroll
+                for (int db = 0; db < NDB; ++db)
+#pragma unroll
+                    for (int q4 = 0; q4 < 4; ++q4) {
+                        O[db][4 * q4] *= gate_fast(a.gate.mode, bf16_lo(graw[db][q4].x)) * inv;
+                        O[db][4 * q4 + 1] *= gate_fast(a.gate.mode, bf16_hi(graw[db][q4].x)) * inv;
+                        O[db][4 * q4 + 2] *= gate_fast(a.gate.mode, bf16_lo(graw[db][q4].y)) * inv;
+                        O[db][4 * q4 + 3] *= gate_fast(a.gate.mode, bf16_hi(graw[db][q4].y)) * inv;
+                    }
+            }
+        } else {
+#pragma unroll
+            for (int db = 0; db < NDB; ++db)
+#pragma unroll
+                for (int q = 0; q < 16; ++q) O[db][q] *= inv;
+        }
+#pragma unroll
+        for (int db = 0; db < NDB; ++db)
+#pragma unroll
+            for (int q4 = 0; q4 < 4; ++q4) {
+                const float4 v = make_float4(O[db][4 * q4], O[db][4 * q4 + 1], O[db][4 * q4 + 2],
+                                             O[db][4 * q4 + 3]);
+                *reinterpret_cast<float4*>(orow + db * 32 + 8 * q4 + 4 * hf) = v;
+            }
+    } else {
+        // partial of this item's row r - r_tile0: O/l in half precision
+        // (a part whose keys are all masked for the row has l = 0, O = 0)
+        float* pr = a.part + ((size_t)item * TILE_ROWS + (r - r_tile0)) * part_row_words(HD);
+        const float inv = l_tot > 0.f ? 1.f / l_tot : 0.f;
+        float mx = 0.f;
+#pragma unroll
+        for (int db = 0; db < NDB; ++db)
+#pragma unroll
+            for (int q = 0; q < 16; ++q) mx = fmaxf(mx, fabsf(O[db][q]));
+        mx = fmaxf(mx, __shfl_xor(mx, 32)) * inv;
+        const int ex = part_scale_exp(mx);
+        const float sc = __builtin_amdgcn_ldexpf(inv, -ex);
+        if (hf == 0) *reinterpret_cast<float4*>(pr) = make_float4(m_run, l_tot, (float)ex, 0.f);
+        uint32_t* ph = reinterpret_cast<uint32_t*>(pr + kPartHead);
+#pragma unroll
+        for (int db = 0; db < NDB; ++db)
+#pragma unroll
+            for (int q4 = 0; q4 < 4; ++q4) {
+                const u32x2_t v = {pack_f16x2(O[db][4 * q4] * sc, O[db][4 * q4 + 1] * sc),
+                                   pack_f16x2(O[db][4 * q4 + 2] * sc, O[db][4 * q4 + 3] * sc)};
+                *reinterpret_cast<u32x2_t*>(ph + (db * 32 + 8 * q4 + 4 * hf) / 2) = v;
+            }
+    }
+}
+
 // Merge split partials (m, l, O/l) of each row: m* = max m_s,
 // l* = sum l_s 2^(m_s - m*), out = sum (O/l)_s l_s 2^(m_s - m*) / l*.  One
 // wave per row, each lane over HD/64 consecutive dims: workgroup
@@ -778,6 +1172,12 @@ __global__ __launch_bounds__(256) void prefill_combine_kernel(PrefillArgs a) {
 #define ATTN_PREFILL_BIG_TILE_BLOCKS 512
 #endif
 constexpr int kBigTileBlocks = ATTN_PREFILL_BIG_TILE_BLOCKS;
+// 128-row work items run the key-split kernel (one 8-wave workgroup per CU)
+// rather than 4 waves over whole tiles (two workgroups per CU)
+#ifndef ATTN_PREFILL_KEY_SPLIT
+#define ATTN_PREFILL_KEY_SPLIT 1
+#endif
+constexpr bool kPrefillKeySplit = ATTN_PREFILL_KEY_SPLIT != 0;
 constexpr int kMaxSplitGroups = 64;      // (sequence, row tile) pairs: one per lane
 
 static int device_cus() {
@@ -807,7 +1207,7 @@ PrefillPlan plan_prefill(int n_seq, int n_heads, int n_kv, int head_dim, int n_t
     p.table_bytes = 0;
     if (base < kBigTileBlocks && tiles > min_tiles_per_split(p.rows_per_tile) &&
         (long)n_seq * p.n_qtiles <= kMaxSplitGroups) {
-        const long slots = (long)device_cus() * (p.rows_per_tile == 256 ? 1 : 2);
+        const long slots = (long)device_cus() * (p.rows_per_tile == 256 || kPrefillKeySplit ? 1 : 2);
         const size_t table = ((size_t)n_seq * p.n_qtiles * 2 * sizeof(int) + 255) / 256 * 256;
         // items <= slots + one extra part per row tile (ceil) -- see split_schedule
         const size_t parts = (size_t)(slots + base) * p.rows_per_tile * part_row_words(head_dim) * sizeof(float);
@@ -836,7 +1236,7 @@ PrefillPlan plan_prefill(int n_seq, int n_heads, int n_kv, int head_dim, int n_t
                     }
                     if (gt[qt] > gmax) gmax = gt[qt];
                 }
-                long best_T = gmax, best_cost = -1, prev_T = 0;
+                long best_T = gmax, best_cost = -1, prev_T = 0, best_n = 0;
                 const int cand[12] = {1, 2, 3, 4, 6, 8, 12, 16, 24, 32, 48, 64};
                 for (int k : cand) {
                     const long T = (gmax + k - 1) / k;
@@ -847,13 +1247,17 @@ PrefillPlan plan_prefill(int n_seq, int n_heads, int n_kv, int head_dim, int n_t
                     for (int qt = 0; qt < p.n_qtiles; ++qt) n += gt[qt] > 0 ? (gt[qt] + T - 1) / T : 0;
                     n *= n_kv;
                     if (n > p.grid) continue;
-                    const long cost = (n + slots - 1) / slots * (T + 2);
+                    const long cost = (n + slots - 1) / slots * (T + item_cost_tiles(p.rows_per_tile));
                     if (best_cost < 0 || cost < best_cost) {
                         best_cost = cost;
                         best_T = T;
+                        best_n = n;
                     }
                 }
                 p.part_tiles = (int)best_T;
+                // exactly one workgroup per item: workgroups without an item
+                // would still wait for a free slot before they exit
+                if (best_n > 0) p.grid = (int)best_n;
             }
         }
     }
@@ -865,6 +1269,9 @@ static void launch_prefill_win(const PrefillArgs& a, dim3 grid, hipStream_t stre
     if (a.rows_per_tile == 256) {
         if (a.head_dim == 128) prefill_bf16_kernel<128, 8, WIN><<<grid, dim3(512), 0, stream>>>(a);
         else prefill_bf16_kernel<64, 8, WIN><<<grid, dim3(512), 0, stream>>>(a);
+    } else if (kPrefillKeySplit) {
+        if (a.head_dim == 128) prefill_bf16_ks_kernel<128, WIN><<<grid, dim3(512), 0, stream>>>(a);
+        else prefill_bf16_ks_kernel<64, WIN><<<grid, dim3(512), 0, stream>>>(a);
     } else {
         if (a.head_dim == 128) prefill_bf16_kernel<128, 4, WIN><<<grid, dim3(256), 0, stream>>>(a);
         else prefill_bf16_kernel<64, 4, WIN><<<grid, dim3(256), 0, stream>>>(a);
