@@ -167,8 +167,9 @@ def cpu_baseline_prefill(w, d, budget_s):
         pos = np.arange(c0, c_end)
         q = oracle.finish_heads(d["q"][c0:c_end].float().numpy(), pos, f, w.rd, w.rope_scale,
                                 store=store, **qn)
-        oracle.attend(q, kc, vc, pos, w.scale, n_threads=threads)
-        flops += 4.0 * w.head_dim * w.n_heads * float(np.sum(pos + 1))
+        oracle.attend(q, kc, vc, pos, w.scale, n_threads=threads, window=w.window)
+        keys = np.minimum(pos + 1, w.window) if w.window > 0 else pos + 1
+        flops += 4.0 * w.head_dim * w.n_heads * float(np.sum(keys))
         rows += c_end - c0
         chunks += 1
         c_end = c0
@@ -198,8 +199,8 @@ def cpu_baseline_decode(w, d, budget_s):
         vc[:, c - 1] = d["v"][b].float().cpu().numpy()
         q = oracle.finish_heads(d["q"][b:b + 1].float().cpu().numpy(), pos, f, w.rd,
                                 store=oracle.STORE_BF16)
-        oracle.attend(q, kc, vc, pos, w.scale, want_probs=True, n_threads=threads)
-        nbytes += 2.0 * c * w.n_kv * w.head_dim * 2
+        oracle.attend(q, kc, vc, pos, w.scale, want_probs=True, n_threads=threads, window=w.window)
+        nbytes += 2.0 * (min(c, w.window) if w.window > 0 else c) * w.n_kv * w.head_dim * 2
         seqs += 1
     dt = time.perf_counter() - t_start
     return {"value": nbytes / dt / 1e9, "unit": "GB/s", "cores": threads, "kind": "oracle",
@@ -252,18 +253,21 @@ def bench_prefill(torch, w, args, stream):
 
 
 def decode_bytes(w, ctx):
-    # K and V of the keys read (the last `window` with a window); the
-    # probability rows are written whole (zeros before the window)
-    kv = 2.0 * sum(min(c, w.window) if w.window > 0 else c for c in ctx) * w.n_kv * w.head_dim * 2
+    # K and V of the keys read once per KV group (the last `window` with a
+    # window, plus the earlier queries' extra key for a multi-token step);
+    # the probability rows are written whole (zeros before the window)
+    span = lambda c: min(c, w.window + w.new_tokens - 1) if w.window > 0 else c
+    kv = 2.0 * sum(span(c) for c in ctx) * w.n_kv * w.head_dim * 2
     probs = 4.0 * sum(ctx) * w.n_heads if w.want_probs else 0.0
-    small = len(ctx) * w.n_heads * w.head_dim * (2 + 4)
+    small = len(ctx) * w.new_tokens * w.n_heads * w.head_dim * (2 + 4)
     return kv, kv + probs + small
 
 
 def bench_decode(torch, w, args, stream):
     from chunked_prefill_causal_rope_amd import runner, workloads as wl
     d = wl.gen_decode(w, device="cuda")
-    step = runner.DecodeStep(w, d, device="cuda")
+    # several new tokens per sequence (a verify) go through the prefill call
+    step = (runner.VerifyStep if w.new_tokens > 1 else runner.DecodeStep)(w, d, device="cuda")
     sec = time_steps(torch, step.run, args.steps, args.warmup, args.eager, stream)
     kv, alg = decode_bytes(w, d["ctx"])
     per_launch = []
@@ -273,13 +277,15 @@ def bench_decode(torch, w, args, stream):
     achieved = alg / (avg_ms * 1e-3) / 1e9
     roof = {"bound": "hbm", "achieved": round(achieved, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
             "frac": round(achieved / PEAK_HBM_GBS, 4), "traffic": recorded_traffic(w.name),
-            "kernel": "attn_decode (decode_split_kernel + decode_combine_kernel)",
+            "kernel": ("attn_prefill_chunk" if w.new_tokens > 1 else "attn_decode")
+                      + " (decode_split_kernel + decode_combine_kernel)",
             "avg_launch_ms": round(avg_ms, 4), "bytes_per_launch": alg,
             "kv_read_gbs": round(kv / (avg_ms * 1e-3) / 1e9, 1)}
     out = {"metric": "decode KV-read GB/s", "value": round(kv / sec / 1e9, 1), "unit": "GB/s",
            "ms_per_step": round(sec * 1e3, 4), "workload": w.name,
            "config": {"n_seq": w.n_seq, "n_heads": w.n_heads, "n_kv": w.n_kv,
                       "head_dim": w.head_dim, "ctx_total": sum(d["ctx"]),
+                      **({"new_tokens": w.new_tokens} if w.new_tokens > 1 else {}),
                       "probs": w.want_probs, **({"window": w.window} if w.window else {})},
            "roofline": roof}
     if w.want_probs:
@@ -333,7 +339,8 @@ def main():
                "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "bf16",
                "data": "synthetic", "config": dict(res["config"], workload=w.name),
                "roofline": res["roofline"], **({"importance": res["importance"]} if "importance" in res else {})}
-        if not args.no_cpu:
+        # the decode baseline covers one new token over a full-length cache
+        if not args.no_cpu and w.new_tokens == 1 and not w.ring:
             res["cpu_baseline"] = cpu_baseline_decode(w, d, args.cpu_seconds)
     else:
         res, d = bench_prefill(torch, w, args, stream)

@@ -53,6 +53,20 @@ size_t decode_part_bytes(int n_seq, int n_heads, int head_dim, int splits) {
     return (size_t)n_seq * n_heads * splits * (head_dim / 2 + kDecodePartHead) * sizeof(float);
 }
 
+// Chunks of at most kSmallChunk tokens per sequence (a two-position
+// speculative verify, a decode step through the prefill call) run on the
+// decode kernels: query rows = heads x tokens of a KV group (at most the
+// decode group limit), the context split into parts streamed once for all
+// of them, instead of row tiles of which a handful of rows would be used.
+constexpr int kSmallChunk = 2;
+bool small_chunk(int max_chunk, int group) {
+    return max_chunk <= kSmallChunk && group * max_chunk <= attn::decode_group_limit();
+}
+int small_chunk_span(int max_end, int window, int max_chunk) {
+    // keys from the first query's window start (rounded down to a step)
+    return attn::decode_key_span(max_end, window > 0 ? window + max_chunk - 1 : 0);
+}
+
 // Output gate arguments: mode 0 needs nothing; per-element modes read
 // head_dim values per row (ld >= head_dim), the per-head mode one (ld >= 1).
 bool gate_ok(const void* gate, int mode, int ld, int head_dim) {
@@ -231,8 +245,14 @@ size_t attn_prefill_workspace_bytes(int n_seq, int n_heads, int n_kv, int head_d
     if (n_seq <= 0 || n_heads <= 0 || n_kv <= 0 || n_heads % n_kv || n_tok <= 0 || max_chunk <= 0 ||
         max_end <= 0 || !hd_ok(head_dim))
         return 0;
-    return attn::plan_prefill(n_seq, n_heads, n_kv, head_dim, n_tok, max_chunk, max_end, 0,
-                              (size_t)-1).ws_bytes;
+    size_t ws = attn::plan_prefill(n_seq, n_heads, n_kv, head_dim, n_tok, max_chunk, max_end, 0,
+                                   (size_t)-1).ws_bytes;
+    if (small_chunk(max_chunk, n_heads / n_kv)) {
+        const int splits = decode_splits_full(small_chunk_span(max_end, 0, max_chunk), n_heads / n_kv * max_chunk);
+        const size_t need = decode_part_bytes(n_seq * max_chunk, n_heads, head_dim, splits);
+        if (need > ws) ws = need;
+    }
+    return ws;
 }
 
 int attn_prefill_chunk(const void* q, const void* k_cache, const void* v_cache, int dtype,
@@ -280,6 +300,43 @@ int attn_prefill_chunk(const void* q, const void* k_cache, const void* v_cache, 
         a.ring = wrapped;
         a.gate = gref;
         return status_of(attn::launch_attend_f32(a, s));
+    }
+    if (small_chunk(max_chunk, group) && workspace &&
+        workspace_bytes >= decode_part_bytes(n_seq * max_chunk, n_heads, head_dim, 1)) {
+        const int span = small_chunk_span(max_end, window, max_chunk);
+        int splits = decode_splits_full(span, group * max_chunk);
+        const size_t fit = workspace_bytes / decode_part_bytes(n_seq * max_chunk, n_heads, head_dim, 1);
+        if ((size_t)splits > fit) splits = (int)fit;
+        int split_len = (span + splits - 1) / splits;
+        split_len = (split_len + 63) / 64 * 64;
+        splits = (span + split_len - 1) / split_len;
+        if ((long)n_seq * splits * n_kv > 0x7fffffffL) return ATTN_EINVAL;
+        attn::DecodeArgs d{};
+        d.q = q;
+        d.k_cache = k_cache;
+        d.v_cache = v_cache;
+        d.out = out;
+        d.probs = nullptr;
+        d.part = (float*)workspace;
+        d.ctx = nullptr;
+        d.scale = scale;
+        d.n_seq = n_seq;
+        d.n_heads = n_heads;
+        d.n_kv = n_kv;
+        d.group = group;
+        d.head_dim = head_dim;
+        d.cap = cap;
+        d.max_ctx = max_end;
+        d.probs_ld = 0;
+        d.split_len = split_len;
+        d.n_splits = splits;
+        d.window = window;
+        d.ring = wrapped;
+        d.gate = gref;
+        d.cu_seq = cu_seq;
+        d.start = start;
+        d.n_q = max_chunk;
+        return status_of(attn::launch_decode_bf16(d, s));
     }
     attn::PrefillArgs a{};
     a.q = q;
@@ -403,6 +460,7 @@ int attn_decode(const void* q, const void* k_cache, const void* v_cache, int dty
     a.window = window;
     a.ring = wrapped;
     a.gate = gref;
+    a.n_q = 1;
     if ((long)n_seq * splits * n_kv > 0x7fffffffL) return ATTN_EINVAL;
     return status_of(attn::launch_decode_bf16(a, s));
 }

@@ -61,6 +61,21 @@ __host__ __device__ constexpr int decode_window_first(int ctx, int window) {
 __host__ __device__ constexpr int decode_part_base(int ctx, int window) {
     return decode_window_first(ctx, window) / kDecKB * kDecKB;
 }
+// The keys and query rows of sequence b: decode, one query at ctx-1; a small
+// chunk, nq queries at ctx-nq .. ctx-1 (ctx = start + len).  Returns false
+// when the sequence has no row.
+__device__ __forceinline__ bool decode_rows(const DecodeArgs& a, int b, int& ctx, int& nq) {
+    if (a.cu_seq) {
+        nq = min(a.cu_seq[b + 1] - a.cu_seq[b], a.n_q);
+        const int st = a.start[b];
+        if (nq <= 0 || st < 0) return false;
+        ctx = a.ring ? st + nq : min(st + nq, a.cap);
+        return true;
+    }
+    nq = 1;
+    ctx = a.ring ? min(a.ctx[b], a.max_ctx) : min(min(a.ctx[b], a.max_ctx), a.cap);
+    return true;
+}
 int decode_key_span(int max_ctx, int window) {
     return window > 0 && window < max_ctx ? std::min(window + kDecKB - 1, max_ctx) : max_ctx;
 }
@@ -195,12 +210,15 @@ __global__ __launch_bounds__(64) void decode_split_kernel(DecodeArgs a) {
     const int s = id % a.n_splits;
     const int b = id / a.n_splits;
     if (b >= a.n_seq) return;
-    const int ctx = a.ring ? min(a.ctx[b], a.max_ctx) : min(min(a.ctx[b], a.max_ctx), a.cap);
-    const int k_first = decode_window_first(ctx, a.window);
-    const int k_lo = decode_part_base(ctx, a.window) + s * a.split_len;
+    int ctx, nq_b;
+    if (!decode_rows(a, b, ctx, nq_b)) return;
+    // the first key any row reads: the window start of the first query
+    const int k_first = decode_window_first(ctx - nq_b + 1, a.window);
+    const int k_lo = decode_part_base(ctx - nq_b + 1, a.window) + s * a.split_len;
     const int k_hi = min(k_lo + a.split_len, ctx);
     if (k_lo >= k_hi) return;
     const int G = a.group;
+    const int GV = G * a.n_q;                   // query rows of the group (heads x queries)
     if (PROBS && lane < GQ) lhalf[lane] = 0.f;
 
     const int col = lane & 15;   // score layout: key within a 16-key block
@@ -210,11 +228,14 @@ __global__ __launch_bounds__(64) void decode_split_kernel(DecodeArgs a) {
 
     bf16x8_t qa[NK];
     {
-        // A row `col` holds head (col/4)*HPL + col%4 when col%4 < HPL
+        // A row `col` holds query row (col/4)*HPL + col%4 when col%4 < HPL:
+        // query qi of head qh of the group
         const int hq = (col >> 2) * HPL + (col & 3);
-        const bool ok = (col & 3) < HPL && hq < G;
+        const int qi = hq / G, qh = hq - qi * G;
+        const bool ok = (col & 3) < HPL && hq < GV && qi < nq_b;
+        const size_t qt = a.cu_seq ? (size_t)a.cu_seq[b] + (ok ? qi : 0) : (size_t)b;
         const uint16_t* qb =
-            reinterpret_cast<const uint16_t*>(a.q) + ((size_t)b * a.n_heads + g * G + (ok ? hq : 0)) * HD;
+            reinterpret_cast<const uint16_t*>(a.q) + (qt * a.n_heads + g * G + (ok ? qh : 0)) * HD;
 #pragma unroll
         for (int k = 0; k < NK; ++k) {
             u32x4_t u = {0u, 0u, 0u, 0u};
@@ -237,6 +258,15 @@ __global__ __launch_bounds__(64) void decode_split_kernel(DecodeArgs a) {
     for (int r = 0; r < HPL; ++r) {
         m_run[r] = -INFINITY;
         l_run[r] = 0.f;
+    }
+    // keys each of this lane's rows may read: up to its own position, from
+    // its window start
+    int key_min[HPL], key_max[HPL];
+#pragma unroll
+    for (int r = 0; r < HPL; ++r) {
+        const int pos = ctx - nq_b + (grp * HPL + r) / G;
+        key_max[r] = min(pos, k_hi - 1);
+        key_min[r] = a.window > 0 ? max(pos - a.window + 1, 0) : 0;
     }
     float o[GQ][8];
 #pragma unroll
@@ -294,15 +324,15 @@ __global__ __launch_bounds__(64) void decode_split_kernel(DecodeArgs a) {
 #pragma unroll
             for (int k = 0; k < NK; ++k) S = mfma16(qa[k], __builtin_bit_cast(bf16x8_t, kf[buf][blk][k]), S);
             const int key = k0 + 16 * blk + col;
-            const bool ok = key < k_hi && key >= k_first;
 #pragma unroll
-            for (int r = 0; r < HPL; ++r) x[blk][r] = ok ? S[r] * sl : -INFINITY;
+            for (int r = 0; r < HPL; ++r)
+                x[blk][r] = key <= key_max[r] && key >= key_min[r] ? S[r] * sl : -INFINITY;
         }
         bool grow_any = false;
         float mt[HPL];
 #pragma unroll
         for (int r = 0; r < HPL; ++r) {
-            mt[r] = row16_max(fmaxf(x[0][r], x[1][r]));   // finite in a part's first step
+            mt[r] = row16_max(fmaxf(x[0][r], x[1][r]));
             grow_any |= mt[r] > m_run[r] + kDecSlack;
         }
         if (__any(grow_any)) {
@@ -332,11 +362,16 @@ __global__ __launch_bounds__(64) void decode_split_kernel(DecodeArgs a) {
                 }
             }
         }
+        // a row none of whose keys so far was readable has m = -inf and
+        // probabilities 0
+        float m_use[HPL];
+#pragma unroll
+        for (int r = 0; r < HPL; ++r) m_use[r] = m_run[r] == -INFINITY ? 0.f : m_run[r];
 #pragma unroll
         for (int blk = 0; blk < 2; ++blk)
 #pragma unroll
             for (int r = 0; r < HPL; ++r) {
-                const float p = __builtin_amdgcn_exp2f(x[blk][r] - m_run[r]);
+                const float p = __builtin_amdgcn_exp2f(x[blk][r] - m_use[r]);
                 l_run[r] += p;
                 pbuf[(16 * blk + col) * GQ + grp * HPL + r] = p;
             }
@@ -427,24 +462,28 @@ __global__ __launch_bounds__(64) void decode_split_kernel(DecodeArgs a) {
         // lanes 16j..16j+15 hold every dim of the row (lanes CPR apart repeat)
         ex[hh] = part_scale_exp(row16_max(mx) * linv[hh]);
     }
+    // partial of output row (b*n_q + qi)*n_heads + g*G + qh, part s
     constexpr int PS = dec_part_words(HD);
-    float* part = a.part + (((size_t)b * a.n_heads + g * G) * a.n_splits + s) * PS;
-    const size_t head_stride = (size_t)a.n_splits * PS;
+    auto part_of = [&](int v) __attribute__((always_inline)) {
+        const int qi = v / G, qh = v - qi * G;
+        const size_t row = ((size_t)b * a.n_q + qi) * a.n_heads + g * G + qh;
+        return a.part + (row * a.n_splits + s) * PS;
+    };
     if (col == 0) {
 #pragma unroll
         for (int r = 0; r < HPL; ++r) {
             const int hh = grp * HPL + r;
-            if (hh < G)
-                *reinterpret_cast<float4*>(part + hh * head_stride) =
+            if (hh < GV && hh / G < nq_b)
+                *reinterpret_cast<float4*>(part_of(hh)) =
                     make_float4(m_run[r], l_run[r], PROBS ? lhalf[hh] : 0.f, (float)ex[hh]);
         }
     }
     if (vr == 0) {
 #pragma unroll
         for (int hh = 0; hh < GQ; ++hh) {
-            if (hh < G) {
+            if (hh < GV && hh / G < nq_b) {
                 const float sc = __builtin_amdgcn_ldexpf(linv[hh], -ex[hh]);
-                uint32_t* dst = reinterpret_cast<uint32_t*>(part + hh * head_stride + kPartHeadD) + 4 * vc_;
+                uint32_t* dst = reinterpret_cast<uint32_t*>(part_of(hh) + kPartHeadD) + 4 * vc_;
                 *reinterpret_cast<u32x4_t*>(dst) =
                     u32x4_t{pack_f16x2(o[hh][0] * sc, o[hh][1] * sc), pack_f16x2(o[hh][2] * sc, o[hh][3] * sc),
                             pack_f16x2(o[hh][4] * sc, o[hh][5] * sc), pack_f16x2(o[hh][6] * sc, o[hh][7] * sc)};
@@ -472,22 +511,27 @@ template <int HD>
 __global__ __launch_bounds__(256) void decode_combine_kernel(DecodeArgs a) {
     __shared__ float red[4];
     __shared__ float osum[256];
+    // output row (b*n_q + qi)*n_heads + h: query qi of sequence b, head h
     const int row = blockIdx.x;
-    const int b = row / a.n_heads;
+    const int b = row / (a.n_heads * a.n_q);
+    const int qi = (row / a.n_heads) % a.n_q;
     const int tid = threadIdx.x;
     if (b >= a.n_seq) return;
-    const int ctx = a.ring ? min(a.ctx[b], a.max_ctx) : min(min(a.ctx[b], a.max_ctx), a.cap);
-    float* orow = a.out + (size_t)row * HD;
+    int ctx, nq_b;
+    if (!decode_rows(a, b, ctx, nq_b) || qi >= nq_b) return;
+    // the packed row of the query (decode: the sequence)
+    const size_t orow_id = a.cu_seq ? ((size_t)a.cu_seq[b] + qi) * a.n_heads + row % a.n_heads : (size_t)row;
+    float* orow = a.out + orow_id * HD;
     if (ctx < 1) {
         for (int d = tid; d < HD; d += 256) orow[d] = 0.f;
         return;
     }
     constexpr int PS = dec_part_words(HD);
     const int k_first = decode_window_first(ctx, a.window);
-    const int k_base = decode_part_base(ctx, a.window);
+    const int k_base = decode_part_base(ctx - nq_b + 1, a.window);
     const int n_parts = min((ctx - k_base + a.split_len - 1) / a.split_len, a.n_splits);
     // output gate factor of this thread's dim, loaded before the merge
-    const float gf = a.gate.mode && tid < HD ? gate_factor_bf16(a.gate, (size_t)row, tid) : 1.f;
+    const float gf = a.gate.mode && tid < HD ? gate_factor_bf16(a.gate, orow_id, tid) : 1.f;
     const float* pr = a.part + (size_t)row * a.n_splits * PS;
     float mm = -INFINITY;
     for (int s = tid; s < n_parts; s += 256) mm = fmaxf(mm, pr[(size_t)s * PS]);
@@ -640,9 +684,10 @@ hipError_t launch_decode_importance(const ImportanceArgs& a, hipStream_t stream)
 template <int HD, bool PROBS, bool LONG, bool RING>
 static void launch_split(const DecodeArgs& a, hipStream_t stream) {
     const dim3 grid((unsigned)((long)a.n_seq * a.n_splits * a.n_kv));
-    if (a.group <= 4)
+    const int rows = a.group * a.n_q;          // query rows per KV group
+    if (rows <= 4)
         decode_split_kernel<HD, 1, PROBS, LONG, RING><<<grid, dim3(64), 0, stream>>>(a);
-    else if (a.group <= 8)
+    else if (rows <= 8)
         decode_split_kernel<HD, 2, PROBS, LONG, RING><<<grid, dim3(64), 0, stream>>>(a);
     else
         decode_split_kernel<HD, 4, PROBS, LONG, RING><<<grid, dim3(64), 0, stream>>>(a);
@@ -664,7 +709,7 @@ static void launch_decode_hd(const DecodeArgs& a, hipStream_t stream) {
         launch_split_any<HD, true>(a, stream);
     else
         launch_split_any<HD, false>(a, stream);
-    decode_combine_kernel<HD><<<dim3((unsigned)(a.n_seq * a.n_heads)), dim3(256), 0, stream>>>(a);
+    decode_combine_kernel<HD><<<dim3((unsigned)(a.n_seq * a.n_q * a.n_heads)), dim3(256), 0, stream>>>(a);
 }
 
 hipError_t launch_decode_bf16(const DecodeArgs& a, hipStream_t stream) {

@@ -96,6 +96,13 @@ struct DecodeArgs {
     int window;                // 0: all ctx keys; W: the last W
     int ring;                  // key j in cache row j mod cap (needs W <= cap)
     GateRef gate;              // output gate (mode 0: none)
+    // A chunk of at most n_q tokens per sequence (a varlen batch, rows packed
+    // as for prefill; no probabilities) instead of one query at ctx[b]-1:
+    // cu_seq/start non-null, sequence b's queries at start[b] .. start[b] +
+    // len_b - 1 attend keys up to their own position.  Decode: null, n_q = 1.
+    const int32_t* cu_seq;
+    const int32_t* start;
+    int n_q;
 };
 int decode_group_limit();
 // Keys one decode row may read, from its part start on: max_ctx, or with a

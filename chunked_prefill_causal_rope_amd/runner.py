@@ -170,3 +170,46 @@ class DecodeStep:
     def run(self):
         self.finish_and_append()
         self.attend()
+
+
+class VerifyStep:
+    """new_tokens (> 1, e.g. a 2-token speculative verify) per sequence of a
+    decode batch, through the prefill calls: finish and append the tokens at
+    ctx-n .. ctx-1, then attend them (each up to its own position)."""
+
+    def __init__(self, w: Workload, data: dict, device="cuda"):
+        self.w = w
+        n = w.new_tokens
+        ctx = data["ctx"]
+        self.ctx_list = ctx
+        n_seq = len(ctx)
+        self.k_cache = data["k_cache"].to(device)
+        self.v_cache = data["v_cache"].to(device)
+        self.q = data["q"].to(device).contiguous()
+        self.k = data["k"].to(device).contiguous()
+        self.v = data["v"].to(device).contiguous()
+        self.q_rot = torch.empty_like(self.q)
+        self.inv_freq = tables(w, device)
+        self.q_norm_w = data["q_norm_w"].to(device) if data.get("q_norm_w") is not None else None
+        self.k_norm_w = data["k_norm_w"].to(device) if data.get("k_norm_w") is not None else None
+        self.gate = data["gate"].to(device).contiguous() if data.get("gate") is not None else None
+        self.batch = api.Batch([c - n for c in ctx], [n] * n_seq, device=device)
+        self.out = torch.empty((n_seq * n, w.n_heads, w.head_dim), dtype=torch.float32, device=device)
+        wsb = api.prefill_workspace_bytes(self.batch, w.n_heads, w.n_kv, w.head_dim)
+        self.workspace = torch.empty(max(wsb, 16) // 4 + 1, dtype=torch.float32, device=device)
+
+    def finish_and_append(self):
+        w = self.w
+        api.rope_qkv(self.q, self.q_rot, self.k_cache, self.v_cache, self.k, self.v, self.batch,
+                     self.inv_freq, w.rd, w.rope_scale, w.norm_style, self.q_norm_w,
+                     self.k_norm_w, w.norm_eps, ring=w.ring, v_norm=w.v_norm)
+
+    def attend(self, workspace=None):
+        api.prefill_chunk(self.q_rot, self.k_cache, self.v_cache, self.batch, self.w.scale,
+                          self.out, self.workspace if workspace is None else workspace,
+                          window=self.w.window, ring=self.w.ring, gate=self.gate,
+                          gate_mode=self.w.gate_mode)
+
+    def run(self):
+        self.finish_and_append()
+        self.attend()

@@ -46,8 +46,10 @@ class Workload:
     prompt_len: int = 0                    # fixed length when len_range is None
     len_range: tuple | None = None         # (lo, hi) inclusive, drawn per sequence
     chunk: int = 0
-    # decode (chunk = 1 at position ctx-1)
+    # decode (chunk = 1 at position ctx-1; new_tokens > 1: that many tokens at
+    # ctx-new_tokens .. ctx-1 through the prefill call, e.g. a 2-token verify)
     decode: bool = False
+    new_tokens: int = 1
     ctx_range: tuple | None = None         # (lo, hi) inclusive
     cap: int | None = None
     want_probs: bool = False
@@ -100,6 +102,10 @@ CONFIGS["c2_decode_sw4096"] = CONFIGS["c2_decode"].replace(name="c2_decode_sw409
 # element).
 CONFIGS["c3_qwen_varlen_gate"] = CONFIGS["c3_qwen_varlen"].replace(name="c3_qwen_varlen_gate",
                                                                    gate_mode=1)
+# A two-token speculative verify over the decode batch: each sequence adds
+# the tokens at ctx-2 and ctx-1 through the prefill call (chunk = 2).
+CONFIGS["c2_verify2"] = CONFIGS["c2_decode"].replace(name="c2_verify2", new_tokens=2,
+                                                     want_probs=False)
 # The same windows over a ring cache: 4096 + 2048 - 1 rows rounded up to a
 # multiple of 64 for the prefill (a chunk is written before it attends), 4096
 # rows for decode.
@@ -159,10 +165,11 @@ def gen_prefill(w: Workload, device="cpu"):
 
 
 def gen_decode(w: Workload, device="cpu"):
-    """Decode inputs: ctx[b] counts the new token, the cache holds ctx[b]-1
-    prior rows (already rotated; every cache row is drawn; with a ring, row r
-    holds the latest position congruent to r), and the new token's q/k/v sit
-    at position ctx[b]-1."""
+    """Decode inputs: ctx[b] counts the new tokens, the cache holds the
+    ctx[b]-new_tokens prior rows (already rotated; every cache row is drawn;
+    with a ring, row r holds the latest position congruent to r), and the new
+    tokens' q/k/v ([n_seq * new_tokens] rows, sequence-major) sit at
+    positions ctx[b]-new_tokens .. ctx[b]-1."""
     g = _gen(w.seed, device)
     lo, hi = w.ctx_range
     ctx = [int(x) for x in torch.randint(lo, hi + 1, (w.n_seq,), generator=g, device=device)]
@@ -170,14 +177,15 @@ def gen_decode(w: Workload, device="cpu"):
     dt = w.torch_dtype
     kc = _normal((w.n_seq, w.n_kv, cap, w.head_dim), g, device, dt)
     vc = _normal((w.n_seq, w.n_kv, cap, w.head_dim), g, device, dt)
-    q = _normal((w.n_seq, w.n_heads, w.head_dim), g, device, dt)
-    k = _normal((w.n_seq, w.n_kv, w.head_dim), g, device, dt)
-    v = _normal((w.n_seq, w.n_kv, w.head_dim), g, device, dt)
+    n = w.n_seq * w.new_tokens
+    q = _normal((n, w.n_heads, w.head_dim), g, device, dt)
+    k = _normal((n, w.n_kv, w.head_dim), g, device, dt)
+    v = _normal((n, w.n_kv, w.head_dim), g, device, dt)
     qw = kw = None
     if w.norm_style != NORM_NONE:
         qw = (1.0 + 0.1 * torch.randn((w.head_dim,), generator=g, device=device)).float()
         kw = (1.0 + 0.1 * torch.randn((w.head_dim,), generator=g, device=device)).float()
-    gate = _gate(w, w.n_seq, g, device)
+    gate = _gate(w, n, g, device)
     return dict(ctx=ctx, k_cache=kc, v_cache=vc, q=q, k=k, v=v, q_norm_w=qw, k_norm_w=kw,
                 cap=cap, gate=gate)
 

@@ -181,3 +181,29 @@ def oracle_decode_row(w, d, b, c):
     probs = np.zeros((w.n_heads, c))
     probs[:, lo:] = P[0]
     return gated(w, o, d["gate"][b:b + 1] if w.gate_mode else None)[0], probs
+
+
+def oracle_verify_rows(w, d, b, c):
+    """Oracle outputs [n][nh][hd] of the n = w.new_tokens queries of sequence
+    b whose context is c: the new tokens' K (finished) and V at positions
+    c-n .. c-1, the prior rows from the drawn cache (row j mod cap with a
+    ring); query i at position c-n+i attends keys up to itself (the last W
+    with a window)."""
+    n = w.new_tokens
+    f = oracle_table(w)
+    cap = d["k_cache"].shape[2]
+    first_pos = c - n
+    lo = max(0, first_pos - w.window + 1) if w.window else 0
+    pos = np.arange(lo, c)
+    rows = torch.as_tensor(pos % cap if w.ring else pos, device=d["k_cache"].device)
+    kc = np64(d["k_cache"][b][:, rows]).copy()
+    vc = np64(d["v_cache"][b][:, rows]).copy()
+    new_pos = np.arange(first_pos, c)
+    sl = slice(b * n, (b + 1) * n)
+    kn = oracle.finish_heads(np64(d["k"][sl]), new_pos, f, w.rd, w.rope_scale, store=store_of(w))
+    kc[:, c - n - lo:] = kn.transpose(1, 0, 2)
+    vc[:, c - n - lo:] = v_rows(w, d["v"][sl]).transpose(1, 0, 2)
+    q = oracle.finish_heads(np64(d["q"][sl]), new_pos, f, w.rd, w.rope_scale, store=store_of(w))
+    # keys lo..c-1 re-indexed from 0
+    o, _ = oracle.attend(q, kc, vc, new_pos - lo, w.scale, window=w.window)
+    return gated(w, o, d["gate"][sl] if w.gate_mode else None)

@@ -9,7 +9,8 @@ import torch
 import oracle
 from chunked_prefill_causal_rope_amd import api, runner, workloads as wl
 from parity_util import (PROB_ABS_FRAC, PROB_REL_TOL, check_bf16_rows, check_f32, check_probs, np64,
-                         oracle_decode_row, oracle_prefill_packed, oracle_table, say, store_of)
+                         oracle_decode_row, oracle_prefill_packed, oracle_table, oracle_verify_rows, say,
+                         store_of)
 
 pytestmark = pytest.mark.gpu
 
@@ -747,6 +748,41 @@ def test_decode_gates_and_vnorm(dtype, mode, v_norm, window):
             check_f32(got_o[b], o, f"seq {b} ctx {c}")
         # the probabilities are not gated
         check_probs(got_p[b, :, :c], P, dtype == wl.BF16, f"seq {b} ctx {c}")
+
+
+# ------------------------------------------------------------------ chunks of 1-2 tokens
+
+@pytest.mark.parametrize("nh,nkv,n_new,window,ring,gate", [
+    (32, 8, 2, 0, 0, 0), (32, 8, 1, 0, 0, 0), (16, 2, 2, 0, 0, 1), (40, 8, 2, 100, 0, 0),
+    (8, 8, 2, 0, 0, 2), (32, 8, 2, 1000, 1088, 0), (64, 8, 2, 0, 0, 0), (32, 2, 2, 0, 0, 0)])
+def test_small_chunk_path_matches_oracle(nh, nkv, n_new, window, ring, gate):
+    """Chunks of at most two tokens run on the decode kernels (query rows =
+    heads x tokens, up to 16: 64/8 heads x 2 tokens is the widest); wider
+    groups (32/2 x 2) take the prefill kernel.  Against the oracle, and against the prefill
+    kernel run on the same batch (a workspace too small for the decode
+    kernels' parts)."""
+    ctx = [2, 3, 63, 64, 65, 1025, 3000, 2049, 97] if n_new == 2 else [1, 2, 64, 1025, 3000]
+    hd = 128
+    cap = ring or 3072
+    w = wl.Workload(name="small-chunk", dtype=wl.BF16, n_heads=nh, n_kv=nkv, head_dim=hd, seed=91,
+                    n_seq=len(ctx), decode=True, ctx_range=(2, 3000), cap=cap, new_tokens=n_new,
+                    window=window, ring=bool(ring), gate_mode=gate)
+    say(f"small chunk nh={nh} nkv={nkv} n={n_new} W={window} ring={ring} gate={gate}")
+    d = wl.gen_decode(w)
+    d["ctx"] = ctx
+    step = runner.VerifyStep(w, d, device=DEV)
+    step.run()
+    torch.cuda.synchronize()
+    got = np64(step.out).reshape(len(ctx), n_new, nh, hd)
+    for b, c in enumerate(ctx):
+        check_bf16_rows(got[b], oracle_verify_rows(w, d, b, c), f"seq {b} ctx {c}")
+    if not ring:
+        # the prefill kernel on the same batch (the cache already holds the rows)
+        small = torch.empty(4, dtype=torch.float32, device=DEV)
+        ref = step.out.clone()
+        step.attend(workspace=small)
+        torch.cuda.synchronize()
+        check_bf16_rows(np64(step.out), np64(ref), "decode kernels vs prefill kernel")
 
 
 # ------------------------------------------------------------------ importance
