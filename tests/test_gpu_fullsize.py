@@ -175,3 +175,24 @@ def test_c3_qwen_varlen_gate_full():
     w, d, run = run_prefill("c3_qwen_varlen_gate")
     for b in (0, 3, 7):
         check_sequence(w, d, run, b, 500 + b, "c3 gate", check_cache=False)
+
+
+def test_c2_verify2_full():
+    # two new tokens per sequence of the decode batch through the prefill
+    # call (the decode kernels), sampled sequences against the oracle
+    from parity_util import oracle_verify_rows
+    w = wl.CONFIGS["c2_verify2"]
+    say(f"full-size verify: {w}")
+    d = wl.gen_decode(w, device=DEV)
+    step = runner.VerifyStep(w, d, device=DEV)
+    step.run()
+    torch.cuda.synchronize()
+    ctx = d["ctx"]
+    order = np.argsort(ctx)
+    picks = sorted({int(order[0]), int(order[-1]), int(order[len(ctx) // 2]), 5})
+    out = np64(step.out).reshape(len(ctx), 2, w.n_heads, w.head_dim)
+    assert np.all(np.isfinite(out))
+    for b in picks:
+        check_bf16_rows(out[b], oracle_verify_rows(w, d, b, ctx[b]), f"verify seq {b} ctx {ctx[b]}")
+    for b, c in enumerate(ctx):
+        assert torch.equal(step.v_cache[b, :, c - 2:c], d["v"][2 * b:2 * b + 2].transpose(0, 1).to(DEV))
