@@ -48,6 +48,14 @@ def v_rows(w, v):
     return oracle.vnorm_heads(v, w.norm_eps, store_of(w)) if w.v_norm else v
 
 
+def gain_of(w, gate, shape):
+    """The output gate's factors (f64, from the same gate values), shaped like
+    an output of `shape`, or None without a gate."""
+    if not w.gate_mode:
+        return None
+    return oracle.output_gate(np.ones(shape), np64(gate).reshape(shape[:-1] + (-1,)), w.gate_mode)
+
+
 def gated(w, out, gate):
     """The oracle output after the workload's output gate (if any)."""
     if not w.gate_mode:
@@ -108,8 +116,14 @@ def oracle_rows(w, d, b, positions, heads=None):
     return positions, gated(w, out, d["gate"][idx] if w.gate_mode else None)
 
 
-def check_bf16_rows(got: np.ndarray, ref: np.ndarray, label=""):
-    """Per-row criterion; returns (worst row err/rms, tensor-level max/rms, rel rmse)."""
+def check_bf16_rows(got: np.ndarray, ref: np.ndarray, label="", gain=None):
+    """Per-row criterion; returns (worst row err/rms, tensor-level max/rms, rel rmse).
+    gain: an output gate's factors, divided out of both sides first -- the
+    bound is on the attention output; a factor per element would otherwise
+    scale each element's error and the row RMS differently."""
+    if gain is not None:
+        got = got / gain
+        ref = ref / gain
     got = got.reshape(-1, got.shape[-1])
     ref = ref.reshape(-1, ref.shape[-1])
     assert np.all(np.isfinite(got)), f"{label}: non-finite output"

@@ -9,8 +9,8 @@ import torch
 
 import oracle
 from chunked_prefill_causal_rope_amd import runner, workloads as wl
-from parity_util import (check_bf16_rows, check_probs, np64, oracle_decode_row, oracle_rows,
-                         oracle_table, say)
+from parity_util import (check_bf16_rows, check_probs, gain_of, np64, oracle_decode_row,
+                         oracle_rows, oracle_table, say)
 
 pytestmark = pytest.mark.gpu
 DEV = "cuda:0"
@@ -61,7 +61,8 @@ def check_sequence(w, d, run, b, seed, label, check_cache=True):
     idx = torch.as_tensor(d["cu_seq"][b] + pos, device=got_all.device)
     got = np64(got_all[idx])
     assert np.all(np.isfinite(np64(got_all[d["cu_seq"][b]:d["cu_seq"][b] + n])))
-    check_bf16_rows(got, ref, f"{label} seq {b} ({len(pos)} positions x {w.n_heads} heads)")
+    gain = gain_of(w, d["gate"][idx], got.shape) if w.gate_mode else None
+    check_bf16_rows(got, ref, f"{label} seq {b} ({len(pos)} positions x {w.n_heads} heads)", gain=gain)
     if check_cache:
         # every cache row of the sequence equals the oracle's rounded K and the input V
         f = oracle_table(w)

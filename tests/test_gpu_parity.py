@@ -8,7 +8,7 @@ import torch
 
 import oracle
 from chunked_prefill_causal_rope_amd import api, runner, workloads as wl
-from parity_util import (PROB_ABS_FRAC, PROB_REL_TOL, check_bf16_rows, check_f32, check_probs, np64,
+from parity_util import (PROB_ABS_FRAC, PROB_REL_TOL, check_bf16_rows, check_f32, check_probs, gain_of, np64,
                          oracle_decode_row, oracle_prefill_packed, oracle_table, oracle_verify_rows, say,
                          store_of)
 
@@ -686,7 +686,7 @@ def test_bf16_prefill_gates_and_vnorm(name, nh, nkv, hd, T, chunk, mode, v_norm)
     run.run_all()
     torch.cuda.synchronize()
     ref = oracle_prefill_packed(w, d, chunk)
-    check_bf16_rows(np64(run.gather("out")), ref["out"], name)
+    check_bf16_rows(np64(run.gather("out")), ref["out"], name, gain=gain_of(w, d["gate"], ref["out"].shape))
     kc_ref, vc_ref = ref["caches"][0]
     want_v = _to_dtype_bits(vc_ref, torch.bfloat16)
     mism = int((_bits(run.v_cache[0]) != want_v).sum())
@@ -743,7 +743,8 @@ def test_decode_gates_and_vnorm(dtype, mode, v_norm, window):
     for b, c in enumerate(ctx):
         o, P = oracle_decode_row(w, d, b, c)
         if dtype == wl.BF16:
-            check_bf16_rows(got_o[b], o, f"seq {b} ctx {c}")
+            gain = gain_of(w, d["gate"][b] if w.gate_mode else None, o.shape)
+            check_bf16_rows(got_o[b], o, f"seq {b} ctx {c}", gain=gain)
         else:
             check_f32(got_o[b], o, f"seq {b} ctx {c}")
         # the probabilities are not gated
@@ -775,7 +776,9 @@ def test_small_chunk_path_matches_oracle(nh, nkv, n_new, window, ring, gate):
     torch.cuda.synchronize()
     got = np64(step.out).reshape(len(ctx), n_new, nh, hd)
     for b, c in enumerate(ctx):
-        check_bf16_rows(got[b], oracle_verify_rows(w, d, b, c), f"seq {b} ctx {c}")
+        ref = oracle_verify_rows(w, d, b, c)
+        g = d["gate"][b * n_new:(b + 1) * n_new] if gate else None
+        check_bf16_rows(got[b], ref, f"seq {b} ctx {c}", gain=gain_of(w, g, ref.shape))
     if not ring:
         # the prefill kernel on the same batch (the cache already holds the rows)
         small = torch.empty(4, dtype=torch.float32, device=DEV)
