@@ -351,7 +351,10 @@ __global__ __launch_bounds__(NW * 64, 8 / NW) void prefill_bf16_kernel(PrefillAr
     // j mod (cap / kTK), never split by the ring's end
     const int ring_tiles = a.cap / kTK;
     auto tile_rsrc = [&](const uint16_t* base, int j) __attribute__((always_inline)) {
-        const int rows = min(max(n_keys - j * kTK, 0), kTK);
+        // the clamp compiles to a vector-ALU instruction; without the
+        // readfirstlane the compiler cannot see that the resource is uniform
+        // and wraps every load in a loop over distinct resource values
+        const int rows = __builtin_amdgcn_readfirstlane(min(max(n_keys - j * kTK, 0), kTK));
         const int jt = WIN && a.ring ? j % ring_tiles : j;
         return __builtin_amdgcn_make_buffer_rsrc((void*)(base + (size_t)jt * kTK * HD), (short)0, rows * HD * 2,
                                                  kBufferWord3);
@@ -767,7 +770,10 @@ __global__ __launch_bounds__(512, 1) void prefill_bf16_ks_kernel(PrefillArgs a) 
     }
     const int ring_tiles = a.cap / kTK;
     auto tile_rsrc = [&](const uint16_t* base, int j) __attribute__((always_inline)) {
-        const int rows = min(max(n_keys - j * kTK, 0), kTK);
+        // the clamp compiles to a vector-ALU instruction; without the
+        // readfirstlane the compiler cannot see that the resource is uniform
+        // and wraps every load in a loop over distinct resource values
+        const int rows = __builtin_amdgcn_readfirstlane(min(max(n_keys - j * kTK, 0), kTK));
         const int jt = WIN && a.ring ? j % ring_tiles : j;
         return __builtin_amdgcn_make_buffer_rsrc((void*)(base + (size_t)jt * kTK * HD), (short)0, rows * HD * 2,
                                                  kBufferWord3);
