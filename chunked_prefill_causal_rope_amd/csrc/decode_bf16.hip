@@ -286,10 +286,34 @@ __global__ __launch_bounds__(64) void decode_split_kernel(DecodeArgs a) {
         return r >= a.cap ? r - a.cap : r;
     };
 
-    // Rows past the part's end re-read its last row (in bounds); their
-    // scores are masked to -inf so their probabilities are exactly 0.
+    // Rows past the part's end read as zeros (buffer loads) or re-read its
+    // last row (ring); their scores are masked to -inf so their
+    // probabilities are exactly 0.
     u32x4_t kf[2][2][NK], vf[2][NV];
+    // Without a ring the part's rows are contiguous: each step's loads are
+    // buffer loads from a resource over that step's rows (base and size in
+    // scalar registers, fixed per-lane offsets: no per-load address
+    // arithmetic), and rows past the part's end read as zeros without
+    // touching memory.  Nontemporal (every byte is used once).
+    constexpr int kNT = 2;       // cache policy bit: nontemporal
+    const int koff = (col * HD + 8 * grp) * 2, voff = (vr * HD + 8 * vc_) * 2;
     auto load = [&](int k0, int buf) __attribute__((always_inline)) {
+        if constexpr (!RING) {
+            const int nb = min(max(k_hi - k0, 0), kDecKB) * HD * 2;
+            const auto krs = uniform_rsrc(kc + (size_t)k0 * HD, nb);
+            const auto vrs = uniform_rsrc(vcache + (size_t)k0 * HD, nb);
+#pragma unroll
+            for (int blk = 0; blk < 2; ++blk)
+#pragma unroll
+                for (int k = 0; k < NK; ++k)
+                    kf[buf][blk][k] = __builtin_bit_cast(
+                        u32x4_t, __builtin_amdgcn_raw_buffer_load_b128(krs, koff + 16 * blk * HD * 2 + 64 * k, 0, kNT));
+#pragma unroll
+            for (int i = 0; i < NV; ++i)
+                vf[buf][i] = __builtin_bit_cast(
+                    u32x4_t, __builtin_amdgcn_raw_buffer_load_b128(vrs, voff + RPI * i * HD * 2, 0, kNT));
+            return;
+        }
 #pragma unroll
         for (int blk = 0; blk < 2; ++blk) {
             const int key = row_of(min(k0 + 16 * blk + col, last));

@@ -15,6 +15,20 @@ typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x2_t __attribute__((ext_vector_type(2)));
 
 // 16-byte global/LDS accesses as native vectors (no struct copies).
+// Fourth word of a raw buffer resource on gfx9-family parts (32-bit data
+// format; byte offsets, no swizzle, no index).
+constexpr int kBufferWord3 = 0x00020000;
+// A raw buffer resource over n_bytes from p.  The values must be the same in
+// every lane; the readfirstlanes let the compiler keep the resource in scalar
+// registers (a resource it cannot prove uniform makes it wrap every load in a
+// loop over the lanes' distinct values).
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t uniform_rsrc(const void* p, int n_bytes) {
+    const uint64_t u = reinterpret_cast<uint64_t>(p);
+    const uint32_t lo = __builtin_amdgcn_readfirstlane((uint32_t)u);
+    const uint32_t hi = __builtin_amdgcn_readfirstlane((uint32_t)(u >> 32));
+    return __builtin_amdgcn_make_buffer_rsrc(reinterpret_cast<void*>(((uint64_t)hi << 32) | lo), (short)0,
+                                             __builtin_amdgcn_readfirstlane(n_bytes), kBufferWord3);
+}
 __device__ __forceinline__ u32x4_t ld16(const void* p) { return *reinterpret_cast<const u32x4_t*>(p); }
 __device__ __forceinline__ void st16(void* p, u32x4_t v) { *reinterpret_cast<u32x4_t*>(p) = v; }
 

@@ -44,9 +44,6 @@
 namespace attn {
 
 constexpr int kTK = 64;                 // keys per tile
-// Fourth word of a raw buffer resource on gfx9-family parts (32-bit data
-// format; byte offsets, no swizzle, no index).
-constexpr int kBufferWord3 = 0x00020000;
 // A split partial row: (m, l, e, 0) as floats, then O/l * 2^-e as head_dim
 // halves (see part_scale_exp).
 constexpr int kPartHead = 4;
