@@ -188,8 +188,11 @@ __device__ __forceinline__ void rescale_half_scores(const float* fac, float* lh,
 // only that instance carries the mid-part writes and their rescale, which
 // would otherwise add to the streaming loop's registers.  RING: the cache is
 // a ring of cap rows (key k in row k mod cap) that has wrapped.
+// Two waves per SIMD (at most 256 registers) where the instance fits them
+// without spilling: occupancy is what keeps HBM busy, and left alone the
+// compiler may take a few registers past the limit and halve it.
 template <int HD, int HPL, bool PROBS, bool LONG, bool RING>
-__global__ __launch_bounds__(64) void decode_split_kernel(DecodeArgs a) {
+__global__ __launch_bounds__(64, (HPL == 1 || (HPL == 2 && !LONG) ? 2 : 1)) void decode_split_kernel(DecodeArgs a) {
     constexpr int GQ = 4 * HPL;                 // query heads per group handled
     constexpr int NK = HD / 32;                 // K-steps per 16x16x32 product
     constexpr int CPR = HD / 8;                 // 16-byte chunks per cache row
