@@ -52,16 +52,26 @@ def parse():
     return ap.parse_args()
 
 
-def kernel_source_hash():
-    """Hash of the HIP sources; recorded counter traffic is only reported while
-    the kernels it was taken on are unchanged."""
-    import glob
+def kernel_code_hash():
+    """Hash of the built library's GPU code (its .hip_fatbin section): recorded
+    counter traffic is only reported while the kernels it was taken on are
+    unchanged.  Edits that leave the machine code alone (comments, host-side
+    code) keep the record."""
     import hashlib
-    h = hashlib.sha256()
-    for f in sorted(glob.glob(os.path.join(ROOT, "chunked_prefill_causal_rope_amd", "csrc", "*"))):
-        h.update(os.path.basename(f).encode())
-        h.update(open(f, "rb").read())
-    return h.hexdigest()[:16]
+    import struct
+    from chunked_prefill_causal_rope_amd import api
+    data = open(api.LIB_PATH, "rb").read()
+    if data[:4] != b"\x7fELF" or data[4] != 2:
+        return None
+    shoff, = struct.unpack_from("<Q", data, 0x28)
+    shentsize, shnum, shstrndx = struct.unpack_from("<HHH", data, 0x3A)
+    secs = [struct.unpack_from("<IIQQQQIIQQ", data, shoff + i * shentsize) for i in range(shnum)]
+    names = secs[shstrndx][4]
+    for sec in secs:
+        name = data[names + sec[0]: data.index(b"\0", names + sec[0])]
+        if name == b".hip_fatbin":
+            return hashlib.sha256(data[sec[4]: sec[4] + sec[5]]).hexdigest()[:16]
+    return None
 
 
 def recorded_traffic(workload):
@@ -72,7 +82,8 @@ def recorded_traffic(workload):
     if not os.path.exists(path):
         return None
     rec = json.load(open(path))
-    if rec.get("kernel_source_hash") != kernel_source_hash():
+    code = kernel_code_hash()
+    if code is None or rec.get("kernel_code_hash") != code:
         return None
     w = rec.get("workloads", {}).get(workload)
     return None if w is None else w.get("bytes_per_launch")
@@ -152,31 +163,44 @@ def cpu_baseline_prefill(w, d, budget_s):
     flops = 0.0
     rows = 0
     chunks = 0
-    c_end = n
-    kc = vc = None
-    while c_end > 0 and time.perf_counter() - t_start < budget_s:
-        c0 = max(0, c_end - w.chunk)
-        if kc is None:
-            kn = dict(norm, norm_w=d["k_norm_w"].numpy()) if w.norm_style else {}
-            k = oracle.finish_heads(d["k"][:c_end].float().numpy(), np.arange(c_end), f, w.rd,
-                                    w.rope_scale, store=store, **kn)
-            kc = np.ascontiguousarray(k.transpose(1, 0, 2))
-            vc = np.ascontiguousarray(d["v"][:c_end].float().numpy().astype(np.float64)
-                                      .transpose(1, 0, 2))
-        qn = dict(norm, norm_w=d["q_norm_w"].numpy()) if w.norm_style else {}
-        pos = np.arange(c0, c_end)
-        q = oracle.finish_heads(d["q"][c0:c_end].float().numpy(), pos, f, w.rd, w.rope_scale,
-                                store=store, **qn)
-        oracle.attend(q, kc, vc, pos, w.scale, n_threads=threads, window=w.window)
-        keys = np.minimum(pos + 1, w.window) if w.window > 0 else pos + 1
-        flops += 4.0 * w.head_dim * w.n_heads * float(np.sum(keys))
-        rows += c_end - c0
-        chunks += 1
-        c_end = c0
+    passes = 0
+    # walk back from the prompt's end; a prompt shorter than the budget is
+    # walked again from scratch (RoPE of the keys included) until it is spent
+    while time.perf_counter() - t_start < budget_s:
+        passes += 1
+        c_end = n
+        kc = vc = None
+        while c_end > 0 and time.perf_counter() - t_start < budget_s:
+            c0 = max(0, c_end - w.chunk)
+            if kc is None:
+                kn = dict(norm, norm_w=d["k_norm_w"].numpy()) if w.norm_style else {}
+                k = oracle.finish_heads(d["k"][:c_end].float().numpy(), np.arange(c_end), f, w.rd,
+                                        w.rope_scale, store=store, **kn)
+                kc = np.ascontiguousarray(k.transpose(1, 0, 2))
+                vc = np.ascontiguousarray(d["v"][:c_end].float().numpy().astype(np.float64)
+                                          .transpose(1, 0, 2))
+            qn = dict(norm, norm_w=d["q_norm_w"].numpy()) if w.norm_style else {}
+            pos = np.arange(c0, c_end)
+            q = oracle.finish_heads(d["q"][c0:c_end].float().numpy(), pos, f, w.rd, w.rope_scale,
+                                    store=store, **qn)
+            oracle.attend(q, kc, vc, pos, w.scale, n_threads=threads, window=w.window)
+            keys = np.minimum(pos + 1, w.window) if w.window > 0 else pos + 1
+            flops += 4.0 * w.head_dim * w.n_heads * float(np.sum(keys))
+            rows += c_end - c0
+            chunks += 1
+            c_end = c0
     dt = time.perf_counter() - t_start
     return {"value": flops / dt / 1e12, "unit": "TFLOP/s", "cores": threads, "kind": "oracle",
-            "sample": f"last {chunks} chunk(s) ({rows} positions x {w.n_heads} heads) of prompt 0, "
-                      f"f64 oracle incl. K/Q RoPE, {dt:.1f} s"}
+            "sample": _prefill_sample(chunks, rows, n, w) + f", f64 oracle incl. K/Q RoPE, {dt:.1f} s"}
+
+
+def _prefill_sample(chunks, rows, n, w):
+    n_ch = -(-n // w.chunk)
+    if chunks < n_ch:
+        return f"last {chunks} chunk(s) ({rows} positions x {w.n_heads} heads) of prompt 0"
+    whole, rest = divmod(chunks, n_ch)
+    return (f"{whole} whole pass(es) over prompt 0 ({n} positions x {w.n_heads} heads, {n_ch} chunks)"
+            + (f" and its last {rest} chunk(s) once more" if rest else ""))
 
 
 def cpu_baseline_decode(w, d, budget_s):
@@ -329,7 +353,7 @@ def main():
         torch.cuda.synchronize()
         y.copy_(x)
         torch.cuda.synchronize()
-        print(json.dumps({"copy_bytes": 4 * n, "kernel_source_hash": kernel_source_hash()}))
+        print(json.dumps({"copy_bytes": 4 * n, "kernel_code_hash": kernel_code_hash()}))
         return
     stream = torch.cuda.Stream()
     w = wl.CONFIGS[args.workload]

@@ -441,8 +441,9 @@ __global__ __launch_bounds__(64, (HPL == 1 || (HPL == 2 && !LONG) ? 2 : 1)) void
     };
 
     // two register sets: the loads of step i+1 are issued before step i
-    // runs.  They are unconditional (a prefetch past the part's end re-reads
-    // its last row) so the compiler's wait counts stay exact.
+    // runs.  They are unconditional (a prefetch past the part's end reads
+    // zeros, or its last row over a ring) so the compiler's wait counts stay
+    // exact.
     // Steps go in pairs; an odd count ends with a step whose keys are all
     // past the part (scores -inf, probabilities 0, nothing stored).
     load(k_lo, 0);
