@@ -223,3 +223,19 @@ def test_importance_validation():
     assert importance(n_seq=-1) == EINVAL
     assert importance(n_seq=0) == OK
     assert importance(max_ctx=0) == OK
+
+
+def test_recorded_traffic_keyed_to_the_built_code():
+    """bench.py reports counter traffic only for the GPU code it was taken on:
+    the key is a hash of the built library's .hip_fatbin section, and a record
+    under another key reads as absent."""
+    import json
+    import bench
+    code = bench.kernel_code_hash()
+    assert code is not None and re.fullmatch(r"[0-9a-f]{16}", code)
+    assert bench.kernel_code_hash() == code          # deterministic
+    rec = json.load(open(os.path.join(os.path.dirname(os.path.dirname(__file__)), "profiles", "traffic.json")))
+    for name, w in rec["workloads"].items():
+        want = w["bytes_per_launch"] if rec.get("kernel_code_hash") == code else None
+        assert bench.recorded_traffic(name) == want
+    assert bench.recorded_traffic("no_such_workload") is None
