@@ -665,46 +665,47 @@ __global__ __launch_bounds__(256) void decode_combine_kernel(DecodeArgs a) {
 // probs[b][h][j], j < ctx[b] ([ATT] the per-head loop of the decode attention
 // adds every head's probability row into one vector, so a position's
 // importance is the total probability the heads give it).  Heads are summed in
-// order, in float, each thread over 4 consecutive positions; the
-// probabilities are read once (16-byte loads, every head's row in flight).
+// order, in float, each thread over 2 consecutive positions (more threads
+// keep more of the rows' reads in flight than wider loads per thread); the
+// probabilities are read once.
 __global__ __launch_bounds__(256) void decode_importance_kernel(ImportanceArgs a) {
     const int b = blockIdx.y;
     if (b >= a.n_seq) return;
     const int ctx = min(min(a.ctx[b], a.max_ctx), a.probs_ld);
-    const int j = (blockIdx.x * 256 + threadIdx.x) * 4;
+    const int j = (blockIdx.x * 256 + threadIdx.x) * 2;
     if (j >= ctx) return;
     const float* pb = a.probs + (size_t)b * a.n_heads * a.probs_ld + j;
     float* dst = a.imp + (size_t)b * a.imp_ld + j;
-    const int n = min(4, ctx - j);
-    float s[4] = {0.f, 0.f, 0.f, 0.f};
-    if (n == 4) {
-        // eight heads' loads in flight at a time, added in head order
-        constexpr int U = 8;
+    const int n = min(2, ctx - j);
+    float s[2] = {0.f, 0.f};
+    if (n == 2) {
+        // sixteen heads' loads in flight at a time, added in head order
+        constexpr int U = 16;
         int h = 0;
         for (; h + U <= a.n_heads; h += U) {
-            f32x4_a4_t v[U];
+            float v[U][2];
 #pragma unroll
-            for (int u = 0; u < U; ++u) v[u] = *reinterpret_cast<const f32x4_a4_t*>(pb + (size_t)(h + u) * a.probs_ld);
+            for (int u = 0; u < U; ++u) {
+                v[u][0] = pb[(size_t)(h + u) * a.probs_ld];
+                v[u][1] = pb[(size_t)(h + u) * a.probs_ld + 1];
+            }
 #pragma unroll
-            for (int u = 0; u < U; ++u)
-#pragma unroll
-                for (int e = 0; e < 4; ++e) s[e] += v[u][e];
+            for (int u = 0; u < U; ++u) {
+                s[0] += v[u][0];
+                s[1] += v[u][1];
+            }
         }
-        for (; h < a.n_heads; ++h) {
-            const f32x4_a4_t v = *reinterpret_cast<const f32x4_a4_t*>(pb + (size_t)h * a.probs_ld);
-#pragma unroll
-            for (int e = 0; e < 4; ++e) s[e] += v[e];
-        }
+        for (; h < a.n_heads; ++h)
+            for (int e = 0; e < 2; ++e) s[e] += pb[(size_t)h * a.probs_ld + e];
     } else {
-        for (int h = 0; h < a.n_heads; ++h)
-            for (int e = 0; e < n; ++e) s[e] += pb[(size_t)h * a.probs_ld + e];
+        for (int h = 0; h < a.n_heads; ++h) s[0] += pb[(size_t)h * a.probs_ld];
     }
     for (int e = 0; e < n; ++e) dst[e] = a.accumulate ? dst[e] + s[e] : s[e];
 }
 
 hipError_t launch_decode_importance(const ImportanceArgs& a, hipStream_t stream) {
     if (a.n_seq <= 0 || a.max_ctx <= 0) return hipSuccess;
-    const dim3 grid((unsigned)((a.max_ctx + 1023) / 1024), (unsigned)a.n_seq);
+    const dim3 grid((unsigned)((a.max_ctx + 511) / 512), (unsigned)a.n_seq);
     decode_importance_kernel<<<grid, dim3(256), 0, stream>>>(a);
     return hipGetLastError();
 }
