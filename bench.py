@@ -10,13 +10,18 @@ Inputs are resident in HBM before timing starts.  The timed steps replay a
 HIP graph of one step (the chunk loop is launch-bound at small chunks); the
 graph was checked against eager execution by the test suite.
 
-Prints ONE JSON line.  `value` is the whole-step throughput (algorithmic
-FLOP/s for prefill, K/V bytes read per second for decode); `roofline` is the
-attention call measured per launch with HIP events on its stream;
-`cpu_baseline` is the CPU oracle timed on a bounded sample of the same
-workload on this host.  The decode line also carries `importance`: the
-per-position importance call (sum over heads of the step's probabilities),
-timed per launch after the step, outside it.
+Prints ONE JSON line.  The headline workload is the 128K-token YaRN
+prefill (64 query / 8 KV heads, chunks of 2048), the largest configuration;
+the line also carries the smaller prefill workloads (`prefill_small`) and the
+decode batch (`decode`) as sub-objects.  `value` is the whole-step
+throughput (algorithmic FLOP/s for prefill, K/V bytes read per second for
+decode); `roofline` is the attention call measured per launch with HIP events
+on its stream, against the published peak and against the peak measured on
+the same GPU in the same run (`calibration`: a matrix-core loop and a
+streaming read); `cpu_baseline` is the CPU oracle timed on a bounded sample
+of the same workload on this host.  The decode line also carries
+`importance`: the per-position importance call (sum over heads of the step's
+probabilities), timed per launch after the step, outside it.
 """
 from __future__ import annotations
 
@@ -42,8 +47,11 @@ def parse():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=10)
     ap.add_argument("--warmup", type=int, default=3)
-    ap.add_argument("--workload", default="c1_llama_prefill")
+    ap.add_argument("--workload", default="c4_yarn_128k")
     ap.add_argument("--no-decode", action="store_true", help="skip the secondary decode line")
+    ap.add_argument("--no-extra", action="store_true",
+                    help="skip the smaller prefill sub-lines (c1, c3)")
+    ap.add_argument("--no-calib", action="store_true", help="skip the measured-peak calibration")
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
     ap.add_argument("--eager", action="store_true", help="time eager launches, not a graph")
@@ -146,6 +154,127 @@ def time_steps(torch, step_fn, steps, warmup, eager, stream):
 
 # ------------------------------------------------------------------ CPU baseline
 
+def _cores(threads):
+    """The oracle's thread count next to the host's core counts.  The oracle
+    runs at most 16 threads: on a one-GPU machine that is the process's CPU share,
+    whatever the host reports."""
+    try:
+        affinity = len(os.sched_getaffinity(0))
+    except (AttributeError, OSError):
+        affinity = None
+    return {"cores": threads, "threads": threads, "host_cores": os.cpu_count(),
+            "affinity_cores": affinity}
+
+
+def sample_rows(w, lengths, n_fixed_rows=512, seed=None):
+    """The seeded (sequence, position, head) sample of a large prefill
+    workload: for prompt 0, position 0, the first and last rows of 8 chunks
+    spread over the prompt and the final row, each with the first, the last
+    and two random heads; the rest random rows of any prompt (position
+    uniform in the prompt, head uniform)."""
+    import numpy as np
+    rng = np.random.default_rng(w.seed if seed is None else seed)
+    n0 = lengths[0]
+    n_ch = -(-n0 // w.chunk)
+    fixed_pos = {0, n0 - 1}
+    for c in np.linspace(0, n_ch - 1, 8).round().astype(int):
+        fixed_pos.add(int(c) * w.chunk)
+        fixed_pos.add(min(n0, (int(c) + 1) * w.chunk) - 1)
+    rows = []
+    for p in sorted(fixed_pos):
+        for h in (0, w.n_heads - 1, int(rng.integers(w.n_heads)), int(rng.integers(w.n_heads))):
+            rows.append((0, p, h))
+    rows = list(dict.fromkeys(rows))
+    while len(rows) < n_fixed_rows:
+        b = int(rng.integers(len(lengths)))
+        rows.append((b, int(rng.integers(lengths[b])), int(rng.integers(w.n_heads))))
+    return rows, rng
+
+
+def cpu_baseline_prefill_sampled(w, d, budget_s):
+    """The oracle, as it stands, on a seeded sample of (sequence, position,
+    head) rows of a workload too large to run whole on the CPU: 512 rows
+    (sample_rows), then further random rows while the time budget lasts.
+    The keys each sampled sequence needs are finished (norm, RoPE, rounding)
+    by the oracle first; that time is included.  Reports the algorithmic FLOP
+    rate of the sample and the full workload's time extrapolated from it."""
+    import numpy as np
+
+    import oracle
+    from chunked_prefill_causal_rope_amd import workloads as wl
+    f = (oracle.yarn_inv_freq(w.rd, w.base, *w.yarn) if w.yarn is not None
+         else oracle.rope_inv_freq(w.rd, w.base))
+    store = oracle.STORE_BF16 if w.dtype == "bf16" else oracle.STORE_F32
+    lengths, cu = d["lengths"], d["cu_seq"]
+    threads = oracle.default_threads()
+    G = w.n_heads // w.n_kv
+    rows, rng = sample_rows(w, lengths)
+    t_start = time.perf_counter()
+    caches = {}
+
+    def cache_of(b):
+        if b not in caches:
+            n = lengths[b]
+            kn = dict(norm_style=w.norm_style, eps=w.norm_eps,
+                      norm_w=d["k_norm_w"].numpy()) if w.norm_style else {}
+            k = oracle.finish_heads(d["k"][cu[b]:cu[b] + n].float().numpy(), np.arange(n), f, w.rd,
+                                    w.rope_scale, store=store, **kn)
+            caches[b] = (np.ascontiguousarray(k.transpose(1, 0, 2)),
+                         np.ascontiguousarray(d["v"][cu[b]:cu[b] + n].float().numpy()
+                                              .astype(np.float64).transpose(1, 0, 2)))
+        return caches[b]
+
+    t_prep = 0.0
+    flops = 0.0
+    done = 0
+    batch = 64
+    i = 0
+    while True:
+        if i >= len(rows):
+            if time.perf_counter() - t_start >= budget_s:
+                break
+            for _ in range(batch):
+                b = int(rng.integers(len(lengths)))
+                rows.append((b, int(rng.integers(lengths[b])), int(rng.integers(w.n_heads))))
+        chunk_rows = rows[i:i + batch]
+        i += len(chunk_rows)
+        tp = time.perf_counter()
+        for b, _, _ in chunk_rows:
+            cache_of(b)
+        t_prep += time.perf_counter() - tp
+        qn = dict(norm_style=w.norm_style, eps=w.norm_eps,
+                  norm_w=d["q_norm_w"].numpy()) if w.norm_style else {}
+        # rows of one (sequence, KV head) go to the oracle together, each as
+        # a one-head query row at its own position (threads over rows)
+        groups = {}
+        for b, p, h in chunk_rows:
+            groups.setdefault((b, h // G), []).append((p, h))
+        for (b, g), items in groups.items():
+            kc, vc = caches[b]
+            pos = np.array([p for p, _ in items])
+            qraw = np.stack([d["q"][cu[b] + p, h:h + 1].float().numpy() for p, h in items])
+            q = oracle.finish_heads(qraw, pos, f, w.rd, w.rope_scale, store=store, **qn)
+            oracle.attend(q, kc[g:g + 1], vc[g:g + 1], pos, w.scale, n_threads=threads,
+                          window=w.window)
+            for p in pos:
+                keys = min(p + 1, w.window) if w.window > 0 else p + 1
+                flops += 4.0 * w.head_dim * float(keys)
+                done += 1
+        if done >= 512 and time.perf_counter() - t_start >= budget_s:
+            break
+    dt = time.perf_counter() - t_start
+    total = wl.prefill_flops(w, lengths)
+    t_attend = dt - t_prep
+    return {"value": flops / dt / 1e12, "unit": "TFLOP/s", **_cores(threads), "kind": "oracle",
+            "sample": f"{done} seeded (sequence, position, head) rows of {w.name} (position 0, first "
+                      f"and last rows of 8 chunks and the final row of prompt 0, then random rows); "
+                      f"f64 oracle incl. the RoPE of the keys they read ({t_prep:.1f} s) and of "
+                      f"their queries; {dt:.1f} s",
+            "sample_flop": flops,
+            "extrapolated_full_s": round(t_prep + t_attend * total / max(flops, 1.0), 1),
+            "extrapolated": True}
+
+
 def cpu_baseline_prefill(w, d, budget_s):
     """The oracle, as it stands, on the last chunks of the first prompt (the
     costliest rows), walking backwards until about budget_s seconds of CPU
@@ -190,7 +319,7 @@ def cpu_baseline_prefill(w, d, budget_s):
             chunks += 1
             c_end = c0
     dt = time.perf_counter() - t_start
-    return {"value": flops / dt / 1e12, "unit": "TFLOP/s", "cores": threads, "kind": "oracle",
+    return {"value": flops / dt / 1e12, "unit": "TFLOP/s", **_cores(threads), "kind": "oracle",
             "sample": _prefill_sample(chunks, rows, n, w) + f", f64 oracle incl. K/Q RoPE, {dt:.1f} s"}
 
 
@@ -227,9 +356,59 @@ def cpu_baseline_decode(w, d, budget_s):
         nbytes += 2.0 * (min(c, w.window) if w.window > 0 else c) * w.n_kv * w.head_dim * 2
         seqs += 1
     dt = time.perf_counter() - t_start
-    return {"value": nbytes / dt / 1e9, "unit": "GB/s", "cores": threads, "kind": "oracle",
+    return {"value": nbytes / dt / 1e9, "unit": "GB/s", **_cores(threads), "kind": "oracle",
             "sample": f"{seqs} of {len(d['ctx'])} sequences (all heads, with probabilities), "
                       f"f64 oracle, {dt:.1f} s"}
+
+
+# ------------------------------------------------------------------ measured peaks
+
+def calibrate(torch, stream):
+    """Measured peaks of this GPU in this run: a loop of bf16 32x32x16 matrix
+    products (two workgroups of 4 waves per CU, four independent accumulators
+    per wave) and a streaming read of 2 GiB with 16-byte nontemporal loads;
+    the best of 5 launches each, timed with events on `stream`."""
+    from chunked_prefill_causal_rope_amd import api
+    cus = torch.cuda.get_device_properties(0).multi_processor_count
+    nwg = 2 * cus
+    out = torch.empty(nwg * 4, dtype=torch.float32, device="cuda")
+    iters = 16384
+    flop = [0.0]
+
+    def mf():
+        flop[0] = api.calibrate_mfma(nwg, iters, out)
+    with torch.cuda.stream(stream):
+        mf()
+    ms = min(time_launches(torch, [mf] * 5, stream))
+    mfma_tflops = flop[0] / (ms * 1e-3) / 1e12
+    src = torch.empty(1 << 29, dtype=torch.int32, device="cuda")     # 2 GiB, contents irrelevant
+    nwr = 8 * cus
+    rout = torch.empty(nwr * 4, dtype=torch.int32, device="cuda")
+    nbytes = [0]
+
+    def rd():
+        nbytes[0] = api.calibrate_read(src, nwr, rout)
+    with torch.cuda.stream(stream):
+        rd()
+    ms_r = min(time_launches(torch, [rd] * 5, stream))
+    read_gbs = nbytes[0] / (ms_r * 1e-3) / 1e9
+    del src
+    torch.cuda.synchronize()
+    return {"mfma_bf16_tflops": round(mfma_tflops, 1), "mfma_kernel": "attn_calibrate_mfma",
+            "mfma_ms": round(ms, 4), "hbm_read_gbs": round(read_gbs, 1),
+            "read_kernel": "attn_calibrate_read", "read_bytes": nbytes[0], "read_ms": round(ms_r, 4),
+            "compute_units": cus}
+
+
+def with_measured_peak(roof, calib):
+    """Add the fraction of the peak measured in this run to a roofline."""
+    if calib is None:
+        return roof
+    peak = calib["mfma_bf16_tflops"] if roof["bound"] == "mfma" else calib["hbm_read_gbs"]
+    roof = dict(roof)
+    roof["measured_peak"] = peak
+    roof["frac_measured"] = round(roof["achieved"] / peak, 4)
+    return roof
 
 
 # ------------------------------------------------------------------ workloads
@@ -356,6 +535,7 @@ def main():
         print(json.dumps({"copy_bytes": 4 * n, "kernel_code_hash": kernel_code_hash()}))
         return
     stream = torch.cuda.Stream()
+    calib = None if args.no_calib else calibrate(torch, stream)
     w = wl.CONFIGS[args.workload]
     if w.decode:
         res, d = bench_decode(torch, w, args, stream)
@@ -363,20 +543,43 @@ def main():
                "steps": args.steps, "warmup": args.warmup, "ms_per_step": res["ms_per_step"],
                "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "bf16",
                "data": "synthetic", "config": dict(res["config"], workload=w.name),
-               "roofline": res["roofline"], **({"importance": res["importance"]} if "importance" in res else {})}
+               "roofline": with_measured_peak(res["roofline"], calib),
+               **({"importance": res["importance"]} if "importance" in res else {})}
         # the decode baseline covers one new token over a full-length cache
         if not args.no_cpu and w.new_tokens == 1 and not w.ring:
             res["cpu_baseline"] = cpu_baseline_decode(w, d, args.cpu_seconds)
     else:
         res, d = bench_prefill(torch, w, args, stream)
+        res["roofline"] = with_measured_peak(res["roofline"], calib)
         if not args.no_cpu:
+            from chunked_prefill_causal_rope_amd import workloads as wl_
             dc = {k: (v.cpu() if hasattr(v, "cpu") else v) for k, v in d.items()}
-            res["cpu_baseline"] = cpu_baseline_prefill(w, dc, args.cpu_seconds)
-        del d
+            del d
+            # whole chunks of the oracle for the small workloads; a row sample
+            # (time extrapolated) where the oracle would take hours
+            big = wl_.prefill_flops(w, dc["lengths"]) > 5e11
+            res["cpu_baseline"] = (cpu_baseline_prefill_sampled(w, dc, args.cpu_seconds) if big
+                                   else cpu_baseline_prefill(w, dc, args.cpu_seconds))
+            del dc
+        else:
+            del d
+        if not args.no_extra and args.workload == "c4_yarn_128k":
+            subs = {}
+            for name in ("c1_llama_prefill", "c3_qwen_varlen"):
+                torch.cuda.empty_cache()
+                sub, dd = bench_prefill(torch, wl.CONFIGS[name], args, stream)
+                del dd
+                subs[name] = {"value": sub["value"], "unit": sub["unit"],
+                              "ms_per_step": sub["ms_per_step"], "config": sub["config"],
+                              "roofline": with_measured_peak(sub["roofline"], calib)}
+            res["prefill_small"] = subs
         if not args.no_decode:
             torch.cuda.empty_cache()
             dec, _ = bench_decode(torch, wl.CONFIGS["c2_decode"], args, stream)
+            dec["roofline"] = with_measured_peak(dec["roofline"], calib)
             res["decode"] = dec
+    if calib is not None:
+        res["calibration"] = calib
     print(json.dumps(res), flush=True)
 
 

@@ -24,8 +24,8 @@ _lib = None
 
 EXPORTS = ("attn_rope_inv_freq", "attn_yarn_inv_freq", "attn_rope_apply", "attn_kv_append",
            "attn_rope_qkv", "attn_prefill_chunk", "attn_prefill_workspace_bytes", "attn_decode",
-           "attn_decode_workspace_bytes", "attn_decode_importance", "attn_status_string",
-           "attn_version")
+           "attn_decode_workspace_bytes", "attn_decode_importance", "attn_calibrate_mfma",
+           "attn_calibrate_read", "attn_status_string", "attn_version")
 
 
 class AttnError(RuntimeError):
@@ -61,6 +61,10 @@ def lib() -> ctypes.CDLL:
     L.attn_decode_importance.argtypes = [vp, i, i, i, vp, i, vp, i, i, vp]
     L.attn_decode_importance.restype = i
     L.attn_decode_workspace_bytes.restype = sz
+    L.attn_calibrate_mfma.argtypes = [i, i, vp, vp]
+    L.attn_calibrate_mfma.restype = i
+    L.attn_calibrate_read.argtypes = [vp, sz, i, vp, vp]
+    L.attn_calibrate_read.restype = i
     L.attn_status_string.argtypes = [i]
     L.attn_status_string.restype = ctypes.c_char_p
     L.attn_version.restype = ctypes.c_char_p
@@ -286,3 +290,23 @@ def decode(q: torch.Tensor, k_cache: torch.Tensor, v_cache: torch.Tensor, ctx: t
         *_gate(gate, gate_mode, n_seq, nh, hd, q.dtype), _dev(out, "out"),
         _dev(probs, "probs"), ld, ws, wsb, _stream())
     _check("attn_decode", st)
+
+
+# ---------------------------------------------------------------- calibration
+
+def calibrate_mfma(n_workgroups: int, iters: int, out: torch.Tensor) -> float:
+    """Launch the matrix-core loop on the current stream; returns its FLOP
+    count (n_workgroups * 4 waves * iters * 4 products * 32768)."""
+    assert out.dtype == torch.float32 and out.numel() >= n_workgroups * 4
+    _check("attn_calibrate_mfma", lib().attn_calibrate_mfma(n_workgroups, iters, _dev(out, "out"),
+                                                             _stream()))
+    return float(n_workgroups) * 4 * iters * 4 * 32768
+
+
+def calibrate_read(src: torch.Tensor, n_workgroups: int, out: torch.Tensor) -> int:
+    """Launch the streaming read of src on the current stream; returns its bytes."""
+    nbytes = src.numel() * src.element_size() // 16 * 16
+    assert out.dtype == torch.int32 and out.numel() >= n_workgroups * 4
+    _check("attn_calibrate_read", lib().attn_calibrate_read(_dev(src, "src"), nbytes, n_workgroups,
+                                                             _dev(out, "out"), _stream()))
+    return nbytes

@@ -165,6 +165,9 @@ int attn_kv_append(void* k_cache, void* v_cache, int dtype, int n_seq, int n_kv,
     if (cap <= 0 || max_end < 0 || (ring != 0 && ring != 1) || (v_norm != 0 && v_norm != 1))
         return ATTN_EINVAL;
     if (!ring && max_end > cap) return ATTN_ECAPACITY;
+    // a wrapped ring gives two positions of one chunk, p and p + cap, the
+    // same row when the chunk is longer than the ring
+    if (ring && max_end > cap && max_chunk > cap) return ATTN_ECAPACITY;
     if (n_seq == 0 || n_tok == 0 || max_chunk == 0) return ATTN_OK;
     if (!k_cache || !v_cache || !k_new || !v_new) return ATTN_EINVAL;
     attn::RopeArgs a{};
@@ -206,6 +209,7 @@ int attn_rope_qkv(const void* q, void* q_out, int n_heads, void* k_cache, void* 
     if (cap <= 0 || max_end < 0 || (ring != 0 && ring != 1) || (v_norm != 0 && v_norm != 1))
         return ATTN_EINVAL;
     if (!ring && max_end > cap) return ATTN_ECAPACITY;
+    if (ring && max_end > cap && max_chunk > cap) return ATTN_ECAPACITY;   // as attn_kv_append
     if (n_seq == 0 || n_tok == 0 || max_chunk == 0) return ATTN_OK;
     if (!q || !q_out || !k_cache || !v_cache || !k_new || !v_new) return ATTN_EINVAL;
     attn::RopeArgs aq{};

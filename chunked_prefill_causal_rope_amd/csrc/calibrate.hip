@@ -1,0 +1,82 @@
+// Measured roofline denominators for this part: a loop of bf16 matrix-core
+// products and a streaming read of device memory.  The attention kernels'
+// throughput is reported against the published peaks and against these
+// measured ones, taken on the same GPU in the same run.
+//
+// Neither kernel computes anything of the method; they exist so the
+// fraction of peak can be stated against what the part actually sustains
+// (clock under load, memory efficiency) as well as against its datasheet.
+#include <hip/hip_runtime.h>
+
+#include "../../include/attn.h"
+#include "device_common.h"
+
+namespace attn {
+
+// Each wave keeps four independent 32x32x16 bf16 accumulators in flight, so
+// the matrix pipe never waits on a result; the operands are fixed, so the
+// loop issues products only.  A lane-dependent sum of the accumulators is
+// written per wave, which keeps the products live.
+__global__ __launch_bounds__(256) void calib_mfma_kernel(int iters, float* out) {
+    const int lane = threadIdx.x & 63;
+    bf16x8_t a, b;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+        a[i] = (__bf16)(0.001f * (float)((lane + i) & 7));
+        b[i] = (__bf16)(0.002f * (float)((lane * 3 + i) & 7));
+    }
+    f32x16_t c0 = {}, c1 = {}, c2 = {}, c3 = {};
+    for (int it = 0; it < iters; ++it) {
+        c0 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c0, 0, 0, 0);
+        c1 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c1, 0, 0, 0);
+        c2 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c2, 0, 0, 0);
+        c3 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c3, 0, 0, 0);
+    }
+    float s = 0.f;
+#pragma unroll
+    for (int q = 0; q < 16; ++q) s += c0[q] + c1[q] + c2[q] + c3[q];
+    s = wave_sum(s);
+    if (lane == 0) out[blockIdx.x * (blockDim.x / 64) + (threadIdx.x >> 6)] = s;
+}
+
+// Grid-stride read of n16 16-byte words with nontemporal loads, four in
+// flight per lane; the words are folded with xor and one value per wave is
+// written.
+__global__ __launch_bounds__(256) void calib_read_kernel(const u32x4_t* src, size_t n16, uint32_t* out) {
+    const size_t stride = (size_t)gridDim.x * blockDim.x;
+    size_t i = (size_t)blockIdx.x * blockDim.x + threadIdx.x;
+    u32x4_t acc = {0u, 0u, 0u, 0u};
+    for (; i + 3 * stride < n16; i += 4 * stride) {
+        const u32x4_t x0 = __builtin_nontemporal_load(src + i);
+        const u32x4_t x1 = __builtin_nontemporal_load(src + i + stride);
+        const u32x4_t x2 = __builtin_nontemporal_load(src + i + 2 * stride);
+        const u32x4_t x3 = __builtin_nontemporal_load(src + i + 3 * stride);
+        acc ^= x0 ^ x1 ^ x2 ^ x3;
+    }
+    for (; i < n16; i += stride) acc ^= __builtin_nontemporal_load(src + i);
+    uint32_t v = acc.x ^ acc.y ^ acc.z ^ acc.w;
+#pragma unroll
+    for (int o = 32; o > 0; o >>= 1) v ^= __shfl_xor(v, o);
+    if ((threadIdx.x & 63) == 0) out[blockIdx.x * (blockDim.x / 64) + (threadIdx.x >> 6)] = v;
+}
+
+}  // namespace attn
+
+extern "C" {
+
+int attn_calibrate_mfma(int n_workgroups, int iters, float* out, void* stream) {
+    if (n_workgroups <= 0 || iters <= 0 || !out) return ATTN_EINVAL;
+    attn::calib_mfma_kernel<<<dim3((unsigned)n_workgroups), dim3(256), 0, (hipStream_t)stream>>>(iters, out);
+    return hipGetLastError() == hipSuccess ? ATTN_OK : ATTN_EDEVICE;
+}
+
+int attn_calibrate_read(const void* src, size_t bytes, int n_workgroups, uint32_t* out, void* stream) {
+    if (!src || !out || n_workgroups <= 0 || bytes < 16 || (bytes & 15) ||
+        (reinterpret_cast<uintptr_t>(src) & 15))
+        return ATTN_EINVAL;
+    attn::calib_read_kernel<<<dim3((unsigned)n_workgroups), dim3(256), 0, (hipStream_t)stream>>>(
+        static_cast<const attn::u32x4_t*>(src), bytes / 16, out);
+    return hipGetLastError() == hipSuccess ? ATTN_OK : ATTN_EDEVICE;
+}
+
+}  // extern "C"

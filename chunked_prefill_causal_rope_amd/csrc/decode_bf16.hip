@@ -3,9 +3,9 @@
 // per KV group, shared by the group's G query heads.
 //
 // cortiq-engine 0.5.39 src/attention.rs: fn attention_head (scores, max-
-// subtracted softmax, output and probabilities; "cost grows linearly with the
-// stored context"), fn attend_all_heads (a KV group's K/V is streamed once for
-// all of its query heads).
+// subtracted softmax, output and probabilities; the work of one decode step is
+// proportional to the number of cached positions), fn attend_all_heads (a KV
+// group's K/V is streamed once for all of its query heads).
 //
 // Design (gfx950):
 //  * The context of each (sequence, KV group) is split into parts of

@@ -165,8 +165,10 @@ int attn_rope_apply(const void *x, void *y, int dtype, int n_tok, int n_heads, i
  *   v_norm           1: each V row is scale-less RMS-normalised first,
  *                    v / sqrt(mean(v^2) + eps), in double and rounded once
  *                    ([ATT] fn vnorm_head, Gemma-4); 0: copied bit for bit
- * Errors: ECAPACITY if max_end > cap without a ring; EINVAL (ring or v_norm
- * not 0/1); otherwise as attn_rope_apply.
+ * Errors: ECAPACITY if max_end > cap without a ring, or with a ring that has
+ * wrapped (max_end > cap) and max_chunk > cap (two positions of one chunk
+ * would share a row); EINVAL (ring or v_norm not 0/1); otherwise as
+ * attn_rope_apply.
  */
 int attn_kv_append(void *k_cache, void *v_cache, int dtype, int n_seq, int n_kv, int head_dim,
                    int cap, int ring, const void *k_new, const void *v_new, int n_tok,
@@ -184,7 +186,7 @@ int attn_kv_append(void *k_cache, void *v_cache, int dtype, int n_seq, int n_kv,
  *   q, q_out  device [n_tok][n_heads][head_dim] (q_out == q is allowed)
  *   k_cache, v_cache, k_new, v_new, n_kv, cap, ring, v_norm   as attn_kv_append
  *   q_norm_w, k_norm_w   the two norm weights (NULL iff norm is NONE)
- * Errors: the union of the two calls' errors.
+ * Errors: the union of the two calls' errors (ECAPACITY as attn_kv_append).
  */
 int attn_rope_qkv(const void *q, void *q_out, int n_heads, void *k_cache, void *v_cache,
                   const void *k_new, const void *v_new, int n_kv, int cap, int ring, int dtype,
@@ -234,9 +236,12 @@ int attn_prefill_chunk(const void *q, const void *k_cache, const void *v_cache, 
                        float *out, void *workspace, size_t workspace_bytes, void *stream);
 
 /*
- * Workspace that lets attn_prefill_chunk split the key range as far as it
- * chooses for these sizes (bytes; 0 when it would not split).  Enough for any
- * window.
+ * Workspace, in bytes, that lets attn_prefill_chunk split the key range as far
+ * as it chooses for these sizes (the split is this library's own scheduling,
+ * not a step of the pages: [ATT] fn attention_head's max-subtracted softmax is
+ * what lets parts of the key range be merged exactly).  0 when the call would
+ * not split, or for invalid sizes (non-positive sizes, n_heads % n_kv != 0,
+ * head_dim not 64/128).  Enough for any window.  Host only; no device call.
  */
 size_t attn_prefill_workspace_bytes(int n_seq, int n_heads, int n_kv, int head_dim, int n_tok,
                                     int max_chunk, int max_end);
@@ -287,6 +292,17 @@ int attn_decode(const void *q, const void *k_cache, const void *v_cache, int dty
                 int gate_ld, float *out, float *probs, int probs_ld,
                 void *workspace, size_t workspace_bytes, void *stream);
 
+/*
+ * Workspace, in bytes, for attn_decode to split every row's key range as far
+ * as it chooses (parts of up to 1024 keys, fewer keys per part for groups of
+ * more than 4 query heads per KV head): per (sequence, head, part) a 16-byte
+ * header (running maximum, row sum, sum of the rounded probabilities, scale
+ * exponent) and head_dim half-precision values.  Arguments as attn_decode;
+ * max_ctx bounds every ctx[b].  Returns 0 for invalid sizes (non-positive
+ * sizes, n_heads % n_kv != 0, head_dim not 64/128).  Host only; no device
+ * call.  A smaller workspace is accepted (fewer, longer parts) down to the
+ * one-part minimum attn_decode documents.
+ */
 size_t attn_decode_workspace_bytes(int n_seq, int n_heads, int n_kv, int head_dim, int max_ctx);
 
 /*
@@ -309,6 +325,25 @@ size_t attn_decode_workspace_bytes(int n_seq, int n_heads, int n_kv, int head_di
 int attn_decode_importance(const float *probs, int n_seq, int n_heads, int probs_ld,
                            const int32_t *ctx, int max_ctx, float *imp, int imp_ld,
                            int accumulate, void *stream);
+
+/*
+ * Measured roofline denominators (not a step of the pages: the throughput of
+ * the attention calls is stated as a fraction of the part's peaks, and these
+ * two kernels measure what the part sustains next to the published figures).
+ *
+ * attn_calibrate_mfma: n_workgroups workgroups of 4 waves, each wave issuing
+ *   iters rounds of four independent 32x32x16 bf16 matrix products
+ *   (32768 FLOP each); total work n_workgroups * 4 * iters * 4 * 32768 FLOP.
+ *   out: device float[n_workgroups * 4], one value per wave, written.
+ * attn_calibrate_read: a streaming read of `bytes` (a multiple of 16, src
+ *   16-byte aligned) with nontemporal 16-byte loads by n_workgroups
+ *   workgroups of 256 threads.  out: device uint32[n_workgroups * 4], one
+ *   value per wave, written.
+ * The caller times the launch on `stream` (e.g. with events).  Errors: EINVAL
+ * for non-positive sizes, NULL pointers, misaligned reads; EDEVICE.
+ */
+int attn_calibrate_mfma(int n_workgroups, int iters, float *out, void *stream);
+int attn_calibrate_read(const void *src, size_t bytes, int n_workgroups, uint32_t *out, void *stream);
 
 /* Static, human-readable name of a status code. */
 const char *attn_status_string(int status);

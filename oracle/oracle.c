@@ -43,55 +43,47 @@ void orc_rope_inv_freq(int rd, double base, float *out)
 }
 
 /*
- * [ATT] fn yarn_inv_freq (Hugging Face style YaRN).  Steps, in the page's order:
- *   correction_dim(r) = d * ln(L0 / (2*pi*r)) / (2 ln base)
- *   low  = max(floor(correction_dim(beta_fast)), 0)
- *   high = clamp(ceil(correction_dim(beta_slow)), 0, d/2 - 1)
- *   denom = max(high - low, 1)          (high - low saturates at 0)
- *   ramp_i = clamp(sat(i - low) / denom, 0, 1)
- *   f'_i = (f_i / factor) * ramp_i + f_i * (1 - ramp_i)
- * d is the rotary dimension.  Reading: double throughout, one final rounding
- * to float; the page's saturating subtractions are followed exactly.
- * Returns the (low, high) pair through *lo_out / *hi_out when non-NULL.
+ * YaRN "by parts" frequency table, Hugging Face flavour ([ATT] fn
+ * yarn_inv_freq; the rotary dimension d plays the role of the head width).
+ *
+ * A rotated pair i turns L0 * f_i / (2 pi) times over the original context L0.
+ * The pair whose count equals r sits at the fractional index
+ *     c(r) = d * ln(L0 / (2 pi r)) / (2 ln base).
+ * Pairs that turn at least beta_fast times (index <= c(beta_fast)) keep their
+ * frequency; pairs that turn fewer than beta_slow times are interpolated, i.e.
+ * divided by the scaling factor s; between the two bounds a linear ramp
+ *     gamma_i = clamp((i - lo) / max(hi - lo, 1), 0, 1),
+ *     lo = max(floor(c(beta_fast)), 0),
+ *     hi = min(max(ceil(c(beta_slow)), 0), d/2 - 1),
+ * blends the two:  f'_i = f_i * (1 - gamma_i) + (f_i / s) * gamma_i.
+ * Reading: the bounds are the integer ones the page forms (floor, ceil, the
+ * clamp of hi to the last pair, the ramp's width at least 1); double
+ * arithmetic, one rounding to float at the end.  The bounds are returned
+ * through *lo_out / *hi_out when non-NULL.
  */
+static double yarn_corr_index(int rd, double base, int orig_max_pos, double rotations)
+{
+    return (double)rd * log((double)orig_max_pos / (2.0 * M_PI * rotations)) / (2.0 * log(base));
+}
+
 void orc_yarn_inv_freq(int rd, double base, double factor, int orig_max_pos,
                        double beta_fast, double beta_slow, float *out,
                        int *lo_out, int *hi_out)
 {
-    int half = rd / 2;
-    double cd_fast = (double)rd * log((double)orig_max_pos / (beta_fast * 2.0 * M_PI)) /
-                     (2.0 * log(base));
-    double cd_slow = (double)rd * log((double)orig_max_pos / (beta_slow * 2.0 * M_PI)) /
-                     (2.0 * log(base));
-    double lo_f = floor(cd_fast);
-    if (lo_f < 0.0)
-        lo_f = 0.0;
-    double hi_f = ceil(cd_slow);
-    double hi_cap = (double)(half > 0 ? half - 1 : 0);
-    if (hi_f < 0.0)
-        hi_f = 0.0;
-    if (hi_f > hi_cap)
-        hi_f = hi_cap;
-    int low = (int)lo_f;
-    int high = (int)hi_f;
-    int diff = high > low ? high - low : 0;
-    int denom = diff > 1 ? diff : 1;
-    for (int i = 0; i < half; i++) {
+    int n_pairs = rd / 2;
+    double lo = fmax(floor(yarn_corr_index(rd, base, orig_max_pos, beta_fast)), 0.0);
+    double hi = fmax(ceil(yarn_corr_index(rd, base, orig_max_pos, beta_slow)), 0.0);
+    hi = fmin(hi, (double)(n_pairs > 0 ? n_pairs - 1 : 0));
+    double width = fmax(hi - lo, 1.0);
+    for (int i = 0; i < n_pairs; i++) {
         double f = 1.0 / pow(base, (2.0 * i) / (double)rd);
-        double interp = f / factor;
-        int num = i > low ? i - low : 0;
-        double ramp = (double)num / (double)denom;
-        if (ramp < 0.0)
-            ramp = 0.0;
-        if (ramp > 1.0)
-            ramp = 1.0;
-        double extrapolation = 1.0 - ramp;
-        out[i] = (float)(interp * (1.0 - extrapolation) + f * extrapolation);
+        double gamma = fmin(fmax(((double)i - lo) / width, 0.0), 1.0);
+        out[i] = (float)(f * (1.0 - gamma) + (f / factor) * gamma);
     }
     if (lo_out)
-        *lo_out = low;
+        *lo_out = (int)lo;
     if (hi_out)
-        *hi_out = high;
+        *hi_out = (int)hi;
 }
 
 /* ------------------------------------------------------------------------ */

@@ -132,6 +132,9 @@ def test_append_validation():
     assert append(ring=3) == EINVAL
     assert append(v_norm=2) == EINVAL
     assert append(ring=1, max_end=300, n_seq=0) == OK     # a ring has a row for every position
+    # a wrapped ring shorter than the chunk would give p and p + cap one row
+    assert append(ring=1, max_end=600, max_chunk=257, n_tok=257) == ECAP
+    assert append(ring=1, max_end=600, max_chunk=256, n_tok=256, n_seq=0) == OK
     assert append(rd=63) == EINVAL
     assert append(f=None) == EINVAL
     assert append(norm=1, w=None) == EINVAL
@@ -140,6 +143,29 @@ def test_append_validation():
     assert append(cap=0) == EINVAL
     assert append(n_tok=0) == OK
     assert append(rd=0, f=None, n_seq=0) == OK
+
+
+def rope_qkv(**kw):
+    a = dict(q=P, qo=P, nh=8, kc=P, vc=P, kn=P, vn=P, nkv=2, cap=256, ring=0, dtype=1, n_tok=16, hd=128,
+             n_seq=1, cu=P, st=P, max_chunk=16, max_end=64, f=P, rd=128, rs=1.0, norm=0, qw=None,
+             kw=None, eps=1e-6, v_norm=0)
+    a.update(kw)
+    return api.lib().attn_rope_qkv(a["q"], a["qo"], a["nh"], a["kc"], a["vc"], a["kn"], a["vn"], a["nkv"],
+                                   a["cap"], a["ring"], a["dtype"], a["n_tok"], a["hd"], a["n_seq"],
+                                   a["cu"], a["st"], a["max_chunk"], a["max_end"], a["f"], a["rd"],
+                                   a["rs"], a["norm"], a["qw"], a["kw"], a["eps"], a["v_norm"], None)
+
+
+def test_rope_qkv_validation():
+    assert rope_qkv(max_end=300) == ECAP
+    assert rope_qkv(ring=1, max_end=600, max_chunk=257, n_tok=257) == ECAP
+    assert rope_qkv(ring=1, max_end=600, max_chunk=256, n_tok=256, n_seq=0) == OK
+    assert rope_qkv(ring=2) == EINVAL
+    assert rope_qkv(norm=1, qw=P, kw=None) == EINVAL
+    assert rope_qkv(nkv=0) == EINVAL
+    assert rope_qkv(hd=96) == EUNSUP
+    assert rope_qkv(q=None) == EINVAL
+    assert rope_qkv(n_tok=0) == OK
 
 
 def rope(**kw):

@@ -1,8 +1,10 @@
 """Parity at the full workload sizes, in the launch configuration bench.py
-times (the same chunk driver and chunk sizes), on sampled outputs the oracle
-computes one row at a time: position 0, rows on both sides of chunk
-boundaries, the final row and seeded random rows, every query head of each.
-The K/V cache is also checked in full where that is cheap."""
+times (the same chunk driver and chunk sizes).  The Llama-shaped prefill
+(4096 positions) and the decode batch (64 sequences) compare every output
+row and every probability row with the oracle; the larger workloads compare
+sampled rows the oracle computes one at a time: position 0, rows on both
+sides of chunk boundaries, the final row and seeded random rows, every query
+head of each.  The K/V cache is also checked in full where that is cheap."""
 import numpy as np
 import pytest
 import torch
@@ -53,9 +55,9 @@ def run_prefill(name):
     return w, d, run
 
 
-def check_sequence(w, d, run, b, seed, label, check_cache=True):
+def check_sequence(w, d, run, b, seed, label, check_cache=True, every_row=False):
     n = d["lengths"][b]
-    positions = sample_positions(n, w.chunk, seed, window=w.window)
+    positions = list(range(n)) if every_row else sample_positions(n, w.chunk, seed, window=w.window)
     pos, ref = oracle_rows(w, d, b, positions)
     got_all = run.gather("out")
     idx = torch.as_tensor(d["cu_seq"][b] + pos, device=got_all.device)
@@ -80,8 +82,9 @@ def check_sequence(w, d, run, b, seed, label, check_cache=True):
 
 
 def test_c1_llama_prefill_full():
+    # every one of the 4096 x 32 output rows against the oracle
     w, d, run = run_prefill("c1_llama_prefill")
-    check_sequence(w, d, run, 0, 101, "c1")
+    check_sequence(w, d, run, 0, 101, "c1", every_row=True)
 
 
 def test_c3_qwen_varlen_full():
@@ -104,7 +107,7 @@ def test_c4_yarn_128k_full():
     assert np.array_equal(_bits(got), want.view(torch.int16).numpy())
 
 
-def check_decode(name):
+def check_decode(name, every_seq=False):
     w = wl.CONFIGS[name]
     say(f"full-size decode: {w}")
     d = wl.gen_decode(w, device=DEV)
@@ -114,8 +117,9 @@ def check_decode(name):
     torch.cuda.synchronize()
     ctx = d["ctx"]
     order = np.argsort(ctx)
-    picks = sorted({int(order[0]), int(order[1]), int(order[-1]), int(order[-2]),
-                    int(order[len(ctx) // 2]), 7})
+    picks = (list(range(len(ctx))) if every_seq else
+             sorted({int(order[0]), int(order[1]), int(order[-1]), int(order[-2]),
+                     int(order[len(ctx) // 2]), 7}))
     say(f"  checking sequences {picks} with ctx {[ctx[b] for b in picks]}")
     out = np64(step.out)
     cap = step.cap
@@ -138,7 +142,8 @@ def check_decode(name):
 
 
 def test_c2_decode_full():
-    check_decode("c2_decode")
+    # every one of the 64 sequences: outputs and probabilities of all heads
+    check_decode("c2_decode", every_seq=True)
 
 
 def test_c2_decode_sw4096_full():

@@ -790,18 +790,21 @@ def test_small_chunk_path_matches_oracle(nh, nkv, n_new, window, ring, gate):
 
 # ------------------------------------------------------------------ importance
 
-@pytest.mark.parametrize("dtype", [wl.BF16, wl.F32])
-def test_decode_importance_matches_oracle(dtype):
+@pytest.mark.parametrize("dtype,nh,nkv", [(wl.BF16, 32, 8), (wl.F32, 32, 8), (wl.BF16, 40, 8),
+                                          (wl.BF16, 10, 2), (wl.F32, 40, 8)])
+def test_decode_importance_matches_oracle(dtype, nh, nkv):
     """Per-position importance after a decode step: the sum over heads of
     the probabilities.  Against the GPU's own probabilities summed in head
     order in float (bit for bit), against the oracle's importance (within the
     probabilities' tolerance, summed over heads), accumulating twice doubles
-    it exactly, and entries past ctx stay untouched."""
+    it exactly, and entries past ctx stay untouched.  40 and 10 heads are not
+    multiples of the kernel's 16-head load groups, so its leftover-heads loop
+    runs too."""
     ctx = [1, 63, 64, 65, 1025, 3000]
-    nh, nkv, hd = 32, 8, 128
+    hd = 128
     w = wl.Workload(name="imp", dtype=dtype, n_heads=nh, n_kv=nkv, head_dim=hd, seed=43,
                     n_seq=len(ctx), decode=True, ctx_range=(1, 3000), cap=3072, want_probs=True)
-    say(f"decode importance dtype={dtype} ctx={ctx}")
+    say(f"decode importance dtype={dtype} heads {nh}/{nkv} ctx={ctx}")
     d = wl.gen_decode(w)
     d["ctx"] = ctx
     step = runner.DecodeStep(w, d, device=DEV, probs_ld_multiple=1)

@@ -44,8 +44,8 @@ def test_rope_inv_freq_closed_forms():
 
 def test_rope_inv_freq_partial_rotary_uses_rotary_dim():
     # For partial rotary the exponent denominator is the rotary dim ([ATT]
-    # QwenAttnCfg: inv_freq has rotary_dim/2 entries; yarn_inv_freq's head_dim
-    # "is the rotary dimension").  rd = 64, base 1e6: f_16 = 1e6^(-1/2).
+    # QwenAttnCfg: inv_freq has rotary_dim/2 entries; the head_dim argument of
+    # yarn_inv_freq is documented there as the rotary width).  rd = 64, base 1e6: f_16 = 1e6^(-1/2).
     f = oracle.rope_inv_freq(64, 1e6)
     assert f.shape == (32,)
     assert f[16] == np.float32(1e-3)
@@ -487,8 +487,8 @@ def test_ring_cache_orders():
 def test_vnorm_worked_example_and_invariants():
     """V-norm ([ATT] fn vnorm_head: x / sqrt(mean(x^2) + eps), no weight, no
     +1).  Pinned by a worked example, unit mean square, scale invariance, and
-    its equality with the Qwen-style qk-norm at unit weight (the pages'
-    "pure normalization")."""
+    its equality with the Qwen-style qk-norm at unit weight (the page calls it
+    a normalisation with no learned scale)."""
     got = oracle.vnorm_heads(np.array([[3.0, 4.0]]), eps=0.0)
     # mean square (9 + 16) / 2 = 12.5; stored as float32
     want = np.array([[3.0 / np.sqrt(12.5), 4.0 / np.sqrt(12.5)]], dtype=np.float32)
@@ -554,6 +554,9 @@ MUTATIONS = {
     "sigmoid_sign": ("f = 1.0 / (1.0 + exp(-g[d]));", "f = 1.0 / (1.0 + exp(g[d]));"),
     "softplus_without_max": ("return fmax(x, 0.0) + log1p(exp(-fabs(x)));", "return log1p(exp(-fabs(x)));"),
     "softplus_head_per_element": ("f = softplus(g[0]);", "f = softplus(g[d]);"),
+    "yarn_ramp_reversed": ("out[i] = (float)(f * (1.0 - gamma) + (f / factor) * gamma);",
+                           "out[i] = (float)(f * gamma + (f / factor) * (1.0 - gamma));"),
+    "yarn_lo_ceil": ("double lo = fmax(floor(yarn_corr_index(", "double lo = fmax(ceil(yarn_corr_index("),
 }
 
 
@@ -576,7 +579,8 @@ def _pins_pass():
               lambda: test_brute_force_matrix_softmax(5, 7), test_gqa_equals_mha_with_repeated_kv,
               test_attention_head_uniform_page_example, test_bf16_rounding_matches_torch_on_float32_values,
               test_head_importance_mass_and_special_cases, test_sliding_window_special_cases,
-              test_vnorm_worked_example_and_invariants, test_output_gates]
+              test_vnorm_worked_example_and_invariants, test_output_gates,
+              test_yarn_page_endpoint_contract, test_yarn_ramp_closed_form_128k]
     for c in checks:
         try:
             c()
