@@ -10,8 +10,9 @@
 //
 // How (gfx950 design, not the pages'):
 //  * GQA packing: the G query heads of one KV group read the same keys, so a
-//    workgroup takes 128 "rows" = (position, head) pairs of one group, ordered
-//    position-major, and streams that group's K/V once for all of them.
+//    workgroup takes 256 (large calls) or 128 (small calls) "rows" =
+//    (position, head) pairs of one group, ordered position-major, and
+//    streams that group's K/V once for all of them.
 //  * The score tile is computed transposed, S^T = K Q^T, with
 //    v_mfma_f32_32x32x16_bf16: the A operand is a 32-key slab of K from LDS,
 //    the B operand is the lane's own query row held in registers.  In the
@@ -20,16 +21,19 @@
 //    softmax step is lane-local.
 //  * O^T = V^T P^T reuses the score registers directly as the B operand (the
 //    key order inside each 16-key step is the same permutation on both
-//    operands); V is written transposed into LDS so the A operand is two
-//    8-byte reads.
+//    operands); V stays in its natural layout in LDS and the A operand is
+//    read with the transposing LDS read.
 //  * Online softmax in registers (exp2 with the scale folded in), the
-//    rescale of O skipped when no row's maximum moved, probabilities rounded
-//    to bf16 for the matrix product and the row sum taken from the rounded
-//    values so the weights stay a convex combination.
-//  * K/V tiles of 64 keys are double-buffered in LDS, the next tile's global
-//    loads are in flight while the current one is multiplied; tiles entirely
-//    above a wave's causal limit are skipped, and only tiles that cross the
-//    diagonal are masked.
+//    rescale of O skipped unless a row's maximum grows by more than 2^8,
+//    probabilities rounded to bf16 for the matrix product and the row sum
+//    taken from the rounded values so the weights stay a convex combination.
+//  * 256-row items (prefill_pp_kernel): two waves per SIMD alternate a
+//    matrix phase and a softmax phase half a tile apart (ping-pong), so one
+//    wave's products overlap the other's exponentials; K/V tiles of 64 keys
+//    in three LDS slots.  128-row items (prefill_bf16_ks_kernel): two waves
+//    share 32 rows and take the two key halves of every tile.  Tiles
+//    entirely above a wave's causal limit are skipped; only tiles that cross
+//    the diagonal are masked.
 //  * Split-KV: when the chunk has too few row tiles to fill 256 CUs, the key
 //    range is split and the parts are merged by a log-sum-exp combine.
 //  * blockIdx -> (group, split, row tile, sequence) with the group fastest,
@@ -65,6 +69,16 @@ struct PrefillSmem {
     uint16_t k[2][kTK * KS];
     uint16_t v[2][kTK * VS];
 };
+
+// Calls f(std::integral_constant<int, i>) for i = I .. N-1, so the body can
+// use i in constant expressions (scheduling-group sizes, register indices).
+template <int I, int N, typename F>
+__device__ __forceinline__ void static_for(F&& f) {
+    if constexpr (I < N) {
+        f(std::integral_constant<int, I>{});
+        static_for<I + 1, N>(f);
+    }
+}
 
 __device__ __forceinline__ f32x16_t mfma32(bf16x8_t a, bf16x8_t b, f32x16_t c) {
     return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
@@ -241,359 +255,20 @@ __device__ PrefillItem split_schedule(const PrefillArgs& a, int item) {
     return PrefillItem{src / a.n_qtiles, src % a.n_qtiles, local % a.n_kv, local / a.n_kv, __shfl(nsp, src)};
 }
 
-// NW waves of 32 query rows each share every K/V tile.  With 8 waves each
-// thread stages half a tile's worth of K and V, which leaves room for two
-// staging sets: the global loads of a tile are then issued two tiles before
-// they are stored to LDS (PD = 2) instead of one.  WIN: the call has a
-// sliding window (only that instance carries the lower mask).
-template <int HD, int NW, bool WIN>
-__global__ __launch_bounds__(NW * 64, 8 / NW) void prefill_bf16_kernel(PrefillArgs a) {
-    using Sm = PrefillSmem<HD>;
-    constexpr int kThreads = NW * 64;
-    constexpr int PD = NW == 8 ? 2 : 1;           // staging sets = prefetch depth
-    constexpr int KS = Sm::KS;
-    constexpr int VS = Sm::VS;
-    constexpr int CH = HD / 8;                    // 16-byte chunks per cache row
-    constexpr int NCH = kTK * CH / kThreads;      // K (and V) chunks per thread
-    constexpr int NDB = HD / 32;                  // 32-dim blocks of O
-    constexpr int NKK = HD / 16;                  // K-steps of a score product
-    constexpr int TILE_ROWS = NW * 32;            // query rows per workgroup
-    __shared__ Sm sm;
-
-    const int tid = threadIdx.x;
-    const int lane = tid & 63;
-    const int wave = tid >> 6;
-    const int hf = lane >> 5;                     // wave half
-    const int rl = lane & 31;
-
-    const int item = blockIdx.x;
-    PrefillItem itm;
-    if (a.split) {
-        itm = split_schedule(a, item);
-    } else {
-        // KV group fastest, long row tiles first
-        itm.g = item % a.n_kv;
-        itm.qt = a.n_qtiles - 1 - (item / a.n_kv) % a.n_qtiles;
-        itm.b = item / (a.n_kv * a.n_qtiles);
-        itm.part = 0;
-        itm.nsp = 1;
-    }
-    if (itm.nsp <= 0) return;
-    // the item is the same in every lane: keep it in scalar registers
-    const int b = __builtin_amdgcn_readfirstlane(itm.b), qt = __builtin_amdgcn_readfirstlane(itm.qt),
-              g = __builtin_amdgcn_readfirstlane(itm.g), s = __builtin_amdgcn_readfirstlane(itm.part),
-              nsp = __builtin_amdgcn_readfirstlane(itm.nsp);
-
-    const int G = a.group;
-    const int t0 = a.cu_seq[b];
-    const int len = min(a.cu_seq[b + 1] - t0, a.max_chunk);
-    const int p0 = a.start[b];
-    const int rows_b = len * G;
-    const int r_tile0 = qt * TILE_ROWS;
-    if (len <= 0 || p0 < 0 || r_tile0 >= rows_b) return;
-
-    const int r_last = min(r_tile0 + TILE_ROWS, rows_b) - 1;
-    // keys 0..n_keys-1 (a ring cache holds positions past its capacity)
-    const int n_keys = WIN && a.ring ? p0 + r_last / G + 1 : min(p0 + r_last / G + 1, a.cap);
-    const int n_tiles = (n_keys + kTK - 1) / kTK;
-    // this item's part of the row tile's key tiles (from the first one its
-    // window reaches), parts of equal length
-    const int t_first = WIN ? min(first_key_tile(p0 + r_tile0 / G, a.window), n_tiles) : 0;
-    const int per = (n_tiles - t_first + nsp - 1) / nsp;
-    const int tb = t_first + s * per;
-    const int te = min(tb + per, n_tiles);
-
-    // this lane's query row (position-major within the group) and its wave's
-    const int r = r_tile0 + wave * 32 + rl;
-    const int i = r / G;
-    const int t = t0 + i;
-    const int h = g * G + (r - i * G);
-    const bool row_ok = r < rows_b && t >= 0 && t < a.n_tok;
-    const int pos = row_ok ? p0 + i : -1;
-    const int rw0 = r_tile0 + wave * 32;
-    const int pw_lo = p0 + rw0 / G;
-    // a key tile below key pw_hi - W + 1 misses the window of some row of
-    // the wave (pw_hi bounds the wave's positions from above)
-    const int win_lo = WIN ? p0 + (rw0 + 31) / G - a.window + 1 : INT_MIN;
-
-    bf16x8_t qf[NKK];
-    {
-        const uint16_t* qrow =
-            reinterpret_cast<const uint16_t*>(a.q) + ((size_t)t * a.n_heads + h) * HD;
-#pragma unroll
-        for (int k = 0; k < NKK; ++k) {
-            u32x4_t u = {0u, 0u, 0u, 0u};
-            if (row_ok) u = ld16(qrow + 16 * k + 8 * hf);
-            qf[k] = __builtin_bit_cast(bf16x8_t, u);
-        }
-    }
-
-    const size_t kvbase = ((size_t)b * a.n_kv + g) * (size_t)a.cap * HD;
-    const uint16_t* kc = reinterpret_cast<const uint16_t*>(a.k_cache) + kvbase;
-    const uint16_t* vc = reinterpret_cast<const uint16_t*>(a.v_cache) + kvbase;
-
-    // staging: thread -> NCH (row, 16-byte chunk) pairs of a tile, fetched
-    // with buffer loads whose resource starts at the tile and ends at the
-    // last key: the per-thread offsets are fixed, the tile moves in scalar
-    // registers, and rows past the last key read as zeros (their scores are
-    // masked to -inf and their probabilities are exactly 0).
-    u32x4_t kreg[PD][NCH], vreg[PD][NCH];
-    int voff[NCH];
-#pragma unroll
-    for (int c = 0; c < NCH; ++c) {
-        const int idx = c * kThreads + tid;
-        voff[c] = ((idx / CH) * HD + (idx % CH) * 8) * 2;
-    }
-    // a ring cache (capacity a multiple of kTK) keeps key tile j at tile
-    // j mod (cap / kTK), never split by the ring's end
-    const int ring_tiles = a.cap / kTK;
-    auto tile_rsrc = [&](const uint16_t* base, int j) __attribute__((always_inline)) {
-        // the clamp compiles to a vector-ALU instruction; without the
-        // readfirstlane the compiler cannot see that the resource is uniform
-        // and wraps every load in a loop over distinct resource values
-        const int rows = __builtin_amdgcn_readfirstlane(min(max(n_keys - j * kTK, 0), kTK));
-        const int jt = WIN && a.ring ? j % ring_tiles : j;
-        return __builtin_amdgcn_make_buffer_rsrc((void*)(base + (size_t)jt * kTK * HD), (short)0, rows * HD * 2,
-                                                 kBufferWord3);
-    };
-    auto lds_off = [&](int c, int stride) __attribute__((always_inline)) {
-        const int idx = c * kThreads + tid;
-        return (idx / CH) * stride + (idx % CH) * 8;
-    };
-    auto load_k = [&](int j, auto set) __attribute__((always_inline)) {
-        const auto rs = tile_rsrc(kc, j);
-#pragma unroll
-        for (int c = 0; c < NCH; ++c)
-            kreg[set.value][c] = __builtin_bit_cast(u32x4_t, __builtin_amdgcn_raw_buffer_load_b128(rs, voff[c], 0, 0));
-    };
-    auto load_v = [&](int j, auto set) __attribute__((always_inline)) {
-        const auto rs = tile_rsrc(vc, j);
-#pragma unroll
-        for (int c = 0; c < NCH; ++c)
-            vreg[set.value][c] = __builtin_bit_cast(u32x4_t, __builtin_amdgcn_raw_buffer_load_b128(rs, voff[c], 0, 0));
-    };
-    auto store_k = [&](int buf, auto set) __attribute__((always_inline)) {
-#pragma unroll
-        for (int c = 0; c < NCH; ++c) st16(&sm.k[buf][lds_off(c, KS)], kreg[set.value][c]);
-    };
-    auto store_v = [&](int buf, auto set) __attribute__((always_inline)) {
-#pragma unroll
-        for (int c = 0; c < NCH; ++c) st16(&sm.v[buf][lds_off(c, VS)], vreg[set.value][c]);
-    };
-    constexpr std::integral_constant<int, 0> set0{};
-    constexpr std::integral_constant<int, PD - 1> set1{};
-    auto scores = [&](const uint16_t* kl, f32x16_t& S0, f32x16_t& S1) __attribute__((always_inline)) {
-#pragma unroll
-        for (int q = 0; q < 16; ++q) {
-            S0[q] = 0.f;
-            S1[q] = 0.f;
-        }
-#pragma unroll
-        for (int kk = 0; kk < NKK; ++kk) {
-            const bf16x8_t a0 = __builtin_bit_cast(bf16x8_t, ld16(kl + rl * KS + kk * 16 + hf * 8));
-            const bf16x8_t a1 =
-                __builtin_bit_cast(bf16x8_t, ld16(kl + (32 + rl) * KS + kk * 16 + hf * 8));
-            S0 = mfma32(a0, qf[kk], S0);
-            S1 = mfma32(a1, qf[kk], S1);
-        }
-    };
-
-    // transposing-read address of this lane inside a V tile: group lane
-    // a = lane % 16 points at key a/4, dims 4(a%4); the wave half picks keys
-    // +4, the 16-lane group picks dims +16
-    const int tr_off = (4 * hf + ((lane & 15) >> 2)) * VS + 4 * (lane & 3) + 16 * ((lane >> 4) & 1);
-
-    f32x16_t O[NDB];
-#pragma unroll
-    for (int db = 0; db < NDB; ++db)
-#pragma unroll
-        for (int q = 0; q < 16; ++q) O[db][q] = 0.f;
-    float m_run = -INFINITY;
-    float l_run = 0.f;
-    const float sl = a.scale * kLog2e;
-
-    if (tb < te) {
-        // K and V are double-buffered one tile apart: during tile j the
-        // workgroup holds K[j+1] (scores of the next tile) and V[j].
-        load_k(tb, set0);
-        load_v(tb, set0);
-        store_k(0, set0);
-        store_v(0, set0);
-        if (tb + 1 < te) {
-            load_k(tb + 1, set0);
-            store_k(1, set0);
-        }
-        __syncthreads();
-        f32x16_t S0, S1;
-        scores(sm.k[0], S0, S1);
-        // Loads are unconditional (tile index clamped into range): past the
-        // last tile they refill LDS slots that are never read again.  With two
-        // staging sets, the loads stored at the end of tile j (K[j+2], V[j+1])
-        // were issued one tile earlier.
-        if (PD == 2) {
-            load_k(min(tb + 2, te - 1), set0);
-            load_v(min(tb + 1, te - 1), set0);
-        }
-
-        auto tile = [&](int j, auto cur, auto nxt) __attribute__((always_inline)) {
-            const int rr = (j - tb) & 1;
-            load_k(min(j + 1 + PD, te - 1), nxt);
-            load_v(min(j + PD, te - 1), nxt);
-            const int k0 = j * kTK;
-
-            // ---- causal mask of the current tile (tiles crossing the diagonal)
-            if (k0 + kTK - 1 > pw_lo) {
-                const int lim = pos - k0 - 4 * hf;
-#pragma unroll
-                for (int q = 0; q < 16; ++q) {
-                    const int off = 8 * (q >> 2) + (q & 3);
-                    if (off > lim) S0[q] = -INFINITY;
-                    if (off + 32 > lim) S1[q] = -INFINITY;
-                }
-            }
-            // ---- sliding window: keys below pos - W + 1
-            if (WIN && k0 < win_lo) {
-                const int llim = pos - a.window + 1 - k0 - 4 * hf;
-#pragma unroll
-                for (int q = 0; q < 16; ++q) {
-                    const int off = 8 * (q >> 2) + (q & 3);
-                    if (off < llim) S0[q] = -INFINITY;
-                    if (off + 32 < llim) S1[q] = -INFINITY;
-                }
-            }
-
-            // ---- row max of this tile and the (rare) rescale of O
-            float mx = fmaxf(S0[0], S1[0]);
-#pragma unroll
-            for (int q = 1; q < 16; ++q) mx = fmaxf(mx, fmaxf(S0[q], S1[q]));
-            mx = fmaxf(mx, __shfl_xor(mx, 32));
-            const float mt = mx * sl;                     // log2 units; -inf stays
-            const bool grow = mt > m_run + kRescaleSlack;
-            const float m_new = grow ? mt : m_run;
-            const float m_use = m_new == -INFINITY ? 0.f : m_new;
-            if (__any(grow)) {
-                const float alpha = grow ? __builtin_amdgcn_exp2f(m_run - m_use) : 1.f;
-                l_run *= alpha;
-#pragma unroll
-                for (int db = 0; db < NDB; ++db)
-#pragma unroll
-                    for (int q = 0; q < 16; ++q) O[db][q] *= alpha;
-            }
-            m_run = m_new;
-            const float nm = -m_use;
-            uint32_t pk[16];
-
-            // ---- next tile's scores on the matrix cores while the vector ALU
-            // computes this tile's probabilities for keys 0..31; K fragments
-            // are read one step ahead
-            f32x16_t N0, N1;
-            {
-                const uint16_t* kl = sm.k[rr ^ 1];
-#pragma unroll
-                for (int q = 0; q < 16; ++q) {
-                    N0[q] = 0.f;
-                    N1[q] = 0.f;
-                }
-                u32x4_t a0 = ld16(kl + rl * KS + hf * 8);
-                u32x4_t a1 = ld16(kl + (32 + rl) * KS + hf * 8);
-#pragma unroll
-                for (int kk = 0; kk < NKK; ++kk) {
-                    u32x4_t b0 = a0, b1 = a1;
-                    if (kk + 1 < NKK) {
-                        b0 = ld16(kl + rl * KS + (kk + 1) * 16 + hf * 8);
-                        b1 = ld16(kl + (32 + rl) * KS + (kk + 1) * 16 + hf * 8);
-                    }
-                    N0 = mfma32(__builtin_bit_cast(bf16x8_t, a0), qf[kk], N0);
-                    N1 = mfma32(__builtin_bit_cast(bf16x8_t, a1), qf[kk], N1);
-                    // keys 0..31 (8 packed pairs) spread over the NKK steps
-#pragma unroll
-                    for (int q = kk * 8 / NKK; q < (kk + 1) * 8 / NKK; ++q)
-                        pk[q] = pack_bf16x2(
-                            __builtin_amdgcn_exp2f(__builtin_fmaf(S0[2 * q], sl, nm)),
-                            __builtin_amdgcn_exp2f(__builtin_fmaf(S0[2 * q + 1], sl, nm)));
-                    a0 = b0;
-                    a1 = b1;
-                }
-                ATTN_INTERLEAVE(NKK, 2, 6);
-            }
-
-            // With two staging sets the K/V data stored at this tile's end
-            // arrived during the previous tile: store it now, so the LDS
-            // writes overlap the P.V products (K[j+2] replaces K[j], read
-            // last in the previous tile; V[j+1] replaces V[j-1]).
-            if (PD == 2) {
-                store_k(rr, cur);
-                store_v(rr ^ 1, cur);
-            }
-
-            // ---- O^T += V^T P^T: keys 0..31 while the probabilities of keys
-            // 32..63 are computed, then keys 32..63; V^T fragments are read
-            // one step ahead
-            {
-                const uint16_t* vl = sm.v[rr] + tr_off;
-                auto vfrag = [&](int kb, int tt, int db) __attribute__((always_inline)) {
-                    const uint16_t* vrow = vl + (kb * 32 + tt * 16) * VS + db * 32;
-                    const u32x2_t lo = lds_read_tr16(vrow);
-                    const u32x2_t hi = lds_read_tr16(vrow + 8 * VS);
-                    const u32x4_t vv = {lo.x, lo.y, hi.x, hi.y};
-                    return vv;
-                };
-                u32x4_t va = vfrag(0, 0, 0);
-#pragma unroll
-                for (int st = 0; st < 4 * NDB; ++st) {          // st = (kb, tt, db)
-                    const int kb = st / (2 * NDB), tt = (st / NDB) % 2, db = st % NDB;
-                    u32x4_t vn = va;
-                    if (st + 1 < 4 * NDB) {
-                        const int st1 = st + 1;
-                        vn = vfrag(st1 / (2 * NDB), (st1 / NDB) % 2, st1 % NDB);
-                    }
-                    const int pq = kb * 8 + tt * 4;
-                    const u32x4_t pv = {pk[pq], pk[pq + 1], pk[pq + 2], pk[pq + 3]};
-                    O[db] = mfma32(__builtin_bit_cast(bf16x8_t, va), __builtin_bit_cast(bf16x8_t, pv), O[db]);
-                    // keys 32..63 (8 packed pairs) spread over the 2*NDB steps
-                    // of keys 0..31, so they are ready before they are used
-                    if (st < 2 * NDB) {
-#pragma unroll
-                        for (int q = st * 8 / (2 * NDB); q < (st + 1) * 8 / (2 * NDB); ++q)
-                            pk[8 + q] = pack_bf16x2(
-                                __builtin_amdgcn_exp2f(__builtin_fmaf(S1[2 * q], sl, nm)),
-                                __builtin_amdgcn_exp2f(__builtin_fmaf(S1[2 * q + 1], sl, nm)));
-                    }
-                    va = vn;
-                }
-                ATTN_INTERLEAVE(2 * NDB, 1, 5);
-            }
-            // the row sum is taken from the rounded probabilities that feed
-            // the P.V product
-            l_run += sum_bf16_pairs(pk);
-
-            if (PD == 1) {
-                store_k(rr, cur);
-                store_v(rr ^ 1, cur);
-            }
-            __syncthreads();
-            S0 = N0;
-            S1 = N1;
-        };
-        for (int j = tb; j < te; ++j) {
-            if (PD == 2) {
-                tile(j, set0, set1);
-                if (++j >= te) break;
-                tile(j, set1, set0);
-            } else {
-                tile(j, set0, set0);
-            }
-        }
-    }
-
-    const float l_tot = l_run + __shfl_xor(l_run, 32);
-    if (!row_ok) return;
+// Output of one lane's half of a query row (dims db*32 + 8*q4 + 4*hf + 0..3
+// of O[db]), after the last key tile: an unsplit row is normalised by its
+// row sum l_tot, gated when asked, and stored as float32; a split part leaves
+// (m, l) and O/l in half precision (scaled by 2^-e when needed) for the
+// combine.  Both wave halves of the row call this.
+template <int HD>
+__device__ __forceinline__ void write_row(const PrefillArgs& a, f32x16_t (&O)[HD / 32], float m_run, float l_tot,
+                                          int t, int h, int hf, int nsp, float* part_row) {
+    constexpr int NDB = HD / 32;
     if (nsp <= 1) {
         const float inv = 1.f / l_tot;
         float* orow = a.out + ((size_t)t * a.n_heads + h) * HD;
         if (a.gate.mode) {
-            // output gate: this lane's dims db*32 + 8*q4 + 4*hf + 0..3, all
-            // loads issued before any factor is formed
+            // output gate: all loads issued before any factor is formed
             const size_t grow = (size_t)t * a.n_heads + h;
             const uint16_t* gp = reinterpret_cast<const uint16_t*>(a.gate.p) + grow * (size_t)a.gate.ld;
             if (a.gate.mode == kGateSoftplusHead) {
@@ -642,9 +317,8 @@ __global__ __launch_bounds__(NW * 64, 8 / NW) void prefill_bf16_kernel(PrefillAr
                 *reinterpret_cast<float4*>(orow + db * 32 + 8 * q4 + 4 * hf) = v;
             }
     } else {
-        // partial of this item's row r - r_tile0: O/l in half precision
-        // (a part whose keys are all masked for the row has l = 0, O = 0)
-        float* pr = a.part + ((size_t)item * TILE_ROWS + (r - r_tile0)) * part_row_words(HD);
+        // partial of the row: O/l in half precision (a part whose keys are
+        // all masked for the row has l = 0, O = 0)
         const float inv = l_tot > 0.f ? 1.f / l_tot : 0.f;
         float mx = 0.f;
 #pragma unroll
@@ -654,8 +328,8 @@ __global__ __launch_bounds__(NW * 64, 8 / NW) void prefill_bf16_kernel(PrefillAr
         mx = fmaxf(mx, __shfl_xor(mx, 32)) * inv;
         const int ex = part_scale_exp(mx);
         const float sc = __builtin_amdgcn_ldexpf(inv, -ex);
-        if (hf == 0) *reinterpret_cast<float4*>(pr) = make_float4(m_run, l_tot, (float)ex, 0.f);
-        uint32_t* ph = reinterpret_cast<uint32_t*>(pr + kPartHead);
+        if (hf == 0) *reinterpret_cast<float4*>(part_row) = make_float4(m_run, l_tot, (float)ex, 0.f);
+        uint32_t* ph = reinterpret_cast<uint32_t*>(part_row + kPartHead);
 #pragma unroll
         for (int db = 0; db < NDB; ++db)
 #pragma unroll
@@ -665,6 +339,346 @@ __global__ __launch_bounds__(NW * 64, 8 / NW) void prefill_bf16_kernel(PrefillAr
                 *reinterpret_cast<u32x2_t*>(ph + (db * 32 + 8 * q4 + 4 * hf) / 2) = v;
             }
     }
+}
+
+// Ping-pong kernel for 256-row work items: 8 waves of 32 query rows, two
+// per SIMD (waves w and w+4).  Each wave alternates a matrix phase (the
+// scores of key tile k on the matrix cores, S^T = K Q^T, together with the
+// P.V product of tile k-1) and a softmax phase (mask, row maximum, the rare
+// rescale of O, exponentials, row sums of tile k, plus its share of the K/V
+// staging).  Waves 4..7 run one phase behind waves 0..3, with a workgroup
+// barrier between phases, so on every SIMD one wave's matrix products run
+// while the other wave's exponentials and bookkeeping use the vector ALU.
+// Three LDS slots per K and V tile give the half-tile offset room: tile j
+// sits in slot (j - tb) mod 3, is written during the softmax phases of the
+// tile two (K) or one (V) before it, and is overwritten only after both
+// wave groups have left the phase that reads it.
+template <int HD>
+struct PingPongSmem {
+    static constexpr int KS = HD + 8;
+    static constexpr int VS = HD + 32;
+    uint16_t k[3][kTK * KS];
+    uint16_t v[3][kTK * VS];
+};
+
+#ifndef ATTN_PP_PRIO
+#define ATTN_PP_PRIO 1
+#endif
+// fragment reads in flight ahead of the matrix products (in product steps)
+#ifndef ATTN_PP_PREFETCH
+#define ATTN_PP_PREFETCH 3
+#endif
+// the row maximum's exchange between wave halves: v_permlane32_swap (vector
+// ALU) rather than an LDS permute, which waits behind the other group's
+// fragment reads
+#ifndef ATTN_PP_PERMLANE
+#define ATTN_PP_PERMLANE 1
+#endif
+
+template <int HD, bool WIN>
+__global__ __launch_bounds__(512, 1) void prefill_pp_kernel(PrefillArgs a) {
+    using Sm = PingPongSmem<HD>;
+    constexpr int kThreads = 512;
+    constexpr int KS = Sm::KS;
+    constexpr int VS = Sm::VS;
+    constexpr int CH = HD / 8;                    // 16-byte chunks per cache row
+    constexpr int NCH = kTK * CH / kThreads;      // K (and V) chunks per thread
+    constexpr int NDB = HD / 32;                  // 32-dim blocks of O
+    constexpr int NKK = HD / 16;                  // K-steps of a score product
+    constexpr int TILE_ROWS = 256;                // query rows per workgroup
+    __shared__ Sm sm;
+
+    const int tid = threadIdx.x;
+    const int lane = tid & 63;
+    const int wave = tid >> 6;
+    const int grp = __builtin_amdgcn_readfirstlane(wave >> 2);   // 0: leads, 1: one phase behind
+    const int hf = lane >> 5;                     // wave half
+    const int rl = lane & 31;
+
+    const int item = blockIdx.x;
+    PrefillItem itm;
+    if (a.split) {
+        itm = split_schedule(a, item);
+    } else {
+        // KV group fastest, long row tiles first
+        itm.g = item % a.n_kv;
+        itm.qt = a.n_qtiles - 1 - (item / a.n_kv) % a.n_qtiles;
+        itm.b = item / (a.n_kv * a.n_qtiles);
+        itm.part = 0;
+        itm.nsp = 1;
+    }
+    if (itm.nsp <= 0) return;
+    const int b = __builtin_amdgcn_readfirstlane(itm.b), qt = __builtin_amdgcn_readfirstlane(itm.qt),
+              g = __builtin_amdgcn_readfirstlane(itm.g), s = __builtin_amdgcn_readfirstlane(itm.part),
+              nsp = __builtin_amdgcn_readfirstlane(itm.nsp);
+
+    const int G = a.group;
+    const int t0 = a.cu_seq[b];
+    const int len = min(a.cu_seq[b + 1] - t0, a.max_chunk);
+    const int p0 = a.start[b];
+    const int rows_b = len * G;
+    const int r_tile0 = qt * TILE_ROWS;
+    if (len <= 0 || p0 < 0 || r_tile0 >= rows_b) return;
+
+    const int r_last = min(r_tile0 + TILE_ROWS, rows_b) - 1;
+    const int n_keys = WIN && a.ring ? p0 + r_last / G + 1 : min(p0 + r_last / G + 1, a.cap);
+    const int n_tiles = (n_keys + kTK - 1) / kTK;
+    const int t_first = WIN ? min(first_key_tile(p0 + r_tile0 / G, a.window), n_tiles) : 0;
+    const int per = (n_tiles - t_first + nsp - 1) / nsp;
+    const int tb = t_first + s * per;
+    const int te = min(tb + per, n_tiles);
+
+    const int r = r_tile0 + wave * 32 + rl;
+    const int i = r / G;
+    const int t = t0 + i;
+    const int h = g * G + (r - i * G);
+    const bool row_ok = r < rows_b && t >= 0 && t < a.n_tok;
+    const int pos = row_ok ? p0 + i : -1;
+    const int rw0 = r_tile0 + wave * 32;
+    const int pw_lo = __builtin_amdgcn_readfirstlane(p0 + rw0 / G);
+    const int win_lo = WIN ? __builtin_amdgcn_readfirstlane(p0 + (rw0 + 31) / G - a.window + 1) : INT_MIN;
+
+    bf16x8_t qf[NKK];
+    {
+        const uint16_t* qrow =
+            reinterpret_cast<const uint16_t*>(a.q) + ((size_t)t * a.n_heads + h) * HD;
+#pragma unroll
+        for (int k = 0; k < NKK; ++k) {
+            u32x4_t u = {0u, 0u, 0u, 0u};
+            if (row_ok) u = ld16(qrow + 16 * k + 8 * hf);
+            qf[k] = __builtin_bit_cast(bf16x8_t, u);
+        }
+    }
+
+    const size_t kvbase = ((size_t)b * a.n_kv + g) * (size_t)a.cap * HD;
+    const uint16_t* kc = reinterpret_cast<const uint16_t*>(a.k_cache) + kvbase;
+    const uint16_t* vc = reinterpret_cast<const uint16_t*>(a.v_cache) + kvbase;
+
+    // staging: thread -> NCH (row, 16-byte chunk) pairs of a tile, buffer
+    // loads from a resource over the tile's rows (rows past the last key
+    // read as zeros: their scores are masked and their probabilities are 0)
+    u32x4_t kreg[NCH], vreg[NCH];
+    int voff[NCH], kls[NCH], vls[NCH];
+#pragma unroll
+    for (int c = 0; c < NCH; ++c) {
+        const int idx = c * kThreads + tid;
+        voff[c] = ((idx / CH) * HD + (idx % CH) * 8) * 2;
+        kls[c] = (idx / CH) * KS + (idx % CH) * 8;
+        vls[c] = (idx / CH) * VS + (idx % CH) * 8;
+    }
+    const int ring_tiles = a.cap / kTK;
+    auto tile_rsrc = [&](const uint16_t* base, int j) __attribute__((always_inline)) {
+        const int rows = __builtin_amdgcn_readfirstlane(min(max(n_keys - j * kTK, 0), kTK));
+        const int jt = WIN && a.ring ? j % ring_tiles : j;
+        return __builtin_amdgcn_make_buffer_rsrc((void*)(base + (size_t)jt * kTK * HD), (short)0, rows * HD * 2,
+                                                 kBufferWord3);
+    };
+    auto load_kv = [&](int jk, int jv) __attribute__((always_inline)) {
+        const auto rk = tile_rsrc(kc, jk);
+        const auto rv = tile_rsrc(vc, jv);
+#pragma unroll
+        for (int c = 0; c < NCH; ++c)
+            kreg[c] = __builtin_bit_cast(u32x4_t, __builtin_amdgcn_raw_buffer_load_b128(rk, voff[c], 0, 0));
+#pragma unroll
+        for (int c = 0; c < NCH; ++c)
+            vreg[c] = __builtin_bit_cast(u32x4_t, __builtin_amdgcn_raw_buffer_load_b128(rv, voff[c], 0, 0));
+    };
+    auto store_k = [&](int slot) __attribute__((always_inline)) {
+#pragma unroll
+        for (int c = 0; c < NCH; ++c) st16(&sm.k[slot][kls[c]], kreg[c]);
+    };
+    auto store_v = [&](int slot) __attribute__((always_inline)) {
+#pragma unroll
+        for (int c = 0; c < NCH; ++c) st16(&sm.v[slot][vls[c]], vreg[c]);
+    };
+
+    // transposing-read address of this lane inside a V tile (see the
+    // full-tile kernel)
+    const int tr_off = (4 * hf + ((lane & 15) >> 2)) * VS + 4 * (lane & 3) + 16 * ((lane >> 4) & 1);
+
+    f32x16_t O[NDB];
+#pragma unroll
+    for (int db = 0; db < NDB; ++db)
+#pragma unroll
+        for (int q = 0; q < 16; ++q) O[db][q] = 0.f;
+    float m_run = -INFINITY;
+    float l_run = 0.f;
+    const float sl = a.scale * kLog2e;
+    f32x16_t S0, S1;
+    uint32_t pk[16];
+
+    // ---- matrix phase: scores of key tile j (slot ks) when SC, and O^T +=
+    // V^T P^T of the previous tile (slot vs, probabilities pk) when PV.
+    // 2*NKK score products and 4*NDB P.V products, alternated; every
+    // fragment is read PFD steps before its product, an order the
+    // scheduling groups pin (the reads otherwise drift next to their
+    // products and each product waits for a full LDS round trip).
+    auto mphase = [&](int ks, int vs, auto SC, auto PV) __attribute__((always_inline)) {
+        // phases are kept whole: nothing is scheduled across their bounds
+        __builtin_amdgcn_sched_barrier(0);
+        if (ATTN_PP_PRIO) __builtin_amdgcn_s_setprio(ATTN_PP_PRIO);
+        const uint16_t* kl = sm.k[ks];
+        const uint16_t* vl = sm.v[vs] + tr_off;
+        auto kload = [&](int st) __attribute__((always_inline)) {   // st = (kk, slab)
+            return ld16(kl + ((st % 2) * 32 + rl) * KS + (st / 2) * 16 + hf * 8);
+        };
+        auto vfrag = [&](int st) __attribute__((always_inline)) {   // st = (kb, tt, db)
+            const int kb = st / (2 * NDB), tt = (st / NDB) % 2, db = st % NDB;
+            const uint16_t* vrow = vl + (kb * 32 + tt * 16) * VS + db * 32;
+            const u32x2_t lo = lds_read_tr16(vrow);
+            const u32x2_t hi = lds_read_tr16(vrow + 8 * VS);
+            const u32x4_t vv = {lo.x, lo.y, hi.x, hi.y};
+            return vv;
+        };
+        if (SC.value) {
+#pragma unroll
+            for (int q = 0; q < 16; ++q) {
+                S0[q] = 0.f;
+                S1[q] = 0.f;
+            }
+        }
+        constexpr int NS = SC.value ? 2 * NKK : 0;
+        constexpr int NP = PV.value ? 4 * NDB : 0;
+        constexpr int NT = NS > NP ? NS : NP;
+        constexpr int PFD = ATTN_PP_PREFETCH;
+        u32x4_t kf[PFD + 1], vf[PFD + 1];
+#pragma unroll
+        for (int st = 0; st < PFD; ++st) {
+            if (st < NS) kf[st] = kload(st);
+            if (st < NP) vf[st] = vfrag(st);
+        }
+        __builtin_amdgcn_sched_group_barrier(0x100, (PFD < NS ? PFD : NS) + 2 * (PFD < NP ? PFD : NP), 0);
+        static_for<0, NT>([&](auto ic) __attribute__((always_inline)) {
+            constexpr int st = decltype(ic)::value;
+            if constexpr (st + PFD < NS) kf[(st + PFD) % (PFD + 1)] = kload(st + PFD);
+            if constexpr (st + PFD < NP) vf[(st + PFD) % (PFD + 1)] = vfrag(st + PFD);
+            if constexpr (st < NS) {
+                if constexpr (st % 2 == 0)
+                    S0 = mfma32(__builtin_bit_cast(bf16x8_t, kf[st % (PFD + 1)]), qf[st / 2], S0);
+                else
+                    S1 = mfma32(__builtin_bit_cast(bf16x8_t, kf[st % (PFD + 1)]), qf[st / 2], S1);
+            }
+            if constexpr (st < NP) {
+                constexpr int kb = st / (2 * NDB), tt = (st / NDB) % 2, db = st % NDB;
+                constexpr int pq = kb * 8 + tt * 4;
+                const u32x4_t pv = {pk[pq], pk[pq + 1], pk[pq + 2], pk[pq + 3]};
+                O[db] = mfma32(__builtin_bit_cast(bf16x8_t, vf[st % (PFD + 1)]), __builtin_bit_cast(bf16x8_t, pv), O[db]);
+            }
+            constexpr int nrd = (st + PFD < NS ? 1 : 0) + (st + PFD < NP ? 2 : 0);
+            if constexpr (nrd > 0) __builtin_amdgcn_sched_group_barrier(0x100, nrd, 0);
+            __builtin_amdgcn_sched_group_barrier(0x008, (st < NS ? 1 : 0) + (st < NP ? 1 : 0), 0);
+        });
+        if (ATTN_PP_PRIO) __builtin_amdgcn_s_setprio(0);
+        __builtin_amdgcn_sched_barrier(0);
+    };
+
+    // ---- softmax phase of key tile j (scores S0/S1): masks, row maximum,
+    // the rare rescale, probabilities rounded to bf16 (pk) and the row sum
+    // of the rounded values; then this thread's staging share is written to
+    // LDS (K[j+2] into slot ksl, V[j+1] into slot vsl) and the next share's
+    // global loads are issued
+    auto vphase = [&](int j, int ksl, int vsl) __attribute__((always_inline)) {
+        const int k0 = j * kTK;
+        if (k0 + kTK - 1 > pw_lo) {
+            const int lim = pos - k0 - 4 * hf;
+#pragma unroll
+            for (int q = 0; q < 16; ++q) {
+                const int off = 8 * (q >> 2) + (q & 3);
+                if (off > lim) S0[q] = -INFINITY;
+                if (off + 32 > lim) S1[q] = -INFINITY;
+            }
+        }
+        if (WIN && k0 < win_lo) {
+            const int llim = pos - a.window + 1 - k0 - 4 * hf;
+#pragma unroll
+            for (int q = 0; q < 16; ++q) {
+                const int off = 8 * (q >> 2) + (q & 3);
+                if (off < llim) S0[q] = -INFINITY;
+                if (off + 32 < llim) S1[q] = -INFINITY;
+            }
+        }
+        float mx = fmaxf(S0[0], S1[0]);
+#pragma unroll
+        for (int q = 1; q < 16; ++q) mx = fmaxf(mx, fmaxf(S0[q], S1[q]));
+        if (ATTN_PP_PERMLANE) {
+            const auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(mx), __float_as_uint(mx), false, false);
+            mx = fmaxf(__uint_as_float(sw[0]), __uint_as_float(sw[1]));
+        } else {
+            mx = fmaxf(mx, __shfl_xor(mx, 32));
+        }
+        const float mt = mx * sl;
+        const bool grow = mt > m_run + kRescaleSlack;
+        const float m_new = grow ? mt : m_run;
+        const float m_use = m_new == -INFINITY ? 0.f : m_new;
+        if (__any(grow)) {
+            const float alpha = grow ? __builtin_amdgcn_exp2f(m_run - m_use) : 1.f;
+            l_run *= alpha;
+#pragma unroll
+            for (int db = 0; db < NDB; ++db)
+#pragma unroll
+                for (int q = 0; q < 16; ++q) O[db][q] *= alpha;
+        }
+        m_run = m_new;
+        const float nm = -m_use;
+#pragma unroll
+        for (int q = 0; q < 8; ++q)
+            pk[q] = pack_bf16x2(__builtin_amdgcn_exp2f(__builtin_fmaf(S0[2 * q], sl, nm)),
+                                __builtin_amdgcn_exp2f(__builtin_fmaf(S0[2 * q + 1], sl, nm)));
+#pragma unroll
+        for (int q = 0; q < 8; ++q)
+            pk[8 + q] = pack_bf16x2(__builtin_amdgcn_exp2f(__builtin_fmaf(S1[2 * q], sl, nm)),
+                                    __builtin_amdgcn_exp2f(__builtin_fmaf(S1[2 * q + 1], sl, nm)));
+        l_run += sum_bf16_pairs(pk);
+        // this thread's staging share, then the next share's global loads
+        // (unconditional, tile index clamped: past the last tile they refill
+        // slots that are never read again).  Measured: issuing them at the
+        // start of the phase, or reading the next matrix phase's first
+        // fragments here, is slower.
+        store_k(ksl);
+        store_v(vsl);
+        load_kv(min(j + 3, te - 1), min(j + 2, te - 1));
+    };
+
+    constexpr std::integral_constant<bool, true> yes{};
+    constexpr std::integral_constant<bool, false> no{};
+    const int n = te - tb;
+    if (n > 0) {
+        // prologue: K[tb], V[tb], K[tb+1] in slots 0, 0, 1; the staging
+        // registers then hold K[tb+2] and V[tb+1] for the first softmax phase
+        load_kv(tb, tb);
+        store_k(0);
+        store_v(0);
+        load_kv(min(tb + 1, te - 1), tb);
+        store_k(1);
+        load_kv(min(tb + 2, te - 1), min(tb + 1, te - 1));
+        __syncthreads();
+        if (grp == 1) __syncthreads();            // the second group starts one phase later
+        mphase(0, 0, yes, no);
+        __syncthreads();
+        // slots of tile tb+k: K and V in (k mod 3)
+        int sk = 0;                               // slot of key tile tb+k
+        for (int k = 0; k < n - 1; ++k) {
+            const int s1 = sk == 2 ? 0 : sk + 1, s2 = s1 == 2 ? 0 : s1 + 1;
+            vphase(tb + k, s2, s1);
+            __syncthreads();
+            mphase(s1, sk, yes, yes);
+            __syncthreads();
+            sk = s1;
+        }
+        {
+            const int s1 = sk == 2 ? 0 : sk + 1, s2 = s1 == 2 ? 0 : s1 + 1;
+            vphase(tb + n - 1, s2, s1);
+            __syncthreads();
+            mphase(s1, sk, no, yes);
+            __syncthreads();
+        }
+        if (grp == 0) __syncthreads();            // the same barrier count in both groups
+    }
+
+    const float l_tot = l_run + __shfl_xor(l_run, 32);
+    if (!row_ok) return;
+    write_row<HD>(a, O, m_run, l_tot, t, h, hf, nsp,
+                  a.part + ((size_t)item * TILE_ROWS + (r - r_tile0)) * part_row_words(HD));
 }
 
 // Key-split variant for 128-row work items: 8 waves, the waves w and w+4
@@ -975,83 +989,8 @@ __global__ __launch_bounds__(512, 1) void prefill_bf16_ks_kernel(PrefillArgs a) 
 
     const float l_tot = l_run + __shfl_xor(l_run, 32);
     if (!row_ok) return;
-    if (nsp <= 1) {
-        const float inv = 1.f / l_tot;
-        float* orow = a.out + ((size_t)t * a.n_heads + h) * HD;
-        if (a.gate.mode) {
-            // output gate: this lane's dims db*32 + 8*q4 + 4*hf + 0..3, all
-            // loads issued before any factor is formed
-            const size_t grow = (size_t)t * a.n_heads + h;
-            const uint16_t* gp = reinterpret_cast<const uint16_t*>(a.gate.p) + grow * (size_t)a.gate.ld;
-            if (a.gate.mode == kGateSoftplusHead) {
-                const float f = gate_fast(a.gate.mode, bf16_to_f32(gp[0])) * inv;
-#pragma unroll
-                for (int db = 0; db < NDB; ++db)
-#pragma unroll
-                    for (int q = 0; q < 16; ++q) O[db][q] *= f;
-            } else {
-                u32x2_t graw[NDB][4];
-                const bool vec = ((a.gate.ld & 3) == 0) && ((reinterpret_cast<uintptr_t>(a.gate.p) & 7) == 0);
-#pragma unroll
-                for (int db = 0; db < NDB; ++db)
-#pragma unroll
-                    for (int q4 = 0; q4 < 4; ++q4) {
-                        const uint16_t* p = gp + db * 32 + 8 * q4 + 4 * hf;
-                        if (vec) {
-                            graw[db][q4] = *reinterpret_cast<const u32x2_t*>(p);
-                        } else {
-                            graw[db][q4] = u32x2_t{(uint32_t)p[0] | ((uint32_t)p[1] << 16),
-                                                   (uint32_t)p[2] | ((uint32_t)p[3] << 16)};
-                        }
-                    }
-#pragma unroll
-                for (int db = 0; db < NDB; ++db)
-#pragma unroll
-                    for (int q4 = 0; q4 < 4; ++q4) {
-                        O[db][4 * q4] *= gate_fast(a.gate.mode, bf16_lo(graw[db][q4].x)) * inv;
-                        O[db][4 * q4 + 1] *= gate_fast(a.gate.mode, bf16_hi(graw[db][q4].x)) * inv;
-                        O[db][4 * q4 + 2] *= gate_fast(a.gate.mode, bf16_lo(graw[db][q4].y)) * inv;
-                        O[db][4 * q4 + 3] *= gate_fast(a.gate.mode, bf16_hi(graw[db][q4].y)) * inv;
-                    }
-            }
-        } else {
-#pragma unroll
-            for (int db = 0; db < NDB; ++db)
-#pragma unroll
-                for (int q = 0; q < 16; ++q) O[db][q] *= inv;
-        }
-#pragma unroll
-        for (int db = 0; db < NDB; ++db)
-#pragma unroll
-            for (int q4 = 0; q4 < 4; ++q4) {
-                const float4 v = make_float4(O[db][4 * q4], O[db][4 * q4 + 1], O[db][4 * q4 + 2],
-                                             O[db][4 * q4 + 3]);
-                *reinterpret_cast<float4*>(orow + db * 32 + 8 * q4 + 4 * hf) = v;
-            }
-    } else {
-        // partial of this item's row r - r_tile0: O/l in half precision
-        // (a part whose keys are all masked for the row has l = 0, O = 0)
-        float* pr = a.part + ((size_t)item * TILE_ROWS + (r - r_tile0)) * part_row_words(HD);
-        const float inv = l_tot > 0.f ? 1.f / l_tot : 0.f;
-        float mx = 0.f;
-#pragma unroll
-        for (int db = 0; db < NDB; ++db)
-#pragma unroll
-            for (int q = 0; q < 16; ++q) mx = fmaxf(mx, fabsf(O[db][q]));
-        mx = fmaxf(mx, __shfl_xor(mx, 32)) * inv;
-        const int ex = part_scale_exp(mx);
-        const float sc = __builtin_amdgcn_ldexpf(inv, -ex);
-        if (hf == 0) *reinterpret_cast<float4*>(pr) = make_float4(m_run, l_tot, (float)ex, 0.f);
-        uint32_t* ph = reinterpret_cast<uint32_t*>(pr + kPartHead);
-#pragma unroll
-        for (int db = 0; db < NDB; ++db)
-#pragma unroll
-            for (int q4 = 0; q4 < 4; ++q4) {
-                const u32x2_t v = {pack_f16x2(O[db][4 * q4] * sc, O[db][4 * q4 + 1] * sc),
-                                   pack_f16x2(O[db][4 * q4 + 2] * sc, O[db][4 * q4 + 3] * sc)};
-                *reinterpret_cast<u32x2_t*>(ph + (db * 32 + 8 * q4 + 4 * hf) / 2) = v;
-            }
-    }
+    write_row<HD>(a, O, m_run, l_tot, t, h, hf, nsp,
+                  a.part + ((size_t)item * TILE_ROWS + (r - r_tile0)) * part_row_words(HD));
 }
 
 // Merge split partials (m, l, O/l) of each row: m* = max m_s,
@@ -1175,12 +1114,6 @@ __global__ __launch_bounds__(256) void prefill_combine_kernel(PrefillArgs a) {
 #define ATTN_PREFILL_BIG_TILE_BLOCKS 512
 #endif
 constexpr int kBigTileBlocks = ATTN_PREFILL_BIG_TILE_BLOCKS;
-// 128-row work items run the key-split kernel (one 8-wave workgroup per CU)
-// rather than 4 waves over whole tiles (two workgroups per CU)
-#ifndef ATTN_PREFILL_KEY_SPLIT
-#define ATTN_PREFILL_KEY_SPLIT 1
-#endif
-constexpr bool kPrefillKeySplit = ATTN_PREFILL_KEY_SPLIT != 0;
 constexpr int kMaxSplitGroups = 64;      // (sequence, row tile) pairs: one per lane
 
 static int device_cus() {
@@ -1210,7 +1143,7 @@ PrefillPlan plan_prefill(int n_seq, int n_heads, int n_kv, int head_dim, int n_t
     p.table_bytes = 0;
     if (base < kBigTileBlocks && tiles > min_tiles_per_split(p.rows_per_tile) &&
         (long)n_seq * p.n_qtiles <= kMaxSplitGroups) {
-        const long slots = (long)device_cus() * (p.rows_per_tile == 256 || kPrefillKeySplit ? 1 : 2);
+        const long slots = device_cus();       // one 8-wave workgroup per CU
         const size_t table = ((size_t)n_seq * p.n_qtiles * 2 * sizeof(int) + 255) / 256 * 256;
         // items <= slots + one extra part per row tile (ceil) -- see split_schedule
         const size_t parts = (size_t)(slots + base) * p.rows_per_tile * part_row_words(head_dim) * sizeof(float);
@@ -1267,17 +1200,16 @@ PrefillPlan plan_prefill(int n_seq, int n_heads, int n_kv, int head_dim, int n_t
     return p;
 }
 
+// 256-row work items run the ping-pong kernel, 128-row ones the key-split
+// kernel; both are one 8-wave workgroup per CU
 template <bool WIN>
 static void launch_prefill_win(const PrefillArgs& a, dim3 grid, hipStream_t stream) {
     if (a.rows_per_tile == 256) {
-        if (a.head_dim == 128) prefill_bf16_kernel<128, 8, WIN><<<grid, dim3(512), 0, stream>>>(a);
-        else prefill_bf16_kernel<64, 8, WIN><<<grid, dim3(512), 0, stream>>>(a);
-    } else if (kPrefillKeySplit) {
+        if (a.head_dim == 128) prefill_pp_kernel<128, WIN><<<grid, dim3(512), 0, stream>>>(a);
+        else prefill_pp_kernel<64, WIN><<<grid, dim3(512), 0, stream>>>(a);
+    } else {
         if (a.head_dim == 128) prefill_bf16_ks_kernel<128, WIN><<<grid, dim3(512), 0, stream>>>(a);
         else prefill_bf16_ks_kernel<64, WIN><<<grid, dim3(512), 0, stream>>>(a);
-    } else {
-        if (a.head_dim == 128) prefill_bf16_kernel<128, 4, WIN><<<grid, dim3(256), 0, stream>>>(a);
-        else prefill_bf16_kernel<64, 4, WIN><<<grid, dim3(256), 0, stream>>>(a);
     }
 }
 
