@@ -18,7 +18,8 @@ LIB_PATH = os.path.join(HERE, "libattn.so")
 F32, BF16 = 0, 1
 NORM_NONE, NORM_W, NORM_1PW = 0, 1, 2
 _STATUS = {0: "ok", -1: "invalid argument", -2: "exceeds cache capacity",
-           -3: "unsupported configuration", -4: "device launch failed"}
+           -3: "unsupported configuration", -4: "device launch failed",
+           -5: "exceeds the library's static scratch"}
 
 _lib = None
 
@@ -58,6 +59,10 @@ def lib() -> ctypes.CDLL:
     L.attn_decode.argtypes = [vp, vp, vp, i, i, i, i, i, i, i, vp, i, f, i, vp, i, i, vp, vp, i, vp,
                               sz, vp]
     L.attn_decode_workspace_bytes.argtypes = [i, i, i, i, i]
+    if hasattr(L, "attn_decode_noalloc"):
+        L.attn_decode_noalloc.argtypes = [vp, vp, vp, i, i, i, i, i, i, i, vp, i, f, i, vp, i, i, vp,
+                                          vp, i, vp]
+        L.attn_decode_noalloc.restype = i
     L.attn_decode_importance.argtypes = [vp, i, i, i, vp, i, vp, i, i, vp]
     L.attn_decode_importance.restype = i
     L.attn_decode_workspace_bytes.restype = sz
@@ -254,6 +259,28 @@ def prefill_chunk(q: torch.Tensor, k_cache: torch.Tensor, v_cache: torch.Tensor,
 
 def decode_workspace_bytes(n_seq: int, n_heads: int, n_kv: int, head_dim: int, max_ctx: int) -> int:
     return int(lib().attn_decode_workspace_bytes(n_seq, n_heads, n_kv, head_dim, max_ctx))
+
+
+def decode_noalloc(q: torch.Tensor, k_cache: torch.Tensor, v_cache: torch.Tensor, ctx: torch.Tensor,
+                   max_ctx: int, scale: float, out: torch.Tensor, probs: torch.Tensor | None = None,
+                   window: int = 0, ring: bool = False, gate: torch.Tensor | None = None,
+                   gate_mode: int = GATE_NONE):
+    """decode() without a workspace: the library's static scratch holds the
+    split partials (calls that overlap on one GPU race on it)."""
+    n_seq, nh, hd = q.shape
+    n_seq_c, n_kv, cap, hd2 = k_cache.shape
+    assert hd2 == hd and n_seq_c >= n_seq and out.shape == (n_seq, nh, hd)
+    assert ctx.shape == (n_seq,) and ctx.dtype == torch.int32
+    ld = 0
+    if probs is not None:
+        assert probs.dim() == 3 and probs.shape[:2] == (n_seq, nh) and probs.dtype == torch.float32
+        ld = probs.shape[2]
+    st = lib().attn_decode_noalloc(
+        _dev(q, "q"), _dev(k_cache, "k_cache"), _dev(v_cache, "v_cache"), _dtype_code(q), n_seq,
+        nh, n_kv, hd, cap, int(ring), _dev(ctx, "ctx"), max_ctx, scale, window,
+        *_gate(gate, gate_mode, n_seq, nh, hd, q.dtype), _dev(out, "out"),
+        _dev(probs, "probs"), ld, _stream())
+    _check("attn_decode_noalloc", st)
 
 
 def decode_importance(probs: torch.Tensor, ctx: torch.Tensor, max_ctx: int, imp: torch.Tensor,

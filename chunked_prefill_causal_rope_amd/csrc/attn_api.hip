@@ -88,6 +88,7 @@ const char* attn_status_string(int status) {
         case ATTN_ECAPACITY: return "exceeds cache capacity";
         case ATTN_EUNSUPPORTED: return "unsupported configuration";
         case ATTN_EDEVICE: return "device launch failed";
+        case ATTN_ESCRATCH: return "exceeds the library's static scratch";
         default: return "unknown status";
     }
 }
@@ -387,7 +388,11 @@ size_t attn_decode_workspace_bytes(int n_seq, int n_heads, int n_kv, int head_di
     return decode_part_bytes(n_seq, n_heads, head_dim, decode_splits_full(max_ctx, n_heads / n_kv));
 }
 
-int attn_decode(const void* q, const void* k_cache, const void* v_cache, int dtype, int n_seq,
+}  // extern "C"
+
+namespace attn {
+
+int decode_impl(const void* q, const void* k_cache, const void* v_cache, int dtype, int n_seq,
                 int n_heads, int n_kv, int head_dim, int cap, int ring, const int32_t* ctx,
                 int max_ctx, float scale, int window, const void* gate, int gate_mode, int gate_ld,
                 float* out, float* probs, int probs_ld, void* workspace,
@@ -467,6 +472,24 @@ int attn_decode(const void* q, const void* k_cache, const void* v_cache, int dty
     a.n_q = 1;
     if ((long)n_seq * splits * n_kv > 0x7fffffffL) return ATTN_EINVAL;
     return status_of(attn::launch_decode_bf16(a, s));
+}
+
+size_t decode_min_workspace_bytes(int n_seq, int n_heads, int head_dim) {
+    return decode_part_bytes(n_seq, n_heads, head_dim, 1);
+}
+
+}  // namespace attn
+
+extern "C" {
+
+int attn_decode(const void* q, const void* k_cache, const void* v_cache, int dtype, int n_seq,
+                int n_heads, int n_kv, int head_dim, int cap, int ring, const int32_t* ctx,
+                int max_ctx, float scale, int window, const void* gate, int gate_mode, int gate_ld,
+                float* out, float* probs, int probs_ld, void* workspace,
+                size_t workspace_bytes, void* stream) {
+    return attn::decode_impl(q, k_cache, v_cache, dtype, n_seq, n_heads, n_kv, head_dim, cap, ring, ctx,
+                             max_ctx, scale, window, gate, gate_mode, gate_ld, out, probs, probs_ld,
+                             workspace, workspace_bytes, stream);
 }
 
 int attn_decode_importance(const float* probs, int n_seq, int n_heads, int probs_ld,

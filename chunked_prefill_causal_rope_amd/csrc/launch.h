@@ -112,6 +112,15 @@ int decode_key_span(int max_ctx, int window);
 int decode_part_limit(int group, bool probs);
 hipError_t launch_decode_bf16(const DecodeArgs& a, hipStream_t stream);
 
+// attn_decode with its workspace given explicitly (the C entry point and the
+// no-allocation variant share it); the smallest workspace it accepts for a
+// bf16 call (one part per row).
+int decode_impl(const void* q, const void* k_cache, const void* v_cache, int dtype, int n_seq, int n_heads,
+                int n_kv, int head_dim, int cap, int ring, const int32_t* ctx, int max_ctx, float scale,
+                int window, const void* gate, int gate_mode, int gate_ld, float* out, float* probs,
+                int probs_ld, void* workspace, size_t workspace_bytes, void* stream);
+size_t decode_min_workspace_bytes(int n_seq, int n_heads, int head_dim);
+
 // Per-position importance of a decode step: sum over heads of the
 // probabilities.
 struct ImportanceArgs {

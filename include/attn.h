@@ -68,7 +68,9 @@ typedef enum {
     ATTN_ECAPACITY = -2,   /* max_end (or max_ctx) exceeds the cache capacity */
     ATTN_EUNSUPPORTED = -3,/* head_dim not 64/128, unknown dtype, or a GQA
                               group wider than the kernel supports */
-    ATTN_EDEVICE = -4      /* a HIP launch failed (hipGetLastError) */
+    ATTN_EDEVICE = -4,     /* a HIP launch failed (hipGetLastError) */
+    ATTN_ESCRATCH = -5     /* the call needs more than the library's static
+                              scratch (attn_decode_noalloc only) */
 } attn_status;
 
 typedef enum {
@@ -304,6 +306,29 @@ int attn_decode(const void *q, const void *k_cache, const void *v_cache, int dty
  * one-part minimum attn_decode documents.
  */
 size_t attn_decode_workspace_bytes(int n_seq, int n_heads, int n_kv, int head_dim, int max_ctx);
+
+/*
+ * attn_decode for callers that cannot allocate device memory (code under
+ * HIP graph capture, tight serving loops, harnesses that forbid hipMalloc):
+ * the same computation, arguments and results as attn_decode, with the split
+ * partials in a static scratch array that the library holds on each GPU it
+ * runs on (ATTN_NOALLOC_SCRATCH_BYTES per GPU, kept until the process ends)
+ * instead of a caller workspace.  Nothing is allocated by the call.  The
+ * call uses as many key-range parts as fit in the scratch (the full split of
+ * attn_decode_workspace_bytes() when that fits, so the results equal
+ * attn_decode's with that workspace).  Every call on one GPU shares that
+ * GPU's scratch: calls that overlap on one GPU (different streams, or other
+ * threads) race on it and must be ordered by the caller.  No part of the
+ * scratch needs to start at zero.
+ * Errors: as attn_decode; ATTN_ESCRATCH (before any device call) when even
+ * one part per row does not fit: n_seq * n_heads * (2 * head_dim + 16)
+ * bytes above ATTN_NOALLOC_SCRATCH_BYTES.
+ */
+#define ATTN_NOALLOC_SCRATCH_BYTES (32u << 20)
+int attn_decode_noalloc(const void *q, const void *k_cache, const void *v_cache, int dtype, int n_seq,
+                        int n_heads, int n_kv, int head_dim, int cap, int ring, const int32_t *ctx,
+                        int max_ctx, float scale, int window, const void *gate, int gate_mode,
+                        int gate_ld, float *out, float *probs, int probs_ld, void *stream);
 
 /*
  * Importance of each cached position after a decode step ([ATT] the decode
