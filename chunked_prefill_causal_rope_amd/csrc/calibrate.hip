@@ -39,25 +39,28 @@ __global__ __launch_bounds__(256) void calib_mfma_kernel(int iters, float* out) 
     if (lane == 0) out[blockIdx.x * (blockDim.x / 64) + (threadIdx.x >> 6)] = s;
 }
 
-// Grid-stride read of n16 16-byte words with nontemporal loads, four in
-// flight per lane; the words are folded with xor and one value per wave is
-// written.
-__global__ __launch_bounds__(256) void calib_read_kernel(const u32x4_t* src, size_t n16, uint32_t* out) {
-    const size_t stride = (size_t)gridDim.x * blockDim.x;
-    size_t i = (size_t)blockIdx.x * blockDim.x + threadIdx.x;
+// Streaming read of n16 16-byte words: workgroup w reads its own contiguous
+// share (per_wg words), eight nontemporal loads in flight per lane; the
+// words are folded with xor and one value per wave is written.
+__global__ __launch_bounds__(256) void calib_read_kernel(const u32x4_t* src, size_t n16, size_t per_wg, uint32_t* out) {
+    const size_t b0 = (size_t)blockIdx.x * per_wg;
+    const size_t b1 = b0 + per_wg < n16 ? b0 + per_wg : n16;
     u32x4_t acc = {0u, 0u, 0u, 0u};
-    for (; i + 3 * stride < n16; i += 4 * stride) {
-        const u32x4_t x0 = __builtin_nontemporal_load(src + i);
-        const u32x4_t x1 = __builtin_nontemporal_load(src + i + stride);
-        const u32x4_t x2 = __builtin_nontemporal_load(src + i + 2 * stride);
-        const u32x4_t x3 = __builtin_nontemporal_load(src + i + 3 * stride);
-        acc ^= x0 ^ x1 ^ x2 ^ x3;
-    }
-    for (; i < n16; i += stride) acc ^= __builtin_nontemporal_load(src + i);
-    uint32_t v = acc.x ^ acc.y ^ acc.z ^ acc.w;
+    constexpr int U = 8;
+    for (size_t i = b0 + threadIdx.x; i < b1; i += 256 * U) {
+        u32x4_t v[U];
 #pragma unroll
-    for (int o = 32; o > 0; o >>= 1) v ^= __shfl_xor(v, o);
-    if ((threadIdx.x & 63) == 0) out[blockIdx.x * (blockDim.x / 64) + (threadIdx.x >> 6)] = v;
+        for (int u = 0; u < U; ++u) {
+            const size_t j = i + (size_t)u * 256;
+            v[u] = j < b1 ? __builtin_nontemporal_load(src + j) : u32x4_t{0u, 0u, 0u, 0u};
+        }
+#pragma unroll
+        for (int u = 0; u < U; ++u) acc ^= v[u];
+    }
+    uint32_t x = acc.x ^ acc.y ^ acc.z ^ acc.w;
+#pragma unroll
+    for (int o = 32; o > 0; o >>= 1) x ^= __shfl_xor(x, o);
+    if ((threadIdx.x & 63) == 0) out[blockIdx.x * (blockDim.x / 64) + (threadIdx.x >> 6)] = x;
 }
 
 }  // namespace attn
@@ -74,8 +77,9 @@ int attn_calibrate_read(const void* src, size_t bytes, int n_workgroups, uint32_
     if (!src || !out || n_workgroups <= 0 || bytes < 16 || (bytes & 15) ||
         (reinterpret_cast<uintptr_t>(src) & 15))
         return ATTN_EINVAL;
+    const size_t n16 = bytes / 16;
     attn::calib_read_kernel<<<dim3((unsigned)n_workgroups), dim3(256), 0, (hipStream_t)stream>>>(
-        static_cast<const attn::u32x4_t*>(src), bytes / 16, out);
+        static_cast<const attn::u32x4_t*>(src), n16, (n16 + n_workgroups - 1) / n_workgroups, out);
     return hipGetLastError() == hipSuccess ? ATTN_OK : ATTN_EDEVICE;
 }
 

@@ -371,6 +371,12 @@ struct PingPongSmem {
 // the row maximum's exchange between wave halves: v_permlane32_swap (vector
 // ALU) rather than an LDS permute, which waits behind the other group's
 // fragment reads
+#ifndef ATTN_PP_STAGE_DEPTH
+#define ATTN_PP_STAGE_DEPTH 2
+#endif
+#ifndef ATTN_PP_LATE_STORE
+#define ATTN_PP_LATE_STORE 1
+#endif
 #ifndef ATTN_PP_PERMLANE
 #define ATTN_PP_PERMLANE 1
 #endif
@@ -457,7 +463,10 @@ __global__ __launch_bounds__(512, 1) void prefill_pp_kernel(PrefillArgs a) {
     // staging: thread -> NCH (row, 16-byte chunk) pairs of a tile, buffer
     // loads from a resource over the tile's rows (rows past the last key
     // read as zeros: their scores are masked and their probabilities are 0)
-    u32x4_t kreg[NCH], vreg[NCH];
+    // SD staging sets: the loads a softmax phase stores were issued SD
+    // softmax phases (tiles) earlier
+    constexpr int SD = ATTN_PP_STAGE_DEPTH;
+    u32x4_t kreg[SD][NCH], vreg[SD][NCH];
     int voff[NCH], kls[NCH], vls[NCH];
 #pragma unroll
     for (int c = 0; c < NCH; ++c) {
@@ -473,24 +482,28 @@ __global__ __launch_bounds__(512, 1) void prefill_pp_kernel(PrefillArgs a) {
         return __builtin_amdgcn_make_buffer_rsrc((void*)(base + (size_t)jt * kTK * HD), (short)0, rows * HD * 2,
                                                  kBufferWord3);
     };
-    auto load_kv = [&](int jk, int jv) __attribute__((always_inline)) {
+    auto load_kv = [&](int jk, int jv, auto set) __attribute__((always_inline)) {
         const auto rk = tile_rsrc(kc, jk);
         const auto rv = tile_rsrc(vc, jv);
 #pragma unroll
         for (int c = 0; c < NCH; ++c)
-            kreg[c] = __builtin_bit_cast(u32x4_t, __builtin_amdgcn_raw_buffer_load_b128(rk, voff[c], 0, 0));
+            kreg[set.value][c] =
+                __builtin_bit_cast(u32x4_t, __builtin_amdgcn_raw_buffer_load_b128(rk, voff[c], 0, 0));
 #pragma unroll
         for (int c = 0; c < NCH; ++c)
-            vreg[c] = __builtin_bit_cast(u32x4_t, __builtin_amdgcn_raw_buffer_load_b128(rv, voff[c], 0, 0));
+            vreg[set.value][c] =
+                __builtin_bit_cast(u32x4_t, __builtin_amdgcn_raw_buffer_load_b128(rv, voff[c], 0, 0));
     };
-    auto store_k = [&](int slot) __attribute__((always_inline)) {
+    auto store_k = [&](int slot, auto set) __attribute__((always_inline)) {
 #pragma unroll
-        for (int c = 0; c < NCH; ++c) st16(&sm.k[slot][kls[c]], kreg[c]);
+        for (int c = 0; c < NCH; ++c) st16(&sm.k[slot][kls[c]], kreg[set.value][c]);
     };
-    auto store_v = [&](int slot) __attribute__((always_inline)) {
+    auto store_v = [&](int slot, auto set) __attribute__((always_inline)) {
 #pragma unroll
-        for (int c = 0; c < NCH; ++c) st16(&sm.v[slot][vls[c]], vreg[c]);
+        for (int c = 0; c < NCH; ++c) st16(&sm.v[slot][vls[c]], vreg[set.value][c]);
     };
+    constexpr std::integral_constant<int, 0> set0{};
+    constexpr std::integral_constant<int, SD - 1> set1{};
 
     // transposing-read address of this lane inside a V tile (see the
     // full-tile kernel)
@@ -577,7 +590,7 @@ __global__ __launch_bounds__(512, 1) void prefill_pp_kernel(PrefillArgs a) {
     // of the rounded values; then this thread's staging share is written to
     // LDS (K[j+2] into slot ksl, V[j+1] into slot vsl) and the next share's
     // global loads are issued
-    auto vphase = [&](int j, int ksl, int vsl) __attribute__((always_inline)) {
+    auto vphase = [&](int j, int ksl, int vsl, auto set) __attribute__((always_inline)) {
         const int k0 = j * kTK;
         if (k0 + kTK - 1 > pw_lo) {
             const int lim = pos - k0 - 4 * hf;
@@ -634,9 +647,10 @@ __global__ __launch_bounds__(512, 1) void prefill_pp_kernel(PrefillArgs a) {
         // slots that are never read again).  Measured: issuing them at the
         // start of the phase, or reading the next matrix phase's first
         // fragments here, is slower.
-        store_k(ksl);
-        store_v(vsl);
-        load_kv(min(j + 3, te - 1), min(j + 2, te - 1));
+        if (ATTN_PP_LATE_STORE) __builtin_amdgcn_sched_barrier(0);
+        store_k(ksl, set);
+        store_v(vsl, set);
+        load_kv(min(j + 2 + SD, te - 1), min(j + 1 + SD, te - 1), set);
     };
 
     constexpr std::integral_constant<bool, true> yes{};
@@ -644,33 +658,45 @@ __global__ __launch_bounds__(512, 1) void prefill_pp_kernel(PrefillArgs a) {
     const int n = te - tb;
     if (n > 0) {
         // prologue: K[tb], V[tb], K[tb+1] in slots 0, 0, 1; the staging
-        // registers then hold K[tb+2] and V[tb+1] for the first softmax phase
-        load_kv(tb, tb);
-        store_k(0);
-        store_v(0);
-        load_kv(min(tb + 1, te - 1), tb);
-        store_k(1);
-        load_kv(min(tb + 2, te - 1), min(tb + 1, te - 1));
+        // sets then hold K[tb+2+s] and V[tb+1+s] for the softmax phase s
+        load_kv(tb, tb, set0);
+        store_k(0, set0);
+        store_v(0, set0);
+        load_kv(min(tb + 1, te - 1), tb, set0);
+        store_k(1, set0);
+        load_kv(min(tb + 2, te - 1), min(tb + 1, te - 1), set0);
+        if (SD == 2) load_kv(min(tb + 3, te - 1), min(tb + 2, te - 1), set1);
         __syncthreads();
         if (grp == 1) __syncthreads();            // the second group starts one phase later
         mphase(0, 0, yes, no);
         __syncthreads();
-        // slots of tile tb+k: K and V in (k mod 3)
+        // slots of tile tb+k: K and V in (k mod 3); staging set k mod SD
         int sk = 0;                               // slot of key tile tb+k
-        for (int k = 0; k < n - 1; ++k) {
+        auto step = [&](int k, auto set) __attribute__((always_inline)) {
             const int s1 = sk == 2 ? 0 : sk + 1, s2 = s1 == 2 ? 0 : s1 + 1;
-            vphase(tb + k, s2, s1);
+            vphase(tb + k, s2, s1, set);
             __syncthreads();
             mphase(s1, sk, yes, yes);
             __syncthreads();
             sk = s1;
-        }
-        {
+        };
+        auto last = [&](auto set) __attribute__((always_inline)) {
             const int s1 = sk == 2 ? 0 : sk + 1, s2 = s1 == 2 ? 0 : s1 + 1;
-            vphase(tb + n - 1, s2, s1);
+            vphase(tb + n - 1, s2, s1, set);
             __syncthreads();
             mphase(s1, sk, no, yes);
             __syncthreads();
+        };
+        int k = 0;
+        for (; k + SD <= n - 1; k += SD) {
+            step(k, set0);
+            if (SD == 2) step(k + 1, set1);
+        }
+        if (SD == 2 && k < n - 1) {
+            step(k, set0);
+            last(set1);
+        } else {
+            last(set0);
         }
         if (grp == 0) __syncthreads();            // the same barrier count in both groups
     }

@@ -362,8 +362,8 @@ int attn_decode_importance(const float *probs, int n_seq, int n_heads, int probs
  *   out: device float[n_workgroups * 4], one value per wave, written.
  * attn_calibrate_read: a streaming read of `bytes` (a multiple of 16, src
  *   16-byte aligned) with nontemporal 16-byte loads by n_workgroups
- *   workgroups of 256 threads.  out: device uint32[n_workgroups * 4], one
- *   value per wave, written.
+ *   workgroups of 256 threads, each reading its own contiguous share.
+ *   out: device uint32[n_workgroups * 4], one value per wave, written.
  * The caller times the launch on `stream` (e.g. with events).  Errors: EINVAL
  * for non-positive sizes, NULL pointers, misaligned reads; EDEVICE.
  */
