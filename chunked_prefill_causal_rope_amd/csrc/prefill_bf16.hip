@@ -610,9 +610,15 @@ __global__ __launch_bounds__(512, 1) void prefill_pp_kernel(PrefillArgs a) {
                 if (off + 32 < llim) S1[q] = -INFINITY;
             }
         }
-        float mx = fmaxf(S0[0], S1[0]);
+        // 32 scores in 16 three-input maxima (two chains, joined at the end)
+        float mx0 = __builtin_fmaxf(__builtin_fmaxf(S0[0], S0[1]), S0[2]);
+        float mx1 = __builtin_fmaxf(__builtin_fmaxf(S1[0], S1[1]), S1[2]);
 #pragma unroll
-        for (int q = 1; q < 16; ++q) mx = fmaxf(mx, fmaxf(S0[q], S1[q]));
+        for (int q = 3; q < 15; q += 2) {
+            mx0 = __builtin_fmaxf(__builtin_fmaxf(mx0, S0[q]), S0[q + 1]);
+            mx1 = __builtin_fmaxf(__builtin_fmaxf(mx1, S1[q]), S1[q + 1]);
+        }
+        float mx = __builtin_fmaxf(__builtin_fmaxf(mx0, S0[15]), __builtin_fmaxf(mx1, S1[15]));
         if (ATTN_PP_PERMLANE) {
             const auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(mx), __float_as_uint(mx), false, false);
             mx = fmaxf(__uint_as_float(sw[0]), __uint_as_float(sw[1]));
