@@ -445,8 +445,8 @@ def bench_prefill(torch, w, args, stream):
     roof = {"bound": "mfma", "achieved": round(achieved, 2), "peak": PEAK_MFMA_BF16_TFLOPS,
             "unit": "TFLOP/s", "frac": round(achieved / PEAK_MFMA_BF16_TFLOPS, 4),
             "traffic": recorded_traffic(w.name),
-            # 256-row items run prefill_bf16_kernel, 128-row ones the key-split kernel
-            "kernel": "attn_prefill_chunk (prefill_bf16_kernel or prefill_bf16_ks_kernel"
+            # 256-row items run the ping-pong kernel, 128-row ones the key-split kernel
+            "kernel": "attn_prefill_chunk (prefill_pp_kernel or prefill_bf16_ks_kernel"
                       + (" + prefill_combine_kernel" if split_calls else "") + ")",
             "launches": n_steps, "avg_launch_ms": round(avg_ms, 4),
             "flop_per_launch": round(sum(flops) / n_steps), "split_calls": split_calls}
