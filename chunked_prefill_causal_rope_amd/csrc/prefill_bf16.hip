@@ -368,15 +368,19 @@ struct PingPongSmem {
 #ifndef ATTN_PP_PREFETCH
 #define ATTN_PP_PREFETCH 3
 #endif
-// the row maximum's exchange between wave halves: v_permlane32_swap (vector
-// ALU) rather than an LDS permute, which waits behind the other group's
-// fragment reads
+// staging register sets: one holds the global loads of the next tile's
+// share; a second (loads issued two softmax phases ahead) does not fit the
+// register budget of two waves per SIMD at a head dimension of 128 and spills
 #ifndef ATTN_PP_STAGE_DEPTH
-#define ATTN_PP_STAGE_DEPTH 2
+#define ATTN_PP_STAGE_DEPTH 1
 #endif
+// the staging share is written to LDS after the probabilities, not among them
 #ifndef ATTN_PP_LATE_STORE
 #define ATTN_PP_LATE_STORE 1
 #endif
+// the row maximum's exchange between wave halves: v_permlane32_swap (vector
+// ALU) rather than an LDS permute, which waits behind the other group's
+// fragment reads
 #ifndef ATTN_PP_PERMLANE
 #define ATTN_PP_PERMLANE 1
 #endif
