@@ -24,9 +24,23 @@ _STATUS = {0: "ok", -1: "invalid argument", -2: "exceeds cache capacity",
 _lib = None
 
 EXPORTS = ("attn_rope_inv_freq", "attn_yarn_inv_freq", "attn_rope_apply", "attn_kv_append",
-           "attn_rope_qkv", "attn_prefill_chunk", "attn_prefill_workspace_bytes", "attn_decode",
+           "attn_rope_qkv", "attn_prefill_chunk", "attn_prefill_chunk_rope_next",
+           "attn_prefill_workspace_bytes", "attn_decode",
            "attn_decode_workspace_bytes", "attn_decode_importance", "attn_calibrate_mfma",
            "attn_calibrate_read", "attn_status_string", "attn_version")
+
+
+class RopeQkvArgs(ctypes.Structure):
+    """attn_rope_qkv_args of attn.h (field for field)."""
+    _fields_ = [("q", ctypes.c_void_p), ("q_out", ctypes.c_void_p), ("n_heads", ctypes.c_int),
+                ("k_cache", ctypes.c_void_p), ("v_cache", ctypes.c_void_p), ("k_new", ctypes.c_void_p),
+                ("v_new", ctypes.c_void_p), ("n_kv", ctypes.c_int), ("cap", ctypes.c_int), ("ring", ctypes.c_int),
+                ("dtype", ctypes.c_int), ("n_tok", ctypes.c_int), ("head_dim", ctypes.c_int),
+                ("n_seq", ctypes.c_int), ("cu_seq", ctypes.c_void_p), ("start", ctypes.c_void_p),
+                ("max_chunk", ctypes.c_int), ("max_end", ctypes.c_int), ("inv_freq", ctypes.c_void_p),
+                ("rotary_dim", ctypes.c_int), ("rope_scale", ctypes.c_float), ("norm", ctypes.c_int),
+                ("q_norm_w", ctypes.c_void_p), ("k_norm_w", ctypes.c_void_p), ("eps", ctypes.c_double),
+                ("v_norm", ctypes.c_int)]
 
 
 class AttnError(RuntimeError):
@@ -54,6 +68,8 @@ def lib() -> ctypes.CDLL:
                                 f, i, vp, vp, d, i, vp]
     L.attn_prefill_chunk.argtypes = [vp, vp, vp, i, i, i, i, i, i, i, i, vp, vp, i, i, f, i, vp, i,
                                      i, vp, vp, sz, vp]
+    L.attn_prefill_chunk_rope_next.argtypes = [vp, vp, vp, i, i, i, i, i, i, i, i, vp, vp, i, i, f, i,
+                                               vp, i, i, vp, vp, sz, ctypes.POINTER(RopeQkvArgs), vp]
     L.attn_prefill_workspace_bytes.argtypes = [i, i, i, i, i, i, i]
     L.attn_prefill_workspace_bytes.restype = sz
     L.attn_decode.argtypes = [vp, vp, vp, i, i, i, i, i, i, i, vp, i, f, i, vp, i, i, vp, vp, i, vp,
@@ -74,7 +90,7 @@ def lib() -> ctypes.CDLL:
     L.attn_status_string.restype = ctypes.c_char_p
     L.attn_version.restype = ctypes.c_char_p
     for name in ("attn_rope_inv_freq", "attn_yarn_inv_freq", "attn_rope_apply", "attn_kv_append",
-                 "attn_rope_qkv", "attn_prefill_chunk", "attn_decode"):
+                 "attn_rope_qkv", "attn_prefill_chunk", "attn_prefill_chunk_rope_next", "attn_decode"):
         getattr(L, name).restype = i
     _lib = L
     return L
@@ -214,21 +230,28 @@ def rope_qkv(q: torch.Tensor, q_out: torch.Tensor, k_cache: torch.Tensor, v_cach
              q_norm_w: torch.Tensor | None = None, k_norm_w: torch.Tensor | None = None,
              eps: float = 1e-6, ring: bool = False, v_norm: bool = False):
     """rope_apply(q -> q_out) and kv_append(k_new, v_new) of one chunk in one call."""
+    st = lib().attn_rope_qkv(*_rope_qkv_args(q, q_out, k_cache, v_cache, k_new, v_new, batch, inv_freq,
+                                             rotary_dim, rope_scale, norm, q_norm_w, k_norm_w, eps, ring,
+                                             v_norm), _stream())
+    _check("attn_rope_qkv", st)
+
+
+def _rope_qkv_args(q, q_out, k_cache, v_cache, k_new, v_new, batch, inv_freq, rotary_dim, rope_scale,
+                   norm, q_norm_w, k_norm_w, eps, ring, v_norm) -> tuple:
+    """attn_rope_qkv's arguments (without the stream), in attn.h's order."""
     n_tok, n_heads, hd = q.shape
     assert q_out.shape == q.shape and q_out.dtype == q.dtype and n_tok >= batch.n_tok
     n_seq_c, n_kv, cap, hd2 = k_cache.shape
     assert hd2 == hd and v_cache.shape == k_cache.shape and n_seq_c >= batch.n_seq
     assert k_new.shape == (n_tok, n_kv, hd) and v_new.shape == k_new.shape
     assert k_new.dtype == k_cache.dtype == v_cache.dtype == v_new.dtype == q.dtype
-    st = lib().attn_rope_qkv(
-        _dev(q, "q"), _dev(q_out, "q_out"), n_heads, _dev(k_cache, "k_cache"),
-        _dev(v_cache, "v_cache"), _dev(k_new, "k_new"), _dev(v_new, "v_new"), n_kv, cap,
-        int(ring), _dtype_code(q), n_tok, hd, batch.n_seq, _dev(batch.cu_seq, "cu_seq", torch.int32),
-        _dev(batch.start, "start", torch.int32), batch.max_chunk, batch.max_end,
-        _dev(inv_freq, "inv_freq", torch.float32) if rotary_dim else None, rotary_dim,
-        rope_scale, norm, _dev(q_norm_w, "q_norm_w", torch.float32),
-        _dev(k_norm_w, "k_norm_w", torch.float32), eps, int(v_norm), _stream())
-    _check("attn_rope_qkv", st)
+    return (_dev(q, "q"), _dev(q_out, "q_out"), n_heads, _dev(k_cache, "k_cache"),
+            _dev(v_cache, "v_cache"), _dev(k_new, "k_new"), _dev(v_new, "v_new"), n_kv, cap,
+            int(ring), _dtype_code(q), n_tok, hd, batch.n_seq, _dev(batch.cu_seq, "cu_seq", torch.int32),
+            _dev(batch.start, "start", torch.int32), batch.max_chunk, batch.max_end,
+            _dev(inv_freq, "inv_freq", torch.float32) if rotary_dim else None, rotary_dim,
+            rope_scale, norm, _dev(q_norm_w, "q_norm_w", torch.float32),
+            _dev(k_norm_w, "k_norm_w", torch.float32), eps, int(v_norm))
 
 
 def prefill_workspace_bytes(batch: Batch, n_heads: int, n_kv: int, head_dim: int) -> int:
@@ -239,22 +262,31 @@ def prefill_workspace_bytes(batch: Batch, n_heads: int, n_kv: int, head_dim: int
 def prefill_chunk(q: torch.Tensor, k_cache: torch.Tensor, v_cache: torch.Tensor, batch: Batch,
                   scale: float, out: torch.Tensor, workspace: torch.Tensor | None = None,
                   window: int = 0, ring: bool = False, gate: torch.Tensor | None = None,
-                  gate_mode: int = GATE_NONE):
+                  gate_mode: int = GATE_NONE, next_rope: dict | None = None):
     """Causal attention of a chunk batch; window > 0 keeps keys p-window+1..p;
     ring=True reads key j from cache row j mod cap; gate/gate_mode gate the
-    output rows."""
+    output rows.  next_rope: rope_qkv's keyword arguments for the next chunk,
+    run by this call (attn_prefill_chunk_rope_next)."""
     n_tok, nh, hd = q.shape
     n_seq_c, n_kv, cap, hd2 = k_cache.shape
     assert hd2 == hd and out.shape == (n_tok, nh, hd) and out.dtype == torch.float32
     assert n_seq_c >= batch.n_seq and n_tok >= batch.n_tok
     ws = _dev(workspace, "workspace") if workspace is not None else None
     wsb = workspace.numel() * workspace.element_size() if workspace is not None else 0
-    st = lib().attn_prefill_chunk(
-        _dev(q, "q"), _dev(k_cache, "k_cache"), _dev(v_cache, "v_cache"), _dtype_code(q),
-        batch.n_seq, nh, n_kv, hd, cap, int(ring), n_tok, _dev(batch.cu_seq, "cu_seq", torch.int32),
-        _dev(batch.start, "start", torch.int32), batch.max_chunk, batch.max_end, scale, window,
-        *_gate(gate, gate_mode, n_tok, nh, hd, q.dtype), _dev(out, "out"), ws, wsb, _stream())
-    _check("attn_prefill_chunk", st)
+    args = (_dev(q, "q"), _dev(k_cache, "k_cache"), _dev(v_cache, "v_cache"), _dtype_code(q),
+            batch.n_seq, nh, n_kv, hd, cap, int(ring), n_tok, _dev(batch.cu_seq, "cu_seq", torch.int32),
+            _dev(batch.start, "start", torch.int32), batch.max_chunk, batch.max_end, scale, window,
+            *_gate(gate, gate_mode, n_tok, nh, hd, q.dtype), _dev(out, "out"), ws, wsb)
+    if next_rope is None:
+        _check("attn_prefill_chunk", lib().attn_prefill_chunk(*args, _stream()))
+        return
+    nr = dict(next_rope)
+    nxt = RopeQkvArgs(*_rope_qkv_args(
+        nr["q"], nr["q_out"], nr["k_cache"], nr["v_cache"], nr["k_new"], nr["v_new"], nr["batch"],
+        nr["inv_freq"], nr["rotary_dim"], nr.get("rope_scale", 1.0), nr.get("norm", NORM_NONE),
+        nr.get("q_norm_w"), nr.get("k_norm_w"), nr.get("eps", 1e-6), nr.get("ring", False),
+        nr.get("v_norm", False)))
+    _check("attn_prefill_chunk_rope_next", lib().attn_prefill_chunk_rope_next(*args, ctypes.byref(nxt), _stream()))
 
 
 def decode_workspace_bytes(n_seq: int, n_heads: int, n_kv: int, head_dim: int, max_ctx: int) -> int:

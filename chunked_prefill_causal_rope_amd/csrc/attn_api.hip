@@ -9,6 +9,11 @@
 #include "../../include/attn.h"
 #include "launch.h"
 
+// 0: the next chunk's finish always runs as its own launch (timing builds)
+#ifndef ATTN_FUSE_NEXT
+#define ATTN_FUSE_NEXT 1
+#endif
+
 namespace {
 
 // a decode partial row: 4 header floats, then head_dim halves
@@ -195,12 +200,19 @@ int attn_kv_append(void* k_cache, void* v_cache, int dtype, int n_seq, int n_kv,
     return status_of(attn::launch_rope_rows(a, dtype, true, (hipStream_t)stream));
 }
 
-int attn_rope_qkv(const void* q, void* q_out, int n_heads, void* k_cache, void* v_cache,
-                  const void* k_new, const void* v_new, int n_kv, int cap, int ring, int dtype, int n_tok,
-                  int head_dim, int n_seq, const int32_t* cu_seq, const int32_t* start, int max_chunk,
-                  int max_end, const float* inv_freq, int rotary_dim, float rope_scale, int norm,
-                  const float* q_norm_w, const float* k_norm_w, double eps, int v_norm,
-                  void* stream) {
+}  // extern "C"
+
+namespace {
+
+// Validation and launch arguments of attn_rope_qkv; *empty when the call has
+// no work (and nothing to launch).
+int rope_qkv_build(const void* q, void* q_out, int n_heads, void* k_cache, void* v_cache,
+                   const void* k_new, const void* v_new, int n_kv, int cap, int ring, int dtype, int n_tok,
+                   int head_dim, int n_seq, const int32_t* cu_seq, const int32_t* start, int max_chunk,
+                   int max_end, const float* inv_freq, int rotary_dim, float rope_scale, int norm,
+                   const float* q_norm_w, const float* k_norm_w, double eps, int v_norm,
+                   attn::RopeArgs& aq, attn::RopeArgs& ak, bool& empty) {
+    empty = true;
     int st = check_rope(dtype, n_tok, n_heads, head_dim, n_seq, cu_seq, start, max_chunk, inv_freq,
                         rotary_dim, norm, q_norm_w);
     if (st != ATTN_OK) return st;
@@ -213,13 +225,14 @@ int attn_rope_qkv(const void* q, void* q_out, int n_heads, void* k_cache, void* 
     if (ring && max_end > cap && max_chunk > cap) return ATTN_ECAPACITY;   // as attn_kv_append
     if (n_seq == 0 || n_tok == 0 || max_chunk == 0) return ATTN_OK;
     if (!q || !q_out || !k_cache || !v_cache || !k_new || !v_new) return ATTN_EINVAL;
-    attn::RopeArgs aq{};
+    empty = false;
+    aq = attn::RopeArgs{};
     aq.x = q;
     aq.y = q_out;
     aq.norm_w = q_norm_w;
     aq.n_heads = n_heads;
     aq.cap = 0;
-    attn::RopeArgs ak{};
+    ak = attn::RopeArgs{};
     ak.x = k_new;
     ak.y = k_cache;
     ak.v_src = v_new;
@@ -242,6 +255,39 @@ int attn_rope_qkv(const void* q, void* q_out, int n_heads, void* k_cache, void* 
         a->rotary_dim = rotary_dim < head_dim ? rotary_dim : head_dim;
         a->norm = norm;
     }
+    return ATTN_OK;
+}
+
+// The next chunk's finish, when it rides in a prefill launch.
+struct NextFinish {
+    const attn::RopeArgs* q;
+    const attn::RopeArgs* kv;
+    int dtype;
+};
+
+int prefill_chunk_impl(const void* q, const void* k_cache, const void* v_cache, int dtype,
+                       int n_seq, int n_heads, int n_kv, int head_dim, int cap, int ring, int n_tok,
+                       const int32_t* cu_seq, const int32_t* start, int max_chunk, int max_end,
+                       float scale, int window, const void* gate, int gate_mode, int gate_ld,
+                       float* out, void* workspace, size_t workspace_bytes, const NextFinish* next,
+                       hipStream_t s);
+
+}  // namespace
+
+extern "C" {
+
+int attn_rope_qkv(const void* q, void* q_out, int n_heads, void* k_cache, void* v_cache,
+                  const void* k_new, const void* v_new, int n_kv, int cap, int ring, int dtype, int n_tok,
+                  int head_dim, int n_seq, const int32_t* cu_seq, const int32_t* start, int max_chunk,
+                  int max_end, const float* inv_freq, int rotary_dim, float rope_scale, int norm,
+                  const float* q_norm_w, const float* k_norm_w, double eps, int v_norm,
+                  void* stream) {
+    attn::RopeArgs aq, ak;
+    bool empty;
+    const int st = rope_qkv_build(q, q_out, n_heads, k_cache, v_cache, k_new, v_new, n_kv, cap, ring, dtype,
+                                  n_tok, head_dim, n_seq, cu_seq, start, max_chunk, max_end, inv_freq,
+                                  rotary_dim, rope_scale, norm, q_norm_w, k_norm_w, eps, v_norm, aq, ak, empty);
+    if (st != ATTN_OK || empty) return st;
     return status_of(attn::launch_rope_qkv(aq, ak, dtype, (hipStream_t)stream));
 }
 
@@ -265,6 +311,49 @@ int attn_prefill_chunk(const void* q, const void* k_cache, const void* v_cache, 
                        const int32_t* cu_seq, const int32_t* start, int max_chunk, int max_end,
                        float scale, int window, const void* gate, int gate_mode, int gate_ld,
                        float* out, void* workspace, size_t workspace_bytes, void* stream) {
+    return prefill_chunk_impl(q, k_cache, v_cache, dtype, n_seq, n_heads, n_kv, head_dim, cap, ring, n_tok,
+                              cu_seq, start, max_chunk, max_end, scale, window, gate, gate_mode, gate_ld, out,
+                              workspace, workspace_bytes, nullptr, (hipStream_t)stream);
+}
+
+int attn_prefill_chunk_rope_next(const void* q, const void* k_cache, const void* v_cache, int dtype,
+                                 int n_seq, int n_heads, int n_kv, int head_dim, int cap, int ring, int n_tok,
+                                 const int32_t* cu_seq, const int32_t* start, int max_chunk, int max_end,
+                                 float scale, int window, const void* gate, int gate_mode, int gate_ld,
+                                 float* out, void* workspace, size_t workspace_bytes,
+                                 const attn_rope_qkv_args* next, void* stream) {
+    if (!next) return ATTN_EINVAL;
+    attn::RopeArgs aq, ak;
+    bool empty;
+    const int st = rope_qkv_build(next->q, next->q_out, next->n_heads, next->k_cache, next->v_cache, next->k_new,
+                                  next->v_new, next->n_kv, next->cap, next->ring, next->dtype, next->n_tok,
+                                  next->head_dim, next->n_seq, next->cu_seq, next->start, next->max_chunk,
+                                  next->max_end, next->inv_freq, next->rotary_dim, next->rope_scale, next->norm,
+                                  next->q_norm_w, next->k_norm_w, next->eps, next->v_norm, aq, ak, empty);
+    if (st != ATTN_OK) return st;
+    const NextFinish nf{&aq, &ak, next->dtype};
+    return prefill_chunk_impl(q, k_cache, v_cache, dtype, n_seq, n_heads, n_kv, head_dim, cap, ring, n_tok,
+                              cu_seq, start, max_chunk, max_end, scale, window, gate, gate_mode, gate_ld, out,
+                              workspace, workspace_bytes, empty ? nullptr : &nf, (hipStream_t)stream);
+}
+
+size_t attn_decode_workspace_bytes(int n_seq, int n_heads, int n_kv, int head_dim, int max_ctx) {
+    if (n_seq <= 0 || n_heads <= 0 || n_kv <= 0 || n_heads % n_kv || max_ctx <= 0 ||
+        !hd_ok(head_dim))
+        return 0;
+    return decode_part_bytes(n_seq, n_heads, head_dim, decode_splits_full(max_ctx, n_heads / n_kv));
+}
+
+}  // extern "C"
+
+namespace {
+
+int prefill_chunk_impl(const void* q, const void* k_cache, const void* v_cache, int dtype,
+                       int n_seq, int n_heads, int n_kv, int head_dim, int cap, int ring, int n_tok,
+                       const int32_t* cu_seq, const int32_t* start, int max_chunk, int max_end,
+                       float scale, int window, const void* gate, int gate_mode, int gate_ld,
+                       float* out, void* workspace, size_t workspace_bytes, const NextFinish* next,
+                       hipStream_t s) {
     if (!dtype_ok(dtype) || !hd_ok(head_dim)) return ATTN_EUNSUPPORTED;
     if (n_seq < 0 || n_tok < 0 || max_chunk < 0 || max_end < 0 || n_heads <= 0 || n_kv <= 0 ||
         cap <= 0 || n_heads % n_kv != 0 || !isfinite(scale) || window < 0 || (ring != 0 && ring != 1))
@@ -277,11 +366,16 @@ int attn_prefill_chunk(const void* q, const void* k_cache, const void* v_cache, 
     if (wrapped && (window <= 0 || (long)window + max_chunk - 1 > cap)) return ATTN_ECAPACITY;
     if (wrapped && dtype == ATTN_BF16 && cap % 64 != 0) return ATTN_EUNSUPPORTED;
     if (!gate_ok(gate, gate_mode, gate_ld, head_dim)) return ATTN_EINVAL;
-    if (n_seq == 0 || n_tok == 0 || max_chunk == 0) return ATTN_OK;
+    // after validation, nothing but the launches can fail: the next chunk's
+    // finish runs after this chunk's attention unless it rides in its launch
+    auto finish_next = [&](hipError_t e) {
+        if (e == hipSuccess && next) e = attn::launch_rope_qkv(*next->q, *next->kv, next->dtype, s);
+        return status_of(e);
+    };
+    if (n_seq == 0 || n_tok == 0 || max_chunk == 0) return finish_next(hipSuccess);
     const attn::GateRef gref{gate, gate_mode, gate_ld, dtype == ATTN_BF16};
     if (!q || !k_cache || !v_cache || !out || !cu_seq || !start) return ATTN_EINVAL;
     if (n_seq > 65535) return ATTN_EINVAL;
-    hipStream_t s = (hipStream_t)stream;
     const int group = n_heads / n_kv;
     if (dtype == ATTN_F32) {
         attn::AttendF32Args a{};
@@ -304,7 +398,7 @@ int attn_prefill_chunk(const void* q, const void* k_cache, const void* v_cache, 
         a.window = window;
         a.ring = wrapped;
         a.gate = gref;
-        return status_of(attn::launch_attend_f32(a, s));
+        return finish_next(attn::launch_attend_f32(a, s));
     }
     if (small_chunk(max_chunk, group) && workspace &&
         workspace_bytes >= decode_part_bytes(n_seq * max_chunk, n_heads, head_dim, 1)) {
@@ -341,7 +435,7 @@ int attn_prefill_chunk(const void* q, const void* k_cache, const void* v_cache, 
         d.cu_seq = cu_seq;
         d.start = start;
         d.n_q = max_chunk;
-        return status_of(attn::launch_decode_bf16(d, s));
+        return finish_next(attn::launch_decode_bf16(d, s));
     }
     attn::PrefillArgs a{};
     a.q = q;
@@ -376,19 +470,33 @@ int attn_prefill_chunk(const void* q, const void* k_cache, const void* v_cache, 
     a.part = plan.split ? (float*)((char*)workspace + plan.table_bytes) : nullptr;
     const long blocks = (long)n_seq * a.n_qtiles * n_kv;
     if (blocks > 0x7fffffffL) return ATTN_EINVAL;
+    // the next chunk's finish rides in this launch on the per-token path
+    // (bf16, the same head size, neither cache wrapped): one workgroup of 512
+    // threads per (token, block of 512 / (head_dim / 8) head rows, sequence).
+    // Those workgroups carry the attention kernel's registers and LDS, one per
+    // CU, so only a finish that fits one such wave rides along (measured: a
+    // 128-token chunk of 40 heads, 256 workgroups, gains 10 % per step; 2048 or
+    // 4096 of them lose 1-3 % against the standalone launch's small workgroups)
+    bool fuse = ATTN_FUSE_NEXT && next && next->dtype == ATTN_BF16 && next->q->head_dim == head_dim &&
+                attn::rope_token_path(*next->q) && !next->kv->ring && !wrapped;
+    if (fuse) {
+        const int nhb_rows = 512 / (head_dim / 8);
+        const int nhb = (next->q->n_heads + next->kv->n_heads + nhb_rows - 1) / nhb_rows;
+        const long nb = (long)next->q->max_chunk * nhb * next->q->n_seq;
+        fuse = nb <= attn::device_cus();
+        if (fuse) {
+            a.next = attn::rope_token_args(*next->q, *next->kv);
+            a.next_chunk = next->q->max_chunk;
+            a.next_nhb = nhb;
+            a.next_blocks = (int)nb;
+        }
+    }
     hipError_t e = attn::launch_prefill_bf16(a, s);
     if (e == hipSuccess && plan.split) e = attn::launch_prefill_combine(a, s);
-    return status_of(e);
+    return fuse ? status_of(e) : finish_next(e);
 }
 
-size_t attn_decode_workspace_bytes(int n_seq, int n_heads, int n_kv, int head_dim, int max_ctx) {
-    if (n_seq <= 0 || n_heads <= 0 || n_kv <= 0 || n_heads % n_kv || max_ctx <= 0 ||
-        !hd_ok(head_dim))
-        return 0;
-    return decode_part_bytes(n_seq, n_heads, head_dim, decode_splits_full(max_ctx, n_heads / n_kv));
-}
-
-}  // extern "C"
+}  // namespace
 
 namespace attn {
 

@@ -31,6 +31,32 @@ hipError_t launch_rope_rows(const RopeArgs& a, int dtype, bool kv, hipStream_t s
 // few launches as the layout allows.
 hipError_t launch_rope_qkv(const RopeArgs& q, const RopeArgs& kv, int dtype, hipStream_t stream);
 
+// One launch can finish a token's query heads (token-major, written to qy)
+// and its key heads (into the cache, values copied alongside): "virtual"
+// heads 0..nq-1 are the queries, nq..nq+nk-1 the keys.
+struct RopeTokArgs {
+    const void* qx;
+    void* qy;
+    const float* qw;
+    int nq;
+    const void* kx;
+    const void* vx;
+    void* kc;
+    void* vc;
+    const float* kw;
+    int nk;
+    const int32_t* cu_seq;
+    const int32_t* start;
+    const float* inv_freq;
+    double eps;
+    float rope_scale;
+    int n_tok, cap, rotary_dim, norm, ring, v_norm;
+};
+// The per-token path serves rotary_dim % 8 == 0 at head_dim 64 or 128; its
+// arguments for a chunk's queries q and keys/values kv.
+bool rope_token_path(const RopeArgs& a);
+RopeTokArgs rope_token_args(const RopeArgs& q, const RopeArgs& kv);
+
 // Causal attention of packed chunk rows over the head-major cache.
 struct PrefillArgs {
     const void* q;
@@ -50,6 +76,12 @@ struct PrefillArgs {
     // grid with device-chosen key-range parts, merged by the combine kernel)
     int rows_per_tile, n_qtiles, split, grid, slots;
     int part_tiles;        // split calls: part length chosen on the host (0: on the device)
+    // the next chunk's finish (bf16, per-token path), run by next_blocks
+    // workgroups past the attention grid: workgroup grid + r takes token
+    // r % next_chunk, head-row block (r / next_chunk) % next_nhb, sequence
+    // r / (next_chunk * next_nhb)
+    RopeTokArgs next;
+    int next_blocks, next_chunk, next_nhb;
 };
 // Launch plan of the bf16 prefill, from host scalars only: query rows per
 // workgroup (128 or 256), row tiles, whether to split, grid, workspace.
@@ -60,6 +92,8 @@ struct PrefillPlan {
 PrefillPlan plan_prefill(int n_seq, int n_heads, int n_kv, int head_dim, int n_tok, int max_chunk,
                          int max_end, int window, size_t ws_available);
 hipError_t launch_prefill_bf16(const PrefillArgs& a, hipStream_t stream);
+// compute units of the current device (256 if the query fails)
+int device_cus();
 hipError_t launch_prefill_combine(const PrefillArgs& a, hipStream_t stream);
 
 // float32 path (prefill rows and decode rows) -- vector ALU, one wave per row.

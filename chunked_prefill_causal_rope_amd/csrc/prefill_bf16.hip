@@ -44,6 +44,7 @@
 
 #include "device_common.h"
 #include "launch.h"
+#include "rope_token.h"
 
 namespace attn {
 
@@ -59,7 +60,7 @@ __host__ __device__ constexpr int part_row_words(int hd) { return kPartHead + hd
 constexpr float kRescaleSlack = 8.f;
 
 template <int HD>
-struct PrefillSmem {
+struct alignas(16) PrefillSmem {
     // K rows padded by 16 B: the 32 rows of an A-operand read start on
     // distinct 4-bank groups.  V rows padded by 64 B: the 8 rows of a
     // transposing read (4 keys per 16-lane group, two groups per half-wave)
@@ -354,7 +355,7 @@ __device__ __forceinline__ void write_row(const PrefillArgs& a, f32x16_t (&O)[HD
 // tile two (K) or one (V) before it, and is overwritten only after both
 // wave groups have left the phase that reads it.
 template <int HD>
-struct PingPongSmem {
+struct alignas(16) PingPongSmem {
     static constexpr int KS = HD + 8;
     static constexpr int VS = HD + 32;
     uint16_t k[3][kTK * KS];
@@ -385,6 +386,20 @@ struct PingPongSmem {
 #define ATTN_PP_PERMLANE 1
 #endif
 
+// Workgroups past the attention grid finish the next chunk's rows (RoPE and
+// cache append), using the kernel's LDS for the token's tables.  The next
+// chunk writes cache rows past every key this chunk reads, so the two are
+// independent.
+template <int HD, typename Sm>
+__device__ __forceinline__ void next_chunk_role(const PrefillArgs& a, Sm& sm) {
+    static_assert(sizeof(RopeTokSmem<HD>) <= sizeof(Sm), "token tables fit the attention LDS");
+    const int r = blockIdx.x - a.grid;
+    const int i = r % a.next_chunk;
+    const int hb = (r / a.next_chunk) % a.next_nhb;
+    const int b = r / (a.next_chunk * a.next_nhb);
+    rope_token_body<uint16_t, HD, 512>(a.next, i, hb, b, reinterpret_cast<RopeTokSmem<HD>&>(sm));
+}
+
 template <int HD, bool WIN>
 __global__ __launch_bounds__(512, 1) void prefill_pp_kernel(PrefillArgs a) {
     using Sm = PingPongSmem<HD>;
@@ -397,6 +412,10 @@ __global__ __launch_bounds__(512, 1) void prefill_pp_kernel(PrefillArgs a) {
     constexpr int NKK = HD / 16;                  // K-steps of a score product
     constexpr int TILE_ROWS = 256;                // query rows per workgroup
     __shared__ Sm sm;
+    if (blockIdx.x >= a.grid) {
+        next_chunk_role<HD>(a, sm);
+        return;
+    }
 
     const int tid = threadIdx.x;
     const int lane = tid & 63;
@@ -738,6 +757,10 @@ __global__ __launch_bounds__(512, 1) void prefill_bf16_ks_kernel(PrefillArgs a) 
     constexpr int NKK = HD / 16;                  // K-steps of a score product
     constexpr int TILE_ROWS = 128;                // query rows per workgroup
     __shared__ Sm sm;
+    if (blockIdx.x >= a.grid) {
+        next_chunk_role<HD>(a, sm);
+        return;
+    }
 
     const int tid = threadIdx.x;
     const int lane = tid & 63;
@@ -1152,7 +1175,7 @@ __global__ __launch_bounds__(256) void prefill_combine_kernel(PrefillArgs a) {
 constexpr int kBigTileBlocks = ATTN_PREFILL_BIG_TILE_BLOCKS;
 constexpr int kMaxSplitGroups = 64;      // (sequence, row tile) pairs: one per lane
 
-static int device_cus() {
+int device_cus() {
     int dev = 0, cus = 0;
     if (hipGetDevice(&dev) != hipSuccess ||
         hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cus <= 0)
@@ -1250,7 +1273,7 @@ static void launch_prefill_win(const PrefillArgs& a, dim3 grid, hipStream_t stre
 }
 
 hipError_t launch_prefill_bf16(const PrefillArgs& a, hipStream_t stream) {
-    const long blocks = a.grid;
+    const long blocks = (long)a.grid + a.next_blocks;
     if (blocks <= 0) return hipSuccess;
     const dim3 grid((unsigned)blocks);
     if (a.window > 0)

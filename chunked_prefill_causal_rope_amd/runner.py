@@ -84,14 +84,20 @@ class ChunkedPrefill:
         ws = max(api.prefill_workspace_bytes(s["batch"], nh, nkv, hd) for s in self.steps)
         self.workspace = torch.empty(max(ws, 16) // 4 + 1, dtype=torch.float32, device=device)
 
+    def rope_kwargs(self, i: int) -> dict:
+        """api.rope_qkv's keyword arguments for chunk i."""
+        w, s = self.w, self.steps[i]
+        return dict(q=s["q"], q_out=s["q_rot"], k_cache=self.k_cache, v_cache=self.v_cache, k_new=s["k"],
+                    v_new=s["v"], batch=s["batch"], inv_freq=self.inv_freq, rotary_dim=w.rd,
+                    rope_scale=w.rope_scale, norm=w.norm_style, q_norm_w=self.q_norm_w,
+                    k_norm_w=self.k_norm_w, eps=w.norm_eps, ring=w.ring, v_norm=w.v_norm)
+
     def run_step(self, i: int, attend: bool = True, fused: bool = True):
         """One chunk: finish Q and append K/V (one fused call, or the two
         separate calls), then attend."""
         w, s = self.w, self.steps[i]
         if fused:
-            api.rope_qkv(s["q"], s["q_rot"], self.k_cache, self.v_cache, s["k"], s["v"], s["batch"],
-                         self.inv_freq, w.rd, w.rope_scale, w.norm_style, self.q_norm_w,
-                         self.k_norm_w, w.norm_eps, ring=w.ring, v_norm=w.v_norm)
+            api.rope_qkv(**self.rope_kwargs(i))
         else:
             api.rope_apply(s["q"], s["q_rot"], s["batch"], self.inv_freq, w.rd, w.rope_scale,
                            w.norm_style, self.q_norm_w, w.norm_eps)
@@ -101,15 +107,24 @@ class ChunkedPrefill:
         if attend:
             self.attend_step(i)
 
-    def attend_step(self, i: int):
+    def attend_step(self, i: int, next_rope: dict | None = None):
         s = self.steps[i]
         api.prefill_chunk(s["q_rot"], self.k_cache, self.v_cache, s["batch"], self.w.scale,
                           s["out"], self.workspace, window=self.w.window, ring=self.w.ring,
-                          gate=s["gate"], gate_mode=self.w.gate_mode)
+                          gate=s["gate"], gate_mode=self.w.gate_mode, next_rope=next_rope)
 
-    def run_all(self, fused: bool = True):
-        for i in range(len(self.steps)):
-            self.run_step(i, fused=fused)
+    def run_all(self, fused: bool = True, pipelined: bool = True):
+        """The chunk loop.  pipelined: chunk 0's finish, then per chunk one
+        call that attends it and finishes the next chunk
+        (attn_prefill_chunk_rope_next); otherwise finish + attend per chunk."""
+        n = len(self.steps)
+        if not (fused and pipelined):
+            for i in range(n):
+                self.run_step(i, fused=fused)
+            return
+        api.rope_qkv(**self.rope_kwargs(0))
+        for i in range(n):
+            self.attend_step(i, self.rope_kwargs(i + 1) if i + 1 < n else None)
 
     def gather(self, key: str) -> torch.Tensor:
         """Per-token results of every step, back in the packed input order."""

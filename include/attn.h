@@ -238,6 +238,64 @@ int attn_prefill_chunk(const void *q, const void *k_cache, const void *v_cache, 
                        float *out, void *workspace, size_t workspace_bytes, void *stream);
 
 /*
+ * attn_rope_qkv's arguments, as a struct, for attn_prefill_chunk_rope_next.
+ */
+typedef struct attn_rope_qkv_args {
+    const void *q;
+    void *q_out;
+    int n_heads;
+    void *k_cache;
+    void *v_cache;
+    const void *k_new;
+    const void *v_new;
+    int n_kv;
+    int cap;
+    int ring;
+    int dtype;
+    int n_tok;
+    int head_dim;
+    int n_seq;
+    const int32_t *cu_seq;
+    const int32_t *start;
+    int max_chunk;
+    int max_end;
+    const float *inv_freq;
+    int rotary_dim;
+    float rope_scale;
+    int norm;
+    const float *q_norm_w;
+    const float *k_norm_w;
+    double eps;
+    int v_norm;
+} attn_rope_qkv_args;
+
+/*
+ * One step of a chunk loop: attn_prefill_chunk on this chunk, then
+ * attn_rope_qkv(*next) on the next chunk -- the same results as the two calls
+ * in that order.  The pages' chunk loop keeps sequential only that a chunk's
+ * rows are in the cache before the chunk attends ([NDL] module docs, "What has
+ * to stay sequential"; [ATT] fn qwen_attention_batch appends the chunk, then
+ * attends); the next chunk's finish writes cache rows past every key this
+ * chunk reads, so with bf16, the same head_dim, rotary_dim a multiple of 8
+ * and neither cache wrapped (ring == 0 or max_end <= cap on both) it runs in
+ * this chunk's attention launch, in the workgroups past the attention items
+ * (one launch fewer per chunk).  Otherwise the two run one after the other.
+ *   next     the next chunk's attn_rope_qkv arguments (not NULL)
+ * Precondition of the single launch (the caller's chunk order): every cache
+ * row next writes lies past every key this chunk reads, i.e. each sequence's
+ * next chunk starts at or after the end of this one.
+ * Errors: those of either call, checked before anything is launched.
+ */
+int attn_prefill_chunk_rope_next(const void *q, const void *k_cache, const void *v_cache, int dtype,
+                                 int n_seq, int n_heads, int n_kv, int head_dim, int cap, int ring,
+                                 int n_tok,
+                                 const int32_t *cu_seq, const int32_t *start, int max_chunk,
+                                 int max_end, float scale, int window, const void *gate,
+                                 int gate_mode, int gate_ld, float *out, void *workspace,
+                                 size_t workspace_bytes, const attn_rope_qkv_args *next,
+                                 void *stream);
+
+/*
  * Workspace, in bytes, that lets attn_prefill_chunk split the key range as far
  * as it chooses for these sizes (the split is this library's own scheduling,
  * not a step of the pages: [ATT] fn attention_head's max-subtracted softmax is

@@ -168,6 +168,43 @@ def test_rope_qkv_validation():
     assert rope_qkv(n_tok=0) == OK
 
 
+def prefill_rope_next(nxt, **kw):
+    """attn_prefill_chunk_rope_next with prefill()'s defaults; nxt: rope_qkv()'s
+    keyword overrides for the next chunk, or None for a NULL next."""
+    a = dict(q=P, k=P, v=P, dtype=1, n_seq=1, nh=8, nkv=2, hd=128, cap=256, ring=0, n_tok=16, cu=P, st=P,
+             max_chunk=16, max_end=64, scale=0.088, window=0, gate=None, gate_mode=0, gate_ld=0,
+             out=P, ws=None, wsb=0, stream=None)
+    a.update(kw)
+    ptr = None
+    if nxt is not None:
+        r = dict(q=P, q_out=P, n_heads=8, k_cache=P, v_cache=P, k_new=P, v_new=P, n_kv=2, cap=256, ring=0,
+                 dtype=1, n_tok=16, head_dim=128, n_seq=1, cu_seq=P, start=P, max_chunk=16, max_end=80,
+                 inv_freq=P, rotary_dim=128, rope_scale=1.0, norm=0, q_norm_w=None, k_norm_w=None, eps=1e-6,
+                 v_norm=0)
+        r.update(nxt)
+        r = {k: (v.value if isinstance(v, ctypes.c_void_p) else v) for k, v in r.items()}
+        ptr = ctypes.byref(api.RopeQkvArgs(**r))
+    return api.lib().attn_prefill_chunk_rope_next(
+        a["q"], a["k"], a["v"], a["dtype"], a["n_seq"], a["nh"], a["nkv"], a["hd"], a["cap"], a["ring"],
+        a["n_tok"], a["cu"], a["st"], a["max_chunk"], a["max_end"], a["scale"], a["window"], a["gate"],
+        a["gate_mode"], a["gate_ld"], a["out"], a["ws"], a["wsb"], ptr, a["stream"])
+
+
+def test_prefill_rope_next_validation():
+    # every error of either call comes back before anything is launched
+    assert prefill_rope_next(None) == EINVAL
+    assert prefill_rope_next({"max_end": 300}) == ECAP          # the next chunk's append
+    assert prefill_rope_next({"head_dim": 96}) == EUNSUP
+    assert prefill_rope_next({"q": None}) == EINVAL
+    assert prefill_rope_next({}, max_end=257) == ECAP            # this chunk's attention
+    assert prefill_rope_next({}, hd=96) == EUNSUP
+    assert prefill_rope_next({}, window=-1) == EINVAL
+    assert prefill_rope_next({}, gate_mode=1) == EINVAL
+    # no work in either call: OK, nothing launched
+    assert prefill_rope_next({"n_tok": 0}, n_tok=0) == OK
+    assert prefill_rope_next({"n_seq": 0}, n_seq=0) == OK
+
+
 def rope(**kw):
     a = dict(x=P, y=P, dtype=0, n_tok=4, nh=4, hd=64, n_seq=1, cu=P, st=P, max_chunk=4, f=P,
              rd=64, rs=1.0, norm=0, w=None, eps=1e-6)
