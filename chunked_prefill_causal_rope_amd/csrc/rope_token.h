@@ -136,41 +136,51 @@ __device__ __forceinline__ double group_sum(double v) {
 
 constexpr int kTokThreads = 256;
 
-// LDS of one token: its cos/sin table and the effective norm weights.
-template <int HD>
+// LDS of TOK tokens: their cos/sin tables and the effective norm weights.
+template <int HD, int TOK = 1>
 struct RopeTokSmem {
-    double cs_cos[HD / 2];
-    double cs_sin[HD / 2];
+    double cs_cos[TOK][HD / 2];
+    double cs_sin[TOK][HD / 2];
     double w_eff[2][HD];
 };
 
-// One workgroup of NT threads finishes head rows hb*HPB .. of token i of
-// sequence b: every exit before the workgroup barrier depends only on
-// (i, hb, b), so the whole workgroup takes it together.
-template <typename T, int HD, int NT>
-__device__ __forceinline__ void rope_token_body(const RopeTokArgs& a, int i, int hb, int b,
-                                                RopeTokSmem<HD>& sm) {
+// One workgroup of NT threads finishes head rows hb*HPB .. of tokens
+// i0 .. i0+TOK-1 of sequence b: every thread issues the loads of all its
+// tokens first, the tables of all of them are built while those are in
+// flight, then each token's rows are finished in turn.  The only exit
+// before the workgroup barrier depends on (i0, hb, b) alone, so the whole
+// workgroup takes it together.
+template <typename T, int HD, int NT, int TOK = 1>
+__device__ __forceinline__ void rope_token_body(const RopeTokArgs& a, int i0, int hb, int b,
+                                                RopeTokSmem<HD, TOK>& sm) {
     constexpr int TPH = HD / 8;                // lanes per head row
     constexpr int HPB = NT / TPH;              // head rows per workgroup
     constexpr int VPER = 16 / sizeof(T);       // elements per 16-byte chunk
     constexpr int VCH = 8 / VPER;              // 16-byte V chunks per lane
-    double* cs_cos = sm.cs_cos;
-    double* cs_sin = sm.cs_sin;
     auto& w_eff = sm.w_eff;                    // query weights, then key weights
 
     const int seq0 = a.cu_seq[b];
     const int len = a.cu_seq[b + 1] - seq0;
-    if (i >= len) return;
-    const int t = seq0 + i;
-    const int pos = a.start[b] + i;
-    if (t < 0 || t >= a.n_tok || pos < 0) return;
+    const int p0 = a.start[b];
     const int nq = a.nq;
-    // no cache row past the capacity (a ring has a row for every position)
-    const int nk = a.ring || pos < a.cap ? a.nk : 0;
-    const int slot = a.ring && a.nk ? pos % a.cap : pos;
-    const int n_all = nq + nk;
     const int h_base = hb * HPB;
-    if (h_base >= n_all) return;               // uniform over the workgroup
+    // the workgroup's tokens: packed row, position, cache row, head rows
+    // (no cache row past the capacity; a ring has a row for every position)
+    int tt[TOK], pp[TOK], slot[TOK], n_all[TOK];
+    bool act[TOK];
+    bool any = false;
+#pragma unroll
+    for (int u = 0; u < TOK; ++u) {
+        const int i = i0 + u;
+        tt[u] = seq0 + i;
+        pp[u] = p0 + i;
+        const int nk = a.ring || pp[u] < a.cap ? a.nk : 0;
+        n_all[u] = nq + nk;
+        slot[u] = a.ring && a.nk ? pp[u] % a.cap : pp[u];
+        act[u] = i < len && tt[u] >= 0 && tt[u] < a.n_tok && pp[u] >= 0 && h_base < n_all[u];
+        any = any || act[u];
+    }
+    if (!any) return;                          // uniform over the workgroup
 
     const int rd = a.rotary_dim;
     const int half = rd / 2;
@@ -184,102 +194,111 @@ __device__ __forceinline__ void rope_token_body(const RopeTokArgs& a, int i, int
     // rows of one head are whole groups of TPH lanes (whole DPP rows or half
     // rows), so a row is entirely valid or entirely past the last head, and
     // the norm's group sum reads only its own row
-    const bool valid = vh < n_all;
     const bool is_q = vh < nq;
     const int kh = vh - nq;
 
-    Raw<T> raw;
-    u32x4_t vbuf[VCH] = {};
-    if (valid) {
-        const T* row = is_q ? reinterpret_cast<const T*>(a.qx) + ((size_t)t * nq + vh) * HD
-                            : reinterpret_cast<const T*>(a.kx) + ((size_t)t * a.nk + kh) * HD;
-        if (pair) raw.load4x2(row + d0, row + d0 + half);
-        else raw.load8(row + d0);
+    Raw<T> raw[TOK];
+    u32x4_t vbuf[TOK][VCH];
+#pragma unroll
+    for (int u = 0; u < TOK; ++u) {
+#pragma unroll
+        for (int j = 0; j < VCH; ++j) vbuf[u][j] = u32x4_t{0u, 0u, 0u, 0u};
+        if (!(act[u] && vh < n_all[u])) continue;
+        const T* row = is_q ? reinterpret_cast<const T*>(a.qx) + ((size_t)tt[u] * nq + vh) * HD
+                            : reinterpret_cast<const T*>(a.kx) + ((size_t)tt[u] * a.nk + kh) * HD;
+        if (pair) raw[u].load4x2(row + d0, row + d0 + half);
+        else raw[u].load8(row + d0);
         if (!is_q) {
             // this lane's share of the matching V row, copied unchanged
-            const T* vs = reinterpret_cast<const T*>(a.vx) + ((size_t)t * a.nk + kh) * HD + c * 8;
+            const T* vs = reinterpret_cast<const T*>(a.vx) + ((size_t)tt[u] * a.nk + kh) * HD + c * 8;
 #pragma unroll
-            for (int j = 0; j < VCH; ++j) vbuf[j] = ld16(vs + j * VPER);
+            for (int j = 0; j < VCH; ++j) vbuf[u][j] = ld16(vs + j * VPER);
         }
     }
 
-    for (int k = tid; k < half; k += NT) {
+    for (int k = tid; k < TOK * half; k += NT) {
+        const int u = k / half, f = k - u * half;
         // position * f_k is exact in double (integer times a float)
-        const double th = (double)pos * (double)a.inv_freq[k];
+        const double th = (double)max(p0 + i0 + u, 0) * (double)a.inv_freq[f];
         double sn, cn;
         sincos_pos(th, &sn, &cn);
-        cs_cos[k] = cn;
-        cs_sin[k] = sn;
+        sm.cs_cos[u][f] = cn;
+        sm.cs_sin[u][f] = sn;
     }
     if (a.norm != 0) {
         for (int k = tid; k < 2 * HD; k += NT) {
             const bool q_side = k < HD;
-            if (q_side ? nq == 0 : nk == 0) continue;
+            if (q_side ? nq == 0 : a.nk == 0) continue;
             const double w = (double)(q_side ? a.qw[k] : a.kw[k - HD]);
             w_eff[q_side ? 0 : 1][k % HD] = a.norm == 2 ? 1.0 + w : w;
         }
     }
     __syncthreads();
-    if (!valid) return;
 
-    double v[8];
 #pragma unroll
-    for (int e = 0; e < 8; ++e) v[e] = raw.get(e);
-    if (a.norm != 0) {
-        double ss = 0.0;
+    for (int u = 0; u < TOK; ++u) {
+        if (!(act[u] && vh < n_all[u])) continue;
+        const double* cs_cos = sm.cs_cos[u];
+        const double* cs_sin = sm.cs_sin[u];
+        double v[8];
 #pragma unroll
-        for (int e = 0; e < 8; ++e) ss += v[e] * v[e];
-        ss = group_sum<TPH>(ss);
-        const double r = 1.0 / sqrt(ss / (double)HD + a.eps);
-        const double* we = w_eff[is_q ? 0 : 1];
+        for (int e = 0; e < 8; ++e) v[e] = raw[u].get(e);
+        if (a.norm != 0) {
+            double ss = 0.0;
 #pragma unroll
-        for (int e = 0; e < 8; ++e) {
-            const int d = pair ? d0 + (e & 3) + (e >> 2) * half : d0 + e;
-            v[e] = v[e] * r * we[d];
+            for (int e = 0; e < 8; ++e) ss += v[e] * v[e];
+            ss = group_sum<TPH>(ss);
+            const double r = 1.0 / sqrt(ss / (double)HD + a.eps);
+            const double* we = w_eff[is_q ? 0 : 1];
+#pragma unroll
+            for (int e = 0; e < 8; ++e) {
+                const int d = pair ? d0 + (e & 3) + (e >> 2) * half : d0 + e;
+                v[e] = v[e] * r * we[d];
+            }
         }
-    }
-    T* dst = is_q ? reinterpret_cast<T*>(a.qy) + ((size_t)t * nq + vh) * HD
-                  : reinterpret_cast<T*>(a.kc) + (((size_t)b * a.nk + kh) * a.cap + slot) * HD;
-    if (pair) {
-        const double rs = (double)a.rope_scale;
-        const bool scaled = a.rope_scale != 1.f;
-        double y[8];
+        T* dst = is_q ? reinterpret_cast<T*>(a.qy) + ((size_t)tt[u] * nq + vh) * HD
+                      : reinterpret_cast<T*>(a.kc) + (((size_t)b * a.nk + kh) * a.cap + slot[u]) * HD;
+        if (pair) {
+            const double rs = (double)a.rope_scale;
+            const bool scaled = a.rope_scale != 1.f;
+            double y[8];
 #pragma unroll
-        for (int e = 0; e < 4; ++e) {
-            const double cn = cs_cos[d0 + e], sn = cs_sin[d0 + e];
-            y[e] = v[e] * cn - v[e + 4] * sn;
-            y[e + 4] = v[e] * sn + v[e + 4] * cn;
+            for (int e = 0; e < 4; ++e) {
+                const double cn = cs_cos[d0 + e], sn = cs_sin[d0 + e];
+                y[e] = v[e] * cn - v[e + 4] * sn;
+                y[e + 4] = v[e] * sn + v[e + 4] * cn;
+            }
+            if (scaled) {
+#pragma unroll
+                for (int e = 0; e < 8; ++e) y[e] *= rs;
+            }
+            store_vals(dst + d0, y, 4);
+            store_vals(dst + d0 + half, y + 4, 4);
+        } else {
+            store_vals(dst + d0, v, 8);
         }
-        if (scaled) {
+        if (a.v_norm) {
+            // V rows: scale-less RMS norm over the row's lanes (dims 8c..8c+7
+            // each), in double, each value rounded once; query rows of the wave
+            // take part in the row sums with their own (unused) groups
+            Raw<T> vr;
+            vr.from_chunks(vbuf[u]);
+            double w[8], ss = 0.0;
 #pragma unroll
-            for (int e = 0; e < 8; ++e) y[e] *= rs;
+            for (int e = 0; e < 8; ++e) {
+                w[e] = vr.get(e);
+                ss += w[e] * w[e];
+            }
+            ss = group_sum<TPH>(ss);
+            const double r = 1.0 / sqrt(ss / (double)HD + a.eps);
+#pragma unroll
+            for (int e = 0; e < 8; ++e) w[e] *= r;
+            if (!is_q) store_vals(reinterpret_cast<T*>(a.vc) + (((size_t)b * a.nk + kh) * a.cap + slot[u]) * HD + c * 8, w, 8);
+        } else if (!is_q) {
+            T* vd = reinterpret_cast<T*>(a.vc) + (((size_t)b * a.nk + kh) * a.cap + slot[u]) * HD + c * 8;
+#pragma unroll
+            for (int j = 0; j < VCH; ++j) st16(vd + j * VPER, vbuf[u][j]);
         }
-        store_vals(dst + d0, y, 4);
-        store_vals(dst + d0 + half, y + 4, 4);
-    } else {
-        store_vals(dst + d0, v, 8);
-    }
-    if (a.v_norm) {
-        // V rows: scale-less RMS norm over the row's lanes (dims 8c..8c+7
-        // each), in double, each value rounded once; query rows of the wave
-        // take part in the row sums with their own (unused) groups
-        Raw<T> vr;
-        vr.from_chunks(vbuf);
-        double w[8], ss = 0.0;
-#pragma unroll
-        for (int e = 0; e < 8; ++e) {
-            w[e] = vr.get(e);
-            ss += w[e] * w[e];
-        }
-        ss = group_sum<TPH>(ss);
-        const double r = 1.0 / sqrt(ss / (double)HD + a.eps);
-#pragma unroll
-        for (int e = 0; e < 8; ++e) w[e] *= r;
-        if (!is_q) store_vals(reinterpret_cast<T*>(a.vc) + (((size_t)b * a.nk + kh) * a.cap + slot) * HD + c * 8, w, 8);
-    } else if (!is_q) {
-        T* vd = reinterpret_cast<T*>(a.vc) + (((size_t)b * a.nk + kh) * a.cap + slot) * HD + c * 8;
-#pragma unroll
-        for (int j = 0; j < VCH; ++j) st16(vd + j * VPER, vbuf[j]);
     }
 }
 
