@@ -1053,18 +1053,32 @@ __global__ __launch_bounds__(512, 1) void prefill_bf16_ks_kernel(PrefillArgs a) 
 }
 
 // Merge split partials (m, l, O/l) of each row: m* = max m_s,
-// l* = sum l_s 2^(m_s - m*), out = sum (O/l)_s l_s 2^(m_s - m*) / l*.  One
-// wave per row, each lane over HD/64 consecutive dims: workgroup
-// (x, sequence) takes 4 rows of the row tile x / (n_kv * R/4) and KV group
-// x % n_kv; row tiles that were not split were written by the attention
-// kernel.
+// l* = sum l_s 2^(m_s - m*), out = sum (O/l)_s l_s 2^(m_s - m*) / l*.  A row
+// is LPR = HD/8 lanes, each over 8 consecutive dims (one 16-byte load of
+// halves per part), so a wave merges 64/LPR rows; lane j of a row also reads
+// part j's (m, l, e), and the row's maximum and sum are reductions over its
+// LPR lanes.  The first parts' values are loaded with the part heads, each
+// later batch of four while the previous one is accumulated.  Workgroup
+// (x, sequence) takes 4*64/LPR rows of the row tile x / (n_kv * R/RPB) and KV
+// group x % n_kv; row tiles that were not split were written by the
+// attention kernel.
+template <int HD>
+struct CombineShape {
+    static constexpr int LPR = HD / 8;        // lanes per row
+    static constexpr int RPW = 64 / LPR;      // rows per wave
+    static constexpr int RPB = 4 * RPW;       // rows per workgroup
+};
 template <int HD>
 __global__ __launch_bounds__(256) void prefill_combine_kernel(PrefillArgs a) {
+    using Sh = CombineShape<HD>;
+    constexpr int LPR = Sh::LPR, RPB = Sh::RPB;
+    constexpr int PS = part_row_words(HD);
+    constexpr int NB = 4;                     // parts per load batch
     const int b = blockIdx.y;
     const int R = a.rows_per_tile;
     const int g = blockIdx.x % a.n_kv;
-    const int rblk = (blockIdx.x / a.n_kv) % (R / 4);
-    const int qt = blockIdx.x / a.n_kv / (R / 4);
+    const int rblk = (blockIdx.x / a.n_kv) % (R / RPB);
+    const int qt = blockIdx.x / a.n_kv / (R / RPB);
     if (b >= a.n_seq || qt >= a.n_qtiles) return;
     const int first = a.table[2 * (b * a.n_qtiles + qt)];
     const int S = a.table[2 * (b * a.n_qtiles + qt) + 1];
@@ -1074,93 +1088,91 @@ __global__ __launch_bounds__(256) void prefill_combine_kernel(PrefillArgs a) {
     const int len = min(a.cu_seq[b + 1] - t0, a.max_chunk);
     const int rows_b = len * G;
     const int lane = threadIdx.x & 63;
-    constexpr int PER = HD / 64;                  // dims lane*PER .. lane*PER+PER-1
-    constexpr int PS = part_row_words(HD);
-    {
-        const int rl = rblk * 4 + (threadIdx.x >> 6);
-        const int r = qt * R + rl;
-        if (r >= rows_b) return;
-        const int i = r / G;
-        const int h = g * G + (r - i * G);
-        const int t = t0 + i;
-        if (t < 0 || t >= a.n_tok) return;
-        // part p of this row tile and group is item first + p * n_kv + g;
-        // lane p < S holds part p's (m, l, e), then its weights
-        auto prow = [&](int p) { return a.part + ((size_t)(first + p * a.n_kv + g) * R + rl) * PS; };
-        // this lane's PER halves of part p's O/l
-        auto vals = [&](int p, float* x) __attribute__((always_inline)) {
-            const uint16_t* ph = reinterpret_cast<const uint16_t*>(prow(p) + kPartHead) + lane * PER;
-            if (PER == 2) {
-                const uint32_t u = *reinterpret_cast<const uint32_t*>(ph);
-                x[0] = f16_value((uint16_t)u);
-                x[PER - 1] = f16_value((uint16_t)(u >> 16));
-            } else {
-                x[0] = f16_value(ph[0]);
-            }
-        };
-        // output gate factors first, so their loads overlap the merge
-        float gf[PER];
+    const int j = lane % LPR;                  // this lane's 8 dims: 8j .. 8j+7
+    const int rl = rblk * RPB + (threadIdx.x / 64) * (64 / LPR) + lane / LPR;
+    const int r = qt * R + rl;
+    const int i = r / G;
+    const int h = g * G + (r - i * G);
+    const int t = t0 + i;
+    // a row's lanes are one aligned group: they skip together, and the
+    // group's shuffles below read only lanes of the same row
+    const bool row_ok = r < rows_b && t >= 0 && t < a.n_tok;
+    auto prow = [&](int p) { return a.part + ((size_t)(first + p * a.n_kv + g) * R + rl) * PS; };
+    auto load_vals = [&](int p) __attribute__((always_inline)) {
+        return p < S && row_ok ? *reinterpret_cast<const u32x4_t*>(prow(p) + kPartHead + 4 * j)
+                               : u32x4_t{0u, 0u, 0u, 0u};
+    };
+    // part heads: lane j holds part j (and j + LPR, ... when S > LPR: max only)
+    float mp = -INFINITY, lp = 0.f, ep = 0.f;
+    u32x4_t xv[NB];
 #pragma unroll
-        for (int e = 0; e < PER; ++e)
-            gf[e] = a.gate.mode ? gate_factor_bf16(a.gate, (size_t)t * a.n_heads + h, lane * PER + e) : 1.f;
-        float mp = -INFINITY, lp = 0.f, ep = 0.f;
-        for (int p = lane; p < S; p += 64) {
+    for (int u = 0; u < NB; ++u) xv[u] = load_vals(u);
+    if (row_ok) {
+        for (int p = j; p < S; p += LPR) {
             const float4 ml = *reinterpret_cast<const float4*>(prow(p));
-            if (p < 64) { mp = ml.x; lp = ml.y; ep = ml.z; }
+            if (p < LPR) { mp = ml.x; lp = ml.y; ep = ml.z; }
             else { mp = fmaxf(mp, ml.x); }
         }
-        const float m = wave_max(mp);
-        const float m_use = m == -INFINITY ? 0.f : m;
-        float o[PER];
+    }
+    // output gate factors, so their loads overlap the merge
+    float gf[8];
 #pragma unroll
-        for (int e = 0; e < PER; ++e) o[e] = 0.f;
-        float l = 0.f;
-        if (S <= 64) {
-            // part weight in l: l_p 2^(m_p - m); on the stored values also 2^e_p
-            const float wl = lane < S ? lp * __builtin_amdgcn_exp2f(mp - m_use) : 0.f;
-            const float wo = __builtin_amdgcn_ldexpf(wl, (int)ep);
-            l = wave_sum(wl);
-            int p = 0;
-            for (; p + 4 <= S; p += 4) {
-                float x[4][PER], w[4];
+    for (int e = 0; e < 8; ++e)
+        gf[e] = a.gate.mode && row_ok ? gate_factor_bf16(a.gate, (size_t)t * a.n_heads + h, 8 * j + e) : 1.f;
+    float m = mp;
 #pragma unroll
-                for (int u = 0; u < 4; ++u) {
-                    w[u] = __shfl(wo, p + u);
-                    vals(p + u, x[u]);
-                }
+    for (int o = 1; o < LPR; o <<= 1) m = fmaxf(m, __shfl_xor(m, o));
+    const float m_use = m == -INFINITY ? 0.f : m;
+    // part weight in l: l_p 2^(m_p - m); on the stored values also 2^e_p
+    const float wl = j < S ? lp * __builtin_amdgcn_exp2f(mp - m_use) : 0.f;
+    const float wo = __builtin_amdgcn_ldexpf(wl, (int)ep);
+    float l = wl;
+    const int gbase = lane - j;
+    float o[8];
 #pragma unroll
-                for (int u = 0; u < 4; ++u)
+    for (int e = 0; e < 8; ++e) o[e] = 0.f;
+    auto accum = [&](const u32x4_t& x, float w) __attribute__((always_inline)) {
 #pragma unroll
-                    for (int e = 0; e < PER; ++e) o[e] += x[u][e] * w[u];
+        for (int q = 0; q < 4; ++q) {
+            o[2 * q] += f16_value((uint16_t)x[q]) * w;
+            o[2 * q + 1] += f16_value((uint16_t)(x[q] >> 16)) * w;
+        }
+    };
+    if (S <= LPR) {
+#pragma unroll
+        for (int o2 = 1; o2 < LPR; o2 <<= 1) l += __shfl_xor(l, o2);
+        for (int p = 0; p < S; p += NB) {
+            u32x4_t nx[NB];
+#pragma unroll
+            for (int u = 0; u < NB; ++u) nx[u] = load_vals(p + NB + u);
+#pragma unroll
+            for (int u = 0; u < NB; ++u) {
+                const float w = __shfl(wo, gbase + min(p + u, LPR - 1));
+                if (p + u < S) accum(xv[u], w);
             }
-            for (; p < S; ++p) {
-                float x[PER];
-                vals(p, x);
-                const float w = __shfl(wo, p);
 #pragma unroll
-                for (int e = 0; e < PER; ++e) o[e] += x[e] * w;
-            }
-        } else {
+            for (int u = 0; u < NB; ++u) xv[u] = nx[u];
+        }
+    } else {
+        // more parts than lanes: every lane forms each weight itself
+        l = 0.f;
+        if (row_ok) {
             for (int p = 0; p < S; ++p) {
                 const float4 hd4 = *reinterpret_cast<const float4*>(prow(p));
                 const float w = hd4.y * __builtin_amdgcn_exp2f(hd4.x - m_use);
                 l += w;
-                float x[PER];
-                vals(p, x);
-                const float wv = __builtin_amdgcn_ldexpf(w, (int)hd4.z);
-#pragma unroll
-                for (int e = 0; e < PER; ++e) o[e] += x[e] * wv;
+                accum(load_vals(p), __builtin_amdgcn_ldexpf(w, (int)hd4.z));
             }
         }
-        const float inv = l > 0.f ? 1.f / l : 0.f;
-        float* orow = a.out + ((size_t)t * a.n_heads + h) * HD + lane * PER;
-        if (PER == 2)
-            *reinterpret_cast<float2*>(orow) = make_float2(o[0] * inv * gf[0], o[PER - 1] * inv * gf[PER - 1]);
-        else
-            orow[0] = o[0] * inv * gf[0];
     }
+    if (!row_ok) return;
+    const float inv = l > 0.f ? 1.f / l : 0.f;
+    float* orow = a.out + ((size_t)t * a.n_heads + h) * HD + 8 * j;
+    *reinterpret_cast<float4*>(orow) =
+        make_float4(o[0] * inv * gf[0], o[1] * inv * gf[1], o[2] * inv * gf[2], o[3] * inv * gf[3]);
+    *reinterpret_cast<float4*>(orow + 4) =
+        make_float4(o[4] * inv * gf[4], o[5] * inv * gf[5], o[6] * inv * gf[6], o[7] * inv * gf[7]);
 }
-
 
 // Launch plan.  256-row workgroups (8 waves, deeper prefetch) when they
 // alone give every CU a workgroup; otherwise 128-row workgroups.  When the
@@ -1285,7 +1297,8 @@ hipError_t launch_prefill_bf16(const PrefillArgs& a, hipStream_t stream) {
 
 hipError_t launch_prefill_combine(const PrefillArgs& a, hipStream_t stream) {
     if (!a.split || a.n_seq <= 0) return hipSuccess;
-    const dim3 grid((unsigned)(a.n_qtiles * a.n_kv * (a.rows_per_tile / 4)), (unsigned)a.n_seq);
+    const int rpb = a.head_dim == 128 ? CombineShape<128>::RPB : CombineShape<64>::RPB;
+    const dim3 grid((unsigned)(a.n_qtiles * a.n_kv * (a.rows_per_tile / rpb)), (unsigned)a.n_seq);
     if (a.head_dim == 128)
         prefill_combine_kernel<128><<<grid, dim3(256), 0, stream>>>(a);
     else
