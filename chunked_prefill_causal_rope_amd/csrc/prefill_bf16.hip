@@ -1021,20 +1021,25 @@ __global__ __launch_bounds__(512, 1) void prefill_bf16_ks_kernel(PrefillArgs a) 
 
     // ---- merge the key halves: waves 4..7 hand (m, l, O) of their rows to
     // waves 0..3 through LDS (the tile buffers are free after the barrier)
+    // (per lane: O, then m and l, in a 16-byte-aligned block of NDB*16 + 4
+    // floats, read and written 16 bytes at a time; the stride of 4 mod 64
+    // words keeps 16 lanes' reads on distinct banks)
     __syncthreads();
-    float* xch = reinterpret_cast<float*>(&sm) + ((size_t)wr * 64 + lane) * (NDB * 16 + 2);
+    static_assert(4 * 64 * (NDB * 16 + 4) * sizeof(float) <= sizeof(Sm), "exchange fits the tile buffers");
+    f32x4_t* xch = reinterpret_cast<f32x4_t*>(&sm) + ((size_t)wr * 64 + lane) * (NDB * 4 + 1);
     if (kh == 1) {
-        xch[0] = m_run;
-        xch[1] = l_run;
 #pragma unroll
         for (int db = 0; db < NDB; ++db)
 #pragma unroll
-            for (int q = 0; q < 16; ++q) xch[2 + db * 16 + q] = O[db][q];
+            for (int q4 = 0; q4 < 4; ++q4)
+                xch[db * 4 + q4] = f32x4_t{O[db][4 * q4], O[db][4 * q4 + 1], O[db][4 * q4 + 2], O[db][4 * q4 + 3]};
+        xch[NDB * 4] = f32x4_t{m_run, l_run, 0.f, 0.f};
     }
     __syncthreads();
     if (kh == 1) return;
     {
-        const float m1 = xch[0], l1 = xch[1];
+        const f32x4_t ml = xch[NDB * 4];
+        const float m1 = ml[0], l1 = ml[1];
         const float mm = fmaxf(m_run, m1);
         const float mu = mm == -INFINITY ? 0.f : mm;
         const float a0 = __builtin_amdgcn_exp2f(m_run - mu), a1 = __builtin_amdgcn_exp2f(m1 - mu);
@@ -1042,7 +1047,11 @@ __global__ __launch_bounds__(512, 1) void prefill_bf16_ks_kernel(PrefillArgs a) 
 #pragma unroll
         for (int db = 0; db < NDB; ++db)
 #pragma unroll
-            for (int q = 0; q < 16; ++q) O[db][q] = O[db][q] * a0 + xch[2 + db * 16 + q] * a1;
+            for (int q4 = 0; q4 < 4; ++q4) {
+                const f32x4_t x = xch[db * 4 + q4];
+#pragma unroll
+                for (int e = 0; e < 4; ++e) O[db][4 * q4 + e] = O[db][4 * q4 + e] * a0 + x[e] * a1;
+            }
         m_run = mm;
     }
 
