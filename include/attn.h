@@ -283,7 +283,10 @@ typedef struct attn_rope_qkv_args {
  *   next     the next chunk's attn_rope_qkv arguments (not NULL)
  * Precondition of the single launch (the caller's chunk order): every cache
  * row next writes lies past every key this chunk reads, i.e. each sequence's
- * next chunk starts at or after the end of this one.
+ * next chunk starts at or after the end of this one.  The call serves a loop
+ * that has the next chunk's projected rows while this chunk attends (one
+ * layer over a projected prompt); a caller that projects the next chunk only
+ * after this one has passed every layer uses the two separate calls.
  * Errors: those of either call, checked before anything is launched.
  */
 int attn_prefill_chunk_rope_next(const void *q, const void *k_cache, const void *v_cache, int dtype,
