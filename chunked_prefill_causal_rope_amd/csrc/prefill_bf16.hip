@@ -1123,11 +1123,30 @@ __global__ __launch_bounds__(256) void prefill_combine_kernel(PrefillArgs a) {
             else { mp = fmaxf(mp, ml.x); }
         }
     }
-    // output gate factors, so their loads overlap the merge
+    // output gate factors, so their loads overlap the merge: the lane's 8
+    // per-element values in one 16-byte load when the rows allow it
     float gf[8];
 #pragma unroll
-    for (int e = 0; e < 8; ++e)
-        gf[e] = a.gate.mode && row_ok ? gate_factor_bf16(a.gate, (size_t)t * a.n_heads + h, 8 * j + e) : 1.f;
+    for (int e = 0; e < 8; ++e) gf[e] = 1.f;
+    if (a.gate.mode && row_ok) {
+        const size_t grow = (size_t)t * a.n_heads + h;
+        const uint16_t* gp = reinterpret_cast<const uint16_t*>(a.gate.p) + grow * (size_t)a.gate.ld;
+        if (a.gate.mode == kGateSoftplusHead) {
+            const float f = gate_fast(a.gate.mode, bf16_to_f32(gp[0]));
+#pragma unroll
+            for (int e = 0; e < 8; ++e) gf[e] = f;
+        } else if (((a.gate.ld & 7) == 0) && ((reinterpret_cast<uintptr_t>(a.gate.p) & 15) == 0)) {
+            const u32x4_t g4 = ld16(gp + 8 * j);
+#pragma unroll
+            for (int q = 0; q < 4; ++q) {
+                gf[2 * q] = gate_fast(a.gate.mode, bf16_lo(g4[q]));
+                gf[2 * q + 1] = gate_fast(a.gate.mode, bf16_hi(g4[q]));
+            }
+        } else {
+#pragma unroll
+            for (int e = 0; e < 8; ++e) gf[e] = gate_fast(a.gate.mode, bf16_to_f32(gp[8 * j + e]));
+        }
+    }
     float m = mp;
 #pragma unroll
     for (int o = 1; o < LPR; o <<= 1) m = fmaxf(m, __shfl_xor(m, o));
