@@ -17,7 +17,8 @@ decode batch (`decode`) as sub-objects.  `value` is the whole-step
 throughput (algorithmic FLOP/s for prefill, K/V bytes read per second for
 decode); `roofline` is the attention call measured per launch with HIP events
 on its stream, against the published peak and against the peak measured on
-the same GPU in the same run (`calibration`: a matrix-core loop and a
+the same GPU in the same run (`calibration`: a matrix-core loop on random
+operands, `measured_peak`, and on constant ones, `measured_peak_const`, and a
 streaming read); `cpu_baseline` is the CPU oracle timed on a bounded sample
 of the same workload on this host.  The decode line also carries
 `importance`: the per-position importance call (sum over heads of the step's
@@ -366,22 +367,29 @@ def cpu_baseline_decode(w, d, budget_s):
 def calibrate(torch, stream):
     """Measured peaks of this GPU in this run: a loop of bf16 32x32x16 matrix
     products (two workgroups of 4 waves per CU, four independent accumulators
-    per wave) and a streaming read of 4 GiB with 16-byte nontemporal loads
-    (each workgroup a contiguous share of 128, 256 or 512 KB, the best
-    kept); the best of 5 launches each, timed with events on `stream`."""
+    per wave), once on hashed random operands (data like the kernels': the
+    part's clock under load falls with the operands' switching activity) and
+    once on small constants (the highest rate it sustains), and a streaming
+    read of 4 GiB with 16-byte nontemporal loads (each workgroup a contiguous
+    share of 128, 256 or 512 KB, the best kept); the best of 5 launches each,
+    timed with events on `stream`.  Each matrix loop launch runs ~7-10 ms,
+    five in a row, so the clock settles."""
     from chunked_prefill_causal_rope_amd import api
     cus = torch.cuda.get_device_properties(0).multi_processor_count
     nwg = 2 * cus
     out = torch.empty(nwg * 4, dtype=torch.float32, device="cuda")
-    iters = 16384
-    flop = [0.0]
+    iters = 65536
+    rates = {}
+    for random_operands in (True, False):
+        flop = [0.0]
 
-    def mf():
-        flop[0] = api.calibrate_mfma(nwg, iters, out)
-    with torch.cuda.stream(stream):
-        mf()
-    ms = min(time_launches(torch, [mf] * 5, stream))
-    mfma_tflops = flop[0] / (ms * 1e-3) / 1e12
+        def mf():
+            flop[0] = api.calibrate_mfma(nwg, iters, out, random_operands)
+        with torch.cuda.stream(stream):
+            mf()
+        ms = min(time_launches(torch, [mf] * 5, stream))
+        rates[random_operands] = (flop[0] / (ms * 1e-3) / 1e12, ms)
+    mfma_tflops, ms = rates[True]
     src = torch.empty(1 << 30, dtype=torch.int32, device="cuda")     # 4 GiB, contents irrelevant
     best = None
     for share_kb in (128, 256, 512):                                  # contiguous bytes per workgroup
@@ -402,7 +410,9 @@ def calibrate(torch, stream):
     del src
     torch.cuda.synchronize()
     return {"mfma_bf16_tflops": round(mfma_tflops, 1), "mfma_kernel": "attn_calibrate_mfma",
-            "mfma_ms": round(ms, 4), "hbm_read_gbs": round(read_gbs, 1),
+            "mfma_operands": "hashed random bf16", "mfma_ms": round(ms, 4),
+            "mfma_bf16_tflops_const": round(rates[False][0], 1), "mfma_ms_const": round(rates[False][1], 4),
+            "hbm_read_gbs": round(read_gbs, 1),
             "read_kernel": "attn_calibrate_read", "read_bytes": nbytes[0], "read_ms": round(ms_r, 4),
             "read_share_kb": share_kb, "compute_units": cus}
 
@@ -415,6 +425,9 @@ def with_measured_peak(roof, calib):
     roof = dict(roof)
     roof["measured_peak"] = peak
     roof["frac_measured"] = round(roof["achieved"] / peak, 4)
+    if roof["bound"] == "mfma":
+        roof["measured_peak_const"] = calib["mfma_bf16_tflops_const"]
+        roof["frac_measured_const"] = round(roof["achieved"] / calib["mfma_bf16_tflops_const"], 4)
     return roof
 
 

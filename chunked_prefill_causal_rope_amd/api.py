@@ -82,7 +82,7 @@ def lib() -> ctypes.CDLL:
     L.attn_decode_importance.argtypes = [vp, i, i, i, vp, i, vp, i, i, vp]
     L.attn_decode_importance.restype = i
     L.attn_decode_workspace_bytes.restype = sz
-    L.attn_calibrate_mfma.argtypes = [i, i, vp, vp]
+    L.attn_calibrate_mfma.argtypes = [i, i, i, vp, vp]
     L.attn_calibrate_mfma.restype = i
     L.attn_calibrate_read.argtypes = [vp, sz, i, vp, vp]
     L.attn_calibrate_read.restype = i
@@ -353,12 +353,13 @@ def decode(q: torch.Tensor, k_cache: torch.Tensor, v_cache: torch.Tensor, ctx: t
 
 # ---------------------------------------------------------------- calibration
 
-def calibrate_mfma(n_workgroups: int, iters: int, out: torch.Tensor) -> float:
-    """Launch the matrix-core loop on the current stream; returns its FLOP
-    count (n_workgroups * 4 waves * iters * 4 products * 32768)."""
+def calibrate_mfma(n_workgroups: int, iters: int, out: torch.Tensor, random_operands: bool = True) -> float:
+    """Launch the matrix-core loop on the current stream (hashed random or
+    small constant operands); returns its FLOP count (n_workgroups * 4 waves
+    * iters * 4 products * 32768)."""
     assert out.dtype == torch.float32 and out.numel() >= n_workgroups * 4
-    _check("attn_calibrate_mfma", lib().attn_calibrate_mfma(n_workgroups, iters, _dev(out, "out"),
-                                                             _stream()))
+    _check("attn_calibrate_mfma", lib().attn_calibrate_mfma(n_workgroups, iters, int(bool(random_operands)),
+                                                             _dev(out, "out"), _stream()))
     return float(n_workgroups) * 4 * iters * 4 * 32768
 
 

@@ -14,23 +14,43 @@
 namespace attn {
 
 // Each wave keeps four independent 32x32x16 bf16 accumulators in flight, so
-// the matrix pipe never waits on a result; the operands are fixed, so the
-// loop issues products only.  A lane-dependent sum of the accumulators is
-// written per wave, which keeps the products live.
-__global__ __launch_bounds__(256) void calib_mfma_kernel(int iters, float* out) {
+// the matrix pipe never waits on a result.  The operands stay in registers,
+// so the loop issues products only.  With random == 0 they are small
+// constants with few distinct bits; with random == 1 each accumulator gets
+// its own hashed bfloat16 operands (random signs and mantissas, magnitudes
+// 2^-2..2^2), so consecutive products see different, fully toggling data, as
+// the attention kernels' products do.  The part's clock under load depends on
+// that switching activity, so the two modes bound the sustained matrix rate
+// from above (constants) and for data like the kernels' (random).  A
+// lane-dependent sum of the accumulators is written per wave, which keeps the
+// products live.
+__device__ __forceinline__ __bf16 hashed_bf16(uint32_t x) {
+    x ^= x >> 16;
+    x *= 0x7feb352du;
+    x ^= x >> 15;
+    x *= 0x846ca68bu;
+    x ^= x >> 16;
+    const uint32_t e = 125u + (x & 3u);   // exponent field: 2^-2 .. 2^1
+    return __builtin_bit_cast(__bf16, (uint16_t)(((x >> 31) << 15) | (e << 7) | ((x >> 8) & 0x7fu)));
+}
+
+__global__ __launch_bounds__(256) void calib_mfma_kernel(int iters, int random, float* out) {
     const int lane = threadIdx.x & 63;
-    bf16x8_t a, b;
+    const uint32_t seed = (blockIdx.x * 256u + threadIdx.x) * 64u;
+    bf16x8_t a[4], b[4];
 #pragma unroll
-    for (int i = 0; i < 8; ++i) {
-        a[i] = (__bf16)(0.001f * (float)((lane + i) & 7));
-        b[i] = (__bf16)(0.002f * (float)((lane * 3 + i) & 7));
-    }
+    for (int k = 0; k < 4; ++k)
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+            a[k][i] = random ? hashed_bf16(seed + 16u * k + i) : (__bf16)(0.001f * (float)((lane + i) & 7));
+            b[k][i] = random ? hashed_bf16(seed + 16u * k + 8u + i) : (__bf16)(0.002f * (float)((lane * 3 + i) & 7));
+        }
     f32x16_t c0 = {}, c1 = {}, c2 = {}, c3 = {};
     for (int it = 0; it < iters; ++it) {
-        c0 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c0, 0, 0, 0);
-        c1 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c1, 0, 0, 0);
-        c2 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c2, 0, 0, 0);
-        c3 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c3, 0, 0, 0);
+        c0 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[0], b[0], c0, 0, 0, 0);
+        c1 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[1], b[1], c1, 0, 0, 0);
+        c2 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[2], b[2], c2, 0, 0, 0);
+        c3 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[3], b[3], c3, 0, 0, 0);
     }
     float s = 0.f;
 #pragma unroll
@@ -67,9 +87,10 @@ __global__ __launch_bounds__(256) void calib_read_kernel(const u32x4_t* src, siz
 
 extern "C" {
 
-int attn_calibrate_mfma(int n_workgroups, int iters, float* out, void* stream) {
-    if (n_workgroups <= 0 || iters <= 0 || !out) return ATTN_EINVAL;
-    attn::calib_mfma_kernel<<<dim3((unsigned)n_workgroups), dim3(256), 0, (hipStream_t)stream>>>(iters, out);
+int attn_calibrate_mfma(int n_workgroups, int iters, int random_operands, float* out, void* stream) {
+    if (n_workgroups <= 0 || iters <= 0 || !out || (random_operands != 0 && random_operands != 1)) return ATTN_EINVAL;
+    attn::calib_mfma_kernel<<<dim3((unsigned)n_workgroups), dim3(256), 0, (hipStream_t)stream>>>(iters, random_operands,
+                                                                                                   out);
     return hipGetLastError() == hipSuccess ? ATTN_OK : ATTN_EDEVICE;
 }
 

@@ -420,15 +420,20 @@ int attn_decode_importance(const float *probs, int n_seq, int n_heads, int probs
  * attn_calibrate_mfma: n_workgroups workgroups of 4 waves, each wave issuing
  *   iters rounds of four independent 32x32x16 bf16 matrix products
  *   (32768 FLOP each); total work n_workgroups * 4 * iters * 4 * 32768 FLOP.
+ *   random_operands 0: small constant operands with few distinct bits (the
+ *   highest rate the part sustains); 1: hashed random bfloat16 operands, a
+ *   different set per accumulator (the rate for data like the attention
+ *   kernels': the clock under load falls with the operands' switching).
  *   out: device float[n_workgroups * 4], one value per wave, written.
  * attn_calibrate_read: a streaming read of `bytes` (a multiple of 16, src
  *   16-byte aligned) with nontemporal 16-byte loads by n_workgroups
  *   workgroups of 256 threads, each reading its own contiguous share.
  *   out: device uint32[n_workgroups * 4], one value per wave, written.
  * The caller times the launch on `stream` (e.g. with events).  Errors: EINVAL
- * for non-positive sizes, NULL pointers, misaligned reads; EDEVICE.
+ * for non-positive sizes, NULL pointers, misaligned reads, random_operands
+ * other than 0/1; EDEVICE.
  */
-int attn_calibrate_mfma(int n_workgroups, int iters, float *out, void *stream);
+int attn_calibrate_mfma(int n_workgroups, int iters, int random_operands, float *out, void *stream);
 int attn_calibrate_read(const void *src, size_t bytes, int n_workgroups, uint32_t *out, void *stream);
 
 /* Static, human-readable name of a status code. */

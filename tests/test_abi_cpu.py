@@ -288,6 +288,20 @@ def test_importance_validation():
     assert importance(max_ctx=0) == OK
 
 
+def test_calibration_validation():
+    L = api.lib()
+    P = ctypes.c_void_p(0x1000)        # never dereferenced: every call fails validation
+    assert L.attn_calibrate_mfma(0, 10, 1, P, None) == EINVAL
+    assert L.attn_calibrate_mfma(4, 0, 0, P, None) == EINVAL
+    assert L.attn_calibrate_mfma(4, 10, 2, P, None) == EINVAL
+    assert L.attn_calibrate_mfma(4, 10, -1, P, None) == EINVAL
+    assert L.attn_calibrate_mfma(4, 10, 1, None, None) == EINVAL
+    assert L.attn_calibrate_read(P, 15, 4, P, None) == EINVAL
+    assert L.attn_calibrate_read(P, 1 << 20, 0, P, None) == EINVAL
+    assert L.attn_calibrate_read(ctypes.c_void_p(0x1008), 1 << 20, 4, P, None) == EINVAL
+    assert L.attn_calibrate_read(None, 1 << 20, 4, P, None) == EINVAL
+
+
 def test_recorded_traffic_keyed_to_the_built_code():
     """bench.py reports counter traffic only for the GPU code it was taken on:
     the key is a hash of the built library's .hip_fatbin section, and a record
