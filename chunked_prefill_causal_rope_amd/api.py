@@ -25,6 +25,7 @@ _lib = None
 
 EXPORTS = ("attn_rope_inv_freq", "attn_yarn_inv_freq", "attn_rope_apply", "attn_kv_append",
            "attn_rope_qkv", "attn_prefill_chunk", "attn_prefill_chunk_rope_next",
+           "attn_prefill_chunk_deferred", "attn_prefill_finish",
            "attn_prefill_workspace_bytes", "attn_decode",
            "attn_decode_workspace_bytes", "attn_decode_importance", "attn_calibrate_mfma",
            "attn_calibrate_read", "attn_status_string", "attn_version")
@@ -41,6 +42,12 @@ class RopeQkvArgs(ctypes.Structure):
                 ("rotary_dim", ctypes.c_int), ("rope_scale", ctypes.c_float), ("norm", ctypes.c_int),
                 ("q_norm_w", ctypes.c_void_p), ("k_norm_w", ctypes.c_void_p), ("eps", ctypes.c_double),
                 ("v_norm", ctypes.c_int)]
+
+
+class PrefillPending(ctypes.Structure):
+    """attn_prefill_pending of attn.h: a split chunk's merge owed to a later
+    launch (active), the rest the library's."""
+    _fields_ = [("active", ctypes.c_int), ("head_dim", ctypes.c_int), ("state", ctypes.c_uint64 * 16)]
 
 
 class AttnError(RuntimeError):
@@ -70,6 +77,11 @@ def lib() -> ctypes.CDLL:
                                      i, vp, vp, sz, vp]
     L.attn_prefill_chunk_rope_next.argtypes = [vp, vp, vp, i, i, i, i, i, i, i, i, vp, vp, i, i, f, i,
                                                vp, i, i, vp, vp, sz, ctypes.POINTER(RopeQkvArgs), vp]
+    pend = ctypes.POINTER(PrefillPending)
+    L.attn_prefill_chunk_deferred.argtypes = [vp, vp, vp, i, i, i, i, i, i, i, i, vp, vp, i, i, f, i,
+                                              vp, i, i, vp, vp, sz, ctypes.POINTER(RopeQkvArgs), pend, pend,
+                                              vp]
+    L.attn_prefill_finish.argtypes = [pend, vp]
     L.attn_prefill_workspace_bytes.argtypes = [i, i, i, i, i, i, i]
     L.attn_prefill_workspace_bytes.restype = sz
     L.attn_decode.argtypes = [vp, vp, vp, i, i, i, i, i, i, i, vp, i, f, i, vp, i, i, vp, vp, i, vp,
@@ -90,7 +102,8 @@ def lib() -> ctypes.CDLL:
     L.attn_status_string.restype = ctypes.c_char_p
     L.attn_version.restype = ctypes.c_char_p
     for name in ("attn_rope_inv_freq", "attn_yarn_inv_freq", "attn_rope_apply", "attn_kv_append",
-                 "attn_rope_qkv", "attn_prefill_chunk", "attn_prefill_chunk_rope_next", "attn_decode"):
+                 "attn_rope_qkv", "attn_prefill_chunk", "attn_prefill_chunk_rope_next",
+                 "attn_prefill_chunk_deferred", "attn_prefill_finish", "attn_decode"):
         getattr(L, name).restype = i
     _lib = L
     return L
@@ -262,11 +275,15 @@ def prefill_workspace_bytes(batch: Batch, n_heads: int, n_kv: int, head_dim: int
 def prefill_chunk(q: torch.Tensor, k_cache: torch.Tensor, v_cache: torch.Tensor, batch: Batch,
                   scale: float, out: torch.Tensor, workspace: torch.Tensor | None = None,
                   window: int = 0, ring: bool = False, gate: torch.Tensor | None = None,
-                  gate_mode: int = GATE_NONE, next_rope: dict | None = None):
+                  gate_mode: int = GATE_NONE, next_rope: dict | None = None,
+                  pending: PrefillPending | None = None, prev: PrefillPending | None = None):
     """Causal attention of a chunk batch; window > 0 keeps keys p-window+1..p;
     ring=True reads key j from cache row j mod cap; gate/gate_mode gate the
     output rows.  next_rope: rope_qkv's keyword arguments for the next chunk,
-    run by this call (attn_prefill_chunk_rope_next)."""
+    run by this call (attn_prefill_chunk_rope_next).  pending: a record that
+    receives this chunk's split merge instead of running it, and prev an
+    earlier chunk's record whose merge this call runs
+    (attn_prefill_chunk_deferred; see prefill_finish)."""
     n_tok, nh, hd = q.shape
     n_seq_c, n_kv, cap, hd2 = k_cache.shape
     assert hd2 == hd and out.shape == (n_tok, nh, hd) and out.dtype == torch.float32
@@ -277,16 +294,29 @@ def prefill_chunk(q: torch.Tensor, k_cache: torch.Tensor, v_cache: torch.Tensor,
             batch.n_seq, nh, n_kv, hd, cap, int(ring), n_tok, _dev(batch.cu_seq, "cu_seq", torch.int32),
             _dev(batch.start, "start", torch.int32), batch.max_chunk, batch.max_end, scale, window,
             *_gate(gate, gate_mode, n_tok, nh, hd, q.dtype), _dev(out, "out"), ws, wsb)
-    if next_rope is None:
+    nxt = None
+    if next_rope is not None:
+        nr = dict(next_rope)
+        nxt = RopeQkvArgs(*_rope_qkv_args(
+            nr["q"], nr["q_out"], nr["k_cache"], nr["v_cache"], nr["k_new"], nr["v_new"], nr["batch"],
+            nr["inv_freq"], nr["rotary_dim"], nr.get("rope_scale", 1.0), nr.get("norm", NORM_NONE),
+            nr.get("q_norm_w"), nr.get("k_norm_w"), nr.get("eps", 1e-6), nr.get("ring", False),
+            nr.get("v_norm", False)))
+    if pending is not None:
+        _check("attn_prefill_chunk_deferred", lib().attn_prefill_chunk_deferred(
+            *args, ctypes.byref(nxt) if nxt is not None else None, ctypes.byref(prev) if prev is not None else None,
+            ctypes.byref(pending), _stream()))
+        return
+    assert prev is None, "prev needs a pending record (attn_prefill_chunk_deferred)"
+    if nxt is None:
         _check("attn_prefill_chunk", lib().attn_prefill_chunk(*args, _stream()))
         return
-    nr = dict(next_rope)
-    nxt = RopeQkvArgs(*_rope_qkv_args(
-        nr["q"], nr["q_out"], nr["k_cache"], nr["v_cache"], nr["k_new"], nr["v_new"], nr["batch"],
-        nr["inv_freq"], nr["rotary_dim"], nr.get("rope_scale", 1.0), nr.get("norm", NORM_NONE),
-        nr.get("q_norm_w"), nr.get("k_norm_w"), nr.get("eps", 1e-6), nr.get("ring", False),
-        nr.get("v_norm", False)))
     _check("attn_prefill_chunk_rope_next", lib().attn_prefill_chunk_rope_next(*args, ctypes.byref(nxt), _stream()))
+
+
+def prefill_finish(pending: PrefillPending):
+    """Run the merge a pending record owes, on the current stream."""
+    _check("attn_prefill_finish", lib().attn_prefill_finish(ctypes.byref(pending), _stream()))
 
 
 def decode_workspace_bytes(n_seq: int, n_heads: int, n_kv: int, head_dim: int, max_ctx: int) -> int:

@@ -3,6 +3,7 @@
 #include <math.h>
 #include <stddef.h>
 #include <stdint.h>
+#include <string.h>
 
 #include <hip/hip_runtime.h>
 
@@ -265,12 +266,30 @@ struct NextFinish {
     int dtype;
 };
 
+// What a pending record holds: the merge a split chunk still owes, and the
+// workspace bytes its partials occupy until then.
+struct PendingState {
+    attn::MergeArgs m;
+    const char* ws_lo;
+    const char* ws_hi;
+};
+static_assert(sizeof(PendingState) <= sizeof(((attn_prefill_pending*)nullptr)->state),
+              "pending state fits the record");
+
+// An earlier chunk's merge to run in this call, and where to leave this
+// chunk's own (deferred mode when `pending` is set).
+struct MergeDefer {
+    const PendingState* prev;     // null: none owed
+    int prev_hd;
+    attn_prefill_pending* pending;
+};
+
 int prefill_chunk_impl(const void* q, const void* k_cache, const void* v_cache, int dtype,
                        int n_seq, int n_heads, int n_kv, int head_dim, int cap, int ring, int n_tok,
                        const int32_t* cu_seq, const int32_t* start, int max_chunk, int max_end,
                        float scale, int window, const void* gate, int gate_mode, int gate_ld,
                        float* out, void* workspace, size_t workspace_bytes, const NextFinish* next,
-                       hipStream_t s);
+                       const MergeDefer* defer, hipStream_t s);
 
 }  // namespace
 
@@ -313,7 +332,7 @@ int attn_prefill_chunk(const void* q, const void* k_cache, const void* v_cache, 
                        float* out, void* workspace, size_t workspace_bytes, void* stream) {
     return prefill_chunk_impl(q, k_cache, v_cache, dtype, n_seq, n_heads, n_kv, head_dim, cap, ring, n_tok,
                               cu_seq, start, max_chunk, max_end, scale, window, gate, gate_mode, gate_ld, out,
-                              workspace, workspace_bytes, nullptr, (hipStream_t)stream);
+                              workspace, workspace_bytes, nullptr, nullptr, (hipStream_t)stream);
 }
 
 int attn_prefill_chunk_rope_next(const void* q, const void* k_cache, const void* v_cache, int dtype,
@@ -334,7 +353,50 @@ int attn_prefill_chunk_rope_next(const void* q, const void* k_cache, const void*
     const NextFinish nf{&aq, &ak, next->dtype};
     return prefill_chunk_impl(q, k_cache, v_cache, dtype, n_seq, n_heads, n_kv, head_dim, cap, ring, n_tok,
                               cu_seq, start, max_chunk, max_end, scale, window, gate, gate_mode, gate_ld, out,
-                              workspace, workspace_bytes, empty ? nullptr : &nf, (hipStream_t)stream);
+                              workspace, workspace_bytes, empty ? nullptr : &nf, nullptr, (hipStream_t)stream);
+}
+
+int attn_prefill_chunk_deferred(const void* q, const void* k_cache, const void* v_cache, int dtype,
+                                int n_seq, int n_heads, int n_kv, int head_dim, int cap, int ring, int n_tok,
+                                const int32_t* cu_seq, const int32_t* start, int max_chunk, int max_end,
+                                float scale, int window, const void* gate, int gate_mode, int gate_ld,
+                                float* out, void* workspace, size_t workspace_bytes,
+                                const attn_rope_qkv_args* next, const attn_prefill_pending* prev,
+                                attn_prefill_pending* pending, void* stream) {
+    if (!pending) return ATTN_EINVAL;
+    // prev may be the record this call rewrites: take its state first
+    PendingState pv{};
+    MergeDefer d{nullptr, 0, pending};
+    if (prev && prev->active) {
+        if (prev->active != 1 || !hd_ok(prev->head_dim)) return ATTN_EINVAL;
+        memcpy(&pv, prev->state, sizeof(pv));
+        d.prev = &pv;
+        d.prev_hd = prev->head_dim;
+    }
+    attn::RopeArgs aq, ak;
+    bool empty = true;
+    if (next) {
+        const int st = rope_qkv_build(next->q, next->q_out, next->n_heads, next->k_cache, next->v_cache,
+                                      next->k_new, next->v_new, next->n_kv, next->cap, next->ring, next->dtype,
+                                      next->n_tok, next->head_dim, next->n_seq, next->cu_seq, next->start,
+                                      next->max_chunk, next->max_end, next->inv_freq, next->rotary_dim,
+                                      next->rope_scale, next->norm, next->q_norm_w, next->k_norm_w, next->eps,
+                                      next->v_norm, aq, ak, empty);
+        if (st != ATTN_OK) return st;
+    }
+    const NextFinish nf{&aq, &ak, next ? next->dtype : 0};
+    return prefill_chunk_impl(q, k_cache, v_cache, dtype, n_seq, n_heads, n_kv, head_dim, cap, ring, n_tok,
+                              cu_seq, start, max_chunk, max_end, scale, window, gate, gate_mode, gate_ld, out,
+                              workspace, workspace_bytes, next && !empty ? &nf : nullptr, &d, (hipStream_t)stream);
+}
+
+int attn_prefill_finish(const attn_prefill_pending* pending, void* stream) {
+    if (!pending) return ATTN_EINVAL;
+    if (!pending->active) return ATTN_OK;
+    if (pending->active != 1 || !hd_ok(pending->head_dim)) return ATTN_EINVAL;
+    PendingState pv;
+    memcpy(&pv, pending->state, sizeof(pv));
+    return status_of(attn::launch_prefill_merge(pv.m, pending->head_dim, (hipStream_t)stream));
 }
 
 size_t attn_decode_workspace_bytes(int n_seq, int n_heads, int n_kv, int head_dim, int max_ctx) {
@@ -353,7 +415,7 @@ int prefill_chunk_impl(const void* q, const void* k_cache, const void* v_cache, 
                        const int32_t* cu_seq, const int32_t* start, int max_chunk, int max_end,
                        float scale, int window, const void* gate, int gate_mode, int gate_ld,
                        float* out, void* workspace, size_t workspace_bytes, const NextFinish* next,
-                       hipStream_t s) {
+                       const MergeDefer* defer, hipStream_t s) {
     if (!dtype_ok(dtype) || !hd_ok(head_dim)) return ATTN_EUNSUPPORTED;
     if (n_seq < 0 || n_tok < 0 || max_chunk < 0 || max_end < 0 || n_heads <= 0 || n_kv <= 0 ||
         cap <= 0 || n_heads % n_kv != 0 || !isfinite(scale) || window < 0 || (ring != 0 && ring != 1))
@@ -366,13 +428,30 @@ int prefill_chunk_impl(const void* q, const void* k_cache, const void* v_cache, 
     if (wrapped && (window <= 0 || (long)window + max_chunk - 1 > cap)) return ATTN_ECAPACITY;
     if (wrapped && dtype == ATTN_BF16 && cap % 64 != 0) return ATTN_EUNSUPPORTED;
     if (!gate_ok(gate, gate_mode, gate_ld, head_dim)) return ATTN_EINVAL;
+    // an earlier chunk's partials stay in its workspace until its merge runs
+    const PendingState* pv = defer ? defer->prev : nullptr;
+    if (pv && workspace && workspace_bytes && (const char*)workspace < pv->ws_hi &&
+        pv->ws_lo < (const char*)workspace + workspace_bytes)
+        return ATTN_EINVAL;
     // after validation, nothing but the launches can fail: the next chunk's
     // finish runs after this chunk's attention unless it rides in its launch
     auto finish_next = [&](hipError_t e) {
         if (e == hipSuccess && next) e = attn::launch_rope_qkv(*next->q, *next->kv, next->dtype, s);
         return status_of(e);
     };
-    if (n_seq == 0 || n_tok == 0 || max_chunk == 0) return finish_next(hipSuccess);
+    // deferred mode: the earlier chunk's merge on a launch of its own (when it
+    // does not ride in this chunk's attention launch), and this chunk's record
+    auto prev_alone = [&]() { return pv ? attn::launch_prefill_merge(pv->m, defer->prev_hd, s) : hipSuccess; };
+    auto owe_nothing = [&]() {
+        if (defer) {
+            defer->pending->active = 0;
+            defer->pending->head_dim = head_dim;
+        }
+    };
+    if (n_seq == 0 || n_tok == 0 || max_chunk == 0) {
+        owe_nothing();
+        return finish_next(prev_alone());
+    }
     const attn::GateRef gref{gate, gate_mode, gate_ld, dtype == ATTN_BF16};
     if (!q || !k_cache || !v_cache || !out || !cu_seq || !start) return ATTN_EINVAL;
     if (n_seq > 65535) return ATTN_EINVAL;
@@ -398,7 +477,10 @@ int prefill_chunk_impl(const void* q, const void* k_cache, const void* v_cache, 
         a.window = window;
         a.ring = wrapped;
         a.gate = gref;
-        return finish_next(attn::launch_attend_f32(a, s));
+        owe_nothing();
+        hipError_t e = prev_alone();
+        if (e == hipSuccess) e = attn::launch_attend_f32(a, s);
+        return finish_next(e);
     }
     if (small_chunk(max_chunk, group) && workspace &&
         workspace_bytes >= decode_part_bytes(n_seq * max_chunk, n_heads, head_dim, 1)) {
@@ -435,7 +517,10 @@ int prefill_chunk_impl(const void* q, const void* k_cache, const void* v_cache, 
         d.cu_seq = cu_seq;
         d.start = start;
         d.n_q = max_chunk;
-        return finish_next(attn::launch_decode_bf16(d, s));
+        owe_nothing();
+        hipError_t e = prev_alone();
+        if (e == hipSuccess) e = attn::launch_decode_bf16(d, s);
+        return finish_next(e);
     }
     attn::PrefillArgs a{};
     a.q = q;
@@ -491,8 +576,37 @@ int prefill_chunk_impl(const void* q, const void* k_cache, const void* v_cache, 
             a.next_blocks = (int)nb;
         }
     }
-    hipError_t e = attn::launch_prefill_bf16(a, s);
-    if (e == hipSuccess && plan.split) e = attn::launch_prefill_combine(a, s);
+    // an earlier chunk's merge of the same head size rides in this launch when
+    // it needs at most half the CUs' worth of workgroups: there it takes the
+    // attention kernel's footprint, one workgroup of two merge blocks per CU,
+    // where its own launch runs eight blocks per CU (measured: 128 merge
+    // workgroups per call gain 3-5 % per step, 2560 lose 2 %)
+    bool ride = pv && defer->prev_hd == head_dim;
+    if (ride) {
+        const int gx = attn::merge_blocks_x(pv->m, head_dim);
+        const long nb = ((long)gx * pv->m.n_seq + 1) / 2;
+        ride = nb <= attn::device_cus() / 2;
+        if (ride) {
+            a.prev = pv->m;
+            a.prev_gx = gx;
+            a.prev_blocks = (int)nb;
+        }
+    }
+    hipError_t e = ride ? hipSuccess : prev_alone();
+    if (e == hipSuccess) e = attn::launch_prefill_bf16(a, s);
+    if (defer) {
+        // this chunk's merge is owed to a later launch
+        owe_nothing();
+        if (plan.split) {
+            const PendingState st{attn::merge_args(a), (const char*)workspace,
+                                  (const char*)workspace + plan.ws_bytes};
+            memset(defer->pending->state, 0, sizeof(defer->pending->state));
+            memcpy(defer->pending->state, &st, sizeof(st));
+            defer->pending->active = 1;
+        }
+    } else if (e == hipSuccess && plan.split) {
+        e = attn::launch_prefill_combine(a, s);
+    }
     return fuse ? status_of(e) : finish_next(e);
 }
 

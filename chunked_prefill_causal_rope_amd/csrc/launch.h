@@ -57,6 +57,17 @@ struct RopeTokArgs {
 bool rope_token_path(const RopeArgs& a);
 RopeTokArgs rope_token_args(const RopeArgs& q, const RopeArgs& kv);
 
+// Merge of a split chunk's partials into its output rows: what the merge
+// reads (partials, schedule table, batch offsets, gate) and writes (out).
+struct MergeArgs {
+    const float* part;
+    const int* table;
+    float* out;
+    const int32_t* cu_seq;
+    GateRef gate;
+    int n_seq, n_heads, n_kv, group, max_chunk, n_tok, rows_per_tile, n_qtiles;
+};
+
 // Causal attention of packed chunk rows over the head-major cache.
 struct PrefillArgs {
     const void* q;
@@ -82,6 +93,11 @@ struct PrefillArgs {
     // r / (next_chunk * next_nhb)
     RopeTokArgs next;
     int next_blocks, next_chunk, next_nhb;
+    // an earlier split chunk's merge (same head size), run by prev_blocks
+    // workgroups past those: each takes two merge blocks of 256 threads,
+    // block f = x + prev_gx * sequence
+    MergeArgs prev;
+    int prev_blocks, prev_gx;
 };
 // Launch plan of the bf16 prefill, from host scalars only: query rows per
 // workgroup (128 or 256), row tiles, whether to split, grid, workspace.
@@ -95,6 +111,11 @@ hipError_t launch_prefill_bf16(const PrefillArgs& a, hipStream_t stream);
 // compute units of the current device (256 if the query fails)
 int device_cus();
 hipError_t launch_prefill_combine(const PrefillArgs& a, hipStream_t stream);
+// the merge of a split chunk on its own launch, and its shape: merge blocks
+// per sequence (256 threads each)
+MergeArgs merge_args(const PrefillArgs& a);
+hipError_t launch_prefill_merge(const MergeArgs& m, int head_dim, hipStream_t stream);
+int merge_blocks_x(const MergeArgs& m, int head_dim);
 
 // float32 path (prefill rows and decode rows) -- vector ALU, one wave per row.
 struct AttendF32Args {

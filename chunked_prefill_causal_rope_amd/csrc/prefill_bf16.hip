@@ -245,7 +245,7 @@ __device__ PrefillItem split_schedule(const PrefillArgs& a, int item) {
         if (lane >= o) incl += v;
     }
     const int excl = incl - cnt;
-    if (blockIdx.x == 0 && threadIdx.x < 64 && lane < n_groups) {
+    if (item == 0 && threadIdx.x < 64 && lane < n_groups) {
         a.table[2 * lane] = excl;
         a.table[2 * lane + 1] = nsp;
     }
@@ -390,14 +390,54 @@ struct alignas(16) PingPongSmem {
 // cache append), using the kernel's LDS for the token's tables.  The next
 // chunk writes cache rows past every key this chunk reads, so the two are
 // independent.
+template <int HD>
+__device__ __forceinline__ void merge_rows(const MergeArgs& a, int bx, int b, int tid);
+
 template <int HD, typename Sm>
-__device__ __forceinline__ void next_chunk_role(const PrefillArgs& a, Sm& sm) {
+__device__ __forceinline__ void next_chunk_role(const PrefillArgs& a, Sm& sm, int r) {
     static_assert(sizeof(RopeTokSmem<HD>) <= sizeof(Sm), "token tables fit the attention LDS");
-    const int r = blockIdx.x - a.grid;
     const int i = r % a.next_chunk;
     const int hb = (r / a.next_chunk) % a.next_nhb;
     const int b = r / (a.next_chunk * a.next_nhb);
     rope_token_body<uint16_t, HD, 512>(a.next, i, hb, b, reinterpret_cast<RopeTokSmem<HD>&>(sm));
+}
+
+// An earlier split chunk's merge, workgroup r of prev_blocks: two merge
+// blocks of 256 threads each (threads 0-255 and 256-511).  The merge reads
+// partials and writes output rows that this launch's attention does not
+// touch.
+template <int HD>
+__device__ __forceinline__ void prev_merge_role(const PrefillArgs& a, int r) {
+    if (a.prev_gx <= 0) return;
+    const int f = 2 * r + (int)(threadIdx.x >> 8);
+    const int by = f / a.prev_gx;
+    if (by < a.prev.n_seq) merge_rows<HD>(a.prev, f - by * a.prev_gx, by, threadIdx.x & 255);
+}
+
+// Workgroups besides the attention items.  The grid is [merge roles when
+// ATTN_MERGE_FIRST] attention items, next-chunk roles, [merge roles]; wg is
+// the workgroup's index past the leading merge roles.  Leading, the merge
+// starts at once beside the first attention items instead of after the
+// next-chunk roles (measured on 128-token chunks of 32 heads, 128 merge
+// workgroups: 0.62 against 0.64 ms per step).
+#ifndef ATTN_MERGE_FIRST
+#define ATTN_MERGE_FIRST 1
+#endif
+__device__ __forceinline__ int attention_wg(const PrefillArgs& a) {
+    return (int)blockIdx.x - (ATTN_MERGE_FIRST ? a.prev_blocks : 0);
+}
+template <int HD, typename Sm>
+__device__ __forceinline__ void extra_role(const PrefillArgs& a, Sm& sm, int wg) {
+    if (wg < 0) {
+        prev_merge_role<HD>(a, (int)blockIdx.x);
+        return;
+    }
+    const int r = wg - a.grid;
+    if (r < a.next_blocks) {
+        next_chunk_role<HD>(a, sm, r);
+        return;
+    }
+    prev_merge_role<HD>(a, r - a.next_blocks);
 }
 
 template <int HD, bool WIN>
@@ -412,8 +452,9 @@ __global__ __launch_bounds__(512, 1) void prefill_pp_kernel(PrefillArgs a) {
     constexpr int NKK = HD / 16;                  // K-steps of a score product
     constexpr int TILE_ROWS = 256;                // query rows per workgroup
     __shared__ Sm sm;
-    if (blockIdx.x >= a.grid) {
-        next_chunk_role<HD>(a, sm);
+    const int wg = attention_wg(a);
+    if (wg < 0 || wg >= a.grid) {
+        extra_role<HD>(a, sm, wg);
         return;
     }
 
@@ -424,7 +465,7 @@ __global__ __launch_bounds__(512, 1) void prefill_pp_kernel(PrefillArgs a) {
     const int hf = lane >> 5;                     // wave half
     const int rl = lane & 31;
 
-    const int item = blockIdx.x;
+    const int item = wg;
     PrefillItem itm;
     if (a.split) {
         itm = split_schedule(a, item);
@@ -757,8 +798,9 @@ __global__ __launch_bounds__(512, 1) void prefill_bf16_ks_kernel(PrefillArgs a) 
     constexpr int NKK = HD / 16;                  // K-steps of a score product
     constexpr int TILE_ROWS = 128;                // query rows per workgroup
     __shared__ Sm sm;
-    if (blockIdx.x >= a.grid) {
-        next_chunk_role<HD>(a, sm);
+    const int wg = attention_wg(a);
+    if (wg < 0 || wg >= a.grid) {
+        extra_role<HD>(a, sm, wg);
         return;
     }
 
@@ -770,7 +812,7 @@ __global__ __launch_bounds__(512, 1) void prefill_bf16_ks_kernel(PrefillArgs a) 
     const int hf = lane >> 5;                     // wave half
     const int rl = lane & 31;
 
-    const int item = blockIdx.x;
+    const int item = wg;
     PrefillItem itm;
     if (a.split) {
         itm = split_schedule(a, item);
@@ -1077,17 +1119,18 @@ struct CombineShape {
     static constexpr int RPW = 64 / LPR;      // rows per wave
     static constexpr int RPB = 4 * RPW;       // rows per workgroup
 };
+// Merge block (bx, b) of 256 threads, thread tid (the standalone kernel's
+// blockIdx.x, blockIdx.y and threadIdx.x).
 template <int HD>
-__global__ __launch_bounds__(256) void prefill_combine_kernel(PrefillArgs a) {
+__device__ __forceinline__ void merge_rows(const MergeArgs& a, int bx, int b, int tid) {
     using Sh = CombineShape<HD>;
     constexpr int LPR = Sh::LPR, RPB = Sh::RPB;
     constexpr int PS = part_row_words(HD);
     constexpr int NB = 4;                     // parts per load batch
-    const int b = blockIdx.y;
     const int R = a.rows_per_tile;
-    const int g = blockIdx.x % a.n_kv;
-    const int rblk = (blockIdx.x / a.n_kv) % (R / RPB);
-    const int qt = blockIdx.x / a.n_kv / (R / RPB);
+    const int g = bx % a.n_kv;
+    const int rblk = (bx / a.n_kv) % (R / RPB);
+    const int qt = bx / a.n_kv / (R / RPB);
     if (b >= a.n_seq || qt >= a.n_qtiles) return;
     const int first = a.table[2 * (b * a.n_qtiles + qt)];
     const int S = a.table[2 * (b * a.n_qtiles + qt) + 1];
@@ -1096,9 +1139,9 @@ __global__ __launch_bounds__(256) void prefill_combine_kernel(PrefillArgs a) {
     const int t0 = a.cu_seq[b];
     const int len = min(a.cu_seq[b + 1] - t0, a.max_chunk);
     const int rows_b = len * G;
-    const int lane = threadIdx.x & 63;
+    const int lane = tid & 63;
     const int j = lane % LPR;                  // this lane's 8 dims: 8j .. 8j+7
-    const int rl = rblk * RPB + (threadIdx.x / 64) * (64 / LPR) + lane / LPR;
+    const int rl = rblk * RPB + (tid / 64) * (64 / LPR) + lane / LPR;
     const int r = qt * R + rl;
     const int i = r / G;
     const int h = g * G + (r - i * G);
@@ -1200,6 +1243,11 @@ __global__ __launch_bounds__(256) void prefill_combine_kernel(PrefillArgs a) {
         make_float4(o[0] * inv * gf[0], o[1] * inv * gf[1], o[2] * inv * gf[2], o[3] * inv * gf[3]);
     *reinterpret_cast<float4*>(orow + 4) =
         make_float4(o[4] * inv * gf[4], o[5] * inv * gf[5], o[6] * inv * gf[6], o[7] * inv * gf[7]);
+}
+
+template <int HD>
+__global__ __launch_bounds__(256) void prefill_combine_kernel(MergeArgs a) {
+    merge_rows<HD>(a, blockIdx.x, blockIdx.y, threadIdx.x);
 }
 
 // Launch plan.  256-row workgroups (8 waves, deeper prefetch) when they
@@ -1313,7 +1361,7 @@ static void launch_prefill_win(const PrefillArgs& a, dim3 grid, hipStream_t stre
 }
 
 hipError_t launch_prefill_bf16(const PrefillArgs& a, hipStream_t stream) {
-    const long blocks = (long)a.grid + a.next_blocks;
+    const long blocks = (long)a.grid + a.next_blocks + a.prev_blocks;
     if (blocks <= 0) return hipSuccess;
     const dim3 grid((unsigned)blocks);
     if (a.window > 0)
@@ -1323,15 +1371,42 @@ hipError_t launch_prefill_bf16(const PrefillArgs& a, hipStream_t stream) {
     return hipGetLastError();
 }
 
+MergeArgs merge_args(const PrefillArgs& a) {
+    MergeArgs m{};
+    m.part = a.part;
+    m.table = a.table;
+    m.out = a.out;
+    m.cu_seq = a.cu_seq;
+    m.gate = a.gate;
+    m.n_seq = a.n_seq;
+    m.n_heads = a.n_heads;
+    m.n_kv = a.n_kv;
+    m.group = a.group;
+    m.max_chunk = a.max_chunk;
+    m.n_tok = a.n_tok;
+    m.rows_per_tile = a.rows_per_tile;
+    m.n_qtiles = a.n_qtiles;
+    return m;
+}
+
+int merge_blocks_x(const MergeArgs& m, int head_dim) {
+    const int rpb = head_dim == 128 ? CombineShape<128>::RPB : CombineShape<64>::RPB;
+    return m.n_qtiles * m.n_kv * (m.rows_per_tile / rpb);
+}
+
+hipError_t launch_prefill_merge(const MergeArgs& m, int head_dim, hipStream_t stream) {
+    if (m.n_seq <= 0) return hipSuccess;
+    const dim3 grid((unsigned)merge_blocks_x(m, head_dim), (unsigned)m.n_seq);
+    if (head_dim == 128)
+        prefill_combine_kernel<128><<<grid, dim3(256), 0, stream>>>(m);
+    else
+        prefill_combine_kernel<64><<<grid, dim3(256), 0, stream>>>(m);
+    return hipGetLastError();
+}
+
 hipError_t launch_prefill_combine(const PrefillArgs& a, hipStream_t stream) {
     if (!a.split || a.n_seq <= 0) return hipSuccess;
-    const int rpb = a.head_dim == 128 ? CombineShape<128>::RPB : CombineShape<64>::RPB;
-    const dim3 grid((unsigned)(a.n_qtiles * a.n_kv * (a.rows_per_tile / rpb)), (unsigned)a.n_seq);
-    if (a.head_dim == 128)
-        prefill_combine_kernel<128><<<grid, dim3(256), 0, stream>>>(a);
-    else
-        prefill_combine_kernel<64><<<grid, dim3(256), 0, stream>>>(a);
-    return hipGetLastError();
+    return launch_prefill_merge(merge_args(a), a.head_dim, stream);
 }
 
 }  // namespace attn

@@ -83,6 +83,9 @@ class ChunkedPrefill:
                 out=torch.empty((n_tok, nh, hd), dtype=torch.float32, device=device)))
         ws = max(api.prefill_workspace_bytes(s["batch"], nh, nkv, hd) for s in self.steps)
         self.workspace = torch.empty(max(ws, 16) // 4 + 1, dtype=torch.float32, device=device)
+        # the deferred loop alternates two: a chunk's partials wait in theirs
+        # until the next chunk's launch merges them
+        self.workspace_alt = torch.empty_like(self.workspace)
 
     def rope_kwargs(self, i: int) -> dict:
         """api.rope_qkv's keyword arguments for chunk i."""
@@ -107,24 +110,41 @@ class ChunkedPrefill:
         if attend:
             self.attend_step(i)
 
-    def attend_step(self, i: int, next_rope: dict | None = None):
+    def attend_step(self, i: int, next_rope: dict | None = None, pending=None, prev=None,
+                    workspace: torch.Tensor | None = None):
         s = self.steps[i]
         api.prefill_chunk(s["q_rot"], self.k_cache, self.v_cache, s["batch"], self.w.scale,
-                          s["out"], self.workspace, window=self.w.window, ring=self.w.ring,
-                          gate=s["gate"], gate_mode=self.w.gate_mode, next_rope=next_rope)
+                          s["out"], self.workspace if workspace is None else workspace,
+                          window=self.w.window, ring=self.w.ring, gate=s["gate"],
+                          gate_mode=self.w.gate_mode, next_rope=next_rope, pending=pending, prev=prev)
 
-    def run_all(self, fused: bool = True, pipelined: bool = True):
+    def run_all(self, fused: bool = True, pipelined: bool = True, deferred: bool = True):
         """The chunk loop.  pipelined: chunk 0's finish, then per chunk one
         call that attends it and finishes the next chunk
-        (attn_prefill_chunk_rope_next); otherwise finish + attend per chunk."""
+        (attn_prefill_chunk_rope_next); deferred (with pipelined): the same
+        calls with each split chunk's merge run in the next chunk's launch
+        (attn_prefill_chunk_deferred, workspaces alternating, the last merge
+        by attn_prefill_finish); otherwise finish + attend per chunk."""
         n = len(self.steps)
         if not (fused and pipelined):
             for i in range(n):
                 self.run_step(i, fused=fused)
             return
         api.rope_qkv(**self.rope_kwargs(0))
+        if not deferred:
+            for i in range(n):
+                self.attend_step(i, self.rope_kwargs(i + 1) if i + 1 < n else None)
+            return
+        recs = (api.PrefillPending(), api.PrefillPending())
+        wss = (self.workspace, self.workspace_alt)
+        prev = None
         for i in range(n):
-            self.attend_step(i, self.rope_kwargs(i + 1) if i + 1 < n else None)
+            cur = recs[i % 2]
+            self.attend_step(i, self.rope_kwargs(i + 1) if i + 1 < n else None, pending=cur, prev=prev,
+                             workspace=wss[i % 2])
+            prev = cur
+        if prev is not None:
+            api.prefill_finish(prev)
 
     def gather(self, key: str) -> torch.Tensor:
         """Per-token results of every step, back in the packed input order."""

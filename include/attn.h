@@ -299,6 +299,63 @@ int attn_prefill_chunk_rope_next(const void *q, const void *k_cache, const void 
                                  void *stream);
 
 /*
+ * A split chunk's merge left for a later launch, recorded by
+ * attn_prefill_chunk_deferred and run by the next such call (as its prev) or
+ * by attn_prefill_finish.  active is 1 while that chunk's output rows wait for
+ * their merge, 0 when nothing is owed; head_dim and state belong to the
+ * library (device pointers and sizes of that chunk's call) and must not be
+ * changed.  Host memory, owned by the caller.
+ */
+typedef struct attn_prefill_pending {
+    int active;
+    int head_dim;
+    uint64_t state[16];
+} attn_prefill_pending;
+
+/*
+ * attn_prefill_chunk_rope_next with the split merge of each chunk moved into a
+ * later launch: the merge of log-sum-exp partials is the same computation as
+ * in attn_prefill_chunk (it exists because the max-subtracted softmax of [ATT]
+ * fn attention_head lets parts of a key range be combined exactly), run
+ * elsewhere.  When this chunk splits, its attention leaves the partials in
+ * `workspace` and *pending records the merge owed: this chunk's rows of `out`
+ * are final only once it has run.  The merge *prev owes (an earlier chunk's
+ * record; NULL or inactive for none) runs in this call: in this chunk's
+ * attention launch, in workgroups past the attention items, when this chunk
+ * takes the bf16 prefill kernels with prev's head_dim, otherwise on a launch
+ * of its own first.  A loop of such calls is one launch per chunk where
+ * attn_prefill_chunk + attn_rope_qkv take up to three.
+ *   next     the next chunk's attn_rope_qkv arguments, or NULL (as in
+ *            attn_prefill_chunk_rope_next, with its precondition)
+ *   prev     an earlier chunk's record, or NULL; read before *pending is
+ *            written (the two may be the same record)
+ *   pending  written (not NULL): this chunk's merge, or active = 0
+ * prev's partials stay in prev's workspace until its merge runs, so this
+ * call's workspace must not overlap it (alternate two workspaces), and prev's
+ * output rows, batch arrays and gate values must stay valid until then; after
+ * the last chunk, run attn_prefill_finish on its record.  The results are
+ * those of the same chunks through attn_prefill_chunk.
+ * Errors: those of attn_prefill_chunk and attn_rope_qkv, checked before
+ * anything is launched; EINVAL for a NULL pending, an invalid prev record or
+ * overlapping workspaces.
+ */
+int attn_prefill_chunk_deferred(const void *q, const void *k_cache, const void *v_cache, int dtype,
+                                int n_seq, int n_heads, int n_kv, int head_dim, int cap, int ring,
+                                int n_tok,
+                                const int32_t *cu_seq, const int32_t *start, int max_chunk,
+                                int max_end, float scale, int window, const void *gate,
+                                int gate_mode, int gate_ld, float *out, void *workspace,
+                                size_t workspace_bytes, const attn_rope_qkv_args *next,
+                                const attn_prefill_pending *prev, attn_prefill_pending *pending,
+                                void *stream);
+
+/*
+ * Runs the merge a record owes, on `stream` (nothing for an inactive record).
+ * Errors: EINVAL for NULL or an invalid record; EDEVICE.
+ */
+int attn_prefill_finish(const attn_prefill_pending *pending, void *stream);
+
+/*
  * Workspace, in bytes, that lets attn_prefill_chunk split the key range as far
  * as it chooses for these sizes (the split is this library's own scheduling,
  * not a step of the pages: [ATT] fn attention_head's max-subtracted softmax is

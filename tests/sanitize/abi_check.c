@@ -61,7 +61,34 @@ int main(void)
     EXPECT(attn_decode_importance((const float *)P, 4, 32, 100, I, 4096, (float *)P, 4096, 1, NULL),
            ATTN_EINVAL);
     EXPECT(attn_calibrate_read(P, 15, 8, (uint32_t *)P, NULL), ATTN_EINVAL);
-    EXPECT(attn_calibrate_mfma(0, 8, (float *)P, NULL), ATTN_EINVAL);
+    EXPECT(attn_calibrate_mfma(0, 8, 1, (float *)P, NULL), ATTN_EINVAL);
+    EXPECT(attn_calibrate_mfma(4, 8, 2, (float *)P, NULL), ATTN_EINVAL);
+    /* the deferred chunk step: records it did not write are refused; with
+       nothing to attend and nothing owed it launches nothing */
+    {
+        attn_prefill_pending rec, bad;
+        memset(&rec, 0, sizeof(rec));
+        memset(&bad, 0, sizeof(bad));
+        bad.active = 1;
+        bad.head_dim = 96;
+        EXPECT(attn_prefill_chunk_deferred(P, P, P, ATTN_BF16, 1, 8, 2, 128, 256, 0, 16, I, I, 16, 64, 0.088f, 0,
+                                           NULL, 0, 0, (float *)P, NULL, 0, NULL, NULL, NULL, NULL),
+               ATTN_EINVAL);
+        EXPECT(attn_prefill_chunk_deferred(P, P, P, ATTN_BF16, 1, 8, 2, 128, 256, 0, 16, I, I, 16, 64, 0.088f, 0,
+                                           NULL, 0, 0, (float *)P, NULL, 0, NULL, &bad, &rec, NULL),
+               ATTN_EINVAL);
+        EXPECT(attn_prefill_chunk_deferred(P, P, P, ATTN_BF16, 1, 8, 2, 128, 256, 0, 16, I, I, 16, 257, 0.088f, 0,
+                                           NULL, 0, 0, (float *)P, NULL, 0, NULL, NULL, &rec, NULL),
+               ATTN_ECAPACITY);
+        rec.active = 1;
+        EXPECT(attn_prefill_chunk_deferred(P, P, P, ATTN_BF16, 0, 8, 2, 128, 256, 0, 16, I, I, 16, 64, 0.088f, 0,
+                                           NULL, 0, 0, (float *)P, NULL, 0, NULL, NULL, &rec, NULL),
+               ATTN_OK);
+        EXPECT(rec.active, 0);
+        EXPECT(attn_prefill_finish(&rec, NULL), ATTN_OK);
+        EXPECT(attn_prefill_finish(&bad, NULL), ATTN_EINVAL);
+        EXPECT(attn_prefill_finish(NULL, NULL), ATTN_EINVAL);
+    }
     /* planners: sizes from host scalars only */
     size_t ws = attn_prefill_workspace_bytes(1, 32, 8, 128, 128, 128, 4096);
     if (!(ws > 256 && (ws - 256) % (128 * (16 + 2 * 128)) == 0)) {

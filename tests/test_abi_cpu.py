@@ -205,6 +205,59 @@ def test_prefill_rope_next_validation():
     assert prefill_rope_next({"n_seq": 0}, n_seq=0) == OK
 
 
+def prefill_deferred(nxt, prev=None, pending="new", **kw):
+    """attn_prefill_chunk_deferred with prefill_rope_next()'s defaults; nxt as
+    there (None: no next chunk); prev / pending: PrefillPending records (or
+    None for NULL; pending defaults to a fresh record)."""
+    a = dict(q=P, k=P, v=P, dtype=1, n_seq=1, nh=8, nkv=2, hd=128, cap=256, ring=0, n_tok=16, cu=P, st=P,
+             max_chunk=16, max_end=64, scale=0.088, window=0, gate=None, gate_mode=0, gate_ld=0,
+             out=P, ws=None, wsb=0, stream=None)
+    a.update(kw)
+    ptr = None
+    if nxt is not None:
+        r = dict(q=P, q_out=P, n_heads=8, k_cache=P, v_cache=P, k_new=P, v_new=P, n_kv=2, cap=256, ring=0,
+                 dtype=1, n_tok=16, head_dim=128, n_seq=1, cu_seq=P, start=P, max_chunk=16, max_end=80,
+                 inv_freq=P, rotary_dim=128, rope_scale=1.0, norm=0, q_norm_w=None, k_norm_w=None, eps=1e-6,
+                 v_norm=0)
+        r.update(nxt)
+        r = {k: (v.value if isinstance(v, ctypes.c_void_p) else v) for k, v in r.items()}
+        ptr = ctypes.byref(api.RopeQkvArgs(**r))
+    if isinstance(pending, str):
+        pending = api.PrefillPending()
+    return api.lib().attn_prefill_chunk_deferred(
+        a["q"], a["k"], a["v"], a["dtype"], a["n_seq"], a["nh"], a["nkv"], a["hd"], a["cap"], a["ring"],
+        a["n_tok"], a["cu"], a["st"], a["max_chunk"], a["max_end"], a["scale"], a["window"], a["gate"],
+        a["gate_mode"], a["gate_ld"], a["out"], a["ws"], a["wsb"], ptr,
+        ctypes.byref(prev) if prev is not None else None,
+        ctypes.byref(pending) if pending is not None else None, a["stream"])
+
+
+def test_prefill_deferred_validation():
+    L = api.lib()
+    assert prefill_deferred(None, pending=None) == EINVAL
+    # every error of the chunk and of the next chunk's finish, before any launch
+    assert prefill_deferred({"max_end": 300}) == ECAP
+    assert prefill_deferred({"head_dim": 96}) == EUNSUP
+    assert prefill_deferred(None, max_end=257) == ECAP
+    assert prefill_deferred(None, hd=96) == EUNSUP
+    assert prefill_deferred(None, gate_mode=1) == EINVAL
+    # a record the library did not write
+    bad = api.PrefillPending()
+    bad.active = 2
+    assert prefill_deferred(None, prev=bad) == EINVAL
+    assert L.attn_prefill_finish(ctypes.byref(bad), None) == EINVAL
+    bad.active, bad.head_dim = 1, 96
+    assert prefill_deferred(None, prev=bad) == EINVAL
+    assert L.attn_prefill_finish(ctypes.byref(bad), None) == EINVAL
+    assert L.attn_prefill_finish(None, None) == EINVAL
+    # nothing owed, nothing to run: OK without a launch, and the record says so
+    rec = api.PrefillPending()
+    rec.active = 1
+    assert prefill_deferred(None, pending=rec, n_seq=0) == OK and rec.active == 0 and rec.head_dim == 128
+    assert prefill_deferred({"n_tok": 0}, prev=rec, pending=rec, n_tok=0) == OK and rec.active == 0
+    assert L.attn_prefill_finish(ctypes.byref(rec), None) == OK
+
+
 def rope(**kw):
     a = dict(x=P, y=P, dtype=0, n_tok=4, nh=4, hd=64, n_seq=1, cu=P, st=P, max_chunk=4, f=P,
              rd=64, rs=1.0, norm=0, w=None, eps=1e-6)
