@@ -415,29 +415,36 @@ __device__ __forceinline__ void prev_merge_role(const PrefillArgs& a, int r) {
 }
 
 // Workgroups besides the attention items.  The grid is [merge roles when
-// ATTN_MERGE_FIRST] attention items, next-chunk roles, [merge roles]; wg is
-// the workgroup's index past the leading merge roles.  Leading, the merge
-// starts at once beside the first attention items instead of after the
-// next-chunk roles (measured on 128-token chunks of 32 heads, 128 merge
-// workgroups: 0.62 against 0.64 ms per step).
+// ATTN_MERGE_FIRST] [next-chunk roles when ATTN_NEXT_FIRST] attention items
+// [next-chunk roles] [merge roles]; wg is the workgroup's index past the
+// leading roles.  Leading, the merge starts at once beside the first
+// attention items instead of after the next-chunk roles (measured on
+// 128-token chunks of 32 heads, 128 merge workgroups: 0.62 against 0.64 ms
+// per step); the next-chunk roles, 256 workgroups there, are better last
+// (0.61 against 0.65 ms leading).
 #ifndef ATTN_MERGE_FIRST
 #define ATTN_MERGE_FIRST 1
 #endif
+#ifndef ATTN_NEXT_FIRST
+#define ATTN_NEXT_FIRST 0
+#endif
 __device__ __forceinline__ int attention_wg(const PrefillArgs& a) {
-    return (int)blockIdx.x - (ATTN_MERGE_FIRST ? a.prev_blocks : 0);
+    return (int)blockIdx.x - (ATTN_MERGE_FIRST ? a.prev_blocks : 0) - (ATTN_NEXT_FIRST ? a.next_blocks : 0);
 }
 template <int HD, typename Sm>
 __device__ __forceinline__ void extra_role(const PrefillArgs& a, Sm& sm, int wg) {
     if (wg < 0) {
-        prev_merge_role<HD>(a, (int)blockIdx.x);
+        const int idx = (int)blockIdx.x - (ATTN_MERGE_FIRST ? a.prev_blocks : 0);
+        if (idx < 0) prev_merge_role<HD>(a, (int)blockIdx.x);
+        else next_chunk_role<HD>(a, sm, idx);
         return;
     }
     const int r = wg - a.grid;
-    if (r < a.next_blocks) {
+    if (!ATTN_NEXT_FIRST && r < a.next_blocks) {
         next_chunk_role<HD>(a, sm, r);
         return;
     }
-    prev_merge_role<HD>(a, r - a.next_blocks);
+    prev_merge_role<HD>(a, r - (ATTN_NEXT_FIRST ? 0 : a.next_blocks));
 }
 
 template <int HD, bool WIN>
