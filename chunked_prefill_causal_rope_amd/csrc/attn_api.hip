@@ -273,8 +273,38 @@ struct PendingState {
     const char* ws_lo;
     const char* ws_hi;
 };
-static_assert(sizeof(PendingState) <= sizeof(((attn_prefill_pending*)nullptr)->state),
-              "pending state fits the record");
+constexpr int kPendingWords = sizeof(((attn_prefill_pending*)nullptr)->state) / sizeof(uint64_t);
+static_assert(sizeof(PendingState) <= sizeof(uint64_t) * (kPendingWords - 1),
+              "pending state fits the record beside its check word");
+
+// The record's last word checks the rest (FNV-1a over head_dim and the state
+// words), so a record the library did not write -- uninitialised memory with
+// active set -- is refused instead of launching a merge on stray pointers.
+uint64_t pending_check(const attn_prefill_pending& r) {
+    uint64_t h = 1469598103934665603ull;
+    auto mix = [&](uint64_t w) {
+        for (int i = 0; i < 8; ++i) {
+            h ^= (w >> (8 * i)) & 0xffu;
+            h *= 1099511628211ull;
+        }
+    };
+    mix((uint64_t)(uint32_t)r.head_dim);
+    for (int i = 0; i < kPendingWords - 1; ++i) mix(r.state[i]);
+    return h;
+}
+void pending_write(attn_prefill_pending* r, int head_dim, const PendingState& st) {
+    memset(r->state, 0, sizeof(r->state));
+    memcpy(r->state, &st, sizeof(st));
+    r->head_dim = head_dim;
+    r->state[kPendingWords - 1] = pending_check(*r);
+    r->active = 1;
+}
+// a record the library wrote and that owes a merge: its state in *st
+bool pending_read(const attn_prefill_pending& r, PendingState* st) {
+    if (r.active != 1 || !hd_ok(r.head_dim) || r.state[kPendingWords - 1] != pending_check(r)) return false;
+    memcpy(st, r.state, sizeof(*st));
+    return true;
+}
 
 // An earlier chunk's merge to run in this call, and where to leave this
 // chunk's own (deferred mode when `pending` is set).
@@ -368,8 +398,7 @@ int attn_prefill_chunk_deferred(const void* q, const void* k_cache, const void* 
     PendingState pv{};
     MergeDefer d{nullptr, 0, pending};
     if (prev && prev->active) {
-        if (prev->active != 1 || !hd_ok(prev->head_dim)) return ATTN_EINVAL;
-        memcpy(&pv, prev->state, sizeof(pv));
+        if (!pending_read(*prev, &pv)) return ATTN_EINVAL;
         d.prev = &pv;
         d.prev_hd = prev->head_dim;
     }
@@ -393,9 +422,8 @@ int attn_prefill_chunk_deferred(const void* q, const void* k_cache, const void* 
 int attn_prefill_finish(const attn_prefill_pending* pending, void* stream) {
     if (!pending) return ATTN_EINVAL;
     if (!pending->active) return ATTN_OK;
-    if (pending->active != 1 || !hd_ok(pending->head_dim)) return ATTN_EINVAL;
     PendingState pv;
-    memcpy(&pv, pending->state, sizeof(pv));
+    if (!pending_read(*pending, &pv)) return ATTN_EINVAL;
     return status_of(attn::launch_prefill_merge(pv.m, pending->head_dim, (hipStream_t)stream));
 }
 
@@ -600,9 +628,7 @@ int prefill_chunk_impl(const void* q, const void* k_cache, const void* v_cache, 
         if (plan.split) {
             const PendingState st{attn::merge_args(a), (const char*)workspace,
                                   (const char*)workspace + plan.ws_bytes};
-            memset(defer->pending->state, 0, sizeof(defer->pending->state));
-            memcpy(defer->pending->state, &st, sizeof(st));
-            defer->pending->active = 1;
+            pending_write(defer->pending, head_dim, st);
         }
     } else if (e == hipSuccess && plan.split) {
         e = attn::launch_prefill_combine(a, s);

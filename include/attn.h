@@ -303,8 +303,9 @@ int attn_prefill_chunk_rope_next(const void *q, const void *k_cache, const void 
  * attn_prefill_chunk_deferred and run by the next such call (as its prev) or
  * by attn_prefill_finish.  active is 1 while that chunk's output rows wait for
  * their merge, 0 when nothing is owed; head_dim and state belong to the
- * library (device pointers and sizes of that chunk's call) and must not be
- * changed.  Host memory, owned by the caller.
+ * library (device pointers and sizes of that chunk's call, and a check word
+ * over them: an active record the library did not write is refused with
+ * EINVAL) and must not be changed.  Host memory, owned by the caller.
  */
 typedef struct attn_prefill_pending {
     int active;

@@ -87,6 +87,11 @@ int main(void)
         EXPECT(rec.active, 0);
         EXPECT(attn_prefill_finish(&rec, NULL), ATTN_OK);
         EXPECT(attn_prefill_finish(&bad, NULL), ATTN_EINVAL);
+        bad.head_dim = 128;       /* a valid size, but not a record the library wrote */
+        EXPECT(attn_prefill_finish(&bad, NULL), ATTN_EINVAL);
+        EXPECT(attn_prefill_chunk_deferred(P, P, P, ATTN_BF16, 1, 8, 2, 128, 256, 0, 16, I, I, 16, 64, 0.088f, 0,
+                                           NULL, 0, 0, (float *)P, NULL, 0, NULL, &bad, &rec, NULL),
+               ATTN_EINVAL);
         EXPECT(attn_prefill_finish(NULL, NULL), ATTN_EINVAL);
     }
     /* planners: sizes from host scalars only */

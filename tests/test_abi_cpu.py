@@ -249,6 +249,11 @@ def test_prefill_deferred_validation():
     bad.active, bad.head_dim = 1, 96
     assert prefill_deferred(None, prev=bad) == EINVAL
     assert L.attn_prefill_finish(ctypes.byref(bad), None) == EINVAL
+    # active with a valid head size, but not written by the library (its
+    # check word does not match): refused before anything could launch
+    bad.head_dim = 128
+    assert prefill_deferred(None, prev=bad) == EINVAL
+    assert L.attn_prefill_finish(ctypes.byref(bad), None) == EINVAL
     assert L.attn_prefill_finish(None, None) == EINVAL
     # nothing owed, nothing to run: OK without a launch, and the record says so
     rec = api.PrefillPending()
