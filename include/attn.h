@@ -324,8 +324,9 @@ typedef struct attn_prefill_pending {
  * record; NULL or inactive for none) runs in this call: in this chunk's
  * attention launch, in workgroups past the attention items, when this chunk
  * takes the bf16 prefill kernels with prev's head_dim, otherwise on a launch
- * of its own first.  A loop of such calls is one launch per chunk where
- * attn_prefill_chunk + attn_rope_qkv take up to three.
+ * of its own first (a merge too large for the attention launch's spare
+ * workgroups takes that launch too).  When both ride, a loop of such calls is
+ * one launch per chunk where attn_prefill_chunk + attn_rope_qkv take three.
  *   next     the next chunk's attn_rope_qkv arguments, or NULL (as in
  *            attn_prefill_chunk_rope_next, with its precondition)
  *   prev     an earlier chunk's record, or NULL; read before *pending is
