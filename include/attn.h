@@ -322,8 +322,8 @@ typedef struct attn_prefill_pending {
  * `workspace` and *pending records the merge owed: this chunk's rows of `out`
  * are final only once it has run.  The merge *prev owes (an earlier chunk's
  * record; NULL or inactive for none) runs in this call: in this chunk's
- * attention launch, in workgroups past the attention items, when this chunk
- * takes the bf16 prefill kernels with prev's head_dim, otherwise on a launch
+ * attention launch, in workgroups of its own ahead of the attention items,
+ * when this chunk takes the bf16 prefill kernels with prev's head_dim, otherwise on a launch
  * of its own first (a merge too large for the attention launch's spare
  * workgroups takes that launch too).  When both ride, a loop of such calls is
  * one launch per chunk where attn_prefill_chunk + attn_rope_qkv take three.
