@@ -35,7 +35,10 @@
 //    entirely above a wave's causal limit are skipped; only tiles that cross
 //    the diagonal are masked.
 //  * Split-KV: when the chunk has too few row tiles to fill 256 CUs, the key
-//    range is split and the parts are merged by a log-sum-exp combine.
+//    range is split and the parts are merged by a log-sum-exp combine: its
+//    own kernel, or (chunk loops) workgroups of the next chunk's launch.
+//  * Workgroups besides the attention items: the previous chunk's merge
+//    (ahead of them) and the next chunk's RoPE + append (after them).
 //  * blockIdx -> (group, split, row tile, sequence) with the group fastest,
 //    so with 8 KV groups every XCD streams one group's K/V from its own L2.
 #include <algorithm>
