@@ -438,6 +438,62 @@ size_t attn_decode_workspace_bytes(int n_seq, int n_heads, int n_kv, int head_di
 
 namespace {
 
+// Byte ranges [p, p + n) that share a byte.
+bool overlap(const void* a, size_t na, const void* b, size_t nb) {
+    if (!a || !b || !na || !nb) return false;
+    const char* x = static_cast<const char*>(a);
+    const char* y = static_cast<const char*>(b);
+    return x < y + nb && y < x + na;
+}
+
+// The work of one pipelined call that may run concurrently -- this chunk's
+// attention, the next chunk's finish and an earlier chunk's merge -- touches
+// disjoint rows outside the caches: no buffer one of them writes overlaps a
+// buffer another one reads or writes.  The cache rows are the caller's
+// chunk-order precondition.
+bool pipeline_disjoint(const void* q, int dtype, int n_tok, int n_heads, int head_dim, const void* gate,
+                       int gate_ld, const float* out, const void* workspace, size_t workspace_bytes,
+                       const NextFinish* next, const PendingState* pv, int prev_hd) {
+    if (!next && !pv) return true;
+    const size_t esz = dtype == ATTN_BF16 ? 2 : 4;
+    const size_t rows = (size_t)(n_tok > 0 ? n_tok : 0) * (size_t)n_heads;
+    struct Span {
+        const void* p;
+        size_t n;
+    };
+    // this chunk: read (q, gate) and written (out, workspace)
+    const Span q_in{q, rows * head_dim * esz};
+    const Span g_in{gate, gate && rows ? ((rows - 1) * (size_t)gate_ld + head_dim) * esz : 0};
+    const Span o_w{out, rows * head_dim * sizeof(float)};
+    const Span ws_w{workspace, workspace ? workspace_bytes : 0};
+    const Span mine[] = {q_in, g_in, o_w, ws_w};
+    auto hits = [&](const Span& x, const Span* set, int n) {
+        for (int i = 0; i < n; ++i)
+            if (overlap(x.p, x.n, set[i].p, set[i].n)) return true;
+        return false;
+    };
+    Span nx_w{nullptr, 0}, nx_in[3] = {};
+    if (next) {
+        const size_t ne = next->dtype == ATTN_BF16 ? 2 : 4;
+        const attn::RopeArgs& a = *next->q;
+        const attn::RopeArgs& k = *next->kv;
+        nx_w = {a.y, (size_t)a.n_tok * a.n_heads * a.head_dim * ne};
+        nx_in[0] = {a.x, (size_t)a.n_tok * a.n_heads * a.head_dim * ne};
+        nx_in[1] = {k.x, (size_t)k.n_tok * k.n_heads * k.head_dim * ne};
+        nx_in[2] = {k.v_src, (size_t)k.n_tok * k.n_heads * k.head_dim * ne};
+        // its query rows are written while this chunk reads and writes its own
+        if (hits(nx_w, mine, 4)) return false;
+        // this chunk's writes against what it reads
+        if (hits(o_w, nx_in, 3) || hits(ws_w, nx_in, 3)) return false;
+    }
+    if (pv) {
+        // the earlier chunk's output rows, written by its merge
+        const Span pw{pv->m.out, (size_t)pv->m.n_tok * pv->m.n_heads * prev_hd * sizeof(float)};
+        if (hits(pw, mine, 4) || hits(pw, nx_in, 3) || overlap(pw.p, pw.n, nx_w.p, nx_w.n)) return false;
+    }
+    return true;
+}
+
 int prefill_chunk_impl(const void* q, const void* k_cache, const void* v_cache, int dtype,
                        int n_seq, int n_heads, int n_kv, int head_dim, int cap, int ring, int n_tok,
                        const int32_t* cu_seq, const int32_t* start, int max_chunk, int max_end,
@@ -460,6 +516,9 @@ int prefill_chunk_impl(const void* q, const void* k_cache, const void* v_cache, 
     const PendingState* pv = defer ? defer->prev : nullptr;
     if (pv && workspace && workspace_bytes && (const char*)workspace < pv->ws_hi &&
         pv->ws_lo < (const char*)workspace + workspace_bytes)
+        return ATTN_EINVAL;
+    if (!pipeline_disjoint(q, dtype, n_tok, n_heads, head_dim, gate, gate_ld, out, workspace, workspace_bytes,
+                           next, pv, defer ? defer->prev_hd : 0))
         return ATTN_EINVAL;
     // after validation, nothing but the launches can fail: the next chunk's
     // finish runs after this chunk's attention unless it rides in its launch

@@ -287,7 +287,12 @@ typedef struct attn_rope_qkv_args {
  * that has the next chunk's projected rows while this chunk attends (one
  * layer over a projected prompt); a caller that projects the next chunk only
  * after this one has passed every layer uses the two separate calls.
- * Errors: those of either call, checked before anything is launched.
+ * Outside the caches the two calls' buffers must not overlap where either
+ * writes: next->q_out against this call's q, gate, out and workspace, and
+ * this call's out and workspace against next->q, k_new and v_new (each as
+ * the rows its sizes span).
+ * Errors: those of either call, checked before anything is launched; EINVAL
+ * for buffers that overlap as above.
  */
 int attn_prefill_chunk_rope_next(const void *q, const void *k_cache, const void *v_cache, int dtype,
                                  int n_seq, int n_heads, int n_kv, int head_dim, int cap, int ring,
@@ -337,9 +342,12 @@ typedef struct attn_prefill_pending {
  * output rows, batch arrays and gate values must stay valid until then; after
  * the last chunk, run attn_prefill_finish on its record.  The results are
  * those of the same chunks through attn_prefill_chunk.
+ * The buffers must not overlap as for attn_prefill_chunk_rope_next, and
+ * prev's output rows (written by its merge) must overlap none of this call's
+ * q, gate, out and workspace nor next's q, q_out, k_new and v_new.
  * Errors: those of attn_prefill_chunk and attn_rope_qkv, checked before
- * anything is launched; EINVAL for a NULL pending, an invalid prev record or
- * overlapping workspaces.
+ * anything is launched; EINVAL for a NULL pending, an invalid prev record,
+ * overlapping workspaces or buffers that overlap as above.
  */
 int attn_prefill_chunk_deferred(const void *q, const void *k_cache, const void *v_cache, int dtype,
                                 int n_seq, int n_heads, int n_kv, int head_dim, int cap, int ring,

@@ -263,6 +263,27 @@ def test_prefill_deferred_validation():
     assert L.attn_prefill_finish(ctypes.byref(rec), None) == OK
 
 
+def test_pipelined_buffers_must_be_disjoint():
+    """The pipelined calls run the next chunk's finish (and a deferred merge)
+    beside this chunk's attention: a buffer one of them writes may not overlap
+    one another reads or writes.  Refused before anything is launched."""
+    def at(mb):
+        return ctypes.c_void_p(mb << 20)
+    # this chunk: q at 16 MB, out at 32 MB; next: q at 48, q_out at 64, k/v at 80 and 96 MB
+    mine = dict(q=at(16), out=at(32))
+    nxt = dict(q=at(48), q_out=at(64), k_new=at(80), v_new=at(96))
+    clash = [({**nxt, "q_out": at(16)}, {}),                 # next's queries written over this q
+             ({**nxt, "q_out": at(32)}, {}),                 # ... over this chunk's output
+             ({**nxt, "q": at(32)}, {}),                     # next reads rows this chunk writes
+             ({**nxt, "v_new": ctypes.c_void_p((32 << 20) + 4096)}, {}),
+             (nxt, {"ws": at(64), "wsb": 4096}),             # workspace over next's rotated queries
+             ({**nxt, "q_out": at(200)}, {"gate": ctypes.c_void_p((200 << 20) - 64), "gate_mode": 1,
+                                          "gate_ld": 128})]  # the gate rows' tail
+    for n, extra in clash:
+        assert prefill_rope_next(n, **mine, **extra) == EINVAL
+        assert prefill_deferred(n, **mine, **extra) == EINVAL
+
+
 def rope(**kw):
     a = dict(x=P, y=P, dtype=0, n_tok=4, nh=4, hd=64, n_seq=1, cu=P, st=P, max_chunk=4, f=P,
              rd=64, rs=1.0, norm=0, w=None, eps=1e-6)

@@ -124,6 +124,10 @@ def test_deferred_merge_across_paths():
     with pytest.raises(api.AttnError) as e:
         ra.attend_step(ia, pending=api.PrefillPending(), prev=rec_a, workspace=ra.workspace)
     assert e.value.status == -1
+    # the pending merge writes its chunk's output rows: a call writing the same rows is refused
+    with pytest.raises(api.AttnError) as e:
+        ra.attend_step(ia, pending=api.PrefillPending(), prev=rec_a, workspace=ra.workspace_alt)
+    assert e.value.status == -1
     rb.attend_step(ib, pending=rec_b, prev=rec_a)      # hd 64 merge alone, then hd 128 attention
     assert rec_b.active == 1 and rec_b.head_dim == 128
     rc.attend_step(ic, pending=rec_c, prev=rec_b)      # bf16 merge alone, then the float32 path
