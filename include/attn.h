@@ -20,8 +20,8 @@
  *   tokens are packed back to back in token-major tensors of n_tok rows.
  *   cu_seq [n_seq+1] (device, int32) gives each sequence's first packed row;
  *   start [n_seq] (device, int32) gives the absolute position of that row
- *   ([ATT] fn qwen_attention_batch: the configured position is the chunk's
- *   FIRST absolute position).  Token i of sequence b is packed row
+ *   ([ATT] fn qwen_attention_batch: the position a call is configured with is
+ *   where its chunk starts).  Token i of sequence b is packed row
  *   cu_seq[b]+i at position start[b]+i.  max_chunk (host) bounds every
  *   sequence's token count; max_end (host) bounds every start[b]+len_b.  The
  *   host checks sizes from these host scalars; the device arrays are trusted

@@ -241,7 +241,7 @@ void orc_finish_heads(double *x, int n_tok, int n_heads, int hd, const int64_t *
  *   s_j = scale * <q, K_j>,  m = max s,  e_j = exp(s_j - m),  l = sum e_j,
  *   P_j = e_j / l,  O = sum_j P_j V_j.
  * [ATT] fn attention_head (max-subtracted softmax, probabilities returned);
- * [NDL] module docs: position p attends to keys at <= p.
+ * [NDL] module docs: a row at position p sees keys 0..p.
  * Readings: no weight is skipped (the page skips |P| < 1e-12); the softmax is
  * normalised before the P.V sum, as in fn attention_head.
  */
@@ -433,9 +433,9 @@ int orc_head_importance(const double *probs, int nh, long ctx, long probs_ld, do
 /* ------------------------------------------------------------------------ */
 
 /*
- * [ATT] fn vnorm_head (Gemma-4): scale-less RMS normalisation of one V head
- * before it enters the cache, x <- x / sqrt(mean(x^2) + eps) -- no weight, no
- * "+1".  x: rows of hd values, in place, then the storage rounding.
+ * [ATT] fn vnorm_head (Gemma-4): a V head is RMS-normalised, without a
+ * weight, ahead of the cache write: x <- x / sqrt(mean(x^2) + eps) -- no
+ * weight, no "+1".  x: rows of hd values, in place, then the storage rounding.
  * Reading: evaluated in double and rounded once, like the qk-norm.
  */
 void orc_vnorm_heads(double *x, long rows, int hd, double eps, int store_dtype)

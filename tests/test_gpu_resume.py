@@ -5,10 +5,10 @@ attn_decode with probabilities) on the cache the prefill left.  Every prefill
 output row and every decode output and probability row is compared with the
 oracle's one-shot run of the whole sequence, one token at a time.
 
-needle-core 0.3.1 src/v2/batch.rs: fn prefill_batch leaves the state exactly
-as the equivalent token-by-token run, so decoding can continue from it; the
-module docs note that the cross-chunk K/V hand-off is what a multi-turn
-session relies on."""
+needle-core 0.3.1 src/v2/batch.rs: fn prefill_batch (after a batched prefill
+the state equals that of feeding the same tokens one at a time, which is what
+lets decode steps pick up from it) and the module docs (a multi-turn session
+depends on the K/V handed from one chunk to the next)."""
 import numpy as np
 import pytest
 import torch
