@@ -22,7 +22,9 @@ operands, `measured_peak`, and on constant ones, `measured_peak_const`, and a
 streaming read); `cpu_baseline` is the CPU oracle timed on a bounded sample
 of the same workload on this host.  The decode line also carries
 `importance`: the per-position importance call (sum over heads of the step's
-probabilities), timed per launch after the step, outside it.
+probabilities), timed per launch after the step, outside it; and
+`without_probs`: the same attention call with no probabilities asked for,
+timed per launch (the K/V read path alone, next to the step's full rate).
 """
 from __future__ import annotations
 
@@ -417,6 +419,15 @@ def calibrate(torch, stream):
             "read_share_kb": share_kb, "compute_units": cus}
 
 
+def bare_with_measured_peak(bare, calib):
+    """The decode line's probability-free sub-line, with the measured read peak."""
+    if calib is None:
+        return bare
+    bare = dict(bare)
+    bare["frac_measured"] = round(bare["kv_read_gbs"] / calib["hbm_read_gbs"], 4)
+    return bare
+
+
 def with_measured_peak(roof, calib):
     """Add the fraction of the peak measured in this run to a roofline."""
     if calib is None:
@@ -528,6 +539,18 @@ def bench_decode(torch, w, args, stream):
                              "avg_launch_ms": round(imp_ms, 4), "bytes_per_launch": imp_bytes,
                              "achieved_gbs": round(imp_bytes / (imp_ms * 1e-3) / 1e9, 1),
                              "frac": round(imp_bytes / (imp_ms * 1e-3) / 1e9 / PEAK_HBM_GBS, 4)}
+        if w.new_tokens == 1:
+            # the same batch and call with probs = NULL: the K/V read path on
+            # its own, so the cost of the probabilities' writes shows apart
+            bare = runner.DecodeStep(w.replace(want_probs=False), d, device="cuda")
+            bare.finish_and_append()
+            for _ in range(2):
+                per = time_launches(torch, [bare.attend] * max(3, args.steps), stream)
+            bare_ms = sum(per) / len(per)
+            out["without_probs"] = {"kernel": "attn_decode, probs NULL (decode_split_kernel + decode_combine_kernel)",
+                                    "avg_launch_ms": round(bare_ms, 4), "bytes_per_launch": kv,
+                                    "kv_read_gbs": round(kv / (bare_ms * 1e-3) / 1e9, 1),
+                                    "frac": round(kv / (bare_ms * 1e-3) / 1e9 / PEAK_HBM_GBS, 4)}
     return out, d
 
 
@@ -564,7 +587,9 @@ def main():
                "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "bf16",
                "data": "synthetic", "config": dict(res["config"], workload=w.name),
                "roofline": with_measured_peak(res["roofline"], calib),
-               **({"importance": res["importance"]} if "importance" in res else {})}
+               **({"importance": res["importance"]} if "importance" in res else {}),
+               **({"without_probs": bare_with_measured_peak(res["without_probs"], calib)}
+                  if "without_probs" in res else {})}
         # the decode baseline covers one new token over a full-length cache
         if not args.no_cpu and w.new_tokens == 1 and not w.ring:
             res["cpu_baseline"] = cpu_baseline_decode(w, d, args.cpu_seconds)
@@ -597,6 +622,8 @@ def main():
             torch.cuda.empty_cache()
             dec, _ = bench_decode(torch, wl.CONFIGS["c2_decode"], args, stream)
             dec["roofline"] = with_measured_peak(dec["roofline"], calib)
+            if "without_probs" in dec:
+                dec["without_probs"] = bare_with_measured_peak(dec["without_probs"], calib)
             res["decode"] = dec
     if calib is not None:
         res["calibration"] = calib
