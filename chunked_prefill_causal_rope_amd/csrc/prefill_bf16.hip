@@ -153,8 +153,11 @@ __host__ __device__ constexpr int min_tiles_per_split(int rows_per_tile) {
 #ifndef ATTN_PREFILL_ITEM_COST_128
 #define ATTN_PREFILL_ITEM_COST_128 4
 #endif
+#ifndef ATTN_PREFILL_ITEM_COST_256
+#define ATTN_PREFILL_ITEM_COST_256 2
+#endif
 __host__ __device__ constexpr int item_cost_tiles(int rows_per_tile) {
-    return rows_per_tile == 256 ? 2 : ATTN_PREFILL_ITEM_COST_128;
+    return rows_per_tile == 256 ? ATTN_PREFILL_ITEM_COST_256 : ATTN_PREFILL_ITEM_COST_128;
 }
 
 // First key tile a row tile reads: with a sliding window of W keys its
