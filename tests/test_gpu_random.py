@@ -49,7 +49,7 @@ def _draw_prefill(seed):
                        window=window, ring=bool(ring), cap=cap, gate_mode=gate, v_norm=v_norm)
 
 
-@pytest.mark.parametrize("seed", range(2000, 2064))
+@pytest.mark.parametrize("seed", [*range(2000, 2064), *range(5000, 5200)])
 def test_random_prefill_configs(seed):
     w = _draw_prefill(seed)
     say(f"random prefill {w}")
@@ -83,7 +83,7 @@ def _draw_decode(seed):
                        v_norm=bool(rng.random() < 0.3))
 
 
-@pytest.mark.parametrize("seed", range(3000, 3032))
+@pytest.mark.parametrize("seed", [*range(3000, 3032), *range(6000, 6100)])
 def test_random_decode_configs(seed):
     w = _draw_decode(seed)
     say(f"random decode {w}")
