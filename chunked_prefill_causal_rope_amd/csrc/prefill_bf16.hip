@@ -391,6 +391,41 @@ struct alignas(16) PingPongSmem {
 #ifndef ATTN_PP_PERMLANE
 #define ATTN_PP_PERMLANE 1
 #endif
+// K/V staging by LDS-DMA loads (head dimension 128): each wave load moves 64
+// keys' 16-byte chunk c of a tile straight into LDS, with no staging
+// registers, so a tile's loads can be issued two tiles ahead into four LDS
+// slots.  A tile is laid out as chunk columns: column c (byte c * kDmaCol)
+// holds chunk c of keys 0..63 at 16 bytes per key.  The 64-byte pad per
+// column puts the 16 keys of a score-fragment read and the four columns of a
+// transposing read on distinct banks.
+#ifndef ATTN_PP_DMA
+#define ATTN_PP_DMA 1
+#endif
+constexpr int kDmaCol = kTK * 16 + 64;
+template <int HD>
+struct alignas(16) PingPongDmaSmem {
+    static constexpr int KS = 0;                  // unused: column layout
+    static constexpr int VS = 0;
+    static constexpr int kTile = HD / 8 * kDmaCol;
+    uint8_t k[4][kTile];
+    uint8_t v[4][kTile];
+};
+// LDS byte address of a shared-memory location (wave-uniform)
+__device__ __forceinline__ uint32_t lds_addr(const void* p) {
+    return __builtin_amdgcn_readfirstlane(
+        (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) void*)p);
+}
+// One wave load of 16 bytes per lane into LDS at m0 + 16 * lane, from the
+// buffer rsrc at byte voff; the compiler sees no LDS write and no counter,
+// so the caller waits (vmcnt) before the barrier that publishes the data.
+__device__ __forceinline__ void dma16(uint32_t m0v, int voff, __amdgpu_buffer_rsrc_t rs) {
+    asm volatile("s_mov_b32 m0, %0\n\tbuffer_load_dwordx4 %1, %2, 0 offen lds"
+                 :: "s"(m0v), "v"(voff), "s"(rs) : "memory");
+}
+template <int N>
+__device__ __forceinline__ void wait_vmcnt() {
+    asm volatile("s_waitcnt vmcnt(%0)" :: "n"(N) : "memory");
+}
 
 // Workgroups past the attention grid finish the next chunk's rows (RoPE and
 // cache append), using the kernel's LDS for the token's tables.  The next
@@ -455,7 +490,8 @@ __device__ __forceinline__ void extra_role(const PrefillArgs& a, Sm& sm, int wg)
 
 template <int HD, bool WIN>
 __global__ __launch_bounds__(512, 1) void prefill_pp_kernel(PrefillArgs a) {
-    using Sm = PingPongSmem<HD>;
+    constexpr bool DMA = ATTN_PP_DMA && HD == 128;
+    using Sm = std::conditional_t<DMA, PingPongDmaSmem<HD>, PingPongSmem<HD>>;
     constexpr int kThreads = 512;
     constexpr int KS = Sm::KS;
     constexpr int VS = Sm::VS;
@@ -585,6 +621,24 @@ __global__ __launch_bounds__(512, 1) void prefill_pp_kernel(PrefillArgs a) {
     // transposing-read address of this lane inside a V tile (see the
     // full-tile kernel)
     const int tr_off = (4 * hf + ((lane & 15) >> 2)) * VS + 4 * (lane & 3) + 16 * ((lane >> 4) & 1);
+    // the same reads in the DMA column layout (byte offsets): a score
+    // fragment's lane reads key rl of column 2*kk + hf; a transposing read's
+    // lane points at key 4*hf + (lane&15)/4 of column 4*db + 2*((lane>>4)&1)
+    // + (lane&3)/2, half (lane&1) of its 16 bytes
+    const int kdma_off = hf * kDmaCol + rl * 16;
+    const int vdma_off = (2 * ((lane >> 4) & 1) + ((lane & 3) >> 1)) * kDmaCol + (4 * hf + ((lane & 15) >> 2)) * 16 +
+                         8 * (lane & 1);
+    // DMA staging: wave w loads columns 2w and 2w+1 of each tile; lane i
+    // takes key i's chunk
+    const uint32_t lds_k = lds_addr(&sm.k[0][0]), lds_v = lds_addr(&sm.v[0][0]);
+    const int dma_c0 = 2 * __builtin_amdgcn_readfirstlane(wave);
+    auto dma_tile = [&](const uint16_t* base, int j, uint32_t lds_slot) __attribute__((always_inline)) {
+        const auto rs = tile_rsrc(base, j);
+#pragma unroll
+        for (int q = 0; q < 2; ++q)
+            dma16(lds_slot + (dma_c0 + q) * kDmaCol, lane * HD * 2 + (dma_c0 + q) * 16, rs);
+    };
+    constexpr int kSlotBytes = DMA ? PingPongDmaSmem<HD>::kTile : 0;
 
     f32x16_t O[NDB];
 #pragma unroll
@@ -607,16 +661,29 @@ __global__ __launch_bounds__(512, 1) void prefill_pp_kernel(PrefillArgs a) {
         // phases are kept whole: nothing is scheduled across their bounds
         __builtin_amdgcn_sched_barrier(0);
         if (ATTN_PP_PRIO) __builtin_amdgcn_s_setprio(ATTN_PP_PRIO);
-        const uint16_t* kl = sm.k[ks];
-        const uint16_t* vl = sm.v[vs] + tr_off;
         auto kload = [&](int st) __attribute__((always_inline)) {   // st = (kk, slab)
-            return ld16(kl + ((st % 2) * 32 + rl) * KS + (st / 2) * 16 + hf * 8);
+            if constexpr (DMA) {
+                const uint8_t* kb8 = reinterpret_cast<const uint8_t*>(sm.k[ks]) + kdma_off;
+                return ld16(kb8 + (st / 2) * 2 * kDmaCol + (st % 2) * 32 * 16);
+            } else {
+                const uint16_t* kl = reinterpret_cast<const uint16_t*>(sm.k[ks]);
+                return ld16(kl + ((st % 2) * 32 + rl) * KS + (st / 2) * 16 + hf * 8);
+            }
         };
         auto vfrag = [&](int st) __attribute__((always_inline)) {   // st = (kb, tt, db)
             const int kb = st / (2 * NDB), tt = (st / NDB) % 2, db = st % NDB;
-            const uint16_t* vrow = vl + (kb * 32 + tt * 16) * VS + db * 32;
-            const u32x2_t lo = lds_read_tr16(vrow);
-            const u32x2_t hi = lds_read_tr16(vrow + 8 * VS);
+            u32x2_t lo, hi;
+            if constexpr (DMA) {
+                const uint8_t* vp = reinterpret_cast<const uint8_t*>(sm.v[vs]) + vdma_off + db * 4 * kDmaCol +
+                                    (kb * 32 + tt * 16) * 16;
+                lo = lds_read_tr16(reinterpret_cast<const uint16_t*>(vp));
+                hi = lds_read_tr16(reinterpret_cast<const uint16_t*>(vp + 8 * 16));
+            } else {
+                const uint16_t* vrow = reinterpret_cast<const uint16_t*>(sm.v[vs]) + tr_off + (kb * 32 + tt * 16) * VS +
+                                       db * 32;
+                lo = lds_read_tr16(vrow);
+                hi = lds_read_tr16(vrow + 8 * VS);
+            }
             const u32x4_t vv = {lo.x, lo.y, hi.x, hi.y};
             return vv;
         };
@@ -731,15 +798,51 @@ __global__ __launch_bounds__(512, 1) void prefill_pp_kernel(PrefillArgs a) {
         // start of the phase, or reading the next matrix phase's first
         // fragments here, is slower.
         if (ATTN_PP_LATE_STORE) __builtin_amdgcn_sched_barrier(0);
-        store_k(ksl, set);
-        store_v(vsl, set);
-        load_kv(min(j + 2 + SD, te - 1), min(j + 1 + SD, te - 1), set);
+        if constexpr (DMA) {
+            // K[j+3] and V[j+2], two tiles ahead (slots given by the caller)
+            dma_tile(kc, min(j + 3, te - 1), lds_k + ksl * kSlotBytes);
+            dma_tile(vc, min(j + 2, te - 1), lds_v + vsl * kSlotBytes);
+        } else {
+            store_k(ksl, set);
+            store_v(vsl, set);
+            load_kv(min(j + 2 + SD, te - 1), min(j + 1 + SD, te - 1), set);
+        }
     };
 
     constexpr std::integral_constant<bool, true> yes{};
     constexpr std::integral_constant<bool, false> no{};
     const int n = te - tb;
-    if (n > 0) {
+    if (DMA && n > 0) {
+        // prologue: K[tb..tb+2] and V[tb..tb+1] in slots 0..2 / 0..1; tile
+        // tb+k sits in slot k mod 4.  Softmax phase k loads K[tb+k+3] and
+        // V[tb+k+2]; the end of matrix phase k waits for the loads of softmax
+        // phase k-1 (those of phase k may still be in flight), which every
+        // wave does before the barrier after which the first reader starts.
+        dma_tile(kc, tb, lds_k);
+        dma_tile(vc, tb, lds_v);
+        dma_tile(kc, min(tb + 1, te - 1), lds_k + kSlotBytes);
+        dma_tile(vc, min(tb + 1, te - 1), lds_v + kSlotBytes);
+        dma_tile(kc, min(tb + 2, te - 1), lds_k + 2 * kSlotBytes);
+        wait_vmcnt<0>();
+        __syncthreads();
+        if (grp == 1) __syncthreads();            // the second group starts one phase later
+        mphase(0, 0, yes, no);
+        __syncthreads();
+        int k = 0;
+        for (; k < n - 1; ++k) {
+            vphase(tb + k, (k + 3) & 3, (k + 2) & 3, set0);
+            __syncthreads();
+            mphase((k + 1) & 3, k & 3, yes, yes);
+            wait_vmcnt<4>();
+            __syncthreads();
+        }
+        vphase(tb + k, (k + 3) & 3, (k + 2) & 3, set0);
+        __syncthreads();
+        mphase((k + 1) & 3, k & 3, no, yes);
+        __syncthreads();
+        if (grp == 0) __syncthreads();            // the same barrier count in both groups
+        wait_vmcnt<0>();                          // no LDS write outlives the workgroup
+    } else if (n > 0) {
         // prologue: K[tb], V[tb], K[tb+1] in slots 0, 0, 1; the staging
         // sets then hold K[tb+2+s] and V[tb+1+s] for the softmax phase s
         load_kv(tb, tb, set0);
