@@ -401,6 +401,12 @@ struct alignas(16) PingPongSmem {
 #ifndef ATTN_PP_DMA
 #define ATTN_PP_DMA 1
 #endif
+// where a softmax phase's tile loads are issued: 1 at its start (measured
+// on c4 +4 % over 0, the end of the phase; issuing them at the start of the
+// matrix phase before it, one tile further ahead, was slower than either)
+#ifndef ATTN_PP_DMA_AT
+#define ATTN_PP_DMA_AT 1
+#endif
 constexpr int kDmaCol = kTK * 16 + 64;
 template <int HD>
 struct alignas(16) PingPongDmaSmem {
@@ -735,6 +741,10 @@ __global__ __launch_bounds__(512, 1) void prefill_pp_kernel(PrefillArgs a) {
     // LDS (K[j+2] into slot ksl, V[j+1] into slot vsl) and the next share's
     // global loads are issued
     auto vphase = [&](int j, int ksl, int vsl, auto set) __attribute__((always_inline)) {
+        if constexpr (DMA && ATTN_PP_DMA_AT == 1) {
+            dma_tile(kc, min(j + 3, te - 1), lds_k + ksl * kSlotBytes);
+            dma_tile(vc, min(j + 2, te - 1), lds_v + vsl * kSlotBytes);
+        }
         const int k0 = j * kTK;
         if (k0 + kTK - 1 > pw_lo) {
             const int lim = pos - k0 - 4 * hf;
@@ -800,8 +810,10 @@ __global__ __launch_bounds__(512, 1) void prefill_pp_kernel(PrefillArgs a) {
         if (ATTN_PP_LATE_STORE) __builtin_amdgcn_sched_barrier(0);
         if constexpr (DMA) {
             // K[j+3] and V[j+2], two tiles ahead (slots given by the caller)
-            dma_tile(kc, min(j + 3, te - 1), lds_k + ksl * kSlotBytes);
-            dma_tile(vc, min(j + 2, te - 1), lds_v + vsl * kSlotBytes);
+            if (ATTN_PP_DMA_AT == 0) {
+                dma_tile(kc, min(j + 3, te - 1), lds_k + ksl * kSlotBytes);
+                dma_tile(vc, min(j + 2, te - 1), lds_v + vsl * kSlotBytes);
+            }
         } else {
             store_k(ksl, set);
             store_v(vsl, set);
