@@ -802,11 +802,12 @@ __global__ __launch_bounds__(512, 1) void prefill_pp_kernel(PrefillArgs a) {
             pk[8 + q] = pack_bf16x2(__builtin_amdgcn_exp2f(__builtin_fmaf(S1[2 * q], sl, nm)),
                                     __builtin_amdgcn_exp2f(__builtin_fmaf(S1[2 * q + 1], sl, nm)));
         l_run += sum_bf16_pairs(pk);
-        // this thread's staging share, then the next share's global loads
-        // (unconditional, tile index clamped: past the last tile they refill
-        // slots that are never read again).  Measured: issuing them at the
-        // start of the phase, or reading the next matrix phase's first
-        // fragments here, is slower.
+        // register staging (head dimension 64): this thread's staging share,
+        // then the next share's global loads (unconditional, tile index
+        // clamped: past the last tile they refill slots that are never read
+        // again).  Measured on that path: issuing them at the start of the
+        // phase, or reading the next matrix phase's first fragments here, is
+        // slower.  The DMA path issues its loads where ATTN_PP_DMA_AT says.
         if (ATTN_PP_LATE_STORE) __builtin_amdgcn_sched_barrier(0);
         if constexpr (DMA) {
             // K[j+3] and V[j+2], two tiles ahead (slots given by the caller)
