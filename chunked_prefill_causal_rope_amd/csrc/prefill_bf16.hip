@@ -424,6 +424,9 @@ __device__ __forceinline__ uint32_t lds_addr(const void* p) {
 // One wave load of 16 bytes per lane into LDS at m0 + 16 * lane, from the
 // buffer rsrc at byte voff; the compiler sees no LDS write and no counter,
 // so the caller waits (vmcnt) before the barrier that publishes the data.
+// M0 is a register the compiler reserves and does not allocate; the
+// assembly of these kernels uses it only in these loads, each setting it
+// in the same asm statement, so it is not listed as a clobber.
 __device__ __forceinline__ void dma16(uint32_t m0v, int voff, __amdgpu_buffer_rsrc_t rs) {
     asm volatile("s_mov_b32 m0, %0\n\tbuffer_load_dwordx4 %1, %2, 0 offen lds"
                  :: "s"(m0v), "v"(voff), "s"(rs) : "memory");
